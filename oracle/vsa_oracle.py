@@ -1,0 +1,333 @@
+"""fp64 CPU oracle for cube block-sparse video attention (forward).
+
+TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
+benchmark's CPU-baseline leg may import this module.  The product path (the
+HIP library and its Python binding) never calls it, and this module imports
+nothing from the product package: the two share no code.
+
+What is computed, and where it comes from
+-----------------------------------------
+The pages describe video sparse attention (VSA) as attention that picks the
+important attention blocks dynamically, keeps roughly 10-20 % of the weights
+at sparsity 0.8-0.9, stays compatible with flash-attention style kernels, and
+(with the sliding-tile variant) avoids "mixed" partially masked blocks
+(FastVideo sparse-distillation article, section "核心技术解析 / 2.
+视频稀疏注意力VSA" and its figure caption; FastVideo attention-backend
+article, figure comparing NATTEN, Tiled NATTEN and STA).  Sparse attention
+paired with a linear-attention branch over the rest keeps global context at
+97 % sparsity (SparkDiffusion article, paragraph 3, RoLA) at linear cost
+(TurboDiffusion article, section "稀疏、蒸馏与全链路量化", SLA).
+
+The pages give no formulas.  This oracle implements the plainest method that
+fits them, with these conventions (each is a reading, not a quote):
+
+  O1  tokens of the latent grid (T, H, W) are grouped into 4x4x4 cubes of 64
+      tokens, so one 64x64 attention block is one whole query cube against
+      one whole key cube (no mixed blocks).  Grid padded up to multiples of 4
+      at the high end; padded tokens are zero and marked invalid.
+      Cube c = ((t//4) * (Hp/4) + y//4) * (Wp/4) + x//4, local index
+      l = ((t%4) * 4 + y%4) * 4 + x%4, cube-major row 64 c + l.
+  O2  coarse stage: each cube is mean-pooled over its valid tokens.
+  O3  block score s_ij = qbar_i . kbar_j (unscaled).
+  O4  each query cube keeps the k key cubes of largest score; equal scores
+      are broken towards the lower cube index; the list is stored ascending.
+  O5  fine stage: softmax(scale * Q_i K^T) V over the valid keys of the
+      selected cubes only (padded keys get -inf).
+  O6  linear branch: phi(x) = elu(x) + 1; for each query cube, over the valid
+      keys of the unselected cubes U,
+      O_lin = phi(Q) (sum_U phi(K)^T V) / (phi(Q) . sum_U phi(K)),
+      and 0 where U is empty.
+  O7  output = O_sparse (+ O_lin), back in raster token order.
+
+Every step is written as its definition, in float64, with no blocking,
+fusion or reordering beyond the definition.  Inputs are bf16 bit patterns
+(numpy uint16); they are widened exactly to float64 here.
+"""
+
+from __future__ import annotations
+
+import math
+from typing import Optional, Sequence, Tuple
+
+import numpy as np
+
+__all__ = [
+    "bf16_to_f64",
+    "padded_grid",
+    "cube_grid",
+    "n_cubes",
+    "token_row",
+    "valid_rows",
+    "cube_permute",
+    "cube_unpermute",
+    "cube_means",
+    "block_scores",
+    "topk_row",
+    "select_topk",
+    "attention_cube",
+    "sparse_attention",
+    "phi",
+    "linear_cube",
+    "linear_branch",
+    "forward",
+]
+
+
+# --------------------------------------------------------------------------
+# Numbers
+# --------------------------------------------------------------------------
+
+def bf16_to_f64(bits: np.ndarray) -> np.ndarray:
+    """Widen bf16 bit patterns to float64 exactly (bf16 is the top half of fp32)."""
+    u32 = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
+    return u32.view(np.float32).astype(np.float64)
+
+
+# --------------------------------------------------------------------------
+# O1: cube tiling and permutation
+# --------------------------------------------------------------------------
+
+def padded_grid(grid: Sequence[int]) -> Tuple[int, int, int]:
+    """Each grid axis rounded up to a multiple of 4 (padding at the high end)."""
+    return tuple(((int(d) + 3) // 4) * 4 for d in grid)
+
+
+def cube_grid(grid: Sequence[int]) -> Tuple[int, int, int]:
+    """Number of cubes along each axis."""
+    tp, hp, wp = padded_grid(grid)
+    return tp // 4, hp // 4, wp // 4
+
+
+def n_cubes(grid: Sequence[int]) -> int:
+    a, b, c = cube_grid(grid)
+    return a * b * c
+
+
+def token_row(t: int, y: int, x: int, grid: Sequence[int]) -> Tuple[int, int]:
+    """(cube c, local l) of the token at (t, y, x), per convention O1."""
+    _, cy, cx = cube_grid(grid)
+    c = ((t // 4) * cy + (y // 4)) * cx + (x // 4)
+    l = ((t % 4) * 4 + (y % 4)) * 4 + (x % 4)
+    return c, l
+
+
+def _row_of_token(grid: Sequence[int]) -> np.ndarray:
+    """Cube-major row 64 c + l of every raster token (t slowest, x fastest)."""
+    T, H, W = grid
+    rows = np.empty(T * H * W, dtype=np.int64)
+    s = 0
+    for t in range(T):
+        for y in range(H):
+            for x in range(W):
+                c, l = token_row(t, y, x, grid)
+                rows[s] = 64 * c + l
+                s += 1
+    return rows
+
+
+def valid_rows(grid: Sequence[int]) -> np.ndarray:
+    """bool[Np]: True for cube-major rows that hold a real token."""
+    valid = np.zeros(n_cubes(grid) * 64, dtype=bool)
+    valid[_row_of_token(grid)] = True
+    return valid
+
+
+def cube_permute(x: np.ndarray, grid: Sequence[int]) -> np.ndarray:
+    """[B, S, H, D] raster tokens -> [B, H, Np, D] cube-major rows (O1).
+
+    Works on any dtype (bit patterns move unchanged); padded rows are zero.
+    """
+    B, S, Hh, D = x.shape
+    rows = _row_of_token(grid)
+    assert S == rows.size, "token count does not match the grid"
+    out = np.zeros((B, Hh, n_cubes(grid) * 64, D), dtype=x.dtype)
+    for s in range(S):
+        out[:, :, rows[s], :] = x[:, s, :, :]
+    return out
+
+
+def cube_unpermute(xc: np.ndarray, grid: Sequence[int]) -> np.ndarray:
+    """Inverse of cube_permute: [B, H, Np, D] -> [B, S, H, D], pads dropped."""
+    B, Hh, Np, D = xc.shape
+    rows = _row_of_token(grid)
+    out = np.zeros((B, rows.size, Hh, D), dtype=xc.dtype)
+    for s in range(rows.size):
+        out[:, s, :, :] = xc[:, :, rows[s], :]
+    return out
+
+
+# --------------------------------------------------------------------------
+# O2-O4: coarse stage
+# --------------------------------------------------------------------------
+
+def cube_means(xc: np.ndarray, valid: np.ndarray) -> np.ndarray:
+    """Mean of each cube over its valid rows (O2): [B, H, Np, D] -> [B, H, Nc, D] f64."""
+    x = bf16_to_f64(xc) if xc.dtype == np.uint16 else np.asarray(xc, dtype=np.float64)
+    B, Hh, Np, D = x.shape
+    nc = Np // 64
+    out = np.zeros((B, Hh, nc, D), dtype=np.float64)
+    for c in range(nc):
+        rows = [64 * c + l for l in range(64) if valid[64 * c + l]]
+        out[:, :, c, :] = x[:, :, rows, :].sum(axis=2) / len(rows)
+    return out
+
+
+def block_scores(qbar: np.ndarray, kbar: np.ndarray) -> np.ndarray:
+    """s_ij = qbar_i . kbar_j, unscaled (O3): [B, H, Nc, D] x2 -> [B, H, Nc, Nc]."""
+    return np.matmul(qbar, np.swapaxes(kbar, -1, -2))
+
+
+def topk_row(scores: np.ndarray, k: int) -> np.ndarray:
+    """The k largest scores of one row, ties to the lower index, ascending (O4).
+
+    A stable sort on the negated score keeps equal scores in index order, so
+    the first k entries are the k best with the lowest-index tie winners.
+    -0.0 and +0.0 compare equal, as they should.
+    """
+    order = np.argsort(-np.asarray(scores, dtype=np.float64), kind="stable")
+    return np.sort(order[:k]).astype(np.int32)
+
+
+def select_topk(qc: np.ndarray, kc: np.ndarray, valid: np.ndarray, k: int) -> np.ndarray:
+    """Block index list int32 [B, H, Nc, k] (O2-O4)."""
+    qbar = cube_means(qc, valid)
+    kbar = cube_means(kc, valid)
+    s = block_scores(qbar, kbar)
+    B, Hh, nc, _ = s.shape
+    idx = np.empty((B, Hh, nc, k), dtype=np.int32)
+    for b in range(B):
+        for h in range(Hh):
+            for i in range(nc):
+                idx[b, h, i] = topk_row(s[b, h, i], k)
+    return idx
+
+
+# --------------------------------------------------------------------------
+# O5: fine stage
+# --------------------------------------------------------------------------
+
+def _as_f64(x: np.ndarray) -> np.ndarray:
+    return bf16_to_f64(x) if x.dtype == np.uint16 else np.asarray(x, dtype=np.float64)
+
+
+def attention_cube(q_rows: np.ndarray, k_all: np.ndarray, v_all: np.ndarray,
+                   valid: np.ndarray, cubes: Sequence[int], scale: float,
+                   return_probs: bool = False):
+    """Softmax attention of one query cube over the selected key cubes (O5).
+
+    q_rows: [64, D] queries of the cube; k_all, v_all: [Np, D] of one (b, h).
+    Returns O [64, D], lse [64] (natural log of the softmax normaliser, in
+    units of the scaled logits) and optionally P [64, n_keys].
+    """
+    q = _as_f64(q_rows)
+    keys = np.array([64 * j + l for j in cubes for l in range(64)], dtype=np.int64)
+    kk = _as_f64(k_all[keys])
+    vv = _as_f64(v_all[keys])
+    logits = scale * (q @ kk.T)
+    logits[:, ~valid[keys]] = -np.inf
+    m = logits.max(axis=1, keepdims=True)
+    e = np.exp(logits - m)
+    z = e.sum(axis=1, keepdims=True)
+    p = e / z
+    out = p @ vv
+    lse = (m + np.log(z))[:, 0]
+    if return_probs:
+        return out, lse, p
+    return out, lse
+
+
+def sparse_attention(qc, kc, vc, valid, idx, scale, cubes: Optional[Sequence[Tuple[int, int, int]]] = None):
+    """O_sparse [B, H, Np, D] f64 and lse [B, H, Np] (O5).
+
+    cubes: optional list of (b, h, i) to compute; other rows stay NaN.
+    """
+    B, Hh, Np, D = qc.shape
+    out = np.full((B, Hh, Np, D), np.nan)
+    lse = np.full((B, Hh, Np), np.nan)
+    todo = cubes if cubes is not None else [
+        (b, h, i) for b in range(B) for h in range(Hh) for i in range(Np // 64)]
+    for b, h, i in todo:
+        o, s = attention_cube(qc[b, h, 64 * i:64 * i + 64], kc[b, h], vc[b, h],
+                              valid, idx[b, h, i], scale)
+        out[b, h, 64 * i:64 * i + 64] = o
+        lse[b, h, 64 * i:64 * i + 64] = s
+    return out, lse
+
+
+# --------------------------------------------------------------------------
+# O6: linear branch
+# --------------------------------------------------------------------------
+
+def phi(x: np.ndarray) -> np.ndarray:
+    """elu(x) + 1 with alpha = 1: x + 1 for x > 0, exp(x) otherwise."""
+    x = np.asarray(x, dtype=np.float64)
+    return np.where(x > 0, x + 1.0, np.exp(np.minimum(x, 0.0)))
+
+
+def _cube_states(k_all: np.ndarray, v_all: np.ndarray, valid: np.ndarray):
+    """Per key cube j: S_j = sum_valid phi(k)^T v  [Nc, D, D], z_j = sum_valid phi(k)  [Nc, D]."""
+    kk = phi(_as_f64(k_all))
+    vv = _as_f64(v_all)
+    nc = kk.shape[0] // 64
+    D = kk.shape[1]
+    S = np.zeros((nc, D, vv.shape[1]))
+    z = np.zeros((nc, D))
+    for j in range(nc):
+        rows = [64 * j + l for l in range(64) if valid[64 * j + l]]
+        S[j] = kk[rows].T @ vv[rows]
+        z[j] = kk[rows].sum(axis=0)
+    return S, z
+
+
+def linear_cube(q_rows: np.ndarray, states, selected: Sequence[int]) -> np.ndarray:
+    """O_lin of one query cube over the unselected key cubes (O6): [64, D]."""
+    S, z = states
+    nc = S.shape[0]
+    sel = set(int(j) for j in selected)
+    unsel = [j for j in range(nc) if j not in sel]
+    if not unsel:
+        return np.zeros((q_rows.shape[0], S.shape[2]))
+    S_u = S[unsel].sum(axis=0)
+    z_u = z[unsel].sum(axis=0)
+    fq = phi(_as_f64(q_rows))
+    return (fq @ S_u) / (fq @ z_u)[:, None]
+
+
+def linear_branch(qc, kc, vc, valid, idx, cubes: Optional[Sequence[Tuple[int, int, int]]] = None):
+    """O_lin [B, H, Np, D] f64 (O6); cubes as in sparse_attention."""
+    B, Hh, Np, D = qc.shape
+    out = np.full((B, Hh, Np, D), np.nan)
+    todo = cubes if cubes is not None else [
+        (b, h, i) for b in range(B) for h in range(Hh) for i in range(Np // 64)]
+    states = {}
+    for b, h, i in todo:
+        if (b, h) not in states:
+            states[(b, h)] = _cube_states(kc[b, h], vc[b, h], valid)
+        out[b, h, 64 * i:64 * i + 64] = linear_cube(qc[b, h, 64 * i:64 * i + 64],
+                                                    states[(b, h)], idx[b, h, i])
+    return out
+
+
+# --------------------------------------------------------------------------
+# O7: whole layer
+# --------------------------------------------------------------------------
+
+def forward(q: np.ndarray, k: np.ndarray, v: np.ndarray, grid: Sequence[int], topk: int,
+            scale: Optional[float] = None, linear: bool = False, idx: Optional[np.ndarray] = None):
+    """Whole forward: [B, S, H, D] bf16 bits -> (O [B, S, H, D] f64, idx).
+
+    idx: optional precomputed block list (to feed a given selection).
+    """
+    D = q.shape[-1]
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    valid = valid_rows(grid)
+    qc = cube_permute(q, grid)
+    kc = cube_permute(k, grid)
+    vc = cube_permute(v, grid)
+    if idx is None:
+        idx = select_topk(qc, kc, valid, topk)
+    o, _ = sparse_attention(qc, kc, vc, valid, idx, scale)
+    if linear:
+        o = o + linear_branch(qc, kc, vc, valid, idx)
+    return cube_unpermute(o, grid), idx

@@ -1,0 +1,78 @@
+"""Pins of the oracle's cube permutation (convention O1) against an independent map.
+
+The independent map pads the raster grid to multiples of 4 with -1 markers and
+splits every axis into (cube, local) with a reshape/transpose, which is how a
+4x4x4 tiling reads in index algebra.  A wrong axis order, a swapped
+cube/local split or a missing pad fails here.
+"""
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+
+GRIDS = [(4, 4, 4), (8, 8, 8), (5, 6, 7), (1, 1, 1), (9, 3, 13), (4, 8, 12), (2, 5, 4)]
+
+
+def reshape_map(grid):
+    """Raster token id at every cube-major row (-1 for padding), via reshape."""
+    T, H, W = grid
+    Tp, Hp, Wp = [((d + 3) // 4) * 4 for d in grid]
+    ids = np.full((Tp, Hp, Wp), -1, dtype=np.int64)
+    ids[:T, :H, :W] = np.arange(T * H * W).reshape(T, H, W)
+    cubes = ids.reshape(Tp // 4, 4, Hp // 4, 4, Wp // 4, 4).transpose(0, 2, 4, 1, 3, 5)
+    return cubes.reshape(-1)
+
+
+@pytest.mark.parametrize("grid", GRIDS)
+def test_permute_matches_reshape_map(grid):
+    T, H, W = grid
+    S = T * H * W
+    B, Hh, D = 2, 3, 4
+    rng = np.random.default_rng(1)
+    x = rng.integers(1, 60000, size=(B, S, Hh, D)).astype(np.uint16)
+    xc = oracle.cube_permute(x, grid)
+    m = reshape_map(grid)
+    assert xc.shape == (B, Hh, m.size, D)
+    for r, s in enumerate(m):
+        if s < 0:
+            assert np.all(xc[:, :, r] == 0)
+        else:
+            assert np.array_equal(xc[:, :, r], x[:, s])
+    assert np.array_equal(oracle.valid_rows(grid), m >= 0)
+
+
+@pytest.mark.parametrize("grid", GRIDS)
+def test_unpermute_inverts_permute(grid):
+    T, H, W = grid
+    rng = np.random.default_rng(2)
+    x = rng.integers(0, 65536, size=(1, T * H * W, 2, 8)).astype(np.uint16)
+    assert np.array_equal(oracle.cube_unpermute(oracle.cube_permute(x, grid), grid), x)
+
+
+def test_token_row_worked_example():
+    # Grid 8x8x8: 2x2x2 cubes.  Token (5, 2, 7) lies in cube (1, 0, 1) -> c = 5,
+    # local (1, 2, 3) -> l = 1*16 + 2*4 + 3 = 27.
+    assert oracle.token_row(5, 2, 7, (8, 8, 8)) == (5, 27)
+    # Padded grid 21x45x80 -> 24x48x80: cubes per axis 6, 12, 20.
+    assert oracle.cube_grid((21, 45, 80)) == (6, 12, 20)
+    assert oracle.n_cubes((21, 45, 80)) == 1440
+    # Last token (20, 44, 79): cube (5, 11, 19) -> (5*12 + 11)*20 + 19 = 1439,
+    # local (0, 0, 3) -> 3.
+    assert oracle.token_row(20, 44, 79, (21, 45, 80)) == (1439, 3)
+
+
+@pytest.mark.parametrize("name", list(workloads.WORKLOADS))
+def test_workload_geometry(name):
+    wl = workloads.workload(name)
+    assert oracle.n_cubes(wl.grid) == wl.n_cubes
+    assert oracle.padded_grid(wl.grid) == wl.padded_grid
+
+
+def test_720p_every_cube_has_valid_tokens():
+    v = oracle.valid_rows((21, 45, 80)).reshape(-1, 64)
+    counts = v.sum(axis=1)
+    assert counts.min() >= 4
+    assert set(np.unique(counts)) <= {4, 16, 64}
+    assert v.sum() == 21 * 45 * 80
