@@ -1,0 +1,263 @@
+"""Benchmark: one cube block-sparse attention layer (forward) on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload wan1.3b]
+
+A step is one pass of the whole layer on inputs already resident in HBM:
+permute Q, K, V -> coarse stage (pool, score, top-k) -> fine block-sparse
+attention -> (linear branch, hybrid workload) -> unpermute.  The default
+workload is the Wan2.1-1.3B-shaped layer (latent 16x28x52, 12 heads,
+head_dim 128, sparsity 0.8 -> k = 73 of 364 cubes).
+
+Prints one JSON line.  `value` is the effective throughput of the whole
+layer: the flops of the computed 64x64 blocks (4 * 64 * 64 * D each, QK^T
+plus PV) divided by the layer time.  `roofline` reports the fine-stage kernel
+alone (the dominant kernel), timed with HIP events on the stream it runs on.
+`cpu_baseline` times the fp64 oracle on a bounded sample of the same layer on
+the host cores.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import platform
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6  # MI355X dense bf16 MFMA: 256 CU x 2.4 GHz x 4096 flop/clk
+PEAK_HBM_GBS = 8000.0
+METRIC = "ms/layer + effective TFLOPS (frac of bf16 MFMA peak), block-sparse attn fwd"
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="wan1.3b")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target oracle sample time")
+    return ap.parse_args()
+
+
+def kernel_source_hash() -> str:
+    path = os.path.join(ROOT, "block_sparse_video_cube_amd", "csrc", "attn_fwd.hip")
+    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per fine-stage launch from committed rocprofv3 counters, if current."""
+    path = os.path.join(ROOT, "profiles", f"attn_fwd_{workload}_traffic.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    if rec.get("kernel_sha256_16") != kernel_source_hash():
+        return None  # the kernel changed since the counters were taken
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(wl, budget_s: float):
+    """Time the fp64 oracle on whole heads of the layer and scale to the layer."""
+    import oracle
+    import workloads
+
+    try:
+        from threadpoolctl import threadpool_info
+
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    valid = oracle.valid_rows(wl.grid)
+    scale = wl.softmax_scale
+    t_total = 0.0
+    heads_done = 0
+    cubes_done = 0
+    n_heads = wl.batch * wl.heads
+    per_head_fixed = 0.0
+    per_cube = 0.0
+    # One head: permute + pool + score + top-k of all rows (fixed per head),
+    # then query cubes one by one until the time budget is spent.
+    b, h = 0, 0
+    sub = {n: workloads.make_head(wl, n, b, h)[None, :, None, :] for n in ("q", "k", "v")}
+    t0 = time.perf_counter()
+    qc, kc, vc = (oracle.cube_permute(sub[n], wl.grid) for n in ("q", "k", "v"))
+    idx = oracle.select_topk(qc, kc, valid, wl.topk)
+    states = oracle.vsa_oracle._cube_states(kc[0, 0], vc[0, 0], valid) if wl.linear else None
+    per_head_fixed = time.perf_counter() - t0
+    t1 = time.perf_counter()
+    for i in range(wl.n_cubes):
+        oracle.attention_cube(qc[0, 0, 64 * i:64 * i + 64], kc[0, 0], vc[0, 0], valid, idx[0, 0, i], scale)
+        if wl.linear:
+            oracle.linear_cube(qc[0, 0, 64 * i:64 * i + 64], states, idx[0, 0, i])
+        cubes_done += 1
+        if time.perf_counter() - t1 > budget_s:
+            break
+    per_cube = (time.perf_counter() - t1) / cubes_done
+    t_total = time.perf_counter() - t0
+    layer_s = n_heads * (per_head_fixed + wl.n_cubes * per_cube)
+    return {
+        "value": wl.fine_flops / layer_s / 1e12,
+        "unit": "TFLOP/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": (f"fp64 numpy oracle, head (b=0,h=0) of {wl.name}: permute+pool+score+top-k of all "
+                   f"{wl.n_cubes} rows plus {cubes_done} of {wl.n_cubes} query cubes "
+                   f"({t_total:.1f} s), scaled to {n_heads} heads"),
+        "ms_per_layer": layer_s * 1e3,
+        "host_cpus": os.cpu_count(),
+        "cpu_model": platform.processor() or platform.machine(),
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (--gpus {args.gpus} requested): every step of the "
+              "layer is independent per (batch, head), so several GPUs would each run this same "
+              "kernel on their share of the heads.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import block_sparse_video_cube_amd as vsa
+    import workloads
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    wl = workloads.workload(args.workload)
+    dev = torch.device("cuda:0")
+
+    def to_dev(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    inp = workloads.make_inputs(wl)
+    q, k, v = (to_dev(inp[n]) for n in ("q", "k", "v"))
+    del inp
+    g = vsa.make_geom(wl.batch, wl.heads, wl.head_dim, wl.grid)
+    d = vsa.geom_dims(g)
+    B, H, D = wl.batch, wl.heads, wl.head_dim
+    qc = torch.empty((B, H, d.rows, D), dtype=torch.bfloat16, device=dev)
+    kc = torch.empty_like(qc)
+    vt = torch.empty((B, H, d.n_cubes, D, 64), dtype=torch.bfloat16, device=dev)
+    oc = torch.empty_like(qc)
+    o = torch.empty_like(q)
+    idx = torch.empty((B, H, d.n_cubes, wl.topk), dtype=torch.int32, device=dev)
+    ws_sel = torch.empty(vsa.workspace_bytes(g), dtype=torch.uint8, device=dev)
+    ws_lin = torch.empty(max(16, vsa.workspace_bytes(g, linear=True)) if wl.linear else 16,
+                         dtype=torch.uint8, device=dev)
+    of = torch.empty((B, H, d.rows, D), dtype=torch.float32, device=dev) if wl.linear else None
+    oc2 = torch.empty_like(qc) if wl.linear else None
+
+    stages = ["permute", "select", "fine", "linear", "unpermute"] if wl.linear else \
+        ["permute", "select", "fine", "unpermute"]
+
+    def step(ev=None):
+        def mark(i):
+            if ev is not None:
+                ev[i].record()
+
+        mark(0)
+        vsa.cube_permute(q, wl.grid, out=qc)
+        vsa.cube_permute(k, wl.grid, out=kc)
+        vsa.cube_permute(v, wl.grid, layout="dim", out=vt)
+        mark(1)
+        vsa.select_topk(qc, kc, wl.grid, wl.topk, out=idx, workspace=ws_sel)
+        mark(2)
+        vsa.sparse_attn_fwd(qc, kc, vt, idx, wl.grid, wl.softmax_scale, out=oc, out_f32=of)
+        mark(3)
+        res = oc
+        if wl.linear:
+            vsa.linear_branch(qc, kc, vt, idx, of, wl.grid, out=oc2, workspace=ws_lin)
+            mark(4)
+            res = oc2
+        vsa.cube_unpermute(res, wl.grid, out=o)
+        mark(len(stages))
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # Timed region: exactly K steps, synchronised on both sides.
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t_start.record()
+    for s in range(args.steps):
+        step(evs[s])
+    t_end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_total = t_start.elapsed_time(t_end)
+    ms_step = ms_total / args.steps
+    per_stage = {name: [] for name in stages}
+    for s in range(args.steps):
+        for i, name in enumerate(stages):
+            per_stage[name].append(evs[s][i].elapsed_time(evs[s][i + 1]))
+    stage_ms = {name: float(np.median(vals)) for name, vals in per_stage.items()}
+    fine_ms = float(np.mean(per_stage["fine"]))
+    if not torch.isfinite(o.float()).all():
+        print("non-finite output", file=sys.stderr)
+        sys.exit(1)
+
+    flops = wl.fine_flops
+    value = flops / (ms_step * 1e-3) / 1e12
+    fine_tflops = flops / (fine_ms * 1e-3) / 1e12
+    # Algorithmic bytes of one fine-stage launch: Q, K, V read once, O written once (bf16).
+    alg_bytes = 4 * B * H * d.rows * D * 2
+    traffic = measured_traffic(wl.name)
+    res = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": wl.name,
+            "batch": B, "heads": H, "head_dim": D,
+            "latent_grid": list(wl.grid), "padded_grid": list(wl.padded_grid),
+            "tokens": wl.tokens, "n_cubes": wl.n_cubes, "topk": wl.topk,
+            "sparsity": wl.sparsity, "linear_branch": wl.linear,
+            "computed_blocks": wl.blocks, "fine_flops": flops,
+        },
+        "ms_per_layer": round(ms_step, 4),
+        "stage_ms_median": {kname: round(x, 4) for kname, x in stage_ms.items()},
+        "fine_stage_tflops": round(fine_tflops, 2),
+        "frac_of_bf16_peak_layer": round(value / PEAK_BF16_TFLOPS, 4),
+        "roofline": {
+            "kernel": "attn_fwd",
+            "bound": "mfma",
+            "achieved": round(fine_tflops, 2),
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(fine_tflops / PEAK_BF16_TFLOPS, 4),
+            "traffic": traffic,
+            "algorithmic_bytes": alg_bytes,
+            "avg_launch_ms": round(fine_ms, 4),
+        },
+        "wall_s_timed": round(wall, 3),
+        "device": torch.cuda.get_device_name(0),
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
+    print(json.dumps(res))
+
+
+if __name__ == "__main__":
+    main()

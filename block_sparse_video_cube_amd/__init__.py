@@ -1,0 +1,204 @@
+"""Cube block-sparse video attention (VSA-style) for MI355X / gfx950.
+
+A thin binding over the C ABI in include/vsa_cube.h: every function here
+only checks and marshals arguments (device pointers of torch tensors and the
+current HIP stream) and calls the HIP library; all arithmetic happens in the
+library's kernels.  There is no CPU fallback: if the library is missing the
+calls raise.
+
+Steps of one attention layer (q, k, v: [B, S, heads, D] bf16 on the GPU):
+
+    qc = cube_permute(q, grid)                  # cube-major rows
+    kc = cube_permute(k, grid)
+    vt = cube_permute(v, grid, layout="dim")    # cubes stored transposed
+    idx = select_topk(qc, kc, grid, topk)       # pooled scores -> top-k
+    oc, of, _ = sparse_attn_fwd(qc, kc, vt, idx, grid, scale, want_f32=linear)
+    if linear:
+        oc = linear_branch(qc, kc, vt, idx, of, grid)
+    o = cube_unpermute(oc, grid)                # back to raster tokens
+
+vsa_attention() runs them in that order.
+"""
+
+from __future__ import annotations
+
+import math
+from typing import Optional, Sequence, Tuple
+
+import torch
+
+from . import _lib
+from ._lib import VSA_LAYOUT_DIM_MAJOR, VSA_LAYOUT_TOKEN_MAJOR, VsaDims, VsaError, VsaGeom
+
+__all__ = [
+    "VsaError",
+    "make_geom",
+    "geom_dims",
+    "cube_permute",
+    "cube_unpermute",
+    "select_topk",
+    "sparse_attn_fwd",
+    "linear_branch",
+    "vsa_attention",
+    "workspace_bytes",
+]
+
+
+def make_geom(batch: int, heads: int, head_dim: int, grid: Sequence[int]) -> VsaGeom:
+    t, h, w = (int(x) for x in grid)
+    return VsaGeom(int(batch), int(heads), int(head_dim), t, h, w)
+
+
+def geom_dims(g: VsaGeom) -> VsaDims:
+    d = VsaDims()
+    _lib.check("vsa_geom_dims", _lib.load().vsa_geom_dims(g, d))
+    return d
+
+
+def _stream() -> int:
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _need(t: torch.Tensor, name: str, dtype: torch.dtype, shape: Tuple[int, ...]) -> None:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on the GPU")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+def workspace_bytes(g: VsaGeom, linear: bool = False) -> int:
+    lib = _lib.load()
+    return int(lib.vsa_linear_workspace_bytes(g) if linear else lib.vsa_select_workspace_bytes(g))
+
+
+def cube_permute(x: torch.Tensor, grid: Sequence[int], layout: str = "token",
+                 out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """[B, S, heads, D] -> [B, heads, Np, D] (layout "token") or [B, heads, Nc, D, 64] ("dim")."""
+    B, S, Hh, D = x.shape
+    g = make_geom(B, Hh, D, grid)
+    d = geom_dims(g)
+    _need(x, "x", torch.bfloat16, (B, d.tokens, Hh, D))
+    code = {"token": VSA_LAYOUT_TOKEN_MAJOR, "dim": VSA_LAYOUT_DIM_MAJOR}[layout]
+    shape = (B, Hh, d.rows, D) if code == VSA_LAYOUT_TOKEN_MAJOR else (B, Hh, d.n_cubes, D, 64)
+    if out is None:
+        out = torch.empty(shape, dtype=torch.bfloat16, device=x.device)
+    _need(out, "out", torch.bfloat16, shape)
+    _lib.check("vsa_cube_permute",
+               _lib.load().vsa_cube_permute(g, x.data_ptr(), out.data_ptr(), code, _stream()))
+    return out
+
+
+def cube_unpermute(xc: torch.Tensor, grid: Sequence[int], out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """[B, heads, Np, D] token-major -> [B, S, heads, D]."""
+    B, Hh, Np, D = xc.shape
+    g = make_geom(B, Hh, D, grid)
+    d = geom_dims(g)
+    _need(xc, "xc", torch.bfloat16, (B, Hh, d.rows, D))
+    if out is None:
+        out = torch.empty((B, d.tokens, Hh, D), dtype=torch.bfloat16, device=xc.device)
+    _need(out, "out", torch.bfloat16, (B, d.tokens, Hh, D))
+    _lib.check("vsa_cube_unpermute",
+               _lib.load().vsa_cube_unpermute(g, xc.data_ptr(), out.data_ptr(), _stream()))
+    return out
+
+
+def select_topk(qc: torch.Tensor, kc: torch.Tensor, grid: Sequence[int], topk: int,
+                out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Block index list int32 [B, heads, Nc, topk], ascending per row."""
+    B, Hh, Np, D = qc.shape
+    g = make_geom(B, Hh, D, grid)
+    d = geom_dims(g)
+    _need(qc, "qc", torch.bfloat16, (B, Hh, d.rows, D))
+    _need(kc, "kc", torch.bfloat16, (B, Hh, d.rows, D))
+    if out is None:
+        out = torch.empty((B, Hh, d.n_cubes, int(topk)), dtype=torch.int32, device=qc.device)
+    _need(out, "idx", torch.int32, (B, Hh, d.n_cubes, int(topk)))
+    nbytes = workspace_bytes(g)
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=qc.device)
+    _lib.check("vsa_select_topk", _lib.load().vsa_select_topk(
+        g, qc.data_ptr(), kc.data_ptr(), int(topk), out.data_ptr(), workspace.data_ptr(),
+        workspace.numel() * workspace.element_size(), _stream()))
+    return out
+
+
+def sparse_attn_fwd(qc: torch.Tensor, kc: torch.Tensor, vt: torch.Tensor, idx: torch.Tensor,
+                    grid: Sequence[int], scale: Optional[float] = None, want_f32: bool = False,
+                    want_lse: bool = False, out: Optional[torch.Tensor] = None,
+                    out_f32: Optional[torch.Tensor] = None):
+    """Fine stage.  Returns (oc bf16, oc_f32 or None, lse or None).
+
+    out / out_f32: optional preallocated outputs (out_f32 implies want_f32).
+    """
+    B, Hh, Np, D = qc.shape
+    g = make_geom(B, Hh, D, grid)
+    d = geom_dims(g)
+    topk = idx.shape[-1]
+    _need(qc, "qc", torch.bfloat16, (B, Hh, d.rows, D))
+    _need(kc, "kc", torch.bfloat16, (B, Hh, d.rows, D))
+    _need(vt, "vt", torch.bfloat16, (B, Hh, d.n_cubes, D, 64))
+    _need(idx, "idx", torch.int32, (B, Hh, d.n_cubes, topk))
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty((B, Hh, d.rows, D), dtype=torch.bfloat16, device=qc.device)
+    _need(out, "oc", torch.bfloat16, (B, Hh, d.rows, D))
+    of = out_f32
+    if of is None and want_f32:
+        of = torch.empty((B, Hh, d.rows, D), dtype=torch.float32, device=qc.device)
+    if of is not None:
+        _need(of, "oc_f32", torch.float32, (B, Hh, d.rows, D))
+    lse = torch.empty((B, Hh, d.rows), dtype=torch.float32, device=qc.device) if want_lse else None
+    _lib.check("vsa_sparse_attn_fwd", _lib.load().vsa_sparse_attn_fwd(
+        g, qc.data_ptr(), kc.data_ptr(), vt.data_ptr(), idx.data_ptr(), int(topk), float(scale),
+        out.data_ptr(), of.data_ptr() if of is not None else None,
+        lse.data_ptr() if lse is not None else None, _stream()))
+    return out, of, lse
+
+
+def linear_branch(qc: torch.Tensor, kc: torch.Tensor, vt: torch.Tensor, idx: torch.Tensor,
+                  o_sparse: torch.Tensor, grid: Sequence[int], out: Optional[torch.Tensor] = None,
+                  workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """bf16(o_sparse + O_lin), token-major."""
+    B, Hh, Np, D = qc.shape
+    g = make_geom(B, Hh, D, grid)
+    d = geom_dims(g)
+    topk = idx.shape[-1]
+    _need(qc, "qc", torch.bfloat16, (B, Hh, d.rows, D))
+    _need(kc, "kc", torch.bfloat16, (B, Hh, d.rows, D))
+    _need(vt, "vt", torch.bfloat16, (B, Hh, d.n_cubes, D, 64))
+    _need(idx, "idx", torch.int32, (B, Hh, d.n_cubes, topk))
+    _need(o_sparse, "o_sparse", torch.float32, (B, Hh, d.rows, D))
+    if out is None:
+        out = torch.empty((B, Hh, d.rows, D), dtype=torch.bfloat16, device=qc.device)
+    _need(out, "oc", torch.bfloat16, (B, Hh, d.rows, D))
+    nbytes = workspace_bytes(g, linear=True)
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=qc.device)
+    _lib.check("vsa_linear_branch", _lib.load().vsa_linear_branch(
+        g, qc.data_ptr(), kc.data_ptr(), vt.data_ptr(), idx.data_ptr(), int(topk), o_sparse.data_ptr(),
+        out.data_ptr(), workspace.data_ptr(), workspace.numel() * workspace.element_size(), _stream()))
+    return out
+
+
+def vsa_attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, grid: Sequence[int], topk: int,
+                  scale: Optional[float] = None, linear: bool = False, idx: Optional[torch.Tensor] = None):
+    """One attention layer: [B, S, heads, D] bf16 -> (o [B, S, heads, D] bf16, idx).
+
+    idx: optional block list to use instead of the coarse-stage selection.
+    """
+    qc = cube_permute(q, grid)
+    kc = cube_permute(k, grid)
+    vt = cube_permute(v, grid, layout="dim")
+    if idx is None:
+        idx = select_topk(qc, kc, grid, topk)
+    oc, of, _ = sparse_attn_fwd(qc, kc, vt, idx, grid, scale, want_f32=linear)
+    if linear:
+        oc = linear_branch(qc, kc, vt, idx, of, grid)
+    return cube_unpermute(oc, grid), idx

@@ -1,0 +1,112 @@
+"""ctypes declarations of the C ABI in include/vsa_cube.h."""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+LIB_NAME = "libvsa_cube.so"
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), LIB_NAME)
+
+VSA_OK = 0
+VSA_ERR_NULL = 1
+VSA_ERR_GEOMETRY = 2
+VSA_ERR_HEAD_DIM = 3
+VSA_ERR_TOPK = 4
+VSA_ERR_ALIGN = 5
+VSA_ERR_WORKSPACE = 6
+VSA_ERR_LAYOUT = 7
+VSA_ERR_SCALE = 8
+VSA_ERR_LAUNCH = 9
+
+VSA_LAYOUT_TOKEN_MAJOR = 0
+VSA_LAYOUT_DIM_MAJOR = 1
+VSA_MAX_CUBES = 4096
+
+ENTRY_POINTS = (
+    "vsa_abi_version",
+    "vsa_status_string",
+    "vsa_geom_dims",
+    "vsa_select_workspace_bytes",
+    "vsa_linear_workspace_bytes",
+    "vsa_cube_permute",
+    "vsa_cube_unpermute",
+    "vsa_select_topk",
+    "vsa_sparse_attn_fwd",
+    "vsa_linear_branch",
+)
+
+
+class VsaGeom(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int32),
+        ("heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("grid_t", ctypes.c_int32),
+        ("grid_h", ctypes.c_int32),
+        ("grid_w", ctypes.c_int32),
+    ]
+
+
+class VsaDims(ctypes.Structure):
+    _fields_ = [
+        ("pad_t", ctypes.c_int32),
+        ("pad_h", ctypes.c_int32),
+        ("pad_w", ctypes.c_int32),
+        ("cubes_t", ctypes.c_int32),
+        ("cubes_h", ctypes.c_int32),
+        ("cubes_w", ctypes.c_int32),
+        ("n_cubes", ctypes.c_int32),
+        ("reserved", ctypes.c_int32),
+        ("tokens", ctypes.c_int64),
+        ("rows", ctypes.c_int64),
+    ]
+
+
+_lib = None
+
+
+class VsaError(RuntimeError):
+    def __init__(self, fn: str, status: int, text: str):
+        super().__init__(f"{fn} failed with status {status}: {text}")
+        self.status = status
+
+
+def load() -> ctypes.CDLL:
+    """Load the built library; raise if it is missing (there is no fallback)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(
+            f"{LIB_PATH} is missing: build the HIP library first "
+            "(python -c 'import __graft_entry__ as g; g.build()')")
+    lib = ctypes.CDLL(LIB_PATH)
+    P = ctypes.c_void_p
+    G = ctypes.POINTER(VsaGeom)
+    i32 = ctypes.c_int32
+    sz = ctypes.c_size_t
+    sig = {
+        "vsa_abi_version": (i32, []),
+        "vsa_status_string": (ctypes.c_char_p, [i32]),
+        "vsa_geom_dims": (i32, [G, ctypes.POINTER(VsaDims)]),
+        "vsa_select_workspace_bytes": (sz, [G]),
+        "vsa_linear_workspace_bytes": (sz, [G]),
+        "vsa_cube_permute": (i32, [G, P, P, i32, P]),
+        "vsa_cube_unpermute": (i32, [G, P, P, P]),
+        "vsa_select_topk": (i32, [G, P, P, i32, P, P, sz, P]),
+        "vsa_sparse_attn_fwd": (i32, [G, P, P, P, P, i32, ctypes.c_float, P, P, P, P]),
+        "vsa_linear_branch": (i32, [G, P, P, P, P, i32, P, P, P, sz, P]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+def check(fn: str, status: int) -> None:
+    if status != VSA_OK:
+        text = load().vsa_status_string(status).decode()
+        raise VsaError(fn, status, text)

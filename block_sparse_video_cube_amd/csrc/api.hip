@@ -1,0 +1,172 @@
+// C ABI entry points: host-side validation, then asynchronous launches.
+#include <math.h>
+#include <string.h>
+
+#include "common.h"
+
+namespace vsa {
+
+KGeom make_kgeom(const vsa_geom& g, const vsa_dims& d) {
+  KGeom k;
+  k.B = g.batch;
+  k.H = g.heads;
+  k.D = g.head_dim;
+  k.T = g.grid_t;
+  k.Hg = g.grid_h;
+  k.W = g.grid_w;
+  k.ct = d.cubes_t;
+  k.ch = d.cubes_h;
+  k.cw = d.cubes_w;
+  k.nc = d.n_cubes;
+  k.S = d.tokens;
+  k.Np = d.rows;
+  return k;
+}
+
+}  // namespace vsa
+
+namespace {
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int32_t launch_status(hipError_t e) { return e == hipSuccess ? VSA_OK : VSA_ERR_LAUNCH; }
+
+// Common prologue: geometry plus the KGeom the kernels use.
+int32_t prepare(const vsa_geom* g, vsa_dims* d, vsa::KGeom* k) {
+  const int32_t st = vsa_geom_dims(g, d);
+  if (st != VSA_OK) return st;
+  *k = vsa::make_kgeom(*g, *d);
+  return VSA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t vsa_abi_version(void) { return VSA_ABI_VERSION; }
+
+const char* vsa_status_string(int32_t status) {
+  switch (status) {
+    case VSA_OK: return "ok";
+    case VSA_ERR_NULL: return "a required pointer is NULL";
+    case VSA_ERR_GEOMETRY: return "invalid geometry (batch, heads or grid out of range)";
+    case VSA_ERR_HEAD_DIM: return "head_dim must be 64 or 128";
+    case VSA_ERR_TOPK: return "topk must lie in [1, n_cubes]";
+    case VSA_ERR_ALIGN: return "pointer not 16-byte aligned";
+    case VSA_ERR_WORKSPACE: return "workspace too small";
+    case VSA_ERR_LAYOUT: return "unknown layout code";
+    case VSA_ERR_SCALE: return "softmax scale must be finite and positive";
+    case VSA_ERR_LAUNCH: return "kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+int32_t vsa_geom_dims(const vsa_geom* g, vsa_dims* out) {
+  if (!g || !out) return VSA_ERR_NULL;
+  if (g->batch < 1 || g->heads < 1 || g->grid_t < 1 || g->grid_h < 1 || g->grid_w < 1)
+    return VSA_ERR_GEOMETRY;
+  if (g->batch > 65535 || g->heads > 65535 || (int64_t)g->batch * g->heads > 65535) return VSA_ERR_GEOMETRY;
+  if (g->head_dim != 64 && g->head_dim != 128) return VSA_ERR_HEAD_DIM;
+  vsa_dims d;
+  memset(&d, 0, sizeof(d));
+  d.pad_t = (int32_t)(((int64_t)g->grid_t + 3) / 4 * 4);
+  d.pad_h = (int32_t)(((int64_t)g->grid_h + 3) / 4 * 4);
+  d.pad_w = (int32_t)(((int64_t)g->grid_w + 3) / 4 * 4);
+  d.cubes_t = d.pad_t / 4;
+  d.cubes_h = d.pad_h / 4;
+  d.cubes_w = d.pad_w / 4;
+  const int64_t nc = (int64_t)d.cubes_t * d.cubes_h * d.cubes_w;
+  if (nc > (int64_t)1 << 24) return VSA_ERR_GEOMETRY;
+  d.n_cubes = (int32_t)nc;
+  d.tokens = (int64_t)g->grid_t * g->grid_h * g->grid_w;
+  d.rows = 64 * nc;
+  const int64_t elems = (int64_t)g->batch * g->heads * d.rows * g->head_dim;
+  if (elems >= ((int64_t)1 << 40)) return VSA_ERR_GEOMETRY;
+  *out = d;
+  return VSA_OK;
+}
+
+size_t vsa_select_workspace_bytes(const vsa_geom* g) {
+  vsa_dims d;
+  vsa::KGeom k;
+  if (prepare(g, &d, &k) != VSA_OK) return 0;
+  return vsa::select_workspace_bytes(k);
+}
+
+size_t vsa_linear_workspace_bytes(const vsa_geom* g) {
+  vsa_dims d;
+  vsa::KGeom k;
+  if (prepare(g, &d, &k) != VSA_OK) return 0;
+  return vsa::linear_workspace_bytes(k);
+}
+
+int32_t vsa_cube_permute(const vsa_geom* g, const uint16_t* x, uint16_t* xc, int32_t layout, void* stream) {
+  vsa_dims d;
+  vsa::KGeom k;
+  int32_t st = prepare(g, &d, &k);
+  if (st != VSA_OK) return st;
+  if (!x || !xc) return VSA_ERR_NULL;
+  if (!aligned16(x) || !aligned16(xc)) return VSA_ERR_ALIGN;
+  if (layout != VSA_LAYOUT_TOKEN_MAJOR && layout != VSA_LAYOUT_DIM_MAJOR) return VSA_ERR_LAYOUT;
+  return launch_status(vsa::launch_permute(k, x, xc, layout, static_cast<hipStream_t>(stream)));
+}
+
+int32_t vsa_cube_unpermute(const vsa_geom* g, const uint16_t* xc, uint16_t* x, void* stream) {
+  vsa_dims d;
+  vsa::KGeom k;
+  int32_t st = prepare(g, &d, &k);
+  if (st != VSA_OK) return st;
+  if (!x || !xc) return VSA_ERR_NULL;
+  if (!aligned16(x) || !aligned16(xc)) return VSA_ERR_ALIGN;
+  return launch_status(vsa::launch_unpermute(k, xc, x, static_cast<hipStream_t>(stream)));
+}
+
+int32_t vsa_select_topk(const vsa_geom* g, const uint16_t* qc, const uint16_t* kc, int32_t topk, int32_t* idx,
+                        void* ws, size_t ws_bytes, void* stream) {
+  vsa_dims d;
+  vsa::KGeom k;
+  int32_t st = prepare(g, &d, &k);
+  if (st != VSA_OK) return st;
+  if (d.n_cubes > VSA_MAX_CUBES) return VSA_ERR_GEOMETRY;
+  if (!qc || !kc || !idx || !ws) return VSA_ERR_NULL;
+  if (!aligned16(qc) || !aligned16(kc) || !aligned16(idx) || !aligned16(ws)) return VSA_ERR_ALIGN;
+  if (topk < 1 || topk > d.n_cubes) return VSA_ERR_TOPK;
+  if (ws_bytes < vsa::select_workspace_bytes(k)) return VSA_ERR_WORKSPACE;
+  return launch_status(vsa::launch_select(k, qc, kc, topk, idx, ws, static_cast<hipStream_t>(stream)));
+}
+
+int32_t vsa_sparse_attn_fwd(const vsa_geom* g, const uint16_t* qc, const uint16_t* kc, const uint16_t* vt,
+                            const int32_t* idx, int32_t topk, float softmax_scale, uint16_t* oc, float* oc_f32,
+                            float* lse, void* stream) {
+  vsa_dims d;
+  vsa::KGeom k;
+  int32_t st = prepare(g, &d, &k);
+  if (st != VSA_OK) return st;
+  if (!qc || !kc || !vt || !idx || !oc) return VSA_ERR_NULL;
+  if (!aligned16(qc) || !aligned16(kc) || !aligned16(vt) || !aligned16(idx) || !aligned16(oc) ||
+      (oc_f32 && !aligned16(oc_f32)) || (lse && !aligned16(lse)))
+    return VSA_ERR_ALIGN;
+  if (topk < 1 || topk > d.n_cubes) return VSA_ERR_TOPK;
+  if (!(softmax_scale > 0.f) || !isfinite(softmax_scale)) return VSA_ERR_SCALE;
+  return launch_status(vsa::launch_attn_fwd(k, qc, kc, vt, idx, topk, softmax_scale, oc, oc_f32, lse,
+                                            static_cast<hipStream_t>(stream)));
+}
+
+int32_t vsa_linear_branch(const vsa_geom* g, const uint16_t* qc, const uint16_t* kc, const uint16_t* vt,
+                          const int32_t* idx, int32_t topk, const float* o_sparse, uint16_t* oc, void* ws,
+                          size_t ws_bytes, void* stream) {
+  vsa_dims d;
+  vsa::KGeom k;
+  int32_t st = prepare(g, &d, &k);
+  if (st != VSA_OK) return st;
+  if (!qc || !kc || !vt || !idx || !o_sparse || !oc || !ws) return VSA_ERR_NULL;
+  if (!aligned16(qc) || !aligned16(kc) || !aligned16(vt) || !aligned16(idx) || !aligned16(o_sparse) ||
+      !aligned16(oc) || !aligned16(ws))
+    return VSA_ERR_ALIGN;
+  if (topk < 1 || topk > d.n_cubes) return VSA_ERR_TOPK;
+  if (ws_bytes < vsa::linear_workspace_bytes(k)) return VSA_ERR_WORKSPACE;
+  return launch_status(vsa::launch_linear(k, qc, kc, vt, idx, topk, o_sparse, oc, ws,
+                                          static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,81 @@
+// Shared definitions of the gfx950 kernels (device side) and their host launchers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "vsa_cube.h"
+
+namespace vsa {
+
+// Geometry handed to every kernel by value.
+struct KGeom {
+  int B, H, D;       // batch, heads, head_dim
+  int T, Hg, W;      // valid latent grid
+  int ct, ch, cw;    // cubes per axis
+  int nc;            // cubes
+  long long S;       // tokens
+  long long Np;      // cube-major rows = 64 * nc
+};
+
+KGeom make_kgeom(const vsa_geom& g, const vsa_dims& d);
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// Cube coordinates of cube c.
+__device__ __forceinline__ void cube_coords(const KGeom& g, int c, int& ct, int& cy, int& cx) {
+  cx = c % g.cw;
+  const int r = c / g.cw;
+  cy = r % g.ch;
+  ct = r / g.ch;
+}
+
+// Is local token l of the cube at (ct, cy, cx) inside the valid grid?
+__device__ __forceinline__ bool local_valid(const KGeom& g, int ct, int cy, int cx, int l) {
+  return (4 * ct + (l >> 4)) < g.T && (4 * cy + ((l >> 2) & 3)) < g.Hg && (4 * cx + (l & 3)) < g.W;
+}
+
+// Are all 64 tokens of the cube valid?
+__device__ __forceinline__ bool cube_full(const KGeom& g, int ct, int cy, int cx) {
+  return 4 * ct + 3 < g.T && 4 * cy + 3 < g.Hg && 4 * cx + 3 < g.W;
+}
+
+// Number of valid tokens of a cube.
+__device__ __forceinline__ int cube_count(const KGeom& g, int ct, int cy, int cx) {
+  const int nt = min(4, g.T - 4 * ct), ny = min(4, g.Hg - 4 * cy), nx = min(4, g.W - 4 * cx);
+  return nt * ny * nx;
+}
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+  return __uint_as_float(((uint32_t)b) << 16);
+}
+
+// fp32 -> bf16 bits, round to nearest even (inputs here are finite).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  const uint32_t u = __float_as_uint(f);
+  return (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
+}
+
+}  // namespace vsa
+
+// Host launchers (each returns hipSuccess or the launch error).
+namespace vsa {
+hipError_t launch_permute(const KGeom& g, const uint16_t* x, uint16_t* xc, int layout, hipStream_t s);
+hipError_t launch_unpermute(const KGeom& g, const uint16_t* xc, uint16_t* x, hipStream_t s);
+hipError_t launch_select(const KGeom& g, const uint16_t* qc, const uint16_t* kc, int topk, int32_t* idx,
+                         void* ws, hipStream_t s);
+size_t select_workspace_bytes(const KGeom& g);
+hipError_t launch_attn_fwd(const KGeom& g, const uint16_t* qc, const uint16_t* kc, const uint16_t* vt,
+                           const int32_t* idx, int topk, float scale, uint16_t* oc, float* oc_f32, float* lse,
+                           hipStream_t s);
+hipError_t launch_linear(const KGeom& g, const uint16_t* qc, const uint16_t* kc, const uint16_t* vt,
+                         const int32_t* idx, int topk, const float* o_sparse, uint16_t* oc, void* ws,
+                         hipStream_t s);
+size_t linear_workspace_bytes(const KGeom& g);
+}  // namespace vsa

@@ -1,0 +1,122 @@
+// Cube permutation kernels: raster tokens <-> cube-major rows.
+//
+// Grouping the latent grid into whole 4x4x4 cubes is what lets every attention
+// block be kept or skipped as a unit, with no partially masked ("mixed")
+// blocks (FastVideo sparse-distillation article, figure comparing attention
+// patterns in section "2. 视频稀疏注意力VSA"; FastVideo attention-backend
+// article, figure on NATTEN / Tiled NATTEN / STA).
+//
+// These kernels only move bits (HBM bound).  One workgroup moves one
+// (batch, head, cube) tile of 64 rows x D: reads are 16-byte chunks of token
+// rows, writes are one contiguous tile.
+#include "common.h"
+
+namespace vsa {
+
+namespace {
+
+constexpr int kThreads = 256;
+
+// [B, S, H, D] -> [B, H, Np, D]; padded rows become zero.
+template <int D>
+__global__ void __launch_bounds__(kThreads) permute_token_major(const uint16_t* __restrict__ x,
+                                                                uint16_t* __restrict__ xc, KGeom g) {
+  constexpr int CH = D / 8;  // 16-byte chunks per row
+  const int c = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  int ct, cy, cx;
+  cube_coords(g, c, ct, cy, cx);
+  uint4* out = reinterpret_cast<uint4*>(xc + (((long long)b * g.H + h) * g.Np + 64LL * c) * D);
+  for (int f = threadIdx.x; f < 64 * CH; f += kThreads) {
+    const int l = f / CH, ch = f % CH;
+    const int t = 4 * ct + (l >> 4), y = 4 * cy + ((l >> 2) & 3), xx = 4 * cx + (l & 3);
+    uint4 val = make_uint4(0, 0, 0, 0);
+    if (t < g.T && y < g.Hg && xx < g.W) {
+      const long long s = ((long long)t * g.Hg + y) * g.W + xx;
+      val = reinterpret_cast<const uint4*>(x + (((long long)b * g.S + s) * g.H + h) * D)[ch];
+    }
+    out[f] = val;
+  }
+}
+
+// [B, S, H, D] -> [B, H, Nc, D, 64]: each cube stored transposed (d-major).
+template <int D>
+__global__ void __launch_bounds__(kThreads) permute_dim_major(const uint16_t* __restrict__ x,
+                                                              uint16_t* __restrict__ xc, KGeom g) {
+  constexpr int CH = D / 8;
+  constexpr int LD = D + 8;  // padded LDS row (halfwords), keeps 16-byte alignment
+  __shared__ __attribute__((aligned(16))) uint16_t tile[64 * LD];
+  const int c = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  int ct, cy, cx;
+  cube_coords(g, c, ct, cy, cx);
+  for (int f = threadIdx.x; f < 64 * CH; f += kThreads) {
+    const int l = f / CH, ch = f % CH;
+    const int t = 4 * ct + (l >> 4), y = 4 * cy + ((l >> 2) & 3), xx = 4 * cx + (l & 3);
+    uint4 val = make_uint4(0, 0, 0, 0);
+    if (t < g.T && y < g.Hg && xx < g.W) {
+      const long long s = ((long long)t * g.Hg + y) * g.W + xx;
+      val = reinterpret_cast<const uint4*>(x + (((long long)b * g.S + s) * g.H + h) * D)[ch];
+    }
+    *reinterpret_cast<uint4*>(tile + l * LD + ch * 8) = val;
+  }
+  __syncthreads();
+  uint4* out = reinterpret_cast<uint4*>(xc + (((long long)b * g.H + h) * g.Np + 64LL * c) * D);
+  for (int f = threadIdx.x; f < D * 8; f += kThreads) {
+    const int d = f >> 3, lg = f & 7;
+    uint32_t w[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const uint32_t lo = tile[(8 * lg + 2 * e) * LD + d];
+      const uint32_t hi = tile[(8 * lg + 2 * e + 1) * LD + d];
+      w[e] = lo | (hi << 16);
+    }
+    out[f] = make_uint4(w[0], w[1], w[2], w[3]);
+  }
+}
+
+// [B, H, Np, D] -> [B, S, H, D]; padded rows are dropped.
+template <int D>
+__global__ void __launch_bounds__(kThreads) unpermute_token_major(const uint16_t* __restrict__ xc,
+                                                                  uint16_t* __restrict__ x, KGeom g) {
+  constexpr int CH = D / 8;
+  const int c = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  int ct, cy, cx;
+  cube_coords(g, c, ct, cy, cx);
+  const uint4* in = reinterpret_cast<const uint4*>(xc + (((long long)b * g.H + h) * g.Np + 64LL * c) * D);
+  for (int f = threadIdx.x; f < 64 * CH; f += kThreads) {
+    const int l = f / CH, ch = f % CH;
+    const int t = 4 * ct + (l >> 4), y = 4 * cy + ((l >> 2) & 3), xx = 4 * cx + (l & 3);
+    if (t < g.T && y < g.Hg && xx < g.W) {
+      const long long s = ((long long)t * g.Hg + y) * g.W + xx;
+      reinterpret_cast<uint4*>(x + (((long long)b * g.S + s) * g.H + h) * D)[ch] = in[f];
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_permute(const KGeom& g, const uint16_t* x, uint16_t* xc, int layout, hipStream_t s) {
+  const dim3 grid(g.nc, g.H, g.B);
+  if (layout == VSA_LAYOUT_TOKEN_MAJOR) {
+    if (g.D == 64)
+      hipLaunchKernelGGL(permute_token_major<64>, grid, dim3(kThreads), 0, s, x, xc, g);
+    else
+      hipLaunchKernelGGL(permute_token_major<128>, grid, dim3(kThreads), 0, s, x, xc, g);
+  } else {
+    if (g.D == 64)
+      hipLaunchKernelGGL(permute_dim_major<64>, grid, dim3(kThreads), 0, s, x, xc, g);
+    else
+      hipLaunchKernelGGL(permute_dim_major<128>, grid, dim3(kThreads), 0, s, x, xc, g);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_unpermute(const KGeom& g, const uint16_t* xc, uint16_t* x, hipStream_t s) {
+  const dim3 grid(g.nc, g.H, g.B);
+  if (g.D == 64)
+    hipLaunchKernelGGL(unpermute_token_major<64>, grid, dim3(kThreads), 0, s, xc, x, g);
+  else
+    hipLaunchKernelGGL(unpermute_token_major<128>, grid, dim3(kThreads), 0, s, xc, x, g);
+  return hipGetLastError();
+}
+
+}  // namespace vsa

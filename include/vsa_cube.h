@@ -1,0 +1,168 @@
+/*
+ * vsa_cube.h - C ABI of the cube block-sparse video attention library (gfx950).
+ *
+ * The method: video sparse attention (VSA) keeps only the important attention
+ * blocks, chosen dynamically, computing about 10-20 % of the attention
+ * weights at sparsity 0.8-0.9 (FastVideo sparse-distillation article,
+ * section "核心技术解析 / 2. 视频稀疏注意力VSA"); grouping tokens so that every
+ * block is either fully kept or fully skipped avoids "mixed" blocks (same
+ * article, figure comparing attention patterns; FastVideo attention-backend
+ * article, figure on NATTEN / Tiled NATTEN / STA).  An optional linear
+ * attention branch over the skipped blocks keeps global context at very high
+ * sparsity (SparkDiffusion article, paragraph 3, RoLA; TurboDiffusion
+ * article, section "稀疏、蒸馏与全链路量化", SLA).
+ *
+ * Conventions this library fixes (the pages give no formulas):
+ *  - tokens of a latent grid T x H x W (raster order, t slowest, x fastest)
+ *    are grouped into 4 x 4 x 4 cubes of 64 tokens; every grid axis is padded
+ *    at its high end to a multiple of 4; padded tokens are zero and invalid;
+ *  - cube c = ((t/4) * Hp/4 + y/4) * Wp/4 + x/4, local token
+ *    l = ((t%4) * 4 + y%4) * 4 + x%4, cube-major row 64 c + l;
+ *  - coarse stage: mean of each cube over its valid tokens, block score
+ *    s_ij = qbar_i . kbar_j (unscaled), the top-k key cubes of each query
+ *    cube (equal scores: lower cube index first), listed ascending;
+ *  - fine stage: softmax(scale * Q_i K^T) V over the valid keys of the
+ *    selected cubes (one 64 x 64 block per selected cube);
+ *  - linear branch: phi(x) = elu(x) + 1, over the valid keys of the
+ *    unselected cubes U: O_lin = phi(Q) (sum_U phi(K)^T V) / (phi(Q) . sum_U phi(K)),
+ *    0 when U is empty; the result is O_sparse + O_lin.
+ *
+ * Memory and streams.  Every data pointer is a device pointer owned by the
+ * caller.  The library never allocates or frees device memory, never
+ * synchronises and keeps no mutable global state; calls are thread-safe.
+ * Every call validates its arguments on the host first and launches nothing
+ * on error; on success it enqueues its kernels on `stream` (a hipStream_t,
+ * NULL = the default stream) and returns at once.  Results are valid when the
+ * stream reaches that point.  bf16 values are passed as uint16_t bit
+ * patterns.  All pointers must be 16-byte aligned.
+ *
+ * Errors are returned as vsa_status codes; NaN or Inf inputs give unspecified
+ * (but memory-safe) outputs; the contents of index lists are trusted.
+ */
+#ifndef VSA_CUBE_H
+#define VSA_CUBE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define VSA_ABI_VERSION 1
+
+typedef enum vsa_status {
+  VSA_OK = 0,
+  VSA_ERR_NULL = 1,      /* a required pointer is NULL                        */
+  VSA_ERR_GEOMETRY = 2,  /* non-positive or too large batch/heads/grid        */
+  VSA_ERR_HEAD_DIM = 3,  /* head_dim is not 64 or 128                         */
+  VSA_ERR_TOPK = 4,      /* topk outside [1, n_cubes]                         */
+  VSA_ERR_ALIGN = 5,     /* a pointer is not 16-byte aligned                  */
+  VSA_ERR_WORKSPACE = 6, /* workspace smaller than the *_workspace_bytes size */
+  VSA_ERR_LAYOUT = 7,    /* unknown layout code                               */
+  VSA_ERR_SCALE = 8,     /* softmax scale not finite and positive             */
+  VSA_ERR_LAUNCH = 9     /* a kernel launch failed (HIP error)                */
+} vsa_status;
+
+/* Shape of one attention layer. */
+typedef struct vsa_geom {
+  int32_t batch;    /* B >= 1                                  */
+  int32_t heads;    /* attention heads >= 1                    */
+  int32_t head_dim; /* D: 64 or 128                            */
+  int32_t grid_t;   /* valid latent grid (T, H, W), each >= 1  */
+  int32_t grid_h;
+  int32_t grid_w;
+} vsa_geom;
+
+/* Sizes derived from a vsa_geom by vsa_geom_dims. */
+typedef struct vsa_dims {
+  int32_t pad_t, pad_h, pad_w;       /* grid rounded up to multiples of 4 */
+  int32_t cubes_t, cubes_h, cubes_w; /* cubes per axis                    */
+  int32_t n_cubes;                   /* Nc                                */
+  int32_t reserved;
+  int64_t tokens;                    /* S = T * H * W                     */
+  int64_t rows;                      /* Np = 64 * Nc                      */
+} vsa_dims;
+
+/* Layout codes of a cube-major tensor.
+ * TOKEN_MAJOR: [B, heads, Np, D], element (b, h, 64 c + l, d).
+ * DIM_MAJOR:   [B, heads, Nc, D, 64], element (b, h, c, d, l): each cube
+ *              stored transposed.  This is the layout the value tensor must
+ *              have for vsa_sparse_attn_fwd and vsa_linear_branch. */
+enum { VSA_LAYOUT_TOKEN_MAJOR = 0, VSA_LAYOUT_DIM_MAJOR = 1 };
+
+/* Limits: n_cubes <= VSA_MAX_CUBES, B * heads * Np * D < 2^40. */
+#define VSA_MAX_CUBES 4096
+
+/* ---------------------------------------------------------------- host only */
+
+/* VSA_ABI_VERSION of the built library. */
+int32_t vsa_abi_version(void);
+
+/* Static English text for a status code (never NULL). */
+const char* vsa_status_string(int32_t status);
+
+/* Validates g and fills *out.  Returns VSA_ERR_NULL, VSA_ERR_GEOMETRY,
+ * VSA_ERR_HEAD_DIM or VSA_OK.  Touches no device. */
+int32_t vsa_geom_dims(const vsa_geom* g, vsa_dims* out);
+
+/* Device workspace bytes needed by vsa_select_topk / vsa_linear_branch for g
+ * (0 if g is invalid).  Touches no device. */
+size_t vsa_select_workspace_bytes(const vsa_geom* g);
+size_t vsa_linear_workspace_bytes(const vsa_geom* g);
+
+/* -------------------------------------------------------------- entry points */
+
+/* Cube permutation (gather).  x: [B, S, heads, D] bf16 raster tokens.
+ * xc: output, layout per `layout` (TOKEN_MAJOR or DIM_MAJOR) with Np rows per
+ * (b, h); padded rows are written as zero.  x and xc must not overlap. */
+int32_t vsa_cube_permute(const vsa_geom* g, const uint16_t* x, uint16_t* xc,
+                         int32_t layout, void* stream);
+
+/* Inverse permutation (scatter).  xc: [B, heads, Np, D] TOKEN_MAJOR bf16;
+ * x: output [B, S, heads, D]; padded rows of xc are dropped. */
+int32_t vsa_cube_unpermute(const vsa_geom* g, const uint16_t* xc, uint16_t* x,
+                           void* stream);
+
+/* Coarse stage: cube means of qc and kc (fp32, over valid rows), block scores
+ * s_ij = qbar_i . kbar_j (fp32) and, per query cube, the topk best key cubes
+ * (equal scores: lower index first; -0 and +0 equal), written ascending.
+ * qc, kc: [B, heads, Np, D] TOKEN_MAJOR bf16.
+ * idx: output int32 [B, heads, Nc, topk].
+ * ws: device workspace of at least vsa_select_workspace_bytes(g) bytes. */
+int32_t vsa_select_topk(const vsa_geom* g, const uint16_t* qc, const uint16_t* kc,
+                        int32_t topk, int32_t* idx, void* ws, size_t ws_bytes,
+                        void* stream);
+
+/* Fine stage: for every (b, h, query cube i), softmax attention of its 64
+ * query rows over the valid keys of the topk key cubes idx[b, h, i, :]
+ * (flash-style online softmax, fp32 accumulation, bf16 matrix cores).
+ * qc, kc: TOKEN_MAJOR bf16; vt: DIM_MAJOR bf16; idx: int32 [B, heads, Nc, topk]
+ * with entries in [0, Nc) (duplicates are computed twice).
+ * softmax_scale: finite, > 0 (usually 1/sqrt(D)).
+ * oc: output bf16 [B, heads, Np, D] TOKEN_MAJOR (padded query rows hold
+ * finite values that unpermute drops).
+ * oc_f32: optional fp32 copy of the output before rounding (NULL to skip).
+ * lse: optional fp32 [B, heads, Np], max + log(sum) of the scaled logits in
+ * natural-log units (NULL to skip). */
+int32_t vsa_sparse_attn_fwd(const vsa_geom* g, const uint16_t* qc, const uint16_t* kc,
+                            const uint16_t* vt, const int32_t* idx, int32_t topk,
+                            float softmax_scale, uint16_t* oc, float* oc_f32,
+                            float* lse, void* stream);
+
+/* Linear branch and combine: oc = bf16(o_sparse + O_lin), O_lin over the valid
+ * keys of the cubes NOT in idx[b, h, i, :] (0 when none are left).
+ * qc, kc: TOKEN_MAJOR bf16; vt: DIM_MAJOR bf16; idx as for the fine stage
+ * (entries distinct); o_sparse: fp32 [B, heads, Np, D] (the oc_f32 output of
+ * vsa_sparse_attn_fwd); oc: output bf16 TOKEN_MAJOR.  o_sparse and oc may not
+ * overlap.  ws: at least vsa_linear_workspace_bytes(g) bytes. */
+int32_t vsa_linear_branch(const vsa_geom* g, const uint16_t* qc, const uint16_t* kc,
+                          const uint16_t* vt, const int32_t* idx, int32_t topk,
+                          const float* o_sparse, uint16_t* oc, void* ws,
+                          size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* VSA_CUBE_H */

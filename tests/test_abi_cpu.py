@@ -1,0 +1,126 @@
+"""C ABI checks that need no GPU: the library loads, exports every function the
+header declares, and host-side validation returns the documented status before
+anything is launched (only invalid arguments are passed, so no kernel runs)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import workloads
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "vsa_cube.h")
+
+
+def header_functions():
+    text = open(HEADER, encoding="utf-8").read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(vsa_[a-z_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from block_sparse_video_cube_amd import _lib
+
+    if not os.path.exists(_lib.LIB_PATH):
+        pytest.fail("libvsa_cube.so is not built (run __graft_entry__.build())")
+    return _lib.load()
+
+
+def test_header_and_binding_agree():
+    from block_sparse_video_cube_amd import _lib
+
+    assert header_functions() == sorted(_lib.ENTRY_POINTS)
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for name in header_functions():
+        assert hasattr(lib, name), name
+
+
+def test_abi_version_and_status_text(lib):
+    assert lib.vsa_abi_version() == 1
+    for code in range(10):
+        assert lib.vsa_status_string(code)
+    assert lib.vsa_status_string(12345) == b"unknown status"
+
+
+def geom(B=1, H=2, D=64, grid=(8, 8, 8)):
+    from block_sparse_video_cube_amd import make_geom
+
+    return make_geom(B, H, D, grid)
+
+
+@pytest.mark.parametrize("name", list(workloads.WORKLOADS))
+def test_geom_dims_match_workloads(lib, name):
+    from block_sparse_video_cube_amd import _lib
+
+    wl = workloads.workload(name)
+    d = _lib.VsaDims()
+    assert lib.vsa_geom_dims(geom(wl.batch, wl.heads, wl.head_dim, wl.grid), ctypes.byref(d)) == 0
+    assert (d.pad_t, d.pad_h, d.pad_w) == wl.padded_grid
+    assert d.n_cubes == wl.n_cubes
+    assert d.tokens == wl.tokens
+    assert d.rows == wl.rows
+
+
+def test_geom_errors(lib):
+    from block_sparse_video_cube_amd import _lib
+
+    d = _lib.VsaDims()
+    assert lib.vsa_geom_dims(None, ctypes.byref(d)) == _lib.VSA_ERR_NULL
+    assert lib.vsa_geom_dims(geom(), None) == _lib.VSA_ERR_NULL
+    assert lib.vsa_geom_dims(geom(B=0), ctypes.byref(d)) == _lib.VSA_ERR_GEOMETRY
+    assert lib.vsa_geom_dims(geom(grid=(0, 4, 4)), ctypes.byref(d)) == _lib.VSA_ERR_GEOMETRY
+    assert lib.vsa_geom_dims(geom(H=-3), ctypes.byref(d)) == _lib.VSA_ERR_GEOMETRY
+    assert lib.vsa_geom_dims(geom(D=96), ctypes.byref(d)) == _lib.VSA_ERR_HEAD_DIM
+    assert lib.vsa_geom_dims(geom(B=300, H=300), ctypes.byref(d)) == _lib.VSA_ERR_GEOMETRY
+
+
+def test_workspace_sizes(lib):
+    g = geom()
+    assert lib.vsa_select_workspace_bytes(g) >= 2 * 2 * 8 * 64 * 4
+    assert lib.vsa_linear_workspace_bytes(g) >= 2 * 512 * 64 * 2
+    assert lib.vsa_select_workspace_bytes(geom(D=65)) == 0
+    assert lib.vsa_linear_workspace_bytes(geom(B=0)) == 0
+
+
+FAKE = 0x10000  # 16-byte aligned, never dereferenced: validation fails first
+ODD = 0x10008   # 8-byte aligned only
+
+
+def test_entry_points_reject_bad_arguments_before_launch(lib):
+    from block_sparse_video_cube_amd import _lib
+
+    g = geom()
+    P = FAKE
+    # Permute / unpermute.
+    assert lib.vsa_cube_permute(g, None, P, 0, None) == _lib.VSA_ERR_NULL
+    assert lib.vsa_cube_permute(g, P, ODD, 0, None) == _lib.VSA_ERR_ALIGN
+    assert lib.vsa_cube_permute(g, P, P, 7, None) == _lib.VSA_ERR_LAYOUT
+    assert lib.vsa_cube_permute(geom(D=32), P, P, 0, None) == _lib.VSA_ERR_HEAD_DIM
+    assert lib.vsa_cube_unpermute(g, P, None, None) == _lib.VSA_ERR_NULL
+    assert lib.vsa_cube_unpermute(geom(grid=(1, 0, 1)), P, P, None) == _lib.VSA_ERR_GEOMETRY
+    # Select.
+    ws = lib.vsa_select_workspace_bytes(g)
+    assert lib.vsa_select_topk(g, P, P, 2, P, None, ws, None) == _lib.VSA_ERR_NULL
+    assert lib.vsa_select_topk(g, P, P, 0, P, P, ws, None) == _lib.VSA_ERR_TOPK
+    assert lib.vsa_select_topk(g, P, P, 9, P, P, ws, None) == _lib.VSA_ERR_TOPK
+    assert lib.vsa_select_topk(g, P, P, 2, P, P, ws - 1, None) == _lib.VSA_ERR_WORKSPACE
+    assert lib.vsa_select_topk(g, P, ODD, 2, P, P, ws, None) == _lib.VSA_ERR_ALIGN
+    big = geom(grid=(4 * 17, 4 * 16, 4 * 16))  # 4352 cubes > VSA_MAX_CUBES
+    assert lib.vsa_select_topk(big, P, P, 2, P, P, 1 << 40, None) == _lib.VSA_ERR_GEOMETRY
+    # Fine stage.
+    assert lib.vsa_sparse_attn_fwd(g, P, P, P, None, 2, 0.125, P, None, None, None) == _lib.VSA_ERR_NULL
+    assert lib.vsa_sparse_attn_fwd(g, P, P, P, P, 0, 0.125, P, None, None, None) == _lib.VSA_ERR_TOPK
+    assert lib.vsa_sparse_attn_fwd(g, P, P, P, P, 2, 0.0, P, None, None, None) == _lib.VSA_ERR_SCALE
+    assert lib.vsa_sparse_attn_fwd(g, P, P, P, P, 2, float("nan"), P, None, None, None) == _lib.VSA_ERR_SCALE
+    assert lib.vsa_sparse_attn_fwd(g, P, P, P, P, 2, float("inf"), P, None, None, None) == _lib.VSA_ERR_SCALE
+    assert lib.vsa_sparse_attn_fwd(g, P, P, P, P, 2, 0.125, P, ODD, None, None) == _lib.VSA_ERR_ALIGN
+    # Linear branch.
+    lws = lib.vsa_linear_workspace_bytes(g)
+    assert lib.vsa_linear_branch(g, P, P, P, P, 2, None, P, P, lws, None) == _lib.VSA_ERR_NULL
+    assert lib.vsa_linear_branch(g, P, P, P, P, 2, P, P, P, lws - 1, None) == _lib.VSA_ERR_WORKSPACE
+    assert lib.vsa_linear_branch(g, P, P, P, P, 99, P, P, P, lws, None) == _lib.VSA_ERR_TOPK

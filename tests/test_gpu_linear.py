@@ -1,0 +1,66 @@
+"""GPU parity: linear branch and combine (bf16(O_sparse + O_lin)) against the oracle."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from tests.gpu_util import assert_close, bf16_f64, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def run(wl, inp, idx=None):
+    import block_sparse_video_cube_amd as vsa
+
+    valid = oracle.valid_rows(wl.grid)
+    qc_o, kc_o, vc_o = (oracle.cube_permute(inp[n], wl.grid) for n in ("q", "k", "v"))
+    if idx is None:
+        idx = oracle.select_topk(qc_o, kc_o, valid, wl.topk)
+    qc = vsa.cube_permute(to_dev(inp["q"]), wl.grid)
+    kc = vsa.cube_permute(to_dev(inp["k"]), wl.grid)
+    vt = vsa.cube_permute(to_dev(inp["v"]), wl.grid, layout="dim")
+    idx_d = torch.from_numpy(np.ascontiguousarray(idx)).to("cuda:0")
+    scale = wl.softmax_scale
+    _, of, _ = vsa.sparse_attn_fwd(qc, kc, vt, idx_d, wl.grid, scale, want_f32=True)
+    out = vsa.linear_branch(qc, kc, vt, idx_d, of, wl.grid)
+    torch.cuda.synchronize()
+    ref_s, _ = oracle.sparse_attention(qc_o, kc_o, vc_o, valid, idx, scale)
+    ref_l = oracle.linear_branch(qc_o, kc_o, vc_o, valid, idx)
+    return bf16_f64(out), ref_s + ref_l, valid
+
+
+CASES = [
+    {"grid": (8, 8, 12), "topk": 2, "batch": 2, "heads": 2},
+    {"grid": (8, 8, 12), "topk": 2, "head_dim": 64},
+    {"grid": (5, 6, 7), "topk": 3, "heads": 2},             # ragged, padded keys excluded
+    {"grid": (5, 6, 7), "topk": 3, "heads": 2, "head_dim": 64},
+    {"grid": (16, 12, 16), "topk": 1, "heads": 1},          # 48 cubes, 47 unselected
+    {"grid": (16, 12, 16), "topk": 10, "heads": 2, "batch": 2},
+]
+
+
+@pytest.mark.parametrize("over", CASES)
+def test_hybrid_matches_oracle(over):
+    wl = workloads.workload("hybrid").with_(**over)
+    inp = workloads.make_inputs(wl)
+    got, ref, valid = run(wl, inp)
+    assert_close(got[:, :, valid], ref[:, :, valid], f"hybrid {over}")
+
+
+def test_all_cubes_selected_leaves_sparse_output():
+    wl = workloads.workload("hybrid").with_(grid=(8, 8, 8), topk=8, batch=1, heads=2)
+    inp = workloads.make_inputs(wl)
+    got, ref, valid = run(wl, inp)
+    assert_close(got[:, :, valid], ref[:, :, valid], "k = Nc")
+
+
+def test_constant_values_give_twice_the_constant():
+    # Both branches average V: with V = c everywhere the result is 2c.
+    wl = workloads.workload("hybrid").with_(grid=(8, 8, 12), topk=2, batch=1, heads=2)
+    inp = workloads.make_inputs(wl)
+    inp["v"][:] = workloads.round_to_bf16_bits(np.full(inp["v"].shape, 0.75, np.float32))
+    got, ref, valid = run(wl, inp)
+    assert np.abs(got[:, :, valid] - 1.5).max() <= 1e-2
+    assert np.abs(ref[:, :, valid] - 1.5).max() <= 1e-12
