@@ -23,6 +23,8 @@ KGeom make_kgeom(const vsa_geom& g, const vsa_dims& d);
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 // Cube coordinates of cube c.
 __device__ __forceinline__ void cube_coords(const KGeom& g, int c, int& ct, int& cy, int& cx) {

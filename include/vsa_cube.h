@@ -144,7 +144,9 @@ int32_t vsa_select_topk(const vsa_geom* g, const uint16_t* qc, const uint16_t* k
  * finite values that unpermute drops).
  * oc_f32: optional fp32 copy of the output before rounding (NULL to skip).
  * lse: optional fp32 [B, heads, Np], max + log(sum) of the scaled logits in
- * natural-log units (NULL to skip). */
+ * natural-log units (NULL to skip).  The sum is taken over the bf16-rounded
+ * exponentials that weight V, so lse is within ln(1 + 2^-8) of the exact
+ * log-sum-exp. */
 int32_t vsa_sparse_attn_fwd(const vsa_geom* g, const uint16_t* qc, const uint16_t* kc,
                             const uint16_t* vt, const int32_t* idx, int32_t topk,
                             float softmax_scale, uint16_t* oc, float* oc_f32,

@@ -59,8 +59,11 @@ def test_fine_stage_matches_oracle(name, over):
     assert_close(bf16_f64(oc)[:, :, valid], ref[:, :, valid], f"{name}{over} bf16")
     assert_close(of.cpu().numpy().astype(np.float64)[:, :, valid], ref[:, :, valid], f"{name}{over} f32",
                  max_abs=1e-2, mean_abs=1e-3)
+    # The kernel's normaliser sums the bf16-rounded exponentials it applies to V
+    # (unit roundoff 2^-8), so its lse is within ln(1 + 2^-8) = 3.9e-3 of the
+    # exact value, plus fp32 noise.
     assert_close(lse.cpu().numpy().astype(np.float64)[:, :, valid], ref_lse[:, :, valid], f"{name}{over} lse",
-                 max_abs=1e-3, mean_abs=1e-4)
+                 max_abs=4.5e-3, mean_abs=1e-3)
     # Padded query rows hold finite values.
     assert torch.isfinite(oc.float()).all()
 

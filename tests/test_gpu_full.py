@@ -18,7 +18,7 @@ from tests.gpu_util import assert_close, to_bits, to_dev, topk_valid_under
 
 pytestmark = pytest.mark.gpu
 
-SAMPLED_HEADS = {"wan1.3b": [0, 11], "wan14b": [3, 38], "720p": [0, 27], "hybrid": [5, 17]}
+SAMPLED_HEADS = {"wan1.3b": [0, 11], "wan14b": [3, 38], "720p": [0, 27], "hybrid": [5, 11]}
 
 
 def sampled_cubes(wl, rng, n=20):
