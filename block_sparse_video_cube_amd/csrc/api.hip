@@ -20,6 +20,7 @@ KGeom make_kgeom(const vsa_geom& g, const vsa_dims& d) {
   k.nc = d.n_cubes;
   k.S = d.tokens;
   k.Np = d.rows;
+  k.partial = (g.grid_t % 4 != 0) || (g.grid_h % 4 != 0) || (g.grid_w % 4 != 0);
   return k;
 }
 

@@ -16,9 +16,10 @@
 //    workgroup, and keeps its own online softmax over its half of the keys;
 //    the two halves are merged through LDS at the end.
 //  * K tile (64 x D, token-major) and V tile (D x 64, stored transposed by the
-//    permute kernel) arrive by direct global->LDS loads
-//    (global_load_lds_dwordx4), double-buffered: the loads of block n+1 are in
-//    flight while block n is computed.  Each 16-byte chunk is placed with an
+//    permute kernel) arrive by direct buffer->LDS loads
+//    (buffer_load_dwordx4 ... lds) through per-tile buffer resources,
+//    double-buffered: the loads of block n+1 are in flight while block n is
+//    computed.  Each 16-byte chunk is placed with an
 //    XOR swizzle, chosen through the global address each lane fetches, so the
 //    MFMA operand reads below are free of bank conflicts.
 //  * S^T = K Q^T with v_mfma_f32_32x32x16_bf16: a lane owns one query column,
@@ -66,64 +67,93 @@ struct Smem {
   uint16_t v[2][D * 64];
 };
 
-// Issue the direct-to-LDS loads of one K tile and one V^T tile (this wave's
-// share).  Every global_load_lds_dwordx4 writes 64 consecutive 16-byte LDS
-// slots; lane L fills slot L with the global chunk that the swizzle maps
-// there.
+// Per-lane byte offsets of this wave's share of one K tile and one V^T tile.
+// Every buffer_load_dwordx4 ... lds writes 64 consecutive 16-byte LDS slots;
+// lane L fills slot L with the global chunk that the swizzle maps there.
 template <int D>
-__device__ __forceinline__ void load_tiles(const uint16_t* __restrict__ ktile, const uint16_t* __restrict__ vtile,
-                                           uint16_t* klds, uint16_t* vlds, int w, int lane) {
-  constexpr int KRPI = 512 / D;  // K rows per instruction (1 KB)
-  constexpr int NI = D / 32;     // instructions per wave per tile
+struct TileOffsets {
+  static constexpr int KRPI = 512 / D;  // K rows per 1 KB instruction
+  static constexpr int NI = D / 32;     // instructions per wave per tile
+  uint32_t k[NI], v[NI];
+  __device__ __forceinline__ TileOffsets(int w, int lane) {
 #pragma unroll
-  for (int i = 0; i < NI; ++i) {
-    const int row0 = (w * NI + i) * KRPI;
-    const int row = row0 + lane / (D / 8);
-    const int cs = lane % (D / 8);
-    const int c = cs ^ k_swz<D>(row);
-    __builtin_amdgcn_global_load_lds(ktile + row * D + c * 8, klds + row0 * D, 16, 0, 0);
+    for (int i = 0; i < NI; ++i) {
+      const int row = (w * NI + i) * KRPI + lane / (D / 8);
+      k[i] = (uint32_t)(row * D + ((lane % (D / 8)) ^ k_swz<D>(row)) * 8) * 2u;
+      const int vrow = (w * NI + i) * 8 + (lane >> 3);
+      v[i] = (uint32_t)(vrow * 64 + ((lane & 7) ^ v_swz(vrow)) * 8) * 2u;
+    }
   }
+};
+
+// Issue the direct-to-LDS loads of one K tile and one V^T tile (this wave's
+// share).  The buffer resources cover exactly one tile each, so every load is
+// range-checked by the hardware.
+template <int D>
+__device__ __forceinline__ void load_tiles(const uint16_t* ktile, const uint16_t* vtile, uint16_t* klds,
+                                           uint16_t* vlds, int w, const TileOffsets<D>& off) {
+  constexpr int KRPI = TileOffsets<D>::KRPI, NI = TileOffsets<D>::NI;
+  const __amdgpu_buffer_rsrc_t kr = make_rsrc(ktile, 64 * D * 2);
+  const __amdgpu_buffer_rsrc_t vr = make_rsrc(vtile, 64 * D * 2);
 #pragma unroll
-  for (int i = 0; i < NI; ++i) {
-    const int row0 = (w * NI + i) * 8;
-    const int row = row0 + (lane >> 3);
-    const int c = (lane & 7) ^ v_swz(row);
-    __builtin_amdgcn_global_load_lds(vtile + row * 64 + c * 8, vlds + row0 * 64, 16, 0, 0);
-  }
+  for (int i = 0; i < NI; ++i)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, (lds_ptr_t)(klds + (w * NI + i) * KRPI * D), 16, off.k[i], 0, 0, 0);
+#pragma unroll
+  for (int i = 0; i < NI; ++i)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (lds_ptr_t)(vlds + (w * NI + i) * 8 * 64), 16, off.v[i], 0, 0, 0);
 }
 
 template <int D>
 __device__ __forceinline__ void block_step(const uint16_t* klds, const uint16_t* vlds, const bf16x8 (&qf)[D / 16],
                                            f32x16 (&o)[D / 32], float& m_run, float& l_run, bool partial,
-                                           const KGeom& g, int ct, int cy, int cx, int wk, int hf, int n, int prow,
+                                           const KGeom& g, int j, int wk, int hf, int n, int prow,
                                            float scale_log2, float lazy_raw) {
   constexpr int DC = D / 16, DT = D / 32;
-  // S^T (32 keys x 32 queries) for this wave's key half.
-  f32x16 s = f32x16{};
+  // S^T (32 keys x 32 queries) for this wave's key half: all K fragments
+  // first, then the MFMA chain.
   const int krow = 32 * wk + prow;
+  bf16x8 ka[DC];
 #pragma unroll
-  for (int dc = 0; dc < DC; ++dc) {
-    const bf16x8 a = *reinterpret_cast<const bf16x8*>(klds + krow * D + (((2 * dc + hf) ^ k_swz<D>(krow)) * 8));
-    s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[dc], s, 0, 0, 0);
-  }
-  if (partial) {
+  for (int dc = 0; dc < DC; ++dc)
+    ka[dc] = *reinterpret_cast<const bf16x8*>(klds + krow * D + (((2 * dc + hf) ^ k_swz<D>(krow)) * 8));
+  f32x16 s = f32x16{};
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int key = 32 * wk + 16 * (r >> 3) + 8 * hf + (r & 7);
-      if (!local_valid(g, ct, cy, cx, key)) s[r] = -INFINITY;
+  for (int dc = 0; dc < DC; ++dc) s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[dc], qf[dc], s, 0, 0, 0);
+  // V^T fragments for this block, read while the softmax runs.
+  bf16x8 va[DT][2];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) {
+    const int vrow = 32 * dt + n;
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      const int chunk = 4 * wk + 2 * kk + hf;
+      va[dt][kk] = *reinterpret_cast<const bf16x8*>(vlds + vrow * 64 + ((chunk ^ v_swz(vrow)) * 8));
     }
   }
+  if (partial) {
+    int ct, cy, cx;
+    cube_coords(g, j, ct, cy, cx);
+    if (!cube_full(g, ct, cy, cx)) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = 32 * wk + 16 * (r >> 3) + 8 * hf + (r & 7);
+        if (!local_valid(g, ct, cy, cx, key)) s[r] = -INFINITY;
+      }
+    }
+  }
+  // Max over this lane's 16 keys.  The reference max moves only when the
+  // block exceeds it by more than kLazyLog2 (log2 units); since each lane
+  // half's max bounds the row max from below, the rare move is decided per
+  // half and only then is the row max taken across lane ^ 32.  A half that
+  // holds padded keys only (mx = -inf) never triggers a move.
   float mx = fmaxf(s[0], s[1]);
 #pragma unroll
   for (int r = 2; r < 16; ++r) mx = fmaxf(mx, s[r]);
-  mx = fmaxf(mx, __shfl_xor(mx, 32));
-  // Lazy rescale: move the reference max only when it is exceeded by more
-  // than kLazyLog2 (in log2 units of the scaled logits).  A wavefront's key
-  // half can hold padded keys only (mx = -inf): such lanes keep m_run.
-  const bool grow = mx > m_run + lazy_raw;
-  if (__builtin_amdgcn_ballot_w64(grow)) {
-    const float alpha = grow ? __builtin_amdgcn_exp2f((m_run - mx) * scale_log2) : 1.f;
-    m_run = grow ? mx : m_run;
+  if (__builtin_amdgcn_ballot_w64(mx > m_run + lazy_raw)) {
+    const float row_max = fmaxf(mx, __shfl_xor(mx, 32));
+    const bool grow = row_max > m_run + lazy_raw;
+    const float alpha = grow ? __builtin_amdgcn_exp2f((m_run - row_max) * scale_log2) : 1.f;
+    m_run = grow ? row_max : m_run;
     l_run *= alpha;
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) o[dt] *= alpha;
@@ -148,15 +178,9 @@ __device__ __forceinline__ void block_step(const uint16_t* klds, const uint16_t*
   pb[1] = __builtin_bit_cast(bf16x8, make_uint4(pw[4], pw[5], pw[6], pw[7]));
   // O^T += V^T P^T over this wave's 32 keys (2 chunks of 16).
 #pragma unroll
-  for (int dt = 0; dt < DT; ++dt) {
-    const int vrow = 32 * dt + n;
+  for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-      const int chunk = 4 * wk + 2 * kk + hf;
-      const bf16x8 a = *reinterpret_cast<const bf16x8*>(vlds + vrow * 64 + ((chunk ^ v_swz(vrow)) * 8));
-      o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[kk], o[dt], 0, 0, 0);
-    }
-  }
+    for (int kk = 0; kk < 2; ++kk) o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[dt][kk], pb[kk], o[dt], 0, 0, 0);
 }
 
 template <int D>
@@ -171,8 +195,9 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd(const uint16_t* __restri
   __shared__ __attribute__((aligned(16))) Smem<D> sm;
 
   const int i = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int wq = w & 1, wk = w >> 1;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wq = w & 1, wk = w >> 1;  // wave-uniform
   const int hf = lane >> 5, n = lane & 31;
   const long long bh = (long long)b * g.H + h;
   const uint16_t* kbase = kc + bh * g.Np * D;
@@ -181,9 +206,10 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd(const uint16_t* __restri
   const int q = 32 * wq + n;
 
   // First tiles in flight before anything else.
+  const TileOffsets<D> toff(w, lane);
   {
     const int j0 = irow[0];
-    load_tiles<D>(kbase + 64LL * j0 * D, vbase + 64LL * j0 * D, sm.k[0], sm.v[0], w, lane);
+    load_tiles<D>(kbase + 64LL * j0 * D, vbase + 64LL * j0 * D, sm.k[0], sm.v[0], w, toff);
   }
 
   bf16x8 qf[DC];
@@ -207,12 +233,10 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd(const uint16_t* __restri
       __syncthreads();  // tiles of block jb have landed (every wave waited for its own loads)
       if (jb + 1 < topk) {
         const int jn = irow[jb + 1];
-        load_tiles<D>(kbase + 64LL * jn * D, vbase + 64LL * jn * D, sm.k[1], sm.v[1], w, lane);
+        load_tiles<D>(kbase + 64LL * jn * D, vbase + 64LL * jn * D, sm.k[1], sm.v[1], w, toff);
       }
-      int ct, cy, cx;
-      cube_coords(g, j, ct, cy, cx);
-      block_step<D>(sm.k[0], sm.v[0], qf, o, m_run, l_run, !cube_full(g, ct, cy, cx), g, ct, cy, cx, wk, hf, n,
-                    prow, scale_log2, lazy_raw);
+      block_step<D>(sm.k[0], sm.v[0], qf, o, m_run, l_run, g.partial, g, j, wk, hf, n, prow, scale_log2,
+                    lazy_raw);
     }
     if (jb + 1 < topk) {
       const int j = irow[jb + 1];
@@ -220,12 +244,10 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd(const uint16_t* __restri
       __syncthreads();
       if (jb + 2 < topk) {
         const int jn = irow[jb + 2];
-        load_tiles<D>(kbase + 64LL * jn * D, vbase + 64LL * jn * D, sm.k[0], sm.v[0], w, lane);
+        load_tiles<D>(kbase + 64LL * jn * D, vbase + 64LL * jn * D, sm.k[0], sm.v[0], w, toff);
       }
-      int ct, cy, cx;
-      cube_coords(g, j, ct, cy, cx);
-      block_step<D>(sm.k[1], sm.v[1], qf, o, m_run, l_run, !cube_full(g, ct, cy, cx), g, ct, cy, cx, wk, hf, n,
-                    prow, scale_log2, lazy_raw);
+      block_step<D>(sm.k[1], sm.v[1], qf, o, m_run, l_run, g.partial, g, j, wk, hf, n, prow, scale_log2,
+                    lazy_raw);
     }
   }
 

@@ -16,6 +16,7 @@ struct KGeom {
   int nc;            // cubes
   long long S;       // tokens
   long long Np;      // cube-major rows = 64 * nc
+  int partial;       // 1 if some cube holds padded tokens
 };
 
 KGeom make_kgeom(const vsa_geom& g, const vsa_dims& d);
@@ -49,6 +50,14 @@ __device__ __forceinline__ int cube_count(const KGeom& g, int ct, int cy, int cx
   const int nt = min(4, g.T - 4 * ct), ny = min(4, g.Hg - 4 * cy), nx = min(4, g.W - 4 * cx);
   return nt * ny * nx;
 }
+
+// Buffer resource over `bytes` bytes at `base` (raw, unswizzled, dword data
+// format): loads outside the range return zero instead of faulting.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, unsigned bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) {
   return __uint_as_float(((uint32_t)b) << 16);
