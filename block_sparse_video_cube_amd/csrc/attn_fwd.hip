@@ -17,9 +17,8 @@
 //    the two halves are merged through LDS at the end.
 //  * K tile (64 x D, token-major) and V tile (D x 64, stored transposed by the
 //    permute kernel) arrive by direct buffer->LDS loads
-//    (buffer_load_dwordx4 ... lds) through per-tile buffer resources,
-//    double-buffered: the loads of block n+1 are in flight while block n is
-//    computed.  Each 16-byte chunk is placed with an
+//    (buffer_load_dwordx4 ... lds) through per-tile buffer resources; K runs
+//    two blocks ahead (three buffers) and V one block ahead (two buffers).  Each 16-byte chunk is placed with an
 //    XOR swizzle, chosen through the global address each lane fetches, so the
 //    MFMA operand reads below are free of bank conflicts.
 //  * S^T = K Q^T with v_mfma_f32_32x32x16_bf16: a lane owns one query column,
@@ -32,120 +31,45 @@
 //    O^T rescale (a full accumulator pass) is skipped almost always.
 #include <math.h>
 
-#include "common.h"
+#include "tile_pipeline.h"
 
 namespace vsa {
 
 namespace {
 
-constexpr int kThreads = 256;
+using namespace tiles;
 constexpr float kLazyLog2 = 8.f;
 
-// Wait until every global load of this wavefront has completed, including the
-// direct-to-LDS tile loads (s_waitcnt vmcnt(0); gfx9 encoding, other
-// counters left at their maximum).  The workgroup fence of __syncthreads()
-// treats those loads as loads and does not wait for them by itself.
-__device__ __forceinline__ void wait_tile_loads() { __builtin_amdgcn_s_waitcnt(0x0F70); }
-
-// Key row loaded by A-operand lane row m (0..31) of a 32-key tile.  With it,
-// accumulator register r of lane half hf holds key 16*(r/8) + 8*hf + r%8.
-__device__ __forceinline__ int pi_row(int m) {
-  const int gq = m >> 3, hq = (m >> 2) & 1, rr = m & 3;
-  return 16 * (gq >> 1) + 8 * hq + 4 * (gq & 1) + rr;
-}
-
-// 16-byte chunk swizzles.
-template <int D>
-__device__ __forceinline__ int k_swz(int row) {
-  return (D == 128) ? (row & 15) : ((row >> 1) & 7);
-}
-__device__ __forceinline__ int v_swz(int row) { return (row >> 1) & 7; }
-
+// Three K buffers (K runs two blocks ahead) and two V buffers: 80 KB at
+// D = 128, so two workgroups fill the 160 KB of LDS of a compute unit.
 template <int D>
 struct Smem {
-  uint16_t k[2][64 * D];
+  uint16_t k[3][64 * D];
   uint16_t v[2][D * 64];
 };
 
-// Per-lane byte offsets of this wave's share of one K tile and one V^T tile.
-// Every buffer_load_dwordx4 ... lds writes 64 consecutive 16-byte LDS slots;
-// lane L fills slot L with the global chunk that the swizzle maps there.
-template <int D>
-struct TileOffsets {
-  static constexpr int KRPI = 512 / D;  // K rows per 1 KB instruction
-  static constexpr int NI = D / 32;     // instructions per wave per tile
-  uint32_t k[NI], v[NI];
-  __device__ __forceinline__ TileOffsets(int w, int lane) {
+// Padded keys of a partial cube take no weight.
+__device__ __forceinline__ void mask_partial(f32x16& s, const KGeom& g, int j, int wk, int hf) {
+  int ct, cy, cx;
+  cube_coords(g, j, ct, cy, cx);
+  if (!cube_full(g, ct, cy, cx)) {
 #pragma unroll
-    for (int i = 0; i < NI; ++i) {
-      const int row = (w * NI + i) * KRPI + lane / (D / 8);
-      k[i] = (uint32_t)(row * D + ((lane % (D / 8)) ^ k_swz<D>(row)) * 8) * 2u;
-      const int vrow = (w * NI + i) * 8 + (lane >> 3);
-      v[i] = (uint32_t)(vrow * 64 + ((lane & 7) ^ v_swz(vrow)) * 8) * 2u;
+    for (int r = 0; r < 16; ++r) {
+      const int key = 32 * wk + 16 * (r >> 3) + 8 * hf + (r & 7);
+      if (!local_valid(g, ct, cy, cx, key)) s[r] = -INFINITY;
     }
   }
-};
-
-// Issue the direct-to-LDS loads of one K tile and one V^T tile (this wave's
-// share).  The buffer resources cover exactly one tile each, so every load is
-// range-checked by the hardware.
-template <int D>
-__device__ __forceinline__ void load_tiles(const uint16_t* ktile, const uint16_t* vtile, uint16_t* klds,
-                                           uint16_t* vlds, int w, const TileOffsets<D>& off) {
-  constexpr int KRPI = TileOffsets<D>::KRPI, NI = TileOffsets<D>::NI;
-  const __amdgpu_buffer_rsrc_t kr = make_rsrc(ktile, 64 * D * 2);
-  const __amdgpu_buffer_rsrc_t vr = make_rsrc(vtile, 64 * D * 2);
-#pragma unroll
-  for (int i = 0; i < NI; ++i)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, (lds_ptr_t)(klds + (w * NI + i) * KRPI * D), 16, off.k[i], 0, 0, 0);
-#pragma unroll
-  for (int i = 0; i < NI; ++i)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (lds_ptr_t)(vlds + (w * NI + i) * 8 * 64), 16, off.v[i], 0, 0, 0);
 }
 
-template <int D>
-__device__ __forceinline__ void block_step(const uint16_t* klds, const uint16_t* vlds, const bf16x8 (&qf)[D / 16],
-                                           f32x16 (&o)[D / 32], float& m_run, float& l_run, bool partial,
-                                           const KGeom& g, int j, int wk, int hf, int n, int prow,
-                                           float scale_log2, float lazy_raw) {
-  constexpr int DC = D / 16, DT = D / 32;
-  // S^T (32 keys x 32 queries) for this wave's key half: all K fragments
-  // first, then the MFMA chain.
-  const int krow = 32 * wk + prow;
-  bf16x8 ka[DC];
-#pragma unroll
-  for (int dc = 0; dc < DC; ++dc)
-    ka[dc] = *reinterpret_cast<const bf16x8*>(klds + krow * D + (((2 * dc + hf) ^ k_swz<D>(krow)) * 8));
-  f32x16 s = f32x16{};
-#pragma unroll
-  for (int dc = 0; dc < DC; ++dc) s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[dc], qf[dc], s, 0, 0, 0);
-  // V^T fragments for this block, read while the softmax runs.
-  bf16x8 va[DT][2];
-#pragma unroll
-  for (int dt = 0; dt < DT; ++dt) {
-    const int vrow = 32 * dt + n;
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-      const int chunk = 4 * wk + 2 * kk + hf;
-      va[dt][kk] = *reinterpret_cast<const bf16x8*>(vlds + vrow * 64 + ((chunk ^ v_swz(vrow)) * 8));
-    }
-  }
-  if (partial) {
-    int ct, cy, cx;
-    cube_coords(g, j, ct, cy, cx);
-    if (!cube_full(g, ct, cy, cx)) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int key = 32 * wk + 16 * (r >> 3) + 8 * hf + (r & 7);
-        if (!local_valid(g, ct, cy, cx, key)) s[r] = -INFINITY;
-      }
-    }
-  }
-  // Max over this lane's 16 keys.  The reference max moves only when the
-  // block exceeds it by more than kLazyLog2 (log2 units); since each lane
-  // half's max bounds the row max from below, the rare move is decided per
-  // half and only then is the row max taken across lane ^ 32.  A half that
-  // holds padded keys only (mx = -inf) never triggers a move.
+// Online-softmax statistics of one S^T tile: row max and the rare lazy
+// rescale of (m_run, l_run, O^T).  The reference max moves only when the
+// block exceeds it by more than kLazyLog2 (log2 units); since each lane
+// half's max bounds the row max from below, the rare move is decided per half
+// and only then is the row max taken across lane ^ 32.  A half that holds
+// padded keys only (max -inf) never triggers a move.
+template <int DT>
+__device__ __forceinline__ float softmax_stats(const f32x16& s, f32x16 (&o)[DT], float& m_run, float& l_run,
+                                               float scale_log2, float lazy_raw) {
   float mx = fmaxf(s[0], s[1]);
 #pragma unroll
   for (int r = 2; r < 16; ++r) mx = fmaxf(mx, s[r]);
@@ -159,16 +83,37 @@ __device__ __forceinline__ void block_step(const uint16_t* klds, const uint16_t*
     for (int dt = 0; dt < DT; ++dt) o[dt] *= alpha;
   }
   // Until a valid key has been seen every logit is -inf and p must be 0.
-  const float mc = (m_run == -INFINITY) ? 0.f : m_run * scale_log2;
-  // P rounded once to bf16 (v_cvt_pk_bf16_f32); the normaliser sums the same
-  // rounded values (v_dot2_f32_bf16 against 1.0), so the weights applied to V
-  // sum exactly to the normaliser.
-  uint32_t pw[8];
+  return (m_run == -INFINITY) ? 0.f : m_run * scale_log2;
+}
+
+// One pipelined block: S^T of the next block is computed on the matrix cores
+// while the vector units turn the current S^T into P (exp2, bf16 pack, row
+// sum); then O^T += V^T P^T.  P is rounded once to bf16 (v_cvt_pk_bf16_f32)
+// and the normaliser sums the same rounded values (v_dot2_f32_bf16 against
+// 1.0), so the weights applied to V sum exactly to the normaliser.
+// The tile loads of later blocks (V of block n+1, K of block n+3) are issued
+// one per MFMA slot here, so that neither the vector units nor the texture
+// path see bursts; vr/kr are their buffer resources, vl/kl the LDS
+// destinations of this wave's first instruction, voff/koff its lane offsets.
+template <int D>
+__device__ __forceinline__ void pipelined_step(const bf16x8 (&ka)[D / 16], const bf16x8 (&va)[D / 32][2],
+                                               const bf16x8 (&qf)[D / 16], const f32x16& s_cur, f32x16& s_next,
+                                               f32x16 (&o)[D / 32], float& l_run, float mc, float scale_log2,
+                                               __amdgpu_buffer_rsrc_t vr, uint16_t* vl, const uint32_t* voff,
+                                               __amdgpu_buffer_rsrc_t kr, uint16_t* kl, const uint32_t* koff) {
+  constexpr int DC = D / 16, DT = D / 32, NI = D / 32, KRPI = 512 / D;
   const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+  uint32_t pw[8];
+  s_next = f32x16{};
 #pragma unroll
   for (int r = 0; r < 8; ++r) {
-    const float p0 = __builtin_amdgcn_exp2f(fmaf(s[2 * r], scale_log2, -mc));
-    const float p1 = __builtin_amdgcn_exp2f(fmaf(s[2 * r + 1], scale_log2, -mc));
+    if (r < DC) s_next = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[r], qf[r], s_next, 0, 0, 0);
+    if (r < NI)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (lds_ptr_t)(vl + r * 8 * 64), 16, voff[r], 0, 0, 0);
+    else if (r < 2 * NI)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, (lds_ptr_t)(kl + (r - NI) * KRPI * D), 16, koff[r - NI], 0, 0, 0);
+    const float p0 = __builtin_amdgcn_exp2f(fmaf(s_cur[2 * r], scale_log2, -mc));
+    const float p1 = __builtin_amdgcn_exp2f(fmaf(s_cur[2 * r + 1], scale_log2, -mc));
     const bf16x2 pk = __builtin_convertvector((f32x2){p0, p1}, bf16x2);
     l_run = __builtin_amdgcn_fdot2_f32_bf16(pk, ones, l_run, false);
     pw[r] = __builtin_bit_cast(uint32_t, pk);
@@ -176,11 +121,16 @@ __device__ __forceinline__ void block_step(const uint16_t* klds, const uint16_t*
   bf16x8 pb[2];
   pb[0] = __builtin_bit_cast(bf16x8, make_uint4(pw[0], pw[1], pw[2], pw[3]));
   pb[1] = __builtin_bit_cast(bf16x8, make_uint4(pw[4], pw[5], pw[6], pw[7]));
-  // O^T += V^T P^T over this wave's 32 keys (2 chunks of 16).
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[dt][kk], pb[kk], o[dt], 0, 0, 0);
+  // Interleave: one MFMA of the next S^T, then the vector work of one P pair.
+#pragma unroll
+  for (int r = 0; r < DC; ++r) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
+  }
 }
 
 template <int D>
@@ -194,7 +144,8 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd(const uint16_t* __restri
   constexpr int DC = D / 16, DT = D / 32;
   __shared__ __attribute__((aligned(16))) Smem<D> sm;
 
-  const int i = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  int i, h, b;
+  if (!map_workgroup(g, i, h, b)) return;  // whole workgroup leaves before any barrier
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wq = w & 1, wk = w >> 1;  // wave-uniform
@@ -209,7 +160,8 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd(const uint16_t* __restri
   const TileOffsets<D> toff(w, lane);
   {
     const int j0 = irow[0];
-    load_tiles<D>(kbase + 64LL * j0 * D, vbase + 64LL * j0 * D, sm.k[0], sm.v[0], w, toff);
+    load_k_tile<D>(kbase + 64LL * j0 * D, sm.k[0], w, toff);
+    load_v_tile<D>(vbase + 64LL * j0 * D, sm.v[0], w, toff);
   }
 
   bf16x8 qf[DC];
@@ -225,29 +177,53 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd(const uint16_t* __restri
   const int prow = pi_row(n);
   const float lazy_raw = kLazyLog2 / scale_log2;
 
-  // Two blocks per trip so that both LDS buffers are compile-time distinct.
-  for (int jb = 0; jb < topk; jb += 2) {
-    {
-      const int j = irow[jb];
-      wait_tile_loads();
-      __syncthreads();  // tiles of block jb have landed (every wave waited for its own loads)
-      if (jb + 1 < topk) {
-        const int jn = irow[jb + 1];
-        load_tiles<D>(kbase + 64LL * jn * D, vbase + 64LL * jn * D, sm.k[1], sm.v[1], w, toff);
+  // Pipeline: entering step n, S^T of block n is in registers, K of blocks
+  // n+1 and n+2 and V of block n are in (or on their way to) LDS.  Step n
+  // waits for K(n+1) and V(n), starts the loads of V(n+1) and K(n+3) into the
+  // buffers freed by step n-1, computes S^T(n+1) while turning S^T(n) into P,
+  // and adds P V(n).  K buffer of block m: m % 3, V buffer: m % 2; steps come
+  // in groups of six so that every buffer is compile-time distinct.
+  constexpr int NI = TileOffsets<D>::NI;
+  // Past the last block the pipeline keeps issuing loads (of a valid tile,
+  // into a free buffer) so that the number of loads in flight is the same at
+  // every step: K(1), K(2) here, then V(n+1), K(n+3) in step n.
+  const auto blk = [&](int m) { return irow[m < topk ? m : topk - 1]; };
+  load_k_tile<D>(kbase + 64LL * blk(1) * D, sm.k[1], w, toff);
+  load_k_tile<D>(kbase + 64LL * blk(2) * D, sm.k[2], w, toff);
+  f32x16 s_cur, s_next;
+  {
+    // K(0) and V(0) were issued first; K(1), K(2) may stay in flight.
+    wait_vmcnt<2 * NI>();
+    pipeline_barrier();
+    bf16x8 ka[DC];
+    read_k<D>(sm.k[0], wk, hf, prow, ka);
+    s_cur = f32x16{};
+#pragma unroll
+    for (int dc = 0; dc < DC; ++dc) s_cur = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[dc], qf[dc], s_cur, 0, 0, 0);
+  }
+  int j_cur = irow[0];
+  for (int jb = 0; jb < topk; jb += 6) {
+#pragma unroll
+    for (int u = 0; u < 6; ++u) {
+      const int nb = jb + u;
+      if (nb < topk) {
+        // Outstanding, oldest first: K(nb+1), V(nb), K(nb+2).
+        wait_vmcnt<NI>();
+        pipeline_barrier();
+        const int j_next = blk(nb + 1);
+        bf16x8 ka[DC];
+        bf16x8 va[DT][2];
+        read_k<D>(sm.k[(u + 1) % 3], wk, hf, prow, ka);
+        read_v<D>(sm.v[u % 2], wk, hf, n, va);
+        if (g.partial) mask_partial(s_cur, g, j_cur, wk, hf);
+        const float mc = softmax_stats<DT>(s_cur, o, m_run, l_run, scale_log2, lazy_raw);
+        pipelined_step<D>(ka, va, qf, s_cur, s_next, o, l_run, mc, scale_log2,
+                          make_rsrc(vbase + 64LL * j_next * D, 64 * D * 2), sm.v[(u + 1) % 2] + w * NI * 8 * 64,
+                          toff.v, make_rsrc(kbase + 64LL * blk(nb + 3) * D, 64 * D * 2),
+                          sm.k[u % 3] + w * NI * TileOffsets<D>::KRPI * D, toff.k);
+        s_cur = s_next;
+        j_cur = j_next;
       }
-      block_step<D>(sm.k[0], sm.v[0], qf, o, m_run, l_run, g.partial, g, j, wk, hf, n, prow, scale_log2,
-                    lazy_raw);
-    }
-    if (jb + 1 < topk) {
-      const int j = irow[jb + 1];
-      wait_tile_loads();
-      __syncthreads();
-      if (jb + 2 < topk) {
-        const int jn = irow[jb + 2];
-        load_tiles<D>(kbase + 64LL * jn * D, vbase + 64LL * jn * D, sm.k[0], sm.v[0], w, toff);
-      }
-      block_step<D>(sm.k[1], sm.v[1], qf, o, m_run, l_run, g.partial, g, j, wk, hf, n, prow, scale_log2,
-                    lazy_raw);
     }
   }
 
@@ -297,7 +273,7 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd(const uint16_t* __restri
 hipError_t launch_attn_fwd(const KGeom& g, const uint16_t* qc, const uint16_t* kc, const uint16_t* vt,
                            const int32_t* idx, int topk, float scale, uint16_t* oc, float* oc_f32, float* lse,
                            hipStream_t s) {
-  const dim3 grid(g.nc, g.H, g.B);
+  const dim3 grid(grid_size(g));
   const float scale_log2 = scale * 1.4426950408889634f;
   if (g.D == 64)
     hipLaunchKernelGGL(attn_fwd<64>, grid, dim3(kThreads), 0, s, qc, kc, vt, idx, topk, scale, scale_log2, oc,

@@ -19,29 +19,21 @@
 //   lin_state   per (b, h, group of 8 cubes): phi(K) (bf16, padded rows 0)
 //               written token-major for lin_apply, and partial
 //               S = phi(K)^T V (bf16 MFMA, fp32 accumulate) and z = sum phi(K);
-//   lin_reduce  per (b, h): S_tot^T split into bf16 hi + lo halves, z_tot;
+//   lin_reduce  per (b, h, 256 state elements): S_tot^T split into bf16
+//               hi + lo halves, z_tot;
 //   lin_apply   per (b, h, query cube): num / den and the combine.
 #include <math.h>
 
-#include "common.h"
+#include "tile_pipeline.h"
 
 namespace vsa {
 
 namespace {
 
+using namespace tiles;
 constexpr int kGroup = 8;  // cubes per partial state
 
 __device__ __forceinline__ float phi(float x) { return x > 0.f ? x + 1.f : __expf(x); }
-
-__device__ __forceinline__ int pi_row(int m) {
-  const int gq = m >> 3, hq = (m >> 2) & 1, rr = m & 3;
-  return 16 * (gq >> 1) + 8 * hq + 4 * (gq & 1) + rr;
-}
-template <int D>
-__device__ __forceinline__ int k_swz(int row) {
-  return (D == 128) ? (row & 15) : ((row >> 1) & 7);
-}
-__device__ __forceinline__ int v_swz(int row) { return (row >> 1) & 7; }
 
 struct LinWs {
   uint16_t* fk;     // [B, H, Np, D] bf16 phi(K), token-major
@@ -156,43 +148,73 @@ __global__ void __launch_bounds__(256) lin_state(const uint16_t* __restrict__ kc
   }
 }
 
+// One thread per state element (d, e) of one (b, h): sums the group partials
+// (coalesced across threads) and writes S_tot^T as bf16 hi + lo.  Workgroup
+// (chunk, bh) covers 256 consecutive elements; the last chunk also sums z.
 template <int D>
 __global__ void __launch_bounds__(256) lin_reduce(LinWs ws, KGeom g) {
-  const long long bh = blockIdx.x;
+  const long long bh = blockIdx.y;
   const int G = (g.nc + kGroup - 1) / kGroup;
+  const int f = blockIdx.x * 256 + threadIdx.x;  // < D * D
   const float* sp = ws.s_part + bh * G * (long long)D * D;
-  for (int f = threadIdx.x; f < D * D; f += 256) {
-    const int d = f / D, e = f % D;
-    float s = 0.f;
-    for (int gi = 0; gi < G; ++gi) s += sp[(long long)gi * D * D + f];
-    const uint16_t hi = f32_to_bf16(s);
-    const uint16_t lo = f32_to_bf16(s - bf16_to_f32(hi));
-    ws.st_hi[bh * D * D + e * D + d] = hi;
-    ws.st_lo[bh * D * D + e * D + d] = lo;
-  }
-  if (threadIdx.x < D) {
-    float s = 0.f;
-    for (int gi = 0; gi < G; ++gi) s += ws.z_part[(bh * G + gi) * D + threadIdx.x];
-    ws.z_tot[bh * D + threadIdx.x] = s;
+  float s = 0.f;
+  for (int gi = 0; gi < G; ++gi) s += sp[(long long)gi * D * D + f];
+  const int d = f / D, e = f % D;
+  const uint16_t hi = f32_to_bf16(s);
+  const uint16_t lo = f32_to_bf16(s - bf16_to_f32(hi));
+  ws.st_hi[bh * D * D + e * D + d] = hi;
+  ws.st_lo[bh * D * D + e * D + d] = lo;
+  if (blockIdx.x == gridDim.x - 1 && threadIdx.x < D) {
+    float z = 0.f;
+    for (int gi = 0; gi < G; ++gi) z += ws.z_part[(bh * G + gi) * D + threadIdx.x];
+    ws.z_tot[bh * D + threadIdx.x] = z;
   }
 }
 
+// Two phi(K) and two V^T tile buffers (64 KB at D = 128).
 template <int D>
-__global__ void __launch_bounds__(128) lin_apply(const uint16_t* __restrict__ qc, const uint16_t* __restrict__ vt,
-                                                 const int32_t* __restrict__ idx, int topk,
-                                                 const float* __restrict__ o_sparse, uint16_t* __restrict__ oc,
-                                                 LinWs ws, KGeom g) {
-  constexpr int DC = D / 16, DT = D / 32, CH = D / 8;
-  __shared__ __attribute__((aligned(16))) uint16_t f_lds[64 * D];
-  __shared__ __attribute__((aligned(16))) uint16_t v_lds[D * 64];
-  const int i = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, hf = lane >> 5, n = lane & 31;
-  const long long bh = (long long)b * g.H + h;
-  const int q = 32 * w + n;
-  const long long row = bh * g.Np + 64LL * i + q;
-  const bool empty_u = topk >= g.nc;
+struct LinSmem {
+  uint16_t f[2][64 * D];
+  uint16_t v[2][D * 64];
+};
 
-  // phi(Q) fragments (bf16) and phi(Q) . z_tot.
+// One workgroup per (b, h, query cube), the same wavefront split and tile
+// pipeline as the fine stage: wavefront (wq, wk) owns queries 32 wq .. +31 and
+// keys 32 wk .. +31 of every selected block.  Per block it forms
+// A^T = phi(K) phi(Q)^T on the matrix cores, rounds A to bf16 (its row sums,
+// taken on the same rounded values, go to the denominator) and accumulates
+// V^T A^T.  The total part phi(Q) S_tot is split between the two key halves
+// (bf16 hi half on wk = 0, lo half on wk = 1) so that the merge through LDS
+// adds num - corr directly.
+template <int D>
+__global__ void __launch_bounds__(kThreads, 2) lin_apply(const uint16_t* __restrict__ qc,
+                                                         const uint16_t* __restrict__ vt,
+                                                         const int32_t* __restrict__ idx, int topk,
+                                                         const float* __restrict__ o_sparse,
+                                                         uint16_t* __restrict__ oc, LinWs ws, KGeom g) {
+  constexpr int DC = D / 16, DT = D / 32;
+  __shared__ __attribute__((aligned(16))) LinSmem<D> sm;
+  int i, h, b;
+  if (!map_workgroup(g, i, h, b)) return;  // whole workgroup leaves before any barrier
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wq = w & 1, wk = w >> 1;
+  const int hf = lane >> 5, n = lane & 31;
+  const long long bh = (long long)b * g.H + h;
+  const int q = 32 * wq + n;
+  const long long row = bh * g.Np + 64LL * i + q;
+  const bool empty_u = topk >= g.nc;  // every cube selected: O_lin = 0
+  const int32_t* irow = idx + (bh * g.nc + i) * topk;
+  const uint16_t* fkb = ws.fk + bh * g.Np * D;
+  const uint16_t* vb = vt + bh * g.Np * D;
+  const TileOffsets<D> toff(w, lane);
+  if (!empty_u) {
+    const int j0 = irow[0];
+    load_k_tile<D>(fkb + 64LL * j0 * D, sm.f[0], w, toff);
+    load_v_tile<D>(vb + 64LL * j0 * D, sm.v[0], w, toff);
+  }
+
+  // phi(Q) fragments (bf16) and this lane's part of phi(Q) . z_tot.
   bf16x8 fq[DC];
   float den_part = 0.f;
   {
@@ -211,76 +233,85 @@ __global__ void __launch_bounds__(128) lin_apply(const uint16_t* __restrict__ qc
         const int d = 16 * dc + 8 * hf + 2 * e2;
         den_part += bf16_to_f32(p0) * zt[d] + bf16_to_f32(p1) * zt[d + 1];
       }
-    }
-  }
-  // num^T = S_tot^T phi(Q)^T (hi + lo halves).
-  f32x16 num[DT], corr[DT];
-  const uint16_t* sth = ws.st_hi + bh * D * D;
-  const uint16_t* stl = ws.st_lo + bh * D * D;
-#pragma unroll
-  for (int dt = 0; dt < DT; ++dt) {
-    num[dt] = f32x16{};
-    corr[dt] = f32x16{};
-    const int e = 32 * dt + n;
-#pragma unroll
-    for (int dc = 0; dc < DC; ++dc) {
-      const bf16x8 ah = *reinterpret_cast<const bf16x8*>(sth + e * D + 16 * dc + 8 * hf);
-      const bf16x8 al = *reinterpret_cast<const bf16x8*>(stl + e * D + 16 * dc + 8 * hf);
-      num[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, fq[dc], num[dt], 0, 0, 0);
-      num[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, fq[dc], num[dt], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);  // one chunk of loads at a time (register budget)
     }
   }
 
-  // Selected part, block by block.
+  // Selected part, block by block (double-buffered tiles).
+  f32x16 c[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) c[dt] = f32x16{};
   float dcorr = 0.f;
-  const int32_t* irow = idx + (bh * g.nc + i) * topk;
-  const uint16_t* fkb = ws.fk + bh * g.Np * D;
-  const uint16_t* vb = vt + bh * g.Np * D;
   const int prow = pi_row(n);
-  for (int jb = 0; jb < (empty_u ? 0 : topk); ++jb) {
-    const int j = irow[jb];
-    __syncthreads();
-    const uint4* fsrc = reinterpret_cast<const uint4*>(fkb + 64LL * j * D);
-    for (int f = tid; f < 64 * CH; f += 128) {
-      const int r = f / CH, ch = f % CH;
-      *reinterpret_cast<uint4*>(f_lds + r * D + ((ch ^ k_swz<D>(r)) * 8)) = fsrc[f];
-    }
-    const uint4* vsrc = reinterpret_cast<const uint4*>(vb + 64LL * j * D);
-    for (int f = tid; f < D * 8; f += 128) {
-      const int r = f >> 3, ch = f & 7;
-      *reinterpret_cast<uint4*>(v_lds + r * 64 + ((ch ^ v_swz(r)) * 8)) = vsrc[f];
-    }
-    __syncthreads();
-    bf16x8 pb[4];
+  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+  for (int jb = 0; jb < (empty_u ? 0 : topk); jb += 2) {
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt) {
-      f32x16 s = f32x16{};
-      const int krow = 32 * mt + prow;
+    for (int par = 0; par < 2; ++par) {
+      const int nb = jb + par;
+      if (nb < topk) {
+        wait_vmcnt<0>();
+        pipeline_barrier();
+        if (nb + 1 < topk) {
+          const int jn = irow[nb + 1];
+          load_k_tile<D>(fkb + 64LL * jn * D, sm.f[1 - par], w, toff);
+          load_v_tile<D>(vb + 64LL * jn * D, sm.v[1 - par], w, toff);
+        }
+        bf16x8 ka[DC];
+        bf16x8 va[DT][2];
+        read_k<D>(sm.f[par], wk, hf, prow, ka);
+        read_v<D>(sm.v[par], wk, hf, n, va);
+        f32x16 sa = f32x16{};
 #pragma unroll
-      for (int dc = 0; dc < DC; ++dc) {
-        const bf16x8 a =
-            *reinterpret_cast<const bf16x8*>(f_lds + krow * D + (((2 * dc + hf) ^ k_swz<D>(krow)) * 8));
-        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, fq[dc], s, 0, 0, 0);
-      }
+        for (int dc = 0; dc < DC; ++dc) sa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[dc], fq[dc], sa, 0, 0, 0);
+        uint32_t pw[8];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const uint16_t pbits = f32_to_bf16(s[r]);
-        dcorr += bf16_to_f32(pbits);
-        pb[2 * mt + (r >> 3)][r & 7] = __builtin_bit_cast(__bf16, pbits);
-      }
-    }
+        for (int r = 0; r < 8; ++r) {
+          const bf16x2 pk = __builtin_convertvector((f32x2){sa[2 * r], sa[2 * r + 1]}, bf16x2);
+          dcorr = __builtin_amdgcn_fdot2_f32_bf16(pk, ones, dcorr, false);
+          pw[r] = __builtin_bit_cast(uint32_t, pk);
+        }
+        bf16x8 pb[2];
+        pb[0] = __builtin_bit_cast(bf16x8, make_uint4(pw[0], pw[1], pw[2], pw[3]));
+        pb[1] = __builtin_bit_cast(bf16x8, make_uint4(pw[4], pw[5], pw[6], pw[7]));
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
-      const int vrow = 32 * dt + n;
+        for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        const bf16x8 a =
-            *reinterpret_cast<const bf16x8*>(v_lds + vrow * 64 + (((2 * kk + hf) ^ v_swz(vrow)) * 8));
-        corr[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[kk], corr[dt], 0, 0, 0);
+          for (int kk = 0; kk < 2; ++kk)
+            c[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[dt][kk], pb[kk], c[dt], 0, 0, 0);
       }
     }
   }
-  const float den = (den_part + __shfl_xor(den_part, 32)) - (dcorr + __shfl_xor(dcorr, 32));
+
+  // c = (this half of phi(Q) S_tot) - (this half's correction).
+  const uint16_t* st = (wk == 0 ? ws.st_hi : ws.st_lo) + bh * D * D;
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) {
+    c[dt] = -c[dt];
+    const int e = 32 * dt + n;
+#pragma unroll
+    for (int dc = 0; dc < DC; ++dc) {
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(st + e * D + 16 * dc + 8 * hf);
+      c[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, fq[dc], c[dt], 0, 0, 0);
+    }
+    // Keep the loads of one e-tile at a time in flight (register budget).
+    __builtin_amdgcn_sched_barrier(0);
+  }
+
+  // Merge the two key halves through LDS.
+  dcorr += __shfl_xor(dcorr, 32);
+  __syncthreads();  // every tile read has completed; reuse the phi(K) buffers
+  float* xo = reinterpret_cast<float*>(&sm.f[0][0]) + wq * (DT * 16 * 64);
+  float* xd = reinterpret_cast<float*>(&sm.v[0][0]) + wq * 64;
+  if (wk == 1) {
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) xo[(dt * 16 + r) * 64 + lane] = c[dt][r];
+    xd[lane] = dcorr;
+  }
+  __syncthreads();
+  if (wk == 1) return;
+  const float den = (den_part + __shfl_xor(den_part, 32)) - (dcorr + xd[lane]);
   const float inv = empty_u ? 0.f : 1.f / den;
   const float* osrc = o_sparse + row * D;
   uint16_t* odst = oc + row * D;
@@ -290,12 +321,14 @@ __global__ void __launch_bounds__(128) lin_apply(const uint16_t* __restrict__ qc
     for (int gq = 0; gq < 4; ++gq) {
       const int e = 32 * dt + 8 * gq + 4 * hf;
       const float4 os = *reinterpret_cast<const float4*>(osrc + e);
-      const float l0 = empty_u ? 0.f : (num[dt][4 * gq + 0] - corr[dt][4 * gq + 0]) * inv;
-      const float l1 = empty_u ? 0.f : (num[dt][4 * gq + 1] - corr[dt][4 * gq + 1]) * inv;
-      const float l2 = empty_u ? 0.f : (num[dt][4 * gq + 2] - corr[dt][4 * gq + 2]) * inv;
-      const float l3 = empty_u ? 0.f : (num[dt][4 * gq + 3] - corr[dt][4 * gq + 3]) * inv;
+      float v[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int r = 4 * gq + u;
+        v[u] = (c[dt][r] + xo[(dt * 16 + r) * 64 + lane]) * inv;
+      }
       *reinterpret_cast<uint2*>(odst + e) =
-          make_uint2(pack_bf16x2(os.x + l0, os.y + l1), pack_bf16x2(os.z + l2, os.w + l3));
+          make_uint2(pack_bf16x2(os.x + v[0], os.y + v[1]), pack_bf16x2(os.z + v[2], os.w + v[3]));
     }
 }
 
@@ -315,13 +348,14 @@ hipError_t launch_linear(const KGeom& g, const uint16_t* qc, const uint16_t* kc,
   const unsigned bh = (unsigned)(g.B * g.H);
   if (g.D == 64) {
     hipLaunchKernelGGL(lin_state<64>, dim3(G, g.H, g.B), dim3(256), 0, s, kc, vt, w, g);
-    hipLaunchKernelGGL(lin_reduce<64>, dim3(bh), dim3(256), 0, s, w, g);
-    hipLaunchKernelGGL(lin_apply<64>, dim3(g.nc, g.H, g.B), dim3(128), 0, s, qc, vt, idx, topk, o_sparse, oc, w, g);
+    hipLaunchKernelGGL(lin_reduce<64>, dim3(64 * 64 / 256, bh), dim3(256), 0, s, w, g);
+    hipLaunchKernelGGL(lin_apply<64>, dim3(grid_size(g)), dim3(kThreads), 0, s, qc, vt, idx, topk, o_sparse, oc,
+                       w, g);
   } else {
     hipLaunchKernelGGL(lin_state<128>, dim3(G, g.H, g.B), dim3(256), 0, s, kc, vt, w, g);
-    hipLaunchKernelGGL(lin_reduce<128>, dim3(bh), dim3(256), 0, s, w, g);
-    hipLaunchKernelGGL(lin_apply<128>, dim3(g.nc, g.H, g.B), dim3(128), 0, s, qc, vt, idx, topk, o_sparse, oc, w,
-                       g);
+    hipLaunchKernelGGL(lin_reduce<128>, dim3(128 * 128 / 256, bh), dim3(256), 0, s, w, g);
+    hipLaunchKernelGGL(lin_apply<128>, dim3(grid_size(g)), dim3(kThreads), 0, s, qc, vt, idx, topk, o_sparse, oc,
+                       w, g);
   }
   return hipGetLastError();
 }

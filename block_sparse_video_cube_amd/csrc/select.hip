@@ -8,8 +8,9 @@
 // lower cube index, listed in ascending order.
 //
 // Three kernels:
-//   cube_mean   one workgroup per (b, h, cube): fp32 mean over valid rows;
-//   block_score 64x64 tiles of the fp32 score matrix per (b, h);
+//   cube_mean   one wavefront per (b, h, cube): fp32 mean over valid rows;
+//   block_score 32x32 tiles of the fp32 score matrix per (b, h) on the
+//               fp32 matrix cores;
 //   topk_rows   one wavefront per score row: exact k-th largest key by a
 //               32-step bitwise search over order-preserving uint32 keys,
 //               then an index-ordered compaction with ballots (no atomics,
@@ -20,72 +21,80 @@ namespace vsa {
 
 namespace {
 
-// Mean of each cube over its valid rows: qc [B, H, Np, D] bf16 -> [B, H, Nc, D] fp32.
+// Mean of each cube over its valid rows: xc [B, H, Np, D] bf16 -> [B, H, Nc, D] fp32.
+// One wavefront per (b, h, cube), four cubes per workgroup.  Lane L reads the
+// 16-byte chunk L % (D/8) of rows L / (D/8), + 64/(D/8), ... (fully coalesced
+// 1 KB per instruction), keeps 8 fp32 partial sums, and the row groups are
+// folded with cross-lane exchanges.
 template <int D>
 __global__ void __launch_bounds__(256) cube_mean(const uint16_t* __restrict__ xc, float* __restrict__ mean,
-                                                 KGeom g) {
-  constexpr int RG = 256 / D;  // row groups
-  __shared__ float part[RG][D];
-  const int c = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+                                                 KGeom g, long long ncubes_total) {
+  constexpr int CH = D / 8;         // lanes per row
+  constexpr int RPI = 64 / CH;      // rows per load
+  const long long cube_id = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (cube_id >= ncubes_total) return;  // whole wavefront leaves together
+  const int lane = threadIdx.x & 63;
+  const int c = (int)(cube_id % g.nc);
   int ct, cy, cx;
   cube_coords(g, c, ct, cy, cx);
-  const int d = threadIdx.x % D, rg = threadIdx.x / D;
-  const uint16_t* base = xc + (((long long)b * g.H + h) * g.Np + 64LL * c) * D;
-  float acc = 0.f;
-  for (int l = rg; l < 64; l += RG) {
-    if (local_valid(g, ct, cy, cx, l)) acc += bf16_to_f32(base[l * D + d]);
-  }
-  part[rg][d] = acc;
-  __syncthreads();
-  if (rg == 0) {
-    float s = part[0][d];
+  const uint4* base = reinterpret_cast<const uint4*>(xc + cube_id * 64 * D);
+  float acc[8] = {};
 #pragma unroll
-    for (int r = 1; r < RG; ++r) s += part[r][d];
-    const float n = (float)cube_count(g, ct, cy, cx);
-    mean[(((long long)b * g.H + h) * g.nc + c) * D + d] = s / n;
+  for (int it = 0; it < 64 / RPI; ++it) {
+    const int row = it * RPI + lane / CH;
+    const uint4 v = base[it * 64 + lane];
+    if (local_valid(g, ct, cy, cx, row)) {
+      const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        acc[2 * e] += __uint_as_float(w4[e] << 16);
+        acc[2 * e + 1] += __uint_as_float(w4[e] & 0xFFFF0000u);
+      }
+    }
+  }
+#pragma unroll
+  for (int off = CH; off < 64; off *= 2)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] += __shfl_xor(acc[e], off);
+  if (lane < CH) {
+    const float inv_n = 1.f / (float)cube_count(g, ct, cy, cx);
+    float4* dst = reinterpret_cast<float4*>(mean + cube_id * D + lane * 8);
+    dst[0] = make_float4(acc[0] * inv_n, acc[1] * inv_n, acc[2] * inv_n, acc[3] * inv_n);
+    dst[1] = make_float4(acc[4] * inv_n, acc[5] * inv_n, acc[6] * inv_n, acc[7] * inv_n);
   }
 }
 
-// scores[bh, i, j] = sum_d qbar[bh, i, d] * kbar[bh, j, d]  (fp32).
-// 64x64 output tile per workgroup, 256 threads x (4x4) outputs, D in chunks of 32.
-__global__ void __launch_bounds__(256) block_score(const float* __restrict__ qbar, const float* __restrict__ kbar,
-                                                   float* __restrict__ scores, int nc, int D) {
-  __shared__ float qs[32][64 + 1];
-  __shared__ float ks[32][64 + 1];
+// scores[bh, i, j] = sum_d qbar[bh, i, d] * kbar[bh, j, d] in fp32 on the
+// matrix cores (v_mfma_f32_32x32x2_f32: fp32 products are exact, sums are
+// fp32).  One wavefront per 32 x 32 output tile.  The contraction order over
+// d is permuted identically for both operands so that each lane reads four
+// consecutive floats: MFMA u of group t takes d = 8t + 4 h + u on lane half h.
+__global__ void __launch_bounds__(64) block_score(const float* __restrict__ qbar, const float* __restrict__ kbar,
+                                                  float* __restrict__ scores, int nc, int D) {
   const long long bh = blockIdx.z;
-  const int i0 = blockIdx.y * 64, j0 = blockIdx.x * 64;
-  const int tx = threadIdx.x % 16, ty = threadIdx.x / 16;
-  const float* qb = qbar + bh * nc * D;
-  const float* kb = kbar + bh * nc * D;
-  float acc[4][4] = {};
-  for (int d0 = 0; d0 < D; d0 += 32) {
-    for (int f = threadIdx.x; f < 64 * 32; f += 256) {
-      const int r = f / 32, dd = f % 32;
-      qs[dd][r] = (i0 + r < nc) ? qb[(long long)(i0 + r) * D + d0 + dd] : 0.f;
-      ks[dd][r] = (j0 + r < nc) ? kb[(long long)(j0 + r) * D + d0 + dd] : 0.f;
-    }
-    __syncthreads();
-#pragma unroll 4
-    for (int dd = 0; dd < 32; ++dd) {
-      float a[4], bb[4];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        a[u] = qs[dd][ty * 4 + u];
-        bb[u] = ks[dd][tx * 4 + u];
-      }
-#pragma unroll
-      for (int u = 0; u < 4; ++u)
-#pragma unroll
-        for (int v = 0; v < 4; ++v) acc[u][v] = fmaf(a[u], bb[v], acc[u][v]);
-    }
-    __syncthreads();
+  const int i0 = blockIdx.y * 32, j0 = blockIdx.x * 32;
+  const int lane = threadIdx.x, h = lane >> 5, m = lane & 31;
+  const float* qrow = qbar + (bh * nc + min(i0 + m, nc - 1)) * D;
+  const float* krow = kbar + (bh * nc + min(j0 + m, nc - 1)) * D;
+  const bool qin = i0 + m < nc, kin = j0 + m < nc;
+  f32x16 acc = f32x16{};
+  for (int t = 0; t < D / 8; ++t) {
+    float4 a = *reinterpret_cast<const float4*>(qrow + 8 * t + 4 * h);
+    float4 b = *reinterpret_cast<const float4*>(krow + 8 * t + 4 * h);
+    if (!qin) a = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (!kin) b = make_float4(0.f, 0.f, 0.f, 0.f);
+    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a.x, b.x, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a.y, b.y, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a.z, b.z, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a.w, b.w, acc, 0, 0, 0);
   }
-  for (int u = 0; u < 4; ++u) {
-    const int i = i0 + ty * 4 + u;
-    if (i >= nc) continue;
-    for (int v = 0; v < 4; ++v) {
-      const int j = j0 + tx * 4 + v;
-      if (j < nc) scores[(bh * nc + i) * nc + j] = acc[u][v];
+  // acc[r]: row i0 + 8 (r/4) + 4 h + r%4, column j0 + m.
+  const int j = j0 + m;
+  if (j < nc) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int i = i0 + 8 * (r >> 2) + 4 * h + (r & 3);
+      if (i < nc) scores[(bh * nc + i) * nc + j] = acc[r];
     }
   }
 }
@@ -167,16 +176,17 @@ hipError_t launch_select(const KGeom& g, const uint16_t* qc, const uint16_t* kc,
   float* qbar = static_cast<float*>(ws);
   float* kbar = qbar + bh * g.nc * g.D;
   float* scores = kbar + bh * g.nc * g.D;
-  const dim3 pg(g.nc, g.H, g.B);
+  const long long ncubes_total = (long long)bh * g.nc;
+  const dim3 pg((unsigned)((ncubes_total + 3) / 4));
   if (g.D == 64) {
-    hipLaunchKernelGGL(cube_mean<64>, pg, dim3(256), 0, s, qc, qbar, g);
-    hipLaunchKernelGGL(cube_mean<64>, pg, dim3(256), 0, s, kc, kbar, g);
+    hipLaunchKernelGGL(cube_mean<64>, pg, dim3(256), 0, s, qc, qbar, g, ncubes_total);
+    hipLaunchKernelGGL(cube_mean<64>, pg, dim3(256), 0, s, kc, kbar, g, ncubes_total);
   } else {
-    hipLaunchKernelGGL(cube_mean<128>, pg, dim3(256), 0, s, qc, qbar, g);
-    hipLaunchKernelGGL(cube_mean<128>, pg, dim3(256), 0, s, kc, kbar, g);
+    hipLaunchKernelGGL(cube_mean<128>, pg, dim3(256), 0, s, qc, qbar, g, ncubes_total);
+    hipLaunchKernelGGL(cube_mean<128>, pg, dim3(256), 0, s, kc, kbar, g, ncubes_total);
   }
-  const int tiles = (g.nc + 63) / 64;
-  hipLaunchKernelGGL(block_score, dim3(tiles, tiles, (unsigned)bh), dim3(256), 0, s, qbar, kbar, scores, g.nc,
+  const int tiles = (g.nc + 31) / 32;
+  hipLaunchKernelGGL(block_score, dim3(tiles, tiles, (unsigned)bh), dim3(64), 0, s, qbar, kbar, scores, g.nc,
                      g.D);
   const long long nrows = (long long)bh * g.nc;
   const int per_lane = (g.nc + 63) / 64;

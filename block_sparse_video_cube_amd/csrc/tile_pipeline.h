@@ -1,0 +1,138 @@
+// Tile pipeline shared by the block-sparse streaming kernels (fine stage and
+// linear-branch correction): gfx950 MFMA operand layouts, LDS swizzles and
+// the direct buffer->LDS loads of 64-row cube tiles.
+//
+// Operand conventions (v_mfma_f32_32x32x16_bf16, per wavefront):
+//  * A tile of K (64 keys x D, token-major) is read as the A operand of
+//    S^T = K Q^T; Q (or phi(Q)) stays in registers as the B operand.
+//  * A tile of V^T (D x 64 keys, i.e. the cube stored transposed) is read as
+//    the A operand of O^T += V^T P^T; P is the S^T accumulator itself.
+#pragma once
+
+#include "common.h"
+
+namespace vsa {
+namespace tiles {
+
+constexpr int kThreads = 256;  // four wavefronts per query cube
+
+// Wait until at most N vector-memory loads of this wavefront are in flight
+// (s_waitcnt vmcnt(N), gfx9 encoding: vmcnt in bits 3:0 and 15:14, the other
+// counters left at their maximum).  Loads complete in issue order, so this
+// waits for every direct-to-LDS tile load except the N most recent ones.  The
+// workgroup fence of __syncthreads() treats those loads as loads and does not
+// wait for them by itself.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt field");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
+}
+
+// Workgroup barrier of the tile pipeline.  Every wavefront has already waited
+// (wait_vmcnt) for its share of the tiles that the next step reads, so after
+// the barrier those tiles are complete in LDS; its own LDS reads have
+// completed (lgkmcnt(0)), so the buffers the next loads overwrite are free.
+// A plain s_barrier is used instead of __syncthreads(): the release fence of
+// the latter would also wait for the tile loads still in flight.
+__device__ __forceinline__ void pipeline_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+}
+
+// Key row loaded by A-operand lane row m (0..31) of a 32-key tile.  With it,
+// accumulator register r of lane half hf holds key 16*(r/8) + 8*hf + r%8.
+__device__ __forceinline__ int pi_row(int m) {
+  const int gq = m >> 3, hq = (m >> 2) & 1, rr = m & 3;
+  return 16 * (gq >> 1) + 8 * hq + 4 * (gq & 1) + rr;
+}
+
+// 16-byte chunk swizzles.
+template <int D>
+__device__ __forceinline__ int k_swz(int row) {
+  return (D == 128) ? (row & 15) : ((row >> 1) & 7);
+}
+__device__ __forceinline__ int v_swz(int row) { return (row >> 1) & 7; }
+
+// Per-lane byte offsets of this wave's share of one K tile and one V^T tile.
+// Every buffer_load_dwordx4 ... lds writes 64 consecutive 16-byte LDS slots;
+// lane L fills slot L with the global chunk that the swizzle maps there.
+template <int D>
+struct TileOffsets {
+  static constexpr int KRPI = 512 / D;  // K rows per 1 KB instruction
+  static constexpr int NI = D / 32;     // instructions per wave per tile
+  uint32_t k[NI], v[NI];
+  __device__ __forceinline__ TileOffsets(int w, int lane) {
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int row = (w * NI + i) * KRPI + lane / (D / 8);
+      k[i] = (uint32_t)(row * D + ((lane % (D / 8)) ^ k_swz<D>(row)) * 8) * 2u;
+      const int vrow = (w * NI + i) * 8 + (lane >> 3);
+      v[i] = (uint32_t)(vrow * 64 + ((lane & 7) ^ v_swz(vrow)) * 8) * 2u;
+    }
+  }
+};
+
+// Issue the direct-to-LDS loads of one K tile or one V^T tile (this wave's
+// share).  The buffer resource covers exactly one tile, so every load is
+// range-checked by the hardware.
+template <int D>
+__device__ __forceinline__ void load_k_tile(const uint16_t* ktile, uint16_t* klds, int w, const TileOffsets<D>& off) {
+  constexpr int KRPI = TileOffsets<D>::KRPI, NI = TileOffsets<D>::NI;
+  const __amdgpu_buffer_rsrc_t kr = make_rsrc(ktile, 64 * D * 2);
+#pragma unroll
+  for (int i = 0; i < NI; ++i)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, (lds_ptr_t)(klds + (w * NI + i) * KRPI * D), 16, off.k[i], 0, 0, 0);
+}
+
+template <int D>
+__device__ __forceinline__ void load_v_tile(const uint16_t* vtile, uint16_t* vlds, int w, const TileOffsets<D>& off) {
+  constexpr int NI = TileOffsets<D>::NI;
+  const __amdgpu_buffer_rsrc_t vr = make_rsrc(vtile, 64 * D * 2);
+#pragma unroll
+  for (int i = 0; i < NI; ++i)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (lds_ptr_t)(vlds + (w * NI + i) * 8 * 64), 16, off.v[i], 0, 0, 0);
+}
+
+// K fragments of S^T = K Q^T for this wave's key half (rows in pi order).
+template <int D>
+__device__ __forceinline__ void read_k(const uint16_t* klds, int wk, int hf, int prow, bf16x8 (&ka)[D / 16]) {
+  const int krow = 32 * wk + prow;
+#pragma unroll
+  for (int dc = 0; dc < D / 16; ++dc)
+    ka[dc] = *reinterpret_cast<const bf16x8*>(klds + krow * D + (((2 * dc + hf) ^ k_swz<D>(krow)) * 8));
+}
+
+// V^T fragments of O^T += V^T P^T for this wave's 32 keys (2 chunks of 16).
+template <int D>
+__device__ __forceinline__ void read_v(const uint16_t* vlds, int wk, int hf, int n, bf16x8 (&va)[D / 32][2]) {
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt) {
+    const int vrow = 32 * dt + n;
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      const int chunk = 4 * wk + 2 * kk + hf;
+      va[dt][kk] = *reinterpret_cast<const bf16x8*>(vlds + vrow * 64 + ((chunk ^ v_swz(vrow)) * 8));
+    }
+  }
+}
+
+// XCD-aware placement: workgroups are handed to the 8 XCDs round-robin, so
+// XCD x receives ids x, x+8, ...  Map them so that each XCD walks a
+// contiguous range of query cubes of the current head: neighbouring query
+// cubes tend to select the same key cubes, which then stay in that XCD's L2,
+// while all XCDs together stay within one or two heads.  Returns false for
+// the few ids past the last cube (the whole workgroup then leaves).
+__device__ __forceinline__ bool map_workgroup(const KGeom& g, int& i, int& h, int& b) {
+  const int R = (g.nc + 7) >> 3;  // query cubes per XCD and head
+  const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+  const int bhi = slot / R;
+  i = xcd * R + (slot - bhi * R);
+  h = bhi % g.H;
+  b = bhi / g.H;
+  return i < g.nc;
+}
+
+inline unsigned grid_size(const KGeom& g) { return (unsigned)(8 * ((g.nc + 7) / 8) * g.H * g.B); }
+
+}  // namespace tiles
+}  // namespace vsa
