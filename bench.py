@@ -44,7 +44,21 @@ def parse():
     ap.add_argument("--workload", default="wan1.3b")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target oracle sample time")
+    ap.add_argument("--copy-bytes", type=int, default=0,
+                    help="only run a plain device-to-device copy of this many bytes (3 times) and exit; "
+                         "used to calibrate the FETCH_SIZE / WRITE_SIZE counters")
     return ap.parse_args()
+
+
+def copy_calibration(nbytes: int) -> None:
+    import torch
+
+    src = torch.ones(nbytes // 2, dtype=torch.int16, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": src.numel() * 2, "copies": 3}))
 
 
 def kernel_source_hash() -> str:
@@ -54,7 +68,7 @@ def kernel_source_hash() -> str:
 
 def measured_traffic(workload: str):
     """HBM bytes per fine-stage launch from committed rocprofv3 counters, if current."""
-    path = os.path.join(ROOT, "profiles", f"attn_fwd_{workload}_traffic.json")
+    path = os.path.join(ROOT, "profiles", f"attn_fwd_{workload}_traffic.txt")
     if not os.path.exists(path):
         return None
     rec = json.load(open(path))
@@ -76,12 +90,8 @@ def cpu_baseline(wl, budget_s: float):
         threads = 1
     valid = oracle.valid_rows(wl.grid)
     scale = wl.softmax_scale
-    t_total = 0.0
-    heads_done = 0
     cubes_done = 0
     n_heads = wl.batch * wl.heads
-    per_head_fixed = 0.0
-    per_cube = 0.0
     # One head: permute + pool + score + top-k of all rows (fixed per head),
     # then query cubes one by one until the time budget is spent.
     b, h = 0, 0
@@ -118,6 +128,9 @@ def cpu_baseline(wl, budget_s: float):
 
 def main():
     args = parse()
+    if args.copy_bytes:
+        copy_calibration(args.copy_bytes)
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (--gpus {args.gpus} requested): every step of the "
               "layer is independent per (batch, head), so several GPUs would each run this same "

@@ -140,12 +140,12 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd(const uint16_t* __restri
                                                         const int32_t* __restrict__ idx, int topk, float scale,
                                                         float scale_log2, uint16_t* __restrict__ oc,
                                                         float* __restrict__ oc_f32, float* __restrict__ lse,
-                                                        KGeom g) {
+                                                        KGeom g, Placement pl) {
   constexpr int DC = D / 16, DT = D / 32;
   __shared__ __attribute__((aligned(16))) Smem<D> sm;
 
   int i, h, b;
-  if (!map_workgroup(g, i, h, b)) return;  // whole workgroup leaves before any barrier
+  if (!map_workgroup(g, pl, i, h, b)) return;  // whole workgroup leaves before any barrier
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wq = w & 1, wk = w >> 1;  // wave-uniform
@@ -273,14 +273,15 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd(const uint16_t* __restri
 hipError_t launch_attn_fwd(const KGeom& g, const uint16_t* qc, const uint16_t* kc, const uint16_t* vt,
                            const int32_t* idx, int topk, float scale, uint16_t* oc, float* oc_f32, float* lse,
                            hipStream_t s) {
+  const Placement pl = make_placement(g);
   const dim3 grid(grid_size(g));
   const float scale_log2 = scale * 1.4426950408889634f;
   if (g.D == 64)
     hipLaunchKernelGGL(attn_fwd<64>, grid, dim3(kThreads), 0, s, qc, kc, vt, idx, topk, scale, scale_log2, oc,
-                       oc_f32, lse, g);
+                       oc_f32, lse, g, pl);
   else
     hipLaunchKernelGGL(attn_fwd<128>, grid, dim3(kThreads), 0, s, qc, kc, vt, idx, topk, scale, scale_log2, oc,
-                       oc_f32, lse, g);
+                       oc_f32, lse, g, pl);
   return hipGetLastError();
 }
 

@@ -191,11 +191,12 @@ __global__ void __launch_bounds__(kThreads, 2) lin_apply(const uint16_t* __restr
                                                          const uint16_t* __restrict__ vt,
                                                          const int32_t* __restrict__ idx, int topk,
                                                          const float* __restrict__ o_sparse,
-                                                         uint16_t* __restrict__ oc, LinWs ws, KGeom g) {
+                                                         uint16_t* __restrict__ oc, LinWs ws, KGeom g,
+                                                         Placement pl) {
   constexpr int DC = D / 16, DT = D / 32;
   __shared__ __attribute__((aligned(16))) LinSmem<D> sm;
   int i, h, b;
-  if (!map_workgroup(g, i, h, b)) return;  // whole workgroup leaves before any barrier
+  if (!map_workgroup(g, pl, i, h, b)) return;  // whole workgroup leaves before any barrier
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wq = w & 1, wk = w >> 1;
@@ -350,12 +351,12 @@ hipError_t launch_linear(const KGeom& g, const uint16_t* qc, const uint16_t* kc,
     hipLaunchKernelGGL(lin_state<64>, dim3(G, g.H, g.B), dim3(256), 0, s, kc, vt, w, g);
     hipLaunchKernelGGL(lin_reduce<64>, dim3(64 * 64 / 256, bh), dim3(256), 0, s, w, g);
     hipLaunchKernelGGL(lin_apply<64>, dim3(grid_size(g)), dim3(kThreads), 0, s, qc, vt, idx, topk, o_sparse, oc,
-                       w, g);
+                       w, g, make_placement(g));
   } else {
     hipLaunchKernelGGL(lin_state<128>, dim3(G, g.H, g.B), dim3(256), 0, s, kc, vt, w, g);
     hipLaunchKernelGGL(lin_reduce<128>, dim3(128 * 128 / 256, bh), dim3(256), 0, s, w, g);
     hipLaunchKernelGGL(lin_apply<128>, dim3(grid_size(g)), dim3(kThreads), 0, s, qc, vt, idx, topk, o_sparse, oc,
-                       w, g);
+                       w, g, make_placement(g));
   }
   return hipGetLastError();
 }

@@ -116,23 +116,52 @@ __device__ __forceinline__ void read_v(const uint16_t* vlds, int wk, int hf, int
   }
 }
 
-// XCD-aware placement: workgroups are handed to the 8 XCDs round-robin, so
-// XCD x receives ids x, x+8, ...  Map them so that each XCD walks a
-// contiguous range of query cubes of the current head: neighbouring query
-// cubes tend to select the same key cubes, which then stay in that XCD's L2,
-// while all XCDs together stay within one or two heads.  Returns false for
-// the few ids past the last cube (the whole workgroup then leaves).
-__device__ __forceinline__ bool map_workgroup(const KGeom& g, int& i, int& h, int& b) {
-  const int R = (g.nc + 7) >> 3;  // query cubes per XCD and head
+// XCD-aware placement.  Workgroups are handed to the 8 XCDs round-robin, so
+// XCD x receives ids x, x+8, x+16, ...  Every workgroup visits its selected
+// key cubes in ascending order and all carry the same work, so workgroups
+// that run together sweep the key range together and share the tiles in
+// their XCD's L2 while they pass.  To keep the workgroups that run together
+// on one XCD inside a single head, each (b, h) is cut into `splits` ranges
+// of consecutive query cubes (the fewest that make the number of ranges a
+// multiple of 8, so the XCDs stay balanced), and XCD x takes ranges
+// x, x+8, ... one after the other.
+struct Placement {
+  int splits;      // query-cube ranges per (b, h)
+  int range_len;   // query cubes per range
+  int ranges;      // B * H * splits
+  int per_xcd;     // ranges per XCD
+};
+
+inline Placement make_placement(const KGeom& g) {
+  Placement p;
+  const int bh = g.B * g.H;
+  int s = 1;
+  while ((bh * s) % 8 != 0 && s < 8 && (g.nc + s) / (s + 1) >= 64) ++s;
+  p.splits = s;
+  p.range_len = (g.nc + s - 1) / s;
+  p.ranges = bh * s;
+  p.per_xcd = (p.ranges + 7) / 8;
+  return p;
+}
+
+inline unsigned grid_size(const KGeom& g) {
+  const Placement p = make_placement(g);
+  return (unsigned)(8 * p.per_xcd * p.range_len);
+}
+
+// Query cube i and head (h, b) of this workgroup; false for the ids past the
+// end (the whole workgroup then leaves before any barrier).
+__device__ __forceinline__ bool map_workgroup(const KGeom& g, const Placement& p, int& i, int& h, int& b) {
   const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
-  const int bhi = slot / R;
-  i = xcd * R + (slot - bhi * R);
+  const int rk = slot / p.range_len;          // k-th range of this XCD
+  const int range = xcd + 8 * rk;             // global range index
+  if (range >= p.ranges) return false;
+  const int bhi = range / p.splits, sp = range - bhi * p.splits;
+  i = sp * p.range_len + (slot - rk * p.range_len);
   h = bhi % g.H;
   b = bhi / g.H;
   return i < g.nc;
 }
-
-inline unsigned grid_size(const KGeom& g) { return (unsigned)(8 * ((g.nc + 7) / 8) * g.H * g.B); }
 
 }  // namespace tiles
 }  // namespace vsa
