@@ -3,8 +3,9 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload wan1.3b]
 
 A step is one pass of the whole layer on inputs already resident in HBM:
-permute Q, K, V -> coarse stage (pool, score, top-k) -> fine block-sparse
-attention -> (linear branch, hybrid workload) -> unpermute.  The default
+permute Q, K, V (cube means of Q and K pooled in the same pass) -> coarse
+stage (block scores, top-k) -> fine block-sparse attention -> (linear
+branch, hybrid workload) -> unpermute.  The default
 workload is the Wan2.1-1.3B-shaped layer (latent 16x28x52, 12 heads,
 head_dim 128, sparsity 0.8 -> k = 73 of 364 cubes).
 
@@ -158,6 +159,8 @@ def main():
     d = vsa.geom_dims(g)
     B, H, D = wl.batch, wl.heads, wl.head_dim
     qc = torch.empty((B, H, d.rows, D), dtype=torch.bfloat16, device=dev)
+    qbar = torch.empty((B, H, d.n_cubes, D), dtype=torch.float32, device=dev)
+    kbar = torch.empty_like(qbar)
     kc = torch.empty_like(qc)
     vt = torch.empty((B, H, d.n_cubes, D, 64), dtype=torch.bfloat16, device=dev)
     oc = torch.empty_like(qc)
@@ -178,11 +181,11 @@ def main():
                 ev[i].record()
 
         mark(0)
-        vsa.cube_permute(q, wl.grid, out=qc)
-        vsa.cube_permute(k, wl.grid, out=kc)
+        vsa.cube_permute_pool(q, wl.grid, out=qc, mean_out=qbar)
+        vsa.cube_permute_pool(k, wl.grid, out=kc, mean_out=kbar)
         vsa.cube_permute(v, wl.grid, layout="dim", out=vt)
         mark(1)
-        vsa.select_topk(qc, kc, wl.grid, wl.topk, out=idx, workspace=ws_sel)
+        vsa.select_topk_pooled(qbar, kbar, wl.grid, wl.topk, out=idx, workspace=ws_sel)
         mark(2)
         vsa.sparse_attn_fwd(qc, kc, vt, idx, wl.grid, wl.softmax_scale, out=oc, out_f32=of)
         mark(3)

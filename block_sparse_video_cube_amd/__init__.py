@@ -8,10 +8,10 @@ calls raise.
 
 Steps of one attention layer (q, k, v: [B, S, heads, D] bf16 on the GPU):
 
-    qc = cube_permute(q, grid)                  # cube-major rows
-    kc = cube_permute(k, grid)
+    qc, qbar = cube_permute_pool(q, grid)       # cube-major rows + cube means
+    kc, kbar = cube_permute_pool(k, grid)
     vt = cube_permute(v, grid, layout="dim")    # cubes stored transposed
-    idx = select_topk(qc, kc, grid, topk)       # pooled scores -> top-k
+    idx = select_topk_pooled(qbar, kbar, grid, topk)  # block scores -> top-k
     oc, of, _ = sparse_attn_fwd(qc, kc, vt, idx, grid, scale, want_f32=linear)
     if linear:
         oc = linear_branch(qc, kc, vt, idx, of, grid)
@@ -35,8 +35,10 @@ __all__ = [
     "make_geom",
     "geom_dims",
     "cube_permute",
+    "cube_permute_pool",
     "cube_unpermute",
     "select_topk",
+    "select_topk_pooled",
     "sparse_attn_fwd",
     "linear_branch",
     "vsa_attention",
@@ -94,6 +96,24 @@ def cube_permute(x: torch.Tensor, grid: Sequence[int], layout: str = "token",
     return out
 
 
+def cube_permute_pool(x: torch.Tensor, grid: Sequence[int], out: Optional[torch.Tensor] = None,
+                      mean_out: Optional[torch.Tensor] = None):
+    """Token-major cube permutation and fp32 cube means in one pass: (xc, mean [B, heads, Nc, D])."""
+    B, S, Hh, D = x.shape
+    g = make_geom(B, Hh, D, grid)
+    d = geom_dims(g)
+    _need(x, "x", torch.bfloat16, (B, d.tokens, Hh, D))
+    if out is None:
+        out = torch.empty((B, Hh, d.rows, D), dtype=torch.bfloat16, device=x.device)
+    if mean_out is None:
+        mean_out = torch.empty((B, Hh, d.n_cubes, D), dtype=torch.float32, device=x.device)
+    _need(out, "out", torch.bfloat16, (B, Hh, d.rows, D))
+    _need(mean_out, "mean", torch.float32, (B, Hh, d.n_cubes, D))
+    _lib.check("vsa_cube_permute_pool", _lib.load().vsa_cube_permute_pool(
+        g, x.data_ptr(), out.data_ptr(), mean_out.data_ptr(), _stream()))
+    return out, mean_out
+
+
 def cube_unpermute(xc: torch.Tensor, grid: Sequence[int], out: Optional[torch.Tensor] = None) -> torch.Tensor:
     """[B, heads, Np, D] token-major -> [B, S, heads, D]."""
     B, Hh, Np, D = xc.shape
@@ -124,6 +144,26 @@ def select_topk(qc: torch.Tensor, kc: torch.Tensor, grid: Sequence[int], topk: i
         workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=qc.device)
     _lib.check("vsa_select_topk", _lib.load().vsa_select_topk(
         g, qc.data_ptr(), kc.data_ptr(), int(topk), out.data_ptr(), workspace.data_ptr(),
+        workspace.numel() * workspace.element_size(), _stream()))
+    return out
+
+
+def select_topk_pooled(qbar: torch.Tensor, kbar: torch.Tensor, grid: Sequence[int], topk: int,
+                       out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Block index list from precomputed fp32 cube means (see cube_permute_pool)."""
+    B, Hh, nc, D = qbar.shape
+    g = make_geom(B, Hh, D, grid)
+    d = geom_dims(g)
+    _need(qbar, "qbar", torch.float32, (B, Hh, d.n_cubes, D))
+    _need(kbar, "kbar", torch.float32, (B, Hh, d.n_cubes, D))
+    if out is None:
+        out = torch.empty((B, Hh, d.n_cubes, int(topk)), dtype=torch.int32, device=qbar.device)
+    _need(out, "idx", torch.int32, (B, Hh, d.n_cubes, int(topk)))
+    nbytes = workspace_bytes(g)
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=qbar.device)
+    _lib.check("vsa_select_topk_pooled", _lib.load().vsa_select_topk_pooled(
+        g, qbar.data_ptr(), kbar.data_ptr(), int(topk), out.data_ptr(), workspace.data_ptr(),
         workspace.numel() * workspace.element_size(), _stream()))
     return out
 
@@ -193,11 +233,11 @@ def vsa_attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, grid: Seque
 
     idx: optional block list to use instead of the coarse-stage selection.
     """
-    qc = cube_permute(q, grid)
-    kc = cube_permute(k, grid)
+    qc, qbar = cube_permute_pool(q, grid)
+    kc, kbar = cube_permute_pool(k, grid)
     vt = cube_permute(v, grid, layout="dim")
     if idx is None:
-        idx = select_topk(qc, kc, grid, topk)
+        idx = select_topk_pooled(qbar, kbar, grid, topk)
     oc, of, _ = sparse_attn_fwd(qc, kc, vt, idx, grid, scale, want_f32=linear)
     if linear:
         oc = linear_branch(qc, kc, vt, idx, of, grid)

@@ -30,8 +30,10 @@ ENTRY_POINTS = (
     "vsa_select_workspace_bytes",
     "vsa_linear_workspace_bytes",
     "vsa_cube_permute",
+    "vsa_cube_permute_pool",
     "vsa_cube_unpermute",
     "vsa_select_topk",
+    "vsa_select_topk_pooled",
     "vsa_sparse_attn_fwd",
     "vsa_linear_branch",
 )
@@ -93,6 +95,8 @@ def load() -> ctypes.CDLL:
         "vsa_select_workspace_bytes": (sz, [G]),
         "vsa_linear_workspace_bytes": (sz, [G]),
         "vsa_cube_permute": (i32, [G, P, P, i32, P]),
+        "vsa_cube_permute_pool": (i32, [G, P, P, P, P]),
+        "vsa_select_topk_pooled": (i32, [G, P, P, i32, P, P, sz, P]),
         "vsa_cube_unpermute": (i32, [G, P, P, P]),
         "vsa_select_topk": (i32, [G, P, P, i32, P, P, sz, P]),
         "vsa_sparse_attn_fwd": (i32, [G, P, P, P, P, i32, ctypes.c_float, P, P, P, P]),

@@ -112,6 +112,31 @@ int32_t vsa_cube_permute(const vsa_geom* g, const uint16_t* x, uint16_t* xc, int
   return launch_status(vsa::launch_permute(k, x, xc, layout, static_cast<hipStream_t>(stream)));
 }
 
+int32_t vsa_cube_permute_pool(const vsa_geom* g, const uint16_t* x, uint16_t* xc, float* mean, void* stream) {
+  vsa_dims d;
+  vsa::KGeom k;
+  int32_t st = prepare(g, &d, &k);
+  if (st != VSA_OK) return st;
+  if (!x || !xc || !mean) return VSA_ERR_NULL;
+  if (!aligned16(x) || !aligned16(xc) || !aligned16(mean)) return VSA_ERR_ALIGN;
+  return launch_status(vsa::launch_permute_pool(k, x, xc, mean, static_cast<hipStream_t>(stream)));
+}
+
+int32_t vsa_select_topk_pooled(const vsa_geom* g, const float* qbar, const float* kbar, int32_t topk,
+                               int32_t* idx, void* ws, size_t ws_bytes, void* stream) {
+  vsa_dims d;
+  vsa::KGeom k;
+  int32_t st = prepare(g, &d, &k);
+  if (st != VSA_OK) return st;
+  if (d.n_cubes > VSA_MAX_CUBES) return VSA_ERR_GEOMETRY;
+  if (!qbar || !kbar || !idx || !ws) return VSA_ERR_NULL;
+  if (!aligned16(qbar) || !aligned16(kbar) || !aligned16(idx) || !aligned16(ws)) return VSA_ERR_ALIGN;
+  if (topk < 1 || topk > d.n_cubes) return VSA_ERR_TOPK;
+  if (ws_bytes < vsa::select_pooled_workspace_bytes(k)) return VSA_ERR_WORKSPACE;
+  return launch_status(vsa::launch_select_pooled(k, qbar, kbar, topk, idx, static_cast<float*>(ws),
+                                                 static_cast<hipStream_t>(stream)));
+}
+
 int32_t vsa_cube_unpermute(const vsa_geom* g, const uint16_t* xc, uint16_t* x, void* stream) {
   vsa_dims d;
   vsa::KGeom k;

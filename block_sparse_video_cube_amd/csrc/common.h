@@ -78,10 +78,14 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 // Host launchers (each returns hipSuccess or the launch error).
 namespace vsa {
 hipError_t launch_permute(const KGeom& g, const uint16_t* x, uint16_t* xc, int layout, hipStream_t s);
+hipError_t launch_permute_pool(const KGeom& g, const uint16_t* x, uint16_t* xc, float* mean, hipStream_t s);
 hipError_t launch_unpermute(const KGeom& g, const uint16_t* xc, uint16_t* x, hipStream_t s);
 hipError_t launch_select(const KGeom& g, const uint16_t* qc, const uint16_t* kc, int topk, int32_t* idx,
                          void* ws, hipStream_t s);
 size_t select_workspace_bytes(const KGeom& g);
+hipError_t launch_select_pooled(const KGeom& g, const float* qbar, const float* kbar, int topk, int32_t* idx,
+                                float* scores, hipStream_t s);
+size_t select_pooled_workspace_bytes(const KGeom& g);
 hipError_t launch_attn_fwd(const KGeom& g, const uint16_t* qc, const uint16_t* kc, const uint16_t* vt,
                            const int32_t* idx, int topk, float scale, uint16_t* oc, float* oc_f32, float* lse,
                            hipStream_t s);

@@ -38,6 +38,56 @@ __global__ void __launch_bounds__(kThreads) permute_token_major(const uint16_t* 
   }
 }
 
+// [B, S, H, D] -> [B, H, Np, D] as permute_token_major, and in the same pass
+// the fp32 mean of every cube over its valid tokens -> mean [B, H, Nc, D].
+// Thread t always handles 16-byte chunk t % (D/8) of its rows, so it keeps 8
+// partial sums; threads with equal chunk are folded by cross-lane exchanges
+// inside a wavefront and through LDS across the four wavefronts.
+template <int D>
+__global__ void __launch_bounds__(kThreads) permute_pool(const uint16_t* __restrict__ x, uint16_t* __restrict__ xc,
+                                                         float* __restrict__ mean, KGeom g) {
+  constexpr int CH = D / 8;
+  __shared__ float part[kThreads / 64][D];
+  const int c = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  int ct, cy, cx;
+  cube_coords(g, c, ct, cy, cx);
+  const long long cube_row = ((long long)b * g.H + h) * g.Np + 64LL * c;
+  uint4* out = reinterpret_cast<uint4*>(xc + cube_row * D);
+  float acc[8] = {};
+  for (int f = threadIdx.x; f < 64 * CH; f += kThreads) {
+    const int l = f / CH, ch = f % CH;
+    const int t = 4 * ct + (l >> 4), y = 4 * cy + ((l >> 2) & 3), xx = 4 * cx + (l & 3);
+    uint4 val = make_uint4(0, 0, 0, 0);
+    if (t < g.T && y < g.Hg && xx < g.W) {
+      const long long s = ((long long)t * g.Hg + y) * g.W + xx;
+      val = reinterpret_cast<const uint4*>(x + (((long long)b * g.S + s) * g.H + h) * D)[ch];
+      const uint32_t w4[4] = {val.x, val.y, val.z, val.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        acc[2 * e] += __uint_as_float(w4[e] << 16);
+        acc[2 * e + 1] += __uint_as_float(w4[e] & 0xFFFF0000u);
+      }
+    }
+    out[f] = val;
+  }
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+#pragma unroll
+  for (int off = CH; off < 64; off *= 2)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] += __shfl_xor(acc[e], off);
+  if (lane < CH) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) part[w][lane * 8 + e] = acc[e];
+  }
+  __syncthreads();
+  if (threadIdx.x < D) {
+    float sum = 0.f;
+#pragma unroll
+    for (int r = 0; r < kThreads / 64; ++r) sum += part[r][threadIdx.x];
+    mean[(((long long)b * g.H + h) * g.nc + c) * D + threadIdx.x] = sum / (float)cube_count(g, ct, cy, cx);
+  }
+}
+
 // [B, S, H, D] -> [B, H, Nc, D, 64]: each cube stored transposed (d-major).
 template <int D>
 __global__ void __launch_bounds__(kThreads) permute_dim_major(const uint16_t* __restrict__ x,
@@ -107,6 +157,15 @@ hipError_t launch_permute(const KGeom& g, const uint16_t* x, uint16_t* xc, int l
     else
       hipLaunchKernelGGL(permute_dim_major<128>, grid, dim3(kThreads), 0, s, x, xc, g);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_permute_pool(const KGeom& g, const uint16_t* x, uint16_t* xc, float* mean, hipStream_t s) {
+  const dim3 grid(g.nc, g.H, g.B);
+  if (g.D == 64)
+    hipLaunchKernelGGL(permute_pool<64>, grid, dim3(kThreads), 0, s, x, xc, mean, g);
+  else
+    hipLaunchKernelGGL(permute_pool<128>, grid, dim3(kThreads), 0, s, x, xc, mean, g);
   return hipGetLastError();
 }
 

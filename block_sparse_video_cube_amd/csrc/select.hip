@@ -170,6 +170,9 @@ size_t select_workspace_bytes(const KGeom& g) {
   return means + scores;
 }
 
+hipError_t launch_select_pooled(const KGeom& g, const float* qbar, const float* kbar, int topk, int32_t* idx,
+                                float* scores, hipStream_t s);
+
 hipError_t launch_select(const KGeom& g, const uint16_t* qc, const uint16_t* kc, int topk, int32_t* idx,
                          void* ws, hipStream_t s) {
   const size_t bh = (size_t)g.B * g.H;
@@ -185,6 +188,16 @@ hipError_t launch_select(const KGeom& g, const uint16_t* qc, const uint16_t* kc,
     hipLaunchKernelGGL(cube_mean<128>, pg, dim3(256), 0, s, qc, qbar, g, ncubes_total);
     hipLaunchKernelGGL(cube_mean<128>, pg, dim3(256), 0, s, kc, kbar, g, ncubes_total);
   }
+  return launch_select_pooled(g, qbar, kbar, topk, idx, scores, s);
+}
+
+size_t select_pooled_workspace_bytes(const KGeom& g) {
+  return (size_t)g.B * g.H * g.nc * (size_t)g.nc * sizeof(float);
+}
+
+hipError_t launch_select_pooled(const KGeom& g, const float* qbar, const float* kbar, int topk, int32_t* idx,
+                                float* scores, hipStream_t s) {
+  const size_t bh = (size_t)g.B * g.H;
   const int tiles = (g.nc + 31) / 32;
   hipLaunchKernelGGL(block_score, dim3(tiles, tiles, (unsigned)bh), dim3(64), 0, s, qbar, kbar, scores, g.nc,
                      g.D);

@@ -119,6 +119,13 @@ size_t vsa_linear_workspace_bytes(const vsa_geom* g);
 int32_t vsa_cube_permute(const vsa_geom* g, const uint16_t* x, uint16_t* xc,
                          int32_t layout, void* stream);
 
+/* Cube permutation fused with the coarse-stage pooling (one pass over x):
+ * xc as vsa_cube_permute with TOKEN_MAJOR layout, and mean: output fp32
+ * [B, heads, Nc, D], the mean of each cube over its valid tokens (the same
+ * values vsa_select_topk computes from xc). */
+int32_t vsa_cube_permute_pool(const vsa_geom* g, const uint16_t* x, uint16_t* xc,
+                              float* mean, void* stream);
+
 /* Inverse permutation (scatter).  xc: [B, heads, Np, D] TOKEN_MAJOR bf16;
  * x: output [B, S, heads, D]; padded rows of xc are dropped. */
 int32_t vsa_cube_unpermute(const vsa_geom* g, const uint16_t* xc, uint16_t* x,
@@ -133,6 +140,13 @@ int32_t vsa_cube_unpermute(const vsa_geom* g, const uint16_t* xc, uint16_t* x,
 int32_t vsa_select_topk(const vsa_geom* g, const uint16_t* qc, const uint16_t* kc,
                         int32_t topk, int32_t* idx, void* ws, size_t ws_bytes,
                         void* stream);
+
+/* Coarse stage from precomputed cube means (qbar, kbar: fp32 [B, heads, Nc, D],
+ * e.g. from vsa_cube_permute_pool): block scores and top-k exactly as
+ * vsa_select_topk.  ws: at least vsa_select_workspace_bytes(g) bytes. */
+int32_t vsa_select_topk_pooled(const vsa_geom* g, const float* qbar, const float* kbar,
+                               int32_t topk, int32_t* idx, void* ws, size_t ws_bytes,
+                               void* stream);
 
 /* Fine stage: for every (b, h, query cube i), softmax attention of its 64
  * query rows over the valid keys of the topk key cubes idx[b, h, i, :]

@@ -124,3 +124,17 @@ def test_entry_points_reject_bad_arguments_before_launch(lib):
     assert lib.vsa_linear_branch(g, P, P, P, P, 2, None, P, P, lws, None) == _lib.VSA_ERR_NULL
     assert lib.vsa_linear_branch(g, P, P, P, P, 2, P, P, P, lws - 1, None) == _lib.VSA_ERR_WORKSPACE
     assert lib.vsa_linear_branch(g, P, P, P, P, 99, P, P, P, lws, None) == _lib.VSA_ERR_TOPK
+
+
+def test_fused_entry_points_reject_bad_arguments(lib):
+    from block_sparse_video_cube_amd import _lib
+
+    g = geom()
+    P = FAKE
+    assert lib.vsa_cube_permute_pool(g, P, P, None, None) == _lib.VSA_ERR_NULL
+    assert lib.vsa_cube_permute_pool(g, P, P, ODD, None) == _lib.VSA_ERR_ALIGN
+    assert lib.vsa_cube_permute_pool(geom(D=16), P, P, P, None) == _lib.VSA_ERR_HEAD_DIM
+    ws = lib.vsa_select_workspace_bytes(g)
+    assert lib.vsa_select_topk_pooled(g, P, None, 2, P, P, ws, None) == _lib.VSA_ERR_NULL
+    assert lib.vsa_select_topk_pooled(g, P, P, 0, P, P, ws, None) == _lib.VSA_ERR_TOPK
+    assert lib.vsa_select_topk_pooled(g, P, P, 2, P, P, 16, None) == _lib.VSA_ERR_WORKSPACE

@@ -80,3 +80,17 @@ def test_roundtrip_720p_shape_one_head():
         assert np.array_equal(xcb[64 * c + l], x[0, (t * H + y) * W + xx, 0])
     valid = oracle.valid_rows(wl.grid)
     assert np.all(xcb[~valid] == 0)
+
+
+@pytest.mark.parametrize("B,H,D,grid", CASES)
+def test_permute_pool_rows_and_means(B, H, D, grid):
+    import block_sparse_video_cube_amd as vsa
+
+    wl = workloads.workload("tiny").with_(batch=B, heads=H, head_dim=D, grid=grid)
+    inp = workloads.make_integer_inputs(wl)  # integer values: every mean is exact (power-of-two counts aside)
+    xc, mean = vsa.cube_permute_pool(to_dev(inp["q"]), grid)
+    assert np.array_equal(to_bits(xc), oracle.cube_permute(inp["q"], grid))
+    ref = oracle.cube_means(oracle.cube_permute(inp["q"], grid), oracle.valid_rows(grid))
+    got = mean.cpu().numpy().astype(np.float64)
+    # fp32 means of integer sums divided by the valid count: within one fp32 rounding.
+    assert np.abs(got - ref).max() <= 1e-6 * max(1.0, np.abs(ref).max())

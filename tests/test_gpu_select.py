@@ -92,3 +92,19 @@ def test_topk_float_inputs_near_tie_valid(grid, topk):
             assert topk_valid_under(s[0, h, i], got[0, h, i], topk)
             exact += int(np.array_equal(got[0, h, i], ref[0, h, i]))
     print(f"rows identical to the oracle: {exact}/{wl.heads * wl.n_cubes}")
+
+
+@pytest.mark.parametrize("name,grid,topk", INT_CASES)
+def test_pooled_path_matches_oracle_integer_inputs(name, grid, topk):
+    import block_sparse_video_cube_amd as vsa
+
+    wl = workloads.workload(name).with_(head_dim=128)
+    if grid is not None:
+        wl = wl.with_(grid=grid)
+    if topk is not None:
+        wl = wl.with_(topk=topk)
+    inp = workloads.make_integer_inputs(wl)
+    _, qbar = vsa.cube_permute_pool(to_dev(inp["q"]), wl.grid)
+    _, kbar = vsa.cube_permute_pool(to_dev(inp["k"]), wl.grid)
+    got = vsa.select_topk_pooled(qbar, kbar, wl.grid, wl.topk).cpu().numpy()
+    assert np.array_equal(got, oracle_select(inp, wl, wl.topk))
