@@ -48,92 +48,108 @@ struct Smem {
   uint16_t v[2][D * 64];
 };
 
-// Padded keys of a partial cube take no weight.
-__device__ __forceinline__ void mask_partial(f32x16& s, const KGeom& g, int j, int wk, int hf) {
+// Padded keys of key cube j take no weight: their logits become -inf.
+// Accumulator register r of lane half hf holds local key
+// 32 wk + 16 (r/8) + 8 hf + r%8, i.e. local (t, y, x) =
+// (2 wk + r/8, 2 hf + (r%8)/4, r%4): the t and x tests are the same for the
+// whole wavefront, the y test depends on the lane half only.  Branch-free, so
+// it sits inside the interleaved region of a step.
+__device__ __forceinline__ void mask_keys(f32x16& s, const KGeom& g, int j, int wk, int hf) {
   int ct, cy, cx;
   cube_coords(g, j, ct, cy, cx);
-  if (!cube_full(g, ct, cy, cx)) {
+  const int nt = g.T - 4 * ct, ny = g.Hg - 4 * cy, nx = g.W - 4 * cx;
+  const bool y0 = 2 * hf < ny, y1 = 2 * hf + 1 < ny;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int key = 32 * wk + 16 * (r >> 3) + 8 * hf + (r & 7);
-      if (!local_valid(g, ct, cy, cx, key)) s[r] = -INFINITY;
-    }
+  for (int r = 0; r < 16; ++r) {
+    const bool tx = (2 * wk + (r >> 3) < nt) && ((r & 3) < nx);
+    const bool ok = tx && (((r >> 2) & 1) ? y1 : y0);
+    s[r] = ok ? s[r] : -INFINITY;
   }
 }
 
-// Online-softmax statistics of one S^T tile: row max and the rare lazy
-// rescale of (m_run, l_run, O^T).  The reference max moves only when the
-// block exceeds it by more than kLazyLog2 (log2 units); since each lane
-// half's max bounds the row max from below, the rare move is decided per half
-// and only then is the row max taken across lane ^ 32.  A half that holds
-// padded keys only (max -inf) never triggers a move.
-template <int DT>
-__device__ __forceinline__ float softmax_stats(const f32x16& s, f32x16 (&o)[DT], float& m_run, float& l_run,
-                                               float scale_log2, float lazy_raw) {
-  float mx = fmaxf(s[0], s[1]);
-#pragma unroll
-  for (int r = 2; r < 16; ++r) mx = fmaxf(mx, s[r]);
-  if (__builtin_amdgcn_ballot_w64(mx > m_run + lazy_raw)) {
-    const float row_max = fmaxf(mx, __shfl_xor(mx, 32));
-    const bool grow = row_max > m_run + lazy_raw;
-    const float alpha = grow ? __builtin_amdgcn_exp2f((m_run - row_max) * scale_log2) : 1.f;
-    m_run = grow ? row_max : m_run;
-    l_run *= alpha;
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt) o[dt] *= alpha;
-  }
-  // Until a valid key has been seen every logit is -inf and p must be 0.
-  return (m_run == -INFINITY) ? 0.f : m_run * scale_log2;
+__device__ __forceinline__ float max16(const f32x16& s) {
+  const float a = fmaxf(fmaxf(s[0], s[1]), s[2]), b = fmaxf(fmaxf(s[3], s[4]), s[5]);
+  const float c = fmaxf(fmaxf(s[6], s[7]), s[8]), d = fmaxf(fmaxf(s[9], s[10]), s[11]);
+  const float e = fmaxf(fmaxf(s[12], s[13]), s[14]);
+  return fmaxf(fmaxf(fmaxf(a, b), c), fmaxf(fmaxf(d, e), s[15]));
 }
 
-// One pipelined block: S^T of the next block is computed on the matrix cores
-// while the vector units turn the current S^T into P (exp2, bf16 pack, row
-// sum); then O^T += V^T P^T.  P is rounded once to bf16 (v_cvt_pk_bf16_f32)
-// and the normaliser sums the same rounded values (v_dot2_f32_bf16 against
-// 1.0), so the weights applied to V sum exactly to the normaliser.
-// The tile loads of later blocks (V of block n+1, K of block n+3) are issued
-// one per MFMA slot here, so that neither the vector units nor the texture
-// path see bursts; vr/kr are their buffer resources, vl/kl the LDS
-// destinations of this wave's first instruction, voff/koff its lane offsets.
-template <int D>
-__device__ __forceinline__ void pipelined_step(const bf16x8 (&ka)[D / 16], const bf16x8 (&va)[D / 32][2],
-                                               const bf16x8 (&qf)[D / 16], const f32x16& s_cur, f32x16& s_next,
-                                               f32x16 (&o)[D / 32], float& l_run, float mc, float scale_log2,
-                                               __amdgpu_buffer_rsrc_t vr, uint16_t* vl, const uint32_t* voff,
-                                               __amdgpu_buffer_rsrc_t kr, uint16_t* kl, const uint32_t* koff) {
+// One pipelined step n.  Entering: S^T(n) (masked) in s_cur, P(n-1) in
+// p_prev, and mc, the exponent offset of block n after its lazy-rescale
+// decision.  The matrix cores compute S^T(n+1) = K(n+1) Q^T and
+// O^T += V(n-1)^T P(n-1)^T; interleaved with them the vector units turn S^T(n)
+// into P(n) = bf16(exp2(scale_log2 S^T(n) - mc)) and its row sum, then mask
+// S^T(n+1) and take its per-lane max.  P is rounded once to bf16
+// (v_cvt_pk_bf16_f32) and the normaliser sums the same rounded values
+// (v_dot2_f32_bf16 against 1.0), so the weights applied to V sum exactly to
+// the normaliser.  The tile loads of V(n) and K(n+3) go out one per MFMA slot
+// of S^T(n+1); vr/kr are their buffer resources, vl/kl the LDS destinations
+// of this wave's first instruction, voff/koff its lane offsets.
+template <int D, bool PARTIAL>
+__device__ __forceinline__ void step(const bf16x8 (&ka)[D / 16], const bf16x8 (&va)[D / 32][2],
+                                     const bf16x8 (&qf)[D / 16], const f32x16& s_cur, f32x16& s_next,
+                                     float& mx_next, const bf16x8 (&p_prev)[2], bf16x8 (&p_cur)[2],
+                                     f32x16 (&o)[D / 32], float& l_run, float mc, float scale_log2, const KGeom& g,
+                                     int j_next, int wk, int hf, __amdgpu_buffer_rsrc_t vr, uint16_t* vl,
+                                     const uint32_t* voff, __amdgpu_buffer_rsrc_t kr, uint16_t* kl,
+                                     const uint32_t* koff) {
   constexpr int DC = D / 16, DT = D / 32, NI = D / 32, KRPI = 512 / D;
+  constexpr int NS = DC + 2 * DT;             // MFMA slots of the step
+  constexpr int NV = 48 + 10 + (PARTIAL ? 16 : 0);  // vector instructions to spread
+  constexpr int VPS = (NV + NS - 1) / NS;
+  static_assert(2 * NI <= DC, "one tile load per S^T slot");
   const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
-  uint32_t pw[8];
   s_next = f32x16{};
 #pragma unroll
-  for (int r = 0; r < 8; ++r) {
-    if (r < DC) s_next = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[r], qf[r], s_next, 0, 0, 0);
+  for (int r = 0; r < DC; ++r) {
+    s_next = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[r], qf[r], s_next, 0, 0, 0);
     if (r < NI)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (lds_ptr_t)(vl + r * 8 * 64), 16, voff[r], 0, 0, 0);
     else if (r < 2 * NI)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, (lds_ptr_t)(kl + (r - NI) * KRPI * D), 16, koff[r - NI], 0, 0, 0);
+  }
+  uint32_t pw[8];
+#pragma unroll
+  for (int r = 0; r < 8; ++r) {
     const float p0 = __builtin_amdgcn_exp2f(fmaf(s_cur[2 * r], scale_log2, -mc));
     const float p1 = __builtin_amdgcn_exp2f(fmaf(s_cur[2 * r + 1], scale_log2, -mc));
     const bf16x2 pk = __builtin_convertvector((f32x2){p0, p1}, bf16x2);
     l_run = __builtin_amdgcn_fdot2_f32_bf16(pk, ones, l_run, false);
     pw[r] = __builtin_bit_cast(uint32_t, pk);
   }
-  bf16x8 pb[2];
-  pb[0] = __builtin_bit_cast(bf16x8, make_uint4(pw[0], pw[1], pw[2], pw[3]));
-  pb[1] = __builtin_bit_cast(bf16x8, make_uint4(pw[4], pw[5], pw[6], pw[7]));
+  p_cur[0] = __builtin_bit_cast(bf16x8, make_uint4(pw[0], pw[1], pw[2], pw[3]));
+  p_cur[1] = __builtin_bit_cast(bf16x8, make_uint4(pw[4], pw[5], pw[6], pw[7]));
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk) o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[dt][kk], pb[kk], o[dt], 0, 0, 0);
-  // Interleave: one MFMA of the next S^T, then the vector work of one P pair.
+    for (int kk = 0; kk < 2; ++kk)
+      o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[dt][kk], p_prev[kk], o[dt], 0, 0, 0);
+  if (PARTIAL) mask_keys(s_next, g, j_next, wk, hf);
+  mx_next = max16(s_next);
+  // P(n) and its row sum are only used by the next step; without this the
+  // compiler sinks them out of the interleaved region.
+  asm volatile("" ::"v"(pw[0]), "v"(pw[1]), "v"(pw[2]), "v"(pw[3]), "v"(pw[4]), "v"(pw[5]), "v"(pw[6]), "v"(pw[7]),
+               "v"(l_run));
+  // S^T(n+1) first (its max closes the step), P V(n-1) after; the vector
+  // work is spread evenly over all slots.
 #pragma unroll
-  for (int r = 0; r < DC; ++r) {
+  for (int s = 0; s < NS; ++s) {
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
+    __builtin_amdgcn_sched_group_barrier(0x002, VPS, 0);
   }
 }
 
+// Direct-to-LDS loads of this wave's share of one K tile (buffer resource kr
+// over the tile, lane offsets off).
 template <int D>
+__device__ __forceinline__ void issue_k_tile(__amdgpu_buffer_rsrc_t kr, uint16_t* klds, int w, const uint32_t* off) {
+  constexpr int NI = D / 32, KRPI = 512 / D;
+#pragma unroll
+  for (int e = 0; e < NI; ++e)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, (lds_ptr_t)(klds + (w * NI + e) * KRPI * D), 16, off[e], 0, 0, 0);
+}
+
+template <int D, bool PARTIAL>
 __global__ void __launch_bounds__(kThreads, 2) attn_fwd(const uint16_t* __restrict__ qc,
                                                         const uint16_t* __restrict__ kc,
                                                         const uint16_t* __restrict__ vt,
@@ -142,6 +158,7 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd(const uint16_t* __restri
                                                         float* __restrict__ oc_f32, float* __restrict__ lse,
                                                         KGeom g, Placement pl) {
   constexpr int DC = D / 16, DT = D / 32;
+  constexpr int NI = TileOffsets<D>::NI, KRPI = TileOffsets<D>::KRPI;
   __shared__ __attribute__((aligned(16))) Smem<D> sm;
 
   int i, h, b;
@@ -155,20 +172,31 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd(const uint16_t* __restri
   const uint16_t* vbase = vt + bh * g.Np * D;
   const int32_t* irow = idx + (bh * g.nc + i) * topk;
   const int q = 32 * wq + n;
+  // Past the last block the pipeline keeps issuing loads (of a valid tile,
+  // into a free buffer) so that the number of loads in flight is the same at
+  // every step.
+  const auto blk = [&](int m) { return irow[m < topk ? m : topk - 1]; };
 
-  // First tiles in flight before anything else.
+  // Pipeline: K(m) lives in K buffer m % 3 and V(m) in V buffer m % 2.
+  // Step n waits for K(n+1) and V(n-1), reads them, issues V(n) and K(n+3)
+  // into the buffers that step n-1 finished with, and (see step) computes
+  // S^T(n+1), P(n) and P(n-1) V(n-1).  V(-1) is a zero tile and P(-1) = 0.
+  // Steps come in groups of six so that every buffer index is compile-time.
   const TileOffsets<D> toff(w, lane);
-  {
-    const int j0 = irow[0];
-    load_k_tile<D>(kbase + 64LL * j0 * D, sm.k[0], w, toff);
-    load_v_tile<D>(vbase + 64LL * j0 * D, sm.v[0], w, toff);
-  }
-
+  // K tile m -> LDS buffer dst (this wave's share).
+  issue_k_tile<D>(make_rsrc(kbase + 64LL * blk(0) * D, 64 * D * 2), sm.k[0], w, toff.k);
   bf16x8 qf[DC];
   {
     const uint16_t* qrow = qc + (bh * g.Np + 64LL * i + q) * D;
 #pragma unroll
     for (int dc = 0; dc < DC; ++dc) qf[dc] = *reinterpret_cast<const bf16x8*>(qrow + 16 * dc + 8 * hf);
+  }
+  issue_k_tile<D>(make_rsrc(kbase + 64LL * blk(1) * D, 64 * D * 2), sm.k[1], w, toff.k);
+  issue_k_tile<D>(make_rsrc(kbase + 64LL * blk(2) * D, 64 * D * 2), sm.k[2], w, toff.k);
+  {
+    uint4* z = reinterpret_cast<uint4*>(sm.v[1]);
+#pragma unroll
+    for (int e = tid; e < D * 64 * 2 / 16; e += kThreads) z[e] = make_uint4(0, 0, 0, 0);
   }
   f32x16 o[DT];
 #pragma unroll
@@ -176,23 +204,12 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd(const uint16_t* __restri
   float m_run = -INFINITY, l_run = 0.f;
   const int prow = pi_row(n);
   const float lazy_raw = kLazyLog2 / scale_log2;
+  bf16x8 p_prev[2] = {};
 
-  // Pipeline: entering step n, S^T of block n is in registers, K of blocks
-  // n+1 and n+2 and V of block n are in (or on their way to) LDS.  Step n
-  // waits for K(n+1) and V(n), starts the loads of V(n+1) and K(n+3) into the
-  // buffers freed by step n-1, computes S^T(n+1) while turning S^T(n) into P,
-  // and adds P V(n).  K buffer of block m: m % 3, V buffer: m % 2; steps come
-  // in groups of six so that every buffer is compile-time distinct.
-  constexpr int NI = TileOffsets<D>::NI;
-  // Past the last block the pipeline keeps issuing loads (of a valid tile,
-  // into a free buffer) so that the number of loads in flight is the same at
-  // every step: K(1), K(2) here, then V(n+1), K(n+3) in step n.
-  const auto blk = [&](int m) { return irow[m < topk ? m : topk - 1]; };
-  load_k_tile<D>(kbase + 64LL * blk(1) * D, sm.k[1], w, toff);
-  load_k_tile<D>(kbase + 64LL * blk(2) * D, sm.k[2], w, toff);
-  f32x16 s_cur, s_next;
+  f32x16 s_cur;
+  float mx_cur;
   {
-    // K(0) and V(0) were issued first; K(1), K(2) may stay in flight.
+    // K(0) and the Q fragments are in; K(1), K(2) may stay in flight.
     wait_vmcnt<2 * NI>();
     pipeline_barrier();
     bf16x8 ka[DC];
@@ -200,35 +217,77 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd(const uint16_t* __restri
     s_cur = f32x16{};
 #pragma unroll
     for (int dc = 0; dc < DC; ++dc) s_cur = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[dc], qf[dc], s_cur, 0, 0, 0);
+    if (PARTIAL) mask_keys(s_cur, g, blk(0), wk, hf);
+    mx_cur = max16(s_cur);
   }
-  int j_cur = irow[0];
+  // Lazy rescaling: the reference max m_run moves only when a block exceeds
+  // it by more than kLazyLog2 (log2 units), so P <= 2^8 and the O^T rescale
+  // (a full accumulator pass) is rare.  Each lane half's max bounds the row
+  // max from below, so the move is first detected per half and only then is
+  // the row max taken across lane ^ 32.  A half holding padded keys only
+  // (max -inf) never triggers it.
+  bool move = __builtin_amdgcn_ballot_w64(mx_cur > m_run + lazy_raw) != 0;
+
   for (int jb = 0; jb < topk; jb += 6) {
 #pragma unroll
     for (int u = 0; u < 6; ++u) {
       const int nb = jb + u;
       if (nb < topk) {
-        // Outstanding, oldest first: K(nb+1), V(nb), K(nb+2).
+        // Outstanding, oldest first: K(nb+1), V(nb-1), K(nb+2).
         wait_vmcnt<NI>();
         pipeline_barrier();
-        const int j_next = blk(nb + 1);
         bf16x8 ka[DC];
         bf16x8 va[DT][2];
         read_k<D>(sm.k[(u + 1) % 3], wk, hf, prow, ka);
-        read_v<D>(sm.v[u % 2], wk, hf, n, va);
-        if (g.partial) mask_partial(s_cur, g, j_cur, wk, hf);
-        const float mc = softmax_stats<DT>(s_cur, o, m_run, l_run, scale_log2, lazy_raw);
-        pipelined_step<D>(ka, va, qf, s_cur, s_next, o, l_run, mc, scale_log2,
-                          make_rsrc(vbase + 64LL * j_next * D, 64 * D * 2), sm.v[(u + 1) % 2] + w * NI * 8 * 64,
-                          toff.v, make_rsrc(kbase + 64LL * blk(nb + 3) * D, 64 * D * 2),
-                          sm.k[u % 3] + w * NI * TileOffsets<D>::KRPI * D, toff.k);
+        read_v<D>(sm.v[(u + 1) % 2], wk, hf, n, va);
+        float alpha = 1.f;
+        const bool resc = move;
+        if (resc) {
+          const float row_max = fmaxf(mx_cur, __shfl_xor(mx_cur, 32));
+          const bool grow = row_max > m_run + lazy_raw;
+          alpha = grow ? __builtin_amdgcn_exp2f((m_run - row_max) * scale_log2) : 1.f;
+          m_run = grow ? row_max : m_run;
+          l_run *= alpha;
+        }
+        // Until a valid key has been seen every logit is -inf and p must be 0.
+        const float mc = (m_run == -INFINITY) ? 0.f : m_run * scale_log2;
+        f32x16 s_next;
+        float mx_next;
+        bf16x8 p_cur[2];
+        step<D, PARTIAL>(ka, va, qf, s_cur, s_next, mx_next, p_prev, p_cur, o, l_run, mc, scale_log2, g,
+                         blk(nb + 1), wk, hf, make_rsrc(vbase + 64LL * blk(nb) * D, 64 * D * 2),
+                         sm.v[u % 2] + w * NI * 8 * 64, toff.v,
+                         make_rsrc(kbase + 64LL * blk(nb + 3) * D, 64 * D * 2), sm.k[u % 3] + w * NI * KRPI * D,
+                         toff.k);
+        move = __builtin_amdgcn_ballot_w64(mx_next > m_run + lazy_raw) != 0;
+        if (resc) {
+          // O^T now holds P(0..n-1) V at the previous reference max.
+#pragma unroll
+          for (int dt = 0; dt < DT; ++dt) o[dt] *= alpha;
+        }
         s_cur = s_next;
-        j_cur = j_next;
+        mx_cur = mx_next;
+        p_prev[0] = p_cur[0];
+        p_prev[1] = p_cur[1];
       }
     }
+  }
+  {
+    // Last product: P(topk-1) V(topk-1).
+    wait_vmcnt<NI>();
+    pipeline_barrier();
+    bf16x8 va[DT][2];
+    read_v<D>(sm.v[(topk - 1) & 1], wk, hf, n, va);
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk)
+        o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[dt][kk], p_prev[kk], o[dt], 0, 0, 0);
   }
 
   // Merge the two key halves: wavefronts with wk = 1 hand (m, l, O^T) over.
   l_run += __shfl_xor(l_run, 32);
+  wait_vmcnt<0>();  // the padding loads past the end target the K buffers
   __syncthreads();  // all LDS tile reads done; reuse the K buffers
   float* xo = reinterpret_cast<float*>(&sm.k[0][0]) + wq * (DT * 16 * 64);
   float* xm = reinterpret_cast<float*>(&sm.v[0][0]) + wq * 128;
@@ -270,18 +329,25 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd(const uint16_t* __restri
 
 }  // namespace
 
+template <int D, bool PARTIAL>
+void launch_fwd(const KGeom& g, const uint16_t* qc, const uint16_t* kc, const uint16_t* vt, const int32_t* idx,
+                int topk, float scale, uint16_t* oc, float* oc_f32, float* lse, hipStream_t s) {
+  const Placement pl = make_placement(g);
+  const float scale_log2 = scale * 1.4426950408889634f;
+  attn_fwd<D, PARTIAL><<<dim3(grid_size(g)), dim3(kThreads), 0, s>>>(qc, kc, vt, idx, topk, scale, scale_log2, oc,
+                                                                      oc_f32, lse, g, pl);
+}
+
 hipError_t launch_attn_fwd(const KGeom& g, const uint16_t* qc, const uint16_t* kc, const uint16_t* vt,
                            const int32_t* idx, int topk, float scale, uint16_t* oc, float* oc_f32, float* lse,
                            hipStream_t s) {
-  const Placement pl = make_placement(g);
-  const dim3 grid(grid_size(g));
-  const float scale_log2 = scale * 1.4426950408889634f;
-  if (g.D == 64)
-    hipLaunchKernelGGL(attn_fwd<64>, grid, dim3(kThreads), 0, s, qc, kc, vt, idx, topk, scale, scale_log2, oc,
-                       oc_f32, lse, g, pl);
-  else
-    hipLaunchKernelGGL(attn_fwd<128>, grid, dim3(kThreads), 0, s, qc, kc, vt, idx, topk, scale, scale_log2, oc,
-                       oc_f32, lse, g, pl);
+  if (g.D == 64) {
+    if (g.partial) launch_fwd<64, true>(g, qc, kc, vt, idx, topk, scale, oc, oc_f32, lse, s);
+    else launch_fwd<64, false>(g, qc, kc, vt, idx, topk, scale, oc, oc_f32, lse, s);
+  } else {
+    if (g.partial) launch_fwd<128, true>(g, qc, kc, vt, idx, topk, scale, oc, oc_f32, lse, s);
+    else launch_fwd<128, false>(g, qc, kc, vt, idx, topk, scale, oc, oc_f32, lse, s);
+  }
   return hipGetLastError();
 }
 
