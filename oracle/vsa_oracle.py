@@ -38,6 +38,14 @@ fits them, with these conventions (each is a reading, not a quote):
       O_lin = phi(Q) (sum_U phi(K)^T V) / (phi(Q) . sum_U phi(K)),
       and 0 where U is empty.
   O7  output = O_sparse (+ O_lin), back in raster token order.
+  O8  sliding-tile variant (STA, named among the attention backends of the
+      FastVideo attention-backend article, item "SLIDING_TILE_ATTN" and the
+      figure comparing NATTEN, Tiled NATTEN and STA): instead of the top-k
+      list, each query cube attends to a fixed window of key cubes,
+      (wt, wh, ww) cubes wide, centred on the query cube where possible and
+      shifted inwards at the grid borders so that every query cube keeps the
+      same number of key cubes (the whole axis when the window is wider).
+      The pages name the pattern but give no window; this is the reading.
 
 Every step is written as its definition, in float64, with no blocking,
 fusion or reordering beyond the definition.  Inputs are bf16 bit patterns
@@ -70,6 +78,8 @@ __all__ = [
     "linear_cube",
     "linear_branch",
     "forward",
+    "sta_window",
+    "sta_index",
 ]
 
 
@@ -331,3 +341,39 @@ def forward(q: np.ndarray, k: np.ndarray, v: np.ndarray, grid: Sequence[int], to
     if linear:
         o = o + linear_branch(qc, kc, vc, valid, idx)
     return cube_unpermute(o, grid), idx
+
+
+# --------------------------------------------------------------------------
+# O8: sliding-tile block lists
+# --------------------------------------------------------------------------
+
+def sta_window(c: int, n: int, w: int) -> range:
+    """Key-cube coordinates along one axis for query coordinate c (O8).
+
+    w consecutive coordinates starting (w - 1) // 2 below c, shifted to stay
+    inside [0, n); all n coordinates when w >= n.
+    """
+    if w >= n:
+        return range(n)
+    start = min(max(c - (w - 1) // 2, 0), n - w)
+    return range(start, start + w)
+
+
+def sta_index(grid: Sequence[int], window: Sequence[int]) -> np.ndarray:
+    """Static block list int32 [Nc, k] of the sliding-tile pattern (O8).
+
+    Row i lists, ascending, the key cubes (tt, yy, xx) with each coordinate in
+    the window of the query cube's coordinate along that axis.
+    """
+    ct, ch, cw = cube_grid(grid)
+    wt, wh, ww = (int(v) for v in window)
+    rows = []
+    for t in range(ct):
+        for y in range(ch):
+            for x in range(cw):
+                row = [(tt * ch + yy) * cw + xx
+                       for tt in sta_window(t, ct, wt)
+                       for yy in sta_window(y, ch, wh)
+                       for xx in sta_window(x, cw, ww)]
+                rows.append(sorted(row))
+    return np.asarray(rows, dtype=np.int32)
