@@ -99,7 +99,10 @@ def cpu_baseline(wl, budget_s: float):
     sub = {n: workloads.make_head(wl, n, b, h)[None, :, None, :] for n in ("q", "k", "v")}
     t0 = time.perf_counter()
     qc, kc, vc = (oracle.cube_permute(sub[n], wl.grid) for n in ("q", "k", "v"))
-    idx = oracle.select_topk(qc, kc, valid, wl.topk)
+    if wl.pattern == "sta":
+        idx = oracle.sta_index(wl.grid, wl.window)[None, None]
+    else:
+        idx = oracle.select_topk(qc, kc, valid, wl.topk)
     states = oracle.vsa_oracle._cube_states(kc[0, 0], vc[0, 0], valid) if wl.linear else None
     per_head_fixed = time.perf_counter() - t0
     t1 = time.perf_counter()
@@ -118,7 +121,8 @@ def cpu_baseline(wl, budget_s: float):
         "unit": "TFLOP/s",
         "cores": int(threads),
         "kind": "oracle",
-        "sample": (f"fp64 numpy oracle, head (b=0,h=0) of {wl.name}: permute+pool+score+top-k of all "
+        "sample": (f"fp64 numpy oracle, head (b=0,h=0) of {wl.name}: permute+"
+                   f"{'sliding-tile lists' if wl.pattern == 'sta' else 'pool+score+top-k'} of all "
                    f"{wl.n_cubes} rows plus {cubes_done} of {wl.n_cubes} query cubes "
                    f"({t_total:.1f} s), scaled to {n_heads} heads"),
         "ms_per_layer": layer_s * 1e3,
@@ -181,11 +185,19 @@ def main():
                 ev[i].record()
 
         mark(0)
-        vsa.cube_permute_pool(q, wl.grid, out=qc, mean_out=qbar)
-        vsa.cube_permute_pool(k, wl.grid, out=kc, mean_out=kbar)
+        if wl.pattern == "sta":
+            vsa.cube_permute(q, wl.grid, out=qc)
+            vsa.cube_permute(k, wl.grid, out=kc)
+        else:
+            vsa.cube_permute_pool(q, wl.grid, out=qc, mean_out=qbar)
+            vsa.cube_permute_pool(k, wl.grid, out=kc, mean_out=kbar)
         vsa.cube_permute(v, wl.grid, layout="dim", out=vt)
         mark(1)
-        vsa.select_topk_pooled(qbar, kbar, wl.grid, wl.topk, out=idx, workspace=ws_sel)
+        if wl.pattern == "sta":
+            # The sliding-tile list is static; it is rebuilt every layer here all the same.
+            vsa.sta_index(wl.grid, wl.window, B, H, head_dim=D, out=idx)
+        else:
+            vsa.select_topk_pooled(qbar, kbar, wl.grid, wl.topk, out=idx, workspace=ws_sel)
         mark(2)
         vsa.sparse_attn_fwd(qc, kc, vt, idx, wl.grid, wl.softmax_scale, out=oc, out_f32=of)
         mark(3)
@@ -249,7 +261,8 @@ def main():
             "batch": B, "heads": H, "head_dim": D,
             "latent_grid": list(wl.grid), "padded_grid": list(wl.padded_grid),
             "tokens": wl.tokens, "n_cubes": wl.n_cubes, "topk": wl.topk,
-            "sparsity": wl.sparsity, "linear_branch": wl.linear,
+            "sparsity": wl.sparsity, "linear_branch": wl.linear, "pattern": wl.pattern,
+            **({"window_cubes": list(wl.window)} if wl.window else {}),
             "computed_blocks": wl.blocks, "fine_flops": flops,
         },
         "ms_per_layer": round(ms_step, 4),

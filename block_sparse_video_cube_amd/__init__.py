@@ -39,6 +39,8 @@ __all__ = [
     "cube_unpermute",
     "select_topk",
     "select_topk_pooled",
+    "sta_topk",
+    "sta_index",
     "sparse_attn_fwd",
     "linear_branch",
     "vsa_attention",
@@ -165,6 +167,30 @@ def select_topk_pooled(qbar: torch.Tensor, kbar: torch.Tensor, grid: Sequence[in
     _lib.check("vsa_select_topk_pooled", _lib.load().vsa_select_topk_pooled(
         g, qbar.data_ptr(), kbar.data_ptr(), int(topk), out.data_ptr(), workspace.data_ptr(),
         workspace.numel() * workspace.element_size(), _stream()))
+    return out
+
+
+def sta_topk(grid: Sequence[int], window: Sequence[int], head_dim: int = 128) -> int:
+    """Length of every sliding-tile block list for this grid and window (cubes)."""
+    wt, wh, ww = (int(x) for x in window)
+    k = _lib.load().vsa_sta_topk(make_geom(1, 1, head_dim, grid), wt, wh, ww)
+    if k < 1:
+        raise VsaError("vsa_sta_topk", _lib.VSA_ERR_WINDOW, "invalid geometry or window")
+    return int(k)
+
+
+def sta_index(grid: Sequence[int], window: Sequence[int], batch: int, heads: int, head_dim: int = 128,
+              device=None, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Static sliding-tile block list int32 [batch, heads, Nc, k] (see include/vsa_cube.h)."""
+    wt, wh, ww = (int(x) for x in window)
+    g = make_geom(batch, heads, head_dim, grid)
+    d = geom_dims(g)
+    k = sta_topk(grid, window, head_dim)
+    if out is None:
+        out = torch.empty((int(batch), int(heads), d.n_cubes, k), dtype=torch.int32,
+                          device=device if device is not None else torch.device("cuda"))
+    _need(out, "idx", torch.int32, (int(batch), int(heads), d.n_cubes, k))
+    _lib.check("vsa_sta_index", _lib.load().vsa_sta_index(g, wt, wh, ww, out.data_ptr(), _stream()))
     return out
 
 

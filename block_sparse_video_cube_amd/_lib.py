@@ -18,6 +18,7 @@ VSA_ERR_WORKSPACE = 6
 VSA_ERR_LAYOUT = 7
 VSA_ERR_SCALE = 8
 VSA_ERR_LAUNCH = 9
+VSA_ERR_WINDOW = 10
 
 VSA_LAYOUT_TOKEN_MAJOR = 0
 VSA_LAYOUT_DIM_MAJOR = 1
@@ -36,6 +37,8 @@ ENTRY_POINTS = (
     "vsa_select_topk_pooled",
     "vsa_sparse_attn_fwd",
     "vsa_linear_branch",
+    "vsa_sta_topk",
+    "vsa_sta_index",
 )
 
 
@@ -101,6 +104,8 @@ def load() -> ctypes.CDLL:
         "vsa_select_topk": (i32, [G, P, P, i32, P, P, sz, P]),
         "vsa_sparse_attn_fwd": (i32, [G, P, P, P, P, i32, ctypes.c_float, P, P, P, P]),
         "vsa_linear_branch": (i32, [G, P, P, P, P, i32, P, P, P, sz, P]),
+        "vsa_sta_topk": (i32, [G, i32, i32, i32]),
+        "vsa_sta_index": (i32, [G, i32, i32, i32, P, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)

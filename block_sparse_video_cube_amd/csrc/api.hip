@@ -58,6 +58,7 @@ const char* vsa_status_string(int32_t status) {
     case VSA_ERR_LAYOUT: return "unknown layout code";
     case VSA_ERR_SCALE: return "softmax scale must be finite and positive";
     case VSA_ERR_LAUNCH: return "kernel launch failed";
+    case VSA_ERR_WINDOW: return "sliding-tile window must be at least 1 cube on every axis";
     default: return "unknown status";
   }
 }
@@ -135,6 +136,29 @@ int32_t vsa_select_topk_pooled(const vsa_geom* g, const float* qbar, const float
   if (ws_bytes < vsa::select_pooled_workspace_bytes(k)) return VSA_ERR_WORKSPACE;
   return launch_status(vsa::launch_select_pooled(k, qbar, kbar, topk, idx, static_cast<float*>(ws),
                                                  static_cast<hipStream_t>(stream)));
+}
+
+int32_t vsa_sta_topk(const vsa_geom* g, int32_t win_t, int32_t win_h, int32_t win_w) {
+  vsa_dims d;
+  vsa::KGeom k;
+  if (prepare(g, &d, &k) != VSA_OK) return 0;
+  if (win_t < 1 || win_h < 1 || win_w < 1) return 0;
+  const int64_t kk = (int64_t)(win_t < d.cubes_t ? win_t : d.cubes_t) * (win_h < d.cubes_h ? win_h : d.cubes_h) *
+                     (win_w < d.cubes_w ? win_w : d.cubes_w);
+  return (int32_t)kk;  // <= n_cubes <= 2^24
+}
+
+int32_t vsa_sta_index(const vsa_geom* g, int32_t win_t, int32_t win_h, int32_t win_w, int32_t* idx, void* stream) {
+  vsa_dims d;
+  vsa::KGeom k;
+  int32_t st = prepare(g, &d, &k);
+  if (st != VSA_OK) return st;
+  if (!idx) return VSA_ERR_NULL;
+  if (!aligned16(idx)) return VSA_ERR_ALIGN;
+  if (win_t < 1 || win_h < 1 || win_w < 1) return VSA_ERR_WINDOW;
+  const int64_t kk = vsa_sta_topk(g, win_t, win_h, win_w);
+  if ((int64_t)g->batch * g->heads * d.n_cubes * kk >= ((int64_t)1 << 40)) return VSA_ERR_GEOMETRY;
+  return launch_status(vsa::launch_sta_index(k, win_t, win_h, win_w, idx, static_cast<hipStream_t>(stream)));
 }
 
 int32_t vsa_cube_unpermute(const vsa_geom* g, const uint16_t* xc, uint16_t* x, void* stream) {

@@ -93,4 +93,5 @@ hipError_t launch_linear(const KGeom& g, const uint16_t* qc, const uint16_t* kc,
                          const int32_t* idx, int topk, const float* o_sparse, uint16_t* oc, void* ws,
                          hipStream_t s);
 size_t linear_workspace_bytes(const KGeom& g);
+hipError_t launch_sta_index(const KGeom& g, int wt, int wh, int ww, int32_t* idx, hipStream_t s);
 }  // namespace vsa

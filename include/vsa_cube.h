@@ -61,7 +61,8 @@ typedef enum vsa_status {
   VSA_ERR_WORKSPACE = 6, /* workspace smaller than the *_workspace_bytes size */
   VSA_ERR_LAYOUT = 7,    /* unknown layout code                               */
   VSA_ERR_SCALE = 8,     /* softmax scale not finite and positive             */
-  VSA_ERR_LAUNCH = 9     /* a kernel launch failed (HIP error)                */
+  VSA_ERR_LAUNCH = 9,    /* a kernel launch failed (HIP error)                */
+  VSA_ERR_WINDOW = 10    /* a sliding-tile window below 1 cube on some axis   */
 } vsa_status;
 
 /* Shape of one attention layer. */
@@ -147,6 +148,26 @@ int32_t vsa_select_topk(const vsa_geom* g, const uint16_t* qc, const uint16_t* k
 int32_t vsa_select_topk_pooled(const vsa_geom* g, const float* qbar, const float* kbar,
                                int32_t topk, int32_t* idx, void* ws, size_t ws_bytes,
                                void* stream);
+
+/* Sliding-tile pattern (STA; FastVideo attention-backend article, item
+ * "SLIDING_TILE_ATTN" and the figure comparing NATTEN, Tiled NATTEN and STA):
+ * a static block list to feed vsa_sparse_attn_fwd instead of vsa_select_topk.
+ * Query cube (t, y, x) attends to the key cubes whose coordinate on each axis
+ * lies in a window of win_t / win_h / win_w cubes that starts (win - 1) / 2
+ * below the query's coordinate, shifted inwards to stay inside the cube grid
+ * (the whole axis when the window is wider than the grid).
+ *
+ * vsa_sta_topk returns the list length
+ * k = min(win_t, cubes_t) * min(win_h, cubes_h) * min(win_w, cubes_w), or 0 for
+ * an invalid geometry or a window below 1.
+ *
+ * vsa_sta_index writes idx int32 [B, heads, Nc, k] (the same ascending rows
+ * for every (b, h)); idx is a 16-byte aligned device buffer owned by the
+ * caller.  Errors: VSA_ERR_NULL, VSA_ERR_ALIGN, VSA_ERR_WINDOW, geometry
+ * errors, VSA_ERR_GEOMETRY when B * heads * Nc * k >= 2^40. */
+int32_t vsa_sta_topk(const vsa_geom* g, int32_t win_t, int32_t win_h, int32_t win_w);
+int32_t vsa_sta_index(const vsa_geom* g, int32_t win_t, int32_t win_h, int32_t win_w,
+                      int32_t* idx, void* stream);
 
 /* Fine stage: for every (b, h, query cube i), softmax attention of its 64
  * query rows over the valid keys of the topk key cubes idx[b, h, i, :]

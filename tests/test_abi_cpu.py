@@ -42,7 +42,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 def test_abi_version_and_status_text(lib):
     assert lib.vsa_abi_version() == 1
-    for code in range(10):
+    for code in range(11):
         assert lib.vsa_status_string(code)
     assert lib.vsa_status_string(12345) == b"unknown status"
 
@@ -138,3 +138,22 @@ def test_fused_entry_points_reject_bad_arguments(lib):
     assert lib.vsa_select_topk_pooled(g, P, None, 2, P, P, ws, None) == _lib.VSA_ERR_NULL
     assert lib.vsa_select_topk_pooled(g, P, P, 0, P, P, ws, None) == _lib.VSA_ERR_TOPK
     assert lib.vsa_select_topk_pooled(g, P, P, 2, P, P, 16, None) == _lib.VSA_ERR_WORKSPACE
+
+
+def test_sta_entry_points(lib):
+    from block_sparse_video_cube_amd import _lib
+
+    P = FAKE
+    # list length: min(window, cubes) per axis; 0 for invalid windows or geometry
+    assert lib.vsa_sta_topk(geom(grid=(16, 28, 52)), 3, 3, 3) == 27
+    assert lib.vsa_sta_topk(geom(grid=(16, 28, 52)), 9, 1, 2) == 4 * 1 * 2
+    assert lib.vsa_sta_topk(geom(grid=(21, 45, 80)), 3, 5, 7) == 3 * 5 * 7
+    assert lib.vsa_sta_topk(geom(grid=(5, 6, 7)), 3, 3, 3) == 8
+    assert lib.vsa_sta_topk(geom(grid=(16, 28, 52)), 0, 3, 3) == 0
+    assert lib.vsa_sta_topk(geom(B=0), 3, 3, 3) == 0
+    g = geom()
+    assert lib.vsa_sta_index(g, 3, 3, 3, None, None) == _lib.VSA_ERR_NULL
+    assert lib.vsa_sta_index(g, 3, 3, 3, ODD, None) == _lib.VSA_ERR_ALIGN
+    assert lib.vsa_sta_index(g, 3, 0, 3, P, None) == _lib.VSA_ERR_WINDOW
+    assert lib.vsa_sta_index(g, 3, 3, -1, P, None) == _lib.VSA_ERR_WINDOW
+    assert lib.vsa_sta_index(geom(D=48), 3, 3, 3, P, None) == _lib.VSA_ERR_HEAD_DIM

@@ -63,6 +63,10 @@ class Workload:
     seed: int
     recipe: str  # "normal", "head_scale", "sinusoid"
     linear: bool = False
+    # Block pattern: "topk" (coarse-stage selection) or "sta" (static sliding
+    # tile window of `window` cubes, see oracle O8).
+    pattern: str = "topk"
+    window: Optional[Tuple[int, int, int]] = None
 
     @property
     def tokens(self) -> int:
@@ -127,6 +131,10 @@ WORKLOADS: Dict[str, Workload] = {
     "720p": Workload("720p", 1, 40, 128, (21, 45, 80), 144, 0.9, 1003, "normal"),
     # High-sparsity hybrid with the linear branch, sparsity 0.97.
     "hybrid": Workload("hybrid", 2, 12, 128, (16, 28, 52), 11, 0.97, 1004, "normal", linear=True),
+    # Sliding-tile pattern on the Wan2.1-1.3B layer: a 3x3x3-cube window
+    # (k = 27 of 364 cubes).  The pages name STA but give no window size.
+    "sta": Workload("sta", 1, 12, 128, (16, 28, 52), 27, None, 1005, "head_scale", pattern="sta",
+                    window=(3, 3, 3)),
 }
 
 
