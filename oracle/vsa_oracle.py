@@ -38,6 +38,14 @@ fits them, with these conventions (each is a reading, not a quote):
       O_lin = phi(Q) (sum_U phi(K)^T V) / (phi(Q) . sum_U phi(K)),
       and 0 where U is empty.
   O7  output = O_sparse (+ O_lin), back in raster token order.
+  O9  backward of the fine stage (the method is trainable: TurboDiffusion
+      article, section "稀疏、蒸馏与全链路量化", SLA is a trainable sparse-linear
+      attention; FastVideo sparse-distillation article, VSA is trained inside
+      the distillation): for a scalar loss with output gradient dO, per query
+      cube over its gathered keys, dV += P^T dO, dP = dO V^T,
+      dS = P * (dP - rowsum(dO * O)), dQ = scale dS K, dK += scale dS^T Q.
+      This is the chain rule through O5, written out; nothing on the pages
+      fixes it further.
   O8  sliding-tile variant (STA, named among the attention backends of the
       FastVideo attention-backend article, item "SLIDING_TILE_ATTN" and the
       figure comparing NATTEN, Tiled NATTEN and STA): instead of the top-k
@@ -80,6 +88,9 @@ __all__ = [
     "forward",
     "sta_window",
     "sta_index",
+    "attention_cube_bwd",
+    "sparse_attention_bwd",
+    "backward",
 ]
 
 
@@ -377,3 +388,67 @@ def sta_index(grid: Sequence[int], window: Sequence[int]) -> np.ndarray:
                        for xx in sta_window(x, cw, ww)]
                 rows.append(sorted(row))
     return np.asarray(rows, dtype=np.int32)
+
+
+# --------------------------------------------------------------------------
+# O9: backward of the fine stage
+# --------------------------------------------------------------------------
+
+def attention_cube_bwd(q_rows, k_all, v_all, valid, cubes: Sequence[int], scale: float, do_rows):
+    """Gradients of O5 for one query cube (O9).
+
+    Returns dQ [64, D], and dK, dV [n_keys, D] for the gathered keys (rows
+    64 j + l for j in cubes, in that order) with the key row indices.
+    """
+    q = _as_f64(q_rows)
+    do = _as_f64(do_rows)
+    keys = np.array([64 * j + l for j in cubes for l in range(64)], dtype=np.int64)
+    kk = _as_f64(k_all[keys])
+    vv = _as_f64(v_all[keys])
+    o, _, p = attention_cube(q_rows, k_all, v_all, valid, cubes, scale, return_probs=True)
+    dv = p.T @ do
+    dp = do @ vv.T
+    delta = (do * o).sum(axis=1, keepdims=True)
+    ds = p * (dp - delta)
+    dq = scale * (ds @ kk)
+    dk = scale * (ds.T @ q)
+    return dq, dk, dv, keys
+
+
+def sparse_attention_bwd(qc, kc, vc, valid, idx, scale, doc, heads: Optional[Sequence[Tuple[int, int]]] = None):
+    """dQ, dK, dV [B, H, Np, D] f64 of O5 (O9) for cube-major inputs.
+
+    doc: output gradient [B, H, Np, D].  heads: optional list of (b, h) to
+    compute (other heads stay NaN); dK and dV of a key cube collect every
+    query cube that selected it.
+    """
+    B, Hh, Np, D = qc.shape
+    dq = np.full((B, Hh, Np, D), np.nan)
+    dk = np.full((B, Hh, Np, D), np.nan)
+    dv = np.full((B, Hh, Np, D), np.nan)
+    todo = heads if heads is not None else [(b, h) for b in range(B) for h in range(Hh)]
+    for b, h in todo:
+        dk[b, h] = 0.0
+        dv[b, h] = 0.0
+        for i in range(Np // 64):
+            gq, gk, gv, keys = attention_cube_bwd(qc[b, h, 64 * i:64 * i + 64], kc[b, h], vc[b, h], valid,
+                                                  idx[b, h, i], scale, doc[b, h, 64 * i:64 * i + 64])
+            dq[b, h, 64 * i:64 * i + 64] = gq
+            np.add.at(dk[b, h], keys, gk)
+            np.add.at(dv[b, h], keys, gv)
+    return dq, dk, dv
+
+
+def backward(q, k, v, do, grid: Sequence[int], idx: np.ndarray, scale: Optional[float] = None):
+    """Whole-layer gradients (O9): raster [B, S, H, D] in, raster dQ, dK, dV f64 out.
+
+    do: gradient of the raster output; padded rows get none.
+    """
+    D = q.shape[-1]
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    valid = valid_rows(grid)
+    qc, kc, vc = (cube_permute(x, grid) for x in (q, k, v))
+    doc = cube_permute(do, grid)
+    dq, dk, dv = sparse_attention_bwd(qc, kc, vc, valid, idx, scale, doc)
+    return cube_unpermute(dq, grid), cube_unpermute(dk, grid), cube_unpermute(dv, grid)
