@@ -43,6 +43,7 @@ __all__ = [
     "sta_index",
     "sparse_attn_fwd",
     "linear_branch",
+    "sparse_attn_bwd",
     "vsa_attention",
     "workspace_bytes",
 ]
@@ -226,6 +227,39 @@ def sparse_attn_fwd(qc: torch.Tensor, kc: torch.Tensor, vt: torch.Tensor, idx: t
         out.data_ptr(), of.data_ptr() if of is not None else None,
         lse.data_ptr() if lse is not None else None, _stream()))
     return out, of, lse
+
+
+def sparse_attn_bwd(qc: torch.Tensor, qt: torch.Tensor, kc: torch.Tensor, kt: torch.Tensor, vc: torch.Tensor,
+                    oc: torch.Tensor, doc: torch.Tensor, dot: torch.Tensor, lse: torch.Tensor, idx: torch.Tensor,
+                    grid: Sequence[int], scale: Optional[float] = None, workspace: Optional[torch.Tensor] = None):
+    """Backward of the fine stage.  Returns (dq, dk, dv), bf16 [B, heads, Np, D] token-major.
+
+    qt, kt, dot: the DIM_MAJOR layouts (cube_permute(..., layout="dim")) of Q, K and dO;
+    vc: V token-major; oc, lse: outputs of sparse_attn_fwd (want_lse=True); idx: its block lists.
+    """
+    B, Hh, Np, D = qc.shape
+    g = make_geom(B, Hh, D, grid)
+    d = geom_dims(g)
+    topk = int(idx.shape[-1])
+    for t, name in ((qc, "qc"), (kc, "kc"), (vc, "vc"), (oc, "oc"), (doc, "doc")):
+        _need(t, name, torch.bfloat16, (B, Hh, d.rows, D))
+    for t, name in ((qt, "qt"), (kt, "kt"), (dot, "dot")):
+        _need(t, name, torch.bfloat16, (B, Hh, d.n_cubes, D, 64))
+    _need(lse, "lse", torch.float32, (B, Hh, d.rows))
+    _need(idx, "idx", torch.int32, (B, Hh, d.n_cubes, topk))
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    lib = _lib.load()
+    nbytes = lib.vsa_attn_bwd_workspace_bytes(g, topk)
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=qc.device)
+    dq, dk, dv = (torch.empty_like(qc) for _ in range(3))
+    _lib.check("vsa_sparse_attn_bwd", lib.vsa_sparse_attn_bwd(
+        g, qc.data_ptr(), qt.data_ptr(), kc.data_ptr(), kt.data_ptr(), vc.data_ptr(), oc.data_ptr(),
+        doc.data_ptr(), dot.data_ptr(), lse.data_ptr(), idx.data_ptr(), topk, float(scale), dq.data_ptr(),
+        dk.data_ptr(), dv.data_ptr(), workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+        _stream()))
+    return dq, dk, dv
 
 
 def linear_branch(qc: torch.Tensor, kc: torch.Tensor, vt: torch.Tensor, idx: torch.Tensor,

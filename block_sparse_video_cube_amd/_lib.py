@@ -39,6 +39,8 @@ ENTRY_POINTS = (
     "vsa_linear_branch",
     "vsa_sta_topk",
     "vsa_sta_index",
+    "vsa_attn_bwd_workspace_bytes",
+    "vsa_sparse_attn_bwd",
 )
 
 
@@ -106,6 +108,8 @@ def load() -> ctypes.CDLL:
         "vsa_linear_branch": (i32, [G, P, P, P, P, i32, P, P, P, sz, P]),
         "vsa_sta_topk": (i32, [G, i32, i32, i32]),
         "vsa_sta_index": (i32, [G, i32, i32, i32, P, P]),
+        "vsa_attn_bwd_workspace_bytes": (sz, [G, i32]),
+        "vsa_sparse_attn_bwd": (i32, [G, P, P, P, P, P, P, P, P, P, P, i32, ctypes.c_float, P, P, P, P, sz, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)

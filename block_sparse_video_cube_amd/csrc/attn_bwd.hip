@@ -1,0 +1,512 @@
+// Backward of the fine stage: dQ, dK, dV of block-sparse attention over the
+// selected 64x64 cube blocks, from the forward's log-sum-exp.
+//
+// VSA is trained inside the sparse distillation (FastVideo sparse-distillation
+// article, sections "核心技术解析" and "2. 视频稀疏注意力VSA"), and SLA is a
+// trainable sparse-linear attention (TurboDiffusion article, section
+// "稀疏、蒸馏与全链路量化"), so the block-sparse attention needs its gradient.
+// For a loss with output gradient dO, per query cube i and each selected key
+// cube j (the chain rule through the masked block softmax):
+//   P_ij = exp(scale Q_i K_j^T - lse_i),   delta_i = rowsum(dO_i * O_i),
+//   dV_j += P_ij^T dO_i,   dP_ij = dO_i V_j^T,   dS_ij = P_ij * (dP_ij - delta_i),
+//   dQ_i += scale dS_ij K_j,   dK_j += scale dS_ij^T Q_i.
+//
+// Kernels.  No atomics: every sum is owned by one workgroup, so the results
+// do not depend on scheduling.
+//  * bwd_delta: delta per row.
+//  * bwd_count / bwd_scan / bwd_fill: the block lists transposed, i.e. for
+//    every key cube the ascending list of query cubes whose (ascending) list
+//    holds it, found by binary search.
+//  * bwd_dq: one workgroup per query cube, S^T = K Q^T as in the forward (a
+//    lane owns a query column); per selected block it streams K_j and V_j
+//    (token-major) and K_j^T (the cube stored transposed), and accumulates
+//    dQ^T = K^T dS^T.
+//  * bwd_dkdv: one workgroup per key cube, S = Q K^T (a lane owns a key
+//    column; Q rows in pi order, so the accumulator is the B operand of the
+//    next product); K_j, V_j stay in registers; per query cube that selected
+//    j it streams Q_i, dO_i (token-major), Q_i^T, dO_i^T, lse_i and delta_i,
+//    and accumulates dV^T = dO^T P and dK^T = Q^T dS.
+// Both stream kernels double-buffer their tiles in LDS (direct buffer->LDS
+// loads one block ahead) and split each block among four wavefronts by
+// 32-row halves as the forward does, merging the halves through LDS.
+#include <math.h>
+
+#include "tile_pipeline.h"
+
+namespace vsa {
+
+namespace {
+
+using namespace tiles;
+constexpr float kLog2e = 1.4426950408889634f;
+
+// ---------------------------------------------------------------- delta --
+
+template <int D>
+__global__ void __launch_bounds__(256) bwd_delta(const uint16_t* __restrict__ o, const uint16_t* __restrict__ dout,
+                                                 float* __restrict__ delta, long long rows) {
+  constexpr int TPR = D / 8;  // threads per row, one 16-byte chunk each
+  const long long t = blockIdx.x * 256LL + threadIdx.x;
+  const long long row = t / TPR;
+  const int c = (int)(t % TPR);
+  float sum = 0.f;
+  if (row < rows) {
+    const uint4 a = reinterpret_cast<const uint4*>(o + row * D)[c];
+    const uint4 d = reinterpret_cast<const uint4*>(dout + row * D)[c];
+    const uint32_t wa[4] = {a.x, a.y, a.z, a.w}, wd[4] = {d.x, d.y, d.z, d.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      sum = fmaf(__uint_as_float(wa[e] << 16), __uint_as_float(wd[e] << 16), sum);
+      sum = fmaf(__uint_as_float(wa[e] & 0xFFFF0000u), __uint_as_float(wd[e] & 0xFFFF0000u), sum);
+    }
+  }
+#pragma unroll
+  for (int off = TPR / 2; off > 0; off >>= 1) sum += __shfl_xor(sum, off);
+  if (c == 0 && row < rows) delta[row] = sum;
+}
+
+// ------------------------------------------------- transposed block lists --
+
+// Does the ascending list row[0..k) hold j?
+__device__ __forceinline__ bool row_has(const int32_t* __restrict__ row, int k, int j) {
+  int lo = 0, hi = k;
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if (row[mid] < j) lo = mid + 1;
+    else hi = mid;
+  }
+  return lo < k && row[lo] == j;
+}
+
+// One wavefront per (b, h, key cube j): how many query cubes selected j.
+__global__ void __launch_bounds__(256) bwd_count(const int32_t* __restrict__ idx, int topk, int32_t* __restrict__ cnt,
+                                                 KGeom g) {
+  const int lane = threadIdx.x & 63;
+  const int j = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const long long bh = blockIdx.y;
+  if (j >= g.nc) return;  // no barrier in this kernel
+  const int32_t* rows = idx + bh * g.nc * (long long)topk;
+  int c = 0;
+  for (int i0 = 0; i0 < g.nc; i0 += 64) {
+    const int i = i0 + lane;
+    const bool has = i < g.nc && row_has(rows + (long long)i * topk, topk, j);
+    c += __popcll(__builtin_amdgcn_ballot_w64(has));
+  }
+  if (lane == 0) cnt[bh * g.nc + j] = c;
+}
+
+// Exclusive prefix sum of the counts over the key cubes of one (b, h).
+__global__ void __launch_bounds__(256) bwd_scan(const int32_t* __restrict__ cnt, int32_t* __restrict__ off, KGeom g) {
+  __shared__ int32_t part[256];
+  const long long base = (long long)blockIdx.x * g.nc;
+  const int per = (g.nc + 255) / 256;
+  const int lo = min((int)threadIdx.x * per, g.nc), hi = min(lo + per, g.nc);
+  int s = 0;
+  for (int j = lo; j < hi; ++j) s += cnt[base + j];
+  part[threadIdx.x] = s;
+  __syncthreads();
+  for (int d = 1; d < 256; d <<= 1) {
+    const int v = (int)threadIdx.x >= d ? part[threadIdx.x - d] : 0;
+    __syncthreads();
+    part[threadIdx.x] += v;
+    __syncthreads();
+  }
+  int run = part[threadIdx.x] - s;
+  for (int j = lo; j < hi; ++j) {
+    off[base + j] = run;
+    run += cnt[base + j];
+  }
+}
+
+// Same search as bwd_count; the query cubes are written in ascending order.
+__global__ void __launch_bounds__(256) bwd_fill(const int32_t* __restrict__ idx, int topk,
+                                                const int32_t* __restrict__ off, int32_t* __restrict__ qlist,
+                                                KGeom g) {
+  const int lane = threadIdx.x & 63;
+  const int j = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const long long bh = blockIdx.y;
+  if (j >= g.nc) return;
+  const int32_t* rows = idx + bh * g.nc * (long long)topk;
+  int32_t* dst = qlist + bh * g.nc * (long long)topk + off[bh * g.nc + j];
+  int run = 0;
+  for (int i0 = 0; i0 < g.nc; i0 += 64) {
+    const int i = i0 + lane;
+    const bool has = i < g.nc && row_has(rows + (long long)i * topk, topk, j);
+    const uint64_t m = __builtin_amdgcn_ballot_w64(has);
+    if (has) {
+      const int pos = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0));
+      dst[run + pos] = i;
+    }
+    run += __popcll(m);
+  }
+}
+
+// --------------------------------------------------------------------- dQ --
+
+template <int D>
+struct DqSmem {
+  uint16_t k[2][64 * D];   // K_j token-major
+  uint16_t v[2][64 * D];   // V_j token-major
+  uint16_t kt[2][D * 64];  // K_j^T (cube stored transposed)
+};
+
+template <int D>
+__device__ __forceinline__ void dq_issue(const uint16_t* kc, const uint16_t* vc, const uint16_t* kt, long long off,
+                                         uint16_t* ks, uint16_t* vs, uint16_t* kts, int w, const uint32_t* ko,
+                                         const uint32_t* vo) {
+  issue_k_tile<D>(make_rsrc(kc + off, 64 * D * 2), ks, w, ko);
+  issue_k_tile<D>(make_rsrc(vc + off, 64 * D * 2), vs, w, ko);
+  issue_v_tile<D>(make_rsrc(kt + off, 64 * D * 2), kts, w, vo);
+}
+
+template <int D, bool PARTIAL>
+__global__ void __launch_bounds__(kThreads, 1) bwd_dq(const uint16_t* __restrict__ qc, const uint16_t* __restrict__ kc,
+                                                      const uint16_t* __restrict__ kt,
+                                                      const uint16_t* __restrict__ vc,
+                                                      const uint16_t* __restrict__ doc,
+                                                      const float* __restrict__ lse, const float* __restrict__ delta,
+                                                      const int32_t* __restrict__ idx, int topk, float scale,
+                                                      float scale_log2, uint16_t* __restrict__ dq, KGeom g,
+                                                      Placement pl) {
+  constexpr int DC = D / 16, DT = D / 32;
+  __shared__ __attribute__((aligned(16))) DqSmem<D> sm;
+  int i, h, b;
+  if (!map_workgroup(g, pl, i, h, b)) return;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wq = w & 1, wk = w >> 1;
+  const int hf = lane >> 5, n = lane & 31;
+  const long long bh = (long long)b * g.H + h;
+  const long long hbase = bh * g.Np * D;
+  const int32_t* irow = idx + (bh * g.nc + i) * topk;
+  const long long row = bh * g.Np + 64LL * i + 32 * wq + n;
+  const TileOffsets<D> toff(w, lane);
+
+  dq_issue<D>(kc + hbase, vc + hbase, kt + hbase, 64LL * irow[0] * D, sm.k[0], sm.v[0], sm.kt[0], w, toff.k,
+              toff.v);
+  bf16x8 qf[DC], df[DC];
+#pragma unroll
+  for (int dc = 0; dc < DC; ++dc) {
+    qf[dc] = *reinterpret_cast<const bf16x8*>(qc + row * D + 16 * dc + 8 * hf);
+    df[dc] = *reinterpret_cast<const bf16x8*>(doc + row * D + 16 * dc + 8 * hf);
+  }
+  const float lse2 = lse[row] * kLog2e, dl = delta[row];
+  const int prow = pi_row(n);
+  f32x16 acc[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) acc[dt] = f32x16{};
+
+  for (int jb = 0; jb < topk; jb += 2) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int nb = jb + u;
+      if (nb < topk) {
+        wait_vmcnt<0>();
+        pipeline_barrier();
+        if (nb + 1 < topk)
+          dq_issue<D>(kc + hbase, vc + hbase, kt + hbase, 64LL * irow[nb + 1] * D, sm.k[u ^ 1], sm.v[u ^ 1],
+                      sm.kt[u ^ 1], w, toff.k, toff.v);
+        bf16x8 ka[DC], va[DC];
+        read_k<D>(sm.k[u], wk, hf, prow, ka);
+        read_k<D>(sm.v[u], wk, hf, prow, va);
+        f32x16 s = f32x16{}, dp = f32x16{};
+#pragma unroll
+        for (int dc = 0; dc < DC; ++dc) {
+          s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[dc], qf[dc], s, 0, 0, 0);
+          dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[dc], df[dc], dp, 0, 0, 0);
+        }
+        if (PARTIAL) mask_keys(s, g, irow[nb], wk, hf);
+        uint32_t sw[8];
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+          const float p0 = __builtin_amdgcn_exp2f(fmaf(s[2 * r], scale_log2, -lse2));
+          const float p1 = __builtin_amdgcn_exp2f(fmaf(s[2 * r + 1], scale_log2, -lse2));
+          const f32x2 d2 = {p0 * (dp[2 * r] - dl), p1 * (dp[2 * r + 1] - dl)};
+          sw[r] = __builtin_bit_cast(uint32_t, __builtin_convertvector(d2, bf16x2));
+        }
+        const bf16x8 sb[2] = {__builtin_bit_cast(bf16x8, make_uint4(sw[0], sw[1], sw[2], sw[3])),
+                              __builtin_bit_cast(bf16x8, make_uint4(sw[4], sw[5], sw[6], sw[7]))};
+        bf16x8 ta[DT][2];
+        read_v<D>(sm.kt[u], wk, hf, n, ta);
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+          for (int kk = 0; kk < 2; ++kk) acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ta[dt][kk], sb[kk], acc[dt], 0, 0, 0);
+      }
+    }
+  }
+
+  // The two key halves hold partial sums of the same dQ^T: add them.
+  wait_vmcnt<0>();
+  __syncthreads();
+  float* xo = reinterpret_cast<float*>(&sm) + wq * (DT * 16 * 64);
+  if (wk == 1) {
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) xo[(dt * 16 + r) * 64 + lane] = acc[dt][r];
+  }
+  __syncthreads();
+  if (wk == 1) return;
+  uint16_t* orow = dq + row * D;
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+    for (int gq = 0; gq < 4; ++gq) {
+      float v[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = 4 * gq + e;
+        v[e] = scale * (acc[dt][r] + xo[(dt * 16 + r) * 64 + lane]);
+      }
+      *reinterpret_cast<uint2*>(orow + 32 * dt + 8 * gq + 4 * hf) =
+          make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+    }
+}
+
+// ------------------------------------------------------------------ dK dV --
+
+template <int D>
+struct DkvSmem {
+  uint16_t q[2][64 * D];    // Q_i token-major
+  uint16_t dout[2][64 * D]; // dO_i token-major
+  uint16_t qt[2][D * 64];   // Q_i^T
+  uint16_t dot[2][D * 64];  // dO_i^T
+  float ls[2][64];          // lse_i
+  float dl[2][64];          // delta_i
+};
+
+template <int D>
+__device__ __forceinline__ void dkdv_issue(const uint16_t* qc, const uint16_t* doc, const uint16_t* qt,
+                                           const uint16_t* dot, const float* lse, const float* delta, long long off,
+                                           long long roff, uint16_t* qs, uint16_t* ds, uint16_t* qts, uint16_t* dts,
+                                           float* lss, float* dls, int w, const uint32_t* ko, const uint32_t* vo,
+                                           int lane) {
+  issue_k_tile<D>(make_rsrc(qc + off, 64 * D * 2), qs, w, ko);
+  issue_k_tile<D>(make_rsrc(doc + off, 64 * D * 2), ds, w, ko);
+  issue_v_tile<D>(make_rsrc(qt + off, 64 * D * 2), qts, w, vo);
+  issue_v_tile<D>(make_rsrc(dot + off, 64 * D * 2), dts, w, vo);
+  // 64 floats each, one dword per lane of wavefronts 0 and 1.
+  if (w == 0)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(make_rsrc(lse + roff, 256), (lds_ptr_t)lss, 4, lane * 4, 0, 0, 0);
+  else if (w == 1)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(make_rsrc(delta + roff, 256), (lds_ptr_t)dls, 4, lane * 4, 0, 0, 0);
+}
+
+template <int D, bool PARTIAL>
+__global__ void __launch_bounds__(kThreads, 1) bwd_dkdv(const uint16_t* __restrict__ qc,
+                                                        const uint16_t* __restrict__ qt,
+                                                        const uint16_t* __restrict__ kc,
+                                                        const uint16_t* __restrict__ vc,
+                                                        const uint16_t* __restrict__ doc,
+                                                        const uint16_t* __restrict__ dot,
+                                                        const float* __restrict__ lse,
+                                                        const float* __restrict__ delta,
+                                                        const int32_t* __restrict__ qoff,
+                                                        const int32_t* __restrict__ qcnt,
+                                                        const int32_t* __restrict__ qlist, int topk, float scale,
+                                                        float scale_log2, uint16_t* __restrict__ dk,
+                                                        uint16_t* __restrict__ dv, KGeom g, Placement pl) {
+  constexpr int DC = D / 16, DT = D / 32;
+  __shared__ __attribute__((aligned(16))) DkvSmem<D> sm;
+  int j, h, b;
+  if (!map_workgroup(g, pl, j, h, b)) return;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wk = w & 1, wq = w >> 1;
+  const int hf = lane >> 5, n = lane & 31;
+  const int key = 32 * wk + n;
+  const long long bh = (long long)b * g.H + h;
+  const long long hbase = bh * g.Np * D, rbase = bh * g.Np;
+  const long long krow = rbase + 64LL * j + key;
+  const TileOffsets<D> toff(w, lane);
+  const int cnt = qcnt[bh * g.nc + j];
+  const int32_t* list = qlist + bh * (long long)g.nc * topk + qoff[bh * g.nc + j];
+
+  if (cnt > 0)
+    dkdv_issue<D>(qc + hbase, doc + hbase, qt + hbase, dot + hbase, lse, delta, 64LL * list[0] * D,
+                  rbase + 64LL * list[0], sm.q[0], sm.dout[0], sm.qt[0], sm.dot[0], sm.ls[0], sm.dl[0], w, toff.k,
+                  toff.v, lane);
+  bf16x8 kb[DC], vb[DC];
+#pragma unroll
+  for (int dc = 0; dc < DC; ++dc) {
+    kb[dc] = *reinterpret_cast<const bf16x8*>(kc + krow * D + 16 * dc + 8 * hf);
+    vb[dc] = *reinterpret_cast<const bf16x8*>(vc + krow * D + 16 * dc + 8 * hf);
+  }
+  float kmask = 1.f;
+  if (PARTIAL) {
+    int ct, cy, cx;
+    cube_coords(g, j, ct, cy, cx);
+    kmask = local_valid(g, ct, cy, cx, key) ? 1.f : 0.f;
+  }
+  const int prow = pi_row(n);
+  f32x16 ka[DT], va[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) ka[dt] = va[dt] = f32x16{};
+
+  for (int mb = 0; mb < cnt; mb += 2) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int m = mb + u;
+      if (m < cnt) {
+        wait_vmcnt<0>();
+        pipeline_barrier();
+        if (m + 1 < cnt) {
+          const int in = list[m + 1];
+          dkdv_issue<D>(qc + hbase, doc + hbase, qt + hbase, dot + hbase, lse, delta, 64LL * in * D,
+                        rbase + 64LL * in, sm.q[u ^ 1], sm.dout[u ^ 1], sm.qt[u ^ 1], sm.dot[u ^ 1], sm.ls[u ^ 1],
+                        sm.dl[u ^ 1], w, toff.k, toff.v, lane);
+        }
+        // S = Q K^T and dP = dO V^T for this wave's 32 queries x 32 keys:
+        // register r holds query 32 wq + 16 (r/8) + 8 hf + r%8.
+        f32x16 s = f32x16{}, dp = f32x16{};
+        {
+          bf16x8 qa[DC];
+          read_k<D>(sm.q[u], wq, hf, prow, qa);
+#pragma unroll
+          for (int dc = 0; dc < DC; ++dc) s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[dc], kb[dc], s, 0, 0, 0);
+        }
+        {
+          bf16x8 da[DC];
+          read_k<D>(sm.dout[u], wq, hf, prow, da);
+#pragma unroll
+          for (int dc = 0; dc < DC; ++dc) dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da[dc], vb[dc], dp, 0, 0, 0);
+        }
+        const int q0 = 32 * wq + 8 * hf;
+        const f32x4* lsp = reinterpret_cast<const f32x4*>(&sm.ls[u][0]);
+        const f32x4* dlp = reinterpret_cast<const f32x4*>(&sm.dl[u][0]);
+        const f32x4 l4[4] = {lsp[q0 / 4], lsp[q0 / 4 + 1], lsp[(q0 + 16) / 4], lsp[(q0 + 16) / 4 + 1]};
+        const f32x4 d4[4] = {dlp[q0 / 4], dlp[q0 / 4 + 1], dlp[(q0 + 16) / 4], dlp[(q0 + 16) / 4 + 1]};
+        uint32_t pw[8], sw[8];
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+          const int r0 = 2 * r, r1 = 2 * r + 1;
+          const float p0 = kmask * __builtin_amdgcn_exp2f(fmaf(s[r0], scale_log2, -l4[r0 / 4][r0 % 4] * kLog2e));
+          const float p1 = kmask * __builtin_amdgcn_exp2f(fmaf(s[r1], scale_log2, -l4[r1 / 4][r1 % 4] * kLog2e));
+          const f32x2 p2 = {p0, p1};
+          const f32x2 d2 = {p0 * (dp[r0] - d4[r0 / 4][r0 % 4]), p1 * (dp[r1] - d4[r1 / 4][r1 % 4])};
+          pw[r] = __builtin_bit_cast(uint32_t, __builtin_convertvector(p2, bf16x2));
+          sw[r] = __builtin_bit_cast(uint32_t, __builtin_convertvector(d2, bf16x2));
+        }
+        const bf16x8 pb[2] = {__builtin_bit_cast(bf16x8, make_uint4(pw[0], pw[1], pw[2], pw[3])),
+                              __builtin_bit_cast(bf16x8, make_uint4(pw[4], pw[5], pw[6], pw[7]))};
+        const bf16x8 sb[2] = {__builtin_bit_cast(bf16x8, make_uint4(sw[0], sw[1], sw[2], sw[3])),
+                              __builtin_bit_cast(bf16x8, make_uint4(sw[4], sw[5], sw[6], sw[7]))};
+        {
+          bf16x8 ta[DT][2];
+          read_v<D>(sm.dot[u], wq, hf, n, ta);
+#pragma unroll
+          for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk) va[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ta[dt][kk], pb[kk], va[dt], 0, 0, 0);
+        }
+        {
+          bf16x8 ta[DT][2];
+          read_v<D>(sm.qt[u], wq, hf, n, ta);
+#pragma unroll
+          for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk) ka[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ta[dt][kk], sb[kk], ka[dt], 0, 0, 0);
+        }
+      }
+    }
+  }
+
+  // The two query halves hold partial sums of the same dK^T, dV^T: add them.
+  wait_vmcnt<0>();
+  __syncthreads();
+  float* xk = reinterpret_cast<float*>(&sm) + wk * (2 * DT * 16 * 64);
+  float* xv = xk + DT * 16 * 64;
+  if (wq == 1) {
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        xk[(dt * 16 + r) * 64 + lane] = ka[dt][r];
+        xv[(dt * 16 + r) * 64 + lane] = va[dt][r];
+      }
+  }
+  __syncthreads();
+  if (wq == 1) return;
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+    for (int gq = 0; gq < 4; ++gq) {
+      float fk[4], fv[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = 4 * gq + e;
+        fk[e] = scale * (ka[dt][r] + xk[(dt * 16 + r) * 64 + lane]);
+        fv[e] = va[dt][r] + xv[(dt * 16 + r) * 64 + lane];
+      }
+      const int d = 32 * dt + 8 * gq + 4 * hf;
+      *reinterpret_cast<uint2*>(dk + krow * D + d) = make_uint2(pack_bf16x2(fk[0], fk[1]), pack_bf16x2(fk[2], fk[3]));
+      *reinterpret_cast<uint2*>(dv + krow * D + d) = make_uint2(pack_bf16x2(fv[0], fv[1]), pack_bf16x2(fv[2], fv[3]));
+    }
+}
+
+// Workspace carve-up: delta [B H Np] f32 | cnt [B H Nc] | off [B H Nc] | list [B H Nc topk] int32.
+struct BwdWs {
+  float* delta;
+  int32_t *cnt, *off, *list;
+};
+
+inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+inline BwdWs carve(const KGeom& g, int topk, void* ws) {
+  char* p = static_cast<char*>(ws);
+  const size_t bh = (size_t)g.B * g.H;
+  BwdWs w;
+  w.delta = reinterpret_cast<float*>(p);
+  p += align256(bh * g.Np * sizeof(float));
+  w.cnt = reinterpret_cast<int32_t*>(p);
+  p += align256(bh * g.nc * sizeof(int32_t));
+  w.off = reinterpret_cast<int32_t*>(p);
+  p += align256(bh * g.nc * sizeof(int32_t));
+  w.list = reinterpret_cast<int32_t*>(p);
+  return w;
+}
+
+template <int D, bool PARTIAL>
+hipError_t launch_bwd_t(const KGeom& g, const uint16_t* qc, const uint16_t* qt, const uint16_t* kc,
+                        const uint16_t* kt, const uint16_t* vc, const uint16_t* oc, const uint16_t* doc,
+                        const uint16_t* dot, const float* lse, const int32_t* idx, int topk, float scale,
+                        uint16_t* dq, uint16_t* dk, uint16_t* dv, void* ws, hipStream_t s) {
+  const BwdWs w = carve(g, topk, ws);
+  const long long rows = (long long)g.B * g.H * g.Np;
+  bwd_delta<D><<<dim3((unsigned)((rows * (D / 8) + 255) / 256)), dim3(256), 0, s>>>(oc, doc, w.delta, rows);
+  const dim3 tgrid((g.nc + 3) / 4, g.B * g.H);
+  bwd_count<<<tgrid, dim3(256), 0, s>>>(idx, topk, w.cnt, g);
+  bwd_scan<<<dim3(g.B * g.H), dim3(256), 0, s>>>(w.cnt, w.off, g);
+  bwd_fill<<<tgrid, dim3(256), 0, s>>>(idx, topk, w.off, w.list, g);
+  const Placement pl = make_placement(g);
+  const float scale_log2 = scale * kLog2e;
+  bwd_dq<D, PARTIAL><<<dim3(grid_size(g)), dim3(kThreads), 0, s>>>(qc, kc, kt, vc, doc, lse, w.delta, idx, topk,
+                                                                    scale, scale_log2, dq, g, pl);
+  bwd_dkdv<D, PARTIAL><<<dim3(grid_size(g)), dim3(kThreads), 0, s>>>(qc, qt, kc, vc, doc, dot, lse, w.delta, w.off,
+                                                                      w.cnt, w.list, topk, scale, scale_log2, dk, dv,
+                                                                      g, pl);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+size_t attn_bwd_workspace_bytes(const KGeom& g, int topk) {
+  const size_t bh = (size_t)g.B * g.H;
+  return align256(bh * g.Np * sizeof(float)) + 2 * align256(bh * g.nc * sizeof(int32_t)) +
+         align256(bh * g.nc * (size_t)topk * sizeof(int32_t));
+}
+
+hipError_t launch_attn_bwd(const KGeom& g, const uint16_t* qc, const uint16_t* qt, const uint16_t* kc,
+                           const uint16_t* kt, const uint16_t* vc, const uint16_t* oc, const uint16_t* doc,
+                           const uint16_t* dot, const float* lse, const int32_t* idx, int topk, float scale,
+                           uint16_t* dq, uint16_t* dk, uint16_t* dv, void* ws, hipStream_t s) {
+  if (g.D == 64) {
+    if (g.partial) return launch_bwd_t<64, true>(g, qc, qt, kc, kt, vc, oc, doc, dot, lse, idx, topk, scale, dq, dk, dv, ws, s);
+    return launch_bwd_t<64, false>(g, qc, qt, kc, kt, vc, oc, doc, dot, lse, idx, topk, scale, dq, dk, dv, ws, s);
+  }
+  if (g.partial) return launch_bwd_t<128, true>(g, qc, qt, kc, kt, vc, oc, doc, dot, lse, idx, topk, scale, dq, dk, dv, ws, s);
+  return launch_bwd_t<128, false>(g, qc, qt, kc, kt, vc, oc, doc, dot, lse, idx, topk, scale, dq, dk, dv, ws, s);
+}
+
+}  // namespace vsa

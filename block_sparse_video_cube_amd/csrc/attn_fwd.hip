@@ -48,25 +48,6 @@ struct Smem {
   uint16_t v[2][D * 64];
 };
 
-// Padded keys of key cube j take no weight: their logits become -inf.
-// Accumulator register r of lane half hf holds local key
-// 32 wk + 16 (r/8) + 8 hf + r%8, i.e. local (t, y, x) =
-// (2 wk + r/8, 2 hf + (r%8)/4, r%4): the t and x tests are the same for the
-// whole wavefront, the y test depends on the lane half only.  Branch-free, so
-// it sits inside the interleaved region of a step.
-__device__ __forceinline__ void mask_keys(f32x16& s, const KGeom& g, int j, int wk, int hf) {
-  int ct, cy, cx;
-  cube_coords(g, j, ct, cy, cx);
-  const int nt = g.T - 4 * ct, ny = g.Hg - 4 * cy, nx = g.W - 4 * cx;
-  const bool y0 = 2 * hf < ny, y1 = 2 * hf + 1 < ny;
-#pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    const bool tx = (2 * wk + (r >> 3) < nt) && ((r & 3) < nx);
-    const bool ok = tx && (((r >> 2) & 1) ? y1 : y0);
-    s[r] = ok ? s[r] : -INFINITY;
-  }
-}
-
 __device__ __forceinline__ float max16(const f32x16& s) {
   const float a = fmaxf(fmaxf(s[0], s[1]), s[2]), b = fmaxf(fmaxf(s[3], s[4]), s[5]);
   const float c = fmaxf(fmaxf(s[6], s[7]), s[8]), d = fmaxf(fmaxf(s[9], s[10]), s[11]);
@@ -137,16 +118,6 @@ __device__ __forceinline__ void step(const bf16x8 (&ka)[D / 16], const bf16x8 (&
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
     __builtin_amdgcn_sched_group_barrier(0x002, VPS, 0);
   }
-}
-
-// Direct-to-LDS loads of this wave's share of one K tile (buffer resource kr
-// over the tile, lane offsets off).
-template <int D>
-__device__ __forceinline__ void issue_k_tile(__amdgpu_buffer_rsrc_t kr, uint16_t* klds, int w, const uint32_t* off) {
-  constexpr int NI = D / 32, KRPI = 512 / D;
-#pragma unroll
-  for (int e = 0; e < NI; ++e)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, (lds_ptr_t)(klds + (w * NI + e) * KRPI * D), 16, off[e], 0, 0, 0);
 }
 
 template <int D, bool PARTIAL>

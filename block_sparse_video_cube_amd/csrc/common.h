@@ -94,4 +94,9 @@ hipError_t launch_linear(const KGeom& g, const uint16_t* qc, const uint16_t* kc,
                          hipStream_t s);
 size_t linear_workspace_bytes(const KGeom& g);
 hipError_t launch_sta_index(const KGeom& g, int wt, int wh, int ww, int32_t* idx, hipStream_t s);
+size_t attn_bwd_workspace_bytes(const KGeom& g, int topk);
+hipError_t launch_attn_bwd(const KGeom& g, const uint16_t* qc, const uint16_t* qt, const uint16_t* kc,
+                           const uint16_t* kt, const uint16_t* vc, const uint16_t* oc, const uint16_t* doc,
+                           const uint16_t* dot, const float* lse, const int32_t* idx, int topk, float scale,
+                           uint16_t* dq, uint16_t* dk, uint16_t* dv, void* ws, hipStream_t s);
 }  // namespace vsa

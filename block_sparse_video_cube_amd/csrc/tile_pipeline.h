@@ -93,6 +93,25 @@ __device__ __forceinline__ void load_v_tile(const uint16_t* vtile, uint16_t* vld
     __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (lds_ptr_t)(vlds + (w * NI + i) * 8 * 64), 16, off.v[i], 0, 0, 0);
 }
 
+// The same loads from a buffer resource built by the caller and this wave's
+// lane offsets (TileOffsets::k or ::v).  Kernels whose tiles change every
+// step use these.
+template <int D>
+__device__ __forceinline__ void issue_k_tile(__amdgpu_buffer_rsrc_t kr, uint16_t* klds, int w, const uint32_t* off) {
+  constexpr int NI = D / 32, KRPI = 512 / D;
+#pragma unroll
+  for (int e = 0; e < NI; ++e)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, (lds_ptr_t)(klds + (w * NI + e) * KRPI * D), 16, off[e], 0, 0, 0);
+}
+
+template <int D>
+__device__ __forceinline__ void issue_v_tile(__amdgpu_buffer_rsrc_t vr, uint16_t* vlds, int w, const uint32_t* off) {
+  constexpr int NI = D / 32;
+#pragma unroll
+  for (int e = 0; e < NI; ++e)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (lds_ptr_t)(vlds + (w * NI + e) * 8 * 64), 16, off[e], 0, 0, 0);
+}
+
 // K fragments of S^T = K Q^T for this wave's key half (rows in pi order).
 template <int D>
 __device__ __forceinline__ void read_k(const uint16_t* klds, int wk, int hf, int prow, bf16x8 (&ka)[D / 16]) {
@@ -113,6 +132,25 @@ __device__ __forceinline__ void read_v(const uint16_t* vlds, int wk, int hf, int
       const int chunk = 4 * wk + 2 * kk + hf;
       va[dt][kk] = *reinterpret_cast<const bf16x8*>(vlds + vrow * 64 + ((chunk ^ v_swz(vrow)) * 8));
     }
+  }
+}
+
+// Padded keys of key cube j take no weight: their logits become -inf.
+// In an S^T = K Q^T tile (keys in rows, read in pi order) accumulator
+// register r of lane half hf holds local key 32 wk + 16 (r/8) + 8 hf + r%8,
+// i.e. local (t, y, x) = (2 wk + r/8, 2 hf + (r%8)/4, r%4): the t and x tests
+// are the same for the whole wavefront, the y test depends on the lane half
+// only.  Branch-free, so it can sit inside an interleaved region.
+__device__ __forceinline__ void mask_keys(f32x16& s, const KGeom& g, int j, int wk, int hf) {
+  int ct, cy, cx;
+  cube_coords(g, j, ct, cy, cx);
+  const int nt = g.T - 4 * ct, ny = g.Hg - 4 * cy, nx = g.W - 4 * cx;
+  const bool y0 = 2 * hf < ny, y1 = 2 * hf + 1 < ny;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const bool tx = (2 * wk + (r >> 3) < nt) && ((r & 3) < nx);
+    const bool ok = tx && (((r >> 2) & 1) ? y1 : y0);
+    s[r] = ok ? s[r] : -INFINITY;
   }
 }
 

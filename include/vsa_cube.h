@@ -187,6 +187,33 @@ int32_t vsa_sparse_attn_fwd(const vsa_geom* g, const uint16_t* qc, const uint16_
                             float softmax_scale, uint16_t* oc, float* oc_f32,
                             float* lse, void* stream);
 
+/* Backward of the fine stage (the gradient of vsa_sparse_attn_fwd with respect
+ * to Q, K and V; VSA and SLA are trained, FastVideo sparse-distillation
+ * article section "2. 视频稀疏注意力VSA", TurboDiffusion article section
+ * "稀疏、蒸馏与全链路量化").  For an output gradient dO, with P the softmax
+ * weights of the forward recovered from its lse:
+ *   dV_j = sum_i P_ij^T dO_i,  dS_ij = P_ij * (dO_i V_j^T - rowsum(dO_i * O_i)),
+ *   dQ_i = scale sum_j dS_ij K_j,  dK_j = scale sum_i dS_ij^T Q_i,
+ * over the blocks (i, j) of idx.  No atomics: the result does not depend on
+ * scheduling.
+ * Inputs (all [B, heads, Np, D] bf16 unless stated; *_t: DIM_MAJOR layout of
+ * the same tensor, [B, heads, Nc, D, 64], from vsa_cube_permute):
+ *   qc, qt: Q; kc, kt: K; vc: V (TOKEN_MAJOR); oc: the forward output;
+ *   doc, dot: dO, whose padded rows must be zero (as vsa_cube_permute writes
+ *   them); lse: fp32 [B, heads, Np], the forward's lse output; idx, topk:
+ *   the forward's block lists (rows ascending, entries distinct).
+ * Outputs (bf16 [B, heads, Np, D] TOKEN_MAJOR, fp32 accumulation): dq, dk, dv;
+ * padded rows hold zero (dq: padded query rows carry no gradient).
+ * ws: at least vsa_attn_bwd_workspace_bytes(g, topk) bytes.
+ * Limits as vsa_select_topk (n_cubes <= VSA_MAX_CUBES). */
+size_t vsa_attn_bwd_workspace_bytes(const vsa_geom* g, int32_t topk);
+int32_t vsa_sparse_attn_bwd(const vsa_geom* g, const uint16_t* qc, const uint16_t* qt,
+                            const uint16_t* kc, const uint16_t* kt, const uint16_t* vc,
+                            const uint16_t* oc, const uint16_t* doc, const uint16_t* dot,
+                            const float* lse, const int32_t* idx, int32_t topk,
+                            float softmax_scale, uint16_t* dq, uint16_t* dk, uint16_t* dv,
+                            void* ws, size_t ws_bytes, void* stream);
+
 /* Linear branch and combine: oc = bf16(o_sparse + O_lin), O_lin over the valid
  * keys of the cubes NOT in idx[b, h, i, :] (0 when none are left).
  * qc, kc: TOKEN_MAJOR bf16; vt: DIM_MAJOR bf16; idx as for the fine stage

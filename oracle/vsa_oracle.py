@@ -434,8 +434,9 @@ def sparse_attention_bwd(qc, kc, vc, valid, idx, scale, doc, heads: Optional[Seq
             gq, gk, gv, keys = attention_cube_bwd(qc[b, h, 64 * i:64 * i + 64], kc[b, h], vc[b, h], valid,
                                                   idx[b, h, i], scale, doc[b, h, 64 * i:64 * i + 64])
             dq[b, h, 64 * i:64 * i + 64] = gq
-            np.add.at(dk[b, h], keys, gk)
-            np.add.at(dv[b, h], keys, gv)
+            for t, j in enumerate(idx[b, h, i]):  # key rows 64 j .. 64 j + 63 are rows 64 t .. of gk, gv
+                dk[b, h, 64 * j:64 * j + 64] += gk[64 * t:64 * t + 64]
+                dv[b, h, 64 * j:64 * j + 64] += gv[64 * t:64 * t + 64]
     return dq, dk, dv
 
 

@@ -42,3 +42,16 @@ def topk_valid_under(scores: np.ndarray, chosen: np.ndarray, k: int, rel: float 
     mask = np.zeros(scores.size, dtype=bool)
     mask[chosen] = True
     return bool(np.all(scores[mask] >= kth - tol) and np.all(scores[~mask] <= kth + tol))
+
+
+def assert_close_rel(got: np.ndarray, ref: np.ndarray, what: str, max_rel: float, mean_rel: float):
+    """Errors measured against the scale of the reference tensor itself:
+    max|d| <= max_rel * max|ref| and mean|d| <= mean_rel * mean|ref|."""
+    assert got.shape == ref.shape, (got.shape, ref.shape)
+    assert np.all(np.isfinite(got)), f"{what}: non-finite values"
+    err = np.abs(got - ref)
+    mx, mn = float(err.max()), float(err.mean())
+    rmx, rmn = float(np.abs(ref).max()), float(np.abs(ref).mean())
+    print(f"{what}: max|d|={mx:.3e} ({mx / max(rmx, 1e-30):.2e} of max|ref| {rmx:.3e}), "
+          f"mean|d|={mn:.3e} ({mn / max(rmn, 1e-30):.2e} of mean|ref| {rmn:.3e})")
+    assert mx <= max_rel * rmx and mn <= mean_rel * rmn, f"{what}: max {mx:.3e} mean {mn:.3e}"
