@@ -45,6 +45,9 @@ def parse():
     ap.add_argument("--workload", default="wan1.3b")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target oracle sample time")
+    ap.add_argument("--backward", action="store_true",
+                    help="also time the backward of the fine stage (dQ, dK, dV) after the forward steps; "
+                         "reported under 'backward', not in 'value'")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="only run a plain device-to-device copy of this many bytes (3 times) and exit; "
                          "used to calibrate the FETCH_SIZE / WRITE_SIZE counters")
@@ -128,6 +131,71 @@ def cpu_baseline(wl, budget_s: float):
         "ms_per_layer": layer_s * 1e3,
         "host_cpus": os.cpu_count(),
         "cpu_model": platform.processor() or platform.machine(),
+    }
+
+
+def time_backward(vsa, wl, q, k, v, o, qc, kc, vt, idx, args, dev):
+    """Backward of the fine stage on the layer's last forward state.
+
+    One backward step: the extra layouts it needs (Q and K cubes transposed, V
+    token-major, dO both ways), the forward's O and lse (one fine-stage call),
+    then vsa_sparse_attn_bwd and the three unpermutes to raster gradients.
+    Flops are counted as 2.5x the forward's (five 64x64xD products per block:
+    the usual accounting; the kernels recompute S and dP in both passes).
+    """
+    import torch
+
+    rng = np.random.default_rng(7)
+    do = torch.from_numpy(rng.standard_normal(tuple(q.shape), dtype=np.float32)).to(dev).to(torch.bfloat16)
+    B, H, D = wl.batch, wl.heads, wl.head_dim
+    oc, _, lse = vsa.sparse_attn_fwd(qc, kc, vt, idx, wl.grid, wl.softmax_scale, want_lse=True)
+    ws = torch.empty(max(16, vsa._lib.load().vsa_attn_bwd_workspace_bytes(
+        vsa.make_geom(B, H, D, wl.grid), wl.topk)), dtype=torch.uint8, device=dev)
+
+    def layouts():
+        return (vsa.cube_permute(q, wl.grid, layout="dim"), vsa.cube_permute(k, wl.grid, layout="dim"),
+                vsa.cube_permute(v, wl.grid), vsa.cube_permute(do, wl.grid),
+                vsa.cube_permute(do, wl.grid, layout="dim"))
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record()
+        qt, kt, vc, doc, dot = layouts()
+        if ev is not None:
+            ev[1].record()
+        dq, dk, dv = vsa.sparse_attn_bwd(qc, qt, kc, kt, vc, oc, doc, dot, lse, idx, wl.grid, wl.softmax_scale,
+                                         workspace=ws)
+        if ev is not None:
+            ev[2].record()
+        outs = [vsa.cube_unpermute(x, wl.grid) for x in (dq, dk, dv)]
+        if ev is not None:
+            ev[3].record()
+        return outs
+
+    for _ in range(max(1, args.warmup)):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for s_ in range(args.steps):
+        outs = step(evs[s_])
+    t1.record()
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / args.steps
+    kern = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+    lay = float(np.median([e[0].elapsed_time(e[1]) for e in evs]))
+    unp = float(np.median([e[2].elapsed_time(e[3]) for e in evs]))
+    finite = all(bool(torch.isfinite(x.float()).all()) for x in outs)
+    flops = 2.5 * wl.fine_flops
+    return {
+        "ms_per_layer": round(ms, 4),
+        "stage_ms": {"layouts": round(lay, 4), "bwd_kernels": round(kern, 4), "unpermute": round(unp, 4)},
+        "bwd_kernels_tflops": round(flops / (kern * 1e-3) / 1e12, 2),
+        "frac_of_bf16_peak": round(flops / (kern * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+        "flops": flops,
+        "finite": finite,
     }
 
 
@@ -283,6 +351,8 @@ def main():
         "wall_s_timed": round(wall, 3),
         "device": torch.cuda.get_device_name(0),
     }
+    if args.backward:
+        res["backward"] = time_backward(vsa, wl, q, k, v, o, qc, kc, vt, idx, args, dev)
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
     print(json.dumps(res))

@@ -157,3 +157,27 @@ def test_sta_entry_points(lib):
     assert lib.vsa_sta_index(g, 3, 0, 3, P, None) == _lib.VSA_ERR_WINDOW
     assert lib.vsa_sta_index(g, 3, 3, -1, P, None) == _lib.VSA_ERR_WINDOW
     assert lib.vsa_sta_index(geom(D=48), 3, 3, 3, P, None) == _lib.VSA_ERR_HEAD_DIM
+
+
+def test_backward_entry_point_validation(lib):
+    from block_sparse_video_cube_amd import _lib
+
+    g = geom()
+    P = FAKE
+    ws = lib.vsa_attn_bwd_workspace_bytes(g, 2)
+    # delta (B H Np f32) + counts + offsets (B H Nc) + lists (B H Nc k), each 256-byte aligned
+    assert ws >= 2 * 512 * 4 + 2 * 2 * 8 * 4 + 2 * 8 * 2 * 4
+    assert lib.vsa_attn_bwd_workspace_bytes(g, 0) == 0
+    assert lib.vsa_attn_bwd_workspace_bytes(g, 9) == 0
+    args = [P] * 10  # qc qt kc kt vc oc doc dot lse idx
+    outs = [P] * 3
+    assert lib.vsa_sparse_attn_bwd(g, *args[:9], None, 2, 0.125, *outs, P, ws, None) == _lib.VSA_ERR_NULL
+    assert lib.vsa_sparse_attn_bwd(g, *args, 2, 0.125, P, P, None, P, ws, None) == _lib.VSA_ERR_NULL
+    assert lib.vsa_sparse_attn_bwd(g, ODD, *args[1:], 2, 0.125, *outs, P, ws, None) == _lib.VSA_ERR_ALIGN
+    assert lib.vsa_sparse_attn_bwd(g, *args, 0, 0.125, *outs, P, ws, None) == _lib.VSA_ERR_TOPK
+    assert lib.vsa_sparse_attn_bwd(g, *args, 9, 0.125, *outs, P, ws, None) == _lib.VSA_ERR_TOPK
+    assert lib.vsa_sparse_attn_bwd(g, *args, 2, -1.0, *outs, P, ws, None) == _lib.VSA_ERR_SCALE
+    assert lib.vsa_sparse_attn_bwd(g, *args, 2, float("nan"), *outs, P, ws, None) == _lib.VSA_ERR_SCALE
+    assert lib.vsa_sparse_attn_bwd(g, *args, 2, 0.125, *outs, P, ws - 1, None) == _lib.VSA_ERR_WORKSPACE
+    big = geom(grid=(4 * 17, 4 * 16, 4 * 16))
+    assert lib.vsa_sparse_attn_bwd(big, *args, 2, 0.125, *outs, P, 1 << 40, None) == _lib.VSA_ERR_GEOMETRY
