@@ -45,6 +45,8 @@ def parse():
     ap.add_argument("--workload", default="wan1.3b")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target oracle sample time")
+    ap.add_argument("--k-raster", action="store_true",
+                    help="let the fine stage gather K tiles from raster rows too (no K permute)")
     ap.add_argument("--backward", action="store_true",
                     help="also time the backward of the fine stage (dQ, dK, dV) after the forward steps; "
                          "reported under 'backward', not in 'value'")
@@ -137,7 +139,7 @@ def cpu_baseline(wl, budget_s: float):
 def time_backward(vsa, wl, q, k, v, o, qc, kc, vt, idx, args, dev):
     """Backward of the fine stage on the layer's last forward state.
 
-    One backward step: the extra layouts it needs (Q and K cubes transposed, V
+    One backward step: the layouts it reads (Q and K cube-major both ways, V
     token-major, dO both ways), the forward's O and lse (one fine-stage call),
     then vsa_sparse_attn_bwd and the three unpermutes to raster gradients.
     Flops are counted as 2.5x the forward's (five 64x64xD products per block:
@@ -148,11 +150,16 @@ def time_backward(vsa, wl, q, k, v, o, qc, kc, vt, idx, args, dev):
     rng = np.random.default_rng(7)
     do = torch.from_numpy(rng.standard_normal(tuple(q.shape), dtype=np.float32)).to(dev).to(torch.bfloat16)
     B, H, D = wl.batch, wl.heads, wl.head_dim
+    qc = vsa.cube_permute(q, wl.grid, out=qc)
+    kc = vsa.cube_permute(k, wl.grid, out=kc)
     oc, _, lse = vsa.sparse_attn_fwd(qc, kc, vt, idx, wl.grid, wl.softmax_scale, want_lse=True)
     ws = torch.empty(max(16, vsa._lib.load().vsa_attn_bwd_workspace_bytes(
         vsa.make_geom(B, H, D, wl.grid), wl.topk)), dtype=torch.uint8, device=dev)
 
     def layouts():
+        # The raster forward keeps no cube-major Q, K: the backward makes every layout it reads.
+        vsa.cube_permute(q, wl.grid, out=qc)
+        vsa.cube_permute(k, wl.grid, out=kc)
         return (vsa.cube_permute(q, wl.grid, layout="dim"), vsa.cube_permute(k, wl.grid, layout="dim"),
                 vsa.cube_permute(v, wl.grid), vsa.cube_permute(do, wl.grid),
                 vsa.cube_permute(do, wl.grid, layout="dim"))
@@ -244,8 +251,13 @@ def main():
     of = torch.empty((B, H, d.rows, D), dtype=torch.float32, device=dev) if wl.linear else None
     oc2 = torch.empty_like(qc) if wl.linear else None
 
-    stages = ["permute", "select", "fine", "linear", "unpermute"] if wl.linear else \
-        ["permute", "select", "fine", "unpermute"]
+    # Without the linear branch the fine stage reads Q and writes the output in
+    # raster order: Q is only pooled, K is pooled and permuted in one pass
+    # (contiguous 16 KB tiles stream faster than tiles gathered from 64 raster
+    # rows; --k-raster gathers them instead), V is permuted into the
+    # cube-transposed layout.  The linear branch works on cube-major rows, so
+    # the hybrid layer keeps the permute / unpermute pair.
+    stages = ["permute", "select", "fine", "linear", "unpermute"] if wl.linear else ["pool", "select", "fine"]
 
     def step(ev=None):
         def mark(i):
@@ -253,12 +265,17 @@ def main():
                 ev[i].record()
 
         mark(0)
-        if wl.pattern == "sta":
-            vsa.cube_permute(q, wl.grid, out=qc)
-            vsa.cube_permute(k, wl.grid, out=kc)
-        else:
+        if wl.linear:
             vsa.cube_permute_pool(q, wl.grid, out=qc, mean_out=qbar)
             vsa.cube_permute_pool(k, wl.grid, out=kc, mean_out=kbar)
+        elif wl.pattern != "sta":
+            vsa.cube_pool(q, wl.grid, mean_out=qbar)
+            if args.k_raster:
+                vsa.cube_pool(k, wl.grid, mean_out=kbar)
+            else:
+                vsa.cube_permute_pool(k, wl.grid, out=kc, mean_out=kbar)
+        elif not args.k_raster:
+            vsa.cube_permute(k, wl.grid, out=kc)
         vsa.cube_permute(v, wl.grid, layout="dim", out=vt)
         mark(1)
         if wl.pattern == "sta":
@@ -267,15 +284,16 @@ def main():
         else:
             vsa.select_topk_pooled(qbar, kbar, wl.grid, wl.topk, out=idx, workspace=ws_sel)
         mark(2)
+        if not wl.linear:
+            vsa.sparse_attn_fwd_raster(q, k if args.k_raster else kc, vt, idx, wl.grid, wl.softmax_scale, out=o)
+            mark(3)
+            return
         vsa.sparse_attn_fwd(qc, kc, vt, idx, wl.grid, wl.softmax_scale, out=oc, out_f32=of)
         mark(3)
-        res = oc
-        if wl.linear:
-            vsa.linear_branch(qc, kc, vt, idx, of, wl.grid, out=oc2, workspace=ws_lin)
-            mark(4)
-            res = oc2
-        vsa.cube_unpermute(res, wl.grid, out=o)
-        mark(len(stages))
+        vsa.linear_branch(qc, kc, vt, idx, of, wl.grid, out=oc2, workspace=ws_lin)
+        mark(4)
+        vsa.cube_unpermute(oc2, wl.grid, out=o)
+        mark(5)
 
     for _ in range(args.warmup):
         step()
@@ -330,6 +348,7 @@ def main():
             "latent_grid": list(wl.grid), "padded_grid": list(wl.padded_grid),
             "tokens": wl.tokens, "n_cubes": wl.n_cubes, "topk": wl.topk,
             "sparsity": wl.sparsity, "linear_branch": wl.linear, "pattern": wl.pattern,
+            "layout": "cube-major" if wl.linear else ("raster q/k/o" if args.k_raster else "raster q/o"),
             **({"window_cubes": list(wl.window)} if wl.window else {}),
             "computed_blocks": wl.blocks, "fine_flops": flops,
         },

@@ -37,12 +37,14 @@ __all__ = [
     "cube_permute",
     "cube_permute_pool",
     "cube_unpermute",
+    "cube_pool",
     "select_topk",
     "select_topk_pooled",
     "sta_topk",
     "sta_index",
     "sparse_attn_fwd",
     "linear_branch",
+    "sparse_attn_fwd_raster",
     "sparse_attn_bwd",
     "vsa_attention",
     "workspace_bytes",
@@ -115,6 +117,19 @@ def cube_permute_pool(x: torch.Tensor, grid: Sequence[int], out: Optional[torch.
     _lib.check("vsa_cube_permute_pool", _lib.load().vsa_cube_permute_pool(
         g, x.data_ptr(), out.data_ptr(), mean_out.data_ptr(), _stream()))
     return out, mean_out
+
+
+def cube_pool(x: torch.Tensor, grid: Sequence[int], mean_out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """fp32 cube means [B, heads, Nc, D] of raster tokens x (no cube-major copy)."""
+    B, S, Hh, D = x.shape
+    g = make_geom(B, Hh, D, grid)
+    d = geom_dims(g)
+    _need(x, "x", torch.bfloat16, (B, d.tokens, Hh, D))
+    if mean_out is None:
+        mean_out = torch.empty((B, Hh, d.n_cubes, D), dtype=torch.float32, device=x.device)
+    _need(mean_out, "mean", torch.float32, (B, Hh, d.n_cubes, D))
+    _lib.check("vsa_cube_pool", _lib.load().vsa_cube_pool(g, x.data_ptr(), mean_out.data_ptr(), _stream()))
+    return mean_out
 
 
 def cube_unpermute(xc: torch.Tensor, grid: Sequence[int], out: Optional[torch.Tensor] = None) -> torch.Tensor:
@@ -227,6 +242,38 @@ def sparse_attn_fwd(qc: torch.Tensor, kc: torch.Tensor, vt: torch.Tensor, idx: t
         out.data_ptr(), of.data_ptr() if of is not None else None,
         lse.data_ptr() if lse is not None else None, _stream()))
     return out, of, lse
+
+
+def sparse_attn_fwd_raster(q: torch.Tensor, k: torch.Tensor, vt: torch.Tensor, idx: torch.Tensor,
+                           grid: Sequence[int], scale: Optional[float] = None, want_lse: bool = False,
+                           out: Optional[torch.Tensor] = None):
+    """Fine stage on raster-order q and output: returns (o [B, S, heads, D] bf16, lse or None).
+
+    k: raster [B, S, heads, D] (tiles gathered in the kernel) or cube-major [B, heads, Np, D].
+    """
+    B, S, Hh, D = q.shape
+    g = make_geom(B, Hh, D, grid)
+    d = geom_dims(g)
+    topk = int(idx.shape[-1])
+    _need(q, "q", torch.bfloat16, (B, d.tokens, Hh, D))
+    if tuple(k.shape) == (B, Hh, d.rows, D):
+        k_layout = _lib.VSA_LAYOUT_TOKEN_MAJOR
+    else:
+        _need(k, "k", torch.bfloat16, (B, d.tokens, Hh, D))
+        k_layout = _lib.VSA_LAYOUT_RASTER
+    _need(k, "k", torch.bfloat16, tuple(k.shape))
+    _need(vt, "vt", torch.bfloat16, (B, Hh, d.n_cubes, D, 64))
+    _need(idx, "idx", torch.int32, (B, Hh, d.n_cubes, topk))
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty_like(q)
+    _need(out, "o", torch.bfloat16, (B, d.tokens, Hh, D))
+    lse = torch.empty((B, Hh, d.rows), dtype=torch.float32, device=q.device) if want_lse else None
+    _lib.check("vsa_sparse_attn_fwd_raster", _lib.load().vsa_sparse_attn_fwd_raster(
+        g, q.data_ptr(), k.data_ptr(), k_layout, vt.data_ptr(), idx.data_ptr(), topk, float(scale),
+        out.data_ptr(), lse.data_ptr() if lse is not None else None, _stream()))
+    return out, lse
 
 
 def sparse_attn_bwd(qc: torch.Tensor, qt: torch.Tensor, kc: torch.Tensor, kt: torch.Tensor, vc: torch.Tensor,

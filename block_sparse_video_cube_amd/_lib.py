@@ -22,6 +22,7 @@ VSA_ERR_WINDOW = 10
 
 VSA_LAYOUT_TOKEN_MAJOR = 0
 VSA_LAYOUT_DIM_MAJOR = 1
+VSA_LAYOUT_RASTER = 2
 VSA_MAX_CUBES = 4096
 
 ENTRY_POINTS = (
@@ -39,6 +40,8 @@ ENTRY_POINTS = (
     "vsa_linear_branch",
     "vsa_sta_topk",
     "vsa_sta_index",
+    "vsa_cube_pool",
+    "vsa_sparse_attn_fwd_raster",
     "vsa_attn_bwd_workspace_bytes",
     "vsa_sparse_attn_bwd",
 )
@@ -108,6 +111,8 @@ def load() -> ctypes.CDLL:
         "vsa_linear_branch": (i32, [G, P, P, P, P, i32, P, P, P, sz, P]),
         "vsa_sta_topk": (i32, [G, i32, i32, i32]),
         "vsa_sta_index": (i32, [G, i32, i32, i32, P, P]),
+        "vsa_cube_pool": (i32, [G, P, P, P]),
+        "vsa_sparse_attn_fwd_raster": (i32, [G, P, P, i32, P, P, i32, ctypes.c_float, P, P, P]),
         "vsa_attn_bwd_workspace_bytes": (sz, [G, i32]),
         "vsa_sparse_attn_bwd": (i32, [G, P, P, P, P, P, P, P, P, P, P, i32, ctypes.c_float, P, P, P, P, sz, P]),
     }

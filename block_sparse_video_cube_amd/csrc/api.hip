@@ -214,6 +214,35 @@ int32_t vsa_select_topk(const vsa_geom* g, const uint16_t* qc, const uint16_t* k
   return launch_status(vsa::launch_select(k, qc, kc, topk, idx, ws, static_cast<hipStream_t>(stream)));
 }
 
+int32_t vsa_sparse_attn_fwd_raster(const vsa_geom* g, const uint16_t* q, const uint16_t* kk, int32_t k_layout,
+                                   const uint16_t* vt, const int32_t* idx, int32_t topk, float softmax_scale,
+                                   uint16_t* o, float* lse, void* stream) {
+  vsa_dims d;
+  vsa::KGeom k;
+  int32_t st = prepare(g, &d, &k);
+  if (st != VSA_OK) return st;
+  if (!q || !kk || !vt || !idx || !o) return VSA_ERR_NULL;
+  if (!aligned16(q) || !aligned16(kk) || !aligned16(vt) || !aligned16(idx) || !aligned16(o) ||
+      (lse && !aligned16(lse)))
+    return VSA_ERR_ALIGN;
+  if (k_layout != VSA_LAYOUT_TOKEN_MAJOR && k_layout != VSA_LAYOUT_RASTER) return VSA_ERR_LAYOUT;
+  if (d.tokens * (int64_t)g->heads * g->head_dim * 2 >= ((int64_t)1 << 31)) return VSA_ERR_GEOMETRY;
+  if (topk < 1 || topk > d.n_cubes) return VSA_ERR_TOPK;
+  if (!(softmax_scale > 0.f) || !isfinite(softmax_scale)) return VSA_ERR_SCALE;
+  return launch_status(vsa::launch_attn_fwd_raster(k, q, kk, k_layout == VSA_LAYOUT_RASTER, vt, idx, topk,
+                                                   softmax_scale, o, lse, static_cast<hipStream_t>(stream)));
+}
+
+int32_t vsa_cube_pool(const vsa_geom* g, const uint16_t* x, float* mean, void* stream) {
+  vsa_dims d;
+  vsa::KGeom k;
+  int32_t st = prepare(g, &d, &k);
+  if (st != VSA_OK) return st;
+  if (!x || !mean) return VSA_ERR_NULL;
+  if (!aligned16(x) || !aligned16(mean)) return VSA_ERR_ALIGN;
+  return launch_status(vsa::launch_permute_pool(k, x, nullptr, mean, static_cast<hipStream_t>(stream)));
+}
+
 int32_t vsa_sparse_attn_fwd(const vsa_geom* g, const uint16_t* qc, const uint16_t* kc, const uint16_t* vt,
                             const int32_t* idx, int32_t topk, float softmax_scale, uint16_t* oc, float* oc_f32,
                             float* lse, void* stream) {

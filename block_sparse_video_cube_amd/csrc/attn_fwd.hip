@@ -120,7 +120,26 @@ __device__ __forceinline__ void step(const bf16x8 (&ka)[D / 16], const bf16x8 (&
   }
 }
 
-template <int D, bool PARTIAL>
+// Buffer resource and lane offsets of the K tile of cube j: the cube-major
+// tile (16 KB contiguous, offsets toff), or gathered from raster rows.
+template <int D, bool PARTIAL, bool RASTER>
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t k_tile_rsrc(const uint16_t* kbase, const KGeom& g, int j,
+                                                             const uint32_t* toff, const uint32_t* roff,
+                                                             const int* rrow, uint32_t* out) {
+  if (RASTER) return raster_tile<D, PARTIAL>(kbase, g, j, roff, rrow, out);
+#pragma unroll
+  for (int e = 0; e < D / 32; ++e) out[e] = toff[e];
+  return make_rsrc(kbase + 64LL * j * D, 64 * D * 2);
+}
+
+// RASTER: Q and the output are raster-order [B, S, heads, D] instead of
+// cube-major rows: Q rows are gathered into registers and output rows
+// scattered back, so the layer needs no permute of Q and no unpermute.
+// KRASTER (with RASTER): K is raster-order too, and its tiles are gathered row
+// by row by the same direct-to-LDS loads (lane offsets from
+// raster_lane_offsets, padded tokens read as zero).  V stays in the
+// cube-transposed layout that the P V product reads.
+template <int D, bool PARTIAL, bool RASTER, bool KRASTER>
 __global__ void __launch_bounds__(kThreads, 2) attn_fwd(const uint16_t* __restrict__ qc,
                                                         const uint16_t* __restrict__ kc,
                                                         const uint16_t* __restrict__ vt,
@@ -139,7 +158,8 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd(const uint16_t* __restri
   const int wq = w & 1, wk = w >> 1;  // wave-uniform
   const int hf = lane >> 5, n = lane & 31;
   const long long bh = (long long)b * g.H + h;
-  const uint16_t* kbase = kc + bh * g.Np * D;
+  // K source: the head's cube-major rows, or (RASTER) its raster rows.
+  const uint16_t* kbase = KRASTER ? kc + ((long long)b * g.S * g.H + h) * D : kc + bh * g.Np * D;
   const uint16_t* vbase = vt + bh * g.Np * D;
   const int32_t* irow = idx + (bh * g.nc + i) * topk;
   const int q = 32 * wq + n;
@@ -154,16 +174,30 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd(const uint16_t* __restri
   // S^T(n+1), P(n) and P(n-1) V(n-1).  V(-1) is a zero tile and P(-1) = 0.
   // Steps come in groups of six so that every buffer index is compile-time.
   const TileOffsets<D> toff(w, lane);
-  // K tile m -> LDS buffer dst (this wave's share).
-  issue_k_tile<D>(make_rsrc(kbase + 64LL * blk(0) * D, 64 * D * 2), sm.k[0], w, toff.k);
+  uint32_t roff[NI];  // RASTER: lane offsets within a cube, and their local rows
+  int rrow[NI];
+  if (KRASTER) raster_lane_offsets<D>(g, w, lane, roff, rrow);
+  uint32_t kto[NI];
+  issue_k_tile<D>(k_tile_rsrc<D, PARTIAL, KRASTER>(kbase, g, blk(0), toff.k, roff, rrow, kto), sm.k[0], w, kto);
+  // Query row q of cube i: its raster token (RASTER) and whether it is real.
+  bool qvalid = true;
+  long long qtok = 0;
+  if (RASTER) {
+    int ct, cy, cx;
+    cube_coords(g, i, ct, cy, cx);
+    const int t = 4 * ct + (q >> 4), y = 4 * cy + ((q >> 2) & 3), x = 4 * cx + (q & 3);
+    qvalid = t < g.T && y < g.Hg && x < g.W;
+    qtok = (((long long)b * g.S + ((long long)t * g.Hg + y) * g.W + x) * g.H + h) * D;
+  }
   bf16x8 qf[DC];
   {
-    const uint16_t* qrow = qc + (bh * g.Np + 64LL * i + q) * D;
+    const uint16_t* qrow = RASTER ? qc + qtok : qc + (bh * g.Np + 64LL * i + q) * D;
 #pragma unroll
-    for (int dc = 0; dc < DC; ++dc) qf[dc] = *reinterpret_cast<const bf16x8*>(qrow + 16 * dc + 8 * hf);
+    for (int dc = 0; dc < DC; ++dc)
+      qf[dc] = qvalid ? *reinterpret_cast<const bf16x8*>(qrow + 16 * dc + 8 * hf) : bf16x8{};
   }
-  issue_k_tile<D>(make_rsrc(kbase + 64LL * blk(1) * D, 64 * D * 2), sm.k[1], w, toff.k);
-  issue_k_tile<D>(make_rsrc(kbase + 64LL * blk(2) * D, 64 * D * 2), sm.k[2], w, toff.k);
+  issue_k_tile<D>(k_tile_rsrc<D, PARTIAL, KRASTER>(kbase, g, blk(1), toff.k, roff, rrow, kto), sm.k[1], w, kto);
+  issue_k_tile<D>(k_tile_rsrc<D, PARTIAL, KRASTER>(kbase, g, blk(2), toff.k, roff, rrow, kto), sm.k[2], w, kto);
   {
     uint4* z = reinterpret_cast<uint4*>(sm.v[1]);
 #pragma unroll
@@ -225,11 +259,10 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd(const uint16_t* __restri
         f32x16 s_next;
         float mx_next;
         bf16x8 p_cur[2];
+        const __amdgpu_buffer_rsrc_t krs = k_tile_rsrc<D, PARTIAL, KRASTER>(kbase, g, blk(nb + 3), toff.k, roff, rrow, kto);
         step<D, PARTIAL>(ka, va, qf, s_cur, s_next, mx_next, p_prev, p_cur, o, l_run, mc, scale_log2, g,
                          blk(nb + 1), wk, hf, make_rsrc(vbase + 64LL * blk(nb) * D, 64 * D * 2),
-                         sm.v[u % 2] + w * NI * 8 * 64, toff.v,
-                         make_rsrc(kbase + 64LL * blk(nb + 3) * D, 64 * D * 2), sm.k[u % 3] + w * NI * KRPI * D,
-                         toff.k);
+                         sm.v[u % 2] + w * NI * 8 * 64, toff.v, krs, sm.k[u % 3] + w * NI * KRPI * D, kto);
         move = __builtin_amdgcn_ballot_w64(mx_next > m_run + lazy_raw) != 0;
         if (resc) {
           // O^T now holds P(0..n-1) V at the previous reference max.
@@ -280,7 +313,7 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd(const uint16_t* __restri
   const float inv = 1.f / l_tot;
   const float c0 = a0 * inv, c1 = a1 * inv;
   const long long row = bh * g.Np + 64LL * i + q;
-  uint16_t* orow = oc + row * D;
+  uint16_t* orow = RASTER ? oc + qtok : oc + row * D;
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
@@ -292,34 +325,48 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd(const uint16_t* __restri
         const int r = 4 * gq + e;
         v[e] = o[dt][r] * c0 + xo[(dt * 16 + r) * 64 + lane] * c1;
       }
-      *reinterpret_cast<uint2*>(orow + d) = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
-      if (oc_f32) *reinterpret_cast<float4*>(oc_f32 + row * D + d) = make_float4(v[0], v[1], v[2], v[3]);
+      if (qvalid) *reinterpret_cast<uint2*>(orow + d) = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+      if (!RASTER && oc_f32) *reinterpret_cast<float4*>(oc_f32 + row * D + d) = make_float4(v[0], v[1], v[2], v[3]);
     }
   if (lse && hf == 0) lse[row] = m * scale + logf(l_tot);
 }
 
 }  // namespace
 
-template <int D, bool PARTIAL>
+template <int D, bool PARTIAL, bool RASTER, bool KRASTER>
 void launch_fwd(const KGeom& g, const uint16_t* qc, const uint16_t* kc, const uint16_t* vt, const int32_t* idx,
                 int topk, float scale, uint16_t* oc, float* oc_f32, float* lse, hipStream_t s) {
   const Placement pl = make_placement(g);
   const float scale_log2 = scale * 1.4426950408889634f;
-  attn_fwd<D, PARTIAL><<<dim3(grid_size(g)), dim3(kThreads), 0, s>>>(qc, kc, vt, idx, topk, scale, scale_log2, oc,
-                                                                      oc_f32, lse, g, pl);
+  attn_fwd<D, PARTIAL, RASTER, KRASTER><<<dim3(grid_size(g)), dim3(kThreads), 0, s>>>(
+      qc, kc, vt, idx, topk, scale, scale_log2, oc, oc_f32, lse, g, pl);
+}
+
+template <bool RASTER, bool KRASTER>
+hipError_t launch_fwd_any(const KGeom& g, const uint16_t* q, const uint16_t* k, const uint16_t* vt,
+                          const int32_t* idx, int topk, float scale, uint16_t* o, float* o_f32, float* lse,
+                          hipStream_t s) {
+  if (g.D == 64) {
+    if (g.partial) launch_fwd<64, true, RASTER, KRASTER>(g, q, k, vt, idx, topk, scale, o, o_f32, lse, s);
+    else launch_fwd<64, false, RASTER, KRASTER>(g, q, k, vt, idx, topk, scale, o, o_f32, lse, s);
+  } else {
+    if (g.partial) launch_fwd<128, true, RASTER, KRASTER>(g, q, k, vt, idx, topk, scale, o, o_f32, lse, s);
+    else launch_fwd<128, false, RASTER, KRASTER>(g, q, k, vt, idx, topk, scale, o, o_f32, lse, s);
+  }
+  return hipGetLastError();
 }
 
 hipError_t launch_attn_fwd(const KGeom& g, const uint16_t* qc, const uint16_t* kc, const uint16_t* vt,
                            const int32_t* idx, int topk, float scale, uint16_t* oc, float* oc_f32, float* lse,
                            hipStream_t s) {
-  if (g.D == 64) {
-    if (g.partial) launch_fwd<64, true>(g, qc, kc, vt, idx, topk, scale, oc, oc_f32, lse, s);
-    else launch_fwd<64, false>(g, qc, kc, vt, idx, topk, scale, oc, oc_f32, lse, s);
-  } else {
-    if (g.partial) launch_fwd<128, true>(g, qc, kc, vt, idx, topk, scale, oc, oc_f32, lse, s);
-    else launch_fwd<128, false>(g, qc, kc, vt, idx, topk, scale, oc, oc_f32, lse, s);
-  }
-  return hipGetLastError();
+  return launch_fwd_any<false, false>(g, qc, kc, vt, idx, topk, scale, oc, oc_f32, lse, s);
+}
+
+hipError_t launch_attn_fwd_raster(const KGeom& g, const uint16_t* q, const uint16_t* k, bool k_raster,
+                                  const uint16_t* vt, const int32_t* idx, int topk, float scale, uint16_t* o,
+                                  float* lse, hipStream_t s) {
+  if (k_raster) return launch_fwd_any<true, true>(g, q, k, vt, idx, topk, scale, o, nullptr, lse, s);
+  return launch_fwd_any<true, false>(g, q, k, vt, idx, topk, scale, o, nullptr, lse, s);
 }
 
 }  // namespace vsa

@@ -89,6 +89,9 @@ size_t select_pooled_workspace_bytes(const KGeom& g);
 hipError_t launch_attn_fwd(const KGeom& g, const uint16_t* qc, const uint16_t* kc, const uint16_t* vt,
                            const int32_t* idx, int topk, float scale, uint16_t* oc, float* oc_f32, float* lse,
                            hipStream_t s);
+hipError_t launch_attn_fwd_raster(const KGeom& g, const uint16_t* q, const uint16_t* k, bool k_raster,
+                                  const uint16_t* vt, const int32_t* idx, int topk, float scale, uint16_t* o,
+                                  float* lse, hipStream_t s);
 hipError_t launch_linear(const KGeom& g, const uint16_t* qc, const uint16_t* kc, const uint16_t* vt,
                          const int32_t* idx, int topk, const float* o_sparse, uint16_t* oc, void* ws,
                          hipStream_t s);

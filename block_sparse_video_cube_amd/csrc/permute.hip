@@ -43,7 +43,10 @@ __global__ void __launch_bounds__(kThreads) permute_token_major(const uint16_t* 
 // Thread t always handles 16-byte chunk t % (D/8) of its rows, so it keeps 8
 // partial sums; threads with equal chunk are folded by cross-lane exchanges
 // inside a wavefront and through LDS across the four wavefronts.
-template <int D>
+//
+// With WRITE = false only the means are produced (the fine stage can gather
+// raster-order rows itself, so the cube-major copy is not needed).
+template <int D, bool WRITE>
 __global__ void __launch_bounds__(kThreads) permute_pool(const uint16_t* __restrict__ x, uint16_t* __restrict__ xc,
                                                          float* __restrict__ mean, KGeom g) {
   constexpr int CH = D / 8;
@@ -52,7 +55,7 @@ __global__ void __launch_bounds__(kThreads) permute_pool(const uint16_t* __restr
   int ct, cy, cx;
   cube_coords(g, c, ct, cy, cx);
   const long long cube_row = ((long long)b * g.H + h) * g.Np + 64LL * c;
-  uint4* out = reinterpret_cast<uint4*>(xc + cube_row * D);
+  uint4* out = WRITE ? reinterpret_cast<uint4*>(xc + cube_row * D) : nullptr;
   float acc[8] = {};
   for (int f = threadIdx.x; f < 64 * CH; f += kThreads) {
     const int l = f / CH, ch = f % CH;
@@ -68,7 +71,7 @@ __global__ void __launch_bounds__(kThreads) permute_pool(const uint16_t* __restr
         acc[2 * e + 1] += __uint_as_float(w4[e] & 0xFFFF0000u);
       }
     }
-    out[f] = val;
+    if (WRITE) out[f] = val;
   }
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
 #pragma unroll
@@ -162,10 +165,13 @@ hipError_t launch_permute(const KGeom& g, const uint16_t* x, uint16_t* xc, int l
 
 hipError_t launch_permute_pool(const KGeom& g, const uint16_t* x, uint16_t* xc, float* mean, hipStream_t s) {
   const dim3 grid(g.nc, g.H, g.B);
-  if (g.D == 64)
-    hipLaunchKernelGGL(permute_pool<64>, grid, dim3(kThreads), 0, s, x, xc, mean, g);
-  else
-    hipLaunchKernelGGL(permute_pool<128>, grid, dim3(kThreads), 0, s, x, xc, mean, g);
+  if (xc) {
+    if (g.D == 64) permute_pool<64, true><<<grid, dim3(kThreads), 0, s>>>(x, xc, mean, g);
+    else permute_pool<128, true><<<grid, dim3(kThreads), 0, s>>>(x, xc, mean, g);
+  } else {
+    if (g.D == 64) permute_pool<64, false><<<grid, dim3(kThreads), 0, s>>>(x, xc, mean, g);
+    else permute_pool<128, false><<<grid, dim3(kThreads), 0, s>>>(x, xc, mean, g);
+  }
   return hipGetLastError();
 }
 

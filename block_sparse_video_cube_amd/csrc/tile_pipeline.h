@@ -112,6 +112,52 @@ __device__ __forceinline__ void issue_v_tile(__amdgpu_buffer_rsrc_t vr, uint16_t
     __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (lds_ptr_t)(vlds + (w * NI + e) * 8 * 64), 16, off[e], 0, 0, 0);
 }
 
+// Gathering a token-major tile straight from raster-order rows
+// ([B, S, heads, D]: consecutive tokens of one head are heads * D elements
+// apart).  Local token l of a cube sits (lt * Hg + ly) * W + lx tokens after
+// the cube's first token, (lt, ly, lx) = (l / 16, l / 4 % 4, l % 4), so each
+// lane's offset within a cube is fixed; only the buffer base moves from cube
+// to cube.  raster_lane_offsets: this wave's lanes, for instructions
+// e < D / 32 of a tile load, the byte offset of its (swizzled) 16-byte chunk
+// and the local token index of its row.
+template <int D>
+__device__ __forceinline__ void raster_lane_offsets(const KGeom& g, int w, int lane, uint32_t* off, int* row) {
+  constexpr int NI = D / 32, KRPI = 512 / D;
+#pragma unroll
+  for (int e = 0; e < NI; ++e) {
+    const int r = (w * NI + e) * KRPI + lane / (D / 8);
+    const int rowoff = ((r >> 4) * g.Hg + ((r >> 2) & 3)) * g.W + (r & 3);
+    off[e] = (uint32_t)(rowoff * g.H * D + ((lane % (D / 8)) ^ k_swz<D>(r)) * 8) * 2u;
+    row[e] = r;
+  }
+}
+
+// Buffer resource over the raster rows from the first token of cube j to the
+// end of the head's tokens (xhead: element (b, token 0, h, 0)), and the lane
+// offsets for it.  Padded tokens of a partial cube get an offset past the
+// range, so the hardware range check returns zeros for them.
+template <int D, bool PARTIAL>
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t raster_tile(const uint16_t* xhead, const KGeom& g, int j,
+                                                             const uint32_t* off, const int* row, uint32_t* out) {
+  constexpr int NI = D / 32;
+  int ct, cy, cx;
+  cube_coords(g, j, ct, cy, cx);
+  const long long corner = ((long long)(4 * ct) * g.Hg + 4 * cy) * g.W + 4 * cx;
+  const long long pitch = (long long)g.H * D;
+#pragma unroll
+  for (int e = 0; e < NI; ++e) out[e] = off[e];
+  if (PARTIAL) {
+    const int nt = g.T - 4 * ct, ny = g.Hg - 4 * cy, nx = g.W - 4 * cx;
+#pragma unroll
+    for (int e = 0; e < NI; ++e) {
+      const int r = row[e];
+      const bool ok = (r >> 4) < nt && ((r >> 2) & 3) < ny && (r & 3) < nx;
+      out[e] = ok ? off[e] : 0xFFFFFFF0u;
+    }
+  }
+  return make_rsrc(xhead + corner * pitch, (unsigned)((g.S - corner) * pitch * 2));
+}
+
 // K fragments of S^T = K Q^T for this wave's key half (rows in pi order).
 template <int D>
 __device__ __forceinline__ void read_k(const uint16_t* klds, int wk, int hf, int prow, bf16x8 (&ka)[D / 16]) {

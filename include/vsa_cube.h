@@ -89,8 +89,10 @@ typedef struct vsa_dims {
  * TOKEN_MAJOR: [B, heads, Np, D], element (b, h, 64 c + l, d).
  * DIM_MAJOR:   [B, heads, Nc, D, 64], element (b, h, c, d, l): each cube
  *              stored transposed.  This is the layout the value tensor must
- *              have for vsa_sparse_attn_fwd and vsa_linear_branch. */
-enum { VSA_LAYOUT_TOKEN_MAJOR = 0, VSA_LAYOUT_DIM_MAJOR = 1 };
+ *              have for vsa_sparse_attn_fwd and vsa_linear_branch.
+ * RASTER: not a cube-major layout; the k_layout code of
+ *              vsa_sparse_attn_fwd_raster for raster-order keys. */
+enum { VSA_LAYOUT_TOKEN_MAJOR = 0, VSA_LAYOUT_DIM_MAJOR = 1, VSA_LAYOUT_RASTER = 2 };
 
 /* Limits: n_cubes <= VSA_MAX_CUBES, B * heads * Np * D < 2^40. */
 #define VSA_MAX_CUBES 4096
@@ -142,12 +144,32 @@ int32_t vsa_select_topk(const vsa_geom* g, const uint16_t* qc, const uint16_t* k
                         int32_t topk, int32_t* idx, void* ws, size_t ws_bytes,
                         void* stream);
 
+/* Cube means only: mean [B, heads, Nc, D] fp32 of the raster tokens x as
+ * vsa_cube_permute_pool computes them, without writing the cube-major copy
+ * (for the raster-order fine stage below, which gathers rows itself). */
+int32_t vsa_cube_pool(const vsa_geom* g, const uint16_t* x, float* mean, void* stream);
+
 /* Coarse stage from precomputed cube means (qbar, kbar: fp32 [B, heads, Nc, D],
  * e.g. from vsa_cube_permute_pool): block scores and top-k exactly as
  * vsa_select_topk.  ws: at least vsa_select_workspace_bytes(g) bytes. */
 int32_t vsa_select_topk_pooled(const vsa_geom* g, const float* qbar, const float* kbar,
                                int32_t topk, int32_t* idx, void* ws, size_t ws_bytes,
                                void* stream);
+
+/* Fine stage reading and writing raster order: as vsa_sparse_attn_fwd, but q
+ * is the raster tokens [B, S, heads, D] bf16 and the output o is raster
+ * [B, S, heads, D] bf16 (every token written), so the layer needs no permute
+ * of Q and no unpermute (gather-on-load of the fine stage).  k_layout:
+ * VSA_LAYOUT_TOKEN_MAJOR, k = kc cube-major rows as for vsa_sparse_attn_fwd,
+ * or VSA_LAYOUT_RASTER, k = raster tokens whose 64-row tiles the kernel
+ * gathers itself (no permute of K either).  vt stays DIM_MAJOR.  Results are
+ * bit-identical to vsa_sparse_attn_fwd followed by vsa_cube_unpermute.
+ * lse: optional fp32 [B, heads, Np] in cube-major row order, as there.
+ * Limit: S * heads * D * 2 < 2^31 bytes (32-bit buffer offsets). */
+int32_t vsa_sparse_attn_fwd_raster(const vsa_geom* g, const uint16_t* q, const uint16_t* k,
+                                   int32_t k_layout, const uint16_t* vt, const int32_t* idx,
+                                   int32_t topk, float softmax_scale, uint16_t* o, float* lse,
+                                   void* stream);
 
 /* Sliding-tile pattern (STA; FastVideo attention-backend article, item
  * "SLIDING_TILE_ATTN" and the figure comparing NATTEN, Tiled NATTEN and STA):

@@ -181,3 +181,22 @@ def test_backward_entry_point_validation(lib):
     assert lib.vsa_sparse_attn_bwd(g, *args, 2, 0.125, *outs, P, ws - 1, None) == _lib.VSA_ERR_WORKSPACE
     big = geom(grid=(4 * 17, 4 * 16, 4 * 16))
     assert lib.vsa_sparse_attn_bwd(big, *args, 2, 0.125, *outs, P, 1 << 40, None) == _lib.VSA_ERR_GEOMETRY
+
+
+def test_raster_entry_point_validation(lib):
+    from block_sparse_video_cube_amd import _lib
+
+    g = geom()
+    P = FAKE
+    assert lib.vsa_cube_pool(g, P, None, None) == _lib.VSA_ERR_NULL
+    assert lib.vsa_cube_pool(g, ODD, P, None) == _lib.VSA_ERR_ALIGN
+    assert lib.vsa_cube_pool(geom(D=16), P, P, None) == _lib.VSA_ERR_HEAD_DIM
+    R = _lib.VSA_LAYOUT_RASTER
+    assert lib.vsa_sparse_attn_fwd_raster(g, P, P, R, P, P, 2, 0.125, None, None, None) == _lib.VSA_ERR_NULL
+    assert lib.vsa_sparse_attn_fwd_raster(g, P, ODD, R, P, P, 2, 0.125, P, None, None) == _lib.VSA_ERR_ALIGN
+    assert lib.vsa_sparse_attn_fwd_raster(g, P, P, 1, P, P, 2, 0.125, P, None, None) == _lib.VSA_ERR_LAYOUT
+    assert lib.vsa_sparse_attn_fwd_raster(g, P, P, R, P, P, 0, 0.125, P, None, None) == _lib.VSA_ERR_TOPK
+    assert lib.vsa_sparse_attn_fwd_raster(g, P, P, 0, P, P, 2, 0.0, P, None, None) == _lib.VSA_ERR_SCALE
+    # 32-bit buffer offsets: S * heads * D * 2 must stay below 2^31
+    huge = geom(B=1, H=512, D=128, grid=(64, 64, 64))
+    assert lib.vsa_sparse_attn_fwd_raster(huge, P, P, R, P, P, 2, 0.125, P, None, None) == _lib.VSA_ERR_GEOMETRY
