@@ -68,8 +68,11 @@ def copy_calibration(nbytes: int) -> None:
 
 
 def kernel_source_hash() -> str:
-    path = os.path.join(ROOT, "block_sparse_video_cube_amd", "csrc", "attn_fwd.hip")
-    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+    """sha256 (first 16 hex digits) of the fine-stage sources: the kernel and the headers it includes."""
+    h = hashlib.sha256()
+    for name in ("attn_fwd.hip", "tile_pipeline.h", "common.h"):
+        h.update(open(os.path.join(ROOT, "block_sparse_video_cube_amd", "csrc", name), "rb").read())
+    return h.hexdigest()[:16]
 
 
 def measured_traffic(workload: str):
