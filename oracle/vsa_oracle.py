@@ -46,6 +46,15 @@ fits them, with these conventions (each is a reading, not a quote):
       dS = P * (dP - rowsum(dO * O)), dQ = scale dS K, dK += scale dS^T Q.
       This is the chain rule through O5, written out; nothing on the pages
       fixes it further.
+  O10 low-precision fine stage: SageAttention-style 8-bit attention
+      (TurboDiffusion article, section "稀疏、蒸馏与全链路量化": the key
+      matrix products of attention at 8 bits or lower, orthogonal to the
+      sparsity).  Reading: fp8 E4M3 (OCP E4M3FN: bias 7, largest finite
+      value 448) with Q and K scaled per (b, h, cube), V per (b, h, channel)
+      over all tokens of the head; the attention itself is O5 on the
+      dequantized values.  The quantizer is written in exact fp32 steps:
+      inv = 448 / m, q = clamp(x * inv, -448, 448), code = RNE to E4M3, with
+      m the block's largest |x| over valid tokens and the stored scale m / 448.
   O8  sliding-tile variant (STA, named among the attention backends of the
       FastVideo attention-backend article, item "SLIDING_TILE_ATTN" and the
       figure comparing NATTEN, Tiled NATTEN and STA): instead of the top-k
@@ -88,6 +97,11 @@ __all__ = [
     "forward",
     "sta_window",
     "sta_index",
+    "E4M3_MAX",
+    "e4m3_decode",
+    "e4m3_encode",
+    "quant_cubes",
+    "quant_channels",
     "attention_cube_bwd",
     "sparse_attention_bwd",
     "backward",
@@ -453,3 +467,85 @@ def backward(q, k, v, do, grid: Sequence[int], idx: np.ndarray, scale: Optional[
     doc = cube_permute(do, grid)
     dq, dk, dv = sparse_attention_bwd(qc, kc, vc, valid, idx, scale, doc)
     return cube_unpermute(dq, grid), cube_unpermute(dk, grid), cube_unpermute(dv, grid)
+
+
+# --------------------------------------------------------------------------
+# O10: 8-bit (fp8 E4M3) quantization of the fine stage's inputs
+# --------------------------------------------------------------------------
+
+E4M3_MAX = 448.0
+
+
+def e4m3_decode(codes: np.ndarray) -> np.ndarray:
+    """Value of OCP E4M3FN codes: sign, 4 exponent bits (bias 7), 3 mantissa
+    bits; exponent 0 is subnormal (m/8 * 2^-6); S.1111.111 is NaN."""
+    c = np.asarray(codes, dtype=np.int64)
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    m = c & 7
+    val = np.where(e == 0, m / 8.0 * 2.0 ** -6, (1.0 + m / 8.0) * np.power(2.0, e - 7.0))
+    val = np.where((e == 15) & (m == 7), np.nan, val)
+    return sign * val
+
+
+# All finite non-negative E4M3 values, ascending (code 0x00 .. 0x7E).
+_E4M3_POS = e4m3_decode(np.arange(0x7F))
+
+
+def e4m3_encode(x: np.ndarray) -> np.ndarray:
+    """Round fp32 values in [-448, 448] to the nearest E4M3 code, ties to the
+    code with even mantissa (round to nearest even), by search over the value
+    table.  The sign bit is kept, also when the magnitude rounds to zero."""
+    x = np.asarray(x, dtype=np.float64)
+    assert np.all(np.abs(x) <= E4M3_MAX), "values must be clamped to the E4M3 range"
+    a = np.abs(x)
+    hi = np.searchsorted(_E4M3_POS, a, side="left")  # first table value >= a
+    hi = np.minimum(hi, 0x7E)
+    lo = np.maximum(hi - 1, 0)
+    d_lo = a - _E4M3_POS[lo]
+    d_hi = _E4M3_POS[hi] - a
+    pick_hi = (d_hi < d_lo) | ((d_hi == d_lo) & (hi % 2 == 0))
+    mag = np.where(pick_hi, hi, lo)
+    mag = np.where(_E4M3_POS[hi] == a, hi, mag)
+    code = np.where(np.signbit(x), mag | 0x80, mag)
+    return code.astype(np.uint8)
+
+
+def _quantize(x32: np.ndarray, m32: np.ndarray):
+    """Codes of x32 (fp32) for block maxima m32 (fp32, broadcastable): the
+    exact fp32 steps of O10."""
+    with np.errstate(divide="ignore"):
+        inv = np.where(m32 > 0, np.float32(E4M3_MAX) / np.where(m32 > 0, m32, np.float32(1)), np.float32(0))
+    inv = inv.astype(np.float32)
+    q = np.clip((x32 * inv).astype(np.float32), -np.float32(E4M3_MAX), np.float32(E4M3_MAX))
+    scale = (m32 / np.float32(E4M3_MAX)).astype(np.float32)
+    return e4m3_encode(q), scale
+
+
+def quant_cubes(xc: np.ndarray, valid: np.ndarray):
+    """Per-(b, h, cube) quantization of cube-major rows (O10).
+
+    xc: [B, H, Np, D] bf16 bits.  Returns codes uint8 [B, H, Np, D] (padded
+    rows 0) and scale fp32 [B, H, Nc] (dequantized value = decode(code) * scale).
+    """
+    B, Hh, Np, D = xc.shape
+    x = bf16_to_f64(xc).astype(np.float32)
+    x[:, :, ~valid] = 0.0
+    m = np.abs(x).reshape(B, Hh, Np // 64, 64 * D).max(axis=-1).astype(np.float32)
+    mrow = np.repeat(m, 64, axis=2)[..., None]
+    codes, _ = _quantize(x, mrow)
+    codes[:, :, ~valid] = 0
+    return codes, (m / np.float32(E4M3_MAX)).astype(np.float32)
+
+
+def quant_channels(xc: np.ndarray, valid: np.ndarray):
+    """Per-(b, h, channel) quantization over all valid rows of a head (O10).
+
+    Returns codes uint8 [B, H, Np, D] (padded rows 0) and scale fp32 [B, H, D].
+    """
+    x = bf16_to_f64(xc).astype(np.float32)
+    x[:, :, ~valid] = 0.0
+    m = np.abs(x).max(axis=2).astype(np.float32)  # [B, H, D]
+    codes, _ = _quantize(x, m[:, :, None, :])
+    codes[:, :, ~valid] = 0
+    return codes, (m / np.float32(E4M3_MAX)).astype(np.float32)
