@@ -46,6 +46,9 @@ __all__ = [
     "linear_branch",
     "sparse_attn_fwd_raster",
     "sparse_attn_bwd",
+    "quant_qk_fp8",
+    "quant_v_fp8",
+    "sparse_attn_fwd_fp8",
     "vsa_attention",
     "workspace_bytes",
 ]
@@ -273,6 +276,74 @@ def sparse_attn_fwd_raster(q: torch.Tensor, k: torch.Tensor, vt: torch.Tensor, i
     _lib.check("vsa_sparse_attn_fwd_raster", _lib.load().vsa_sparse_attn_fwd_raster(
         g, q.data_ptr(), k.data_ptr(), k_layout, vt.data_ptr(), idx.data_ptr(), topk, float(scale),
         out.data_ptr(), lse.data_ptr() if lse is not None else None, _stream()))
+    return out, lse
+
+
+def quant_qk_fp8(x: torch.Tensor, grid: Sequence[int], out: Optional[torch.Tensor] = None,
+                 scale_out: Optional[torch.Tensor] = None):
+    """E4M3 codes of raster Q or K per (b, h, cube): (x8 uint8 [B, heads, Np, D], scale f32 [B, heads, Nc])."""
+    B, S, Hh, D = x.shape
+    g = make_geom(B, Hh, D, grid)
+    d = geom_dims(g)
+    _need(x, "x", torch.bfloat16, (B, d.tokens, Hh, D))
+    if out is None:
+        out = torch.empty((B, Hh, d.rows, D), dtype=torch.uint8, device=x.device)
+    if scale_out is None:
+        scale_out = torch.empty((B, Hh, d.n_cubes), dtype=torch.float32, device=x.device)
+    _need(out, "x8", torch.uint8, (B, Hh, d.rows, D))
+    _need(scale_out, "scale", torch.float32, (B, Hh, d.n_cubes))
+    _lib.check("vsa_quant_qk_fp8", _lib.load().vsa_quant_qk_fp8(g, x.data_ptr(), out.data_ptr(),
+                                                                scale_out.data_ptr(), _stream()))
+    return out, scale_out
+
+
+def quant_v_fp8(v: torch.Tensor, grid: Sequence[int], out: Optional[torch.Tensor] = None,
+                scale_out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None):
+    """E4M3 codes of raster V per (b, h, channel): (v8t uint8 [B, heads, Nc, D, 64], scale f32 [B, heads, D])."""
+    B, S, Hh, D = v.shape
+    g = make_geom(B, Hh, D, grid)
+    d = geom_dims(g)
+    _need(v, "v", torch.bfloat16, (B, d.tokens, Hh, D))
+    if out is None:
+        out = torch.empty((B, Hh, d.n_cubes, D, 64), dtype=torch.uint8, device=v.device)
+    if scale_out is None:
+        scale_out = torch.empty((B, Hh, D), dtype=torch.float32, device=v.device)
+    _need(out, "v8t", torch.uint8, (B, Hh, d.n_cubes, D, 64))
+    _need(scale_out, "scale", torch.float32, (B, Hh, D))
+    lib = _lib.load()
+    nbytes = lib.vsa_quant_v_fp8_workspace_bytes(g)
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=v.device)
+    _lib.check("vsa_quant_v_fp8", lib.vsa_quant_v_fp8(g, v.data_ptr(), out.data_ptr(), scale_out.data_ptr(),
+                                                      workspace.data_ptr(),
+                                                      workspace.numel() * workspace.element_size(), _stream()))
+    return out, scale_out
+
+
+def sparse_attn_fwd_fp8(q8: torch.Tensor, qscale: torch.Tensor, k8: torch.Tensor, kscale: torch.Tensor,
+                        v8t: torch.Tensor, vscale: torch.Tensor, idx: torch.Tensor, grid: Sequence[int],
+                        scale: Optional[float] = None, want_lse: bool = False, out: Optional[torch.Tensor] = None):
+    """fp8 fine stage.  Returns (oc bf16 [B, heads, Np, D] token-major, lse or None)."""
+    B, Hh, Np, D = q8.shape
+    g = make_geom(B, Hh, D, grid)
+    d = geom_dims(g)
+    topk = int(idx.shape[-1])
+    _need(q8, "q8", torch.uint8, (B, Hh, d.rows, D))
+    _need(k8, "k8", torch.uint8, (B, Hh, d.rows, D))
+    _need(v8t, "v8t", torch.uint8, (B, Hh, d.n_cubes, D, 64))
+    _need(qscale, "qscale", torch.float32, (B, Hh, d.n_cubes))
+    _need(kscale, "kscale", torch.float32, (B, Hh, d.n_cubes))
+    _need(vscale, "vscale", torch.float32, (B, Hh, D))
+    _need(idx, "idx", torch.int32, (B, Hh, d.n_cubes, topk))
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty((B, Hh, d.rows, D), dtype=torch.bfloat16, device=q8.device)
+    _need(out, "oc", torch.bfloat16, (B, Hh, d.rows, D))
+    lse = torch.empty((B, Hh, d.rows), dtype=torch.float32, device=q8.device) if want_lse else None
+    _lib.check("vsa_sparse_attn_fwd_fp8", _lib.load().vsa_sparse_attn_fwd_fp8(
+        g, q8.data_ptr(), qscale.data_ptr(), k8.data_ptr(), kscale.data_ptr(), v8t.data_ptr(), vscale.data_ptr(),
+        idx.data_ptr(), topk, float(scale), out.data_ptr(), lse.data_ptr() if lse is not None else None, _stream()))
     return out, lse
 
 

@@ -190,6 +190,54 @@ int32_t vsa_sparse_attn_bwd(const vsa_geom* g, const uint16_t* qc, const uint16_
                                             dv, ws, static_cast<hipStream_t>(stream)));
 }
 
+size_t vsa_quant_v_fp8_workspace_bytes(const vsa_geom* g) {
+  vsa_dims d;
+  vsa::KGeom k;
+  if (prepare(g, &d, &k) != VSA_OK) return 0;
+  return vsa::quant_v_workspace_bytes(k);
+}
+
+int32_t vsa_quant_qk_fp8(const vsa_geom* g, const uint16_t* x, uint8_t* x8, float* scale, void* stream) {
+  vsa_dims d;
+  vsa::KGeom k;
+  int32_t st = prepare(g, &d, &k);
+  if (st != VSA_OK) return st;
+  if (!x || !x8 || !scale) return VSA_ERR_NULL;
+  if (!aligned16(x) || !aligned16(x8) || !aligned16(scale)) return VSA_ERR_ALIGN;
+  return launch_status(vsa::launch_quant_qk(k, x, x8, scale, static_cast<hipStream_t>(stream)));
+}
+
+int32_t vsa_quant_v_fp8(const vsa_geom* g, const uint16_t* v, uint8_t* v8t, float* scale, void* ws,
+                        size_t ws_bytes, void* stream) {
+  vsa_dims d;
+  vsa::KGeom k;
+  int32_t st = prepare(g, &d, &k);
+  if (st != VSA_OK) return st;
+  if (!v || !v8t || !scale || !ws) return VSA_ERR_NULL;
+  if (!aligned16(v) || !aligned16(v8t) || !aligned16(scale) || !aligned16(ws)) return VSA_ERR_ALIGN;
+  if (ws_bytes < vsa::quant_v_workspace_bytes(k)) return VSA_ERR_WORKSPACE;
+  return launch_status(vsa::launch_quant_v(k, v, v8t, scale, ws, static_cast<hipStream_t>(stream)));
+}
+
+int32_t vsa_sparse_attn_fwd_fp8(const vsa_geom* g, const uint8_t* q8, const float* qscale, const uint8_t* k8,
+                                const float* kscale, const uint8_t* v8t, const float* vscale, const int32_t* idx,
+                                int32_t topk, float softmax_scale, uint16_t* oc, float* lse, void* stream) {
+  vsa_dims d;
+  vsa::KGeom k;
+  int32_t st = prepare(g, &d, &k);
+  if (st != VSA_OK) return st;
+  const void* ptrs[] = {q8, qscale, k8, kscale, v8t, vscale, idx, oc};
+  for (const void* p : ptrs)
+    if (!p) return VSA_ERR_NULL;
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return VSA_ERR_ALIGN;
+  if (lse && !aligned16(lse)) return VSA_ERR_ALIGN;
+  if (topk < 1 || topk > d.n_cubes) return VSA_ERR_TOPK;
+  if (!(softmax_scale > 0.f) || !isfinite(softmax_scale)) return VSA_ERR_SCALE;
+  return launch_status(vsa::launch_attn_fwd_fp8(k, q8, qscale, k8, kscale, v8t, vscale, idx, topk, softmax_scale,
+                                                oc, lse, static_cast<hipStream_t>(stream)));
+}
+
 int32_t vsa_cube_unpermute(const vsa_geom* g, const uint16_t* xc, uint16_t* x, void* stream) {
   vsa_dims d;
   vsa::KGeom k;

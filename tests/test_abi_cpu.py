@@ -17,7 +17,7 @@ HEADER = os.path.join(ROOT, "include", "vsa_cube.h")
 def header_functions():
     text = open(HEADER, encoding="utf-8").read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(vsa_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(vsa_[a-z0-9_]+)\s*\(", text)))
 
 
 @pytest.fixture(scope="module")
@@ -200,3 +200,29 @@ def test_raster_entry_point_validation(lib):
     # 32-bit buffer offsets: S * heads * D * 2 must stay below 2^31
     huge = geom(B=1, H=512, D=128, grid=(64, 64, 64))
     assert lib.vsa_sparse_attn_fwd_raster(huge, P, P, R, P, P, 2, 0.125, P, None, None) == _lib.VSA_ERR_GEOMETRY
+
+
+def test_fp8_entry_point_validation(lib):
+    from block_sparse_video_cube_amd import _lib
+
+    g = geom()
+    P = FAKE
+    ws = lib.vsa_quant_v_fp8_workspace_bytes(g)
+    # per-(b, h, cube) channel maxima plus per-(b, h) maxima, fp32
+    assert ws == 1 * 2 * (8 + 1) * 64 * 4
+    assert lib.vsa_quant_v_fp8_workspace_bytes(geom(D=16)) == 0
+    assert lib.vsa_quant_qk_fp8(g, P, P, None, None) == _lib.VSA_ERR_NULL
+    assert lib.vsa_quant_qk_fp8(g, P, ODD, P, None) == _lib.VSA_ERR_ALIGN
+    assert lib.vsa_quant_qk_fp8(geom(D=16), P, P, P, None) == _lib.VSA_ERR_HEAD_DIM
+    assert lib.vsa_quant_v_fp8(g, P, P, P, None, ws, None) == _lib.VSA_ERR_NULL
+    assert lib.vsa_quant_v_fp8(g, P, P, ODD, P, ws, None) == _lib.VSA_ERR_ALIGN
+    assert lib.vsa_quant_v_fp8(g, P, P, P, P, ws - 1, None) == _lib.VSA_ERR_WORKSPACE
+    args = [P] * 7  # q8 qscale k8 kscale v8t vscale idx
+    assert lib.vsa_sparse_attn_fwd_fp8(g, *args, 2, 0.125, None, None, None) == _lib.VSA_ERR_NULL
+    assert lib.vsa_sparse_attn_fwd_fp8(g, *args[:6], None, 2, 0.125, P, None, None) == _lib.VSA_ERR_NULL
+    assert lib.vsa_sparse_attn_fwd_fp8(g, ODD, *args[1:], 2, 0.125, P, None, None) == _lib.VSA_ERR_ALIGN
+    assert lib.vsa_sparse_attn_fwd_fp8(g, *args, 2, 0.125, P, ODD, None) == _lib.VSA_ERR_ALIGN
+    assert lib.vsa_sparse_attn_fwd_fp8(g, *args, 0, 0.125, P, None, None) == _lib.VSA_ERR_TOPK
+    assert lib.vsa_sparse_attn_fwd_fp8(g, *args, 9, 0.125, P, None, None) == _lib.VSA_ERR_TOPK
+    assert lib.vsa_sparse_attn_fwd_fp8(g, *args, 2, float("inf"), P, None, None) == _lib.VSA_ERR_SCALE
+    assert lib.vsa_sparse_attn_fwd_fp8(geom(D=96), *args, 2, 0.125, P, None, None) == _lib.VSA_ERR_HEAD_DIM
