@@ -33,6 +33,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2516.6  # MI355X dense bf16 MFMA: 256 CU x 2.4 GHz x 4096 flop/clk
+PEAK_FP8_TFLOPS = 5033.2  # dense fp8 MFMA: twice the bf16 rate
 PEAK_HBM_GBS = 8000.0
 METRIC = "ms/layer + effective TFLOPS (frac of bf16 MFMA peak), block-sparse attn fwd"
 
@@ -50,6 +51,9 @@ def parse():
     ap.add_argument("--backward", action="store_true",
                     help="also time the backward of the fine stage (dQ, dK, dV) after the forward steps; "
                          "reported under 'backward', not in 'value'")
+    ap.add_argument("--fp8", action="store_true",
+                    help="low-precision layer: Q, K, V quantized to fp8 E4M3 in the step, fine stage on the "
+                         "fp8 matrix cores (roofline against the fp8 peak)")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="only run a plain device-to-device copy of this many bytes (3 times) and exit; "
                          "used to calibrate the FETCH_SIZE / WRITE_SIZE counters")
@@ -261,8 +265,51 @@ def main():
     # cube-transposed layout.  The linear branch works on cube-major rows, so
     # the hybrid layer keeps the permute / unpermute pair.
     stages = ["permute", "select", "fine", "linear", "unpermute"] if wl.linear else ["pool", "select", "fine"]
+    if args.fp8:
+        if wl.linear:
+            print("--fp8 covers the fine stage without the linear branch", file=sys.stderr)
+            sys.exit(2)
+        # Q, K quantized per cube and V per channel in the step; the fp8 fine
+        # stage writes cube-major rows, unpermuted to raster at the end.
+        stages = ["pool", "quant", "select", "fine", "unpermute"]
+        q8 = torch.empty((B, H, d.rows, D), dtype=torch.uint8, device=dev)
+        k8 = torch.empty_like(q8)
+        qs = torch.empty((B, H, d.n_cubes), dtype=torch.float32, device=dev)
+        ks = torch.empty_like(qs)
+        v8t = torch.empty((B, H, d.n_cubes, D, 64), dtype=torch.uint8, device=dev)
+        vs = torch.empty((B, H, D), dtype=torch.float32, device=dev)
+        ws_v = torch.empty(vsa.quant_v_fp8_workspace_bytes(g), dtype=torch.uint8,
+                           device=dev)
+
+    def step_fp8(ev=None):
+        def mark(i):
+            if ev is not None:
+                ev[i].record()
+
+        mark(0)
+        if wl.pattern != "sta":
+            vsa.cube_pool(q, wl.grid, mean_out=qbar)
+            vsa.cube_pool(k, wl.grid, mean_out=kbar)
+        mark(1)
+        vsa.quant_qk_fp8(q, wl.grid, out=q8, scale_out=qs)
+        vsa.quant_qk_fp8(k, wl.grid, out=k8, scale_out=ks)
+        vsa.quant_v_fp8(v, wl.grid, out=v8t, scale_out=vs, workspace=ws_v)
+        mark(2)
+        if wl.pattern == "sta":
+            vsa.sta_index(wl.grid, wl.window, B, H, head_dim=D, out=idx)
+        else:
+            vsa.select_topk_pooled(qbar, kbar, wl.grid, wl.topk, out=idx, workspace=ws_sel)
+        mark(3)
+        vsa.sparse_attn_fwd_fp8(q8, qs, k8, ks, v8t, vs, idx, wl.grid, wl.softmax_scale, out=oc)
+        mark(4)
+        vsa.cube_unpermute(oc, wl.grid, out=o)
+        mark(5)
 
     def step(ev=None):
+        if args.fp8:
+            step_fp8(ev)
+            return
+
         def mark(i):
             if ev is not None:
                 ev[i].record()
@@ -329,9 +376,15 @@ def main():
     flops = wl.fine_flops
     value = flops / (ms_step * 1e-3) / 1e12
     fine_tflops = flops / (fine_ms * 1e-3) / 1e12
-    # Algorithmic bytes of one fine-stage launch: Q, K, V read once, O written once (bf16).
+    # Algorithmic bytes of one fine-stage launch: Q, K, V read once, O written
+    # once (bf16; fp8 codes are one byte, plus their scales).
     alg_bytes = 4 * B * H * d.rows * D * 2
+    peak, kname = PEAK_BF16_TFLOPS, "attn_fwd"
     traffic = measured_traffic(wl.name)
+    if args.fp8:
+        alg_bytes = B * H * d.rows * D * (1 + 1 + 1 + 2) + 4 * B * H * (2 * d.n_cubes + D)
+        peak, kname = PEAK_FP8_TFLOPS, "attn_fwd_fp8"
+        traffic = None
     res = {
         "metric": METRIC,
         "value": round(value, 3),
@@ -343,7 +396,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "fp8e4m3 (fp32 softmax)" if args.fp8 else "bf16",
         "data": "synthetic",
         "config": {
             "workload": wl.name,
@@ -351,7 +404,9 @@ def main():
             "latent_grid": list(wl.grid), "padded_grid": list(wl.padded_grid),
             "tokens": wl.tokens, "n_cubes": wl.n_cubes, "topk": wl.topk,
             "sparsity": wl.sparsity, "linear_branch": wl.linear, "pattern": wl.pattern,
-            "layout": "cube-major" if wl.linear else ("raster q/k/o" if args.k_raster else "raster q/o"),
+            "layout": ("cube-major" if wl.linear or args.fp8 else
+                       ("raster q/k/o" if args.k_raster else "raster q/o")),
+            **({"precision": "fp8 e4m3: Q, K per cube, V per channel; P e4m3"} if args.fp8 else {}),
             **({"window_cubes": list(wl.window)} if wl.window else {}),
             "computed_blocks": wl.blocks, "fine_flops": flops,
         },
@@ -360,12 +415,12 @@ def main():
         "fine_stage_tflops": round(fine_tflops, 2),
         "frac_of_bf16_peak_layer": round(value / PEAK_BF16_TFLOPS, 4),
         "roofline": {
-            "kernel": "attn_fwd",
+            "kernel": kname,
             "bound": "mfma",
             "achieved": round(fine_tflops, 2),
-            "peak": PEAK_BF16_TFLOPS,
+            "peak": peak,
             "unit": "TFLOP/s",
-            "frac": round(fine_tflops / PEAK_BF16_TFLOPS, 4),
+            "frac": round(fine_tflops / peak, 4),
             "traffic": traffic,
             "algorithmic_bytes": alg_bytes,
             "avg_launch_ms": round(fine_ms, 4),
@@ -373,7 +428,7 @@ def main():
         "wall_s_timed": round(wall, 3),
         "device": torch.cuda.get_device_name(0),
     }
-    if args.backward:
+    if args.backward and not args.fp8:
         res["backward"] = time_backward(vsa, wl, q, k, v, o, qc, kc, vt, idx, args, dev)
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)

@@ -48,6 +48,7 @@ __all__ = [
     "sparse_attn_bwd",
     "quant_qk_fp8",
     "quant_v_fp8",
+    "quant_v_fp8_workspace_bytes",
     "sparse_attn_fwd_fp8",
     "vsa_attention",
     "workspace_bytes",
@@ -295,6 +296,10 @@ def quant_qk_fp8(x: torch.Tensor, grid: Sequence[int], out: Optional[torch.Tenso
     _lib.check("vsa_quant_qk_fp8", _lib.load().vsa_quant_qk_fp8(g, x.data_ptr(), out.data_ptr(),
                                                                 scale_out.data_ptr(), _stream()))
     return out, scale_out
+
+
+def quant_v_fp8_workspace_bytes(g: VsaGeom) -> int:
+    return int(_lib.load().vsa_quant_v_fp8_workspace_bytes(g))
 
 
 def quant_v_fp8(v: torch.Tensor, grid: Sequence[int], out: Optional[torch.Tensor] = None,
