@@ -271,15 +271,15 @@ def main():
             sys.exit(2)
         # Q, K quantized per cube and V per channel in the step; the fp8 fine
         # stage writes cube-major rows, unpermuted to raster at the end.
-        stages = ["pool", "quant", "select", "fine", "unpermute"]
-        q8 = torch.empty((B, H, d.rows, D), dtype=torch.uint8, device=dev)
-        k8 = torch.empty_like(q8)
-        qs = torch.empty((B, H, d.n_cubes), dtype=torch.float32, device=dev)
-        ks = torch.empty_like(qs)
-        v8t = torch.empty((B, H, d.n_cubes, D, 64), dtype=torch.uint8, device=dev)
-        vs = torch.empty((B, H, D), dtype=torch.float32, device=dev)
-        ws_v = torch.empty(vsa.quant_v_fp8_workspace_bytes(g), dtype=torch.uint8,
-                           device=dev)
+        stages = ["quant", "select", "fine", "unpermute"]
+        fp8_bufs = (torch.empty((B, H, d.rows, D), dtype=torch.uint8, device=dev),
+                    torch.empty((B, H, d.n_cubes), dtype=torch.float32, device=dev),
+                    torch.empty((B, H, d.rows, D), dtype=torch.uint8, device=dev),
+                    torch.empty((B, H, d.n_cubes), dtype=torch.float32, device=dev),
+                    torch.empty((B, H, d.n_cubes, D, 64), dtype=torch.uint8, device=dev),
+                    torch.empty((B, H, D), dtype=torch.float32, device=dev),
+                    qbar if wl.pattern != "sta" else None, kbar if wl.pattern != "sta" else None)
+        ws_q = torch.empty(vsa.quant_fp8_workspace_bytes(g), dtype=torch.uint8, device=dev)
 
     def step_fp8(ev=None):
         def mark(i):
@@ -287,23 +287,19 @@ def main():
                 ev[i].record()
 
         mark(0)
-        if wl.pattern != "sta":
-            vsa.cube_pool(q, wl.grid, mean_out=qbar)
-            vsa.cube_pool(k, wl.grid, mean_out=kbar)
+        # One pass over Q, K, V: codes, scales, the cube means of Q and K for the
+        # coarse stage, V's channel maxima; a second pass for V's codes.
+        q8, qs, k8, ks, v8t, vs, _, _ = vsa.quant_fp8(q, k, v, wl.grid, out=fp8_bufs, workspace=ws_q)
         mark(1)
-        vsa.quant_qk_fp8(q, wl.grid, out=q8, scale_out=qs)
-        vsa.quant_qk_fp8(k, wl.grid, out=k8, scale_out=ks)
-        vsa.quant_v_fp8(v, wl.grid, out=v8t, scale_out=vs, workspace=ws_v)
-        mark(2)
         if wl.pattern == "sta":
             vsa.sta_index(wl.grid, wl.window, B, H, head_dim=D, out=idx)
         else:
             vsa.select_topk_pooled(qbar, kbar, wl.grid, wl.topk, out=idx, workspace=ws_sel)
-        mark(3)
+        mark(2)
         vsa.sparse_attn_fwd_fp8(q8, qs, k8, ks, v8t, vs, idx, wl.grid, wl.softmax_scale, out=oc)
-        mark(4)
+        mark(3)
         vsa.cube_unpermute(oc, wl.grid, out=o)
-        mark(5)
+        mark(4)
 
     def step(ev=None):
         if args.fp8:

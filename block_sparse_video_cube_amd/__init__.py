@@ -46,9 +46,8 @@ __all__ = [
     "linear_branch",
     "sparse_attn_fwd_raster",
     "sparse_attn_bwd",
-    "quant_qk_fp8",
-    "quant_v_fp8",
-    "quant_v_fp8_workspace_bytes",
+    "quant_fp8",
+    "quant_fp8_workspace_bytes",
     "sparse_attn_fwd_fp8",
     "vsa_attention",
     "workspace_bytes",
@@ -280,49 +279,53 @@ def sparse_attn_fwd_raster(q: torch.Tensor, k: torch.Tensor, vt: torch.Tensor, i
     return out, lse
 
 
-def quant_qk_fp8(x: torch.Tensor, grid: Sequence[int], out: Optional[torch.Tensor] = None,
-                 scale_out: Optional[torch.Tensor] = None):
-    """E4M3 codes of raster Q or K per (b, h, cube): (x8 uint8 [B, heads, Np, D], scale f32 [B, heads, Nc])."""
-    B, S, Hh, D = x.shape
+def quant_fp8_workspace_bytes(g: VsaGeom) -> int:
+    return int(_lib.load().vsa_quant_fp8_workspace_bytes(g))
+
+
+def quant_fp8(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, grid: Sequence[int], want_means: bool = False,
+              out=None, workspace: Optional[torch.Tensor] = None):
+    """E4M3 codes of raster Q, K (per (b, h, cube)) and V (per (b, h, channel)).
+
+    Returns (q8, qscale, k8, kscale, v8t, vscale, qmean, kmean): codes uint8
+    [B, heads, Np, D] and [B, heads, Nc, D, 64], scales f32 [B, heads, Nc] and
+    [B, heads, D], cube means f32 [B, heads, Nc, D] or None.  `out`: optional
+    tuple of the same eight tensors to write into (means may be None).
+    """
+    B, S, Hh, D = q.shape
     g = make_geom(B, Hh, D, grid)
     d = geom_dims(g)
-    _need(x, "x", torch.bfloat16, (B, d.tokens, Hh, D))
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _need(t, n, torch.bfloat16, (B, d.tokens, Hh, D))
+    dev = q.device
     if out is None:
-        out = torch.empty((B, Hh, d.rows, D), dtype=torch.uint8, device=x.device)
-    if scale_out is None:
-        scale_out = torch.empty((B, Hh, d.n_cubes), dtype=torch.float32, device=x.device)
-    _need(out, "x8", torch.uint8, (B, Hh, d.rows, D))
-    _need(scale_out, "scale", torch.float32, (B, Hh, d.n_cubes))
-    _lib.check("vsa_quant_qk_fp8", _lib.load().vsa_quant_qk_fp8(g, x.data_ptr(), out.data_ptr(),
-                                                                scale_out.data_ptr(), _stream()))
-    return out, scale_out
-
-
-def quant_v_fp8_workspace_bytes(g: VsaGeom) -> int:
-    return int(_lib.load().vsa_quant_v_fp8_workspace_bytes(g))
-
-
-def quant_v_fp8(v: torch.Tensor, grid: Sequence[int], out: Optional[torch.Tensor] = None,
-                scale_out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None):
-    """E4M3 codes of raster V per (b, h, channel): (v8t uint8 [B, heads, Nc, D, 64], scale f32 [B, heads, D])."""
-    B, S, Hh, D = v.shape
-    g = make_geom(B, Hh, D, grid)
-    d = geom_dims(g)
-    _need(v, "v", torch.bfloat16, (B, d.tokens, Hh, D))
-    if out is None:
-        out = torch.empty((B, Hh, d.n_cubes, D, 64), dtype=torch.uint8, device=v.device)
-    if scale_out is None:
-        scale_out = torch.empty((B, Hh, D), dtype=torch.float32, device=v.device)
-    _need(out, "v8t", torch.uint8, (B, Hh, d.n_cubes, D, 64))
-    _need(scale_out, "scale", torch.float32, (B, Hh, D))
+        u8 = dict(dtype=torch.uint8, device=dev)
+        f32 = dict(dtype=torch.float32, device=dev)
+        out = (torch.empty((B, Hh, d.rows, D), **u8), torch.empty((B, Hh, d.n_cubes), **f32),
+               torch.empty((B, Hh, d.rows, D), **u8), torch.empty((B, Hh, d.n_cubes), **f32),
+               torch.empty((B, Hh, d.n_cubes, D, 64), **u8), torch.empty((B, Hh, D), **f32),
+               torch.empty((B, Hh, d.n_cubes, D), **f32) if want_means else None,
+               torch.empty((B, Hh, d.n_cubes, D), **f32) if want_means else None)
+    q8, qs, k8, ks, v8t, vs, qm, km = out
+    _need(q8, "q8", torch.uint8, (B, Hh, d.rows, D))
+    _need(k8, "k8", torch.uint8, (B, Hh, d.rows, D))
+    _need(v8t, "v8t", torch.uint8, (B, Hh, d.n_cubes, D, 64))
+    _need(qs, "qscale", torch.float32, (B, Hh, d.n_cubes))
+    _need(ks, "kscale", torch.float32, (B, Hh, d.n_cubes))
+    _need(vs, "vscale", torch.float32, (B, Hh, D))
+    for t, n in ((qm, "qmean"), (km, "kmean")):
+        if t is not None:
+            _need(t, n, torch.float32, (B, Hh, d.n_cubes, D))
     lib = _lib.load()
-    nbytes = lib.vsa_quant_v_fp8_workspace_bytes(g)
+    nbytes = lib.vsa_quant_fp8_workspace_bytes(g)
     if workspace is None:
-        workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=v.device)
-    _lib.check("vsa_quant_v_fp8", lib.vsa_quant_v_fp8(g, v.data_ptr(), out.data_ptr(), scale_out.data_ptr(),
-                                                      workspace.data_ptr(),
-                                                      workspace.numel() * workspace.element_size(), _stream()))
-    return out, scale_out
+        workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=dev)
+    _lib.check("vsa_quant_fp8", lib.vsa_quant_fp8(
+        g, q.data_ptr(), k.data_ptr(), v.data_ptr(), q8.data_ptr(), qs.data_ptr(), k8.data_ptr(), ks.data_ptr(),
+        v8t.data_ptr(), vs.data_ptr(), qm.data_ptr() if qm is not None else None,
+        km.data_ptr() if km is not None else None, workspace.data_ptr(),
+        workspace.numel() * workspace.element_size(), _stream()))
+    return q8, qs, k8, ks, v8t, vs, qm, km
 
 
 def sparse_attn_fwd_fp8(q8: torch.Tensor, qscale: torch.Tensor, k8: torch.Tensor, kscale: torch.Tensor,

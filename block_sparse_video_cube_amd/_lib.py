@@ -44,9 +44,8 @@ ENTRY_POINTS = (
     "vsa_sparse_attn_fwd_raster",
     "vsa_attn_bwd_workspace_bytes",
     "vsa_sparse_attn_bwd",
-    "vsa_quant_v_fp8_workspace_bytes",
-    "vsa_quant_qk_fp8",
-    "vsa_quant_v_fp8",
+    "vsa_quant_fp8_workspace_bytes",
+    "vsa_quant_fp8",
     "vsa_sparse_attn_fwd_fp8",
 )
 
@@ -118,9 +117,8 @@ def load() -> ctypes.CDLL:
         "vsa_cube_pool": (i32, [G, P, P, P]),
         "vsa_sparse_attn_fwd_raster": (i32, [G, P, P, i32, P, P, i32, ctypes.c_float, P, P, P]),
         "vsa_attn_bwd_workspace_bytes": (sz, [G, i32]),
-        "vsa_quant_v_fp8_workspace_bytes": (sz, [G]),
-        "vsa_quant_qk_fp8": (i32, [G, P, P, P, P]),
-        "vsa_quant_v_fp8": (i32, [G, P, P, P, P, sz, P]),
+        "vsa_quant_fp8_workspace_bytes": (sz, [G]),
+        "vsa_quant_fp8": (i32, [G, P, P, P, P, P, P, P, P, P, P, P, P, sz, P]),
         "vsa_sparse_attn_fwd_fp8": (i32, [G, P, P, P, P, P, P, P, i32, ctypes.c_float, P, P, P]),
         "vsa_sparse_attn_bwd": (i32, [G, P, P, P, P, P, P, P, P, P, P, i32, ctypes.c_float, P, P, P, P, sz, P]),
     }

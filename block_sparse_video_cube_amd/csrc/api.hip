@@ -190,33 +190,29 @@ int32_t vsa_sparse_attn_bwd(const vsa_geom* g, const uint16_t* qc, const uint16_
                                             dv, ws, static_cast<hipStream_t>(stream)));
 }
 
-size_t vsa_quant_v_fp8_workspace_bytes(const vsa_geom* g) {
+size_t vsa_quant_fp8_workspace_bytes(const vsa_geom* g) {
   vsa_dims d;
   vsa::KGeom k;
   if (prepare(g, &d, &k) != VSA_OK) return 0;
-  return vsa::quant_v_workspace_bytes(k);
+  return vsa::quant_workspace_bytes(k);
 }
 
-int32_t vsa_quant_qk_fp8(const vsa_geom* g, const uint16_t* x, uint8_t* x8, float* scale, void* stream) {
+int32_t vsa_quant_fp8(const vsa_geom* g, const uint16_t* q, const uint16_t* k, const uint16_t* v, uint8_t* q8,
+                      float* qscale, uint8_t* k8, float* kscale, uint8_t* v8t, float* vscale, float* qmean,
+                      float* kmean, void* ws, size_t ws_bytes, void* stream) {
   vsa_dims d;
-  vsa::KGeom k;
-  int32_t st = prepare(g, &d, &k);
+  vsa::KGeom kg;
+  int32_t st = prepare(g, &d, &kg);
   if (st != VSA_OK) return st;
-  if (!x || !x8 || !scale) return VSA_ERR_NULL;
-  if (!aligned16(x) || !aligned16(x8) || !aligned16(scale)) return VSA_ERR_ALIGN;
-  return launch_status(vsa::launch_quant_qk(k, x, x8, scale, static_cast<hipStream_t>(stream)));
-}
-
-int32_t vsa_quant_v_fp8(const vsa_geom* g, const uint16_t* v, uint8_t* v8t, float* scale, void* ws,
-                        size_t ws_bytes, void* stream) {
-  vsa_dims d;
-  vsa::KGeom k;
-  int32_t st = prepare(g, &d, &k);
-  if (st != VSA_OK) return st;
-  if (!v || !v8t || !scale || !ws) return VSA_ERR_NULL;
-  if (!aligned16(v) || !aligned16(v8t) || !aligned16(scale) || !aligned16(ws)) return VSA_ERR_ALIGN;
-  if (ws_bytes < vsa::quant_v_workspace_bytes(k)) return VSA_ERR_WORKSPACE;
-  return launch_status(vsa::launch_quant_v(k, v, v8t, scale, ws, static_cast<hipStream_t>(stream)));
+  const void* ptrs[] = {q, k, v, q8, qscale, k8, kscale, v8t, vscale, ws};
+  for (const void* p : ptrs)
+    if (!p) return VSA_ERR_NULL;
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return VSA_ERR_ALIGN;
+  if ((qmean && !aligned16(qmean)) || (kmean && !aligned16(kmean))) return VSA_ERR_ALIGN;
+  if (ws_bytes < vsa::quant_workspace_bytes(kg)) return VSA_ERR_WORKSPACE;
+  return launch_status(vsa::launch_quant(kg, q, k, v, q8, qscale, k8, kscale, v8t, vscale, qmean, kmean, ws,
+                                         static_cast<hipStream_t>(stream)));
 }
 
 int32_t vsa_sparse_attn_fwd_fp8(const vsa_geom* g, const uint8_t* q8, const float* qscale, const uint8_t* k8,

@@ -98,9 +98,10 @@ hipError_t launch_linear(const KGeom& g, const uint16_t* qc, const uint16_t* kc,
 size_t linear_workspace_bytes(const KGeom& g);
 hipError_t launch_sta_index(const KGeom& g, int wt, int wh, int ww, int32_t* idx, hipStream_t s);
 size_t attn_bwd_workspace_bytes(const KGeom& g, int topk);
-size_t quant_v_workspace_bytes(const KGeom& g);
-hipError_t launch_quant_qk(const KGeom& g, const uint16_t* x, uint8_t* x8, float* scale, hipStream_t s);
-hipError_t launch_quant_v(const KGeom& g, const uint16_t* x, uint8_t* v8t, float* scale, void* ws, hipStream_t s);
+size_t quant_workspace_bytes(const KGeom& g);
+hipError_t launch_quant(const KGeom& g, const uint16_t* q, const uint16_t* k, const uint16_t* v, uint8_t* q8,
+                        float* qs, uint8_t* k8, float* ks, uint8_t* v8t, float* vs, float* qmean, float* kmean,
+                        void* ws, hipStream_t s);
 hipError_t launch_attn_fwd_fp8(const KGeom& g, const uint8_t* q8, const float* qs, const uint8_t* k8,
                                const float* ks, const uint8_t* v8t, const float* vs, const int32_t* idx, int topk,
                                float scale, uint16_t* oc, float* lse, hipStream_t s);

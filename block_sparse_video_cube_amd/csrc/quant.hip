@@ -12,6 +12,15 @@
 //   m = largest |x| of the block over valid tokens, inv = 448 / m (0 if m = 0),
 //   q = clamp(x * inv, -448, 448), code = E4M3 round-to-nearest-even of q,
 //   stored scale = m / 448 (dequantized value = code * scale).
+//
+// Two passes over raster [B, S, H, D] inputs (HBM bound):
+//   pass 1, one workgroup per (b, h, cube): Q and K codes and scales, and
+//     optionally their cube means (the coarse stage's pooled Q and K, summed
+//     in the same order as the pooling kernel, so bit-identical to it); V's
+//     per-channel maxima over the cube, folded into the head maxima with
+//     atomic max on the fp32 bit patterns (non-negative floats order as
+//     unsigned integers);
+//   pass 2, one workgroup per (b, h, cube): V's codes, transposed per cube.
 #include "common.h"
 
 namespace vsa {
@@ -19,6 +28,7 @@ namespace vsa {
 namespace {
 
 constexpr float kE4M3Max = 448.f;
+constexpr int kQThreads = 256;
 
 __device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
@@ -40,89 +50,137 @@ __device__ __forceinline__ long long cube_token(const KGeom& g, int ct, int cy, 
   return ((long long)t * g.Hg + y) * g.W + x;
 }
 
-// Q or K: one workgroup per (b, h, cube).  Reads the cube's raster rows,
-// reduces the block maximum, writes the codes as token-major rows
-// [B, H, Np, D] (bytes) and the scale [B, H, Nc].
+// The cube's rows of one head: thread t holds 16-byte chunk t % (D / 8) of
+// rows t / (D / 8) + 256 k / (D / 8), zeros for padded tokens.
 template <int D>
-__global__ void __launch_bounds__(256) quant_cube(const uint16_t* __restrict__ x, uint8_t* __restrict__ x8,
-                                                  float* __restrict__ scale, KGeom g) {
-  constexpr int CH = D / 8;             // 16-byte bf16 chunks per row
-  constexpr int PER = 64 * CH / 256;    // chunks per thread
-  __shared__ float red[256 / 64];
-  const int c = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
-  int ct, cy, cx;
-  cube_coords(g, c, ct, cy, cx);
-  uint4 v[PER];
-  float m = 0.f;
+struct CubeRows {
+  static constexpr int CH = D / 8;
+  static constexpr int PER = 64 * CH / kQThreads;
+  uint4 x[PER];
+  __device__ __forceinline__ void load(const uint16_t* __restrict__ src, const KGeom& g, int b, int h, int ct, int cy,
+                                       int cx) {
 #pragma unroll
-  for (int k = 0; k < PER; ++k) {
-    const int f = threadIdx.x + 256 * k, l = f / CH, ch = f % CH;
-    const long long tok = cube_token(g, ct, cy, cx, l);
-    v[k] = make_uint4(0, 0, 0, 0);
-    if (tok >= 0) v[k] = reinterpret_cast<const uint4*>(x + (((long long)b * g.S + tok) * g.H + h) * D)[ch];
-    const uint32_t w4[4] = {v[k].x, v[k].y, v[k].z, v[k].w};
-#pragma unroll
-    for (int e = 0; e < 4; ++e) m = fmaxf(m, fmaxf(fabsf(bf_lo(w4[e])), fabsf(bf_hi(w4[e]))));
+    for (int k = 0; k < PER; ++k) {
+      const int f = threadIdx.x + kQThreads * k, l = f / CH, ch = f % CH;
+      const long long tok = cube_token(g, ct, cy, cx, l);
+      x[k] = make_uint4(0, 0, 0, 0);
+      if (tok >= 0) x[k] = reinterpret_cast<const uint4*>(src + (((long long)b * g.S + tok) * g.H + h) * D)[ch];
+    }
   }
+};
+
+// Largest |x| over the workgroup (all threads get it).  red: 4 floats of LDS.
+__device__ __forceinline__ float block_max(float m, float* red) {
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
   __syncthreads();
-  m = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-  const float inv = inv_of(m);
-  const long long row0 = ((long long)b * g.H + h) * g.Np + 64LL * c;
+  return fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+}
+
+// Q or K of one cube: codes [B, H, Np, D] bytes, scale [B, H, Nc], and the
+// cube mean over valid tokens when mean != nullptr.  The mean is summed as
+// the pooling kernel sums it: per thread over its rows in order, then across
+// the threads of a chunk by exchanges at lane distances D/8 .. 32, then the
+// four wavefronts in order, divided by the count of valid tokens.  (Padded
+// rows hold zeros here; adding +0 to the fp32 sums changes no bit.)
+template <int D>
+__device__ __forceinline__ void quant_block(const CubeRows<D>& r, uint8_t* __restrict__ x8,
+                                            float* __restrict__ scale, float* __restrict__ mean, const KGeom& g,
+                                            long long bh, int c, int count, float* red, float (*part)[D]) {
+  constexpr int CH = D / 8, PER = CubeRows<D>::PER;
+  float m = 0.f;
+  float acc[8] = {};
 #pragma unroll
   for (int k = 0; k < PER; ++k) {
-    const int f = threadIdx.x + 256 * k, l = f / CH, ch = f % CH;
-    const uint32_t w4[4] = {v[k].x, v[k].y, v[k].z, v[k].w};
+    const uint32_t w4[4] = {r.x[k].x, r.x[k].y, r.x[k].z, r.x[k].w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float lo = bf_lo(w4[e]), hi = bf_hi(w4[e]);
+      m = fmaxf(m, fmaxf(fabsf(lo), fabsf(hi)));
+      acc[2 * e] += lo;
+      acc[2 * e + 1] += hi;
+    }
+  }
+  m = block_max(m, red);
+  const float inv = inv_of(m);
+  const long long row0 = bh * g.Np + 64LL * c;
+#pragma unroll
+  for (int k = 0; k < PER; ++k) {
+    const int f = threadIdx.x + kQThreads * k, l = f / CH, ch = f % CH;
+    const uint32_t w4[4] = {r.x[k].x, r.x[k].y, r.x[k].z, r.x[k].w};
     const uint32_t lo = to_e4m3x4(bf_lo(w4[0]) * inv, bf_hi(w4[0]) * inv, bf_lo(w4[1]) * inv, bf_hi(w4[1]) * inv);
     const uint32_t hi = to_e4m3x4(bf_lo(w4[2]) * inv, bf_hi(w4[2]) * inv, bf_lo(w4[3]) * inv, bf_hi(w4[3]) * inv);
     *reinterpret_cast<uint2*>(x8 + (row0 + l) * D + 8 * ch) = make_uint2(lo, hi);
   }
-  if (threadIdx.x == 0) scale[((long long)b * g.H + h) * g.nc + c] = __fdiv_rn(m, kE4M3Max);
-}
-
-// V, pass 1: per (b, h, cube) the largest |v| of every channel -> cmax [B, H, Nc, D].
-template <int D>
-__global__ void __launch_bounds__(256) chan_max_cube(const uint16_t* __restrict__ x, float* __restrict__ cmax,
-                                                     KGeom g) {
-  constexpr int CH = D / 8;
-  __shared__ float part[256 / CH][D];
-  const int c = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
-  int ct, cy, cx;
-  cube_coords(g, c, ct, cy, cx);
-  const int ch = threadIdx.x % CH, r0 = threadIdx.x / CH;  // rows r0, r0 + 256/CH, ...
-  float m[8] = {};
-  for (int l = r0; l < 64; l += 256 / CH) {
-    const long long tok = cube_token(g, ct, cy, cx, l);
-    if (tok < 0) continue;
-    const uint4 v = reinterpret_cast<const uint4*>(x + (((long long)b * g.S + tok) * g.H + h) * D)[ch];
-    const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+  if (threadIdx.x == 0) scale[bh * g.nc + c] = __fdiv_rn(m, kE4M3Max);
+  if (mean == nullptr) return;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      m[2 * e] = fmaxf(m[2 * e], fabsf(bf_lo(w4[e])));
-      m[2 * e + 1] = fmaxf(m[2 * e + 1], fabsf(bf_hi(w4[e])));
-    }
+  for (int off = CH; off < 64; off *= 2)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] += __shfl_xor(acc[e], off);
+  if (lane < CH) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) part[w][lane * 8 + e] = acc[e];
   }
-#pragma unroll
-  for (int e = 0; e < 8; ++e) part[r0][8 * ch + e] = m[e];
   __syncthreads();
   if (threadIdx.x < D) {
-    float r = 0.f;
-    for (int k = 0; k < 256 / CH; ++k) r = fmaxf(r, part[k][threadIdx.x]);
-    cmax[(((long long)b * g.H + h) * g.nc + c) * D + threadIdx.x] = r;
+    float sum = 0.f;
+#pragma unroll
+    for (int rr = 0; rr < kQThreads / 64; ++rr) sum += part[rr][threadIdx.x];
+    mean[(bh * g.nc + c) * D + threadIdx.x] = sum / (float)count;
   }
 }
 
-// V, pass 2: per (b, h) the channel maxima over all cubes -> scale [B, H, D].
-__global__ void __launch_bounds__(256) chan_max_head(const float* __restrict__ cmax, float* __restrict__ vmax,
-                                                     float* __restrict__ scale, KGeom g) {
-  const long long bh = blockIdx.x;
-  for (int d = threadIdx.x; d < g.D; d += 256) {
-    float r = 0.f;
-    for (int c = 0; c < g.nc; ++c) r = fmaxf(r, cmax[(bh * g.nc + c) * g.D + d]);
-    vmax[bh * g.D + d] = r;
-    scale[bh * g.D + d] = __fdiv_rn(r, kE4M3Max);
+// Pass 1.  vmax: [B, H, D] fp32 bit patterns, zero on entry.
+template <int D>
+__global__ void __launch_bounds__(kQThreads) quant_pass1(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+                                                          const uint16_t* __restrict__ v, uint8_t* __restrict__ q8,
+                                                          float* __restrict__ qscale, float* __restrict__ qmean,
+                                                          uint8_t* __restrict__ k8, float* __restrict__ kscale,
+                                                          float* __restrict__ kmean, uint32_t* __restrict__ vmax,
+                                                          KGeom g) {
+  constexpr int CH = D / 8, PER = CubeRows<D>::PER;
+  __shared__ float red[2][kQThreads / 64];
+  __shared__ float part[3][kQThreads / 64][D];
+  const int c = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const long long bh = (long long)b * g.H + h;
+  int ct, cy, cx;
+  cube_coords(g, c, ct, cy, cx);
+  CubeRows<D> rq, rk, rv;
+  rq.load(q, g, b, h, ct, cy, cx);
+  rk.load(k, g, b, h, ct, cy, cx);
+  rv.load(v, g, b, h, ct, cy, cx);
+  const int count = cube_count(g, ct, cy, cx);
+  quant_block<D>(rq, q8, qscale, qmean, g, bh, c, count, red[0], part[0]);
+  quant_block<D>(rk, k8, kscale, kmean, g, bh, c, count, red[1], part[1]);
+  // V: largest |v| of every channel over the cube's rows.
+  float cm[8] = {};
+#pragma unroll
+  for (int kk = 0; kk < PER; ++kk) {
+    const uint32_t w4[4] = {rv.x[kk].x, rv.x[kk].y, rv.x[kk].z, rv.x[kk].w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      cm[2 * e] = fmaxf(cm[2 * e], fabsf(bf_lo(w4[e])));
+      cm[2 * e + 1] = fmaxf(cm[2 * e + 1], fabsf(bf_hi(w4[e])));
+    }
+  }
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+#pragma unroll
+  for (int off = CH; off < 64; off *= 2)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) cm[e] = fmaxf(cm[e], __shfl_xor(cm[e], off));
+  if (lane < CH) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) part[2][w][lane * 8 + e] = cm[e];
+  }
+  __syncthreads();
+  if (threadIdx.x < D) {
+    float r = part[2][0][threadIdx.x];
+#pragma unroll
+    for (int rr = 1; rr < kQThreads / 64; ++rr) r = fmaxf(r, part[2][rr][threadIdx.x]);
+    atomicMax(vmax + bh * D + threadIdx.x, __float_as_uint(r));
   }
 }
 
@@ -135,70 +193,82 @@ __device__ __forceinline__ int vkey_pos(int k) {
   return 32 * hh + 16 * t + 8 * gg + e;
 }
 
-// V, pass 3: per (b, h, cube) codes of v * (448 / vmax[channel]), stored as
-// the cube transposed: [B, H, Nc, D, 64] bytes, keys in vkey_pos order.
+// Pass 2: codes of v * (448 / vmax[channel]) stored as the cube transposed,
+// [B, H, Nc, D, 64] bytes with keys in vkey_pos order; cube 0's workgroup
+// also writes the scales [B, H, D].
 template <int D>
-__global__ void __launch_bounds__(256) quant_v(const uint16_t* __restrict__ x, const float* __restrict__ vmax,
-                                               uint8_t* __restrict__ v8t, KGeom g) {
-  constexpr int CH = D / 8;
-  __shared__ uint8_t tile[D][64 + 4];  // [channel][key position], padded rows
+__global__ void __launch_bounds__(kQThreads) quant_pass2(const uint16_t* __restrict__ v,
+                                                          const uint32_t* __restrict__ vmax,
+                                                          uint8_t* __restrict__ v8t, float* __restrict__ vscale,
+                                                          KGeom g) {
+  constexpr int CH = D / 8, PER = CubeRows<D>::PER, LD = 68;  // LDS row: 64 key bytes + 4
+  __shared__ __attribute__((aligned(16))) uint8_t tile[D * LD];
   const int c = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const long long bh = (long long)b * g.H + h;
   int ct, cy, cx;
   cube_coords(g, c, ct, cy, cx);
-  for (int f = threadIdx.x; f < 64 * CH; f += 256) {
-    const int l = f / CH, ch = f % CH;
-    const long long tok = cube_token(g, ct, cy, cx, l);
-    uint4 v = make_uint4(0, 0, 0, 0);
-    if (tok >= 0) v = reinterpret_cast<const uint4*>(x + (((long long)b * g.S + tok) * g.H + h) * D)[ch];
-    const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+  CubeRows<D> rv;
+  rv.load(v, g, b, h, ct, cy, cx);
+  const int ch = threadIdx.x % CH;  // the same chunk (8 channels) on every row of this thread
+  float inv[8];
+  {
+    const uint4 m0 = reinterpret_cast<const uint4*>(vmax + bh * D)[2 * ch];
+    const uint4 m1 = reinterpret_cast<const uint4*>(vmax + bh * D)[2 * ch + 1];
+    const uint32_t mm[8] = {m0.x, m0.y, m0.z, m0.w, m1.x, m1.y, m1.z, m1.w};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) inv[e] = inv_of(__uint_as_float(mm[e]));
+  }
+#pragma unroll
+  for (int k = 0; k < PER; ++k) {
+    const int f = threadIdx.x + kQThreads * k, l = f / CH;
     const int pos = vkey_pos(l);
+    const uint32_t w4[4] = {rv.x[k].x, rv.x[k].y, rv.x[k].z, rv.x[k].w};
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const int d0 = 8 * ch + 2 * e;
-      const float a = bf_lo(w4[e]) * inv_of(vmax[bh * D + d0]);
-      const float bb = bf_hi(w4[e]) * inv_of(vmax[bh * D + d0 + 1]);
-      const uint32_t w = to_e4m3x4(a, bb, 0.f, 0.f);
-      tile[d0][pos] = (uint8_t)(w & 0xFF);
-      tile[d0 + 1][pos] = (uint8_t)((w >> 8) & 0xFF);
+      const uint32_t wd = to_e4m3x4(bf_lo(w4[e]) * inv[2 * e], bf_hi(w4[e]) * inv[2 * e + 1], 0.f, 0.f);
+      tile[(8 * ch + 2 * e) * LD + pos] = (uint8_t)(wd & 0xFF);
+      tile[(8 * ch + 2 * e + 1) * LD + pos] = (uint8_t)((wd >> 8) & 0xFF);
     }
   }
   __syncthreads();
-  // D rows of 64 bytes: 4 x 16 bytes per row.
   uint8_t* out = v8t + (bh * g.nc + c) * (long long)D * 64;
-  for (int f = threadIdx.x; f < D * 4; f += 256) {
-    const int d = f >> 2, q = f & 3;
-    uint32_t w[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e)
-      w[e] = (uint32_t)tile[d][16 * q + 4 * e] | ((uint32_t)tile[d][16 * q + 4 * e + 1] << 8) |
-             ((uint32_t)tile[d][16 * q + 4 * e + 2] << 16) | ((uint32_t)tile[d][16 * q + 4 * e + 3] << 24);
-    *reinterpret_cast<uint4*>(out + d * 64 + 16 * q) = make_uint4(w[0], w[1], w[2], w[3]);
+  for (int f = threadIdx.x; f < D * 4; f += kQThreads) {
+    const int d = f >> 2, qq = f & 3;
+    const uint32_t* src = reinterpret_cast<const uint32_t*>(tile + d * LD + 16 * qq);
+    *reinterpret_cast<uint4*>(out + d * 64 + 16 * qq) = make_uint4(src[0], src[1], src[2], src[3]);
   }
+  if (c == 0 && threadIdx.x < D)
+    vscale[bh * D + threadIdx.x] = __fdiv_rn(__uint_as_float(vmax[bh * D + threadIdx.x]), kE4M3Max);
+}
+
+__global__ void __launch_bounds__(kQThreads) zero_words(uint32_t* __restrict__ p, long long n) {
+  for (long long i = (long long)blockIdx.x * kQThreads + threadIdx.x; i < n; i += (long long)gridDim.x * kQThreads)
+    p[i] = 0u;
+}
+
+template <int D>
+void launch_quant_t(const KGeom& g, const uint16_t* q, const uint16_t* k, const uint16_t* v, uint8_t* q8, float* qs,
+                    uint8_t* k8, float* ks, uint8_t* v8t, float* vs, float* qmean, float* kmean, uint32_t* vmax,
+                    hipStream_t s) {
+  const long long nmax = (long long)g.B * g.H * D;
+  zero_words<<<dim3((unsigned)((nmax + kQThreads - 1) / kQThreads)), dim3(kQThreads), 0, s>>>(vmax, nmax);
+  const dim3 grid(g.nc, g.H, g.B);
+  quant_pass1<D><<<grid, dim3(kQThreads), 0, s>>>(q, k, v, q8, qs, qmean, k8, ks, kmean, vmax, g);
+  quant_pass2<D><<<grid, dim3(kQThreads), 0, s>>>(v, vmax, v8t, vs, g);
 }
 
 }  // namespace
 
-size_t quant_v_workspace_bytes(const KGeom& g) {
-  return (size_t)g.B * g.H * ((size_t)g.nc + 1) * g.D * sizeof(float);
+size_t quant_workspace_bytes(const KGeom& g) {
+  return ((size_t)g.B * g.H * g.D * sizeof(uint32_t) + 255) / 256 * 256;
 }
 
-hipError_t launch_quant_qk(const KGeom& g, const uint16_t* x, uint8_t* x8, float* scale, hipStream_t s) {
-  const dim3 grid(g.nc, g.H, g.B);
-  if (g.D == 64) quant_cube<64><<<grid, dim3(256), 0, s>>>(x, x8, scale, g);
-  else quant_cube<128><<<grid, dim3(256), 0, s>>>(x, x8, scale, g);
-  return hipGetLastError();
-}
-
-hipError_t launch_quant_v(const KGeom& g, const uint16_t* x, uint8_t* v8t, float* scale, void* ws, hipStream_t s) {
-  float* cmax = static_cast<float*>(ws);
-  float* vmax = cmax + (size_t)g.B * g.H * g.nc * g.D;
-  const dim3 grid(g.nc, g.H, g.B);
-  if (g.D == 64) chan_max_cube<64><<<grid, dim3(256), 0, s>>>(x, cmax, g);
-  else chan_max_cube<128><<<grid, dim3(256), 0, s>>>(x, cmax, g);
-  chan_max_head<<<dim3(g.B * g.H), dim3(256), 0, s>>>(cmax, vmax, scale, g);
-  if (g.D == 64) quant_v<64><<<grid, dim3(256), 0, s>>>(x, vmax, v8t, g);
-  else quant_v<128><<<grid, dim3(256), 0, s>>>(x, vmax, v8t, g);
+hipError_t launch_quant(const KGeom& g, const uint16_t* q, const uint16_t* k, const uint16_t* v, uint8_t* q8,
+                        float* qs, uint8_t* k8, float* ks, uint8_t* v8t, float* vs, float* qmean, float* kmean,
+                        void* ws, hipStream_t s) {
+  uint32_t* vmax = static_cast<uint32_t*>(ws);
+  if (g.D == 64) launch_quant_t<64>(g, q, k, v, q8, qs, k8, ks, v8t, vs, qmean, kmean, vmax, s);
+  else launch_quant_t<128>(g, q, k, v, q8, qs, k8, ks, v8t, vs, qmean, kmean, vmax, s);
   return hipGetLastError();
 }
 

@@ -216,15 +216,18 @@ int32_t vsa_sparse_attn_fwd(const vsa_geom* g, const uint16_t* qc, const uint16_
  * round-to-nearest-even of clamp(x * inv, -448, 448) in fp32, and
  * scale = m / 448, so that x ~ code * scale.
  *
- * vsa_quant_qk_fp8: x raster [B, S, heads, D] bf16 (Q or K) -> x8 codes
- * [B, heads, Np, D] uint8 (cube-major rows, padded rows 0) and scale
- * [B, heads, Nc] fp32, one block per (b, h, cube).
- *
- * vsa_quant_v_fp8: v raster bf16 -> v8t codes [B, heads, Nc, D, 64] uint8
- * (each cube transposed, keys within a channel row in the order the fine
- * stage consumes them: key 32 t + 16 g + 8 h + e at 32 h + 16 t + 8 g + e) and
- * scale [B, heads, D] fp32, one block per (b, h, channel) over the head.
- * ws: at least vsa_quant_v_fp8_workspace_bytes(g) bytes.
+ * vsa_quant_fp8: raster [B, S, heads, D] bf16 q, k, v ->
+ *   q8, k8: codes [B, heads, Np, D] uint8 (cube-major rows, padded rows 0),
+ *     qscale, kscale [B, heads, Nc] fp32, one block per (b, h, cube);
+ *   v8t: codes [B, heads, Nc, D, 64] uint8 (each cube transposed, keys within
+ *     a channel row in the order the fine stage consumes them: key
+ *     32 t + 16 g + 8 h + e at 32 h + 16 t + 8 g + e), vscale [B, heads, D]
+ *     fp32, one block per (b, h, channel) over the head;
+ *   qmean, kmean: optional (may be NULL) fp32 [B, heads, Nc, D] cube means over
+ *     valid tokens, bit-identical to vsa_cube_permute_pool's, for the coarse
+ *     stage.
+ * ws: at least vsa_quant_fp8_workspace_bytes(g) bytes of device memory,
+ * overwritten (the head maxima of V).  Three launches on `stream`.
  *
  * vsa_sparse_attn_fwd_fp8: the fine stage of vsa_sparse_attn_fwd on these
  * codes with fp8 matrix products: logits scale * sq_i * sk_j * (q8 . k8),
@@ -232,10 +235,10 @@ int32_t vsa_sparse_attn_fwd(const vsa_geom* g, const uint16_t* qc, const uint16_
  * that its largest lies in [2^4, 2^8], O = sv * (v8^T P) / sum(P) over the
  * rounded weights.  oc: bf16 [B, heads, Np, D] TOKEN_MAJOR; lse optional as
  * there.  All pointers 16-byte aligned. */
-size_t vsa_quant_v_fp8_workspace_bytes(const vsa_geom* g);
-int32_t vsa_quant_qk_fp8(const vsa_geom* g, const uint16_t* x, uint8_t* x8, float* scale, void* stream);
-int32_t vsa_quant_v_fp8(const vsa_geom* g, const uint16_t* v, uint8_t* v8t, float* scale, void* ws,
-                        size_t ws_bytes, void* stream);
+size_t vsa_quant_fp8_workspace_bytes(const vsa_geom* g);
+int32_t vsa_quant_fp8(const vsa_geom* g, const uint16_t* q, const uint16_t* k, const uint16_t* v, uint8_t* q8,
+                      float* qscale, uint8_t* k8, float* kscale, uint8_t* v8t, float* vscale, float* qmean,
+                      float* kmean, void* ws, size_t ws_bytes, void* stream);
 int32_t vsa_sparse_attn_fwd_fp8(const vsa_geom* g, const uint8_t* q8, const float* qscale,
                                 const uint8_t* k8, const float* kscale, const uint8_t* v8t,
                                 const float* vscale, const int32_t* idx, int32_t topk,

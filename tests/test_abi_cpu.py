@@ -207,16 +207,17 @@ def test_fp8_entry_point_validation(lib):
 
     g = geom()
     P = FAKE
-    ws = lib.vsa_quant_v_fp8_workspace_bytes(g)
-    # per-(b, h, cube) channel maxima plus per-(b, h) maxima, fp32
-    assert ws == 1 * 2 * (8 + 1) * 64 * 4
-    assert lib.vsa_quant_v_fp8_workspace_bytes(geom(D=16)) == 0
-    assert lib.vsa_quant_qk_fp8(g, P, P, None, None) == _lib.VSA_ERR_NULL
-    assert lib.vsa_quant_qk_fp8(g, P, ODD, P, None) == _lib.VSA_ERR_ALIGN
-    assert lib.vsa_quant_qk_fp8(geom(D=16), P, P, P, None) == _lib.VSA_ERR_HEAD_DIM
-    assert lib.vsa_quant_v_fp8(g, P, P, P, None, ws, None) == _lib.VSA_ERR_NULL
-    assert lib.vsa_quant_v_fp8(g, P, P, ODD, P, ws, None) == _lib.VSA_ERR_ALIGN
-    assert lib.vsa_quant_v_fp8(g, P, P, P, P, ws - 1, None) == _lib.VSA_ERR_WORKSPACE
+    ws = lib.vsa_quant_fp8_workspace_bytes(g)
+    assert ws == 512  # the head maxima of V, B x H x D fp32, rounded up to 256 bytes
+    assert lib.vsa_quant_fp8_workspace_bytes(geom(D=16)) == 0
+    qa = [P] * 10  # q k v q8 qscale k8 kscale v8t vscale qmean
+    assert lib.vsa_quant_fp8(g, *qa[:9], None, None, None, ws, None) == _lib.VSA_ERR_NULL   # workspace
+    assert lib.vsa_quant_fp8(g, None, *qa[1:], None, P, ws, None) == _lib.VSA_ERR_NULL
+    assert lib.vsa_quant_fp8(g, *qa[:8], None, None, None, P, ws, None) == _lib.VSA_ERR_NULL  # vscale
+    assert lib.vsa_quant_fp8(g, *qa[:3], ODD, *qa[4:], None, P, ws, None) == _lib.VSA_ERR_ALIGN
+    assert lib.vsa_quant_fp8(g, *qa, ODD, P, ws, None) == _lib.VSA_ERR_ALIGN               # kmean
+    assert lib.vsa_quant_fp8(g, *qa, None, P, ws - 1, None) == _lib.VSA_ERR_WORKSPACE
+    assert lib.vsa_quant_fp8(geom(D=16), *qa, None, P, ws, None) == _lib.VSA_ERR_HEAD_DIM
     args = [P] * 7  # q8 qscale k8 kscale v8t vscale idx
     assert lib.vsa_sparse_attn_fwd_fp8(g, *args, 2, 0.125, None, None, None) == _lib.VSA_ERR_NULL
     assert lib.vsa_sparse_attn_fwd_fp8(g, *args[:6], None, 2, 0.125, P, None, None) == _lib.VSA_ERR_NULL

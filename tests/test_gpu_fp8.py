@@ -4,7 +4,8 @@ products) against the fp64 oracle.
 1. The quantizers are bit-exact against the oracle's (O10): codes and scales
    of Q and K per (b, h, cube), of V per (b, h, channel); V's codes in the
    documented tile order (each cube transposed, key k = 32 t + 16 g + 8 h + e
-   at position 32 h + 16 t + 8 g + e).
+   at position 32 h + 16 t + 8 g + e).  The cube means the same pass writes
+   are bit-identical to the pooling kernel's.
 2. With Q = 0 every weight is exactly 1, so the fp8 stage must give the mean
    of the dequantized V over the selected valid keys, up to fp32 sums and the
    bf16 output rounding.
@@ -83,11 +84,11 @@ def gpu_fp8(inp, grid, idx_np, scale, q_zero=False):
     q, k, v = (to_dev(inp[n]) for n in ("q", "k", "v"))
     if q_zero:
         q = torch.zeros_like(q)
-    q8, qs = vsa.quant_qk_fp8(q, grid)
-    k8, ks = vsa.quant_qk_fp8(k, grid)
-    v8t, vs = vsa.quant_v_fp8(v, grid)
+    q8, qs, k8, ks, v8t, vs, qm, km = vsa.quant_fp8(q, k, v, grid, want_means=True)
     idx = torch.from_numpy(np.ascontiguousarray(idx_np, dtype=np.int32)).to("cuda:0")
     oc, lse = vsa.sparse_attn_fwd_fp8(q8, qs, k8, ks, v8t, vs, idx, grid, scale, want_lse=True)
+    # The means for the coarse stage come out of the same pass, bit-identical to the pooling kernel's.
+    assert torch.equal(qm, vsa.cube_pool(q, grid)) and torch.equal(km, vsa.cube_pool(k, grid))
     torch.cuda.synchronize()
     codes = tuple(t.cpu().numpy() for t in (q8, qs, k8, ks, v8t, vs))
     return oracle.bf16_to_f64(to_bits(oc)), lse.cpu().numpy().astype(np.float64), codes
