@@ -51,6 +51,9 @@ def parse():
     ap.add_argument("--backward", action="store_true",
                     help="also time the backward of the fine stage (dQ, dK, dV) after the forward steps; "
                          "reported under 'backward', not in 'value'")
+    ap.add_argument("--fused-linear", action="store_true",
+                    help="hybrid layer: the fine stage and the linear branch in one fused pass "
+                         "(vsa_sparse_attn_linear_fwd) instead of two calls with fp32 O_sparse in between")
     ap.add_argument("--fp8", action="store_true",
                     help="low-precision layer: Q, K, V quantized to fp8 E4M3 in the step, fine stage on the "
                          "fp8 matrix cores (roofline against the fp8 peak)")
@@ -255,7 +258,7 @@ def main():
     ws_sel = torch.empty(vsa.workspace_bytes(g), dtype=torch.uint8, device=dev)
     ws_lin = torch.empty(max(16, vsa.workspace_bytes(g, linear=True)) if wl.linear else 16,
                          dtype=torch.uint8, device=dev)
-    of = torch.empty((B, H, d.rows, D), dtype=torch.float32, device=dev) if wl.linear else None
+    of = torch.empty((B, H, d.rows, D), dtype=torch.float32, device=dev) if wl.linear and not args.fused_linear else None
     oc2 = torch.empty_like(qc) if wl.linear else None
 
     # Without the linear branch the fine stage reads Q and writes the output in
@@ -264,7 +267,10 @@ def main():
     # rows; --k-raster gathers them instead), V is permuted into the
     # cube-transposed layout.  The linear branch works on cube-major rows, so
     # the hybrid layer keeps the permute / unpermute pair.
-    stages = ["permute", "select", "fine", "linear", "unpermute"] if wl.linear else ["pool", "select", "fine"]
+    stages = ["pool", "select", "fine"]
+    if wl.linear:
+        stages = (["permute", "select", "fine+linear", "unpermute"] if args.fused_linear else
+                  ["permute", "select", "fine", "linear", "unpermute"])
     if args.fp8:
         if wl.linear:
             print("--fp8 covers the fine stage without the linear branch", file=sys.stderr)
@@ -334,6 +340,14 @@ def main():
             vsa.sparse_attn_fwd_raster(q, k if args.k_raster else kc, vt, idx, wl.grid, wl.softmax_scale, out=o)
             mark(3)
             return
+        if args.fused_linear:
+            # One pass: softmax branch and the linear branch's selected-block
+            # correction on the same tiles, combined in the kernel.
+            vsa.sparse_attn_linear_fwd(qc, kc, vt, idx, wl.grid, wl.softmax_scale, out=oc2, workspace=ws_lin)
+            mark(3)
+            vsa.cube_unpermute(oc2, wl.grid, out=o)
+            mark(4)
+            return
         vsa.sparse_attn_fwd(qc, kc, vt, idx, wl.grid, wl.softmax_scale, out=oc, out_f32=of)
         mark(3)
         vsa.linear_branch(qc, kc, vt, idx, of, wl.grid, out=oc2, workspace=ws_lin)
@@ -364,7 +378,8 @@ def main():
         for i, name in enumerate(stages):
             per_stage[name].append(evs[s][i].elapsed_time(evs[s][i + 1]))
     stage_ms = {name: float(np.median(vals)) for name, vals in per_stage.items()}
-    fine_ms = float(np.mean(per_stage["fine"]))
+    fine_key = "fine+linear" if "fine+linear" in per_stage else "fine"
+    fine_ms = float(np.mean(per_stage[fine_key]))
     if not torch.isfinite(o.float()).all():
         print("non-finite output", file=sys.stderr)
         sys.exit(1)
@@ -377,6 +392,9 @@ def main():
     alg_bytes = 4 * B * H * d.rows * D * 2
     peak, kname = PEAK_BF16_TFLOPS, "attn_fwd"
     traffic = measured_traffic(wl.name)
+    if wl.linear and args.fused_linear:
+        kname = "attn_lin_fwd (stage includes lin_state, lin_reduce)"
+        traffic = None
     if args.fp8:
         alg_bytes = B * H * d.rows * D * (1 + 1 + 1 + 2) + 4 * B * H * (2 * d.n_cubes + D)
         peak, kname = PEAK_FP8_TFLOPS, "attn_fwd_fp8"

@@ -46,6 +46,7 @@ __all__ = [
     "linear_branch",
     "sparse_attn_fwd_raster",
     "sparse_attn_bwd",
+    "sparse_attn_linear_fwd",
     "quant_fp8",
     "quant_fp8_workspace_bytes",
     "sparse_attn_fwd_fp8",
@@ -413,6 +414,34 @@ def linear_branch(qc: torch.Tensor, kc: torch.Tensor, vt: torch.Tensor, idx: tor
     return out
 
 
+def sparse_attn_linear_fwd(qc: torch.Tensor, kc: torch.Tensor, vt: torch.Tensor, idx: torch.Tensor,
+                           grid: Sequence[int], scale: Optional[float] = None, want_lse: bool = False,
+                           out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None):
+    """Fine stage and linear branch in one pass: (bf16(O_sparse + O_lin) token-major, lse or None)."""
+    B, Hh, Np, D = qc.shape
+    g = make_geom(B, Hh, D, grid)
+    d = geom_dims(g)
+    topk = idx.shape[-1]
+    _need(qc, "qc", torch.bfloat16, (B, Hh, d.rows, D))
+    _need(kc, "kc", torch.bfloat16, (B, Hh, d.rows, D))
+    _need(vt, "vt", torch.bfloat16, (B, Hh, d.n_cubes, D, 64))
+    _need(idx, "idx", torch.int32, (B, Hh, d.n_cubes, topk))
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty((B, Hh, d.rows, D), dtype=torch.bfloat16, device=qc.device)
+    _need(out, "oc", torch.bfloat16, (B, Hh, d.rows, D))
+    lse = torch.empty((B, Hh, d.rows), dtype=torch.float32, device=qc.device) if want_lse else None
+    nbytes = workspace_bytes(g, linear=True)
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=qc.device)
+    _lib.check("vsa_sparse_attn_linear_fwd", _lib.load().vsa_sparse_attn_linear_fwd(
+        g, qc.data_ptr(), kc.data_ptr(), vt.data_ptr(), idx.data_ptr(), int(topk), float(scale), out.data_ptr(),
+        lse.data_ptr() if lse is not None else None, workspace.data_ptr(),
+        workspace.numel() * workspace.element_size(), _stream()))
+    return out, lse
+
+
 def vsa_attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, grid: Sequence[int], topk: int,
                   scale: Optional[float] = None, linear: bool = False, idx: Optional[torch.Tensor] = None):
     """One attention layer: [B, S, heads, D] bf16 -> (o [B, S, heads, D] bf16, idx).
@@ -424,7 +453,8 @@ def vsa_attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, grid: Seque
     vt = cube_permute(v, grid, layout="dim")
     if idx is None:
         idx = select_topk_pooled(qbar, kbar, grid, topk)
-    oc, of, _ = sparse_attn_fwd(qc, kc, vt, idx, grid, scale, want_f32=linear)
     if linear:
-        oc = linear_branch(qc, kc, vt, idx, of, grid)
+        oc, _ = sparse_attn_linear_fwd(qc, kc, vt, idx, grid, scale)
+    else:
+        oc, _, _ = sparse_attn_fwd(qc, kc, vt, idx, grid, scale)
     return cube_unpermute(oc, grid), idx

@@ -47,6 +47,7 @@ ENTRY_POINTS = (
     "vsa_quant_fp8_workspace_bytes",
     "vsa_quant_fp8",
     "vsa_sparse_attn_fwd_fp8",
+    "vsa_sparse_attn_linear_fwd",
 )
 
 
@@ -120,6 +121,7 @@ def load() -> ctypes.CDLL:
         "vsa_quant_fp8_workspace_bytes": (sz, [G]),
         "vsa_quant_fp8": (i32, [G, P, P, P, P, P, P, P, P, P, P, P, P, sz, P]),
         "vsa_sparse_attn_fwd_fp8": (i32, [G, P, P, P, P, P, P, P, i32, ctypes.c_float, P, P, P]),
+        "vsa_sparse_attn_linear_fwd": (i32, [G, P, P, P, P, i32, ctypes.c_float, P, P, P, sz, P]),
         "vsa_sparse_attn_bwd": (i32, [G, P, P, P, P, P, P, P, P, P, P, i32, ctypes.c_float, P, P, P, P, sz, P]),
     }
     for name, (res, args) in sig.items():

@@ -304,6 +304,24 @@ int32_t vsa_sparse_attn_fwd(const vsa_geom* g, const uint16_t* qc, const uint16_
                                             static_cast<hipStream_t>(stream)));
 }
 
+int32_t vsa_sparse_attn_linear_fwd(const vsa_geom* g, const uint16_t* qc, const uint16_t* kc, const uint16_t* vt,
+                                   const int32_t* idx, int32_t topk, float softmax_scale, uint16_t* oc, float* lse,
+                                   void* ws, size_t ws_bytes, void* stream) {
+  vsa_dims d;
+  vsa::KGeom k;
+  int32_t st = prepare(g, &d, &k);
+  if (st != VSA_OK) return st;
+  if (!qc || !kc || !vt || !idx || !oc || !ws) return VSA_ERR_NULL;
+  if (!aligned16(qc) || !aligned16(kc) || !aligned16(vt) || !aligned16(idx) || !aligned16(oc) || !aligned16(ws) ||
+      (lse && !aligned16(lse)))
+    return VSA_ERR_ALIGN;
+  if (topk < 1 || topk > d.n_cubes) return VSA_ERR_TOPK;
+  if (!(softmax_scale > 0.f) || !isfinite(softmax_scale)) return VSA_ERR_SCALE;
+  if (ws_bytes < vsa::linear_workspace_bytes(k)) return VSA_ERR_WORKSPACE;
+  return launch_status(vsa::launch_attn_lin_fwd(k, qc, kc, vt, idx, topk, softmax_scale, ws, oc, lse,
+                                                static_cast<hipStream_t>(stream)));
+}
+
 int32_t vsa_linear_branch(const vsa_geom* g, const uint16_t* qc, const uint16_t* kc, const uint16_t* vt,
                           const int32_t* idx, int32_t topk, const float* o_sparse, uint16_t* oc, void* ws,
                           size_t ws_bytes, void* stream) {

@@ -73,6 +73,9 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
 }
 
+// Feature map of the linear branch: phi(x) = elu(x) + 1 (alpha = 1).
+__device__ __forceinline__ float phi_elu1(float x) { return x > 0.f ? x + 1.f : __expf(x); }
+
 }  // namespace vsa
 
 // Host launchers (each returns hipSuccess or the launch error).
@@ -96,6 +99,20 @@ hipError_t launch_linear(const KGeom& g, const uint16_t* qc, const uint16_t* kc,
                          const int32_t* idx, int topk, const float* o_sparse, uint16_t* oc, void* ws,
                          hipStream_t s);
 size_t linear_workspace_bytes(const KGeom& g);
+// The parts of the linear workspace the selected-block correction reads:
+// phi(K) token-major bf16 [B, H, Np, D], S_tot^T as bf16 hi + lo [B, H, D, D],
+// z_tot fp32 [B, H, D].  launch_lin_prep fills them (lin_state, lin_reduce).
+struct LinTensors {
+  const uint16_t* fk;
+  const uint16_t* st_hi;
+  const uint16_t* st_lo;
+  const float* z_tot;
+};
+LinTensors lin_tensors(const KGeom& g, void* ws);
+hipError_t launch_lin_prep(const KGeom& g, const uint16_t* kc, const uint16_t* vt, void* ws, hipStream_t s);
+hipError_t launch_attn_lin_fwd(const KGeom& g, const uint16_t* qc, const uint16_t* kc, const uint16_t* vt,
+                               const int32_t* idx, int topk, float scale, void* ws, uint16_t* oc, float* lse,
+                               hipStream_t s);
 hipError_t launch_sta_index(const KGeom& g, int wt, int wh, int ww, int32_t* idx, hipStream_t s);
 size_t attn_bwd_workspace_bytes(const KGeom& g, int topk);
 size_t quant_workspace_bytes(const KGeom& g);

@@ -33,7 +33,7 @@ namespace {
 using namespace tiles;
 constexpr int kGroup = 8;  // cubes per partial state
 
-__device__ __forceinline__ float phi(float x) { return x > 0.f ? x + 1.f : __expf(x); }
+__device__ __forceinline__ float phi(float x) { return phi_elu1(x); }
 
 struct LinWs {
   uint16_t* fk;     // [B, H, Np, D] bf16 phi(K), token-major
@@ -341,23 +341,37 @@ size_t linear_workspace_bytes(const KGeom& g) {
   return total;
 }
 
-hipError_t launch_linear(const KGeom& g, const uint16_t* qc, const uint16_t* kc, const uint16_t* vt,
-                         const int32_t* idx, int topk, const float* o_sparse, uint16_t* oc, void* ws,
-                         hipStream_t s) {
+LinTensors lin_tensors(const KGeom& g, void* ws) {
+  const LinWs w = carve(g, ws, nullptr);
+  return LinTensors{w.fk, w.st_hi, w.st_lo, w.z_tot};
+}
+
+hipError_t launch_lin_prep(const KGeom& g, const uint16_t* kc, const uint16_t* vt, void* ws, hipStream_t s) {
   const LinWs w = carve(g, ws, nullptr);
   const int G = (g.nc + kGroup - 1) / kGroup;
   const unsigned bh = (unsigned)(g.B * g.H);
   if (g.D == 64) {
     hipLaunchKernelGGL(lin_state<64>, dim3(G, g.H, g.B), dim3(256), 0, s, kc, vt, w, g);
     hipLaunchKernelGGL(lin_reduce<64>, dim3(64 * 64 / 256, bh), dim3(256), 0, s, w, g);
-    hipLaunchKernelGGL(lin_apply<64>, dim3(grid_size(g)), dim3(kThreads), 0, s, qc, vt, idx, topk, o_sparse, oc,
-                       w, g, make_placement(g));
   } else {
     hipLaunchKernelGGL(lin_state<128>, dim3(G, g.H, g.B), dim3(256), 0, s, kc, vt, w, g);
     hipLaunchKernelGGL(lin_reduce<128>, dim3(128 * 128 / 256, bh), dim3(256), 0, s, w, g);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_linear(const KGeom& g, const uint16_t* qc, const uint16_t* kc, const uint16_t* vt,
+                         const int32_t* idx, int topk, const float* o_sparse, uint16_t* oc, void* ws,
+                         hipStream_t s) {
+  hipError_t e = launch_lin_prep(g, kc, vt, ws, s);
+  if (e != hipSuccess) return e;
+  const LinWs w = carve(g, ws, nullptr);
+  if (g.D == 64)
+    hipLaunchKernelGGL(lin_apply<64>, dim3(grid_size(g)), dim3(kThreads), 0, s, qc, vt, idx, topk, o_sparse, oc,
+                       w, g, make_placement(g));
+  else
     hipLaunchKernelGGL(lin_apply<128>, dim3(grid_size(g)), dim3(kThreads), 0, s, qc, vt, idx, topk, o_sparse, oc,
                        w, g, make_placement(g));
-  }
   return hipGetLastError();
 }
 

@@ -282,6 +282,24 @@ int32_t vsa_linear_branch(const vsa_geom* g, const uint16_t* qc, const uint16_t*
                           const float* o_sparse, uint16_t* oc, void* ws,
                           size_t ws_bytes, void* stream);
 
+/* Fine stage and linear branch in one pass:
+ * oc = bf16(O_sparse + O_lin), the result of vsa_sparse_attn_fwd followed by
+ * vsa_linear_branch, without the fp32 O_sparse round trip and without reading
+ * the selected V tiles twice.  The selected-block correction of the linear
+ * branch runs on the same tile pipeline as the softmax (one workgroup of 8
+ * wavefronts per query cube).  qc, kc: TOKEN_MAJOR bf16; vt: DIM_MAJOR
+ * bf16; idx, topk, softmax_scale as for vsa_sparse_attn_fwd; oc: output bf16
+ * TOKEN_MAJOR; lse: optional fp32 [B, heads, Np], the log-sum-exp of the
+ * softmax branch alone.  ws: at least vsa_linear_workspace_bytes(g) bytes
+ * (overwritten: phi(K), the total state).  Three launches on `stream`.
+ * The fp32 sums are those of the two-call chain, in the same order; outputs
+ * can differ from it in the last bf16 bits where multiply-add contraction in
+ * the final combine differs. */
+int32_t vsa_sparse_attn_linear_fwd(const vsa_geom* g, const uint16_t* qc, const uint16_t* kc,
+                                   const uint16_t* vt, const int32_t* idx, int32_t topk,
+                                   float softmax_scale, uint16_t* oc, float* lse, void* ws,
+                                   size_t ws_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

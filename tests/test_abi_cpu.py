@@ -227,3 +227,21 @@ def test_fp8_entry_point_validation(lib):
     assert lib.vsa_sparse_attn_fwd_fp8(g, *args, 9, 0.125, P, None, None) == _lib.VSA_ERR_TOPK
     assert lib.vsa_sparse_attn_fwd_fp8(g, *args, 2, float("inf"), P, None, None) == _lib.VSA_ERR_SCALE
     assert lib.vsa_sparse_attn_fwd_fp8(geom(D=96), *args, 2, 0.125, P, None, None) == _lib.VSA_ERR_HEAD_DIM
+
+
+def test_fused_linear_entry_point_validation(lib):
+    from block_sparse_video_cube_amd import _lib
+
+    g = geom()
+    P = FAKE
+    ws = lib.vsa_linear_workspace_bytes(g)
+    f = lib.vsa_sparse_attn_linear_fwd
+    assert f(g, P, P, P, P, 2, 0.125, None, None, P, ws, None) == _lib.VSA_ERR_NULL
+    assert f(g, P, P, P, P, 2, 0.125, P, None, None, ws, None) == _lib.VSA_ERR_NULL
+    assert f(g, P, ODD, P, P, 2, 0.125, P, None, P, ws, None) == _lib.VSA_ERR_ALIGN
+    assert f(g, P, P, P, P, 2, 0.125, P, ODD, P, ws, None) == _lib.VSA_ERR_ALIGN
+    assert f(g, P, P, P, P, 0, 0.125, P, None, P, ws, None) == _lib.VSA_ERR_TOPK
+    assert f(g, P, P, P, P, 9, 0.125, P, None, P, ws, None) == _lib.VSA_ERR_TOPK
+    assert f(g, P, P, P, P, 2, float("nan"), P, None, P, ws, None) == _lib.VSA_ERR_SCALE
+    assert f(g, P, P, P, P, 2, 0.125, P, None, P, ws - 1, None) == _lib.VSA_ERR_WORKSPACE
+    assert f(geom(D=32), P, P, P, P, 2, 0.125, P, None, P, ws, None) == _lib.VSA_ERR_HEAD_DIM
