@@ -276,8 +276,8 @@ def main():
             print("--fp8 covers the fine stage without the linear branch", file=sys.stderr)
             sys.exit(2)
         # Q, K quantized per cube and V per channel in the step; the fp8 fine
-        # stage writes cube-major rows, unpermuted to raster at the end.
-        stages = ["quant", "select", "fine", "unpermute"]
+        # stage writes the raster-order output itself.
+        stages = ["quant", "select", "fine"]
         fp8_bufs = (torch.empty((B, H, d.rows, D), dtype=torch.uint8, device=dev),
                     torch.empty((B, H, d.n_cubes), dtype=torch.float32, device=dev),
                     torch.empty((B, H, d.rows, D), dtype=torch.uint8, device=dev),
@@ -302,10 +302,8 @@ def main():
         else:
             vsa.select_topk_pooled(qbar, kbar, wl.grid, wl.topk, out=idx, workspace=ws_sel)
         mark(2)
-        vsa.sparse_attn_fwd_fp8(q8, qs, k8, ks, v8t, vs, idx, wl.grid, wl.softmax_scale, out=oc)
+        vsa.sparse_attn_fwd_fp8(q8, qs, k8, ks, v8t, vs, idx, wl.grid, wl.softmax_scale, out=o, raster=True)
         mark(3)
-        vsa.cube_unpermute(oc, wl.grid, out=o)
-        mark(4)
 
     def step(ev=None):
         if args.fp8:
@@ -418,8 +416,8 @@ def main():
             "latent_grid": list(wl.grid), "padded_grid": list(wl.padded_grid),
             "tokens": wl.tokens, "n_cubes": wl.n_cubes, "topk": wl.topk,
             "sparsity": wl.sparsity, "linear_branch": wl.linear, "pattern": wl.pattern,
-            "layout": ("cube-major" if wl.linear or args.fp8 else
-                       ("raster q/k/o" if args.k_raster else "raster q/o")),
+            "layout": ("cube-major" if wl.linear else "raster q, k, v in; fp8 cube-major codes; raster o"
+                       if args.fp8 else ("raster q/k/o" if args.k_raster else "raster q/o")),
             **({"precision": "fp8 e4m3: Q, K per cube, V per channel; P e4m3"} if args.fp8 else {}),
             **({"window_cubes": list(wl.window)} if wl.window else {}),
             "computed_blocks": wl.blocks, "fine_flops": flops,

@@ -331,8 +331,10 @@ def quant_fp8(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, grid: Sequence[
 
 def sparse_attn_fwd_fp8(q8: torch.Tensor, qscale: torch.Tensor, k8: torch.Tensor, kscale: torch.Tensor,
                         v8t: torch.Tensor, vscale: torch.Tensor, idx: torch.Tensor, grid: Sequence[int],
-                        scale: Optional[float] = None, want_lse: bool = False, out: Optional[torch.Tensor] = None):
-    """fp8 fine stage.  Returns (oc bf16 [B, heads, Np, D] token-major, lse or None)."""
+                        scale: Optional[float] = None, want_lse: bool = False, out: Optional[torch.Tensor] = None,
+                        raster: bool = False):
+    """fp8 fine stage.  Returns (o bf16, lse or None): o is cube-major [B, heads, Np, D], or raster
+    [B, S, heads, D] with raster=True (padded query rows not written)."""
     B, Hh, Np, D = q8.shape
     g = make_geom(B, Hh, D, grid)
     d = geom_dims(g)
@@ -346,13 +348,16 @@ def sparse_attn_fwd_fp8(q8: torch.Tensor, qscale: torch.Tensor, k8: torch.Tensor
     _need(idx, "idx", torch.int32, (B, Hh, d.n_cubes, topk))
     if scale is None:
         scale = 1.0 / math.sqrt(D)
+    oshape = (B, d.tokens, Hh, D) if raster else (B, Hh, d.rows, D)
     if out is None:
-        out = torch.empty((B, Hh, d.rows, D), dtype=torch.bfloat16, device=q8.device)
-    _need(out, "oc", torch.bfloat16, (B, Hh, d.rows, D))
+        out = torch.empty(oshape, dtype=torch.bfloat16, device=q8.device)
+    _need(out, "o", torch.bfloat16, oshape)
     lse = torch.empty((B, Hh, d.rows), dtype=torch.float32, device=q8.device) if want_lse else None
+    layout = _lib.VSA_LAYOUT_RASTER if raster else _lib.VSA_LAYOUT_TOKEN_MAJOR
     _lib.check("vsa_sparse_attn_fwd_fp8", _lib.load().vsa_sparse_attn_fwd_fp8(
         g, q8.data_ptr(), qscale.data_ptr(), k8.data_ptr(), kscale.data_ptr(), v8t.data_ptr(), vscale.data_ptr(),
-        idx.data_ptr(), topk, float(scale), out.data_ptr(), lse.data_ptr() if lse is not None else None, _stream()))
+        idx.data_ptr(), topk, float(scale), layout, out.data_ptr(), lse.data_ptr() if lse is not None else None,
+        _stream()))
     return out, lse
 
 

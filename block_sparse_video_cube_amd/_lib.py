@@ -120,7 +120,7 @@ def load() -> ctypes.CDLL:
         "vsa_attn_bwd_workspace_bytes": (sz, [G, i32]),
         "vsa_quant_fp8_workspace_bytes": (sz, [G]),
         "vsa_quant_fp8": (i32, [G, P, P, P, P, P, P, P, P, P, P, P, P, sz, P]),
-        "vsa_sparse_attn_fwd_fp8": (i32, [G, P, P, P, P, P, P, P, i32, ctypes.c_float, P, P, P]),
+        "vsa_sparse_attn_fwd_fp8": (i32, [G, P, P, P, P, P, P, P, i32, ctypes.c_float, i32, P, P, P]),
         "vsa_sparse_attn_linear_fwd": (i32, [G, P, P, P, P, i32, ctypes.c_float, P, P, P, sz, P]),
         "vsa_sparse_attn_bwd": (i32, [G, P, P, P, P, P, P, P, P, P, P, i32, ctypes.c_float, P, P, P, P, sz, P]),
     }

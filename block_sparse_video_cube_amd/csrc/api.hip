@@ -217,12 +217,13 @@ int32_t vsa_quant_fp8(const vsa_geom* g, const uint16_t* q, const uint16_t* k, c
 
 int32_t vsa_sparse_attn_fwd_fp8(const vsa_geom* g, const uint8_t* q8, const float* qscale, const uint8_t* k8,
                                 const float* kscale, const uint8_t* v8t, const float* vscale, const int32_t* idx,
-                                int32_t topk, float softmax_scale, uint16_t* oc, float* lse, void* stream) {
+                                int32_t topk, float softmax_scale, int32_t o_layout, uint16_t* o, float* lse,
+                                void* stream) {
   vsa_dims d;
   vsa::KGeom k;
   int32_t st = prepare(g, &d, &k);
   if (st != VSA_OK) return st;
-  const void* ptrs[] = {q8, qscale, k8, kscale, v8t, vscale, idx, oc};
+  const void* ptrs[] = {q8, qscale, k8, kscale, v8t, vscale, idx, o};
   for (const void* p : ptrs)
     if (!p) return VSA_ERR_NULL;
   for (const void* p : ptrs)
@@ -230,8 +231,10 @@ int32_t vsa_sparse_attn_fwd_fp8(const vsa_geom* g, const uint8_t* q8, const floa
   if (lse && !aligned16(lse)) return VSA_ERR_ALIGN;
   if (topk < 1 || topk > d.n_cubes) return VSA_ERR_TOPK;
   if (!(softmax_scale > 0.f) || !isfinite(softmax_scale)) return VSA_ERR_SCALE;
+  if (o_layout != VSA_LAYOUT_TOKEN_MAJOR && o_layout != VSA_LAYOUT_RASTER) return VSA_ERR_LAYOUT;
   return launch_status(vsa::launch_attn_fwd_fp8(k, q8, qscale, k8, kscale, v8t, vscale, idx, topk, softmax_scale,
-                                                oc, lse, static_cast<hipStream_t>(stream)));
+                                                o_layout == VSA_LAYOUT_RASTER, o, lse,
+                                                static_cast<hipStream_t>(stream)));
 }
 
 int32_t vsa_cube_unpermute(const vsa_geom* g, const uint16_t* xc, uint16_t* x, void* stream) {

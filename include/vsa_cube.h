@@ -233,7 +233,10 @@ int32_t vsa_sparse_attn_fwd(const vsa_geom* g, const uint16_t* qc, const uint16_
  * codes with fp8 matrix products: logits scale * sq_i * sk_j * (q8 . k8),
  * fp32 online softmax, P rounded to E4M3 after scaling each row's weights so
  * that its largest lies in [2^4, 2^8], O = sv * (v8^T P) / sum(P) over the
- * rounded weights.  oc: bf16 [B, heads, Np, D] TOKEN_MAJOR; lse optional as
+ * rounded weights.  o: bf16 output, cube-major [B, heads, Np, D] when
+ * o_layout is VSA_LAYOUT_TOKEN_MAJOR, or raster [B, S, heads, D] when it is
+ * VSA_LAYOUT_RASTER (padded query rows are then not written); other values
+ * give VSA_ERR_LAYOUT.  lse: optional fp32 [B, heads, Np] (cube-major rows) as
  * there.  All pointers 16-byte aligned. */
 size_t vsa_quant_fp8_workspace_bytes(const vsa_geom* g);
 int32_t vsa_quant_fp8(const vsa_geom* g, const uint16_t* q, const uint16_t* k, const uint16_t* v, uint8_t* q8,
@@ -242,7 +245,8 @@ int32_t vsa_quant_fp8(const vsa_geom* g, const uint16_t* q, const uint16_t* k, c
 int32_t vsa_sparse_attn_fwd_fp8(const vsa_geom* g, const uint8_t* q8, const float* qscale,
                                 const uint8_t* k8, const float* kscale, const uint8_t* v8t,
                                 const float* vscale, const int32_t* idx, int32_t topk,
-                                float softmax_scale, uint16_t* oc, float* lse, void* stream);
+                                float softmax_scale, int32_t o_layout, uint16_t* o, float* lse,
+                                void* stream);
 
 /* Backward of the fine stage (the gradient of vsa_sparse_attn_fwd with respect
  * to Q, K and V; VSA and SLA are trained, FastVideo sparse-distillation

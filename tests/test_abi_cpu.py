@@ -219,15 +219,17 @@ def test_fp8_entry_point_validation(lib):
     assert lib.vsa_quant_fp8(g, *qa, None, P, ws - 1, None) == _lib.VSA_ERR_WORKSPACE
     assert lib.vsa_quant_fp8(geom(D=16), *qa, None, P, ws, None) == _lib.VSA_ERR_HEAD_DIM
     args = [P] * 7  # q8 qscale k8 kscale v8t vscale idx
-    assert lib.vsa_sparse_attn_fwd_fp8(g, *args, 2, 0.125, None, None, None) == _lib.VSA_ERR_NULL
-    assert lib.vsa_sparse_attn_fwd_fp8(g, *args[:6], None, 2, 0.125, P, None, None) == _lib.VSA_ERR_NULL
-    assert lib.vsa_sparse_attn_fwd_fp8(g, ODD, *args[1:], 2, 0.125, P, None, None) == _lib.VSA_ERR_ALIGN
-    assert lib.vsa_sparse_attn_fwd_fp8(g, *args, 2, 0.125, P, ODD, None) == _lib.VSA_ERR_ALIGN
-    assert lib.vsa_sparse_attn_fwd_fp8(g, *args, 0, 0.125, P, None, None) == _lib.VSA_ERR_TOPK
-    assert lib.vsa_sparse_attn_fwd_fp8(g, *args, 9, 0.125, P, None, None) == _lib.VSA_ERR_TOPK
-    assert lib.vsa_sparse_attn_fwd_fp8(g, *args, 2, float("inf"), P, None, None) == _lib.VSA_ERR_SCALE
-    assert lib.vsa_sparse_attn_fwd_fp8(geom(D=96), *args, 2, 0.125, P, None, None) == _lib.VSA_ERR_HEAD_DIM
-
+    f = lib.vsa_sparse_attn_fwd_fp8
+    TM = _lib.VSA_LAYOUT_TOKEN_MAJOR
+    assert f(g, *args, 2, 0.125, TM, None, None, None) == _lib.VSA_ERR_NULL
+    assert f(g, *args[:6], None, 2, 0.125, TM, P, None, None) == _lib.VSA_ERR_NULL
+    assert f(g, ODD, *args[1:], 2, 0.125, TM, P, None, None) == _lib.VSA_ERR_ALIGN
+    assert f(g, *args, 2, 0.125, TM, P, ODD, None) == _lib.VSA_ERR_ALIGN
+    assert f(g, *args, 0, 0.125, TM, P, None, None) == _lib.VSA_ERR_TOPK
+    assert f(g, *args, 9, 0.125, TM, P, None, None) == _lib.VSA_ERR_TOPK
+    assert f(g, *args, 2, float("inf"), TM, P, None, None) == _lib.VSA_ERR_SCALE
+    assert f(g, *args, 2, 0.125, _lib.VSA_LAYOUT_DIM_MAJOR, P, None, None) == _lib.VSA_ERR_LAYOUT
+    assert f(geom(D=96), *args, 2, 0.125, TM, P, None, None) == _lib.VSA_ERR_HEAD_DIM
 
 def test_fused_linear_entry_point_validation(lib):
     from block_sparse_video_cube_amd import _lib

@@ -87,6 +87,9 @@ def gpu_fp8(inp, grid, idx_np, scale, q_zero=False):
     q8, qs, k8, ks, v8t, vs, qm, km = vsa.quant_fp8(q, k, v, grid, want_means=True)
     idx = torch.from_numpy(np.ascontiguousarray(idx_np, dtype=np.int32)).to("cuda:0")
     oc, lse = vsa.sparse_attn_fwd_fp8(q8, qs, k8, ks, v8t, vs, idx, grid, scale, want_lse=True)
+    # The raster-order output is the same values at raster positions.
+    o_r, lse_r = vsa.sparse_attn_fwd_fp8(q8, qs, k8, ks, v8t, vs, idx, grid, scale, want_lse=True, raster=True)
+    assert torch.equal(o_r, vsa.cube_unpermute(oc, grid)) and torch.equal(lse_r, lse)
     # The means for the coarse stage come out of the same pass, bit-identical to the pooling kernel's.
     assert torch.equal(qm, vsa.cube_pool(q, grid)) and torch.equal(km, vsa.cube_pool(k, grid))
     torch.cuda.synchronize()
