@@ -74,21 +74,27 @@ def copy_calibration(nbytes: int) -> None:
     print(json.dumps({"copy_bytes": src.numel() * 2, "copies": 3}))
 
 
-def kernel_source_hash() -> str:
-    """sha256 (first 16 hex digits) of the fine-stage sources: the kernel and the headers it includes."""
+KERNEL_SOURCES = {
+    "attn_fwd": ("attn_fwd.hip", "attn_core.h", "tile_pipeline.h", "common.h"),
+    "attn_fwd_fp8": ("attn_fp8.hip", "tile_pipeline.h", "common.h"),
+}
+
+
+def kernel_source_hash(kernel: str = "attn_fwd") -> str:
+    """sha256 (first 16 hex digits) of a fine-stage kernel's sources: the kernel and the headers it includes."""
     h = hashlib.sha256()
-    for name in ("attn_fwd.hip", "tile_pipeline.h", "common.h"):
+    for name in KERNEL_SOURCES[kernel]:
         h.update(open(os.path.join(ROOT, "block_sparse_video_cube_amd", "csrc", name), "rb").read())
     return h.hexdigest()[:16]
 
 
-def measured_traffic(workload: str):
+def measured_traffic(workload: str, kernel: str = "attn_fwd"):
     """HBM bytes per fine-stage launch from committed rocprofv3 counters, if current."""
-    path = os.path.join(ROOT, "profiles", f"attn_fwd_{workload}_traffic.txt")
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_traffic.txt")
     if not os.path.exists(path):
         return None
     rec = json.load(open(path))
-    if rec.get("kernel_sha256_16") != kernel_source_hash():
+    if rec.get("kernel_sha256_16") != kernel_source_hash(kernel):
         return None  # the kernel changed since the counters were taken
     return rec.get("hbm_bytes_per_launch")
 
@@ -396,7 +402,7 @@ def main():
     if args.fp8:
         alg_bytes = B * H * d.rows * D * (1 + 1 + 1 + 2) + 4 * B * H * (2 * d.n_cubes + D)
         peak, kname = PEAK_FP8_TFLOPS, "attn_fwd_fp8"
-        traffic = None
+        traffic = measured_traffic(wl.name, "attn_fwd_fp8")
     res = {
         "metric": METRIC,
         "value": round(value, 3),
