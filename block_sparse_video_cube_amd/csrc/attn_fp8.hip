@@ -299,9 +299,10 @@ __global__ void __launch_bounds__(kThreads8, 2) attn_fwd_fp8(const uint8_t* __re
         f32x16 s_next[2];
         float mx_next;
         i32x8 p_cur;
+        // Past the last block the padding loads of K target a zero-size range: no memory traffic.
         step8<D, PARTIAL>(ka, sm.v[(u + 1) % 2], n, ones, qf, s_cur, s_next, mx_next, p_prev, p_cur, o, c_cur, mc, g, j_next, hf,
                           make_rsrc(vbase + 64LL * blk(nb) * D, 64 * D), sm.v[u % 2] + wq * NI8 * 1024, off.v,
-                          make_rsrc(kbase + 64LL * blk(nb + 3) * D, 64 * D), sm.k[u % 3] + wq * NI8 * 1024,
+                          (nb + 3 < topk ? make_rsrc(kbase + 64LL * blk(nb + 3) * D, 64 * D) : make_rsrc(kbase, 0)), sm.k[u % 3] + wq * NI8 * 1024,
                           off.k);
         mx_next *= c_next;
         move = __builtin_amdgcn_ballot_w64(mx_next > m_run + kLazy8) != 0;

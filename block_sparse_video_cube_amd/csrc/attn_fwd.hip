@@ -83,9 +83,9 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd(const uint16_t* __restri
   const uint16_t* vbase = vt + bh * g.Np * D;
   const int32_t* irow = idx + (bh * g.nc + i) * topk;
   const int q = 32 * wq + n;
-  // Past the last block the pipeline keeps issuing loads (of a valid tile,
-  // into a free buffer) so that the number of loads in flight is the same at
-  // every step.
+  // Past the last block the pipeline keeps issuing loads (into a free buffer;
+  // the K loads with a zero-size range, so they move no data) so that the
+  // number of loads in flight is the same at every step.
   const auto blk = [&](int m) { return irow[m < topk ? m : topk - 1]; };
 
   // Pipeline: K(m) lives in K buffer m % 3 and V(m) in V buffer m % 2.
@@ -179,7 +179,10 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd(const uint16_t* __restri
         f32x16 s_next;
         float mx_next;
         bf16x8 p_cur[2];
-        const __amdgpu_buffer_rsrc_t krs = k_tile_rsrc<D, PARTIAL, KRASTER>(kbase, g, blk(nb + 3), toff.k, roff, rrow, kto);
+        // Past the last block the padding loads target a zero-size range: no memory traffic.
+        const __amdgpu_buffer_rsrc_t krs = (nb + 3 < topk)
+            ? k_tile_rsrc<D, PARTIAL, KRASTER>(kbase, g, blk(nb + 3), toff.k, roff, rrow, kto)
+            : make_rsrc(kbase, 0);
         step<D, PARTIAL>(ka, va, qf, s_cur, s_next, mx_next, p_prev, p_cur, o, l_run, mc, scale_log2, g,
                          blk(nb + 1), wk, hf, make_rsrc(vbase + 64LL * blk(nb) * D, 64 * D * 2),
                          sm.v[u % 2] + w * NI * 8 * 64, toff.v, krs, sm.k[u % 3] + w * NI * KRPI * D, kto);
