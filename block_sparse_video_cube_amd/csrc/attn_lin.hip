@@ -47,8 +47,8 @@ struct SmemL {
 
 // One pipelined step n of a linear wavefront, mirroring step():
 // S'^T(n+1) = phiK(n+1) phiQ^T on the matrix cores, P'(n) = bf16(S'^T(n)) and
-// its row sum, C^T += V(n-1)^T P'(n-1)^T; the loads of phiK(n+3) go out one
-// per product slot.
+// its row sum, C^T -= V(n-1)^T P'(n-1)^T (the weights enter negated, exactly);
+// the loads of phiK(n+3) go out one per product slot.
 template <int D>
 __device__ __forceinline__ void lin_step(const bf16x8 (&fa)[D / 16], const bf16x8 (&va)[D / 32][2],
                                          const bf16x8 (&fq)[D / 16], const f32x16& s_cur, f32x16& s_next,
@@ -69,7 +69,7 @@ __device__ __forceinline__ void lin_step(const bf16x8 (&fa)[D / 16], const bf16x
   for (int r = 0; r < 8; ++r) {
     const bf16x2 pk = __builtin_convertvector((f32x2){s_cur[2 * r], s_cur[2 * r + 1]}, bf16x2);
     dcorr = __builtin_amdgcn_fdot2_f32_bf16(pk, ones, dcorr, false);
-    pw[r] = __builtin_bit_cast(uint32_t, pk);
+    pw[r] = __builtin_bit_cast(uint32_t, pk) ^ 0x80008000u;  // -P' (exact in bf16): C^T collects phi(Q) S_tot - sum
   }
   p_cur[0] = __builtin_bit_cast(bf16x8, make_uint4(pw[0], pw[1], pw[2], pw[3]));
   p_cur[1] = __builtin_bit_cast(bf16x8, make_uint4(pw[4], pw[5], pw[6], pw[7]));
@@ -271,9 +271,22 @@ __global__ void __launch_bounds__(kLinThreads, 2) attn_lin_fwd(
     }
     issue_k_tile<D>(make_rsrc(fbase + 64LL * blk(1) * D, 64 * D * 2), sm.f[1], w4, toff.k);
     issue_k_tile<D>(make_rsrc(fbase + 64LL * blk(2) * D, 64 * D * 2), sm.f[2], w4, toff.k);
+    // c starts as this key half's share of phi(Q) S_tot (the hi or the lo
+    // half), while the first tiles arrive; the steps subtract the selected part.
     f32x16 c[DT];
+    {
+      const uint16_t* st = (wk == 0 ? lt.st_hi : lt.st_lo) + bh * D * D;
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) c[dt] = f32x16{};
+      for (int dt = 0; dt < DT; ++dt) {
+        c[dt] = f32x16{};
+        const int e = 32 * dt + n;
+#pragma unroll
+        for (int dc = 0; dc < DC; ++dc) {
+          const bf16x8 a = *reinterpret_cast<const bf16x8*>(st + e * D + 16 * dc + 8 * hf);
+          c[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, fq[dc], c[dt], 0, 0, 0);
+        }
+      }
+    }
     float dcorr = 0.f;
     bf16x8 p_prev[2] = {};
     f32x16 s_cur;
@@ -318,19 +331,6 @@ __global__ void __launch_bounds__(kLinThreads, 2) attn_lin_fwd(
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk)
           c[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[dt][kk], p_prev[kk], c[dt], 0, 0, 0);
-    }
-    // c = (this key half's share of phi(Q) S_tot: the hi or the lo half) - (its selected part).
-    const uint16_t* st = (wk == 0 ? lt.st_hi : lt.st_lo) + bh * D * D;
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
-      c[dt] = -c[dt];
-      const int e = 32 * dt + n;
-#pragma unroll
-      for (int dc = 0; dc < DC; ++dc) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(st + e * D + 16 * dc + 8 * hf);
-        c[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, fq[dc], c[dt], 0, 0, 0);
-      }
-      __builtin_amdgcn_sched_barrier(0);  // one e-tile of loads in flight at a time
     }
     dcorr += __shfl_xor(dcorr, 32);
     wait_vmcnt<0>();

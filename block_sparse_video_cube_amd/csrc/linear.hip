@@ -238,10 +238,25 @@ __global__ void __launch_bounds__(kThreads, 2) lin_apply(const uint16_t* __restr
     }
   }
 
-  // Selected part, block by block (double-buffered tiles).
+  // c starts as this key half's share of phi(Q) S_tot (the hi or the lo
+  // half), computed while the first tiles arrive; the loop below subtracts
+  // the selected part by feeding the products exactly negated weights.
   f32x16 c[DT];
+  {
+    const uint16_t* st = (wk == 0 ? ws.st_hi : ws.st_lo) + bh * D * D;
 #pragma unroll
-  for (int dt = 0; dt < DT; ++dt) c[dt] = f32x16{};
+    for (int dt = 0; dt < DT; ++dt) {
+      c[dt] = f32x16{};
+      const int e = 32 * dt + n;
+#pragma unroll
+      for (int dc = 0; dc < DC; ++dc) {
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(st + e * D + 16 * dc + 8 * hf);
+        c[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, fq[dc], c[dt], 0, 0, 0);
+      }
+    }
+  }
+
+  // Selected part, block by block (double-buffered tiles).
   float dcorr = 0.f;
   const int prow = pi_row(n);
   const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
@@ -269,7 +284,7 @@ __global__ void __launch_bounds__(kThreads, 2) lin_apply(const uint16_t* __restr
         for (int r = 0; r < 8; ++r) {
           const bf16x2 pk = __builtin_convertvector((f32x2){sa[2 * r], sa[2 * r + 1]}, bf16x2);
           dcorr = __builtin_amdgcn_fdot2_f32_bf16(pk, ones, dcorr, false);
-          pw[r] = __builtin_bit_cast(uint32_t, pk);
+          pw[r] = __builtin_bit_cast(uint32_t, pk) ^ 0x80008000u;  // -P' (exact in bf16)
         }
         bf16x8 pb[2];
         pb[0] = __builtin_bit_cast(bf16x8, make_uint4(pw[0], pw[1], pw[2], pw[3]));
@@ -281,21 +296,6 @@ __global__ void __launch_bounds__(kThreads, 2) lin_apply(const uint16_t* __restr
             c[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[dt][kk], pb[kk], c[dt], 0, 0, 0);
       }
     }
-  }
-
-  // c = (this half of phi(Q) S_tot) - (this half's correction).
-  const uint16_t* st = (wk == 0 ? ws.st_hi : ws.st_lo) + bh * D * D;
-#pragma unroll
-  for (int dt = 0; dt < DT; ++dt) {
-    c[dt] = -c[dt];
-    const int e = 32 * dt + n;
-#pragma unroll
-    for (int dc = 0; dc < DC; ++dc) {
-      const bf16x8 a = *reinterpret_cast<const bf16x8*>(st + e * D + 16 * dc + 8 * hf);
-      c[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, fq[dc], c[dt], 0, 0, 0);
-    }
-    // Keep the loads of one e-tile at a time in flight (register budget).
-    __builtin_amdgcn_sched_barrier(0);
   }
 
   // Merge the two key halves through LDS.
