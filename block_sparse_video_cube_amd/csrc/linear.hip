@@ -171,10 +171,10 @@ __global__ void __launch_bounds__(256) lin_reduce(LinWs ws, KGeom g) {
   }
 }
 
-// Two phi(K) and two V^T tile buffers (64 KB at D = 128).
+// Three phi(K) and two V^T tile buffers (80 KB at D = 128).
 template <int D>
 struct LinSmem {
-  uint16_t f[2][64 * D];
+  uint16_t f[3][64 * D];
   uint16_t v[2][D * 64];
 };
 
@@ -209,11 +209,13 @@ __global__ void __launch_bounds__(kThreads, 2) lin_apply(const uint16_t* __restr
   const uint16_t* fkb = ws.fk + bh * g.Np * D;
   const uint16_t* vb = vt + bh * g.Np * D;
   const TileOffsets<D> toff(w, lane);
-  if (!empty_u) {
-    const int j0 = irow[0];
-    load_k_tile<D>(fkb + 64LL * j0 * D, sm.f[0], w, toff);
-    load_v_tile<D>(vb + 64LL * j0 * D, sm.v[0], w, toff);
-  }
+  // phiK(0), V(0) and phiK(1); past the end of the list (or with no
+  // unselected cube) a zero-size range, so every step issues the same loads.
+  constexpr unsigned kTile = 64 * D * 2;
+  issue_k_tile<D>(make_rsrc(fkb + 64LL * irow[0] * D, empty_u ? 0 : kTile), sm.f[0], w, toff.k);
+  issue_v_tile<D>(make_rsrc(vb + 64LL * irow[0] * D, empty_u ? 0 : kTile), sm.v[0], w, toff.v);
+  issue_k_tile<D>(make_rsrc(fkb + 64LL * irow[topk > 1 ? 1 : 0] * D, (empty_u || topk < 2) ? 0 : kTile), sm.f[1], w,
+                  toff.k);
 
   // phi(Q) fragments (bf16) and this lane's part of phi(Q) . z_tot.
   bf16x8 fq[DC];
@@ -256,26 +258,28 @@ __global__ void __launch_bounds__(kThreads, 2) lin_apply(const uint16_t* __restr
     }
   }
 
-  // Selected part, block by block (double-buffered tiles).
+  // Selected part, block by block.
   float dcorr = 0.f;
   const int prow = pi_row(n);
   const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
-  for (int jb = 0; jb < (empty_u ? 0 : topk); jb += 2) {
+  // phiK runs two blocks ahead (three buffers), V one (two buffers); steps
+  // come in groups of six so that every buffer index is compile-time.
+  for (int jb = 0; jb < (empty_u ? 0 : topk); jb += 6) {
 #pragma unroll
-    for (int par = 0; par < 2; ++par) {
-      const int nb = jb + par;
+    for (int u = 0; u < 6; ++u) {
+      const int nb = jb + u;
       if (nb < topk) {
-        wait_vmcnt<0>();
+        // Outstanding, oldest first: phiK(nb), V(nb), phiK(nb+1).
+        wait_vmcnt<TileOffsets<D>::NI>();
         pipeline_barrier();
-        if (nb + 1 < topk) {
-          const int jn = irow[nb + 1];
-          load_k_tile<D>(fkb + 64LL * jn * D, sm.f[1 - par], w, toff);
-          load_v_tile<D>(vb + 64LL * jn * D, sm.v[1 - par], w, toff);
-        }
+        issue_v_tile<D>(make_rsrc(vb + 64LL * irow[nb + 1 < topk ? nb + 1 : nb] * D, nb + 1 < topk ? kTile : 0),
+                        sm.v[(u + 1) % 2], w, toff.v);
+        issue_k_tile<D>(make_rsrc(fkb + 64LL * irow[nb + 2 < topk ? nb + 2 : nb] * D, nb + 2 < topk ? kTile : 0),
+                        sm.f[(u + 2) % 3], w, toff.k);
         bf16x8 ka[DC];
         bf16x8 va[DT][2];
-        read_k<D>(sm.f[par], wk, hf, prow, ka);
-        read_v<D>(sm.v[par], wk, hf, n, va);
+        read_k<D>(sm.f[u % 3], wk, hf, prow, ka);
+        read_v<D>(sm.v[u % 2], wk, hf, n, va);
         f32x16 sa = f32x16{};
 #pragma unroll
         for (int dc = 0; dc < DC; ++dc) sa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[dc], fq[dc], sa, 0, 0, 0);
@@ -300,7 +304,8 @@ __global__ void __launch_bounds__(kThreads, 2) lin_apply(const uint16_t* __restr
 
   // Merge the two key halves through LDS.
   dcorr += __shfl_xor(dcorr, 32);
-  __syncthreads();  // every tile read has completed; reuse the phi(K) buffers
+  wait_vmcnt<0>();  // the last steps' zero-size loads land in f[] and v[] too
+  __syncthreads();  // every tile read has completed; reuse the tile buffers
   float* xo = reinterpret_cast<float*>(&sm.f[0][0]) + wq * (DT * 16 * 64);
   float* xd = reinterpret_cast<float*>(&sm.v[0][0]) + wq * 64;
   if (wk == 1) {
