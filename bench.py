@@ -155,9 +155,9 @@ def cpu_baseline(wl, budget_s: float):
 def time_backward(vsa, wl, q, k, v, o, qc, kc, vt, idx, args, dev):
     """Backward of the fine stage on the layer's last forward state.
 
-    One backward step: the layouts it reads (Q and K cube-major both ways, V
-    token-major, dO both ways), the forward's O and lse (one fine-stage call),
-    then vsa_sparse_attn_bwd and the three unpermutes to raster gradients.
+    One backward step: the layouts it reads (Q, K, V and dO cube-major,
+    token-major), the forward's O and lse (one fine-stage call), then
+    vsa_sparse_attn_bwd and the three unpermutes to raster gradients.
     Flops are counted as 2.5x the forward's (five 64x64xD products per block:
     the usual accounting; the kernels recompute S and dP in both passes).
     """
@@ -176,18 +176,15 @@ def time_backward(vsa, wl, q, k, v, o, qc, kc, vt, idx, args, dev):
         # The raster forward keeps no cube-major Q, K: the backward makes every layout it reads.
         vsa.cube_permute(q, wl.grid, out=qc)
         vsa.cube_permute(k, wl.grid, out=kc)
-        return (vsa.cube_permute(q, wl.grid, layout="dim"), vsa.cube_permute(k, wl.grid, layout="dim"),
-                vsa.cube_permute(v, wl.grid), vsa.cube_permute(do, wl.grid),
-                vsa.cube_permute(do, wl.grid, layout="dim"))
+        return vsa.cube_permute(v, wl.grid), vsa.cube_permute(do, wl.grid)
 
     def step(ev=None):
         if ev is not None:
             ev[0].record()
-        qt, kt, vc, doc, dot = layouts()
+        vc, doc = layouts()
         if ev is not None:
             ev[1].record()
-        dq, dk, dv = vsa.sparse_attn_bwd(qc, qt, kc, kt, vc, oc, doc, dot, lse, idx, wl.grid, wl.softmax_scale,
-                                         workspace=ws)
+        dq, dk, dv = vsa.sparse_attn_bwd(qc, kc, vc, oc, doc, lse, idx, wl.grid, wl.softmax_scale, workspace=ws)
         if ev is not None:
             ev[2].record()
         outs = [vsa.cube_unpermute(x, wl.grid) for x in (dq, dk, dv)]

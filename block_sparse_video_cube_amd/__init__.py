@@ -361,13 +361,13 @@ def sparse_attn_fwd_fp8(q8: torch.Tensor, qscale: torch.Tensor, k8: torch.Tensor
     return out, lse
 
 
-def sparse_attn_bwd(qc: torch.Tensor, qt: torch.Tensor, kc: torch.Tensor, kt: torch.Tensor, vc: torch.Tensor,
-                    oc: torch.Tensor, doc: torch.Tensor, dot: torch.Tensor, lse: torch.Tensor, idx: torch.Tensor,
-                    grid: Sequence[int], scale: Optional[float] = None, workspace: Optional[torch.Tensor] = None):
+def sparse_attn_bwd(qc: torch.Tensor, kc: torch.Tensor, vc: torch.Tensor, oc: torch.Tensor, doc: torch.Tensor,
+                    lse: torch.Tensor, idx: torch.Tensor, grid: Sequence[int], scale: Optional[float] = None,
+                    workspace: Optional[torch.Tensor] = None):
     """Backward of the fine stage.  Returns (dq, dk, dv), bf16 [B, heads, Np, D] token-major.
 
-    qt, kt, dot: the DIM_MAJOR layouts (cube_permute(..., layout="dim")) of Q, K and dO;
-    vc: V token-major; oc, lse: outputs of sparse_attn_fwd (want_lse=True); idx: its block lists.
+    qc, kc, vc, doc: Q, K, V and dO token-major (cube_permute); oc, lse: outputs of
+    sparse_attn_fwd (want_lse=True); idx: its block lists.
     """
     B, Hh, Np, D = qc.shape
     g = make_geom(B, Hh, D, grid)
@@ -375,8 +375,6 @@ def sparse_attn_bwd(qc: torch.Tensor, qt: torch.Tensor, kc: torch.Tensor, kt: to
     topk = int(idx.shape[-1])
     for t, name in ((qc, "qc"), (kc, "kc"), (vc, "vc"), (oc, "oc"), (doc, "doc")):
         _need(t, name, torch.bfloat16, (B, Hh, d.rows, D))
-    for t, name in ((qt, "qt"), (kt, "kt"), (dot, "dot")):
-        _need(t, name, torch.bfloat16, (B, Hh, d.n_cubes, D, 64))
     _need(lse, "lse", torch.float32, (B, Hh, d.rows))
     _need(idx, "idx", torch.int32, (B, Hh, d.n_cubes, topk))
     if scale is None:
@@ -387,8 +385,8 @@ def sparse_attn_bwd(qc: torch.Tensor, qt: torch.Tensor, kc: torch.Tensor, kt: to
         workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=qc.device)
     dq, dk, dv = (torch.empty_like(qc) for _ in range(3))
     _lib.check("vsa_sparse_attn_bwd", lib.vsa_sparse_attn_bwd(
-        g, qc.data_ptr(), qt.data_ptr(), kc.data_ptr(), kt.data_ptr(), vc.data_ptr(), oc.data_ptr(),
-        doc.data_ptr(), dot.data_ptr(), lse.data_ptr(), idx.data_ptr(), topk, float(scale), dq.data_ptr(),
+        g, qc.data_ptr(), kc.data_ptr(), vc.data_ptr(), oc.data_ptr(), doc.data_ptr(), lse.data_ptr(),
+        idx.data_ptr(), topk, float(scale), dq.data_ptr(),
         dk.data_ptr(), dv.data_ptr(), workspace.data_ptr(), workspace.numel() * workspace.element_size(),
         _stream()))
     return dq, dk, dv

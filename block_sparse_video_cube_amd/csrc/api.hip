@@ -168,17 +168,16 @@ size_t vsa_attn_bwd_workspace_bytes(const vsa_geom* g, int32_t topk) {
   return vsa::attn_bwd_workspace_bytes(k, topk);
 }
 
-int32_t vsa_sparse_attn_bwd(const vsa_geom* g, const uint16_t* qc, const uint16_t* qt, const uint16_t* kc,
-                            const uint16_t* kt, const uint16_t* vc, const uint16_t* oc, const uint16_t* doc,
-                            const uint16_t* dot, const float* lse, const int32_t* idx, int32_t topk,
-                            float softmax_scale, uint16_t* dq, uint16_t* dk, uint16_t* dv, void* ws,
+int32_t vsa_sparse_attn_bwd(const vsa_geom* g, const uint16_t* qc, const uint16_t* kc, const uint16_t* vc,
+                            const uint16_t* oc, const uint16_t* doc, const float* lse, const int32_t* idx,
+                            int32_t topk, float softmax_scale, uint16_t* dq, uint16_t* dk, uint16_t* dv, void* ws,
                             size_t ws_bytes, void* stream) {
   vsa_dims d;
   vsa::KGeom k;
   int32_t st = prepare(g, &d, &k);
   if (st != VSA_OK) return st;
   if (d.n_cubes > VSA_MAX_CUBES) return VSA_ERR_GEOMETRY;
-  const void* ptrs[] = {qc, qt, kc, kt, vc, oc, doc, dot, lse, idx, dq, dk, dv, ws};
+  const void* ptrs[] = {qc, kc, vc, oc, doc, lse, idx, dq, dk, dv, ws};
   for (const void* p : ptrs)
     if (!p) return VSA_ERR_NULL;
   for (const void* p : ptrs)
@@ -186,8 +185,8 @@ int32_t vsa_sparse_attn_bwd(const vsa_geom* g, const uint16_t* qc, const uint16_
   if (topk < 1 || topk > d.n_cubes) return VSA_ERR_TOPK;
   if (!(softmax_scale > 0.f) || !isfinite(softmax_scale)) return VSA_ERR_SCALE;
   if (ws_bytes < vsa::attn_bwd_workspace_bytes(k, topk)) return VSA_ERR_WORKSPACE;
-  return launch_status(vsa::launch_attn_bwd(k, qc, qt, kc, kt, vc, oc, doc, dot, lse, idx, topk, softmax_scale, dq, dk,
-                                            dv, ws, static_cast<hipStream_t>(stream)));
+  return launch_status(vsa::launch_attn_bwd(k, qc, kc, vc, oc, doc, lse, idx, topk, softmax_scale, dq, dk, dv, ws,
+                                            static_cast<hipStream_t>(stream)));
 }
 
 size_t vsa_quant_fp8_workspace_bytes(const vsa_geom* g) {

@@ -141,27 +141,29 @@ __global__ void __launch_bounds__(256) bwd_fill(const int32_t* __restrict__ idx,
   }
 }
 
+// 64 consecutive floats (one cube's rows of lse or delta) into LDS: one
+// dword per lane of the calling wavefront.
+__device__ __forceinline__ void issue_row_f32(const float* src, float* dst, int lane) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(make_rsrc(src, 256), (lds_ptr_t)dst, 4, lane * 4, 0, 0, 0);
+}
+
 // --------------------------------------------------------------------- dQ --
 
 template <int D>
 struct DqSmem {
-  uint16_t k[2][64 * D];   // K_j token-major
-  uint16_t v[2][64 * D];   // V_j token-major
-  uint16_t kt[2][D * 64];  // K_j^T (cube stored transposed)
+  uint16_t k[2][64 * D];  // K_j token-major (kt_swz: also read transposed)
+  uint16_t v[2][64 * D];  // V_j token-major
 };
 
 template <int D>
-__device__ __forceinline__ void dq_issue(const uint16_t* kc, const uint16_t* vc, const uint16_t* kt, long long off,
-                                         uint16_t* ks, uint16_t* vs, uint16_t* kts, int w, const uint32_t* ko,
-                                         const uint32_t* vo) {
-  issue_k_tile<D>(make_rsrc(kc + off, 64 * D * 2), ks, w, ko);
+__device__ __forceinline__ void dq_issue(const uint16_t* kc, const uint16_t* vc, long long off, uint16_t* ks,
+                                         uint16_t* vs, int w, const uint32_t* kto, const uint32_t* ko) {
+  issue_k_tile<D>(make_rsrc(kc + off, 64 * D * 2), ks, w, kto);
   issue_k_tile<D>(make_rsrc(vc + off, 64 * D * 2), vs, w, ko);
-  issue_v_tile<D>(make_rsrc(kt + off, 64 * D * 2), kts, w, vo);
 }
 
 template <int D, bool PARTIAL>
-__global__ void __launch_bounds__(kThreads, 1) bwd_dq(const uint16_t* __restrict__ qc, const uint16_t* __restrict__ kc,
-                                                      const uint16_t* __restrict__ kt,
+__global__ void __launch_bounds__(kThreads, 2) bwd_dq(const uint16_t* __restrict__ qc, const uint16_t* __restrict__ kc,
                                                       const uint16_t* __restrict__ vc,
                                                       const uint16_t* __restrict__ doc,
                                                       const float* __restrict__ lse, const float* __restrict__ delta,
@@ -181,9 +183,9 @@ __global__ void __launch_bounds__(kThreads, 1) bwd_dq(const uint16_t* __restrict
   const int32_t* irow = idx + (bh * g.nc + i) * topk;
   const long long row = bh * g.Np + 64LL * i + 32 * wq + n;
   const TileOffsets<D> toff(w, lane);
+  const TileOffsets<D, true> ttoff(w, lane);
 
-  dq_issue<D>(kc + hbase, vc + hbase, kt + hbase, 64LL * irow[0] * D, sm.k[0], sm.v[0], sm.kt[0], w, toff.k,
-              toff.v);
+  dq_issue<D>(kc + hbase, vc + hbase, 64LL * irow[0] * D, sm.k[0], sm.v[0], w, ttoff.k, toff.k);
   bf16x8 qf[DC], df[DC];
 #pragma unroll
   for (int dc = 0; dc < DC; ++dc) {
@@ -204,10 +206,10 @@ __global__ void __launch_bounds__(kThreads, 1) bwd_dq(const uint16_t* __restrict
         wait_vmcnt<0>();
         pipeline_barrier();
         if (nb + 1 < topk)
-          dq_issue<D>(kc + hbase, vc + hbase, kt + hbase, 64LL * irow[nb + 1] * D, sm.k[u ^ 1], sm.v[u ^ 1],
-                      sm.kt[u ^ 1], w, toff.k, toff.v);
+          dq_issue<D>(kc + hbase, vc + hbase, 64LL * irow[nb + 1] * D, sm.k[u ^ 1], sm.v[u ^ 1], w, ttoff.k,
+                      toff.k);
         bf16x8 ka[DC], va[DC];
-        read_k<D>(sm.k[u], wk, hf, prow, ka);
+        read_k<D, true>(sm.k[u], wk, hf, prow, ka);
         read_k<D>(sm.v[u], wk, hf, prow, va);
         f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
@@ -227,7 +229,7 @@ __global__ void __launch_bounds__(kThreads, 1) bwd_dq(const uint16_t* __restrict
         const bf16x8 sb[2] = {__builtin_bit_cast(bf16x8, make_uint4(sw[0], sw[1], sw[2], sw[3])),
                               __builtin_bit_cast(bf16x8, make_uint4(sw[4], sw[5], sw[6], sw[7]))};
         bf16x8 ta[DT][2];
-        read_v<D>(sm.kt[u], wk, hf, n, ta);
+        read_tr<D>(sm.k[u], wk, lane, ta);
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
@@ -265,73 +267,72 @@ __global__ void __launch_bounds__(kThreads, 1) bwd_dq(const uint16_t* __restrict
 }
 
 // ------------------------------------------------------------------ dK dV --
+//
+// One workgroup of 8 wavefronts per key cube j.  Wavefronts 0-3 and 4-7
+// split the work of each (key, query) quadrant (wk, wq), 32 keys x 32 queries,
+// by product, so that each SIMD holds one of each kind and the two overlap:
+//  * P wavefronts (0-3): S = Q K^T, P = exp(scale S - lse), dV^T += dO^T P;
+//    they hand P (fp32) to their partner through LDS;
+//  * dS wavefronts (4-7), one step behind: dP = dO V^T,
+//    dS = P * (dP - delta), dK^T += Q^T dS.
+// Q and dO tiles therefore live for two steps: a ring of three.  A lane owns
+// a key column (S = Q K^T with Q rows in pi order, so the accumulator is the
+// B operand of the next product); K (P wavefronts) or V (dS wavefronts) stays
+// in registers.
 
 template <int D>
 struct DkvSmem {
-  uint16_t q[2][64 * D];    // Q_i token-major
-  uint16_t dout[2][64 * D]; // dO_i token-major
-  uint16_t qt[2][D * 64];   // Q_i^T
-  uint16_t dot[2][D * 64];  // dO_i^T
-  float ls[2][64];          // lse_i
-  float dl[2][64];          // delta_i
+  uint16_t q[3][64 * D];     // Q_i token-major (kt_swz: also read transposed)
+  uint16_t dout[3][64 * D];  // dO_i token-major (kt_swz)
+  float ls[3][64];           // lse_i
+  float dl[3][64];           // delta_i
+  f32x4 p[2][4][4][64];      // P of one step: [slot][quadrant][register / 4][lane]
 };
 
-template <int D>
-__device__ __forceinline__ void dkdv_issue(const uint16_t* qc, const uint16_t* doc, const uint16_t* qt,
-                                           const uint16_t* dot, const float* lse, const float* delta, long long off,
-                                           long long roff, uint16_t* qs, uint16_t* ds, uint16_t* qts, uint16_t* dts,
-                                           float* lss, float* dls, int w, const uint32_t* ko, const uint32_t* vo,
-                                           int lane) {
-  issue_k_tile<D>(make_rsrc(qc + off, 64 * D * 2), qs, w, ko);
-  issue_k_tile<D>(make_rsrc(doc + off, 64 * D * 2), ds, w, ko);
-  issue_v_tile<D>(make_rsrc(qt + off, 64 * D * 2), qts, w, vo);
-  issue_v_tile<D>(make_rsrc(dot + off, 64 * D * 2), dts, w, vo);
-  // 64 floats each, one dword per lane of wavefronts 0 and 1.
-  if (w == 0)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(make_rsrc(lse + roff, 256), (lds_ptr_t)lss, 4, lane * 4, 0, 0, 0);
-  else if (w == 1)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(make_rsrc(delta + roff, 256), (lds_ptr_t)dls, 4, lane * 4, 0, 0, 0);
-}
-
 template <int D, bool PARTIAL>
-__global__ void __launch_bounds__(kThreads, 1) bwd_dkdv(const uint16_t* __restrict__ qc,
-                                                        const uint16_t* __restrict__ qt,
-                                                        const uint16_t* __restrict__ kc,
-                                                        const uint16_t* __restrict__ vc,
-                                                        const uint16_t* __restrict__ doc,
-                                                        const uint16_t* __restrict__ dot,
-                                                        const float* __restrict__ lse,
-                                                        const float* __restrict__ delta,
-                                                        const int32_t* __restrict__ qoff,
-                                                        const int32_t* __restrict__ qcnt,
-                                                        const int32_t* __restrict__ qlist, int topk, float scale,
-                                                        float scale_log2, uint16_t* __restrict__ dk,
-                                                        uint16_t* __restrict__ dv, KGeom g, Placement pl) {
+__global__ void __launch_bounds__(2 * kThreads, 1) bwd_dkdv(const uint16_t* __restrict__ qc,
+                                                            const uint16_t* __restrict__ kc,
+                                                            const uint16_t* __restrict__ vc,
+                                                            const uint16_t* __restrict__ doc,
+                                                            const float* __restrict__ lse,
+                                                            const float* __restrict__ delta,
+                                                            const int32_t* __restrict__ qoff,
+                                                            const int32_t* __restrict__ qcnt,
+                                                            const int32_t* __restrict__ qlist, int topk, float scale,
+                                                            float scale_log2, uint16_t* __restrict__ dk,
+                                                            uint16_t* __restrict__ dv, KGeom g, Placement pl) {
   constexpr int DC = D / 16, DT = D / 32;
   __shared__ __attribute__((aligned(16))) DkvSmem<D> sm;
   int j, h, b;
-  if (!map_workgroup(g, pl, j, h, b)) return;
+  if (!map_workgroup(g, pl, j, h, b)) return;  // whole workgroup leaves before any barrier
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wk = w & 1, wq = w >> 1;
+  const bool ds_wave = w >= 4;  // false: P wavefront
+  const int quad = w & 3, wk = quad & 1, wq = quad >> 1;
   const int hf = lane >> 5, n = lane & 31;
   const int key = 32 * wk + n;
   const long long bh = (long long)b * g.H + h;
   const long long hbase = bh * g.Np * D, rbase = bh * g.Np;
   const long long krow = rbase + 64LL * j + key;
-  const TileOffsets<D> toff(w, lane);
+  const TileOffsets<D, true> toff(quad, lane);
   const int cnt = qcnt[bh * g.nc + j];
   const int32_t* list = qlist + bh * (long long)g.nc * topk + qoff[bh * g.nc + j];
+  // P wavefronts load the Q tiles and lse, dS wavefronts the dO tiles and delta.
+  const uint16_t* src = (ds_wave ? doc : qc) + hbase;
+  const float* rsrc_f = ds_wave ? delta : lse;
+  auto issue = [&](int m, uint16_t* qs, uint16_t* ds, float* lss, float* dls) {
+    const int i = list[m];
+    issue_k_tile<D>(make_rsrc(src + 64LL * i * D, 64 * D * 2), ds_wave ? ds : qs, quad, toff.k);
+    if (quad == 0) issue_row_f32(rsrc_f + rbase + 64LL * i, ds_wave ? dls : lss, lane);
+  };
+  if (cnt > 0) issue(0, sm.q[0], sm.dout[0], sm.ls[0], sm.dl[0]);
 
-  if (cnt > 0)
-    dkdv_issue<D>(qc + hbase, doc + hbase, qt + hbase, dot + hbase, lse, delta, 64LL * list[0] * D,
-                  rbase + 64LL * list[0], sm.q[0], sm.dout[0], sm.qt[0], sm.dot[0], sm.ls[0], sm.dl[0], w, toff.k,
-                  toff.v, lane);
-  bf16x8 kb[DC], vb[DC];
+  // This wavefront's 32 keys of K (P) or V (dS), B operand fragments.
+  bf16x8 kv[DC];
+  {
+    const uint16_t* kvrow = (ds_wave ? vc : kc) + krow * D;
 #pragma unroll
-  for (int dc = 0; dc < DC; ++dc) {
-    kb[dc] = *reinterpret_cast<const bf16x8*>(kc + krow * D + 16 * dc + 8 * hf);
-    vb[dc] = *reinterpret_cast<const bf16x8*>(vc + krow * D + 16 * dc + 8 * hf);
+    for (int dc = 0; dc < DC; ++dc) kv[dc] = *reinterpret_cast<const bf16x8*>(kvrow + 16 * dc + 8 * hf);
   }
   float kmask = 1.f;
   if (PARTIAL) {
@@ -340,108 +341,117 @@ __global__ void __launch_bounds__(kThreads, 1) bwd_dkdv(const uint16_t* __restri
     kmask = local_valid(g, ct, cy, cx, key) ? 1.f : 0.f;
   }
   const int prow = pi_row(n);
-  f32x16 ka[DT], va[DT];
+  // Register r of a 32 x 32 accumulator holds query 32 wq + 16 (r/8) + 8 hf + r%8.
+  const int q0 = 32 * wq + 8 * hf;
+  f32x16 acc[DT];  // dV^T (P wavefronts) or dK^T (dS wavefronts)
 #pragma unroll
-  for (int dt = 0; dt < DT; ++dt) ka[dt] = va[dt] = f32x16{};
+  for (int dt = 0; dt < DT; ++dt) acc[dt] = f32x16{};
 
-  for (int mb = 0; mb < cnt; mb += 2) {
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int m = mb + u;
+  // Step m: P wavefronts take query cube m, dS wavefronts query cube m - 1.
+  // Ring slots: Q/dO/lse/delta of cube m in m % 3, P of cube m in m % 2.  The
+  // slot bases are run-time values, so every LDS address is one loop-invariant
+  // lane offset plus a uniform base (the ring spans more than the 64 KB that
+  // an instruction offset reaches).
+  int s3 = 0;  // m % 3
+  for (int m = 0; m <= cnt && cnt > 0; ++m) {
+    const int n3 = s3 == 2 ? 0 : s3 + 1;  // (m + 1) % 3
+    const int p3 = s3 == 0 ? 2 : s3 - 1;  // (m - 1) % 3
+    wait_vmcnt<0>();
+    pipeline_barrier();
+    if (m + 1 < cnt) issue(m + 1, sm.q[n3], sm.dout[n3], sm.ls[n3], sm.dl[n3]);
+    if (!ds_wave) {
       if (m < cnt) {
-        wait_vmcnt<0>();
-        pipeline_barrier();
-        if (m + 1 < cnt) {
-          const int in = list[m + 1];
-          dkdv_issue<D>(qc + hbase, doc + hbase, qt + hbase, dot + hbase, lse, delta, 64LL * in * D,
-                        rbase + 64LL * in, sm.q[u ^ 1], sm.dout[u ^ 1], sm.qt[u ^ 1], sm.dot[u ^ 1], sm.ls[u ^ 1],
-                        sm.dl[u ^ 1], w, toff.k, toff.v, lane);
-        }
-        // S = Q K^T and dP = dO V^T for this wave's 32 queries x 32 keys:
-        // register r holds query 32 wq + 16 (r/8) + 8 hf + r%8.
-        f32x16 s = f32x16{}, dp = f32x16{};
+        f32x16 s = f32x16{};
         {
           bf16x8 qa[DC];
-          read_k<D>(sm.q[u], wq, hf, prow, qa);
+          read_k<D, true>(sm.q[s3], wq, hf, prow, qa);
 #pragma unroll
-          for (int dc = 0; dc < DC; ++dc) s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[dc], kb[dc], s, 0, 0, 0);
+          for (int dc = 0; dc < DC; ++dc) s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[dc], kv[dc], s, 0, 0, 0);
         }
-        {
-          bf16x8 da[DC];
-          read_k<D>(sm.dout[u], wq, hf, prow, da);
-#pragma unroll
-          for (int dc = 0; dc < DC; ++dc) dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da[dc], vb[dc], dp, 0, 0, 0);
-        }
-        const int q0 = 32 * wq + 8 * hf;
-        const f32x4* lsp = reinterpret_cast<const f32x4*>(&sm.ls[u][0]);
-        const f32x4* dlp = reinterpret_cast<const f32x4*>(&sm.dl[u][0]);
+        const f32x4* lsp = reinterpret_cast<const f32x4*>(&sm.ls[s3][0]);
         const f32x4 l4[4] = {lsp[q0 / 4], lsp[q0 / 4 + 1], lsp[(q0 + 16) / 4], lsp[(q0 + 16) / 4 + 1]};
-        const f32x4 d4[4] = {dlp[q0 / 4], dlp[q0 / 4 + 1], dlp[(q0 + 16) / 4], dlp[(q0 + 16) / 4 + 1]};
-        uint32_t pw[8], sw[8];
+        f32x4 pv[4];
+        uint32_t pw[8];
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          pv[r / 4][r % 4] = kmask * __builtin_amdgcn_exp2f(fmaf(s[r], scale_log2, -l4[r / 4][r % 4] * kLog2e));
 #pragma unroll
         for (int r = 0; r < 8; ++r) {
-          const int r0 = 2 * r, r1 = 2 * r + 1;
-          const float p0 = kmask * __builtin_amdgcn_exp2f(fmaf(s[r0], scale_log2, -l4[r0 / 4][r0 % 4] * kLog2e));
-          const float p1 = kmask * __builtin_amdgcn_exp2f(fmaf(s[r1], scale_log2, -l4[r1 / 4][r1 % 4] * kLog2e));
-          const f32x2 p2 = {p0, p1};
-          const f32x2 d2 = {p0 * (dp[r0] - d4[r0 / 4][r0 % 4]), p1 * (dp[r1] - d4[r1 / 4][r1 % 4])};
+          const f32x2 p2 = {pv[r / 2][2 * (r % 2)], pv[r / 2][2 * (r % 2) + 1]};
           pw[r] = __builtin_bit_cast(uint32_t, __builtin_convertvector(p2, bf16x2));
-          sw[r] = __builtin_bit_cast(uint32_t, __builtin_convertvector(d2, bf16x2));
         }
+#pragma unroll
+        for (int c = 0; c < 4; ++c) sm.p[m & 1][quad][c][lane] = pv[c];
         const bf16x8 pb[2] = {__builtin_bit_cast(bf16x8, make_uint4(pw[0], pw[1], pw[2], pw[3])),
                               __builtin_bit_cast(bf16x8, make_uint4(pw[4], pw[5], pw[6], pw[7]))};
-        const bf16x8 sb[2] = {__builtin_bit_cast(bf16x8, make_uint4(sw[0], sw[1], sw[2], sw[3])),
-                              __builtin_bit_cast(bf16x8, make_uint4(sw[4], sw[5], sw[6], sw[7]))};
-        {
-          bf16x8 ta[DT][2];
-          read_v<D>(sm.dot[u], wq, hf, n, ta);
+        bf16x8 ta[DT][2];
+        read_tr<D>(sm.dout[s3], wq, lane, ta);
 #pragma unroll
-          for (int dt = 0; dt < DT; ++dt)
+        for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-            for (int kk = 0; kk < 2; ++kk) va[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ta[dt][kk], pb[kk], va[dt], 0, 0, 0);
-        }
-        {
-          bf16x8 ta[DT][2];
-          read_v<D>(sm.qt[u], wq, hf, n, ta);
-#pragma unroll
-          for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-            for (int kk = 0; kk < 2; ++kk) ka[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ta[dt][kk], sb[kk], ka[dt], 0, 0, 0);
-        }
+          for (int kk = 0; kk < 2; ++kk)
+            acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ta[dt][kk], pb[kk], acc[dt], 0, 0, 0);
       }
+    } else if (m >= 1) {
+      f32x16 dp = f32x16{};
+      {
+        bf16x8 da[DC];
+        read_k<D, true>(sm.dout[p3], wq, hf, prow, da);
+#pragma unroll
+        for (int dc = 0; dc < DC; ++dc) dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da[dc], kv[dc], dp, 0, 0, 0);
+      }
+      const f32x4* dlp = reinterpret_cast<const f32x4*>(&sm.dl[p3][0]);
+      const f32x4 d4[4] = {dlp[q0 / 4], dlp[q0 / 4 + 1], dlp[(q0 + 16) / 4], dlp[(q0 + 16) / 4 + 1]};
+      f32x4 pv[4];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) pv[c] = sm.p[(m - 1) & 1][quad][c][lane];
+      uint32_t sw[8];
+#pragma unroll
+      for (int r = 0; r < 8; ++r) {
+        const int r0 = 2 * r, r1 = 2 * r + 1;
+        const f32x2 d2 = {pv[r0 / 4][r0 % 4] * (dp[r0] - d4[r0 / 4][r0 % 4]),
+                          pv[r1 / 4][r1 % 4] * (dp[r1] - d4[r1 / 4][r1 % 4])};
+        sw[r] = __builtin_bit_cast(uint32_t, __builtin_convertvector(d2, bf16x2));
+      }
+      const bf16x8 sb[2] = {__builtin_bit_cast(bf16x8, make_uint4(sw[0], sw[1], sw[2], sw[3])),
+                            __builtin_bit_cast(bf16x8, make_uint4(sw[4], sw[5], sw[6], sw[7]))};
+      bf16x8 ta[DT][2];
+      read_tr<D>(sm.q[p3], wq, lane, ta);
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk)
+          acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ta[dt][kk], sb[kk], acc[dt], 0, 0, 0);
     }
+    s3 = n3;
   }
 
-  // The two query halves hold partial sums of the same dK^T, dV^T: add them.
+  // The two query halves hold partial sums of the same dK^T (dV^T): add them.
   wait_vmcnt<0>();
   __syncthreads();
-  float* xk = reinterpret_cast<float*>(&sm) + wk * (2 * DT * 16 * 64);
-  float* xv = xk + DT * 16 * 64;
+  float* x = reinterpret_cast<float*>(&sm) + ((ds_wave ? 2 : 0) + wk) * (DT * 16 * 64);
   if (wq == 1) {
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        xk[(dt * 16 + r) * 64 + lane] = ka[dt][r];
-        xv[(dt * 16 + r) * 64 + lane] = va[dt][r];
-      }
+      for (int r = 0; r < 16; ++r) x[(dt * 16 + r) * 64 + lane] = acc[dt][r];
   }
   __syncthreads();
   if (wq == 1) return;
+  const float f = ds_wave ? scale : 1.f;
+  uint16_t* out = (ds_wave ? dk : dv) + krow * D;
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
     for (int gq = 0; gq < 4; ++gq) {
-      float fk[4], fv[4];
+      float o[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int r = 4 * gq + e;
-        fk[e] = scale * (ka[dt][r] + xk[(dt * 16 + r) * 64 + lane]);
-        fv[e] = va[dt][r] + xv[(dt * 16 + r) * 64 + lane];
+        o[e] = f * (acc[dt][r] + x[(dt * 16 + r) * 64 + lane]);
       }
-      const int d = 32 * dt + 8 * gq + 4 * hf;
-      *reinterpret_cast<uint2*>(dk + krow * D + d) = make_uint2(pack_bf16x2(fk[0], fk[1]), pack_bf16x2(fk[2], fk[3]));
-      *reinterpret_cast<uint2*>(dv + krow * D + d) = make_uint2(pack_bf16x2(fv[0], fv[1]), pack_bf16x2(fv[2], fv[3]));
+      *reinterpret_cast<uint2*>(out + 32 * dt + 8 * gq + 4 * hf) =
+          make_uint2(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]));
     }
 }
 
@@ -468,10 +478,9 @@ inline BwdWs carve(const KGeom& g, int topk, void* ws) {
 }
 
 template <int D, bool PARTIAL>
-hipError_t launch_bwd_t(const KGeom& g, const uint16_t* qc, const uint16_t* qt, const uint16_t* kc,
-                        const uint16_t* kt, const uint16_t* vc, const uint16_t* oc, const uint16_t* doc,
-                        const uint16_t* dot, const float* lse, const int32_t* idx, int topk, float scale,
-                        uint16_t* dq, uint16_t* dk, uint16_t* dv, void* ws, hipStream_t s) {
+hipError_t launch_bwd_t(const KGeom& g, const uint16_t* qc, const uint16_t* kc, const uint16_t* vc,
+                        const uint16_t* oc, const uint16_t* doc, const float* lse, const int32_t* idx, int topk,
+                        float scale, uint16_t* dq, uint16_t* dk, uint16_t* dv, void* ws, hipStream_t s) {
   const BwdWs w = carve(g, topk, ws);
   const long long rows = (long long)g.B * g.H * g.Np;
   bwd_delta<D><<<dim3((unsigned)((rows * (D / 8) + 255) / 256)), dim3(256), 0, s>>>(oc, doc, w.delta, rows);
@@ -481,11 +490,10 @@ hipError_t launch_bwd_t(const KGeom& g, const uint16_t* qc, const uint16_t* qt, 
   bwd_fill<<<tgrid, dim3(256), 0, s>>>(idx, topk, w.off, w.list, g);
   const Placement pl = make_placement(g);
   const float scale_log2 = scale * kLog2e;
-  bwd_dq<D, PARTIAL><<<dim3(grid_size(g)), dim3(kThreads), 0, s>>>(qc, kc, kt, vc, doc, lse, w.delta, idx, topk,
-                                                                    scale, scale_log2, dq, g, pl);
-  bwd_dkdv<D, PARTIAL><<<dim3(grid_size(g)), dim3(kThreads), 0, s>>>(qc, qt, kc, vc, doc, dot, lse, w.delta, w.off,
-                                                                      w.cnt, w.list, topk, scale, scale_log2, dk, dv,
-                                                                      g, pl);
+  bwd_dq<D, PARTIAL><<<dim3(grid_size(g)), dim3(kThreads), 0, s>>>(qc, kc, vc, doc, lse, w.delta, idx, topk, scale,
+                                                                    scale_log2, dq, g, pl);
+  bwd_dkdv<D, PARTIAL><<<dim3(grid_size(g)), dim3(2 * kThreads), 0, s>>>(qc, kc, vc, doc, lse, w.delta, w.off, w.cnt,
+                                                                      w.list, topk, scale, scale_log2, dk, dv, g, pl);
   return hipGetLastError();
 }
 
@@ -497,16 +505,15 @@ size_t attn_bwd_workspace_bytes(const KGeom& g, int topk) {
          align256(bh * g.nc * (size_t)topk * sizeof(int32_t));
 }
 
-hipError_t launch_attn_bwd(const KGeom& g, const uint16_t* qc, const uint16_t* qt, const uint16_t* kc,
-                           const uint16_t* kt, const uint16_t* vc, const uint16_t* oc, const uint16_t* doc,
-                           const uint16_t* dot, const float* lse, const int32_t* idx, int topk, float scale,
-                           uint16_t* dq, uint16_t* dk, uint16_t* dv, void* ws, hipStream_t s) {
+hipError_t launch_attn_bwd(const KGeom& g, const uint16_t* qc, const uint16_t* kc, const uint16_t* vc,
+                           const uint16_t* oc, const uint16_t* doc, const float* lse, const int32_t* idx, int topk,
+                           float scale, uint16_t* dq, uint16_t* dk, uint16_t* dv, void* ws, hipStream_t s) {
   if (g.D == 64) {
-    if (g.partial) return launch_bwd_t<64, true>(g, qc, qt, kc, kt, vc, oc, doc, dot, lse, idx, topk, scale, dq, dk, dv, ws, s);
-    return launch_bwd_t<64, false>(g, qc, qt, kc, kt, vc, oc, doc, dot, lse, idx, topk, scale, dq, dk, dv, ws, s);
+    if (g.partial) return launch_bwd_t<64, true>(g, qc, kc, vc, oc, doc, lse, idx, topk, scale, dq, dk, dv, ws, s);
+    return launch_bwd_t<64, false>(g, qc, kc, vc, oc, doc, lse, idx, topk, scale, dq, dk, dv, ws, s);
   }
-  if (g.partial) return launch_bwd_t<128, true>(g, qc, qt, kc, kt, vc, oc, doc, dot, lse, idx, topk, scale, dq, dk, dv, ws, s);
-  return launch_bwd_t<128, false>(g, qc, qt, kc, kt, vc, oc, doc, dot, lse, idx, topk, scale, dq, dk, dv, ws, s);
+  if (g.partial) return launch_bwd_t<128, true>(g, qc, kc, vc, oc, doc, lse, idx, topk, scale, dq, dk, dv, ws, s);
+  return launch_bwd_t<128, false>(g, qc, kc, vc, oc, doc, lse, idx, topk, scale, dq, dk, dv, ws, s);
 }
 
 }  // namespace vsa

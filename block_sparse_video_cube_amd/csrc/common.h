@@ -122,8 +122,7 @@ hipError_t launch_quant(const KGeom& g, const uint16_t* q, const uint16_t* k, co
 hipError_t launch_attn_fwd_fp8(const KGeom& g, const uint8_t* q8, const float* qs, const uint8_t* k8,
                                const float* ks, const uint8_t* v8t, const float* vs, const int32_t* idx, int topk,
                                float scale, bool raster_out, uint16_t* o, float* lse, hipStream_t s);
-hipError_t launch_attn_bwd(const KGeom& g, const uint16_t* qc, const uint16_t* qt, const uint16_t* kc,
-                           const uint16_t* kt, const uint16_t* vc, const uint16_t* oc, const uint16_t* doc,
-                           const uint16_t* dot, const float* lse, const int32_t* idx, int topk, float scale,
-                           uint16_t* dq, uint16_t* dk, uint16_t* dv, void* ws, hipStream_t s);
+hipError_t launch_attn_bwd(const KGeom& g, const uint16_t* qc, const uint16_t* kc, const uint16_t* vc,
+                           const uint16_t* oc, const uint16_t* doc, const float* lse, const int32_t* idx, int topk,
+                           float scale, uint16_t* dq, uint16_t* dk, uint16_t* dv, void* ws, hipStream_t s);
 }  // namespace vsa

@@ -53,10 +53,26 @@ __device__ __forceinline__ int k_swz(int row) {
 }
 __device__ __forceinline__ int v_swz(int row) { return (row >> 1) & 7; }
 
+// Token-major tiles that are also read transposed (read_tr) use another chunk
+// swizzle: at D = 128 the two 2-bit fields of the row index trade places, so
+// the four rows that one 16-lane group of a transposed read touches land in
+// four different quarters of the banks; read_k stays conflict-free (the map
+// is a bijection of row % 16).  At D = 64 two rows share 256 bytes and the
+// same idea takes (row >> 1) & 1 to the top bit.
+template <int D>
+__device__ __forceinline__ int kt_swz(int row) {
+  return (D == 128) ? (((row & 3) << 2) | ((row >> 2) & 3)) : ((((row >> 1) & 1) << 2) | ((row >> 2) & 3));
+}
+template <int D, bool TR>
+__device__ __forceinline__ int row_swz(int row) {
+  return TR ? kt_swz<D>(row) : k_swz<D>(row);
+}
+
 // Per-lane byte offsets of this wave's share of one K tile and one V^T tile.
 // Every buffer_load_dwordx4 ... lds writes 64 consecutive 16-byte LDS slots;
 // lane L fills slot L with the global chunk that the swizzle maps there.
-template <int D>
+// TR: K-style tiles in the kt_swz layout.
+template <int D, bool TR = false>
 struct TileOffsets {
   static constexpr int KRPI = 512 / D;  // K rows per 1 KB instruction
   static constexpr int NI = D / 32;     // instructions per wave per tile
@@ -65,7 +81,7 @@ struct TileOffsets {
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
       const int row = (w * NI + i) * KRPI + lane / (D / 8);
-      k[i] = (uint32_t)(row * D + ((lane % (D / 8)) ^ k_swz<D>(row)) * 8) * 2u;
+      k[i] = (uint32_t)(row * D + ((lane % (D / 8)) ^ row_swz<D, TR>(row)) * 8) * 2u;
       const int vrow = (w * NI + i) * 8 + (lane >> 3);
       v[i] = (uint32_t)(vrow * 64 + ((lane & 7) ^ v_swz(vrow)) * 8) * 2u;
     }
@@ -159,12 +175,42 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t raster_tile(const uint16_t* xh
 }
 
 // K fragments of S^T = K Q^T for this wave's key half (rows in pi order).
-template <int D>
+template <int D, bool TR = false>
 __device__ __forceinline__ void read_k(const uint16_t* klds, int wk, int hf, int prow, bf16x8 (&ka)[D / 16]) {
   const int krow = 32 * wk + prow;
 #pragma unroll
   for (int dc = 0; dc < D / 16; ++dc)
-    ka[dc] = *reinterpret_cast<const bf16x8*>(klds + krow * D + (((2 * dc + hf) ^ k_swz<D>(krow)) * 8));
+    ka[dc] = *reinterpret_cast<const bf16x8*>(klds + krow * D + (((2 * dc + hf) ^ row_swz<D, TR>(krow)) * 8));
+}
+
+// The transpose of a token-major tile (kt_swz layout) as A operands:
+// xa[dt][kk] of lane (hf, n) holds X[32 w + 16 kk + 8 hf + e][32 dt + n],
+// e = 0..7, the same fragments read_v gives from a stored transpose.
+// ds_read_b64_tr_b16 works on groups of 16 lanes: each lane points at 4
+// consecutive elements of one row, and lane l of the group receives element
+// l % 4 of the rows pointed at by lanes l / 4, 4 + l / 4, 8 + l / 4 and
+// 12 + l / 4.  So lane s of the group points at row (s / 4) of a 4-row
+// slice, columns 4 (s % 4) .. +3 of a 16-column slice, and lane l gets
+// column l of the 4 rows.  Two reads give the 8 rows of one fragment.
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4* lds_i16x4_ptr;
+template <int D>
+__device__ __forceinline__ void read_tr(const uint16_t* lds, int w, int lane, bf16x8 (&xa)[D / 32][2]) {
+  const int s = lane & 15, grp = lane >> 4, hf = grp >> 1;
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      i16x4 part[2];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int r = 32 * w + 16 * kk + 8 * hf + 4 * h + (s >> 2);
+        const int d = 32 * dt + 16 * (grp & 1) + 4 * (s & 3);
+        const uint16_t* p = lds + r * D + (((d >> 3) ^ kt_swz<D>(r)) << 3) + (d & 4);
+        part[h] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_ptr)(p));
+      }
+      xa[dt][kk] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(part[0], part[1], 0, 1, 2, 3, 4, 5, 6, 7));
+    }
 }
 
 // V^T fragments of O^T += V^T P^T for this wave's 32 keys (2 chunks of 16).

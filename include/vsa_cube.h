@@ -257,20 +257,19 @@ int32_t vsa_sparse_attn_fwd_fp8(const vsa_geom* g, const uint8_t* q8, const floa
  *   dQ_i = scale sum_j dS_ij K_j,  dK_j = scale sum_i dS_ij^T Q_i,
  * over the blocks (i, j) of idx.  No atomics: the result does not depend on
  * scheduling.
- * Inputs (all [B, heads, Np, D] bf16 unless stated; *_t: DIM_MAJOR layout of
- * the same tensor, [B, heads, Nc, D, 64], from vsa_cube_permute):
- *   qc, qt: Q; kc, kt: K; vc: V (TOKEN_MAJOR); oc: the forward output;
- *   doc, dot: dO, whose padded rows must be zero (as vsa_cube_permute writes
- *   them); lse: fp32 [B, heads, Np], the forward's lse output; idx, topk:
- *   the forward's block lists (rows ascending, entries distinct).
+ * Inputs (all [B, heads, Np, D] bf16 TOKEN_MAJOR unless stated; the kernels
+ * read the transposed operands out of the same tiles):
+ *   qc: Q; kc: K; vc: V; oc: the forward output; doc: dO, whose padded rows
+ *   must be zero (as vsa_cube_permute writes them); lse: fp32 [B, heads, Np],
+ *   the forward's lse output; idx, topk: the forward's block lists (rows
+ *   ascending, entries distinct).
  * Outputs (bf16 [B, heads, Np, D] TOKEN_MAJOR, fp32 accumulation): dq, dk, dv;
  * padded rows hold zero (dq: padded query rows carry no gradient).
  * ws: at least vsa_attn_bwd_workspace_bytes(g, topk) bytes.
  * Limits as vsa_select_topk (n_cubes <= VSA_MAX_CUBES). */
 size_t vsa_attn_bwd_workspace_bytes(const vsa_geom* g, int32_t topk);
-int32_t vsa_sparse_attn_bwd(const vsa_geom* g, const uint16_t* qc, const uint16_t* qt,
-                            const uint16_t* kc, const uint16_t* kt, const uint16_t* vc,
-                            const uint16_t* oc, const uint16_t* doc, const uint16_t* dot,
+int32_t vsa_sparse_attn_bwd(const vsa_geom* g, const uint16_t* qc, const uint16_t* kc,
+                            const uint16_t* vc, const uint16_t* oc, const uint16_t* doc,
                             const float* lse, const int32_t* idx, int32_t topk,
                             float softmax_scale, uint16_t* dq, uint16_t* dk, uint16_t* dv,
                             void* ws, size_t ws_bytes, void* stream);

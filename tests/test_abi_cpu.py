@@ -169,9 +169,9 @@ def test_backward_entry_point_validation(lib):
     assert ws >= 2 * 512 * 4 + 2 * 2 * 8 * 4 + 2 * 8 * 2 * 4
     assert lib.vsa_attn_bwd_workspace_bytes(g, 0) == 0
     assert lib.vsa_attn_bwd_workspace_bytes(g, 9) == 0
-    args = [P] * 10  # qc qt kc kt vc oc doc dot lse idx
+    args = [P] * 7  # qc kc vc oc doc lse idx
     outs = [P] * 3
-    assert lib.vsa_sparse_attn_bwd(g, *args[:9], None, 2, 0.125, *outs, P, ws, None) == _lib.VSA_ERR_NULL
+    assert lib.vsa_sparse_attn_bwd(g, *args[:6], None, 2, 0.125, *outs, P, ws, None) == _lib.VSA_ERR_NULL
     assert lib.vsa_sparse_attn_bwd(g, *args, 2, 0.125, P, P, None, P, ws, None) == _lib.VSA_ERR_NULL
     assert lib.vsa_sparse_attn_bwd(g, ODD, *args[1:], 2, 0.125, *outs, P, ws, None) == _lib.VSA_ERR_ALIGN
     assert lib.vsa_sparse_attn_bwd(g, *args, 0, 0.125, *outs, P, ws, None) == _lib.VSA_ERR_TOPK

@@ -38,6 +38,7 @@ def calls(vsa):
     sc = torch.zeros((B, H, 8), dtype=torch.float32)
     v8t = torch.zeros((B, H, 8, D, 64), dtype=torch.uint8)
     vs = torch.zeros((B, H, D), dtype=torch.float32)
+    lse = torch.zeros((B, H, 512), dtype=torch.float32)
     return {
         "cube_permute": lambda: vsa.cube_permute(x, GRID),
         "cube_permute_pool": lambda: vsa.cube_permute_pool(x, GRID),
@@ -50,11 +51,13 @@ def calls(vsa):
         "sparse_attn_linear_fwd": lambda: vsa.sparse_attn_linear_fwd(qc, qc, vt, idx, GRID),
         "quant_fp8": lambda: vsa.quant_fp8(x, x, x, GRID),
         "sparse_attn_fwd_fp8": lambda: vsa.sparse_attn_fwd_fp8(u8, sc, u8, sc, v8t, vs, idx, GRID),
+        "sparse_attn_bwd": lambda: vsa.sparse_attn_bwd(qc, qc, qc, qc, qc, lse, idx, GRID),
     }
 
 
 NAMES = ["cube_permute", "cube_permute_pool", "cube_pool", "cube_unpermute", "select_topk", "select_topk_pooled",
-         "sparse_attn_fwd", "sparse_attn_fwd_raster", "sparse_attn_linear_fwd", "quant_fp8", "sparse_attn_fwd_fp8"]
+         "sparse_attn_fwd", "sparse_attn_fwd_raster", "sparse_attn_linear_fwd", "quant_fp8", "sparse_attn_fwd_fp8",
+         "sparse_attn_bwd"]
 
 
 @pytest.mark.parametrize("name", NAMES)

@@ -39,11 +39,10 @@ def gpu_backward(inp, do_bits, grid, idx_np, scale):
 
     q, k, v, do = (to_dev(x) for x in (inp["q"], inp["k"], inp["v"], do_bits))
     qc, kc, vc, doc = (vsa.cube_permute(x, grid) for x in (q, k, v, do))
-    qt, kt, dot = (vsa.cube_permute(x, grid, layout="dim") for x in (q, k, do))
     vt = vsa.cube_permute(v, grid, layout="dim")
     idx = torch.from_numpy(np.ascontiguousarray(idx_np, dtype=np.int32)).to("cuda:0")
     oc, _, lse = vsa.sparse_attn_fwd(qc, kc, vt, idx, grid, scale, want_lse=True)
-    dq, dk, dv = vsa.sparse_attn_bwd(qc, qt, kc, kt, vc, oc, doc, dot, lse, idx, grid, scale)
+    dq, dk, dv = vsa.sparse_attn_bwd(qc, kc, vc, oc, doc, lse, idx, grid, scale)
     out = tuple(vsa.cube_unpermute(x, grid) for x in (dq, dk, dv))
     torch.cuda.synchronize()
     return tuple(oracle.bf16_to_f64(to_bits(x)) for x in out)
