@@ -356,72 +356,65 @@ __global__ void __launch_bounds__(2 * kThreads, 1) bwd_dkdv(const uint16_t* __re
   for (int m = 0; m <= cnt && cnt > 0; ++m) {
     const int n3 = s3 == 2 ? 0 : s3 + 1;  // (m + 1) % 3
     const int p3 = s3 == 0 ? 2 : s3 - 1;  // (m - 1) % 3
+    // P wavefronts: S = Q(m) K^T, then dV^T += dO(m)^T P.
+    // dS wavefronts: dP = dO(m-1) V^T, then dK^T += Q(m-1)^T dS.
+    const bool active = ds_wave ? m >= 1 : m < cnt;
+    const int sl = ds_wave ? p3 : s3;
+    const uint16_t* a_tile = ds_wave ? sm.dout[sl] : sm.q[sl];
+    const uint16_t* t_tile = ds_wave ? sm.q[sl] : sm.dout[sl];
     wait_vmcnt<0>();
     pipeline_barrier();
+    // The transposed reads go first: the compiler makes every
+    // ds_read_b64_tr_b16 wait for all tile loads in flight, and at this point
+    // none are.
+    bf16x8 ta[DT][2];
+    if (active) read_tr<D>(t_tile, wq, lane, ta);
     if (m + 1 < cnt) issue(m + 1, sm.q[n3], sm.dout[n3], sm.ls[n3], sm.dl[n3]);
-    if (!ds_wave) {
-      if (m < cnt) {
-        f32x16 s = f32x16{};
-        {
-          bf16x8 qa[DC];
-          read_k<D, true>(sm.q[s3], wq, hf, prow, qa);
+    if (active) {
+      f32x16 x = f32x16{};  // S or dP
+      {
+        bf16x8 xa[DC];
+        read_k<D, true>(a_tile, wq, hf, prow, xa);
 #pragma unroll
-          for (int dc = 0; dc < DC; ++dc) s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[dc], kv[dc], s, 0, 0, 0);
-        }
-        const f32x4* lsp = reinterpret_cast<const f32x4*>(&sm.ls[s3][0]);
+        for (int dc = 0; dc < DC; ++dc) x = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xa[dc], kv[dc], x, 0, 0, 0);
+      }
+      f32x4* pslot = &sm.p[(m & 1) ^ (ds_wave ? 1 : 0)][quad][0][lane];  // P(m) out, P(m-1) in
+      uint32_t bw[8];
+      if (!ds_wave) {
+        const f32x4* lsp = reinterpret_cast<const f32x4*>(&sm.ls[sl][0]);
         const f32x4 l4[4] = {lsp[q0 / 4], lsp[q0 / 4 + 1], lsp[(q0 + 16) / 4], lsp[(q0 + 16) / 4 + 1]};
         f32x4 pv[4];
-        uint32_t pw[8];
 #pragma unroll
         for (int r = 0; r < 16; ++r)
-          pv[r / 4][r % 4] = kmask * __builtin_amdgcn_exp2f(fmaf(s[r], scale_log2, -l4[r / 4][r % 4] * kLog2e));
+          pv[r / 4][r % 4] = kmask * __builtin_amdgcn_exp2f(fmaf(x[r], scale_log2, -l4[r / 4][r % 4] * kLog2e));
+#pragma unroll
+        for (int c = 0; c < 4; ++c) pslot[64 * c] = pv[c];
 #pragma unroll
         for (int r = 0; r < 8; ++r) {
           const f32x2 p2 = {pv[r / 2][2 * (r % 2)], pv[r / 2][2 * (r % 2) + 1]};
-          pw[r] = __builtin_bit_cast(uint32_t, __builtin_convertvector(p2, bf16x2));
+          bw[r] = __builtin_bit_cast(uint32_t, __builtin_convertvector(p2, bf16x2));
         }
+      } else {
+        const f32x4* dlp = reinterpret_cast<const f32x4*>(&sm.dl[sl][0]);
+        const f32x4 d4[4] = {dlp[q0 / 4], dlp[q0 / 4 + 1], dlp[(q0 + 16) / 4], dlp[(q0 + 16) / 4 + 1]};
+        f32x4 pv[4];
 #pragma unroll
-        for (int c = 0; c < 4; ++c) sm.p[m & 1][quad][c][lane] = pv[c];
-        const bf16x8 pb[2] = {__builtin_bit_cast(bf16x8, make_uint4(pw[0], pw[1], pw[2], pw[3])),
-                              __builtin_bit_cast(bf16x8, make_uint4(pw[4], pw[5], pw[6], pw[7]))};
-        bf16x8 ta[DT][2];
-        read_tr<D>(sm.dout[s3], wq, lane, ta);
+        for (int c = 0; c < 4; ++c) pv[c] = pslot[64 * c];
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-          for (int kk = 0; kk < 2; ++kk)
-            acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ta[dt][kk], pb[kk], acc[dt], 0, 0, 0);
+        for (int r = 0; r < 8; ++r) {
+          const int r0 = 2 * r, r1 = 2 * r + 1;
+          const f32x2 d2 = {pv[r0 / 4][r0 % 4] * (x[r0] - d4[r0 / 4][r0 % 4]),
+                            pv[r1 / 4][r1 % 4] * (x[r1] - d4[r1 / 4][r1 % 4])};
+          bw[r] = __builtin_bit_cast(uint32_t, __builtin_convertvector(d2, bf16x2));
+        }
       }
-    } else if (m >= 1) {
-      f32x16 dp = f32x16{};
-      {
-        bf16x8 da[DC];
-        read_k<D, true>(sm.dout[p3], wq, hf, prow, da);
-#pragma unroll
-        for (int dc = 0; dc < DC; ++dc) dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da[dc], kv[dc], dp, 0, 0, 0);
-      }
-      const f32x4* dlp = reinterpret_cast<const f32x4*>(&sm.dl[p3][0]);
-      const f32x4 d4[4] = {dlp[q0 / 4], dlp[q0 / 4 + 1], dlp[(q0 + 16) / 4], dlp[(q0 + 16) / 4 + 1]};
-      f32x4 pv[4];
-#pragma unroll
-      for (int c = 0; c < 4; ++c) pv[c] = sm.p[(m - 1) & 1][quad][c][lane];
-      uint32_t sw[8];
-#pragma unroll
-      for (int r = 0; r < 8; ++r) {
-        const int r0 = 2 * r, r1 = 2 * r + 1;
-        const f32x2 d2 = {pv[r0 / 4][r0 % 4] * (dp[r0] - d4[r0 / 4][r0 % 4]),
-                          pv[r1 / 4][r1 % 4] * (dp[r1] - d4[r1 / 4][r1 % 4])};
-        sw[r] = __builtin_bit_cast(uint32_t, __builtin_convertvector(d2, bf16x2));
-      }
-      const bf16x8 sb[2] = {__builtin_bit_cast(bf16x8, make_uint4(sw[0], sw[1], sw[2], sw[3])),
-                            __builtin_bit_cast(bf16x8, make_uint4(sw[4], sw[5], sw[6], sw[7]))};
-      bf16x8 ta[DT][2];
-      read_tr<D>(sm.q[p3], wq, lane, ta);
+      const bf16x8 bop[2] = {__builtin_bit_cast(bf16x8, make_uint4(bw[0], bw[1], bw[2], bw[3])),
+                             __builtin_bit_cast(bf16x8, make_uint4(bw[4], bw[5], bw[6], bw[7]))};
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk)
-          acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ta[dt][kk], sb[kk], acc[dt], 0, 0, 0);
+          acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ta[dt][kk], bop[kk], acc[dt], 0, 0, 0);
     }
     s3 = n3;
   }
