@@ -75,6 +75,21 @@ def test_topk_integer_720p_shape_two_heads():
     assert np.array_equal(got, ref)
 
 
+@pytest.mark.parametrize("name", ["wan1.3b", "wan14b"])
+def test_topk_integer_wan_shapes_two_heads(name):
+    # 364 and 455 cubes (12 and 15 score tiles of 32, the last one ragged),
+    # both entry points.
+    import block_sparse_video_cube_amd as vsa
+
+    wl = workloads.workload(name).with_(heads=2)
+    inp = workloads.make_integer_inputs(wl)
+    ref = oracle_select(inp, wl, wl.topk)
+    assert np.array_equal(run_select(inp, wl, wl.topk), ref)
+    _, qbar = vsa.cube_permute_pool(to_dev(inp["q"]), wl.grid)
+    _, kbar = vsa.cube_permute_pool(to_dev(inp["k"]), wl.grid)
+    assert np.array_equal(vsa.select_topk_pooled(qbar, kbar, wl.grid, wl.topk).cpu().numpy(), ref)
+
+
 @pytest.mark.parametrize("grid,topk", [((8, 8, 8), 2), ((5, 6, 7), 3), ((13, 10, 22), 9)])
 def test_topk_float_inputs_near_tie_valid(grid, topk):
     wl = workloads.workload("tiny").with_(grid=grid, topk=topk, heads=3)
