@@ -16,9 +16,10 @@
 //   den = phi(Q) z_tot - sum_{j in sel} rowsum(phi(Q) phi(K_j)^T).
 //
 // Kernels:
-//   lin_state   per (b, h, group of 8 cubes): phi(K) (bf16, padded rows 0)
+//   lin_state   per (b, h, group of cubes): phi(K) (bf16, padded rows 0)
 //               written token-major for lin_apply, and partial
-//               S = phi(K)^T V (bf16 MFMA, fp32 accumulate) and z = sum phi(K);
+//               S = phi(K)^T V (bf16 MFMA, fp32 accumulate; phi(K)^T read
+//               with the transposed LDS read) and z = sum phi(K);
 //   lin_reduce  per (b, h, 256 state elements): S_tot^T split into bf16
 //               hi + lo halves, z_tot;
 //   lin_apply   per (b, h, query cube): num / den and the combine.
@@ -31,7 +32,20 @@ namespace vsa {
 namespace {
 
 using namespace tiles;
-constexpr int kGroup = 8;  // cubes per partial state
+// Cubes per partial state: the groups of all (b, h) fill the resident
+// workgroup slots of lin_state (two per CU on the 256 CUs) in one round,
+// which also keeps the partial-state traffic small.
+struct LinGroups {
+  int size;   // cubes per group
+  int count;  // groups per (b, h)
+};
+constexpr int kStateSlots = 2 * 256;
+__host__ __device__ inline LinGroups lin_groups(const KGeom& g) {
+  const int bh = g.B * g.H;
+  const int want = bh >= kStateSlots ? 1 : kStateSlots / bh;
+  const int size = (g.nc + want - 1) / want;
+  return LinGroups{size, (g.nc + size - 1) / size};
+}
 
 __device__ __forceinline__ float phi(float x) { return phi_elu1(x); }
 
@@ -48,7 +62,7 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 LinWs carve(const KGeom& g, void* ws, size_t* total) {
   const size_t bh = (size_t)g.B * g.H;
-  const size_t G = (g.nc + kGroup - 1) / kGroup;
+  const size_t G = lin_groups(g).count;
   const size_t D = g.D;
   size_t off = 0;
   char* base = static_cast<char*>(ws);
@@ -69,37 +83,58 @@ LinWs carve(const KGeom& g, void* ws, size_t* total) {
   return w;
 }
 
+// Per cube of the group: phi(K) goes to HBM (token-major, for lin_apply) and
+// to one of two LDS slots (token-major, kt_swz), from which each wavefront
+// reads phi(K)^T fragments with the transposed LDS read; the V^T tile goes
+// to an LDS slot too (v_swz layout) for the B operands.  Each thread loads
+// its share of the next cube's K and V^T rows while the current cube's
+// products run, and one barrier per cube orders the slots.  Wavefront w owns
+// state rows d = 32 mt .. +31 and NT column tiles.
 template <int D>
-__global__ void __launch_bounds__(256) lin_state(const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vt,
-                                                 LinWs ws, KGeom g) {
-  constexpr int CH = D / 8;
-  constexpr int RGS = 256 / CH;                 // threads sharing one d chunk
-  constexpr int NT = (D == 128) ? 4 : 1;        // e tiles per wave
-  __shared__ __attribute__((aligned(16))) uint16_t fkT[D * 64];
+__global__ void __launch_bounds__(256, 2) lin_state(const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vt,
+                                                    LinWs ws, KGeom g) {
+  constexpr int CH = D / 8;              // 16-byte chunks per row
+  constexpr int PT = 64 * CH / 256;      // chunks per thread per tile
+  constexpr int RGS = 256 / CH;          // threads sharing one d chunk
+  constexpr int NT = (D == 128) ? 4 : 1; // e tiles per wave
+  __shared__ __attribute__((aligned(16))) uint16_t fks[2][64 * D];
+  __shared__ __attribute__((aligned(16))) uint16_t vts[2][D * 64];
   __shared__ float zred[RGS][D];
   const int grp = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, hf = lane >> 5, n = lane & 31;
   const long long bh = (long long)b * g.H + h;
-  const int G = (g.nc + kGroup - 1) / kGroup;
+  const LinGroups lg = lin_groups(g);
+  const int G = lg.count;
   const int mt = (D == 128) ? w : (w >> 1);
   const int nt0 = (D == 128) ? 0 : (w & 1);
+  const int ch = tid % CH;
+  const int c0 = grp * lg.size, c1 = min(g.nc, c0 + lg.size);
   f32x16 acc[NT];
 #pragma unroll
   for (int t = 0; t < NT; ++t) acc[t] = f32x16{};
   float zacc[8] = {};
-  const int ch = tid % CH;
 
-  for (int c = grp * kGroup; c < min(g.nc, (grp + 1) * kGroup); ++c) {
+  uint4 kreg[PT], vreg[PT];
+  auto load = [&](int c) {
+    const uint4* ksrc = reinterpret_cast<const uint4*>(kc + (bh * g.Np + 64LL * c) * D);
+    const uint4* vsrc = reinterpret_cast<const uint4*>(vt + (bh * g.Np + 64LL * c) * D);
+#pragma unroll
+    for (int p = 0; p < PT; ++p) {
+      kreg[p] = ksrc[tid + 256 * p];
+      vreg[p] = vsrc[tid + 256 * p];
+    }
+  };
+  load(c0);
+  for (int c = c0; c < c1; ++c) {
+    const int slot = (c - c0) & 1;
     int ct, cy, cx;
     cube_coords(g, c, ct, cy, cx);
-    __syncthreads();
-    const uint4* ksrc = reinterpret_cast<const uint4*>(kc + (bh * g.Np + 64LL * c) * D);
     uint4* fdst = reinterpret_cast<uint4*>(ws.fk + (bh * g.Np + 64LL * c) * D);
-    for (int f = tid; f < 64 * CH; f += 256) {
-      const int row = f / CH;
+#pragma unroll
+    for (int p = 0; p < PT; ++p) {
+      const int f = tid + 256 * p, row = f / CH;
       const bool valid = local_valid(g, ct, cy, cx, row);
-      const uint4 raw = ksrc[f];
-      const uint32_t wv[4] = {raw.x, raw.y, raw.z, raw.w};
+      const uint32_t wv[4] = {kreg[p].x, kreg[p].y, kreg[p].z, kreg[p].w};
       uint32_t outw[4];
 #pragma unroll
       for (int e2 = 0; e2 < 4; ++e2) {
@@ -108,23 +143,29 @@ __global__ void __launch_bounds__(256) lin_state(const uint16_t* __restrict__ kc
         zacc[2 * e2] += bf16_to_f32(p0);
         zacc[2 * e2 + 1] += bf16_to_f32(p1);
         outw[e2] = (uint32_t)p0 | ((uint32_t)p1 << 16);
-        const int d0 = 8 * ch + 2 * e2;
-        fkT[d0 * 64 + (((row >> 3) ^ v_swz(d0)) * 8) + (row & 7)] = p0;
-        fkT[(d0 + 1) * 64 + (((row >> 3) ^ v_swz(d0 + 1)) * 8) + (row & 7)] = p1;
       }
-      fdst[f] = make_uint4(outw[0], outw[1], outw[2], outw[3]);
+      const uint4 o = make_uint4(outw[0], outw[1], outw[2], outw[3]);
+      fdst[f] = o;
+      *reinterpret_cast<uint4*>(&fks[slot][row * D + ((ch ^ kt_swz<D>(row)) << 3)]) = o;
+      // V^T row e = f / 8 (64 tokens, 8 chunks of 8).
+      const int vrow = f >> 3, vch = f & 7;
+      *reinterpret_cast<uint4*>(&vts[slot][vrow * 64 + ((vch ^ v_swz(vrow)) << 3)]) = vreg[p];
     }
-    __syncthreads();
-    const uint16_t* vcube = vt + (bh * g.Np + 64LL * c) * D;
-    const int drow = 32 * mt + n;
+    if (c + 1 < c1) load(c + 1);
+    pipeline_barrier();  // this cube's slots are complete; the slots written next were last read two cubes ago
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      const bf16x8 a = *reinterpret_cast<const bf16x8*>(fkT + drow * 64 + (((2 * kk + hf) ^ v_swz(drow)) * 8));
+    for (int wk = 0; wk < 2; ++wk) {
+      bf16x8 va[D / 32][2];
+      read_v<D>(vts[slot], wk, hf, n, va);
 #pragma unroll
-      for (int t = 0; t < NT; ++t) {
-        const int e = 32 * (nt0 + t) + n;
-        const bf16x8 bv = *reinterpret_cast<const bf16x8*>(vcube + e * 64 + 16 * kk + 8 * hf);
-        acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bv, acc[t], 0, 0, 0);
+      for (int kk = 0; kk < 2; ++kk) {
+        const bf16x8 a = read_tr_one<D>(fks[slot], 32 * wk + 16 * kk, mt, lane);
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+          // D = 64: one column tile per wave, picked by the uniform nt0.
+          const bf16x8 bop = (D == 128) ? va[t][kk] : (nt0 ? va[D / 32 - 1][kk] : va[0][kk]);
+          acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bop, acc[t], 0, 0, 0);
+        }
       }
     }
   }
@@ -154,10 +195,11 @@ __global__ void __launch_bounds__(256) lin_state(const uint16_t* __restrict__ kc
 template <int D>
 __global__ void __launch_bounds__(256) lin_reduce(LinWs ws, KGeom g) {
   const long long bh = blockIdx.y;
-  const int G = (g.nc + kGroup - 1) / kGroup;
+  const int G = lin_groups(g).count;
   const int f = blockIdx.x * 256 + threadIdx.x;  // < D * D
   const float* sp = ws.s_part + bh * G * (long long)D * D;
   float s = 0.f;
+#pragma unroll 8
   for (int gi = 0; gi < G; ++gi) s += sp[(long long)gi * D * D + f];
   const int d = f / D, e = f % D;
   const uint16_t hi = f32_to_bf16(s);
@@ -353,7 +395,7 @@ LinTensors lin_tensors(const KGeom& g, void* ws) {
 
 hipError_t launch_lin_prep(const KGeom& g, const uint16_t* kc, const uint16_t* vt, void* ws, hipStream_t s) {
   const LinWs w = carve(g, ws, nullptr);
-  const int G = (g.nc + kGroup - 1) / kGroup;
+  const int G = lin_groups(g).count;
   const unsigned bh = (unsigned)(g.B * g.H);
   if (g.D == 64) {
     hipLaunchKernelGGL(lin_state<64>, dim3(G, g.H, g.B), dim3(256), 0, s, kc, vt, w, g);

@@ -194,23 +194,28 @@ __device__ __forceinline__ void read_k(const uint16_t* klds, int wk, int hf, int
 // column l of the 4 rows.  Two reads give the 8 rows of one fragment.
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) i16x4* lds_i16x4_ptr;
+// One such fragment: rows row0 + 8 hf + e (row0 a multiple of 16), column
+// 32 dt + n.
+template <int D>
+__device__ __forceinline__ bf16x8 read_tr_one(const uint16_t* lds, int row0, int dt, int lane) {
+  const int s = lane & 15, grp = lane >> 4, hf = grp >> 1;
+  i16x4 part[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int r = row0 + 8 * hf + 4 * h + (s >> 2);
+    const int d = 32 * dt + 16 * (grp & 1) + 4 * (s & 3);
+    const uint16_t* p = lds + r * D + (((d >> 3) ^ kt_swz<D>(r)) << 3) + (d & 4);
+    part[h] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_ptr)(p));
+  }
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(part[0], part[1], 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
 template <int D>
 __device__ __forceinline__ void read_tr(const uint16_t* lds, int w, int lane, bf16x8 (&xa)[D / 32][2]) {
-  const int s = lane & 15, grp = lane >> 4, hf = grp >> 1;
 #pragma unroll
   for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-      i16x4 part[2];
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int r = 32 * w + 16 * kk + 8 * hf + 4 * h + (s >> 2);
-        const int d = 32 * dt + 16 * (grp & 1) + 4 * (s & 3);
-        const uint16_t* p = lds + r * D + (((d >> 3) ^ kt_swz<D>(r)) << 3) + (d & 4);
-        part[h] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_ptr)(p));
-      }
-      xa[dt][kk] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(part[0], part[1], 0, 1, 2, 3, 4, 5, 6, 7));
-    }
+    for (int kk = 0; kk < 2; ++kk) xa[dt][kk] = read_tr_one<D>(lds, 32 * w + 16 * kk, dt, lane);
 }
 
 // V^T fragments of O^T += V^T P^T for this wave's 32 keys (2 chunks of 16).

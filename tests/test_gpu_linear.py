@@ -4,8 +4,10 @@ vsa_linear_branch) and as the single fused pass (vsa_sparse_attn_linear_fwd).
 The two run the same fp32 sums in the same order; where the compiler fuses
 a multiply and an add in one kernel's combine but not in the other's, the
 fp32 results differ in the last bits, and a few outputs land on the other
-side of a bf16 rounding boundary: they agree to two bf16 steps, with at most
-one output in a thousand differing at all."""
+side of a bf16 rounding boundary.  Those last bits are relative to the two
+operands O_sparse and O_lin, not to their sum, which can cancel: the two
+outputs agree to two bf16 steps of the result plus 2^-20 (|O_sparse| +
+|O_lin|), with at most one output in a thousand differing at all."""
 
 import numpy as np
 import pytest
@@ -41,8 +43,10 @@ def run(wl, inp, idx=None):
     vt_ = torch.from_numpy(valid).to(lse.device)
     assert torch.equal(lse[:, :, vt_], lse_f[:, :, vt_]), "fused softmax branch: lse differs"
     d = np.abs(a - f)[:, :, valid]
-    step = 2.0 ** -7 * np.maximum(np.abs(a), np.abs(f))[:, :, valid] + 1e-30
-    print(f"fused vs two calls: max |d| {d.max():.3e}, bf16 steps {np.max(d / step):.2f}, "
+    o_s = of.double().cpu().numpy()
+    operands = (np.abs(o_s) + np.abs(a - o_s))[:, :, valid]
+    step = 2.0 ** -7 * np.maximum(np.abs(a), np.abs(f))[:, :, valid] + 2.0 ** -20 * operands + 1e-30
+    print(f"fused vs two calls: max |d| {d.max():.3e}, bound ratio {np.max(d / step):.2f}, "
           f"differing {np.count_nonzero(d)}/{d.size}")
     assert np.all(d <= 2 * step)
     assert np.count_nonzero(d) <= d.size // 1000 + 1
