@@ -152,6 +152,40 @@ def cpu_baseline(wl, budget_s: float):
     }
 
 
+def mfma_probe(vsa, torch, blocks=2048, iters=2000):
+    """Sustained bf16 matrix-core rate and shader clock (vsa_mfma_probe): a
+    measured denominator beside the published peak."""
+    vsa.mfma_probe(blocks, iters)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    reps = 3
+    e0.record()
+    for _ in range(reps):
+        _, clk = vsa.mfma_probe(blocks, iters)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    tflops = blocks * 4 * iters * 8 * 32768 / (ms * 1e-3) / 1e12
+    c = clk.cpu().numpy().astype(np.float64)
+    ghz = float(np.median(c[:, 0] / (c[:, 1] / 100e6))) / 1e9
+    return {"kernel": "v_mfma_f32_32x32x16_bf16, 8 independent chains per wavefront",
+            "tflops": round(tflops, 1), "frac_of_published_peak": round(tflops / PEAK_BF16_TFLOPS, 4),
+            "shader_clock_ghz": round(ghz, 3), "ms": round(ms, 4)}
+
+
+def valid_fine_flops(wl, idx, torch):
+    """Flops of the computed blocks over valid query and key tokens only
+    (4 D n_valid(i) n_valid(j) per block), from the block lists."""
+    (t, h, w), (tp, hp, wp) = wl.grid, wl.padded_grid
+    nt = np.minimum(4, t - 4 * np.arange(tp // 4))
+    ny = np.minimum(4, h - 4 * np.arange(hp // 4))
+    nx = np.minimum(4, w - 4 * np.arange(wp // 4))
+    nv = (nt[:, None, None] * ny[None, :, None] * nx[None, None, :]).reshape(-1)
+    nvt = torch.from_numpy(nv.astype(np.float64)).to(idx.device)
+    per_row = nvt[idx.long()].sum(-1) * nvt  # [B, H, Nc]
+    return float(4 * wl.head_dim * per_row.sum().item())
+
+
 def time_backward(vsa, wl, q, k, v, o, qc, kc, vt, idx, args, dev):
     """Backward of the fine stage on the layer's last forward state.
 
@@ -388,6 +422,9 @@ def main():
     flops = wl.fine_flops
     value = flops / (ms_step * 1e-3) / 1e12
     fine_tflops = flops / (fine_ms * 1e-3) / 1e12
+    step_ms = [evs[s][0].elapsed_time(evs[s][len(stages)]) for s in range(args.steps)]
+    vflops = valid_fine_flops(wl, idx, torch)
+    probe = mfma_probe(vsa, torch)
     # Algorithmic bytes of one fine-stage launch: Q, K, V read once, O written
     # once (bf16; fp8 codes are one byte, plus their scales).
     alg_bytes = 4 * B * H * d.rows * D * 2
@@ -426,6 +463,7 @@ def main():
             "computed_blocks": wl.blocks, "fine_flops": flops,
         },
         "ms_per_layer": round(ms_step, 4),
+        "step_ms_median_p10_p90": [round(float(np.percentile(step_ms, p)), 4) for p in (50, 10, 90)],
         "stage_ms_median": {kname: round(x, 4) for kname, x in stage_ms.items()},
         "fine_stage_tflops": round(fine_tflops, 2),
         "frac_of_bf16_peak_layer": round(value / PEAK_BF16_TFLOPS, 4),
@@ -439,7 +477,14 @@ def main():
             "traffic": traffic,
             "algorithmic_bytes": alg_bytes,
             "avg_launch_ms": round(fine_ms, 4),
+            **({} if args.fp8 else {"frac_of_measured_peak": round(fine_tflops / probe["tflops"], 4)}),
         },
+        "valid_tokens_only": {
+            "fine_flops": vflops,
+            "value": round(vflops / (ms_step * 1e-3) / 1e12, 3),
+            "fine_stage_tflops": round(vflops / (fine_ms * 1e-3) / 1e12, 2),
+        },
+        "mfma_probe": probe,
         "wall_s_timed": round(wall, 3),
         "device": torch.cuda.get_device_name(0),
     }

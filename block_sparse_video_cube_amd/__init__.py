@@ -52,6 +52,7 @@ __all__ = [
     "sparse_attn_fwd_fp8",
     "vsa_attention",
     "workspace_bytes",
+    "mfma_probe",
 ]
 
 
@@ -415,6 +416,21 @@ def linear_branch(qc: torch.Tensor, kc: torch.Tensor, vt: torch.Tensor, idx: tor
         g, qc.data_ptr(), kc.data_ptr(), vt.data_ptr(), idx.data_ptr(), int(topk), o_sparse.data_ptr(),
         out.data_ptr(), workspace.data_ptr(), workspace.numel() * workspace.element_size(), _stream()))
     return out
+
+
+def mfma_probe(blocks: int, iters: int, device: str = "cuda:0"):
+    """Launch the matrix-core probe (vsa_mfma_probe) on the current stream.
+
+    Returns (sink, clk): the fp32 checksums [blocks * 256] and, per workgroup,
+    the shader-clock cycles and 100 MHz ticks of its loop (int64 [blocks, 2]).
+    Each wavefront issues iters x 8 products of 32768 flops."""
+    sink = torch.empty(int(blocks) * 256, dtype=torch.float32, device=device)
+    clk = torch.empty((int(blocks), 2), dtype=torch.int64, device=device)
+    if not sink.is_cuda:
+        raise ValueError("mfma_probe: sink must be on the GPU")
+    _lib.check("vsa_mfma_probe", _lib.load().vsa_mfma_probe(int(blocks), int(iters), sink.data_ptr(),
+                                                             clk.data_ptr(), _stream()))
+    return sink, clk
 
 
 def sparse_attn_linear_fwd(qc: torch.Tensor, kc: torch.Tensor, vt: torch.Tensor, idx: torch.Tensor,

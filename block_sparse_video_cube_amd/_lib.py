@@ -48,6 +48,7 @@ ENTRY_POINTS = (
     "vsa_quant_fp8",
     "vsa_sparse_attn_fwd_fp8",
     "vsa_sparse_attn_linear_fwd",
+    "vsa_mfma_probe",
 )
 
 
@@ -123,6 +124,7 @@ def load() -> ctypes.CDLL:
         "vsa_sparse_attn_fwd_fp8": (i32, [G, P, P, P, P, P, P, P, i32, ctypes.c_float, i32, P, P, P]),
         "vsa_sparse_attn_linear_fwd": (i32, [G, P, P, P, P, i32, ctypes.c_float, P, P, P, sz, P]),
         "vsa_sparse_attn_bwd": (i32, [G, P, P, P, P, P, P, P, i32, ctypes.c_float, P, P, P, P, sz, P]),
+        "vsa_mfma_probe": (i32, [i32, i32, P, P, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)

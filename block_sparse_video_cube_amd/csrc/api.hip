@@ -324,6 +324,14 @@ int32_t vsa_sparse_attn_linear_fwd(const vsa_geom* g, const uint16_t* qc, const 
                                                 static_cast<hipStream_t>(stream)));
 }
 
+int32_t vsa_mfma_probe(int32_t blocks, int32_t iters, float* sink, uint64_t* clk, void* stream) {
+  if (!sink || !clk) return VSA_ERR_NULL;
+  if (!aligned16(sink) || !aligned16(clk)) return VSA_ERR_ALIGN;
+  if (blocks < 1 || iters < 1 || blocks > (1 << 20)) return VSA_ERR_GEOMETRY;
+  return launch_status(vsa::launch_mfma_probe(blocks, iters, sink, reinterpret_cast<unsigned long long*>(clk),
+                                              static_cast<hipStream_t>(stream)));
+}
+
 int32_t vsa_linear_branch(const vsa_geom* g, const uint16_t* qc, const uint16_t* kc, const uint16_t* vt,
                           const int32_t* idx, int32_t topk, const float* o_sparse, uint16_t* oc, void* ws,
                           size_t ws_bytes, void* stream) {

@@ -303,6 +303,18 @@ int32_t vsa_sparse_attn_linear_fwd(const vsa_geom* g, const uint16_t* qc, const 
                                    float softmax_scale, uint16_t* oc, float* lse, void* ws,
                                    size_t ws_bytes, void* stream);
 
+/* Matrix-core probe (measurement support, not part of the attention path):
+ * the sustained rate of the bf16 matrix cores on this device, a measured
+ * denominator beside the published bf16 peak, and the shader clock during it.
+ * Launches `blocks` workgroups of 256 threads on `stream`; every wavefront
+ * issues iters x 8 independent 32x32x16 bf16 products (32768 flops each) on
+ * register operands.  sink: device fp32 [blocks * 256], overwritten with
+ * checksums; clk: device uint64 [2 * blocks], per workgroup the shader-clock
+ * cycles and the 100 MHz counter ticks its first wavefront spent in the loop.
+ * Errors: VSA_ERR_NULL, VSA_ERR_ALIGN, VSA_ERR_GEOMETRY (blocks or iters < 1,
+ * blocks > 2^20), VSA_ERR_LAUNCH. */
+int32_t vsa_mfma_probe(int32_t blocks, int32_t iters, float* sink, uint64_t* clk, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -247,3 +247,15 @@ def test_fused_linear_entry_point_validation(lib):
     assert f(g, P, P, P, P, 2, float("nan"), P, None, P, ws, None) == _lib.VSA_ERR_SCALE
     assert f(g, P, P, P, P, 2, 0.125, P, None, P, ws - 1, None) == _lib.VSA_ERR_WORKSPACE
     assert f(geom(D=32), P, P, P, P, 2, 0.125, P, None, P, ws, None) == _lib.VSA_ERR_HEAD_DIM
+
+
+def test_mfma_probe_validation(lib):
+    from block_sparse_video_cube_amd import _lib
+
+    P = FAKE
+    assert lib.vsa_mfma_probe(8, 10, None, P, None) == _lib.VSA_ERR_NULL
+    assert lib.vsa_mfma_probe(8, 10, P, None, None) == _lib.VSA_ERR_NULL
+    assert lib.vsa_mfma_probe(8, 10, ODD, P, None) == _lib.VSA_ERR_ALIGN
+    assert lib.vsa_mfma_probe(0, 10, P, P, None) == _lib.VSA_ERR_GEOMETRY
+    assert lib.vsa_mfma_probe(8, 0, P, P, None) == _lib.VSA_ERR_GEOMETRY
+    assert lib.vsa_mfma_probe((1 << 20) + 1, 10, P, P, None) == _lib.VSA_ERR_GEOMETRY
