@@ -105,6 +105,8 @@ __all__ = [
     "attention_cube_bwd",
     "sparse_attention_bwd",
     "backward",
+    "phi_grad",
+    "linear_branch_bwd",
 ]
 
 
@@ -467,6 +469,73 @@ def backward(q, k, v, do, grid: Sequence[int], idx: np.ndarray, scale: Optional[
     doc = cube_permute(do, grid)
     dq, dk, dv = sparse_attention_bwd(qc, kc, vc, valid, idx, scale, doc)
     return cube_unpermute(dq, grid), cube_unpermute(dk, grid), cube_unpermute(dv, grid)
+
+
+# --------------------------------------------------------------------------
+# O11: backward of the linear branch
+# --------------------------------------------------------------------------
+
+def phi_grad(x: np.ndarray) -> np.ndarray:
+    """d phi / dx: 1 for x > 0, exp(x) otherwise."""
+    x = np.asarray(x, dtype=np.float64)
+    return np.where(x > 0, 1.0, np.exp(np.minimum(x, 0.0)))
+
+
+def linear_branch_bwd(qc, kc, vc, valid, idx, doc, heads: Optional[Sequence[Tuple[int, int]]] = None):
+    """dQ, dK, dV [B, H, Np, D] f64 of O_lin (O6) for the output gradient doc.
+
+    The chain rule through the steps of O6, per query cube i with unselected
+    set U (nothing when U is empty, where O_lin is the constant 0):
+      num = phi(Q_i) S_U, den = phi(Q_i) . z_U, O = num / den;
+      dnum = dO / den, dden = -(dO . O) / den;
+      d phi(Q_i) = dnum S_U^T + dden z_U^T, dS_U = phi(Q_i)^T dnum, dz_U = phi(Q_i)^T dden,
+    and dS_U, dz_U flow to every key cube j of U.  Per key cube j,
+    S_j = sum_r phi(k_r)^T v_r and z_j = sum_r phi(k_r) over its valid rows r give
+      d phi(k_r) = dS_j v_r + dz_j, dv_r = dS_j^T phi(k_r).
+    Finally dQ = d phi(Q) * phi'(Q), dK = d phi(K) * phi'(K); padded rows get
+    none.  heads: optional list of (b, h) to compute (others stay NaN).
+    """
+    B, Hh, Np, D = qc.shape
+    nc = Np // 64
+    dq = np.full((B, Hh, Np, D), np.nan)
+    dk = np.full((B, Hh, Np, D), np.nan)
+    dv = np.full((B, Hh, Np, D), np.nan)
+    todo = heads if heads is not None else [(b, h) for b in range(B) for h in range(Hh)]
+    vmask = valid[:, None].astype(np.float64)
+    for b, h in todo:
+        S, z = _cube_states(kc[b, h], vc[b, h], valid)
+        dS = np.zeros_like(S)
+        dz = np.zeros_like(z)
+        dq[b, h] = 0.0
+        for i in range(nc):
+            sel = set(int(j) for j in idx[b, h, i])
+            unsel = [j for j in range(nc) if j not in sel]
+            if not unsel:
+                continue
+            rows = slice(64 * i, 64 * i + 64)
+            xq = _as_f64(qc[b, h, rows])
+            fq = phi(xq)
+            S_u = S[unsel].sum(axis=0)
+            z_u = z[unsel].sum(axis=0)
+            num = fq @ S_u
+            den = fq @ z_u
+            o = num / den[:, None]
+            g = _as_f64(doc[b, h, rows]) * vmask[rows]
+            dnum = g / den[:, None]
+            dden = -(g * o).sum(axis=1) / den
+            dfq = dnum @ S_u.T + dden[:, None] * z_u[None, :]
+            dq[b, h, rows] = dfq * phi_grad(xq) * vmask[rows]
+            dS[unsel] += fq.T @ dnum
+            dz[unsel] += fq.T @ dden
+        xk = _as_f64(kc[b, h])
+        fk = phi(xk)
+        vv = _as_f64(vc[b, h])
+        for j in range(nc):
+            rows = slice(64 * j, 64 * j + 64)
+            dfk = vv[rows] @ dS[j].T + dz[j][None, :]
+            dk[b, h, rows] = dfk * phi_grad(xk[rows]) * vmask[rows]
+            dv[b, h, rows] = (fk[rows] @ dS[j]) * vmask[rows]
+    return dq, dk, dv
 
 
 # --------------------------------------------------------------------------
