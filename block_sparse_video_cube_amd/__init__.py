@@ -53,6 +53,7 @@ __all__ = [
     "vsa_attention",
     "workspace_bytes",
     "mfma_probe",
+    "linear_branch_bwd",
 ]
 
 
@@ -416,6 +417,32 @@ def linear_branch(qc: torch.Tensor, kc: torch.Tensor, vt: torch.Tensor, idx: tor
         g, qc.data_ptr(), kc.data_ptr(), vt.data_ptr(), idx.data_ptr(), int(topk), o_sparse.data_ptr(),
         out.data_ptr(), workspace.data_ptr(), workspace.numel() * workspace.element_size(), _stream()))
     return out
+
+
+def linear_branch_bwd(qc: torch.Tensor, kc: torch.Tensor, vc: torch.Tensor, vt: torch.Tensor, idx: torch.Tensor,
+                      doc: torch.Tensor, grid: Sequence[int], workspace: Optional[torch.Tensor] = None):
+    """Gradients of the linear branch alone.  Returns (dq, dk, dv), bf16 [B, heads, Np, D] token-major.
+
+    qc, kc, vc, doc: Q, K, V and dO token-major; vt: V DIM_MAJOR; idx: the block lists.
+    """
+    B, Hh, Np, D = qc.shape
+    g = make_geom(B, Hh, D, grid)
+    d = geom_dims(g)
+    topk = int(idx.shape[-1])
+    for t, name in ((qc, "qc"), (kc, "kc"), (vc, "vc"), (doc, "doc")):
+        _need(t, name, torch.bfloat16, (B, Hh, d.rows, D))
+    _need(vt, "vt", torch.bfloat16, (B, Hh, d.n_cubes, D, 64))
+    _need(idx, "idx", torch.int32, (B, Hh, d.n_cubes, topk))
+    lib = _lib.load()
+    nbytes = lib.vsa_linear_bwd_workspace_bytes(g, topk)
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=qc.device)
+    dq, dk, dv = (torch.empty_like(qc) for _ in range(3))
+    _lib.check("vsa_linear_branch_bwd", lib.vsa_linear_branch_bwd(
+        g, qc.data_ptr(), kc.data_ptr(), vc.data_ptr(), vt.data_ptr(), idx.data_ptr(), topk, doc.data_ptr(),
+        dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), workspace.data_ptr(),
+        workspace.numel() * workspace.element_size(), _stream()))
+    return dq, dk, dv
 
 
 def mfma_probe(blocks: int, iters: int, device: str = "cuda:0"):

@@ -324,6 +324,32 @@ int32_t vsa_sparse_attn_linear_fwd(const vsa_geom* g, const uint16_t* qc, const 
                                                 static_cast<hipStream_t>(stream)));
 }
 
+size_t vsa_linear_bwd_workspace_bytes(const vsa_geom* g, int32_t topk) {
+  vsa_dims d;
+  vsa::KGeom k;
+  if (prepare(g, &d, &k) != VSA_OK || topk < 1 || topk > d.n_cubes) return 0;
+  return vsa::linear_bwd_workspace_bytes(k, topk);
+}
+
+int32_t vsa_linear_branch_bwd(const vsa_geom* g, const uint16_t* qc, const uint16_t* kc, const uint16_t* vc,
+                              const uint16_t* vt, const int32_t* idx, int32_t topk, const uint16_t* doc,
+                              uint16_t* dq, uint16_t* dk, uint16_t* dv, void* ws, size_t ws_bytes, void* stream) {
+  vsa_dims d;
+  vsa::KGeom k;
+  int32_t st = prepare(g, &d, &k);
+  if (st != VSA_OK) return st;
+  if (d.n_cubes > VSA_MAX_CUBES) return VSA_ERR_GEOMETRY;
+  const void* ptrs[] = {qc, kc, vc, vt, idx, doc, dq, dk, dv, ws};
+  for (const void* p : ptrs)
+    if (!p) return VSA_ERR_NULL;
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return VSA_ERR_ALIGN;
+  if (topk < 1 || topk > d.n_cubes) return VSA_ERR_TOPK;
+  if (ws_bytes < vsa::linear_bwd_workspace_bytes(k, topk)) return VSA_ERR_WORKSPACE;
+  return launch_status(vsa::launch_linear_bwd(k, qc, kc, vc, vt, idx, topk, doc, dq, dk, dv, ws,
+                                              static_cast<hipStream_t>(stream)));
+}
+
 int32_t vsa_mfma_probe(int32_t blocks, int32_t iters, float* sink, uint64_t* clk, void* stream) {
   if (!sink || !clk) return VSA_ERR_NULL;
   if (!aligned16(sink) || !aligned16(clk)) return VSA_ERR_ALIGN;

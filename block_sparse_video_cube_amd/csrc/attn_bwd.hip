@@ -492,6 +492,15 @@ hipError_t launch_bwd_t(const KGeom& g, const uint16_t* qc, const uint16_t* kc, 
 
 }  // namespace
 
+hipError_t launch_block_lists_t(const KGeom& g, const int32_t* idx, int topk, int32_t* cnt, int32_t* off,
+                                int32_t* list, hipStream_t s) {
+  const dim3 tgrid((g.nc + 3) / 4, g.B * g.H);
+  bwd_count<<<tgrid, dim3(256), 0, s>>>(idx, topk, cnt, g);
+  bwd_scan<<<dim3(g.B * g.H), dim3(256), 0, s>>>(cnt, off, g);
+  bwd_fill<<<tgrid, dim3(256), 0, s>>>(idx, topk, off, list, g);
+  return hipGetLastError();
+}
+
 size_t attn_bwd_workspace_bytes(const KGeom& g, int topk) {
   const size_t bh = (size_t)g.B * g.H;
   return align256(bh * g.Np * sizeof(float)) + 2 * align256(bh * g.nc * sizeof(int32_t)) +

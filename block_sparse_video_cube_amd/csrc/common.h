@@ -109,6 +109,32 @@ struct LinTensors {
   const float* z_tot;
 };
 LinTensors lin_tensors(const KGeom& g, void* ws);
+// Per-row inputs of the linear branch's backward, written by the forward's
+// selected-block pass in its backward mode (all token-major [B, H, Np, ...]).
+struct LinBwdRows {
+  const uint16_t* doc;  // dO, bf16
+  uint16_t* w;          // dO / den, bf16
+  float* c;             // (dO . O_lin) / den, fp32 [B, H, Np]
+  uint16_t* fq;         // phi(Q), bf16
+};
+hipError_t launch_lin_bwd_rows(const KGeom& g, const uint16_t* qc, const uint16_t* vt, const int32_t* idx, int topk,
+                               const LinBwdRows& br, void* ws, hipStream_t s);
+// The parts of the linear workspace the backward reuses: phi(K), the group
+// partials of the state (reused for the backward's own state), z_tot.
+struct LinState {
+  const uint16_t* fk;
+  float* s_part;  // [B, H, count, D, D]
+  float* z_part;  // [B, H, count, D]
+  const float* z_tot;
+  int group_size, group_count;
+};
+LinState lin_state_parts(const KGeom& g, void* ws);
+hipError_t launch_block_lists_t(const KGeom& g, const int32_t* idx, int topk, int32_t* cnt, int32_t* off,
+                                int32_t* list, hipStream_t s);
+size_t linear_bwd_workspace_bytes(const KGeom& g, int topk);
+hipError_t launch_linear_bwd(const KGeom& g, const uint16_t* qc, const uint16_t* kc, const uint16_t* vc,
+                             const uint16_t* vt, const int32_t* idx, int topk, const uint16_t* doc, uint16_t* dq,
+                             uint16_t* dk, uint16_t* dv, void* ws, hipStream_t s);
 hipError_t launch_lin_prep(const KGeom& g, const uint16_t* kc, const uint16_t* vt, void* ws, hipStream_t s);
 hipError_t launch_attn_lin_fwd(const KGeom& g, const uint16_t* qc, const uint16_t* kc, const uint16_t* vt,
                                const int32_t* idx, int topk, float scale, void* ws, uint16_t* oc, float* lse,

@@ -228,13 +228,17 @@ struct LinSmem {
 // V^T A^T.  The total part phi(Q) S_tot is split between the two key halves
 // (bf16 hi half on wk = 0, lo half on wk = 1) so that the merge through LDS
 // adds num - corr directly.
-template <int D>
+//
+// BWD: instead of the combine, the per-row inputs of the linear branch's
+// backward: w = dO / den (bf16), c = (dO . O_lin) / den (fp32) and phi(Q)
+// (bf16), zero on padded query rows and when no cube is left unselected.
+template <int D, bool BWD>
 __global__ void __launch_bounds__(kThreads, 2) lin_apply(const uint16_t* __restrict__ qc,
                                                          const uint16_t* __restrict__ vt,
                                                          const int32_t* __restrict__ idx, int topk,
                                                          const float* __restrict__ o_sparse,
                                                          uint16_t* __restrict__ oc, LinWs ws, KGeom g,
-                                                         Placement pl) {
+                                                         Placement pl, LinBwdRows br) {
   constexpr int DC = D / 16, DT = D / 32;
   __shared__ __attribute__((aligned(16))) LinSmem<D> sm;
   int i, h, b;
@@ -361,6 +365,43 @@ __global__ void __launch_bounds__(kThreads, 2) lin_apply(const uint16_t* __restr
   if (wk == 1) return;
   const float den = (den_part + __shfl_xor(den_part, 32)) - (dcorr + xd[lane]);
   const float inv = empty_u ? 0.f : 1.f / den;
+  if (BWD) {
+    int ct, cy, cx;
+    cube_coords(g, i, ct, cy, cx);
+    const float inv_b = local_valid(g, ct, cy, cx, q) ? inv : 0.f;
+    const uint16_t* dsrc = br.doc + row * D;
+    uint16_t* wdst = br.w + row * D;
+    float cp = 0.f;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int gq = 0; gq < 4; ++gq) {
+        const int e = 32 * dt + 8 * gq + 4 * hf;
+        const uint2 draw = *reinterpret_cast<const uint2*>(dsrc + e);
+        const float dov[4] = {__uint_as_float(draw.x << 16), __uint_as_float(draw.x & 0xFFFF0000u),
+                              __uint_as_float(draw.y << 16), __uint_as_float(draw.y & 0xFFFF0000u)};
+        // c is taken from the same bf16-rounded w that the backward's
+        // products use, so that S_U w and c z_U, which nearly cancel, carry
+        // the same rounding.
+        const uint2 wbits = make_uint2(pack_bf16x2(dov[0] * inv_b, dov[1] * inv_b),
+                                       pack_bf16x2(dov[2] * inv_b, dov[3] * inv_b));
+        const float wr[4] = {__uint_as_float(wbits.x << 16), __uint_as_float(wbits.x & 0xFFFF0000u),
+                             __uint_as_float(wbits.y << 16), __uint_as_float(wbits.y & 0xFFFF0000u)};
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int r = 4 * gq + u;
+          const float olin = (c[dt][r] + xo[(dt * 16 + r) * 64 + lane]) * inv;
+          cp = fmaf(wr[u], olin, cp);
+        }
+        *reinterpret_cast<uint2*>(wdst + e) = wbits;
+      }
+    cp += __shfl_xor(cp, 32);
+    if (hf == 0) br.c[row] = cp;
+#pragma unroll
+    for (int dc = 0; dc < DC; ++dc)
+      *reinterpret_cast<bf16x8*>(br.fq + row * D + 16 * dc + 8 * hf) = inv_b != 0.f ? fq[dc] : bf16x8{};
+    return;
+  }
   const float* osrc = o_sparse + row * D;
   uint16_t* odst = oc + row * D;
 #pragma unroll
@@ -413,13 +454,32 @@ hipError_t launch_linear(const KGeom& g, const uint16_t* qc, const uint16_t* kc,
   hipError_t e = launch_lin_prep(g, kc, vt, ws, s);
   if (e != hipSuccess) return e;
   const LinWs w = carve(g, ws, nullptr);
+  const LinBwdRows none{};
   if (g.D == 64)
-    hipLaunchKernelGGL(lin_apply<64>, dim3(grid_size(g)), dim3(kThreads), 0, s, qc, vt, idx, topk, o_sparse, oc,
-                       w, g, make_placement(g));
+    hipLaunchKernelGGL((lin_apply<64, false>), dim3(grid_size(g)), dim3(kThreads), 0, s, qc, vt, idx, topk,
+                       o_sparse, oc, w, g, make_placement(g), none);
   else
-    hipLaunchKernelGGL(lin_apply<128>, dim3(grid_size(g)), dim3(kThreads), 0, s, qc, vt, idx, topk, o_sparse, oc,
-                       w, g, make_placement(g));
+    hipLaunchKernelGGL((lin_apply<128, false>), dim3(grid_size(g)), dim3(kThreads), 0, s, qc, vt, idx, topk,
+                       o_sparse, oc, w, g, make_placement(g), none);
   return hipGetLastError();
+}
+
+hipError_t launch_lin_bwd_rows(const KGeom& g, const uint16_t* qc, const uint16_t* vt, const int32_t* idx, int topk,
+                               const LinBwdRows& br, void* ws, hipStream_t s) {
+  const LinWs w = carve(g, ws, nullptr);
+  if (g.D == 64)
+    hipLaunchKernelGGL((lin_apply<64, true>), dim3(grid_size(g)), dim3(kThreads), 0, s, qc, vt, idx, topk, nullptr,
+                       nullptr, w, g, make_placement(g), br);
+  else
+    hipLaunchKernelGGL((lin_apply<128, true>), dim3(grid_size(g)), dim3(kThreads), 0, s, qc, vt, idx, topk,
+                       nullptr, nullptr, w, g, make_placement(g), br);
+  return hipGetLastError();
+}
+
+LinState lin_state_parts(const KGeom& g, void* ws) {
+  const LinWs w = carve(g, ws, nullptr);
+  const LinGroups lg = lin_groups(g);
+  return LinState{w.fk, w.s_part, w.z_part, w.z_tot, lg.size, lg.count};
 }
 
 }  // namespace vsa

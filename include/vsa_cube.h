@@ -303,6 +303,29 @@ int32_t vsa_sparse_attn_linear_fwd(const vsa_geom* g, const uint16_t* qc, const 
                                    float softmax_scale, uint16_t* oc, float* lse, void* ws,
                                    size_t ws_bytes, void* stream);
 
+/* Backward of the linear branch (the branch is trained with the sparse one:
+ * TurboDiffusion article, section "稀疏、蒸馏与全链路量化"; SparkDiffusion
+ * article, paragraph 3): the gradients of O_lin alone, to be added to those
+ * of the fine stage (vsa_sparse_attn_bwd) for the hybrid layer.  With
+ * w = dO / den and c = (dO . O_lin) / den per query row (O_lin and den
+ * recomputed as in vsa_linear_branch), over the unselected key rows r of a
+ * query row q:
+ *   dQ_q = (sum_r (w_q . v_r - c_q) phi(k_r)) * phi'(q),
+ *   dK_r = (sum_q (w_q . v_r - c_q) phi(q)) * phi'(k_r),
+ *   dV_r = sum_q (phi(q) . phi(k_r)) w_q,
+ * phi'(x) = 1 for x > 0, e^x otherwise.  No gradient when every cube is
+ * selected (O_lin is then the constant 0).
+ * Inputs: qc, kc, vc, doc TOKEN_MAJOR bf16 (doc: dO, padded rows zero); vt
+ * DIM_MAJOR bf16 (V); idx, topk as for vsa_linear_branch.  Outputs: dq, dk,
+ * dv bf16 TOKEN_MAJOR, padded rows zero.  ws: at least
+ * vsa_linear_bwd_workspace_bytes(g, topk) bytes (it holds the forward's
+ * linear workspace too).  n_cubes <= VSA_MAX_CUBES.  No atomics. */
+size_t vsa_linear_bwd_workspace_bytes(const vsa_geom* g, int32_t topk);
+int32_t vsa_linear_branch_bwd(const vsa_geom* g, const uint16_t* qc, const uint16_t* kc,
+                              const uint16_t* vc, const uint16_t* vt, const int32_t* idx,
+                              int32_t topk, const uint16_t* doc, uint16_t* dq, uint16_t* dk,
+                              uint16_t* dv, void* ws, size_t ws_bytes, void* stream);
+
 /* Matrix-core probe (measurement support, not part of the attention path):
  * the sustained rate of the bf16 matrix cores on this device, a measured
  * denominator beside the published bf16 peak, and the shader clock during it.

@@ -259,3 +259,23 @@ def test_mfma_probe_validation(lib):
     assert lib.vsa_mfma_probe(0, 10, P, P, None) == _lib.VSA_ERR_GEOMETRY
     assert lib.vsa_mfma_probe(8, 0, P, P, None) == _lib.VSA_ERR_GEOMETRY
     assert lib.vsa_mfma_probe((1 << 20) + 1, 10, P, P, None) == _lib.VSA_ERR_GEOMETRY
+
+
+def test_linear_backward_entry_point_validation(lib):
+    from block_sparse_video_cube_amd import _lib
+
+    g = geom()
+    P = FAKE
+    ws = lib.vsa_linear_bwd_workspace_bytes(g, 2)
+    assert ws >= lib.vsa_linear_workspace_bytes(g)
+    assert lib.vsa_linear_bwd_workspace_bytes(g, 0) == 0
+    assert lib.vsa_linear_bwd_workspace_bytes(g, 9) == 0
+    ins = [P] * 5  # qc kc vc vt idx
+    outs = [P] * 3
+    assert lib.vsa_linear_branch_bwd(g, *ins, 2, None, *outs, P, ws, None) == _lib.VSA_ERR_NULL
+    assert lib.vsa_linear_branch_bwd(g, *ins, 2, P, P, P, None, P, ws, None) == _lib.VSA_ERR_NULL
+    assert lib.vsa_linear_branch_bwd(g, ODD, *ins[1:], 2, P, *outs, P, ws, None) == _lib.VSA_ERR_ALIGN
+    assert lib.vsa_linear_branch_bwd(g, *ins, 0, P, *outs, P, ws, None) == _lib.VSA_ERR_TOPK
+    assert lib.vsa_linear_branch_bwd(g, *ins, 9, P, *outs, P, ws, None) == _lib.VSA_ERR_TOPK
+    assert lib.vsa_linear_branch_bwd(g, *ins, 2, P, *outs, P, ws - 1, None) == _lib.VSA_ERR_WORKSPACE
+    assert lib.vsa_linear_branch_bwd(geom(D=48), *ins, 2, P, *outs, P, ws, None) == _lib.VSA_ERR_HEAD_DIM

@@ -52,12 +52,13 @@ def calls(vsa):
         "quant_fp8": lambda: vsa.quant_fp8(x, x, x, GRID),
         "sparse_attn_fwd_fp8": lambda: vsa.sparse_attn_fwd_fp8(u8, sc, u8, sc, v8t, vs, idx, GRID),
         "sparse_attn_bwd": lambda: vsa.sparse_attn_bwd(qc, qc, qc, qc, qc, lse, idx, GRID),
+        "linear_branch_bwd": lambda: vsa.linear_branch_bwd(qc, qc, qc, vt, idx, qc, GRID),
     }
 
 
 NAMES = ["cube_permute", "cube_permute_pool", "cube_pool", "cube_unpermute", "select_topk", "select_topk_pooled",
          "sparse_attn_fwd", "sparse_attn_fwd_raster", "sparse_attn_linear_fwd", "quant_fp8", "sparse_attn_fwd_fp8",
-         "sparse_attn_bwd"]
+         "sparse_attn_bwd", "linear_branch_bwd"]
 
 
 @pytest.mark.parametrize("name", NAMES)
