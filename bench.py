@@ -243,6 +243,23 @@ def time_backward(vsa, wl, q, k, v, o, qc, kc, vt, idx, args, dev):
     unp = float(np.median([e[2].elapsed_time(e[3]) for e in evs]))
     finite = all(bool(torch.isfinite(x.float()).all()) for x in outs)
     flops = 2.5 * wl.fine_flops
+    lin = None
+    if wl.linear:
+        # The linear branch's own gradients (recomputing its forward state).
+        vc, doc = layouts()
+        wsl = torch.empty(max(16, vsa._lib.load().vsa_linear_bwd_workspace_bytes(
+            vsa.make_geom(B, H, D, wl.grid), wl.topk)), dtype=torch.uint8, device=dev)
+        for _ in range(max(1, args.warmup)):
+            vsa.linear_branch_bwd(qc, kc, vc, vt, idx, doc, wl.grid, workspace=wsl)
+        torch.cuda.synchronize()
+        l0, l1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        l0.record()
+        for _ in range(args.steps):
+            lo = vsa.linear_branch_bwd(qc, kc, vc, vt, idx, doc, wl.grid, workspace=wsl)
+        l1.record()
+        torch.cuda.synchronize()
+        lin = {"ms": round(l0.elapsed_time(l1) / args.steps, 4),
+               "finite": all(bool(torch.isfinite(x.float()).all()) for x in lo)}
     return {
         "ms_per_layer": round(ms, 4),
         "stage_ms": {"layouts": round(lay, 4), "bwd_kernels": round(kern, 4), "unpermute": round(unp, 4)},
@@ -250,6 +267,7 @@ def time_backward(vsa, wl, q, k, v, o, qc, kc, vt, idx, args, dev):
         "frac_of_bf16_peak": round(flops / (kern * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
         "flops": flops,
         "finite": finite,
+        **({"linear_branch_bwd": lin} if lin is not None else {}),
     }
 
 
