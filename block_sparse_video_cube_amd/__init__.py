@@ -420,10 +420,13 @@ def linear_branch(qc: torch.Tensor, kc: torch.Tensor, vt: torch.Tensor, idx: tor
 
 
 def linear_branch_bwd(qc: torch.Tensor, kc: torch.Tensor, vc: torch.Tensor, vt: torch.Tensor, idx: torch.Tensor,
-                      doc: torch.Tensor, grid: Sequence[int], workspace: Optional[torch.Tensor] = None):
-    """Gradients of the linear branch alone.  Returns (dq, dk, dv), bf16 [B, heads, Np, D] token-major.
+                      doc: torch.Tensor, grid: Sequence[int], workspace: Optional[torch.Tensor] = None,
+                      add: Optional[Tuple[torch.Tensor, torch.Tensor, torch.Tensor]] = None, out=None):
+    """Gradients of the linear branch.  Returns (dq, dk, dv), bf16 [B, heads, Np, D] token-major.
 
     qc, kc, vc, doc: Q, K, V and dO token-major; vt: V DIM_MAJOR; idx: the block lists.
+    add: optional (dq, dk, dv) added before the one bf16 rounding (the fine stage's, for the
+    hybrid layer); out: optional output tensors (may be the addends themselves).
     """
     B, Hh, Np, D = qc.shape
     g = make_geom(B, Hh, D, grid)
@@ -433,14 +436,20 @@ def linear_branch_bwd(qc: torch.Tensor, kc: torch.Tensor, vc: torch.Tensor, vt: 
         _need(t, name, torch.bfloat16, (B, Hh, d.rows, D))
     _need(vt, "vt", torch.bfloat16, (B, Hh, d.n_cubes, D, 64))
     _need(idx, "idx", torch.int32, (B, Hh, d.n_cubes, topk))
+    if add is not None:
+        for t, name in zip(add, ("dq_add", "dk_add", "dv_add")):
+            _need(t, name, torch.bfloat16, (B, Hh, d.rows, D))
     lib = _lib.load()
     nbytes = lib.vsa_linear_bwd_workspace_bytes(g, topk)
     if workspace is None:
         workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=qc.device)
-    dq, dk, dv = (torch.empty_like(qc) for _ in range(3))
+    dq, dk, dv = out if out is not None else (torch.empty_like(qc) for _ in range(3))
+    for t, name in ((dq, "dq"), (dk, "dk"), (dv, "dv")):
+        _need(t, name, torch.bfloat16, (B, Hh, d.rows, D))
+    adds = [t.data_ptr() for t in add] if add is not None else [None, None, None]
     _lib.check("vsa_linear_branch_bwd", lib.vsa_linear_branch_bwd(
         g, qc.data_ptr(), kc.data_ptr(), vc.data_ptr(), vt.data_ptr(), idx.data_ptr(), topk, doc.data_ptr(),
-        dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), workspace.data_ptr(),
+        *adds, dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), workspace.data_ptr(),
         workspace.numel() * workspace.element_size(), _stream()))
     return dq, dk, dv
 
@@ -488,12 +497,54 @@ def sparse_attn_linear_fwd(qc: torch.Tensor, kc: torch.Tensor, vt: torch.Tensor,
     return out, lse
 
 
+class _VsaAttention(torch.autograd.Function):
+    """The layer as one autograd node: the forward's kernels, and in backward
+    vsa_sparse_attn_bwd (plus vsa_linear_branch_bwd with the fine stage's
+    gradients as addends for the hybrid layer) and the unpermutes."""
+
+    @staticmethod
+    def forward(ctx, q, k, v, grid, topk, scale, linear, idx):
+        qc, qbar = cube_permute_pool(q, grid)
+        kc, kbar = cube_permute_pool(k, grid)
+        vt = cube_permute(v, grid, layout="dim")
+        if idx is None:
+            idx = select_topk_pooled(qbar, kbar, grid, topk)
+        if linear:
+            oc_s, of, lse = sparse_attn_fwd(qc, kc, vt, idx, grid, scale, want_f32=True, want_lse=True)
+            oc = linear_branch(qc, kc, vt, idx, of, grid)
+        else:
+            oc_s, _, lse = sparse_attn_fwd(qc, kc, vt, idx, grid, scale, want_lse=True)
+            oc = oc_s
+        ctx.save_for_backward(qc, kc, vt, v, oc_s, lse, idx)
+        ctx.grid, ctx.scale, ctx.linear = tuple(grid), scale, linear
+        ctx.mark_non_differentiable(idx)
+        return cube_unpermute(oc, grid), idx
+
+    @staticmethod
+    def backward(ctx, do, _unused):
+        qc, kc, vt, v, oc_s, lse, idx = ctx.saved_tensors
+        grid = ctx.grid
+        doc = cube_permute(do.contiguous(), grid)
+        vc = cube_permute(v, grid)
+        dq, dk, dv = sparse_attn_bwd(qc, kc, vc, oc_s, doc, lse, idx, grid, ctx.scale)
+        if ctx.linear:
+            dq, dk, dv = linear_branch_bwd(qc, kc, vc, vt, idx, doc, grid, add=(dq, dk, dv), out=(dq, dk, dv))
+        return (cube_unpermute(dq, grid), cube_unpermute(dk, grid), cube_unpermute(dv, grid),
+                None, None, None, None, None)
+
+
 def vsa_attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, grid: Sequence[int], topk: int,
                   scale: Optional[float] = None, linear: bool = False, idx: Optional[torch.Tensor] = None):
     """One attention layer: [B, S, heads, D] bf16 -> (o [B, S, heads, D] bf16, idx).
 
-    idx: optional block list to use instead of the coarse-stage selection.
+    idx: optional block list to use instead of the coarse-stage selection.  When
+    gradients are enabled and q, k or v requires them, the layer is one
+    autograd node whose backward runs the library's backward kernels.
     """
+    if scale is None:
+        scale = 1.0 / math.sqrt(q.shape[-1])
+    if torch.is_grad_enabled() and (q.requires_grad or k.requires_grad or v.requires_grad):
+        return _VsaAttention.apply(q, k, v, grid, topk, scale, linear, idx)
     qc, qbar = cube_permute_pool(q, grid)
     kc, kbar = cube_permute_pool(k, grid)
     vt = cube_permute(v, grid, layout="dim")

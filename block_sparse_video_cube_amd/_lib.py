@@ -128,7 +128,7 @@ def load() -> ctypes.CDLL:
         "vsa_sparse_attn_bwd": (i32, [G, P, P, P, P, P, P, P, i32, ctypes.c_float, P, P, P, P, sz, P]),
         "vsa_mfma_probe": (i32, [i32, i32, P, P, P]),
         "vsa_linear_bwd_workspace_bytes": (sz, [G, i32]),
-        "vsa_linear_branch_bwd": (i32, [G, P, P, P, P, P, i32, P, P, P, P, P, sz, P]),
+        "vsa_linear_branch_bwd": (i32, [G, P, P, P, P, P, i32, P, P, P, P, P, P, P, P, sz, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)

@@ -333,7 +333,8 @@ size_t vsa_linear_bwd_workspace_bytes(const vsa_geom* g, int32_t topk) {
 
 int32_t vsa_linear_branch_bwd(const vsa_geom* g, const uint16_t* qc, const uint16_t* kc, const uint16_t* vc,
                               const uint16_t* vt, const int32_t* idx, int32_t topk, const uint16_t* doc,
-                              uint16_t* dq, uint16_t* dk, uint16_t* dv, void* ws, size_t ws_bytes, void* stream) {
+                              const uint16_t* dq_add, const uint16_t* dk_add, const uint16_t* dv_add, uint16_t* dq,
+                              uint16_t* dk, uint16_t* dv, void* ws, size_t ws_bytes, void* stream) {
   vsa_dims d;
   vsa::KGeom k;
   int32_t st = prepare(g, &d, &k);
@@ -344,10 +345,12 @@ int32_t vsa_linear_branch_bwd(const vsa_geom* g, const uint16_t* qc, const uint1
     if (!p) return VSA_ERR_NULL;
   for (const void* p : ptrs)
     if (!aligned16(p)) return VSA_ERR_ALIGN;
+  if ((dq_add && !aligned16(dq_add)) || (dk_add && !aligned16(dk_add)) || (dv_add && !aligned16(dv_add)))
+    return VSA_ERR_ALIGN;
   if (topk < 1 || topk > d.n_cubes) return VSA_ERR_TOPK;
   if (ws_bytes < vsa::linear_bwd_workspace_bytes(k, topk)) return VSA_ERR_WORKSPACE;
-  return launch_status(vsa::launch_linear_bwd(k, qc, kc, vc, vt, idx, topk, doc, dq, dk, dv, ws,
-                                              static_cast<hipStream_t>(stream)));
+  return launch_status(vsa::launch_linear_bwd(k, qc, kc, vc, vt, idx, topk, doc, dq_add, dk_add, dv_add, dq, dk, dv,
+                                              ws, static_cast<hipStream_t>(stream)));
 }
 
 int32_t vsa_mfma_probe(int32_t blocks, int32_t iters, float* sink, uint64_t* clk, void* stream) {

@@ -133,7 +133,8 @@ hipError_t launch_block_lists_t(const KGeom& g, const int32_t* idx, int topk, in
                                 int32_t* list, hipStream_t s);
 size_t linear_bwd_workspace_bytes(const KGeom& g, int topk);
 hipError_t launch_linear_bwd(const KGeom& g, const uint16_t* qc, const uint16_t* kc, const uint16_t* vc,
-                             const uint16_t* vt, const int32_t* idx, int topk, const uint16_t* doc, uint16_t* dq,
+                             const uint16_t* vt, const int32_t* idx, int topk, const uint16_t* doc,
+                             const uint16_t* dq_add, const uint16_t* dk_add, const uint16_t* dv_add, uint16_t* dq,
                              uint16_t* dk, uint16_t* dv, void* ws, hipStream_t s);
 hipError_t launch_lin_prep(const KGeom& g, const uint16_t* kc, const uint16_t* vt, void* ws, hipStream_t s);
 hipError_t launch_attn_lin_fwd(const KGeom& g, const uint16_t* qc, const uint16_t* kc, const uint16_t* vt,

@@ -246,6 +246,7 @@ __global__ void __launch_bounds__(kThreads, 2) lin_bwd_dq(const uint16_t* __rest
                                                           const int32_t* __restrict__ idx, int topk,
                                                           const uint16_t* __restrict__ fk,
                                                           const float* __restrict__ z_tot, LinBwdWs t,
+                                                          const uint16_t* __restrict__ dq_add,
                                                           uint16_t* __restrict__ dq, KGeom g, Placement pl) {
   constexpr int DC = D / 16, DT = D / 32;
   __shared__ __attribute__((aligned(16))) uint16_t v0[64 * D];
@@ -351,6 +352,7 @@ __global__ void __launch_bounds__(kThreads, 2) lin_bwd_dq(const uint16_t* __rest
   const float cq = t.c[row];
   const float* zt = z_tot + bh * D;
   const uint16_t* qrow = qc + row * D;
+  const uint16_t* arow = dq_add ? dq_add + row * D : nullptr;
   uint16_t* out = dq + row * D;
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt)
@@ -360,12 +362,19 @@ __global__ void __launch_bounds__(kThreads, 2) lin_bwd_dq(const uint16_t* __rest
       const uint2 qraw = *reinterpret_cast<const uint2*>(qrow + d);
       const float xq[4] = {__uint_as_float(qraw.x << 16), __uint_as_float(qraw.x & 0xFFFF0000u),
                            __uint_as_float(qraw.y << 16), __uint_as_float(qraw.y & 0xFFFF0000u)};
-      float o[4];
+      float o[4], ad[4] = {0.f, 0.f, 0.f, 0.f};
+      if (arow) {
+        const uint2 araw = *reinterpret_cast<const uint2*>(arow + d);
+        ad[0] = __uint_as_float(araw.x << 16);
+        ad[1] = __uint_as_float(araw.x & 0xFFFF0000u);
+        ad[2] = __uint_as_float(araw.y << 16);
+        ad[3] = __uint_as_float(araw.y & 0xFFFF0000u);
+      }
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         const int r = 4 * gq + u;
         const float dphi = (acc[dt][r] + x[(dt * 16 + r) * 64 + lane]) - cq * (zt[d + u] - zs[d + u]);
-        o[u] = valid ? dphi * phi_grad(xq[u]) : 0.f;
+        o[u] = valid ? dphi * phi_grad(xq[u]) + ad[u] : 0.f;
       }
       *reinterpret_cast<uint2*>(out + d) = make_uint2(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]));
     }
@@ -385,6 +394,7 @@ template <int D, bool DV>
 __global__ void __launch_bounds__(kThreads, 2) lin_bwd_dkv(const uint16_t* __restrict__ kc,
                                                            const uint16_t* __restrict__ vc,
                                                            const uint16_t* __restrict__ fk, LinBwdWs t, int topk,
+                                                           const uint16_t* __restrict__ add,
                                                            uint16_t* __restrict__ out, KGeom g, Placement pl) {
   constexpr int DC = D / 16, DT = D / 32;
   __shared__ __attribute__((aligned(16))) uint16_t w0[64 * D];
@@ -507,21 +517,29 @@ __global__ void __launch_bounds__(kThreads, 2) lin_bwd_dkv(const uint16_t* __res
   cube_coords(g, j, ct, cy, cx);
   const bool valid = local_valid(g, ct, cy, cx, key);
   const uint16_t* krw = kc + krow * D;
+  const uint16_t* arow = add ? add + krow * D : nullptr;
   uint16_t* orow = out + krow * D;
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
     for (int gq = 0; gq < 4; ++gq) {
       const int d = 32 * dt + 8 * gq + 4 * hf;
-      float o[4];
+      float o[4], ad[4] = {0.f, 0.f, 0.f, 0.f};
       const uint2 kraw = *reinterpret_cast<const uint2*>(krw + d);
       const float xk[4] = {__uint_as_float(kraw.x << 16), __uint_as_float(kraw.x & 0xFFFF0000u),
                            __uint_as_float(kraw.y << 16), __uint_as_float(kraw.y & 0xFFFF0000u)};
+      if (arow) {
+        const uint2 araw = *reinterpret_cast<const uint2*>(arow + d);
+        ad[0] = __uint_as_float(araw.x << 16);
+        ad[1] = __uint_as_float(araw.x & 0xFFFF0000u);
+        ad[2] = __uint_as_float(araw.y << 16);
+        ad[3] = __uint_as_float(araw.y & 0xFFFF0000u);
+      }
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         const int r = 4 * gq + u;
         const float s = acc[dt][r] + x[(dt * 16 + r) * 64 + lane];
-        o[u] = valid ? (DV ? s : s * phi_grad(xk[u])) : 0.f;
+        o[u] = valid ? (DV ? s : s * phi_grad(xk[u])) + ad[u] : 0.f;
       }
       *reinterpret_cast<uint2*>(orow + d) = make_uint2(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]));
     }
@@ -529,8 +547,8 @@ __global__ void __launch_bounds__(kThreads, 2) lin_bwd_dkv(const uint16_t* __res
 
 template <int D>
 hipError_t launch_t(const KGeom& g, const uint16_t* qc, const uint16_t* kc, const uint16_t* vc, const uint16_t* vt,
-                    const int32_t* idx, int topk, const uint16_t* doc, uint16_t* dq, uint16_t* dk, uint16_t* dv,
-                    void* ws, hipStream_t s) {
+                    const int32_t* idx, int topk, const uint16_t* doc, const uint16_t* const* add, uint16_t* dq,
+                    uint16_t* dk, uint16_t* dv, void* ws, hipStream_t s) {
   hipError_t e = launch_lin_prep(g, kc, vt, ws, s);  // phi(K), S_tot (e-major), z_tot; S partials kept
   if (e != hipSuccess) return e;
   const LinState ls = lin_state_parts(g, ws);
@@ -553,11 +571,11 @@ hipError_t launch_t(const KGeom& g, const uint16_t* qc, const uint16_t* kc, cons
   if (e != hipSuccess) return e;
   const Placement pl = make_placement(g);
   hipLaunchKernelGGL(lin_bwd_dq<D>, dim3(grid_size(g)), dim3(kThreads), 0, s, qc, vc, idx, topk, ls.fk, ls.z_tot, t,
-                     dq, g, pl);
-  hipLaunchKernelGGL((lin_bwd_dkv<D, false>), dim3(grid_size(g)), dim3(kThreads), 0, s, kc, vc, ls.fk, t, topk, dk,
-                     g, pl);
-  hipLaunchKernelGGL((lin_bwd_dkv<D, true>), dim3(grid_size(g)), dim3(kThreads), 0, s, kc, vc, ls.fk, t, topk, dv,
-                     g, pl);
+                     add[0], dq, g, pl);
+  hipLaunchKernelGGL((lin_bwd_dkv<D, false>), dim3(grid_size(g)), dim3(kThreads), 0, s, kc, vc, ls.fk, t, topk,
+                     add[1], dk, g, pl);
+  hipLaunchKernelGGL((lin_bwd_dkv<D, true>), dim3(grid_size(g)), dim3(kThreads), 0, s, kc, vc, ls.fk, t, topk,
+                     add[2], dv, g, pl);
   return hipGetLastError();
 }
 
@@ -570,10 +588,12 @@ size_t linear_bwd_workspace_bytes(const KGeom& g, int topk) {
 }
 
 hipError_t launch_linear_bwd(const KGeom& g, const uint16_t* qc, const uint16_t* kc, const uint16_t* vc,
-                             const uint16_t* vt, const int32_t* idx, int topk, const uint16_t* doc, uint16_t* dq,
+                             const uint16_t* vt, const int32_t* idx, int topk, const uint16_t* doc,
+                             const uint16_t* dq_add, const uint16_t* dk_add, const uint16_t* dv_add, uint16_t* dq,
                              uint16_t* dk, uint16_t* dv, void* ws, hipStream_t s) {
-  if (g.D == 64) return launch_t<64>(g, qc, kc, vc, vt, idx, topk, doc, dq, dk, dv, ws, s);
-  return launch_t<128>(g, qc, kc, vc, vt, idx, topk, doc, dq, dk, dv, ws, s);
+  const uint16_t* const add[3] = {dq_add, dk_add, dv_add};
+  if (g.D == 64) return launch_t<64>(g, qc, kc, vc, vt, idx, topk, doc, add, dq, dk, dv, ws, s);
+  return launch_t<128>(g, qc, kc, vc, vt, idx, topk, doc, add, dq, dk, dv, ws, s);
 }
 
 }  // namespace vsa

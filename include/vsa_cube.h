@@ -317,14 +317,18 @@ int32_t vsa_sparse_attn_linear_fwd(const vsa_geom* g, const uint16_t* qc, const 
  * selected (O_lin is then the constant 0).
  * Inputs: qc, kc, vc, doc TOKEN_MAJOR bf16 (doc: dO, padded rows zero); vt
  * DIM_MAJOR bf16 (V); idx, topk as for vsa_linear_branch.  Outputs: dq, dk,
- * dv bf16 TOKEN_MAJOR, padded rows zero.  ws: at least
+ * dv bf16 TOKEN_MAJOR, padded rows zero.  dq_add, dk_add, dv_add: optional
+ * (NULL or bf16 TOKEN_MAJOR) gradients to add before the one bf16 rounding,
+ * e.g. those of the fine stage for the hybrid layer; an output may alias its
+ * addend.  ws: at least
  * vsa_linear_bwd_workspace_bytes(g, topk) bytes (it holds the forward's
  * linear workspace too).  n_cubes <= VSA_MAX_CUBES.  No atomics. */
 size_t vsa_linear_bwd_workspace_bytes(const vsa_geom* g, int32_t topk);
 int32_t vsa_linear_branch_bwd(const vsa_geom* g, const uint16_t* qc, const uint16_t* kc,
                               const uint16_t* vc, const uint16_t* vt, const int32_t* idx,
-                              int32_t topk, const uint16_t* doc, uint16_t* dq, uint16_t* dk,
-                              uint16_t* dv, void* ws, size_t ws_bytes, void* stream);
+                              int32_t topk, const uint16_t* doc, const uint16_t* dq_add,
+                              const uint16_t* dk_add, const uint16_t* dv_add, uint16_t* dq,
+                              uint16_t* dk, uint16_t* dv, void* ws, size_t ws_bytes, void* stream);
 
 /* Matrix-core probe (measurement support, not part of the attention path):
  * the sustained rate of the bf16 matrix cores on this device, a measured

@@ -271,11 +271,13 @@ def test_linear_backward_entry_point_validation(lib):
     assert lib.vsa_linear_bwd_workspace_bytes(g, 0) == 0
     assert lib.vsa_linear_bwd_workspace_bytes(g, 9) == 0
     ins = [P] * 5  # qc kc vc vt idx
+    adds = [None] * 3
     outs = [P] * 3
-    assert lib.vsa_linear_branch_bwd(g, *ins, 2, None, *outs, P, ws, None) == _lib.VSA_ERR_NULL
-    assert lib.vsa_linear_branch_bwd(g, *ins, 2, P, P, P, None, P, ws, None) == _lib.VSA_ERR_NULL
-    assert lib.vsa_linear_branch_bwd(g, ODD, *ins[1:], 2, P, *outs, P, ws, None) == _lib.VSA_ERR_ALIGN
-    assert lib.vsa_linear_branch_bwd(g, *ins, 0, P, *outs, P, ws, None) == _lib.VSA_ERR_TOPK
-    assert lib.vsa_linear_branch_bwd(g, *ins, 9, P, *outs, P, ws, None) == _lib.VSA_ERR_TOPK
-    assert lib.vsa_linear_branch_bwd(g, *ins, 2, P, *outs, P, ws - 1, None) == _lib.VSA_ERR_WORKSPACE
-    assert lib.vsa_linear_branch_bwd(geom(D=48), *ins, 2, P, *outs, P, ws, None) == _lib.VSA_ERR_HEAD_DIM
+    assert lib.vsa_linear_branch_bwd(g, *ins, 2, None, *adds, *outs, P, ws, None) == _lib.VSA_ERR_NULL
+    assert lib.vsa_linear_branch_bwd(g, *ins, 2, P, *adds, P, P, None, P, ws, None) == _lib.VSA_ERR_NULL
+    assert lib.vsa_linear_branch_bwd(g, ODD, *ins[1:], 2, P, *adds, *outs, P, ws, None) == _lib.VSA_ERR_ALIGN
+    assert lib.vsa_linear_branch_bwd(g, *ins, 2, P, ODD, None, None, *outs, P, ws, None) == _lib.VSA_ERR_ALIGN
+    assert lib.vsa_linear_branch_bwd(g, *ins, 0, P, *adds, *outs, P, ws, None) == _lib.VSA_ERR_TOPK
+    assert lib.vsa_linear_branch_bwd(g, *ins, 9, P, *adds, *outs, P, ws, None) == _lib.VSA_ERR_TOPK
+    assert lib.vsa_linear_branch_bwd(g, *ins, 2, P, *adds, *outs, P, ws - 1, None) == _lib.VSA_ERR_WORKSPACE
+    assert lib.vsa_linear_branch_bwd(geom(D=48), *ins, 2, P, *adds, *outs, P, ws, None) == _lib.VSA_ERR_HEAD_DIM
