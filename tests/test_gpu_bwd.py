@@ -102,3 +102,26 @@ def test_backward_full_size_sampled_heads(name, heads):
     ref = oracle.backward(sub["q"], sub["k"], sub["v"], do, wl.grid, idx, wl.softmax_scale)
     for what, g_, r in zip(("dq", "dk", "dv"), got, ref):
         assert_close_rel(g_, r, f"{name} {what}", MAX_REL, MEAN_REL)
+
+
+def test_backward_is_deterministic():
+    # No atomics: two runs (the second with a fresh workspace) agree bit for bit,
+    # at the Wan2.1-1.3B shape with two heads.
+    import block_sparse_video_cube_amd as vsa
+
+    wl = workloads.workload("wan1.3b").with_(heads=2)
+    inp = workloads.make_inputs(wl)
+    do = grad_out(inp["q"].shape, 4242)
+    valid = oracle.valid_rows(wl.grid)
+    idx = oracle.select_topk(oracle.cube_permute(inp["q"], wl.grid), oracle.cube_permute(inp["k"], wl.grid), valid,
+                             wl.topk)
+    q, k, v, dd = (to_dev(x) for x in (inp["q"], inp["k"], inp["v"], do))
+    qc, kc, vc, doc = (vsa.cube_permute(x, wl.grid) for x in (q, k, v, dd))
+    vt = vsa.cube_permute(v, wl.grid, layout="dim")
+    idx_d = torch.from_numpy(np.ascontiguousarray(idx, dtype=np.int32)).to("cuda:0")
+    oc, _, lse = vsa.sparse_attn_fwd(qc, kc, vt, idx_d, wl.grid, wl.softmax_scale, want_lse=True)
+    first = vsa.sparse_attn_bwd(qc, kc, vc, oc, doc, lse, idx_d, wl.grid, wl.softmax_scale)
+    again = vsa.sparse_attn_bwd(qc, kc, vc, oc, doc, lse, idx_d, wl.grid, wl.softmax_scale)
+    torch.cuda.synchronize()
+    for a, b in zip(first, again):
+        assert torch.equal(a, b)

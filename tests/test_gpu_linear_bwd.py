@@ -82,3 +82,25 @@ def test_linear_backward_hybrid_shape_one_head():
     got, ref, valid = run(wl, 320, heads=[(0, 1)])
     for name, g, r in zip(("dq", "dk", "dv"), got, ref):
         assert_close_rel(g[0, 1][valid], r[0, 1][valid], f"{name} hybrid (0, 1)", MAX_REL, MEAN_REL)
+
+
+def test_linear_backward_is_deterministic():
+    # No atomics: two runs agree bit for bit (hybrid shape, one batch, two heads).
+    import block_sparse_video_cube_amd as vsa
+
+    wl = workloads.workload("hybrid").with_(batch=1, heads=2)
+    inp = workloads.make_inputs(wl)
+    rng = np.random.default_rng(330)
+    do = workloads.round_to_bf16_bits(rng.standard_normal(inp["q"].shape).astype(np.float32))
+    valid = oracle.valid_rows(wl.grid)
+    idx = oracle.select_topk(oracle.cube_permute(inp["q"], wl.grid), oracle.cube_permute(inp["k"], wl.grid), valid,
+                             wl.topk)
+    q, k, v, dd = (to_dev(x) for x in (inp["q"], inp["k"], inp["v"], do))
+    qc, kc, vc, doc = (vsa.cube_permute(x, wl.grid) for x in (q, k, v, dd))
+    vt = vsa.cube_permute(v, wl.grid, layout="dim")
+    idx_d = torch.from_numpy(np.ascontiguousarray(idx, dtype=np.int32)).to("cuda:0")
+    first = vsa.linear_branch_bwd(qc, kc, vc, vt, idx_d, doc, wl.grid)
+    again = vsa.linear_branch_bwd(qc, kc, vc, vt, idx_d, doc, wl.grid)
+    torch.cuda.synchronize()
+    for a, b in zip(first, again):
+        assert torch.equal(a, b)
