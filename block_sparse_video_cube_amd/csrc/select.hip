@@ -203,12 +203,22 @@ hipError_t launch_select_pooled(const KGeom& g, const float* qbar, const float* 
                      g.D);
   const long long nrows = (long long)bh * g.nc;
   const int per_lane = (g.nc + 63) / 64;
+  // Up to 512 cubes every keys-per-lane count has its own instantiation (the
+  // 32-step search costs one ballot per key slot).
   if (per_lane <= 1)
     launch_topk<1>(scores, idx, nrows, g.nc, topk, s);
   else if (per_lane <= 2)
     launch_topk<2>(scores, idx, nrows, g.nc, topk, s);
+  else if (per_lane <= 3)
+    launch_topk<3>(scores, idx, nrows, g.nc, topk, s);
   else if (per_lane <= 4)
     launch_topk<4>(scores, idx, nrows, g.nc, topk, s);
+  else if (per_lane <= 5)
+    launch_topk<5>(scores, idx, nrows, g.nc, topk, s);
+  else if (per_lane <= 6)
+    launch_topk<6>(scores, idx, nrows, g.nc, topk, s);
+  else if (per_lane <= 7)
+    launch_topk<7>(scores, idx, nrows, g.nc, topk, s);
   else if (per_lane <= 8)
     launch_topk<8>(scores, idx, nrows, g.nc, topk, s);
   else if (per_lane <= 16)
