@@ -69,8 +69,9 @@ __global__ void __launch_bounds__(256) cube_mean(const uint16_t* __restrict__ xc
 // fp32).  One wavefront per 32 x 32 output tile.  The contraction order over
 // d is permuted identically for both operands so that each lane reads four
 // consecutive floats: MFMA u of group t takes d = 8t + 4 h + u on lane half h.
+template <int D>
 __global__ void __launch_bounds__(64) block_score(const float* __restrict__ qbar, const float* __restrict__ kbar,
-                                                  float* __restrict__ scores, int nc, int D) {
+                                                  float* __restrict__ scores, int nc) {
   const long long bh = blockIdx.z;
   const int i0 = blockIdx.y * 32, j0 = blockIdx.x * 32;
   const int lane = threadIdx.x, h = lane >> 5, m = lane & 31;
@@ -78,11 +79,17 @@ __global__ void __launch_bounds__(64) block_score(const float* __restrict__ qbar
   const float* krow = kbar + (bh * nc + min(j0 + m, nc - 1)) * D;
   const bool qin = i0 + m < nc, kin = j0 + m < nc;
   f32x16 acc = f32x16{};
+  // All operand loads are issued before the first product (fully unrolled).
+  float4 av[D / 8], bv[D / 8];
+#pragma unroll
   for (int t = 0; t < D / 8; ++t) {
-    float4 a = *reinterpret_cast<const float4*>(qrow + 8 * t + 4 * h);
-    float4 b = *reinterpret_cast<const float4*>(krow + 8 * t + 4 * h);
-    if (!qin) a = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (!kin) b = make_float4(0.f, 0.f, 0.f, 0.f);
+    av[t] = *reinterpret_cast<const float4*>(qrow + 8 * t + 4 * h);
+    bv[t] = *reinterpret_cast<const float4*>(krow + 8 * t + 4 * h);
+  }
+#pragma unroll
+  for (int t = 0; t < D / 8; ++t) {
+    const float4 a = qin ? av[t] : make_float4(0.f, 0.f, 0.f, 0.f);
+    const float4 b = kin ? bv[t] : make_float4(0.f, 0.f, 0.f, 0.f);
     acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a.x, b.x, acc, 0, 0, 0);
     acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a.y, b.y, acc, 0, 0, 0);
     acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a.z, b.z, acc, 0, 0, 0);
@@ -199,8 +206,10 @@ hipError_t launch_select_pooled(const KGeom& g, const float* qbar, const float* 
                                 float* scores, hipStream_t s) {
   const size_t bh = (size_t)g.B * g.H;
   const int tiles = (g.nc + 31) / 32;
-  hipLaunchKernelGGL(block_score, dim3(tiles, tiles, (unsigned)bh), dim3(64), 0, s, qbar, kbar, scores, g.nc,
-                     g.D);
+  if (g.D == 64)
+    hipLaunchKernelGGL(block_score<64>, dim3(tiles, tiles, (unsigned)bh), dim3(64), 0, s, qbar, kbar, scores, g.nc);
+  else
+    hipLaunchKernelGGL(block_score<128>, dim3(tiles, tiles, (unsigned)bh), dim3(64), 0, s, qbar, kbar, scores, g.nc);
   const long long nrows = (long long)bh * g.nc;
   const int per_lane = (g.nc + 63) / 64;
   // Up to 512 cubes every keys-per-lane count has its own instantiation (the
