@@ -212,8 +212,9 @@ hipError_t launch_select_pooled(const KGeom& g, const float* qbar, const float* 
     hipLaunchKernelGGL(block_score<128>, dim3(tiles, tiles, (unsigned)bh), dim3(64), 0, s, qbar, kbar, scores, g.nc);
   const long long nrows = (long long)bh * g.nc;
   const int per_lane = (g.nc + 63) / 64;
-  // Up to 512 cubes every keys-per-lane count has its own instantiation (the
-  // 32-step search costs one ballot per key slot).
+  // Every keys-per-lane count up to 8 has its own instantiation, larger ones
+  // come in steps of a quarter to a half (the 32-step search costs one ballot
+  // per key slot).
   if (per_lane <= 1)
     launch_topk<1>(scores, idx, nrows, g.nc, topk, s);
   else if (per_lane <= 2)
@@ -230,10 +231,16 @@ hipError_t launch_select_pooled(const KGeom& g, const float* qbar, const float* 
     launch_topk<7>(scores, idx, nrows, g.nc, topk, s);
   else if (per_lane <= 8)
     launch_topk<8>(scores, idx, nrows, g.nc, topk, s);
+  else if (per_lane <= 12)
+    launch_topk<12>(scores, idx, nrows, g.nc, topk, s);
   else if (per_lane <= 16)
     launch_topk<16>(scores, idx, nrows, g.nc, topk, s);
+  else if (per_lane <= 24)
+    launch_topk<24>(scores, idx, nrows, g.nc, topk, s);
   else if (per_lane <= 32)
     launch_topk<32>(scores, idx, nrows, g.nc, topk, s);
+  else if (per_lane <= 48)
+    launch_topk<48>(scores, idx, nrows, g.nc, topk, s);
   else
     launch_topk<64>(scores, idx, nrows, g.nc, topk, s);
   return hipGetLastError();
