@@ -13,7 +13,7 @@
 //
 // Kernels.  No atomics: every sum is owned by one workgroup, so the results
 // do not depend on scheduling.
-//  * bwd_delta: delta per row.
+//  * bwd_delta: delta per row (and lse in log2 units).
 //  * bwd_count / bwd_scan / bwd_fill: the block lists transposed, i.e. for
 //    every key cube the ascending list of query cubes whose (ascending) list
 //    holds it, found by binary search.
@@ -26,9 +26,9 @@
 //    next product); K_j, V_j stay in registers; per query cube that selected
 //    j it streams Q_i, dO_i (token-major), Q_i^T, dO_i^T, lse_i and delta_i,
 //    and accumulates dV^T = dO^T P and dK^T = Q^T dS.
-// Both stream kernels double-buffer their tiles in LDS (direct buffer->LDS
-// loads one block ahead) and split each block among four wavefronts by
-// 32-row halves as the forward does, merging the halves through LDS.
+// Both stream tiles into LDS by direct buffer->LDS loads (bwd_dq one block
+// ahead, bwd_dkdv two cubes ahead) and split each block by 32-row halves as
+// the forward does, merging the halves through LDS.
 #include <math.h>
 
 #include "tile_pipeline.h"
@@ -42,9 +42,11 @@ constexpr float kLog2e = 1.4426950408889634f;
 
 // ---------------------------------------------------------------- delta --
 
+// delta per row, and the forward's lse in log2 units (lse log2 e) for bwd_dkdv.
 template <int D>
 __global__ void __launch_bounds__(256) bwd_delta(const uint16_t* __restrict__ o, const uint16_t* __restrict__ dout,
-                                                 float* __restrict__ delta, long long rows) {
+                                                 const float* __restrict__ lse, float* __restrict__ delta,
+                                                 float* __restrict__ lse2, long long rows) {
   constexpr int TPR = D / 8;  // threads per row, one 16-byte chunk each
   const long long t = blockIdx.x * 256LL + threadIdx.x;
   const long long row = t / TPR;
@@ -62,7 +64,10 @@ __global__ void __launch_bounds__(256) bwd_delta(const uint16_t* __restrict__ o,
   }
 #pragma unroll
   for (int off = TPR / 2; off > 0; off >>= 1) sum += __shfl_xor(sum, off);
-  if (c == 0 && row < rows) delta[row] = sum;
+  if (c == 0 && row < rows) {
+    delta[row] = sum;
+    lse2[row] = lse[row] * kLog2e;
+  }
 }
 
 // ------------------------------------------------- transposed block lists --
@@ -270,23 +275,41 @@ __global__ void __launch_bounds__(kThreads, 2) bwd_dq(const uint16_t* __restrict
 //
 // One workgroup of 8 wavefronts per key cube j.  Wavefronts 0-3 and 4-7
 // split the work of each (key, query) quadrant (wk, wq), 32 keys x 32 queries,
-// by product, so that each SIMD holds one of each kind and the two overlap:
+// by product, so that each SIMD holds one of each kind:
 //  * P wavefronts (0-3): S = Q K^T, P = exp(scale S - lse), dV^T += dO^T P;
 //    they hand P (fp32) to their partner through LDS;
-//  * dS wavefronts (4-7), one step behind: dP = dO V^T,
-//    dS = P * (dP - delta), dK^T += Q^T dS.
-// Q and dO tiles therefore live for two steps: a ring of three.  A lane owns
-// a key column (S = Q K^T with Q rows in pi order, so the accumulator is the
-// B operand of the next product); K (P wavefronts) or V (dS wavefronts) stays
-// in registers.
+//  * dS wavefronts (4-7), one cube behind: dP = dO V^T, dS = P * (dP - delta),
+//    dK^T += Q^T dS.
+// Every step has two phases split by a barrier.  In phase A the P wavefronts
+// read their operands for cube m from LDS while the dS wavefronts run their
+// products for cube m - 1 on operands already in registers; in phase B the
+// roles swap: the P wavefronts run cube m, the dS wavefronts read cube m.  So
+// on every SIMD one wavefront reads while the other computes, and the LDS
+// reads of the step no longer all land at once after a single barrier.
+// A lane owns a key column (S = Q K^T with Q rows in pi order, so the
+// accumulator is the B operand of the next product); K (P wavefronts) or V
+// (dS wavefronts) stays in registers.
+//
+// Tiles: P wavefronts load Q and lse, dS wavefronts dO and delta, each two
+// cubes ahead into a ring of three, right after their own reads of the step.
+// A wavefront waits for its previous loads just before those reads (one step
+// after issuing them); every reader of that cube comes at least one barrier
+// later.  The ring slot a load overwrites was last read in the previous step.
+// That wait also leaves no tile load of the wavefront in flight when it issues
+// ds_read_b64_tr_b16, for which the compiler waits for all of them.
+
+template <int N>
+struct SlotC {
+  static constexpr int value = N;
+};
 
 template <int D>
 struct DkvSmem {
   uint16_t q[3][64 * D];     // Q_i token-major (kt_swz: also read transposed)
   uint16_t dout[3][64 * D];  // dO_i token-major (kt_swz)
-  float ls[3][64];           // lse_i
+  float ls[3][64];           // lse_i log2 e
   float dl[3][64];           // delta_i
-  f32x4 p[2][4][4][64];      // P of one step: [slot][quadrant][register / 4][lane]
+  f32x4 p[4][4][64];         // P of one cube: [quadrant][register / 4][lane]
 };
 
 template <int D, bool PARTIAL>
@@ -294,7 +317,7 @@ __global__ void __launch_bounds__(2 * kThreads, 1) bwd_dkdv(const uint16_t* __re
                                                             const uint16_t* __restrict__ kc,
                                                             const uint16_t* __restrict__ vc,
                                                             const uint16_t* __restrict__ doc,
-                                                            const float* __restrict__ lse,
+                                                            const float* __restrict__ lse2,
                                                             const float* __restrict__ delta,
                                                             const int32_t* __restrict__ qoff,
                                                             const int32_t* __restrict__ qcnt,
@@ -317,15 +340,16 @@ __global__ void __launch_bounds__(2 * kThreads, 1) bwd_dkdv(const uint16_t* __re
   const TileOffsets<D, true> toff(quad, lane);
   const int cnt = qcnt[bh * g.nc + j];
   const int32_t* list = qlist + bh * (long long)g.nc * topk + qoff[bh * g.nc + j];
-  // P wavefronts load the Q tiles and lse, dS wavefronts the dO tiles and delta.
+  // P wavefronts load the Q tiles and lse log2 e, dS wavefronts the dO tiles and delta.
   const uint16_t* src = (ds_wave ? doc : qc) + hbase;
-  const float* rsrc_f = ds_wave ? delta : lse;
-  auto issue = [&](int m, uint16_t* qs, uint16_t* ds, float* lss, float* dls) {
+  const float* rsrc_f = ds_wave ? delta : lse2;
+  auto issue = [&](int m, int slot) {
     const int i = list[m];
-    issue_k_tile<D>(make_rsrc(src + 64LL * i * D, 64 * D * 2), ds_wave ? ds : qs, quad, toff.k);
-    if (quad == 0) issue_row_f32(rsrc_f + rbase + 64LL * i, ds_wave ? dls : lss, lane);
+    issue_k_tile<D>(make_rsrc(src + 64LL * i * D, 64 * D * 2), ds_wave ? sm.dout[slot] : sm.q[slot], quad, toff.k);
+    if (quad == 0) issue_row_f32(rsrc_f + rbase + 64LL * i, ds_wave ? sm.dl[slot] : sm.ls[slot], lane);
   };
-  if (cnt > 0) issue(0, sm.q[0], sm.dout[0], sm.ls[0], sm.dl[0]);
+  if (cnt > 0) issue(0, 0);
+  if (cnt > 1) issue(1, 1);
 
   // This wavefront's 32 keys of K (P) or V (dS), B operand fragments.
   bf16x8 kv[DC];
@@ -346,60 +370,137 @@ __global__ void __launch_bounds__(2 * kThreads, 1) bwd_dkdv(const uint16_t* __re
   f32x16 acc[DT];  // dV^T (P wavefronts) or dK^T (dS wavefronts)
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) acc[dt] = f32x16{};
+  // The transposed operand is read one phase ahead of its product: dO^T (P)
+  // or Q^T (dS).  The row operands are read right before their products.
+  bf16x8 ta[DT][2];
+  bf16x8 bop[2];  // B operand of the deferred product: P (P wavefronts) or dS (dS wavefronts), bf16
+  f32x4* const pslot = &sm.p[quad][0][lane];
+  wait_vmcnt<0>();  // the first two cubes
 
-  // Step m: P wavefronts take query cube m, dS wavefronts query cube m - 1.
-  // Ring slots: Q/dO/lse/delta of cube m in m % 3, P of cube m in m % 2.  The
-  // slot bases are run-time values, so every LDS address is one loop-invariant
-  // lane offset plus a uniform base (the ring spans more than the 64 KB that
-  // an instruction offset reaches).
-  int s3 = 0;  // m % 3
-  for (int m = 0; m <= cnt && cnt > 0; ++m) {
-    const int n3 = s3 == 2 ? 0 : s3 + 1;  // (m + 1) % 3
-    const int p3 = s3 == 0 ? 2 : s3 - 1;  // (m - 1) % 3
-    // P wavefronts: S = Q(m) K^T, then dV^T += dO(m)^T P.
-    // dS wavefronts: dP = dO(m-1) V^T, then dK^T += Q(m-1)^T dS.
-    const bool active = ds_wave ? m >= 1 : m < cnt;
-    const int sl = ds_wave ? p3 : s3;
-    const uint16_t* a_tile = ds_wave ? sm.dout[sl] : sm.q[sl];
-    const uint16_t* t_tile = ds_wave ? sm.q[sl] : sm.dout[sl];
-    wait_vmcnt<0>();
-    pipeline_barrier();
-    // The transposed reads go first: the compiler makes every
-    // ds_read_b64_tr_b16 wait for all tile loads in flight, and at this point
-    // none are.
-    bf16x8 ta[DT][2];
-    if (active) read_tr<D>(t_tile, wq, lane, ta);
-    if (m + 1 < cnt) issue(m + 1, sm.q[n3], sm.dout[n3], sm.ls[n3], sm.dl[n3]);
-    if (active) {
-      f32x16 x = f32x16{};  // S or dP
-      {
+  // Ring slots: cube m in m % 3, unrolled by three so that every slot base is
+  // a compile-time constant in the instruction offset.  Each read kind adds
+  // it to a loop-invariant lane offset that already holds its ring's base, so
+  // no offset exceeds the 64 KB an instruction reaches and the loops compute
+  // no LDS address.  The two kinds run separate loops with the same barriers:
+  // two per step, steps m = 0 .. cnt.
+  constexpr uint32_t kTile = 64 * D * 2;  // bytes per Q or dO tile
+  const char* const lds0 = reinterpret_cast<const char*>(&sm);
+  const uint32_t q_base = (uint32_t)(reinterpret_cast<const char*>(&sm.q[0][0]) - lds0);
+  const uint32_t d_base = (uint32_t)(reinterpret_cast<const char*>(&sm.dout[0][0]) - lds0);
+  // Row operand (A of S or dP; rows 32 wq + pi order) and transposed operand
+  // (A of dV^T or dK^T, read_tr_one's lane layout, kk = 0) of this wavefront,
+  // byte offsets within a tile, plus the base of the ring each kind reads.
+  uint32_t ko[DC], to[2 * DT];
+  {
+    const int krow = 32 * wq + prow;
+    const uint32_t rb = ds_wave ? d_base : q_base;
+#pragma unroll
+    for (int dc = 0; dc < DC; ++dc)
+      ko[dc] = rb + (uint32_t)(krow * D + (((2 * dc + hf) ^ kt_swz<D>(krow)) * 8)) * 2u;
+    const int s = lane & 15, grp = lane >> 4;
+    const uint32_t tb = ds_wave ? q_base : d_base;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int r = 32 * wq + 8 * hf + 4 * h + (s >> 2);
+        const int d = 32 * dt + 16 * (grp & 1) + 4 * (s & 3);
+        to[2 * dt + h] = tb + (uint32_t)(r * D + (((d >> 3) ^ kt_swz<D>(r)) << 3) + (d & 4)) * 2u;
+      }
+    // Opaque to the optimiser, so that it keeps these sums and puts only the
+    // slot's constant into each instruction.
+#pragma unroll
+    for (int dc = 0; dc < DC; ++dc) asm volatile("" : "+v"(ko[dc]));
+#pragma unroll
+    for (int e = 0; e < 2 * DT; ++e) asm volatile("" : "+v"(to[e]));
+  }
+  auto read_rows = [&](uint32_t slot_off, bf16x8(&xa)[DC]) {
+#pragma unroll
+    for (int dc = 0; dc < DC; ++dc) xa[dc] = *reinterpret_cast<const bf16x8*>(lds0 + ko[dc] + slot_off);
+  };
+  auto read_cols = [&](uint32_t slot_off) {
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        i16x4 part[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+          part[h] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (lds_i16x4_ptr)(lds0 + to[2 * dt + h] + slot_off + kk * 16 * D * 2));
+        ta[dt][kk] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(part[0], part[1], 0, 1, 2, 3, 4, 5, 6, 7));
+      }
+  };
+  auto dmma = [&]() {  // the deferred product: acc += ta bop
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk)
+        acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ta[dt][kk], bop[kk], acc[dt], 0, 0, 0);
+  };
+  const int steps = cnt > 0 ? cnt + 1 : 0;
+  if (!ds_wave) {
+    auto step = [&](int m, auto slot) {
+      constexpr int S = decltype(slot)::value, S2 = (S + 2) % 3;
+      pipeline_barrier();
+      // Phase A: dV^T += dO(m-1)^T P(m-1) on registers, then dO(m)^T into
+      // registers and the loads of Q(m + 2).
+      if (m >= 1) dmma();
+      if (m < cnt) {
+        wait_vmcnt<0>();  // Q(m + 1), read from the next step on
+        read_cols(S * kTile);
+        if (m + 2 < cnt) issue(m + 2, S2);
+      }
+      pipeline_barrier();
+      // Phase B: S = Q(m) K^T, P = exp(scale S - lse) to LDS and, as bf16,
+      // to the next phase A.
+      if (m < cnt) {
         bf16x8 xa[DC];
-        read_k<D, true>(a_tile, wq, hf, prow, xa);
+        read_rows(S * kTile, xa);
+        f32x16 x = f32x16{};
 #pragma unroll
         for (int dc = 0; dc < DC; ++dc) x = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xa[dc], kv[dc], x, 0, 0, 0);
-      }
-      f32x4* pslot = &sm.p[(m & 1) ^ (ds_wave ? 1 : 0)][quad][0][lane];  // P(m) out, P(m-1) in
-      uint32_t bw[8];
-      if (!ds_wave) {
-        const f32x4* lsp = reinterpret_cast<const f32x4*>(&sm.ls[sl][0]);
+        const f32x4* lsp = reinterpret_cast<const f32x4*>(&sm.ls[S][0]);
         const f32x4 l4[4] = {lsp[q0 / 4], lsp[q0 / 4 + 1], lsp[(q0 + 16) / 4], lsp[(q0 + 16) / 4 + 1]};
         f32x4 pv[4];
 #pragma unroll
         for (int r = 0; r < 16; ++r)
-          pv[r / 4][r % 4] = kmask * __builtin_amdgcn_exp2f(fmaf(x[r], scale_log2, -l4[r / 4][r % 4] * kLog2e));
+          pv[r / 4][r % 4] = kmask * __builtin_amdgcn_exp2f(fmaf(x[r], scale_log2, -l4[r / 4][r % 4]));
 #pragma unroll
         for (int c = 0; c < 4; ++c) pslot[64 * c] = pv[c];
+        uint32_t bw[8];
 #pragma unroll
         for (int r = 0; r < 8; ++r) {
           const f32x2 p2 = {pv[r / 2][2 * (r % 2)], pv[r / 2][2 * (r % 2) + 1]};
           bw[r] = __builtin_bit_cast(uint32_t, __builtin_convertvector(p2, bf16x2));
         }
-      } else {
-        const f32x4* dlp = reinterpret_cast<const f32x4*>(&sm.dl[sl][0]);
+        bop[0] = __builtin_bit_cast(bf16x8, make_uint4(bw[0], bw[1], bw[2], bw[3]));
+        bop[1] = __builtin_bit_cast(bf16x8, make_uint4(bw[4], bw[5], bw[6], bw[7]));
+      }
+    };
+    for (int m = 0; m < steps; m += 3) {
+      step(m, SlotC<0>{});
+      if (m + 1 < steps) step(m + 1, SlotC<1>{});
+      if (m + 2 < steps) step(m + 2, SlotC<2>{});
+    }
+  } else {
+    auto step = [&](int m, auto slot) {
+      constexpr int S = decltype(slot)::value, S2 = (S + 2) % 3;  // S2: also (m - 1) % 3
+      pipeline_barrier();
+      // Phase A, cube m - 1: dP = dO V^T, dS = P * (dP - delta) in bf16 for
+      // the next phase B.
+      if (m >= 1) {
+        bf16x8 xa[DC];
+        read_rows(S2 * kTile, xa);
+        f32x16 x = f32x16{};
+#pragma unroll
+        for (int dc = 0; dc < DC; ++dc) x = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xa[dc], kv[dc], x, 0, 0, 0);
+        const f32x4* dlp = reinterpret_cast<const f32x4*>(&sm.dl[S2][0]);
         const f32x4 d4[4] = {dlp[q0 / 4], dlp[q0 / 4 + 1], dlp[(q0 + 16) / 4], dlp[(q0 + 16) / 4 + 1]};
         f32x4 pv[4];
 #pragma unroll
         for (int c = 0; c < 4; ++c) pv[c] = pslot[64 * c];
+        uint32_t bw[8];
 #pragma unroll
         for (int r = 0; r < 8; ++r) {
           const int r0 = 2 * r, r1 = 2 * r + 1;
@@ -407,16 +508,24 @@ __global__ void __launch_bounds__(2 * kThreads, 1) bwd_dkdv(const uint16_t* __re
                             pv[r1 / 4][r1 % 4] * (x[r1] - d4[r1 / 4][r1 % 4])};
           bw[r] = __builtin_bit_cast(uint32_t, __builtin_convertvector(d2, bf16x2));
         }
+        bop[0] = __builtin_bit_cast(bf16x8, make_uint4(bw[0], bw[1], bw[2], bw[3]));
+        bop[1] = __builtin_bit_cast(bf16x8, make_uint4(bw[4], bw[5], bw[6], bw[7]));
       }
-      const bf16x8 bop[2] = {__builtin_bit_cast(bf16x8, make_uint4(bw[0], bw[1], bw[2], bw[3])),
-                             __builtin_bit_cast(bf16x8, make_uint4(bw[4], bw[5], bw[6], bw[7]))};
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk)
-          acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ta[dt][kk], bop[kk], acc[dt], 0, 0, 0);
+      pipeline_barrier();
+      // Phase B: dK^T += Q(m-1)^T dS on registers, then Q(m)^T into
+      // registers and the loads of dO(m + 2).
+      if (m >= 1) dmma();
+      if (m < cnt) {
+        wait_vmcnt<0>();  // dO(m + 1), read from the next step on
+        read_cols(S * kTile);
+        if (m + 2 < cnt) issue(m + 2, S2);
+      }
+    };
+    for (int m = 0; m < steps; m += 3) {
+      step(m, SlotC<0>{});
+      if (m + 1 < steps) step(m + 1, SlotC<1>{});
+      if (m + 2 < steps) step(m + 2, SlotC<2>{});
     }
-    s3 = n3;
   }
 
   // The two query halves hold partial sums of the same dK^T (dV^T): add them.
@@ -448,9 +557,10 @@ __global__ void __launch_bounds__(2 * kThreads, 1) bwd_dkdv(const uint16_t* __re
     }
 }
 
-// Workspace carve-up: delta [B H Np] f32 | cnt [B H Nc] | off [B H Nc] | list [B H Nc topk] int32.
+// Workspace carve-up: delta [B H Np] f32 | lse log2 e [B H Np] f32 | cnt [B H Nc] | off [B H Nc] |
+// list [B H Nc topk] int32.
 struct BwdWs {
-  float* delta;
+  float *delta, *lse2;
   int32_t *cnt, *off, *list;
 };
 
@@ -461,6 +571,8 @@ inline BwdWs carve(const KGeom& g, int topk, void* ws) {
   const size_t bh = (size_t)g.B * g.H;
   BwdWs w;
   w.delta = reinterpret_cast<float*>(p);
+  p += align256(bh * g.Np * sizeof(float));
+  w.lse2 = reinterpret_cast<float*>(p);
   p += align256(bh * g.Np * sizeof(float));
   w.cnt = reinterpret_cast<int32_t*>(p);
   p += align256(bh * g.nc * sizeof(int32_t));
@@ -476,7 +588,8 @@ hipError_t launch_bwd_t(const KGeom& g, const uint16_t* qc, const uint16_t* kc, 
                         float scale, uint16_t* dq, uint16_t* dk, uint16_t* dv, void* ws, hipStream_t s) {
   const BwdWs w = carve(g, topk, ws);
   const long long rows = (long long)g.B * g.H * g.Np;
-  bwd_delta<D><<<dim3((unsigned)((rows * (D / 8) + 255) / 256)), dim3(256), 0, s>>>(oc, doc, w.delta, rows);
+  bwd_delta<D><<<dim3((unsigned)((rows * (D / 8) + 255) / 256)), dim3(256), 0, s>>>(oc, doc, lse, w.delta, w.lse2,
+                                                                                    rows);
   const dim3 tgrid((g.nc + 3) / 4, g.B * g.H);
   bwd_count<<<tgrid, dim3(256), 0, s>>>(idx, topk, w.cnt, g);
   bwd_scan<<<dim3(g.B * g.H), dim3(256), 0, s>>>(w.cnt, w.off, g);
@@ -485,7 +598,7 @@ hipError_t launch_bwd_t(const KGeom& g, const uint16_t* qc, const uint16_t* kc, 
   const float scale_log2 = scale * kLog2e;
   bwd_dq<D, PARTIAL><<<dim3(grid_size(g)), dim3(kThreads), 0, s>>>(qc, kc, vc, doc, lse, w.delta, idx, topk, scale,
                                                                     scale_log2, dq, g, pl);
-  bwd_dkdv<D, PARTIAL><<<dim3(grid_size(g)), dim3(2 * kThreads), 0, s>>>(qc, kc, vc, doc, lse, w.delta, w.off, w.cnt,
+  bwd_dkdv<D, PARTIAL><<<dim3(grid_size(g)), dim3(2 * kThreads), 0, s>>>(qc, kc, vc, doc, w.lse2, w.delta, w.off, w.cnt,
                                                                       w.list, topk, scale, scale_log2, dk, dv, g, pl);
   return hipGetLastError();
 }
@@ -503,7 +616,7 @@ hipError_t launch_block_lists_t(const KGeom& g, const int32_t* idx, int topk, in
 
 size_t attn_bwd_workspace_bytes(const KGeom& g, int topk) {
   const size_t bh = (size_t)g.B * g.H;
-  return align256(bh * g.Np * sizeof(float)) + 2 * align256(bh * g.nc * sizeof(int32_t)) +
+  return 2 * align256(bh * g.Np * sizeof(float)) + 2 * align256(bh * g.nc * sizeof(int32_t)) +
          align256(bh * g.nc * (size_t)topk * sizeof(int32_t));
 }
 

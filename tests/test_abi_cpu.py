@@ -165,8 +165,9 @@ def test_backward_entry_point_validation(lib):
     g = geom()
     P = FAKE
     ws = lib.vsa_attn_bwd_workspace_bytes(g, 2)
-    # delta (B H Np f32) + counts + offsets (B H Nc) + lists (B H Nc k), each 256-byte aligned
-    assert ws >= 2 * 512 * 4 + 2 * 2 * 8 * 4 + 2 * 8 * 2 * 4
+    # delta and lse log2 e (B H Np f32 each) + counts + offsets (B H Nc) + lists (B H Nc k), each
+    # 256-byte aligned
+    assert ws >= 2 * 2 * 512 * 4 + 2 * 2 * 8 * 4 + 2 * 8 * 2 * 4
     assert lib.vsa_attn_bwd_workspace_bytes(g, 0) == 0
     assert lib.vsa_attn_bwd_workspace_bytes(g, 9) == 0
     args = [P] * 7  # qc kc vc oc doc lse idx
