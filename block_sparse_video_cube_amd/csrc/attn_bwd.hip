@@ -457,6 +457,7 @@ __global__ void __launch_bounds__(2 * kThreads, 1) bwd_dkdv(const uint16_t* __re
       if (m < cnt) {
         bf16x8 xa[DC];
         read_rows(S * kTile, xa);
+        __builtin_amdgcn_sched_barrier(0);  // all row reads in flight before the chain
         f32x16 x = f32x16{};
 #pragma unroll
         for (int dc = 0; dc < DC; ++dc) x = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xa[dc], kv[dc], x, 0, 0, 0);
@@ -492,6 +493,7 @@ __global__ void __launch_bounds__(2 * kThreads, 1) bwd_dkdv(const uint16_t* __re
       if (m >= 1) {
         bf16x8 xa[DC];
         read_rows(S2 * kTile, xa);
+        __builtin_amdgcn_sched_barrier(0);  // all row reads in flight before the chain
         f32x16 x = f32x16{};
 #pragma unroll
         for (int dc = 0; dc < DC; ++dc) x = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xa[dc], kv[dc], x, 0, 0, 0);
