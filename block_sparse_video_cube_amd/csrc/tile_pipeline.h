@@ -35,8 +35,10 @@ __device__ __forceinline__ void wait_vmcnt() {
 // A plain s_barrier is used instead of __syncthreads(): the release fence of
 // the latter would also wait for the tile loads still in flight.
 __device__ __forceinline__ void pipeline_barrier() {
+  asm volatile("" ::: "memory");  // keep the compiler's LDS accesses on their side
   __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
   __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
 }
 
 // Key row loaded by A-operand lane row m (0..31) of a 32-key tile.  With it,
