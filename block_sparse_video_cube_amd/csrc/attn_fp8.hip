@@ -275,49 +275,62 @@ __global__ void __launch_bounds__(kThreads8, 2) attn_fwd_fp8(const uint8_t* __re
   }
   bool move = __builtin_amdgcn_ballot_w64(mx_cur > m_run + kLazy8) != 0;
 
-  for (int jb = 0; jb < topk; jb += 6) {
-#pragma unroll
-    for (int u = 0; u < 6; ++u) {
-      const int nb = jb + u;
-      if (nb < topk) {
-        wait_vmcnt<NI8>();  // K(nb+1), V(nb-1) in; K(nb+2) may stay in flight
-        pipeline_barrier();
-        i32x8 ka[2][DC];
-        read_k8<D>(sm.k[(u + 1) % 3], 0, hf, prow, ka[0]);
-        read_k8<D>(sm.k[(u + 1) % 3], 1, hf, prow, ka[1]);
-        float alpha = 1.f;
-        const bool resc = move;
-        if (resc) {
-          const float row_max = fmaxf(mx_cur, __shfl_xor(mx_cur, 32));
-          const bool grow = row_max > m_run + kLazy8;
-          alpha = grow ? __builtin_amdgcn_exp2f(m_run - row_max) : 1.f;
-          m_run = grow ? row_max : m_run;
-        }
-        const float mc = (m_run == -INFINITY) ? 0.f : m_run - kShift8;
-        const int j_next = blk(nb + 1);
-        const float c_next = cblk(j_next);
-        f32x16 s_next[2];
-        float mx_next;
-        i32x8 p_cur;
-        // Past the last block the padding loads of K target a zero-size range: no memory traffic.
-        step8<D, PARTIAL>(ka, sm.v[(u + 1) % 2], n, ones, qf, s_cur, s_next, mx_next, p_prev, p_cur, o, c_cur, mc, g, j_next, hf,
-                          make_rsrc(vbase + 64LL * blk(nb) * D, 64 * D), sm.v[u % 2] + wq * NI8 * 1024, off.v,
-                          (nb + 3 < topk ? make_rsrc(kbase + 64LL * blk(nb + 3) * D, 64 * D) : make_rsrc(kbase, 0)), sm.k[u % 3] + wq * NI8 * 1024,
-                          off.k);
-        mx_next *= c_next;
-        move = __builtin_amdgcn_ballot_w64(mx_next > m_run + kLazy8) != 0;
-        if (resc) {
-#pragma unroll
-          for (int dt = 0; dt <= DT; ++dt) o[dt] *= alpha;
-        }
-        s_cur[0] = s_next[0];
-        s_cur[1] = s_next[1];
-        c_cur = c_next;
-        mx_cur = mx_next;
-        p_prev = p_cur;
-      }
+  // One step, u = nb % 6 (compile-time).  Full groups of six steps run
+  // without a per-step guard, so the values a step hands to the next stay in
+  // place instead of being copied where a guarded step would rejoin; at most
+  // five guarded steps finish the list.
+  auto run_step = [&](int nb, auto uc) {
+    constexpr int u = decltype(uc)::value;
+    wait_vmcnt<NI8>();  // K(nb+1), V(nb-1) in; K(nb+2) may stay in flight
+    pipeline_barrier();
+    i32x8 ka[2][DC];
+    read_k8<D>(sm.k[(u + 1) % 3], 0, hf, prow, ka[0]);
+    read_k8<D>(sm.k[(u + 1) % 3], 1, hf, prow, ka[1]);
+    float alpha = 1.f;
+    const bool resc = move;
+    if (resc) {
+      const float row_max = fmaxf(mx_cur, __shfl_xor(mx_cur, 32));
+      const bool grow = row_max > m_run + kLazy8;
+      alpha = grow ? __builtin_amdgcn_exp2f(m_run - row_max) : 1.f;
+      m_run = grow ? row_max : m_run;
     }
+    const float mc = (m_run == -INFINITY) ? 0.f : m_run - kShift8;
+    const int j_next = blk(nb + 1);
+    const float c_next = cblk(j_next);
+    f32x16 s_next[2];
+    float mx_next;
+    i32x8 p_cur;
+    // Past the last block the padding loads of K target a zero-size range: no memory traffic.
+    step8<D, PARTIAL>(ka, sm.v[(u + 1) % 2], n, ones, qf, s_cur, s_next, mx_next, p_prev, p_cur, o, c_cur, mc, g, j_next, hf,
+                      make_rsrc(vbase + 64LL * blk(nb) * D, 64 * D), sm.v[u % 2] + wq * NI8 * 1024, off.v,
+                      (nb + 3 < topk ? make_rsrc(kbase + 64LL * blk(nb + 3) * D, 64 * D) : make_rsrc(kbase, 0)), sm.k[u % 3] + wq * NI8 * 1024,
+                      off.k);
+    mx_next *= c_next;
+    move = __builtin_amdgcn_ballot_w64(mx_next > m_run + kLazy8) != 0;
+    if (resc) {
+#pragma unroll
+      for (int dt = 0; dt <= DT; ++dt) o[dt] *= alpha;
+    }
+    s_cur[0] = s_next[0];
+    s_cur[1] = s_next[1];
+    c_cur = c_next;
+    mx_cur = mx_next;
+    p_prev = p_cur;
+  };
+  int jb = 0;
+  for (; jb + 6 <= topk; jb += 6) {
+    run_step(jb, StepC<0>{});
+    run_step(jb + 1, StepC<1>{});
+    run_step(jb + 2, StepC<2>{});
+    run_step(jb + 3, StepC<3>{});
+    run_step(jb + 4, StepC<4>{});
+    run_step(jb + 5, StepC<5>{});
   }
+  if (jb < topk) run_step(jb, StepC<0>{});
+  if (jb + 1 < topk) run_step(jb + 1, StepC<1>{});
+  if (jb + 2 < topk) run_step(jb + 2, StepC<2>{});
+  if (jb + 3 < topk) run_step(jb + 3, StepC<3>{});
+  if (jb + 4 < topk) run_step(jb + 4, StepC<4>{});
   {
     wait_vmcnt<NI8>();
     pipeline_barrier();

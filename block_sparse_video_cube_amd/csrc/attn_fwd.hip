@@ -153,52 +153,65 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd(const uint16_t* __restri
   // (max -inf) never triggers it.
   bool move = __builtin_amdgcn_ballot_w64(mx_cur > m_run + lazy_raw) != 0;
 
-  for (int jb = 0; jb < topk; jb += 6) {
-#pragma unroll
-    for (int u = 0; u < 6; ++u) {
-      const int nb = jb + u;
-      if (nb < topk) {
-        // Outstanding, oldest first: K(nb+1), V(nb-1), K(nb+2).
-        wait_vmcnt<NI>();
-        pipeline_barrier();
-        bf16x8 ka[DC];
-        bf16x8 va[DT][2];
-        read_k<D>(sm.k[(u + 1) % 3], wk, hf, prow, ka);
-        read_v<D>(sm.v[(u + 1) % 2], wk, hf, n, va);
-        float alpha = 1.f;
-        const bool resc = move;
-        if (resc) {
-          const float row_max = fmaxf(mx_cur, __shfl_xor(mx_cur, 32));
-          const bool grow = row_max > m_run + lazy_raw;
-          alpha = grow ? __builtin_amdgcn_exp2f((m_run - row_max) * scale_log2) : 1.f;
-          m_run = grow ? row_max : m_run;
-          l_run *= alpha;
-        }
-        // Until a valid key has been seen every logit is -inf and p must be 0.
-        const float mc = (m_run == -INFINITY) ? 0.f : m_run * scale_log2;
-        f32x16 s_next;
-        float mx_next;
-        bf16x8 p_cur[2];
-        // Past the last block the padding loads target a zero-size range: no memory traffic.
-        const __amdgpu_buffer_rsrc_t krs = (nb + 3 < topk)
-            ? k_tile_rsrc<D, PARTIAL, KRASTER>(kbase, g, blk(nb + 3), toff.k, roff, rrow, kto)
-            : make_rsrc(kbase, 0);
-        step<D, PARTIAL>(ka, va, qf, s_cur, s_next, mx_next, p_prev, p_cur, o, l_run, mc, scale_log2, g,
-                         blk(nb + 1), wk, hf, make_rsrc(vbase + 64LL * blk(nb) * D, 64 * D * 2),
-                         sm.v[u % 2] + w * NI * 8 * 64, toff.v, krs, sm.k[u % 3] + w * NI * KRPI * D, kto);
-        move = __builtin_amdgcn_ballot_w64(mx_next > m_run + lazy_raw) != 0;
-        if (resc) {
-          // O^T now holds P(0..n-1) V at the previous reference max.
-#pragma unroll
-          for (int dt = 0; dt < DT; ++dt) o[dt] *= alpha;
-        }
-        s_cur = s_next;
-        mx_cur = mx_next;
-        p_prev[0] = p_cur[0];
-        p_prev[1] = p_cur[1];
-      }
+  // One step, u = nb % 6 (compile-time).  Full groups of six steps run
+  // without a per-step guard, so the values a step hands to the next (S^T,
+  // its max, P) stay in place instead of being copied where a guarded step
+  // would rejoin; at most five guarded steps finish the list.
+  auto run_step = [&](int nb, auto uc) {
+    constexpr int u = decltype(uc)::value;
+    // Outstanding, oldest first: K(nb+1), V(nb-1), K(nb+2).
+    wait_vmcnt<NI>();
+    pipeline_barrier();
+    bf16x8 ka[DC];
+    bf16x8 va[DT][2];
+    read_k<D>(sm.k[(u + 1) % 3], wk, hf, prow, ka);
+    read_v<D>(sm.v[(u + 1) % 2], wk, hf, n, va);
+    float alpha = 1.f;
+    const bool resc = move;
+    if (resc) {
+      const float row_max = fmaxf(mx_cur, __shfl_xor(mx_cur, 32));
+      const bool grow = row_max > m_run + lazy_raw;
+      alpha = grow ? __builtin_amdgcn_exp2f((m_run - row_max) * scale_log2) : 1.f;
+      m_run = grow ? row_max : m_run;
+      l_run *= alpha;
     }
+    // Until a valid key has been seen every logit is -inf and p must be 0.
+    const float mc = (m_run == -INFINITY) ? 0.f : m_run * scale_log2;
+    f32x16 s_next;
+    float mx_next;
+    bf16x8 p_cur[2];
+    // Past the last block the padding loads target a zero-size range: no memory traffic.
+    const __amdgpu_buffer_rsrc_t krs = (nb + 3 < topk)
+        ? k_tile_rsrc<D, PARTIAL, KRASTER>(kbase, g, blk(nb + 3), toff.k, roff, rrow, kto)
+        : make_rsrc(kbase, 0);
+    step<D, PARTIAL>(ka, va, qf, s_cur, s_next, mx_next, p_prev, p_cur, o, l_run, mc, scale_log2, g,
+                     blk(nb + 1), wk, hf, make_rsrc(vbase + 64LL * blk(nb) * D, 64 * D * 2),
+                     sm.v[u % 2] + w * NI * 8 * 64, toff.v, krs, sm.k[u % 3] + w * NI * KRPI * D, kto);
+    move = __builtin_amdgcn_ballot_w64(mx_next > m_run + lazy_raw) != 0;
+    if (resc) {
+      // O^T now holds P(0..n-1) V at the previous reference max.
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) o[dt] *= alpha;
+    }
+    s_cur = s_next;
+    mx_cur = mx_next;
+    p_prev[0] = p_cur[0];
+    p_prev[1] = p_cur[1];
+  };
+  int jb = 0;
+  for (; jb + 6 <= topk; jb += 6) {
+    run_step(jb, StepC<0>{});
+    run_step(jb + 1, StepC<1>{});
+    run_step(jb + 2, StepC<2>{});
+    run_step(jb + 3, StepC<3>{});
+    run_step(jb + 4, StepC<4>{});
+    run_step(jb + 5, StepC<5>{});
   }
+  if (jb < topk) run_step(jb, StepC<0>{});
+  if (jb + 1 < topk) run_step(jb + 1, StepC<1>{});
+  if (jb + 2 < topk) run_step(jb + 2, StepC<2>{});
+  if (jb + 3 < topk) run_step(jb + 3, StepC<3>{});
+  if (jb + 4 < topk) run_step(jb + 4, StepC<4>{});
   {
     // Last product: P(topk-1) V(topk-1).
     wait_vmcnt<NI>();

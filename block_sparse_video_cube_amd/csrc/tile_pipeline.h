@@ -16,6 +16,13 @@ namespace tiles {
 
 constexpr int kThreads = 256;  // four wavefronts per query cube
 
+// A compile-time step index (a ring slot is a function of it), passed to
+// generic lambdas that run one pipeline step.
+template <int N>
+struct StepC {
+  static constexpr int value = N;
+};
+
 // Wait until at most N vector-memory loads of this wavefront are in flight
 // (s_waitcnt vmcnt(N), gfx9 encoding: vmcnt in bits 3:0 and 15:14, the other
 // counters left at their maximum).  Loads complete in issue order, so this
