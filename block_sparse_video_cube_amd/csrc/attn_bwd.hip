@@ -479,11 +479,14 @@ __global__ void __launch_bounds__(2 * kThreads, 1) bwd_dkdv(const uint16_t* __re
         bop[1] = __builtin_bit_cast(bf16x8, make_uint4(bw[4], bw[5], bw[6], bw[7]));
       }
     };
-    for (int m = 0; m < steps; m += 3) {
+    int m = 0;
+    for (; m + 3 <= steps; m += 3) {  // full groups: no per-step guard, no register copies between steps
       step(m, SlotC<0>{});
-      if (m + 1 < steps) step(m + 1, SlotC<1>{});
-      if (m + 2 < steps) step(m + 2, SlotC<2>{});
+      step(m + 1, SlotC<1>{});
+      step(m + 2, SlotC<2>{});
     }
+    if (m < steps) step(m, SlotC<0>{});
+    if (m + 1 < steps) step(m + 1, SlotC<1>{});
   } else {
     auto step = [&](int m, auto slot) {
       constexpr int S = decltype(slot)::value, S2 = (S + 2) % 3;  // S2: also (m - 1) % 3
@@ -523,11 +526,14 @@ __global__ void __launch_bounds__(2 * kThreads, 1) bwd_dkdv(const uint16_t* __re
         if (m + 2 < cnt) issue(m + 2, S2);
       }
     };
-    for (int m = 0; m < steps; m += 3) {
+    int m = 0;
+    for (; m + 3 <= steps; m += 3) {  // full groups: no per-step guard, no register copies between steps
       step(m, SlotC<0>{});
-      if (m + 1 < steps) step(m + 1, SlotC<1>{});
-      if (m + 2 < steps) step(m + 2, SlotC<2>{});
+      step(m + 1, SlotC<1>{});
+      step(m + 2, SlotC<2>{});
     }
+    if (m < steps) step(m, SlotC<0>{});
+    if (m + 1 < steps) step(m + 1, SlotC<1>{});
   }
 
   // The two query halves hold partial sums of the same dK^T (dV^T): add them.
