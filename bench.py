@@ -112,40 +112,46 @@ def cpu_baseline(wl, budget_s: float):
         threads = 1
     valid = oracle.valid_rows(wl.grid)
     scale = wl.softmax_scale
-    cubes_done = 0
     n_heads = wl.batch * wl.heads
-    # One head: permute + pool + score + top-k of all rows (fixed per head),
-    # then query cubes one by one until the time budget is spent.
-    b, h = 0, 0
-    sub = {n: workloads.make_head(wl, n, b, h)[None, :, None, :] for n in ("q", "k", "v")}
-    t0 = time.perf_counter()
-    qc, kc, vc = (oracle.cube_permute(sub[n], wl.grid) for n in ("q", "k", "v"))
-    if wl.pattern == "sta":
-        idx = oracle.sta_index(wl.grid, wl.window)[None, None]
-    else:
-        idx = oracle.select_topk(qc, kc, valid, wl.topk)
-    states = oracle.vsa_oracle._cube_states(kc[0, 0], vc[0, 0], valid) if wl.linear else None
-    per_head_fixed = time.perf_counter() - t0
-    t1 = time.perf_counter()
-    for i in range(wl.n_cubes):
-        oracle.attention_cube(qc[0, 0, 64 * i:64 * i + 64], kc[0, 0], vc[0, 0], valid, idx[0, 0, i], scale)
-        if wl.linear:
-            oracle.linear_cube(qc[0, 0, 64 * i:64 * i + 64], states, idx[0, 0, i])
-        cubes_done += 1
-        if time.perf_counter() - t1 > budget_s:
+    # Whole heads in order, each: permute + pool + score + top-k of all rows,
+    # then its query cubes one by one, until the time budget is spent (the
+    # last head may stop part-way; its remaining cubes are estimated from its
+    # own per-cube time).
+    head_s, cubes_total, t0 = [], 0, time.perf_counter()
+    for bh in range(n_heads):
+        b, h = divmod(bh, wl.heads)
+        sub = {n: workloads.make_head(wl, n, b, h)[None, :, None, :] for n in ("q", "k", "v")}
+        th = time.perf_counter()
+        qc, kc, vc = (oracle.cube_permute(sub[n], wl.grid) for n in ("q", "k", "v"))
+        if wl.pattern == "sta":
+            idx = oracle.sta_index(wl.grid, wl.window)[None, None]
+        else:
+            idx = oracle.select_topk(qc, kc, valid, wl.topk)
+        states = oracle.vsa_oracle._cube_states(kc[0, 0], vc[0, 0], valid) if wl.linear else None
+        fixed = time.perf_counter() - th
+        t1, done = time.perf_counter(), 0
+        for i in range(wl.n_cubes):
+            oracle.attention_cube(qc[0, 0, 64 * i:64 * i + 64], kc[0, 0], vc[0, 0], valid, idx[0, 0, i], scale)
+            if wl.linear:
+                oracle.linear_cube(qc[0, 0, 64 * i:64 * i + 64], states, idx[0, 0, i])
+            done += 1
+            if time.perf_counter() - t0 > budget_s:
+                break
+        head_s.append(fixed + wl.n_cubes * (time.perf_counter() - t1) / done)
+        cubes_total += done
+        if time.perf_counter() - t0 > budget_s:
             break
-    per_cube = (time.perf_counter() - t1) / cubes_done
     t_total = time.perf_counter() - t0
-    layer_s = n_heads * (per_head_fixed + wl.n_cubes * per_cube)
+    layer_s = n_heads * float(np.mean(head_s))
     return {
         "value": wl.fine_flops / layer_s / 1e12,
         "unit": "TFLOP/s",
         "cores": int(threads),
         "kind": "oracle",
-        "sample": (f"fp64 numpy oracle, head (b=0,h=0) of {wl.name}: permute+"
+        "sample": (f"fp64 numpy oracle on {len(head_s)} of {n_heads} heads of {wl.name} (each: permute+"
                    f"{'sliding-tile lists' if wl.pattern == 'sta' else 'pool+score+top-k'} of all "
-                   f"{wl.n_cubes} rows plus {cubes_done} of {wl.n_cubes} query cubes "
-                   f"({t_total:.1f} s), scaled to {n_heads} heads"),
+                   f"{wl.n_cubes} rows, then its query cubes; {cubes_total} query cubes in all, "
+                   f"{t_total:.1f} s), scaled to {n_heads} heads"),
         "ms_per_layer": layer_s * 1e3,
         "host_cpus": os.cpu_count(),
         "cpu_model": platform.processor() or platform.machine(),
