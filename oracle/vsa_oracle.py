@@ -64,6 +64,15 @@ fits them, with these conventions (each is a reading, not a quote):
       same number of key cubes (the whole axis when the window is wider).
       The pages name the pattern but give no window; this is the reading.
 
+  O12 packed cube layouts (a data layout, not a step of the method; the
+      pages only fix that blocks are whole cubes, so the order of tokens
+      inside a cube is free): "compact" order puts a cube's valid tokens
+      first, in raster order within the cube, then its padded slots, so a
+      cube with n valid tokens fills rows 0 .. n-1 of its 64.  The "slots"
+      layout cuts each compact cube into four 16-row slots and stores each
+      slot transposed (channel-major).  For a full cube compact order is the
+      O1 order.
+
 Every step is written as its definition, in float64, with no blocking,
 fusion or reordering beyond the definition.  Inputs are bf16 bit patterns
 (numpy uint16); they are widened exactly to float64 here.
@@ -85,6 +94,9 @@ __all__ = [
     "valid_rows",
     "cube_permute",
     "cube_unpermute",
+    "compact_order",
+    "cube_permute_compact",
+    "cube_slots",
     "cube_means",
     "block_scores",
     "topk_row",
@@ -190,6 +202,52 @@ def cube_unpermute(xc: np.ndarray, grid: Sequence[int]) -> np.ndarray:
     out = np.zeros((B, rows.size, Hh, D), dtype=xc.dtype)
     for s in range(rows.size):
         out[:, s, :, :] = xc[:, :, rows[s], :]
+    return out
+
+
+def compact_order(grid: Sequence[int]) -> np.ndarray:
+    """int[Nc, 64]: for each cube, its local indices l (O1) in compact order
+    (O12): the valid ones ascending, then the padded ones ascending."""
+    T, H, W = grid
+    nct, ncy, ncx = cube_grid(grid)
+    order = np.empty((n_cubes(grid), 64), dtype=np.int64)
+    for ct in range(nct):
+        for cy in range(ncy):
+            for cx in range(ncx):
+                c = (ct * ncy + cy) * ncx + cx
+                real, pad = [], []
+                for lt in range(4):
+                    for ly in range(4):
+                        for lx in range(4):
+                            l = (lt * 4 + ly) * 4 + lx
+                            inside = 4 * ct + lt < T and 4 * cy + ly < H and 4 * cx + lx < W
+                            (real if inside else pad).append(l)
+                order[c] = real + pad
+    return order
+
+
+def cube_permute_compact(x: np.ndarray, grid: Sequence[int]) -> np.ndarray:
+    """[B, S, H, D] raster tokens -> [B, H, Np, D] cube-major rows in compact
+    order (O12): row 64 c + r holds local token compact_order(grid)[c, r];
+    padded rows are zero."""
+    xc = cube_permute(x, grid)
+    order = compact_order(grid)
+    out = np.zeros_like(xc)
+    for c in range(order.shape[0]):
+        for r in range(64):
+            out[:, :, 64 * c + r, :] = xc[:, :, 64 * c + order[c, r], :]
+    return out
+
+
+def cube_slots(xc_compact: np.ndarray) -> np.ndarray:
+    """[B, H, Np, D] compact rows -> [B, H, Nc, 4, D, 16] (O12): element
+    (c, s, d, e) is channel d of compact row 16 s + e of cube c."""
+    B, Hh, Np, D = xc_compact.shape
+    out = np.zeros((B, Hh, Np // 64, 4, D, 16), dtype=xc_compact.dtype)
+    for c in range(Np // 64):
+        for s_ in range(4):
+            for e in range(16):
+                out[:, :, c, s_, :, e] = xc_compact[:, :, 64 * c + 16 * s_ + e, :]
     return out
 
 

@@ -76,3 +76,58 @@ def test_720p_every_cube_has_valid_tokens():
     assert counts.min() >= 4
     assert set(np.unique(counts)) <= {4, 16, 64}
     assert v.sum() == 21 * 45 * 80
+
+
+# ---------------------------------------------------------------- O12 layouts
+
+@pytest.mark.parametrize("grid", GRIDS + [(21, 45, 20), (6, 7, 5)])
+def test_compact_rows_are_the_valid_rows_first(grid):
+    # Independent construction: the O1 rows of each cube, split by the valid
+    # mask with a boolean selection (valid ones first, in row order, then the
+    # zero pads).
+    T, H, W = grid
+    rng = np.random.default_rng(3)
+    x = rng.integers(1, 60000, size=(2, T * H * W, 2, 3)).astype(np.uint16)
+    xc = oracle.cube_permute(x, grid)
+    valid = oracle.valid_rows(grid)
+    got = oracle.cube_permute_compact(x, grid)
+    for c in range(oracle.n_cubes(grid)):
+        rows = xc[:, :, 64 * c:64 * c + 64]
+        v = valid[64 * c:64 * c + 64]
+        n = int(v.sum())
+        assert np.array_equal(got[:, :, 64 * c:64 * c + n], rows[:, :, v])
+        assert np.all(got[:, :, 64 * c + n:64 * c + 64] == 0)
+    order = oracle.compact_order(grid)
+    assert all(sorted(order[c]) == list(range(64)) for c in range(order.shape[0]))
+
+
+def test_compact_equals_o1_order_on_full_grids():
+    x = np.random.default_rng(4).integers(0, 65536, size=(1, 8 * 4 * 12, 2, 4)).astype(np.uint16)
+    assert np.array_equal(oracle.cube_permute_compact(x, (8, 4, 12)), oracle.cube_permute(x, (8, 4, 12)))
+
+
+def test_compact_worked_example():
+    # Grid 4x5x4: cubes (0,0,0) full and (0,1,0) with one valid y row (y = 4).
+    # Its valid tokens (t, 4, x) in raster order sit at compact rows t*4 + x;
+    # token (1, 4, 2) is raster token (1*5 + 4)*4 + 2 = 38, compact row
+    # 64 + 6.  Its O1 local index is (1*4 + 0)*4 + 2 = 18.
+    grid = (4, 5, 4)
+    x = np.zeros((1, 80, 1, 1), dtype=np.uint16)
+    x[0, 38, 0, 0] = 777
+    assert oracle.cube_permute(x, grid)[0, 0, 64 + 18, 0] == 777
+    xc = oracle.cube_permute_compact(x, grid)
+    assert xc[0, 0, 64 + 6, 0] == 777 and int((xc != 0).sum()) == 1
+    assert list(oracle.compact_order(grid)[1, :16]) == [0, 1, 2, 3, 16, 17, 18, 19, 32, 33, 34, 35, 48, 49, 50, 51]
+
+
+def test_slots_layout_index_map():
+    grid = (5, 6, 7)
+    rng = np.random.default_rng(5)
+    x = rng.integers(1, 60000, size=(1, 5 * 6 * 7, 2, 8)).astype(np.uint16)
+    xc = oracle.cube_permute_compact(x, grid)
+    sl = oracle.cube_slots(xc)
+    nc = oracle.n_cubes(grid)
+    assert sl.shape == (1, 2, nc, 4, 8, 16)
+    # Slot-major, each 16-row slot transposed: a reshape/transpose of the rows.
+    ref = xc.reshape(1, 2, nc, 4, 16, 8).transpose(0, 1, 2, 3, 5, 4)
+    assert np.array_equal(sl, ref)
