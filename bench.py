@@ -1,13 +1,14 @@
 """Benchmark: one cube block-sparse attention layer (forward) on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload wan1.3b]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 720p]
 
 A step is one pass of the whole layer on inputs already resident in HBM:
 permute Q, K, V (cube means of Q and K pooled in the same pass) -> coarse
 stage (block scores, top-k) -> fine block-sparse attention -> (linear
-branch, hybrid workload) -> unpermute.  The default
-workload is the Wan2.1-1.3B-shaped layer (latent 16x28x52, 12 heads,
-head_dim 128, sparsity 0.8 -> k = 73 of 364 cubes).
+branch, hybrid workload) -> unpermute.  The default workload is the largest
+one-GPU layer, 720P video (81 frames at 720x1280: latent 21x45x80, padded to
+24x48x80, 1440 cubes, 40 heads, head_dim 128, sparsity 0.9 -> k = 144).
+The others (wan1.3b, wan14b, hybrid, sta, tiny) are selected with --workload.
 
 Prints one JSON line.  `value` is the effective throughput of the whole
 layer: the flops of the computed 64x64 blocks (4 * 64 * 64 * D each, QK^T
@@ -41,13 +42,16 @@ METRIC = "ms/layer + effective TFLOPS (frac of bf16 MFMA peak), block-sparse att
 def parse():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="wan1.3b")
+    ap.add_argument("--workload", default="720p")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target oracle sample time")
     ap.add_argument("--k-raster", action="store_true",
                     help="let the fine stage gather K tiles from raster rows too (no K permute)")
+    ap.add_argument("--unpacked", action="store_true",
+                    help="the unpacked fine stage (one 64-key tile per selected cube, K token-major, V "
+                         "cube-transposed) instead of the packed one (cubes with few valid keys share tiles)")
     ap.add_argument("--backward", action="store_true",
                     help="also time the backward of the fine stage (dQ, dK, dV) after the forward steps; "
                          "reported under 'backward', not in 'value'")
@@ -308,30 +312,19 @@ def main():
     g = vsa.make_geom(wl.batch, wl.heads, wl.head_dim, wl.grid)
     d = vsa.geom_dims(g)
     B, H, D = wl.batch, wl.heads, wl.head_dim
-    qc = torch.empty((B, H, d.rows, D), dtype=torch.bfloat16, device=dev)
-    qbar = torch.empty((B, H, d.n_cubes, D), dtype=torch.float32, device=dev)
-    kbar = torch.empty_like(qbar)
-    kc = torch.empty_like(qc)
-    vt = torch.empty((B, H, d.n_cubes, D, 64), dtype=torch.bfloat16, device=dev)
-    oc = torch.empty_like(qc)
+    bufs = vsa.LayerBuffers(B, H, D, wl.grid, wl.topk, linear=wl.linear, device=dev)
+    qc, kc, vt, qbar, kbar, idx = bufs.qc, bufs.kc, bufs.vt, bufs.qbar, bufs.kbar, bufs.idx
+    ws_sel = bufs.ws_sel
     o = torch.empty_like(q)
-    idx = torch.empty((B, H, d.n_cubes, wl.topk), dtype=torch.int32, device=dev)
-    ws_sel = torch.empty(vsa.workspace_bytes(g), dtype=torch.uint8, device=dev)
-    ws_lin = torch.empty(max(16, vsa.workspace_bytes(g, linear=True)) if wl.linear else 16,
-                         dtype=torch.uint8, device=dev)
-    of = torch.empty((B, H, d.rows, D), dtype=torch.float32, device=dev) if wl.linear and not args.fused_linear else None
-    oc2 = torch.empty_like(qc) if wl.linear else None
 
-    # Without the linear branch the fine stage reads Q and writes the output in
-    # raster order: Q is only pooled, K is pooled and permuted in one pass
-    # (contiguous 16 KB tiles stream faster than tiles gathered from 64 raster
-    # rows; --k-raster gathers them instead), V is permuted into the
-    # cube-transposed layout.  The linear branch works on cube-major rows, so
-    # the hybrid layer keeps the permute / unpermute pair.
-    stages = ["pool", "select", "fine"]
-    if wl.linear:
-        stages = (["permute", "select", "fine+linear", "unpermute"] if args.fused_linear else
-                  ["permute", "select", "fine", "linear", "unpermute"])
+    # The layer's chain (vsa.layer_forward; the full-size GPU tests run the
+    # same function): without the linear branch the fine stage reads Q and
+    # writes the output in raster order, Q is only pooled, K is pooled and
+    # permuted in one pass (contiguous 16 KB tiles stream faster than tiles
+    # gathered from 64 raster rows; --k-raster gathers them instead), V is
+    # permuted into the cube-transposed layout.  The linear branch works on
+    # cube-major rows, so the hybrid layer keeps the permute / unpermute pair.
+    stages = vsa.layer_stages(wl.linear, args.fused_linear)
     if args.fp8:
         if wl.linear:
             print("--fp8 covers the fine stage without the linear branch", file=sys.stderr)
@@ -370,49 +363,11 @@ def main():
         if args.fp8:
             step_fp8(ev)
             return
-
-        def mark(i):
-            if ev is not None:
-                ev[i].record()
-
-        mark(0)
-        if wl.linear:
-            vsa.cube_permute_pool(q, wl.grid, out=qc, mean_out=qbar)
-            vsa.cube_permute_pool(k, wl.grid, out=kc, mean_out=kbar)
-        elif wl.pattern != "sta":
-            vsa.cube_pool(q, wl.grid, mean_out=qbar)
-            if args.k_raster:
-                vsa.cube_pool(k, wl.grid, mean_out=kbar)
-            else:
-                vsa.cube_permute_pool(k, wl.grid, out=kc, mean_out=kbar)
-        elif not args.k_raster:
-            vsa.cube_permute(k, wl.grid, out=kc)
-        vsa.cube_permute(v, wl.grid, layout="dim", out=vt)
-        mark(1)
-        if wl.pattern == "sta":
-            # The sliding-tile list is static; it is rebuilt every layer here all the same.
-            vsa.sta_index(wl.grid, wl.window, B, H, head_dim=D, out=idx)
-        else:
-            vsa.select_topk_pooled(qbar, kbar, wl.grid, wl.topk, out=idx, workspace=ws_sel)
-        mark(2)
-        if not wl.linear:
-            vsa.sparse_attn_fwd_raster(q, k if args.k_raster else kc, vt, idx, wl.grid, wl.softmax_scale, out=o)
-            mark(3)
-            return
-        if args.fused_linear:
-            # One pass: softmax branch and the linear branch's selected-block
-            # correction on the same tiles, combined in the kernel.
-            vsa.sparse_attn_linear_fwd(qc, kc, vt, idx, wl.grid, wl.softmax_scale, out=oc2, workspace=ws_lin)
-            mark(3)
-            vsa.cube_unpermute(oc2, wl.grid, out=o)
-            mark(4)
-            return
-        vsa.sparse_attn_fwd(qc, kc, vt, idx, wl.grid, wl.softmax_scale, out=oc, out_f32=of)
-        mark(3)
-        vsa.linear_branch(qc, kc, vt, idx, of, wl.grid, out=oc2, workspace=ws_lin)
-        mark(4)
-        vsa.cube_unpermute(oc2, wl.grid, out=o)
-        mark(5)
+        vsa.layer_forward(q, k, v, wl.grid, wl.topk, wl.softmax_scale, linear=wl.linear,
+                          fused_linear=args.fused_linear, k_raster=args.k_raster,
+                          window=wl.window if wl.pattern == "sta" else None, bufs=bufs, out=o,
+                          mark=(lambda i: ev[i].record()) if ev is not None else None,
+                          packed=not args.unpacked)
 
     for _ in range(args.warmup):
         step()
@@ -481,7 +436,9 @@ def main():
             "tokens": wl.tokens, "n_cubes": wl.n_cubes, "topk": wl.topk,
             "sparsity": wl.sparsity, "linear_branch": wl.linear, "pattern": wl.pattern,
             "layout": ("cube-major" if wl.linear else "raster q, k, v in; fp8 cube-major codes; raster o"
-                       if args.fp8 else ("raster q/k/o" if args.k_raster else "raster q/o")),
+                       if args.fp8 else ("raster q/k/o" if args.k_raster else
+                                         "raster q/o" + ("" if args.unpacked else
+                                                         "; packed tiles: compact k, slot-layout v"))),
             **({"precision": "fp8 e4m3: Q, K per cube, V per channel; P e4m3"} if args.fp8 else {}),
             **({"window_cubes": list(wl.window)} if wl.window else {}),
             "computed_blocks": wl.blocks, "fine_flops": flops,

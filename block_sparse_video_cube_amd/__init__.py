@@ -45,6 +45,8 @@ __all__ = [
     "sparse_attn_fwd",
     "linear_branch",
     "sparse_attn_fwd_raster",
+    "sparse_attn_fwd_packed",
+    "packed_workspace_bytes",
     "sparse_attn_bwd",
     "sparse_attn_linear_fwd",
     "quant_fp8",
@@ -54,6 +56,9 @@ __all__ = [
     "workspace_bytes",
     "mfma_probe",
     "linear_branch_bwd",
+    "LayerBuffers",
+    "layer_stages",
+    "layer_forward",
 ]
 
 
@@ -90,15 +95,22 @@ def workspace_bytes(g: VsaGeom, linear: bool = False) -> int:
     return int(lib.vsa_linear_workspace_bytes(g) if linear else lib.vsa_select_workspace_bytes(g))
 
 
+_LAYOUTS = {"token": _lib.VSA_LAYOUT_TOKEN_MAJOR, "dim": _lib.VSA_LAYOUT_DIM_MAJOR,
+            "compact": _lib.VSA_LAYOUT_TOKEN_COMPACT, "slots": _lib.VSA_LAYOUT_DIM_SLOTS}
+
+
 def cube_permute(x: torch.Tensor, grid: Sequence[int], layout: str = "token",
                  out: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """[B, S, heads, D] -> [B, heads, Np, D] (layout "token") or [B, heads, Nc, D, 64] ("dim")."""
+    """[B, S, heads, D] -> cube-major: [B, heads, Np, D] (layout "token", or
+    "compact": valid tokens first in each cube), [B, heads, Nc, D, 64] ("dim")
+    or [B, heads, Nc, 4, D, 16] ("slots")."""
     B, S, Hh, D = x.shape
     g = make_geom(B, Hh, D, grid)
     d = geom_dims(g)
     _need(x, "x", torch.bfloat16, (B, d.tokens, Hh, D))
-    code = {"token": VSA_LAYOUT_TOKEN_MAJOR, "dim": VSA_LAYOUT_DIM_MAJOR}[layout]
-    shape = (B, Hh, d.rows, D) if code == VSA_LAYOUT_TOKEN_MAJOR else (B, Hh, d.n_cubes, D, 64)
+    code = _LAYOUTS[layout]
+    shape = {"token": (B, Hh, d.rows, D), "compact": (B, Hh, d.rows, D), "dim": (B, Hh, d.n_cubes, D, 64),
+             "slots": (B, Hh, d.n_cubes, 4, D, 16)}[layout]
     if out is None:
         out = torch.empty(shape, dtype=torch.bfloat16, device=x.device)
     _need(out, "out", torch.bfloat16, shape)
@@ -108,8 +120,9 @@ def cube_permute(x: torch.Tensor, grid: Sequence[int], layout: str = "token",
 
 
 def cube_permute_pool(x: torch.Tensor, grid: Sequence[int], out: Optional[torch.Tensor] = None,
-                      mean_out: Optional[torch.Tensor] = None):
-    """Token-major cube permutation and fp32 cube means in one pass: (xc, mean [B, heads, Nc, D])."""
+                      mean_out: Optional[torch.Tensor] = None, compact: bool = False):
+    """Token-major cube permutation and fp32 cube means in one pass: (xc, mean [B, heads, Nc, D]).
+    compact: xc in compact order (vsa_cube_permute_pool_compact)."""
     B, S, Hh, D = x.shape
     g = make_geom(B, Hh, D, grid)
     d = geom_dims(g)
@@ -120,8 +133,8 @@ def cube_permute_pool(x: torch.Tensor, grid: Sequence[int], out: Optional[torch.
         mean_out = torch.empty((B, Hh, d.n_cubes, D), dtype=torch.float32, device=x.device)
     _need(out, "out", torch.bfloat16, (B, Hh, d.rows, D))
     _need(mean_out, "mean", torch.float32, (B, Hh, d.n_cubes, D))
-    _lib.check("vsa_cube_permute_pool", _lib.load().vsa_cube_permute_pool(
-        g, x.data_ptr(), out.data_ptr(), mean_out.data_ptr(), _stream()))
+    fn = "vsa_cube_permute_pool_compact" if compact else "vsa_cube_permute_pool"
+    _lib.check(fn, getattr(_lib.load(), fn)(g, x.data_ptr(), out.data_ptr(), mean_out.data_ptr(), _stream()))
     return out, mean_out
 
 
@@ -279,6 +292,52 @@ def sparse_attn_fwd_raster(q: torch.Tensor, k: torch.Tensor, vt: torch.Tensor, i
     _lib.check("vsa_sparse_attn_fwd_raster", _lib.load().vsa_sparse_attn_fwd_raster(
         g, q.data_ptr(), k.data_ptr(), k_layout, vt.data_ptr(), idx.data_ptr(), topk, float(scale),
         out.data_ptr(), lse.data_ptr() if lse is not None else None, _stream()))
+    return out, lse
+
+
+def packed_workspace_bytes(g: VsaGeom, topk: int) -> int:
+    return int(_lib.load().vsa_sparse_attn_packed_workspace_bytes(g, int(topk)))
+
+
+def sparse_attn_fwd_packed(q: torch.Tensor, kc: torch.Tensor, vs: torch.Tensor, idx: torch.Tensor,
+                           grid: Sequence[int], scale: Optional[float] = None, want_lse: bool = False,
+                           out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                           raster: bool = True):
+    """Packed fine stage: (o, lse or None).
+
+    q: raster [B, S, heads, D] with o raster (raster=True), or cube-major
+    [B, heads, Np, D] with o cube-major (raster=False); kc: compact cube-major
+    keys; vs: values in the slot layout [B, heads, Nc, 4, D, 16].
+    """
+    if raster:
+        B, S, Hh, D = q.shape
+    else:
+        B, Hh, _, D = q.shape
+    g = make_geom(B, Hh, D, grid)
+    d = geom_dims(g)
+    topk = int(idx.shape[-1])
+    if raster:
+        _need(q, "q", torch.bfloat16, (B, d.tokens, Hh, D))
+    else:
+        _need(q, "qc", torch.bfloat16, (B, Hh, d.rows, D))
+    _need(kc, "kc", torch.bfloat16, (B, Hh, d.rows, D))
+    _need(vs, "vs", torch.bfloat16, (B, Hh, d.n_cubes, 4, D, 16))
+    _need(idx, "idx", torch.int32, (B, Hh, d.n_cubes, topk))
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty_like(q)
+    _need(out, "o", torch.bfloat16, tuple(q.shape))
+    lse = torch.empty((B, Hh, d.rows), dtype=torch.float32, device=q.device) if want_lse else None
+    nbytes = packed_workspace_bytes(g, topk)
+    if workspace is None and nbytes:
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
+    _lib.check("vsa_sparse_attn_fwd_packed", _lib.load().vsa_sparse_attn_fwd_packed(
+        g, q.data_ptr(), _lib.VSA_LAYOUT_RASTER if raster else _lib.VSA_LAYOUT_TOKEN_MAJOR, kc.data_ptr(),
+        vs.data_ptr(), idx.data_ptr(), topk, float(scale), out.data_ptr(),
+        lse.data_ptr() if lse is not None else None,
+        workspace.data_ptr() if workspace is not None else None,
+        workspace.numel() * workspace.element_size() if workspace is not None else 0, _stream()))
     return out, lse
 
 
@@ -555,3 +614,118 @@ def vsa_attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, grid: Seque
     else:
         oc, _, _ = sparse_attn_fwd(qc, kc, vt, idx, grid, scale)
     return cube_unpermute(oc, grid), idx
+
+
+class LayerBuffers:
+    """Device tensors of one forward layer (layer_forward), allocated once so
+    that repeated layers allocate nothing."""
+
+    def __init__(self, batch: int, heads: int, head_dim: int, grid: Sequence[int], topk: int,
+                 linear: bool = False, device="cuda:0"):
+        B, H, D = int(batch), int(heads), int(head_dim)
+        self.geom = g = make_geom(B, H, D, grid)
+        d = geom_dims(g)
+        dev = torch.device(device)
+        self.qc = torch.empty((B, H, d.rows, D), dtype=torch.bfloat16, device=dev)
+        self.kc = torch.empty_like(self.qc)
+        self.vt = torch.empty((B, H, d.n_cubes, D, 64), dtype=torch.bfloat16, device=dev)
+        self.qbar = torch.empty((B, H, d.n_cubes, D), dtype=torch.float32, device=dev)
+        self.kbar = torch.empty_like(self.qbar)
+        self.idx = torch.empty((B, H, d.n_cubes, int(topk)), dtype=torch.int32, device=dev)
+        self.ws_sel = torch.empty(max(16, workspace_bytes(g)), dtype=torch.uint8, device=dev)
+        # Packed fine stage: V in the slot layout and the packing plan.
+        self.vs = torch.empty((B, H, d.n_cubes, 4, D, 16), dtype=torch.bfloat16, device=dev)
+        nplan = packed_workspace_bytes(g, topk)
+        self.ws_plan = torch.empty(nplan, dtype=torch.uint8, device=dev) if nplan else None
+        self.oc = torch.empty_like(self.qc) if linear else None
+        self.oc2 = torch.empty_like(self.qc) if linear else None
+        self.of = torch.empty((B, H, d.rows, D), dtype=torch.float32, device=dev) if linear else None
+        self.ws_lin = (torch.empty(max(16, workspace_bytes(g, linear=True)), dtype=torch.uint8, device=dev)
+                       if linear else None)
+
+
+def layer_stages(linear: bool = False, fused_linear: bool = False):
+    """Names of the stages layer_forward runs, in order (its `mark` hook is
+    called once before the first and once after each)."""
+    if linear:
+        return (["permute", "select", "fine+linear", "unpermute"] if fused_linear else
+                ["permute", "select", "fine", "linear", "unpermute"])
+    return ["pool", "select", "fine"]
+
+
+def layer_forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, grid: Sequence[int], topk: int,
+                  scale: Optional[float] = None, linear: bool = False, fused_linear: bool = False,
+                  k_raster: bool = False, window: Optional[Sequence[int]] = None,
+                  bufs: Optional[LayerBuffers] = None, out: Optional[torch.Tensor] = None, mark=None,
+                  packed: bool = True):
+    """One forward attention layer on raster q, k, v [B, S, heads, D] bf16:
+    returns (o [B, S, heads, D] bf16, idx).
+
+    Without the linear branch the fine stage reads Q and writes O in raster
+    order: Q is only pooled, K is pooled and permuted in one pass, V is
+    permuted; with `packed` (the default) and a grid with partial cubes, K in
+    compact order, V in the slot layout and the packed fine stage (edge cubes
+    share tiles), otherwise K
+    token-major (or, with k_raster, only pooled and its tiles gathered by the
+    fine stage), V cube-transposed and the unpacked stage.  window: a sliding-tile window
+    (cubes per axis) whose static block lists replace the coarse stage.  The
+    linear branch works on cube-major rows, so the hybrid layer permutes Q and
+    K, runs the fine stage and the linear branch (two calls, or one fused pass
+    with fused_linear) and unpermutes.  mark(i), if given, is called before
+    stage 0 and after each stage i - 1 (layer_stages names them).
+    """
+    B, S, H, D = q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if bufs is None:
+        bufs = LayerBuffers(B, H, D, grid, topk, linear=linear, device=q.device)
+    if out is None:
+        out = torch.empty_like(q)
+    mark = mark or (lambda i: None)
+    b = bufs
+    mark(0)
+    # Packing pays only where cubes hold padding; on other grids the packed
+    # stage is the unpacked one with another V layout (and slightly slower).
+    packed = packed and not k_raster and any(int(x) % 4 for x in grid)
+    if linear:
+        cube_permute_pool(q, grid, out=b.qc, mean_out=b.qbar)
+        cube_permute_pool(k, grid, out=b.kc, mean_out=b.kbar)
+    elif window is None:
+        cube_pool(q, grid, mean_out=b.qbar)
+        if k_raster:
+            cube_pool(k, grid, mean_out=b.kbar)
+        else:
+            cube_permute_pool(k, grid, out=b.kc, mean_out=b.kbar, compact=packed)
+    elif not k_raster:
+        cube_permute(k, grid, layout="compact" if packed else "token", out=b.kc)
+    if packed and not linear:
+        cube_permute(v, grid, layout="slots", out=b.vs)
+    else:
+        cube_permute(v, grid, layout="dim", out=b.vt)
+    mark(1)
+    if window is not None:
+        # The sliding-tile list is static; it is rebuilt every layer all the same.
+        sta_index(grid, window, B, H, head_dim=D, out=b.idx)
+    else:
+        select_topk_pooled(b.qbar, b.kbar, grid, topk, out=b.idx, workspace=b.ws_sel)
+    mark(2)
+    if not linear:
+        if packed:
+            sparse_attn_fwd_packed(q, b.kc, b.vs, b.idx, grid, scale, out=out, workspace=b.ws_plan)
+        else:
+            sparse_attn_fwd_raster(q, k if k_raster else b.kc, b.vt, b.idx, grid, scale, out=out)
+        mark(3)
+        return out, b.idx
+    if fused_linear:
+        sparse_attn_linear_fwd(b.qc, b.kc, b.vt, b.idx, grid, scale, out=b.oc2, workspace=b.ws_lin)
+        mark(3)
+        cube_unpermute(b.oc2, grid, out=out)
+        mark(4)
+        return out, b.idx
+    sparse_attn_fwd(b.qc, b.kc, b.vt, b.idx, grid, scale, out=b.oc, out_f32=b.of)
+    mark(3)
+    linear_branch(b.qc, b.kc, b.vt, b.idx, b.of, grid, out=b.oc2, workspace=b.ws_lin)
+    mark(4)
+    cube_unpermute(b.oc2, grid, out=out)
+    mark(5)
+    return out, b.idx

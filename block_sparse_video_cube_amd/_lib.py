@@ -23,6 +23,8 @@ VSA_ERR_WINDOW = 10
 VSA_LAYOUT_TOKEN_MAJOR = 0
 VSA_LAYOUT_DIM_MAJOR = 1
 VSA_LAYOUT_RASTER = 2
+VSA_LAYOUT_TOKEN_COMPACT = 3
+VSA_LAYOUT_DIM_SLOTS = 4
 VSA_MAX_CUBES = 4096
 
 ENTRY_POINTS = (
@@ -51,6 +53,9 @@ ENTRY_POINTS = (
     "vsa_mfma_probe",
     "vsa_linear_bwd_workspace_bytes",
     "vsa_linear_branch_bwd",
+    "vsa_cube_permute_pool_compact",
+    "vsa_sparse_attn_packed_workspace_bytes",
+    "vsa_sparse_attn_fwd_packed",
 )
 
 
@@ -129,6 +134,9 @@ def load() -> ctypes.CDLL:
         "vsa_mfma_probe": (i32, [i32, i32, P, P, P]),
         "vsa_linear_bwd_workspace_bytes": (sz, [G, i32]),
         "vsa_linear_branch_bwd": (i32, [G, P, P, P, P, P, i32, P, P, P, P, P, P, P, P, sz, P]),
+        "vsa_cube_permute_pool_compact": (i32, [G, P, P, P, P]),
+        "vsa_sparse_attn_packed_workspace_bytes": (sz, [G, i32]),
+        "vsa_sparse_attn_fwd_packed": (i32, [G, P, i32, P, P, P, i32, ctypes.c_float, P, P, P, sz, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)

@@ -109,7 +109,9 @@ int32_t vsa_cube_permute(const vsa_geom* g, const uint16_t* x, uint16_t* xc, int
   if (st != VSA_OK) return st;
   if (!x || !xc) return VSA_ERR_NULL;
   if (!aligned16(x) || !aligned16(xc)) return VSA_ERR_ALIGN;
-  if (layout != VSA_LAYOUT_TOKEN_MAJOR && layout != VSA_LAYOUT_DIM_MAJOR) return VSA_ERR_LAYOUT;
+  if (layout != VSA_LAYOUT_TOKEN_MAJOR && layout != VSA_LAYOUT_DIM_MAJOR && layout != VSA_LAYOUT_TOKEN_COMPACT &&
+      layout != VSA_LAYOUT_DIM_SLOTS)
+    return VSA_ERR_LAYOUT;
   return launch_status(vsa::launch_permute(k, x, xc, layout, static_cast<hipStream_t>(stream)));
 }
 
@@ -120,7 +122,50 @@ int32_t vsa_cube_permute_pool(const vsa_geom* g, const uint16_t* x, uint16_t* xc
   if (st != VSA_OK) return st;
   if (!x || !xc || !mean) return VSA_ERR_NULL;
   if (!aligned16(x) || !aligned16(xc) || !aligned16(mean)) return VSA_ERR_ALIGN;
-  return launch_status(vsa::launch_permute_pool(k, x, xc, mean, static_cast<hipStream_t>(stream)));
+  return launch_status(vsa::launch_permute_pool(k, x, xc, mean, false, static_cast<hipStream_t>(stream)));
+}
+
+int32_t vsa_cube_permute_pool_compact(const vsa_geom* g, const uint16_t* x, uint16_t* xc, float* mean,
+                                      void* stream) {
+  vsa_dims d;
+  vsa::KGeom k;
+  int32_t st = prepare(g, &d, &k);
+  if (st != VSA_OK) return st;
+  if (!x || !xc || !mean) return VSA_ERR_NULL;
+  if (!aligned16(x) || !aligned16(xc) || !aligned16(mean)) return VSA_ERR_ALIGN;
+  return launch_status(vsa::launch_permute_pool(k, x, xc, mean, true, static_cast<hipStream_t>(stream)));
+}
+
+size_t vsa_sparse_attn_packed_workspace_bytes(const vsa_geom* g, int32_t topk) {
+  vsa_dims d;
+  vsa::KGeom k;
+  if (prepare(g, &d, &k) != VSA_OK || topk < 1 || topk > d.n_cubes) return 0;
+  return vsa::attn_packed_workspace_bytes(k, topk);
+}
+
+int32_t vsa_sparse_attn_fwd_packed(const vsa_geom* g, const uint16_t* q, int32_t q_layout, const uint16_t* kc,
+                                   const uint16_t* vs, const int32_t* idx, int32_t topk, float softmax_scale,
+                                   uint16_t* o, float* lse, void* ws, size_t ws_bytes, void* stream) {
+  vsa_dims d;
+  vsa::KGeom k;
+  int32_t st = prepare(g, &d, &k);
+  if (st != VSA_OK) return st;
+  if (d.n_cubes >= (1 << 23)) return VSA_ERR_GEOMETRY;  // slot codes hold the cube index in 23 bits
+  if (!q || !kc || !vs || !idx || !o) return VSA_ERR_NULL;
+  if (!aligned16(q) || !aligned16(kc) || !aligned16(vs) || !aligned16(idx) || !aligned16(o) ||
+      (lse && !aligned16(lse)))
+    return VSA_ERR_ALIGN;
+  if (q_layout != VSA_LAYOUT_TOKEN_MAJOR && q_layout != VSA_LAYOUT_RASTER) return VSA_ERR_LAYOUT;
+  if (topk < 1 || topk > d.n_cubes) return VSA_ERR_TOPK;
+  if (!(softmax_scale > 0.f) || !isfinite(softmax_scale)) return VSA_ERR_SCALE;
+  const size_t need = vsa::attn_packed_workspace_bytes(k, topk);
+  if (need) {
+    if (!ws) return VSA_ERR_NULL;
+    if (!aligned16(ws)) return VSA_ERR_ALIGN;
+    if (ws_bytes < need) return VSA_ERR_WORKSPACE;
+  }
+  return launch_status(vsa::launch_attn_fwd_packed(k, q, q_layout == VSA_LAYOUT_RASTER, kc, vs, idx, topk,
+                                                   softmax_scale, o, lse, ws, static_cast<hipStream_t>(stream)));
 }
 
 int32_t vsa_select_topk_pooled(const vsa_geom* g, const float* qbar, const float* kbar, int32_t topk,
@@ -286,7 +331,7 @@ int32_t vsa_cube_pool(const vsa_geom* g, const uint16_t* x, float* mean, void* s
   if (st != VSA_OK) return st;
   if (!x || !mean) return VSA_ERR_NULL;
   if (!aligned16(x) || !aligned16(mean)) return VSA_ERR_ALIGN;
-  return launch_status(vsa::launch_permute_pool(k, x, nullptr, mean, static_cast<hipStream_t>(stream)));
+  return launch_status(vsa::launch_permute_pool(k, x, nullptr, mean, false, static_cast<hipStream_t>(stream)));
 }
 
 int32_t vsa_sparse_attn_fwd(const vsa_geom* g, const uint16_t* qc, const uint16_t* kc, const uint16_t* vt,

@@ -40,12 +40,13 @@ __device__ __forceinline__ float max16(const f32x16& s) {
 // the normaliser.  The tile loads of V(n) and K(n+3) go out one per MFMA slot
 // of S^T(n+1); vr/kr are their buffer resources, vl/kl the LDS destinations
 // of this wave's first instruction, voff/koff its lane offsets.
-template <int D, bool PARTIAL>
+// PARTIAL: mask(s) masks the padded keys of S^T(n+1) (branch-free).
+template <int D, bool PARTIAL, typename Mask>
 __device__ __forceinline__ void step(const bf16x8 (&ka)[D / 16], const bf16x8 (&va)[D / 32][2],
                                      const bf16x8 (&qf)[D / 16], const f32x16& s_cur, f32x16& s_next,
                                      float& mx_next, const bf16x8 (&p_prev)[2], bf16x8 (&p_cur)[2],
-                                     f32x16 (&o)[D / 32], float& l_run, float mc, float scale_log2, const KGeom& g,
-                                     int j_next, int wk, int hf, __amdgpu_buffer_rsrc_t vr, uint16_t* vl,
+                                     f32x16 (&o)[D / 32], float& l_run, float mc, float scale_log2,
+                                     const Mask& mask, __amdgpu_buffer_rsrc_t vr, uint16_t* vl,
                                      const uint32_t* voff, __amdgpu_buffer_rsrc_t kr, uint16_t* kl,
                                      const uint32_t* koff) {
   constexpr int DC = D / 16, DT = D / 32, NI = D / 32, KRPI = 512 / D;
@@ -79,7 +80,7 @@ __device__ __forceinline__ void step(const bf16x8 (&ka)[D / 16], const bf16x8 (&
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk)
       o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[dt][kk], p_prev[kk], o[dt], 0, 0, 0);
-  if (PARTIAL) mask_keys(s_next, g, j_next, wk, hf);
+  if (PARTIAL) mask(s_next);
   mx_next = max16(s_next);
   // P(n) and its row sum are only used by the next step; without this the
   // compiler sinks them out of the interleaved region.

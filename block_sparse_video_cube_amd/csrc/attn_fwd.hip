@@ -59,14 +59,22 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t k_tile_rsrc(const uint16_t* kb
 // by row by the same direct-to-LDS loads (lane offsets from
 // raster_lane_offsets, padded tokens read as zero).  V stays in the
 // cube-transposed layout that the P V product reads.
-template <int D, bool PARTIAL, bool RASTER, bool KRASTER>
+// SLOTS: packed tiles (tile_pipeline.h): K in compact cube-major rows, V in
+// the slot layout [4][D][16] per cube, wavefront w loading slot w of every
+// tile.  With PARTIAL the tiles come from a packing plan (block_plan: up to
+// four cubes with few valid keys share a tile) and keys are masked by slot
+// counts; without it every tile is one whole cube of the list.
+template <int D, bool PARTIAL, bool RASTER, bool KRASTER, bool SLOTS>
 __global__ void __launch_bounds__(kThreads, 2) attn_fwd(const uint16_t* __restrict__ qc,
                                                         const uint16_t* __restrict__ kc,
                                                         const uint16_t* __restrict__ vt,
-                                                        const int32_t* __restrict__ idx, int topk, float scale,
+                                                        const int32_t* __restrict__ idx,
+                                                        const int32_t* __restrict__ plan, int topk, float scale,
                                                         float scale_log2, uint16_t* __restrict__ oc,
                                                         float* __restrict__ oc_f32, float* __restrict__ lse,
                                                         KGeom g, Placement pl) {
+  static_assert(!(SLOTS && KRASTER), "packed tiles read cube-major K");
+  constexpr bool PLAN = SLOTS && PARTIAL;
   constexpr int DC = D / 16, DT = D / 32;
   constexpr int NI = TileOffsets<D>::NI, KRPI = TileOffsets<D>::KRPI;
   __shared__ __attribute__((aligned(16))) Smem<D> sm;
@@ -82,11 +90,30 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd(const uint16_t* __restri
   const uint16_t* kbase = KRASTER ? kc + ((long long)b * g.S * g.H + h) * D : kc + bh * g.Np * D;
   const uint16_t* vbase = vt + bh * g.Np * D;
   const int32_t* irow = idx + (bh * g.nc + i) * topk;
+  // PLAN: the row of the packing plan (a header whose first word is the
+  // number of tiles, then four slot codes per tile).
+  const int32_t* prow = PLAN ? plan + (bh * g.nc + i) * 4LL * (topk + 1) : nullptr;
+  const int ntiles = PLAN ? prow[0] : topk;
   const int q = 32 * wq + n;
   // Past the last block the pipeline keeps issuing loads (into a free buffer;
   // the K loads with a zero-size range, so they move no data) so that the
   // number of loads in flight is the same at every step.
-  const auto blk = [&](int m) { return irow[m < topk ? m : topk - 1]; };
+  const auto blk = [&](int m) { return irow[m < ntiles ? m : ntiles - 1]; };
+  // SLOTS: the code of slot s of tile m (tiles past the end: the last one).
+  const auto slot = [&](int m, int s) {
+    const int mm = m < ntiles ? m : ntiles - 1;
+    return PLAN ? prow[4 * (mm + 1) + s] : ((irow[mm] << 8) | (s << 5) | 16);
+  };
+  // The key mask of tile m for this wavefront (PARTIAL).
+  const auto mask_of = [&](int m) {
+    if constexpr (SLOTS) {
+      const int c0 = slot_count(slot(m, 2 * wk)), c1 = slot_count(slot(m, 2 * wk + 1));
+      return [=](f32x16& s) { mask_slots(s, c0, c1, hf); };
+    } else {
+      const int j = blk(m);
+      return [=, &g](f32x16& s) { mask_keys(s, g, j, wk, hf); };
+    }
+  };
 
   // Pipeline: K(m) lives in K buffer m % 3 and V(m) in V buffer m % 2.
   // Step n waits for K(n+1) and V(n-1), reads them, issues V(n) and K(n+3)
@@ -97,8 +124,29 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd(const uint16_t* __restri
   uint32_t roff[NI];  // RASTER: lane offsets within a cube, and their local rows
   int rrow[NI];
   if (KRASTER) raster_lane_offsets<D>(g, w, lane, roff, rrow);
+  // SLOTS: lane offsets of this wavefront's V slot (one contiguous block).
+  uint32_t vso[NI];
+#pragma unroll
+  for (int e = 0; e < NI; ++e) vso[e] = (uint32_t)(e * 64 + lane) * 16u;
+  const uint32_t* voffs = SLOTS ? vso : toff.v;
   uint32_t kto[NI];
-  issue_k_tile<D>(k_tile_rsrc<D, PARTIAL, KRASTER>(kbase, g, blk(0), toff.k, roff, rrow, kto), sm.k[0], w, kto);
+  // Buffer resource of this wavefront's K loads of tile m (offsets in kto).
+  const auto k_rsrc = [&](int m) {
+    if constexpr (SLOTS) {
+#pragma unroll
+      for (int e = 0; e < NI; ++e) kto[e] = toff.k[e];
+      return k_slot_rsrc<D>(kbase, slot(m, w), w);
+    } else {
+      return k_tile_rsrc<D, PARTIAL, KRASTER>(kbase, g, blk(m), toff.k, roff, rrow, kto);
+    }
+  };
+  // Buffer resource and LDS destination of this wavefront's V loads of tile m.
+  const auto v_rsrc = [&](int m) {
+    if constexpr (SLOTS) return v_slot_rsrc<D>(vbase, slot(m, w));
+    else return make_rsrc(vbase + 64LL * blk(m) * D, 64 * D * 2);
+  };
+  const int vl_off = SLOTS ? w * 16 * D : w * NI * 8 * 64;
+  issue_k_tile<D>(k_rsrc(0), sm.k[0], w, kto);
   // Query row q of cube i: its raster token (RASTER) and whether it is real.
   bool qvalid = true;
   long long qtok = 0;
@@ -116,8 +164,8 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd(const uint16_t* __restri
     for (int dc = 0; dc < DC; ++dc)
       qf[dc] = qvalid ? *reinterpret_cast<const bf16x8*>(qrow + 16 * dc + 8 * hf) : bf16x8{};
   }
-  issue_k_tile<D>(k_tile_rsrc<D, PARTIAL, KRASTER>(kbase, g, blk(1), toff.k, roff, rrow, kto), sm.k[1], w, kto);
-  issue_k_tile<D>(k_tile_rsrc<D, PARTIAL, KRASTER>(kbase, g, blk(2), toff.k, roff, rrow, kto), sm.k[2], w, kto);
+  issue_k_tile<D>(k_rsrc(1), sm.k[1], w, kto);
+  issue_k_tile<D>(k_rsrc(2), sm.k[2], w, kto);
   {
     uint4* z = reinterpret_cast<uint4*>(sm.v[1]);
 #pragma unroll
@@ -127,9 +175,13 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd(const uint16_t* __restri
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) o[dt] = f32x16{};
   float m_run = -INFINITY, l_run = 0.f;
-  const int prow = pi_row(n);
+  const int prow_pi = pi_row(n);
   const float lazy_raw = kLazyLog2 / scale_log2;
   bf16x8 p_prev[2] = {};
+  const auto read_vt = [&](const uint16_t* vlds, bf16x8 (&va)[DT][2]) {
+    if constexpr (SLOTS) read_v_slots<D>(vlds, wk, hf, n, va);
+    else read_v<D>(vlds, wk, hf, n, va);
+  };
 
   f32x16 s_cur;
   float mx_cur;
@@ -138,11 +190,11 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd(const uint16_t* __restri
     wait_vmcnt<2 * NI>();
     pipeline_barrier();
     bf16x8 ka[DC];
-    read_k<D>(sm.k[0], wk, hf, prow, ka);
+    read_k<D>(sm.k[0], wk, hf, prow_pi, ka);
     s_cur = f32x16{};
 #pragma unroll
     for (int dc = 0; dc < DC; ++dc) s_cur = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[dc], qf[dc], s_cur, 0, 0, 0);
-    if (PARTIAL) mask_keys(s_cur, g, blk(0), wk, hf);
+    if (PARTIAL) mask_of(0)(s_cur);
     mx_cur = max16(s_cur);
   }
   // Lazy rescaling: the reference max m_run moves only when a block exceeds
@@ -164,8 +216,8 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd(const uint16_t* __restri
     pipeline_barrier();
     bf16x8 ka[DC];
     bf16x8 va[DT][2];
-    read_k<D>(sm.k[(u + 1) % 3], wk, hf, prow, ka);
-    read_v<D>(sm.v[(u + 1) % 2], wk, hf, n, va);
+    read_k<D>(sm.k[(u + 1) % 3], wk, hf, prow_pi, ka);
+    read_vt(sm.v[(u + 1) % 2], va);
     float alpha = 1.f;
     const bool resc = move;
     if (resc) {
@@ -181,12 +233,10 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd(const uint16_t* __restri
     float mx_next;
     bf16x8 p_cur[2];
     // Past the last block the padding loads target a zero-size range: no memory traffic.
-    const __amdgpu_buffer_rsrc_t krs = (nb + 3 < topk)
-        ? k_tile_rsrc<D, PARTIAL, KRASTER>(kbase, g, blk(nb + 3), toff.k, roff, rrow, kto)
-        : make_rsrc(kbase, 0);
-    step<D, PARTIAL>(ka, va, qf, s_cur, s_next, mx_next, p_prev, p_cur, o, l_run, mc, scale_log2, g,
-                     blk(nb + 1), wk, hf, make_rsrc(vbase + 64LL * blk(nb) * D, 64 * D * 2),
-                     sm.v[u % 2] + w * NI * 8 * 64, toff.v, krs, sm.k[u % 3] + w * NI * KRPI * D, kto);
+    const __amdgpu_buffer_rsrc_t krs = (nb + 3 < ntiles) ? k_rsrc(nb + 3) : make_rsrc(kbase, 0);
+    step<D, PARTIAL>(ka, va, qf, s_cur, s_next, mx_next, p_prev, p_cur, o, l_run, mc, scale_log2,
+                     mask_of(nb + 1), v_rsrc(nb), sm.v[u % 2] + vl_off, voffs, krs,
+                     sm.k[u % 3] + w * NI * KRPI * D, kto);
     move = __builtin_amdgcn_ballot_w64(mx_next > m_run + lazy_raw) != 0;
     if (resc) {
       // O^T now holds P(0..n-1) V at the previous reference max.
@@ -199,7 +249,7 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd(const uint16_t* __restri
     p_prev[1] = p_cur[1];
   };
   int jb = 0;
-  for (; jb + 6 <= topk; jb += 6) {
+  for (; jb + 6 <= ntiles; jb += 6) {
     run_step(jb, StepC<0>{});
     run_step(jb + 1, StepC<1>{});
     run_step(jb + 2, StepC<2>{});
@@ -207,17 +257,17 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd(const uint16_t* __restri
     run_step(jb + 4, StepC<4>{});
     run_step(jb + 5, StepC<5>{});
   }
-  if (jb < topk) run_step(jb, StepC<0>{});
-  if (jb + 1 < topk) run_step(jb + 1, StepC<1>{});
-  if (jb + 2 < topk) run_step(jb + 2, StepC<2>{});
-  if (jb + 3 < topk) run_step(jb + 3, StepC<3>{});
-  if (jb + 4 < topk) run_step(jb + 4, StepC<4>{});
+  if (jb < ntiles) run_step(jb, StepC<0>{});
+  if (jb + 1 < ntiles) run_step(jb + 1, StepC<1>{});
+  if (jb + 2 < ntiles) run_step(jb + 2, StepC<2>{});
+  if (jb + 3 < ntiles) run_step(jb + 3, StepC<3>{});
+  if (jb + 4 < ntiles) run_step(jb + 4, StepC<4>{});
   {
-    // Last product: P(topk-1) V(topk-1).
+    // Last product: P(ntiles-1) V(ntiles-1).
     wait_vmcnt<NI>();
     pipeline_barrier();
     bf16x8 va[DT][2];
-    read_v<D>(sm.v[(topk - 1) & 1], wk, hf, n, va);
+    read_vt(sm.v[(ntiles - 1) & 1], va);
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
@@ -267,15 +317,76 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd(const uint16_t* __restri
   if (lse && hf == 0) lse[row] = m * scale + logf(l_tot);
 }
 
-}  // namespace
+// Packing plan of the fine stage's tiles for one list row per wavefront.  A
+// selected cube with n valid keys needs ceil(n / 16) slots (compact order puts
+// its valid keys first).  Cubes of three or four slots get a tile each (in
+// list order), then cubes of two slots go two to a tile, then cubes of one
+// slot four to a tile (each class in list order; the last tile of a class may
+// have empty slots).  Row layout (int32): word 0 the number of tiles, words
+// 1..3 unused, then four slot codes per tile (tile_pipeline.h).  Positions
+// come from ballot prefix counts: no atomics, the plan is deterministic.
+__global__ void __launch_bounds__(256) block_plan(const int32_t* __restrict__ idx, int topk,
+                                                  int32_t* __restrict__ plan, KGeom g, long long nrows) {
+  const int lane = threadIdx.x & 63;
+  const long long row = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= nrows) return;  // whole wavefront leaves together
+  const int32_t* irow = idx + row * topk;
+  int32_t* prow = plan + row * 4LL * (topk + 1);
+  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  const auto valid_count = [&](int j) {
+    int ct, cy, cx;
+    cube_coords(g, j, ct, cy, cx);
+    return cube_count(g, ct, cy, cx);
+  };
+  int nb = 0, n2 = 0, n1 = 0;
+  for (int base = 0; base < topk; base += 64) {
+    const int m = base + lane;
+    const int sl = m < topk ? (valid_count(irow[m]) + 15) >> 4 : 0;
+    nb += __popcll(__ballot(sl >= 3));
+    n2 += __popcll(__ballot(sl == 2));
+    n1 += __popcll(__ballot(sl == 1));
+  }
+  const int t2 = (n2 + 1) >> 1, t1 = (n1 + 3) >> 2;
+  const int base2 = nb, base1 = nb + t2;
+  int cb = 0, c2 = 0, c1 = 0;
+  for (int base = 0; base < topk; base += 64) {
+    const int m = base + lane;
+    const int j = m < topk ? irow[m] : 0;
+    const int nv = m < topk ? valid_count(j) : 0;
+    const int sl = (nv + 15) >> 4;
+    const uint64_t mb = __ballot(sl >= 3), m2 = __ballot(sl == 2), m1 = __ballot(sl == 1);
+    const auto code = [&](int sc) {
+      const int cnt = min(16, max(0, nv - 16 * sc));
+      return cnt ? (j << 8) | (sc << 5) | cnt : 0;
+    };
+    if (sl >= 3) {
+      const int t = cb + __popcll(mb & below);
+      *reinterpret_cast<int4*>(prow + 4 * (t + 1)) = make_int4(code(0), code(1), code(2), code(3));
+    } else if (sl == 2) {
+      const int r = c2 + __popcll(m2 & below);
+      *reinterpret_cast<int2*>(prow + 4 * (base2 + (r >> 1) + 1) + 2 * (r & 1)) = make_int2(code(0), code(1));
+    } else if (sl == 1) {
+      const int r = c1 + __popcll(m1 & below);
+      prow[4 * (base1 + (r >> 2) + 1) + (r & 3)] = code(0);
+    }
+    cb += __popcll(mb);
+    c2 += __popcll(m2);
+    c1 += __popcll(m1);
+  }
+  if (lane == 0) {
+    prow[0] = nb + t2 + t1;
+    if (n2 & 1) *reinterpret_cast<int2*>(prow + 4 * (base2 + t2) + 2) = make_int2(0, 0);
+    for (int r = n1; r < 4 * t1; ++r) prow[4 * (base1 + (r >> 2) + 1) + (r & 3)] = 0;
+  }
+}
 
-template <int D, bool PARTIAL, bool RASTER, bool KRASTER>
+template <int D, bool PARTIAL, bool RASTER, bool KRASTER, bool SLOTS = false>
 void launch_fwd(const KGeom& g, const uint16_t* qc, const uint16_t* kc, const uint16_t* vt, const int32_t* idx,
-                int topk, float scale, uint16_t* oc, float* oc_f32, float* lse, hipStream_t s) {
+                const int32_t* plan, int topk, float scale, uint16_t* oc, float* oc_f32, float* lse, hipStream_t s) {
   const Placement pl = make_placement(g);
   const float scale_log2 = scale * 1.4426950408889634f;
-  attn_fwd<D, PARTIAL, RASTER, KRASTER><<<dim3(grid_size(g)), dim3(kThreads), 0, s>>>(
-      qc, kc, vt, idx, topk, scale, scale_log2, oc, oc_f32, lse, g, pl);
+  attn_fwd<D, PARTIAL, RASTER, KRASTER, SLOTS><<<dim3(grid_size(g)), dim3(kThreads), 0, s>>>(
+      qc, kc, vt, idx, plan, topk, scale, scale_log2, oc, oc_f32, lse, g, pl);
 }
 
 template <bool RASTER, bool KRASTER>
@@ -283,14 +394,16 @@ hipError_t launch_fwd_any(const KGeom& g, const uint16_t* q, const uint16_t* k, 
                           const int32_t* idx, int topk, float scale, uint16_t* o, float* o_f32, float* lse,
                           hipStream_t s) {
   if (g.D == 64) {
-    if (g.partial) launch_fwd<64, true, RASTER, KRASTER>(g, q, k, vt, idx, topk, scale, o, o_f32, lse, s);
-    else launch_fwd<64, false, RASTER, KRASTER>(g, q, k, vt, idx, topk, scale, o, o_f32, lse, s);
+    if (g.partial) launch_fwd<64, true, RASTER, KRASTER>(g, q, k, vt, idx, nullptr, topk, scale, o, o_f32, lse, s);
+    else launch_fwd<64, false, RASTER, KRASTER>(g, q, k, vt, idx, nullptr, topk, scale, o, o_f32, lse, s);
   } else {
-    if (g.partial) launch_fwd<128, true, RASTER, KRASTER>(g, q, k, vt, idx, topk, scale, o, o_f32, lse, s);
-    else launch_fwd<128, false, RASTER, KRASTER>(g, q, k, vt, idx, topk, scale, o, o_f32, lse, s);
+    if (g.partial) launch_fwd<128, true, RASTER, KRASTER>(g, q, k, vt, idx, nullptr, topk, scale, o, o_f32, lse, s);
+    else launch_fwd<128, false, RASTER, KRASTER>(g, q, k, vt, idx, nullptr, topk, scale, o, o_f32, lse, s);
   }
   return hipGetLastError();
 }
+
+}  // namespace
 
 hipError_t launch_attn_fwd(const KGeom& g, const uint16_t* qc, const uint16_t* kc, const uint16_t* vt,
                            const int32_t* idx, int topk, float scale, uint16_t* oc, float* oc_f32, float* lse,
@@ -303,6 +416,32 @@ hipError_t launch_attn_fwd_raster(const KGeom& g, const uint16_t* q, const uint1
                                   float* lse, hipStream_t s) {
   if (k_raster) return launch_fwd_any<true, true>(g, q, k, vt, idx, topk, scale, o, nullptr, lse, s);
   return launch_fwd_any<true, false>(g, q, k, vt, idx, topk, scale, o, nullptr, lse, s);
+}
+
+size_t attn_packed_workspace_bytes(const KGeom& g, int topk) {
+  if (!g.partial) return 0;
+  return (size_t)g.B * g.H * g.nc * 16u * ((size_t)topk + 1);
+}
+
+hipError_t launch_attn_fwd_packed(const KGeom& g, const uint16_t* q, bool raster, const uint16_t* kc,
+                                  const uint16_t* vs, const int32_t* idx, int topk, float scale, uint16_t* o,
+                                  float* lse, void* ws, hipStream_t s) {
+  int32_t* plan = static_cast<int32_t*>(ws);
+  if (g.partial) {
+    const long long nrows = (long long)g.B * g.H * g.nc;
+    block_plan<<<dim3((unsigned)((nrows + 3) / 4)), dim3(256), 0, s>>>(idx, topk, plan, g, nrows);
+  }
+#define VSA_PACKED(DD, PP, RR) \
+  launch_fwd<DD, PP, RR, false, true>(g, q, kc, vs, idx, plan, topk, scale, o, nullptr, lse, s)
+  if (g.D == 64) {
+    if (g.partial) { if (raster) VSA_PACKED(64, true, true); else VSA_PACKED(64, true, false); }
+    else { if (raster) VSA_PACKED(64, false, true); else VSA_PACKED(64, false, false); }
+  } else {
+    if (g.partial) { if (raster) VSA_PACKED(128, true, true); else VSA_PACKED(128, true, false); }
+    else { if (raster) VSA_PACKED(128, false, true); else VSA_PACKED(128, false, false); }
+  }
+#undef VSA_PACKED
+  return hipGetLastError();
 }
 
 }  // namespace vsa

@@ -178,8 +178,10 @@ __global__ void __launch_bounds__(kLinThreads, 2) attn_lin_fwd(
           f32x16 s_next;
           float mx_next;
           bf16x8 p_cur[2];
-          step<D, PARTIAL>(ka, va, qf, s_cur, s_next, mx_next, p_prev, p_cur, o, l_run, mc, scale_log2, g,
-                           blk(nb + 1), wk, hf, make_rsrc(vbase + 64LL * blk(nb) * D, 64 * D * 2),
+          const int j_next = blk(nb + 1);
+          step<D, PARTIAL>(ka, va, qf, s_cur, s_next, mx_next, p_prev, p_cur, o, l_run, mc, scale_log2,
+                           [&](f32x16& s) { mask_keys(s, g, j_next, wk, hf); },
+                           make_rsrc(vbase + 64LL * blk(nb) * D, 64 * D * 2),
                            sm.v[u % 2] + w4 * NI * 8 * 64, toff.v,
                            make_rsrc(kbase + 64LL * blk(nb + 3) * D, 64 * D * 2), sm.k[u % 3] + w4 * NI * KRPI * D,
                            toff.k);

@@ -51,6 +51,19 @@ __device__ __forceinline__ int cube_count(const KGeom& g, int ct, int cy, int cx
   return nt * ny * nx;
 }
 
+// Row of local token l inside its cube in compact order: the cube's valid
+// tokens first, in raster order within the cube (rank among them), then its
+// padded slots in the same order.  A bijection of 0..63; the identity for a
+// full cube.
+__device__ __forceinline__ int compact_row(const KGeom& g, int ct, int cy, int cx, int l) {
+  const int nt = min(4, g.T - 4 * ct), ny = min(4, g.Hg - 4 * cy), nx = min(4, g.W - 4 * cx);
+  const int lt = l >> 4, ly = (l >> 2) & 3, lx = l & 3;
+  const bool in_t = lt < nt, in_y = ly < ny;
+  const int before = min(lt, nt) * ny * nx + (in_t ? min(ly, ny) * nx + (in_y ? min(lx, nx) : 0) : 0);
+  const bool valid = in_t && in_y && lx < nx;
+  return valid ? before : nt * ny * nx + (l - before);
+}
+
 // Buffer resource over `bytes` bytes at `base` (raw, unswizzled, dword data
 // format): loads outside the range return zero instead of faulting.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, unsigned bytes) {
@@ -81,7 +94,8 @@ __device__ __forceinline__ float phi_elu1(float x) { return x > 0.f ? x + 1.f : 
 // Host launchers (each returns hipSuccess or the launch error).
 namespace vsa {
 hipError_t launch_permute(const KGeom& g, const uint16_t* x, uint16_t* xc, int layout, hipStream_t s);
-hipError_t launch_permute_pool(const KGeom& g, const uint16_t* x, uint16_t* xc, float* mean, hipStream_t s);
+hipError_t launch_permute_pool(const KGeom& g, const uint16_t* x, uint16_t* xc, float* mean, bool compact,
+                               hipStream_t s);
 hipError_t launch_unpermute(const KGeom& g, const uint16_t* xc, uint16_t* x, hipStream_t s);
 hipError_t launch_select(const KGeom& g, const uint16_t* qc, const uint16_t* kc, int topk, int32_t* idx,
                          void* ws, hipStream_t s);
@@ -95,6 +109,13 @@ hipError_t launch_attn_fwd(const KGeom& g, const uint16_t* qc, const uint16_t* k
 hipError_t launch_attn_fwd_raster(const KGeom& g, const uint16_t* q, const uint16_t* k, bool k_raster,
                                   const uint16_t* vt, const int32_t* idx, int topk, float scale, uint16_t* o,
                                   float* lse, hipStream_t s);
+// Packed fine stage: K in compact cube-major rows, V in the slot layout;
+// q/o raster (raster = true) or cube-major.  ws: the packing plan of a grid
+// with partial cubes (attn_packed_workspace_bytes; 0 for full grids).
+size_t attn_packed_workspace_bytes(const KGeom& g, int topk);
+hipError_t launch_attn_fwd_packed(const KGeom& g, const uint16_t* q, bool raster, const uint16_t* kc,
+                                  const uint16_t* vs, const int32_t* idx, int topk, float scale, uint16_t* o,
+                                  float* lse, void* ws, hipStream_t s);
 hipError_t launch_linear(const KGeom& g, const uint16_t* qc, const uint16_t* kc, const uint16_t* vt,
                          const int32_t* idx, int topk, const float* o_sparse, uint16_t* oc, void* ws,
                          hipStream_t s);

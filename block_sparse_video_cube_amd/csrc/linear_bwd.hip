@@ -246,8 +246,8 @@ __global__ void __launch_bounds__(kThreads, 2) lin_bwd_dq(const uint16_t* __rest
                                                           const int32_t* __restrict__ idx, int topk,
                                                           const uint16_t* __restrict__ fk,
                                                           const float* __restrict__ z_tot, LinBwdWs t,
-                                                          const uint16_t* __restrict__ dq_add,
-                                                          uint16_t* __restrict__ dq, KGeom g, Placement pl) {
+                                                          const uint16_t* dq_add, uint16_t* dq, KGeom g,
+                                                          Placement pl) {
   constexpr int DC = D / 16, DT = D / 32;
   __shared__ __attribute__((aligned(16))) uint16_t v0[64 * D];
   __shared__ __attribute__((aligned(16))) uint16_t v1[64 * D];
@@ -352,6 +352,8 @@ __global__ void __launch_bounds__(kThreads, 2) lin_bwd_dq(const uint16_t* __rest
   const float cq = t.c[row];
   const float* zt = z_tot + bh * D;
   const uint16_t* qrow = qc + row * D;
+  // The addend may alias the output (not restrict): each lane reads its
+  // addend elements before it writes the same elements.
   const uint16_t* arow = dq_add ? dq_add + row * D : nullptr;
   uint16_t* out = dq + row * D;
 #pragma unroll
@@ -394,8 +396,8 @@ template <int D, bool DV>
 __global__ void __launch_bounds__(kThreads, 2) lin_bwd_dkv(const uint16_t* __restrict__ kc,
                                                            const uint16_t* __restrict__ vc,
                                                            const uint16_t* __restrict__ fk, LinBwdWs t, int topk,
-                                                           const uint16_t* __restrict__ add,
-                                                           uint16_t* __restrict__ out, KGeom g, Placement pl) {
+                                                           const uint16_t* add, uint16_t* out, KGeom g,
+                                                           Placement pl) {
   constexpr int DC = D / 16, DT = D / 32;
   __shared__ __attribute__((aligned(16))) uint16_t w0[64 * D];
   __shared__ __attribute__((aligned(16))) uint16_t w1[64 * D];
@@ -517,6 +519,8 @@ __global__ void __launch_bounds__(kThreads, 2) lin_bwd_dkv(const uint16_t* __res
   cube_coords(g, j, ct, cy, cx);
   const bool valid = local_valid(g, ct, cy, cx, key);
   const uint16_t* krw = kc + krow * D;
+  // The addend may alias the output (not restrict): each lane reads its
+  // addend elements before it writes the same elements.
   const uint16_t* arow = add ? add + krow * D : nullptr;
   uint16_t* orow = out + krow * D;
 #pragma unroll

@@ -17,8 +17,9 @@ namespace {
 
 constexpr int kThreads = 256;
 
-// [B, S, H, D] -> [B, H, Np, D]; padded rows become zero.
-template <int D>
+// [B, S, H, D] -> [B, H, Np, D]; padded rows become zero.  COMPACT: local
+// token l goes to row compact_row(l) of its cube (valid tokens first).
+template <int D, bool COMPACT>
 __global__ void __launch_bounds__(kThreads) permute_token_major(const uint16_t* __restrict__ x,
                                                                 uint16_t* __restrict__ xc, KGeom g) {
   constexpr int CH = D / 8;  // 16-byte chunks per row
@@ -34,7 +35,7 @@ __global__ void __launch_bounds__(kThreads) permute_token_major(const uint16_t* 
       const long long s = ((long long)t * g.Hg + y) * g.W + xx;
       val = reinterpret_cast<const uint4*>(x + (((long long)b * g.S + s) * g.H + h) * D)[ch];
     }
-    out[f] = val;
+    out[COMPACT ? compact_row(g, ct, cy, cx, l) * CH + ch : f] = val;
   }
 }
 
@@ -45,8 +46,10 @@ __global__ void __launch_bounds__(kThreads) permute_token_major(const uint16_t* 
 // inside a wavefront and through LDS across the four wavefronts.
 //
 // With WRITE = false only the means are produced (the fine stage can gather
-// raster-order rows itself, so the cube-major copy is not needed).
-template <int D, bool WRITE>
+// raster-order rows itself, so the cube-major copy is not needed).  COMPACT:
+// the copy is in compact order (rows as permute_token_major<D, true>); the
+// sums are the same, in the same order.
+template <int D, bool WRITE, bool COMPACT>
 __global__ void __launch_bounds__(kThreads) permute_pool(const uint16_t* __restrict__ x, uint16_t* __restrict__ xc,
                                                          float* __restrict__ mean, KGeom g) {
   constexpr int CH = D / 8;
@@ -71,7 +74,7 @@ __global__ void __launch_bounds__(kThreads) permute_pool(const uint16_t* __restr
         acc[2 * e + 1] += __uint_as_float(w4[e] & 0xFFFF0000u);
       }
     }
-    if (WRITE) out[f] = val;
+    if (WRITE) out[COMPACT ? compact_row(g, ct, cy, cx, l) * CH + ch : f] = val;
   }
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
 #pragma unroll
@@ -126,6 +129,45 @@ __global__ void __launch_bounds__(kThreads) permute_dim_major(const uint16_t* __
   }
 }
 
+// [B, S, H, D] -> [B, H, Nc, 4, D, 16]: each cube in compact order, cut
+// into four 16-row slots, each slot stored transposed (channel-major), so a
+// slot is one contiguous D x 16 block.
+template <int D>
+__global__ void __launch_bounds__(kThreads) permute_slots(const uint16_t* __restrict__ x,
+                                                          uint16_t* __restrict__ xs, KGeom g) {
+  constexpr int CH = D / 8;
+  constexpr int LD = D + 8;  // padded LDS row (halfwords), keeps 16-byte alignment
+  __shared__ __attribute__((aligned(16))) uint16_t tile[64 * LD];
+  const int c = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  int ct, cy, cx;
+  cube_coords(g, c, ct, cy, cx);
+  for (int f = threadIdx.x; f < 64 * CH; f += kThreads) {
+    const int l = f / CH, ch = f % CH;
+    const int t = 4 * ct + (l >> 4), y = 4 * cy + ((l >> 2) & 3), xx = 4 * cx + (l & 3);
+    uint4 val = make_uint4(0, 0, 0, 0);
+    if (t < g.T && y < g.Hg && xx < g.W) {
+      const long long s = ((long long)t * g.Hg + y) * g.W + xx;
+      val = reinterpret_cast<const uint4*>(x + (((long long)b * g.S + s) * g.H + h) * D)[ch];
+    }
+    *reinterpret_cast<uint4*>(tile + compact_row(g, ct, cy, cx, l) * LD + ch * 8) = val;
+  }
+  __syncthreads();
+  // 16-byte chunk f of the output cube: slot f / (2 D), channel (f / 2) % D,
+  // compact rows 16 slot + 8 (f % 2) .. + 7.
+  uint4* out = reinterpret_cast<uint4*>(xs + (((long long)b * g.H + h) * g.Np + 64LL * c) * D);
+  for (int f = threadIdx.x; f < D * 8; f += kThreads) {
+    const int sl = f / (2 * D), d = (f >> 1) % D, r0 = 16 * sl + 8 * (f & 1);
+    uint32_t w[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const uint32_t lo = tile[(r0 + 2 * e) * LD + d];
+      const uint32_t hi = tile[(r0 + 2 * e + 1) * LD + d];
+      w[e] = lo | (hi << 16);
+    }
+    out[f] = make_uint4(w[0], w[1], w[2], w[3]);
+  }
+}
+
 // [B, H, Np, D] -> [B, S, H, D]; padded rows are dropped.
 template <int D>
 __global__ void __launch_bounds__(kThreads) unpermute_token_major(const uint16_t* __restrict__ xc,
@@ -147,31 +189,36 @@ __global__ void __launch_bounds__(kThreads) unpermute_token_major(const uint16_t
 
 }  // namespace
 
-hipError_t launch_permute(const KGeom& g, const uint16_t* x, uint16_t* xc, int layout, hipStream_t s) {
+template <int D>
+void launch_permute_d(const KGeom& g, const uint16_t* x, uint16_t* xc, int layout, hipStream_t s) {
   const dim3 grid(g.nc, g.H, g.B);
-  if (layout == VSA_LAYOUT_TOKEN_MAJOR) {
-    if (g.D == 64)
-      hipLaunchKernelGGL(permute_token_major<64>, grid, dim3(kThreads), 0, s, x, xc, g);
-    else
-      hipLaunchKernelGGL(permute_token_major<128>, grid, dim3(kThreads), 0, s, x, xc, g);
-  } else {
-    if (g.D == 64)
-      hipLaunchKernelGGL(permute_dim_major<64>, grid, dim3(kThreads), 0, s, x, xc, g);
-    else
-      hipLaunchKernelGGL(permute_dim_major<128>, grid, dim3(kThreads), 0, s, x, xc, g);
+  switch (layout) {
+    case VSA_LAYOUT_TOKEN_MAJOR: permute_token_major<D, false><<<grid, dim3(kThreads), 0, s>>>(x, xc, g); break;
+    case VSA_LAYOUT_TOKEN_COMPACT: permute_token_major<D, true><<<grid, dim3(kThreads), 0, s>>>(x, xc, g); break;
+    case VSA_LAYOUT_DIM_SLOTS: permute_slots<D><<<grid, dim3(kThreads), 0, s>>>(x, xc, g); break;
+    default: permute_dim_major<D><<<grid, dim3(kThreads), 0, s>>>(x, xc, g); break;
   }
+}
+
+hipError_t launch_permute(const KGeom& g, const uint16_t* x, uint16_t* xc, int layout, hipStream_t s) {
+  if (g.D == 64) launch_permute_d<64>(g, x, xc, layout, s);
+  else launch_permute_d<128>(g, x, xc, layout, s);
   return hipGetLastError();
 }
 
-hipError_t launch_permute_pool(const KGeom& g, const uint16_t* x, uint16_t* xc, float* mean, hipStream_t s) {
+template <int D>
+void launch_permute_pool_d(const KGeom& g, const uint16_t* x, uint16_t* xc, float* mean, bool compact,
+                           hipStream_t s) {
   const dim3 grid(g.nc, g.H, g.B);
-  if (xc) {
-    if (g.D == 64) permute_pool<64, true><<<grid, dim3(kThreads), 0, s>>>(x, xc, mean, g);
-    else permute_pool<128, true><<<grid, dim3(kThreads), 0, s>>>(x, xc, mean, g);
-  } else {
-    if (g.D == 64) permute_pool<64, false><<<grid, dim3(kThreads), 0, s>>>(x, xc, mean, g);
-    else permute_pool<128, false><<<grid, dim3(kThreads), 0, s>>>(x, xc, mean, g);
-  }
+  if (!xc) permute_pool<D, false, false><<<grid, dim3(kThreads), 0, s>>>(x, xc, mean, g);
+  else if (compact) permute_pool<D, true, true><<<grid, dim3(kThreads), 0, s>>>(x, xc, mean, g);
+  else permute_pool<D, true, false><<<grid, dim3(kThreads), 0, s>>>(x, xc, mean, g);
+}
+
+hipError_t launch_permute_pool(const KGeom& g, const uint16_t* x, uint16_t* xc, float* mean, bool compact,
+                               hipStream_t s) {
+  if (g.D == 64) launch_permute_pool_d<64>(g, x, xc, mean, compact, s);
+  else launch_permute_pool_d<128>(g, x, xc, mean, compact, s);
   return hipGetLastError();
 }
 

@@ -22,15 +22,20 @@ namespace vsa {
 namespace {
 
 // Mean of each cube over its valid rows: xc [B, H, Np, D] bf16 -> [B, H, Nc, D] fp32.
-// One wavefront per (b, h, cube), four cubes per workgroup.  Lane L reads the
-// 16-byte chunk L % (D/8) of rows L / (D/8), + 64/(D/8), ... (fully coalesced
-// 1 KB per instruction), keeps 8 fp32 partial sums, and the row groups are
-// folded with cross-lane exchanges.
+// One wavefront per (b, h, cube), four cubes per workgroup.  The fp32 sums
+// are taken in exactly the order of the pooling kernel that permute_pool
+// runs on the raster rows (so both entry points of the coarse stage see the
+// same means, bit for bit): that kernel's thread 64 w + L (w = 0..3) adds
+// chunk L % (D/8) of rows (64 w + L) / (D/8) + 256 it / (D/8), it = 0, 1, ...
+// in turn, folds its wavefront with cross-lane exchanges, and the four
+// wavefront sums are added in order w = 0..3 and divided by the count.  Here
+// lane L keeps those four partial sums itself.  Every load is a fully
+// coalesced 1 KB (chunk 64 w + 256 it + L of the tile).
 template <int D>
 __global__ void __launch_bounds__(256) cube_mean(const uint16_t* __restrict__ xc, float* __restrict__ mean,
                                                  KGeom g, long long ncubes_total) {
   constexpr int CH = D / 8;         // lanes per row
-  constexpr int RPI = 64 / CH;      // rows per load
+  constexpr int IT = 64 * CH / 256; // rows per thread of the pooling kernel
   const long long cube_id = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (cube_id >= ncubes_total) return;  // whole wavefront leaves together
   const int lane = threadIdx.x & 63;
@@ -38,29 +43,41 @@ __global__ void __launch_bounds__(256) cube_mean(const uint16_t* __restrict__ xc
   int ct, cy, cx;
   cube_coords(g, c, ct, cy, cx);
   const uint4* base = reinterpret_cast<const uint4*>(xc + cube_id * 64 * D);
-  float acc[8] = {};
+  float acc[4][8] = {};
 #pragma unroll
-  for (int it = 0; it < 64 / RPI; ++it) {
-    const int row = it * RPI + lane / CH;
-    const uint4 v = base[it * 64 + lane];
-    if (local_valid(g, ct, cy, cx, row)) {
-      const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+  for (int w = 0; w < 4; ++w)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        acc[2 * e] += __uint_as_float(w4[e] << 16);
-        acc[2 * e + 1] += __uint_as_float(w4[e] & 0xFFFF0000u);
+    for (int it = 0; it < IT; ++it) {
+      const int f = 64 * w + 256 * it + lane;
+      const uint4 v = base[f];
+      if (local_valid(g, ct, cy, cx, f / CH)) {
+        const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          acc[w][2 * e] += __uint_as_float(w4[e] << 16);
+          acc[w][2 * e + 1] += __uint_as_float(w4[e] & 0xFFFF0000u);
+        }
       }
     }
-  }
 #pragma unroll
-  for (int off = CH; off < 64; off *= 2)
+  for (int w = 0; w < 4; ++w)
 #pragma unroll
-    for (int e = 0; e < 8; ++e) acc[e] += __shfl_xor(acc[e], off);
+    for (int off = CH; off < 64; off *= 2)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[w][e] += __shfl_xor(acc[w][e], off);
   if (lane < CH) {
-    const float inv_n = 1.f / (float)cube_count(g, ct, cy, cx);
+    const float n = (float)cube_count(g, ct, cy, cx);
+    float r[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      float sum = 0.f;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) sum += acc[w][e];
+      r[e] = sum / n;
+    }
     float4* dst = reinterpret_cast<float4*>(mean + cube_id * D + lane * 8);
-    dst[0] = make_float4(acc[0] * inv_n, acc[1] * inv_n, acc[2] * inv_n, acc[3] * inv_n);
-    dst[1] = make_float4(acc[4] * inv_n, acc[5] * inv_n, acc[6] * inv_n, acc[7] * inv_n);
+    dst[0] = make_float4(r[0], r[1], r[2], r[3]);
+    dst[1] = make_float4(r[4], r[5], r[6], r[7]);
   }
 }
 

@@ -241,6 +241,57 @@ __device__ __forceinline__ void read_v(const uint16_t* vlds, int wk, int hf, int
   }
 }
 
+// Packed tiles.  A tile's 64 key rows are four slots of 16 rows; slot s
+// holds rows 16 sc .. 16 sc + 15 of key cube j in compact order (the cube's
+// valid keys first), of which the first `count` are valid keys.  A slot code
+// is j << 8 | sc << 5 | count, and 0 for an empty slot.  Wavefront w loads
+// slot w of K (rows 16 w .. 16 w + 15 of the tile, in the TileOffsets layout)
+// and of V, whose slots are stored channel-major in HBM ([4][D][16] per cube)
+// and in LDS, so each is one contiguous D x 16 block.
+__device__ __forceinline__ int slot_cube(int code) { return code >> 8; }
+__device__ __forceinline__ int slot_sub(int code) { return (code >> 5) & 3; }
+__device__ __forceinline__ int slot_count(int code) { return code & 31; }
+
+// Buffer resource for wavefront w's share of the K tile (slot w): based so
+// that the TileOffsets lane offsets of rows 16 w .. 16 w + 15 land on the
+// slot's rows; only the slot's `count` valid rows are in range (the rest
+// read as zero without a memory access).
+template <int D>
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t k_slot_rsrc(const uint16_t* khead, int code, int w) {
+  const int cnt = slot_count(code);
+  const long long row0 = 64LL * slot_cube(code) + 16 * slot_sub(code) - 16 * w;
+  return make_rsrc(khead + row0 * D, cnt ? (unsigned)((16 * w + cnt) * D * 2) : 0u);
+}
+
+// Buffer resource of one V slot (D x 16, 16 * D * 2 contiguous bytes).
+template <int D>
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t v_slot_rsrc(const uint16_t* vhead, int code) {
+  const long long off = (64LL * slot_cube(code) + 16 * slot_sub(code)) * D;
+  return make_rsrc(vhead + off, slot_count(code) ? (unsigned)(16 * D * 2) : 0u);
+}
+
+// V^T fragments from a slot-layout V tile in LDS: the same operands as
+// read_v (chunk 4 wk + 2 kk + hf of channel row 32 dt + n is keys 8 hf ..
+// 8 hf + 7 of slot 2 wk + kk); a wavefront reads 1 KB contiguous.
+template <int D>
+__device__ __forceinline__ void read_v_slots(const uint16_t* vlds, int wk, int hf, int n,
+                                             bf16x8 (&va)[D / 32][2]) {
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk)
+      va[dt][kk] = *reinterpret_cast<const bf16x8*>(vlds + (2 * wk + kk) * (D * 16) + (32 * dt + n) * 16 + 8 * hf);
+}
+
+// Keys of a packed tile past their slot's count take no weight.  In the S^T
+// accumulator, register r of lane half hf holds position 8 hf + r % 8 of slot
+// 2 wk + r / 8; c0, c1 are the counts of this wavefront's two slots.
+__device__ __forceinline__ void mask_slots(f32x16& s, int c0, int c1, int hf) {
+  const int l0 = c0 - 8 * hf, l1 = c1 - 8 * hf;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) s[r] = ((r & 7) < (r < 8 ? l0 : l1)) ? s[r] : -INFINITY;
+}
+
 // Padded keys of key cube j take no weight: their logits become -inf.
 // In an S^T = K Q^T tile (keys in rows, read in pi order) accumulator
 // register r of lane half hf holds local key 32 wk + 16 (r/8) + 8 hf + r%8,

@@ -49,7 +49,7 @@
 extern "C" {
 #endif
 
-#define VSA_ABI_VERSION 1
+#define VSA_ABI_VERSION 2
 
 typedef enum vsa_status {
   VSA_OK = 0,
@@ -91,8 +91,23 @@ typedef struct vsa_dims {
  *              stored transposed.  This is the layout the value tensor must
  *              have for vsa_sparse_attn_fwd and vsa_linear_branch.
  * RASTER: not a cube-major layout; the k_layout code of
- *              vsa_sparse_attn_fwd_raster for raster-order keys. */
-enum { VSA_LAYOUT_TOKEN_MAJOR = 0, VSA_LAYOUT_DIM_MAJOR = 1, VSA_LAYOUT_RASTER = 2 };
+ *              vsa_sparse_attn_fwd_raster for raster-order keys.
+ * TOKEN_COMPACT: [B, heads, Np, D] in compact order: row 64 c + r holds the
+ *              r-th valid token of cube c (raster order within the cube) for
+ *              r < n_c (its valid count), and zero for r >= n_c.  Identical to
+ *              TOKEN_MAJOR for a cube without padding.  The keys of
+ *              vsa_sparse_attn_fwd_packed.
+ * DIM_SLOTS:   [B, heads, Nc, 4, D, 16], element (b, h, c, s, d, e) = element
+ *              d of compact row 16 s + e of cube c: each cube cut into four
+ *              16-row slots, each slot stored transposed.  The values of
+ *              vsa_sparse_attn_fwd_packed. */
+enum {
+  VSA_LAYOUT_TOKEN_MAJOR = 0,
+  VSA_LAYOUT_DIM_MAJOR = 1,
+  VSA_LAYOUT_RASTER = 2,
+  VSA_LAYOUT_TOKEN_COMPACT = 3,
+  VSA_LAYOUT_DIM_SLOTS = 4
+};
 
 /* Limits: n_cubes <= VSA_MAX_CUBES, B * heads * Np * D < 2^40. */
 #define VSA_MAX_CUBES 4096
@@ -116,27 +131,42 @@ size_t vsa_linear_workspace_bytes(const vsa_geom* g);
 
 /* -------------------------------------------------------------- entry points */
 
-/* Cube permutation (gather).  x: [B, S, heads, D] bf16 raster tokens.
- * xc: output, layout per `layout` (TOKEN_MAJOR or DIM_MAJOR) with Np rows per
- * (b, h); padded rows are written as zero.  x and xc must not overlap. */
+/* Cube permutation (gather): the grouping of the latent tokens into 4 x 4 x 4
+ * cubes that makes every attention block a whole cube (FastVideo
+ * sparse-distillation article, section "2. 视频稀疏注意力VSA" and its figure
+ * of attention patterns without mixed blocks).  x: [B, S, heads, D] bf16
+ * raster tokens.  xc: output, layout per `layout` (TOKEN_MAJOR, DIM_MAJOR,
+ * TOKEN_COMPACT or DIM_SLOTS; else VSA_ERR_LAYOUT) with Np rows per (b, h);
+ * padded rows are written as zero.  x and xc must not overlap. */
 int32_t vsa_cube_permute(const vsa_geom* g, const uint16_t* x, uint16_t* xc,
                          int32_t layout, void* stream);
 
-/* Cube permutation fused with the coarse-stage pooling (one pass over x):
+/* Cube permutation fused with the coarse-stage pooling (one pass over x; the
+ * coarse stage summarises each cube to choose the blocks dynamically,
+ * FastVideo sparse-distillation article, section "2. 视频稀疏注意力VSA"):
  * xc as vsa_cube_permute with TOKEN_MAJOR layout, and mean: output fp32
- * [B, heads, Nc, D], the mean of each cube over its valid tokens (the same
- * values vsa_select_topk computes from xc). */
+ * [B, heads, Nc, D], the mean of each cube over its valid tokens.  The fp32
+ * sums are taken in one fixed order that vsa_cube_pool, vsa_quant_fp8 and the
+ * pooling inside vsa_select_topk share, so all four give bit-identical means.
+ * vsa_cube_permute_pool_compact: the same with xc in TOKEN_COMPACT layout. */
 int32_t vsa_cube_permute_pool(const vsa_geom* g, const uint16_t* x, uint16_t* xc,
                               float* mean, void* stream);
+int32_t vsa_cube_permute_pool_compact(const vsa_geom* g, const uint16_t* x, uint16_t* xc,
+                                      float* mean, void* stream);
 
-/* Inverse permutation (scatter).  xc: [B, heads, Np, D] TOKEN_MAJOR bf16;
- * x: output [B, S, heads, D]; padded rows of xc are dropped. */
+/* Inverse permutation (scatter), back to the raster token order the model
+ * uses (same passage as vsa_cube_permute).  xc: [B, heads, Np, D]
+ * TOKEN_MAJOR bf16; x: output [B, S, heads, D]; padded rows of xc are
+ * dropped. */
 int32_t vsa_cube_unpermute(const vsa_geom* g, const uint16_t* xc, uint16_t* x,
                            void* stream);
 
-/* Coarse stage: cube means of qc and kc (fp32, over valid rows), block scores
- * s_ij = qbar_i . kbar_j (fp32) and, per query cube, the topk best key cubes
- * (equal scores: lower index first; -0 and +0 equal), written ascending.
+/* Coarse stage (the dynamic choice of the important blocks, keeping 1 -
+ * sparsity of them: FastVideo sparse-distillation article, section
+ * "2. 视频稀疏注意力VSA"): cube means of qc and kc (fp32, over valid rows),
+ * block scores s_ij = qbar_i . kbar_j (fp32) and, per query cube, the topk
+ * best key cubes (equal scores: lower index first; -0 and +0 equal), written
+ * ascending.
  * qc, kc: [B, heads, Np, D] TOKEN_MAJOR bf16.
  * idx: output int32 [B, heads, Nc, topk].
  * ws: device workspace of at least vsa_select_workspace_bytes(g) bytes. */
@@ -191,9 +221,12 @@ int32_t vsa_sta_topk(const vsa_geom* g, int32_t win_t, int32_t win_h, int32_t wi
 int32_t vsa_sta_index(const vsa_geom* g, int32_t win_t, int32_t win_h, int32_t win_w,
                       int32_t* idx, void* stream);
 
-/* Fine stage: for every (b, h, query cube i), softmax attention of its 64
- * query rows over the valid keys of the topk key cubes idx[b, h, i, :]
- * (flash-style online softmax, fp32 accumulation, bf16 matrix cores).
+/* Fine stage (attention over the selected blocks only, in a flash-attention
+ * compatible kernel: FastVideo sparse-distillation article, section
+ * "2. 视频稀疏注意力VSA"): for every (b, h, query cube i), softmax attention
+ * of its 64 query rows over the valid keys of the topk key cubes
+ * idx[b, h, i, :] (flash-style online softmax, fp32 accumulation, bf16
+ * matrix cores).
  * qc, kc: TOKEN_MAJOR bf16; vt: DIM_MAJOR bf16; idx: int32 [B, heads, Nc, topk]
  * with entries in [0, Nc) (duplicates are computed twice).
  * softmax_scale: finite, > 0 (usually 1/sqrt(D)).
@@ -208,6 +241,31 @@ int32_t vsa_sparse_attn_fwd(const vsa_geom* g, const uint16_t* qc, const uint16_
                             const uint16_t* vt, const int32_t* idx, int32_t topk,
                             float softmax_scale, uint16_t* oc, float* oc_f32,
                             float* lse, void* stream);
+
+/* Packed fine stage: the result of vsa_sparse_attn_fwd (same passage) with
+ * the keys of the selected cubes packed into 64-key tiles.  A selected cube
+ * with n valid keys fills ceil(n / 16) slots of 16 keys; cubes of at most two
+ * slots share tiles (two or four to a tile), so a cube at the edge of the
+ * grid with 16 valid keys costs a quarter of a block's loads and matrix
+ * work.  The per-row packing is computed on the device (one launch) into ws.
+ * q: raster [B, S, heads, D] bf16 when q_layout is VSA_LAYOUT_RASTER, and o
+ *    is then raster [B, S, heads, D] (padded query rows not written); or
+ *    TOKEN_MAJOR qc [B, heads, Np, D] and o cube-major TOKEN_MAJOR.  Other
+ *    codes: VSA_ERR_LAYOUT.
+ * kc: TOKEN_COMPACT keys; vs: DIM_SLOTS values (vsa_cube_permute[_pool_compact]).
+ * idx, topk, softmax_scale: as for vsa_sparse_attn_fwd; lse: optional fp32
+ *    [B, heads, Np] in cube-major row order.
+ * ws: at least vsa_sparse_attn_packed_workspace_bytes(g, topk) bytes
+ *    (overwritten); that size is 0 when no cube of the grid holds padding, and
+ *    ws may then be NULL.
+ * Results agree with vsa_sparse_attn_fwd within fp32 summation order (the
+ * blocks are summed in tile order); the raster and cube-major forms are
+ * bit-identical to each other.  Limit: n_cubes < 2^23. */
+size_t vsa_sparse_attn_packed_workspace_bytes(const vsa_geom* g, int32_t topk);
+int32_t vsa_sparse_attn_fwd_packed(const vsa_geom* g, const uint16_t* q, int32_t q_layout,
+                                   const uint16_t* kc, const uint16_t* vs, const int32_t* idx,
+                                   int32_t topk, float softmax_scale, uint16_t* o, float* lse,
+                                   void* ws, size_t ws_bytes, void* stream);
 
 /* Low-precision fine stage (8-bit attention after SageAttention, which the
  * TurboDiffusion article's SLA builds on, section "稀疏、蒸馏与全链路量化").
@@ -274,8 +332,11 @@ int32_t vsa_sparse_attn_bwd(const vsa_geom* g, const uint16_t* qc, const uint16_
                             float softmax_scale, uint16_t* dq, uint16_t* dk, uint16_t* dv,
                             void* ws, size_t ws_bytes, void* stream);
 
-/* Linear branch and combine: oc = bf16(o_sparse + O_lin), O_lin over the valid
- * keys of the cubes NOT in idx[b, h, i, :] (0 when none are left).
+/* Linear branch and combine (a linear-attention branch beside the sparse one
+ * keeps the global context of the skipped blocks at linear cost:
+ * SparkDiffusion article, paragraph 3, RoLA; TurboDiffusion article, section
+ * "稀疏、蒸馏与全链路量化", SLA): oc = bf16(o_sparse + O_lin), O_lin over the
+ * valid keys of the cubes NOT in idx[b, h, i, :] (0 when none are left).
  * qc, kc: TOKEN_MAJOR bf16; vt: DIM_MAJOR bf16; idx as for the fine stage
  * (entries distinct); o_sparse: fp32 [B, heads, Np, D] (the oc_f32 output of
  * vsa_sparse_attn_fwd); oc: output bf16 TOKEN_MAJOR.  o_sparse and oc may not

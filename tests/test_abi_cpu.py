@@ -41,7 +41,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_abi_version_and_status_text(lib):
-    assert lib.vsa_abi_version() == 1
+    assert lib.vsa_abi_version() == 2
     for code in range(11):
         assert lib.vsa_status_string(code)
     assert lib.vsa_status_string(12345) == b"unknown status"
@@ -282,3 +282,36 @@ def test_linear_backward_entry_point_validation(lib):
     assert lib.vsa_linear_branch_bwd(g, *ins, 9, P, *adds, *outs, P, ws, None) == _lib.VSA_ERR_TOPK
     assert lib.vsa_linear_branch_bwd(g, *ins, 2, P, *adds, *outs, P, ws - 1, None) == _lib.VSA_ERR_WORKSPACE
     assert lib.vsa_linear_branch_bwd(geom(D=48), *ins, 2, P, *adds, *outs, P, ws, None) == _lib.VSA_ERR_HEAD_DIM
+
+
+def test_packed_entry_point_validation(lib):
+    from block_sparse_video_cube_amd import _lib
+
+    P = FAKE
+    R, T = _lib.VSA_LAYOUT_RASTER, _lib.VSA_LAYOUT_TOKEN_MAJOR
+    full = geom(grid=(8, 8, 8))
+    part = geom(grid=(5, 6, 7))
+    # Workspace: the packing plan, 16 bytes per tile slot row; none for full grids.
+    assert lib.vsa_sparse_attn_packed_workspace_bytes(full, 2) == 0
+    assert lib.vsa_sparse_attn_packed_workspace_bytes(part, 3) == 1 * 2 * 8 * 16 * 4
+    assert lib.vsa_sparse_attn_packed_workspace_bytes(part, 0) == 0
+    assert lib.vsa_sparse_attn_packed_workspace_bytes(part, 9) == 0
+    ws = lib.vsa_sparse_attn_packed_workspace_bytes(part, 3)
+    f = lib.vsa_sparse_attn_fwd_packed
+    assert f(part, P, R, P, P, P, 3, 0.125, P, None, None, ws, None) == _lib.VSA_ERR_NULL
+    assert f(part, P, R, P, P, P, 3, 0.125, P, None, P, ws - 1, None) == _lib.VSA_ERR_WORKSPACE
+    assert f(part, P, R, P, P, P, 3, 0.125, P, None, ODD, ws, None) == _lib.VSA_ERR_ALIGN
+    assert f(part, P, 1, P, P, P, 3, 0.125, P, None, P, ws, None) == _lib.VSA_ERR_LAYOUT
+    assert f(part, P, R, P, P, P, 0, 0.125, P, None, P, ws, None) == _lib.VSA_ERR_TOPK
+    assert f(part, P, T, P, P, P, 3, -1.0, P, None, P, ws, None) == _lib.VSA_ERR_SCALE
+    assert f(part, P, R, None, P, P, 3, 0.125, P, None, P, ws, None) == _lib.VSA_ERR_NULL
+    assert f(part, P, R, P, P, P, 3, 0.125, P, ODD, P, ws, None) == _lib.VSA_ERR_ALIGN
+    # A full grid needs no workspace, but the other checks still apply.
+    assert f(full, P, R, P, P, P, 9, 0.125, P, None, None, 0, None) == _lib.VSA_ERR_TOPK
+    assert f(geom(D=32), P, R, P, P, P, 2, 0.125, P, None, None, 0, None) == _lib.VSA_ERR_HEAD_DIM
+    # Compact permutes.
+    assert lib.vsa_cube_permute(part, P, None, _lib.VSA_LAYOUT_TOKEN_COMPACT, None) == _lib.VSA_ERR_NULL
+    assert lib.vsa_cube_permute(part, None, P, _lib.VSA_LAYOUT_DIM_SLOTS, None) == _lib.VSA_ERR_NULL
+    assert lib.vsa_cube_permute(part, P, P, 5, None) == _lib.VSA_ERR_LAYOUT
+    assert lib.vsa_cube_permute_pool_compact(part, P, None, P, None) == _lib.VSA_ERR_NULL
+    assert lib.vsa_cube_permute_pool_compact(part, P, P, ODD, None) == _lib.VSA_ERR_ALIGN

@@ -123,3 +123,60 @@ def test_pooled_path_matches_oracle_integer_inputs(name, grid, topk):
     _, kbar = vsa.cube_permute_pool(to_dev(inp["k"]), wl.grid)
     got = vsa.select_topk_pooled(qbar, kbar, wl.grid, wl.topk).cpu().numpy()
     assert np.array_equal(got, oracle_select(inp, wl, wl.topk))
+
+
+FLOAT_GRIDS = [((8, 8, 8), 2), ((5, 6, 7), 3), ((13, 10, 22), 9), ((21, 45, 20), 30)]
+
+
+@pytest.mark.parametrize("grid,topk", FLOAT_GRIDS)
+@pytest.mark.parametrize("D", [64, 128])
+def test_pooled_topk_float_inputs_near_tie_valid(grid, topk, D):
+    # The benchmark's chain: means of Q from vsa_cube_pool, of K from
+    # vsa_cube_permute_pool, then vsa_select_topk_pooled; on float inputs and
+    # partial cubes with non-power-of-two valid counts (5 x 6 x 7: counts
+    # 1..3 per axis).
+    import block_sparse_video_cube_amd as vsa
+
+    wl = workloads.workload("tiny").with_(grid=grid, topk=topk, heads=3, head_dim=D)
+    inp = workloads.make_inputs(wl)
+    qbar = vsa.cube_pool(to_dev(inp["q"]), wl.grid)
+    _, kbar = vsa.cube_permute_pool(to_dev(inp["k"]), wl.grid)
+    got = vsa.select_topk_pooled(qbar, kbar, wl.grid, topk).cpu().numpy()
+    valid = oracle.valid_rows(wl.grid)
+    qc, kc = oracle.cube_permute(inp["q"], wl.grid), oracle.cube_permute(inp["k"], wl.grid)
+    s = oracle.block_scores(oracle.cube_means(qc, valid), oracle.cube_means(kc, valid))
+    ref = oracle.select_topk(qc, kc, valid, topk)
+    exact = 0
+    for h in range(wl.heads):
+        for i in range(wl.n_cubes):
+            assert topk_valid_under(s[0, h, i], got[0, h, i], topk), (h, i)
+            exact += int(np.array_equal(got[0, h, i], ref[0, h, i]))
+    print(f"pooled rows identical to the oracle: {exact}/{wl.heads * wl.n_cubes}")
+
+
+@pytest.mark.parametrize("grid", [(5, 6, 7), (13, 10, 22), (8, 8, 8)])
+@pytest.mark.parametrize("D", [64, 128])
+def test_cube_means_identical_across_entry_points(grid, D):
+    # vsa_select_topk pools cube-major rows itself (its workspace starts with
+    # the Q means, then the K means); vsa_cube_permute_pool and vsa_cube_pool
+    # pool raster rows.  All three sum in the same order, so the means and the
+    # selections agree bit for bit on float inputs.
+    import torch
+
+    import block_sparse_video_cube_amd as vsa
+
+    wl = workloads.workload("tiny").with_(grid=grid, heads=2, head_dim=D, topk=3)
+    inp = workloads.make_inputs(wl)
+    q, k = to_dev(inp["q"]), to_dev(inp["k"])
+    qc, qbar = vsa.cube_permute_pool(q, wl.grid)
+    kc, kbar = vsa.cube_permute_pool(k, wl.grid)
+    assert torch.equal(vsa.cube_pool(q, wl.grid), qbar)
+    g = vsa.make_geom(wl.batch, wl.heads, D, wl.grid)
+    ws = torch.empty(vsa.workspace_bytes(g), dtype=torch.uint8, device="cuda:0")
+    idx = vsa.select_topk(qc, kc, wl.grid, wl.topk, workspace=ws)
+    torch.cuda.synchronize()
+    n = qbar.numel()
+    means = ws[:8 * n].view(torch.float32)
+    assert torch.equal(means[:n].view_as(qbar), qbar)
+    assert torch.equal(means[n:].view_as(kbar), kbar)
+    assert torch.equal(vsa.select_topk_pooled(qbar, kbar, wl.grid, wl.topk), idx)

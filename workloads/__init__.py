@@ -26,7 +26,9 @@ a single head without drawing the whole tensor.
 
 from __future__ import annotations
 
+import concurrent.futures
 import dataclasses
+import os
 from fractions import Fraction
 from typing import Dict, Optional, Tuple
 
@@ -216,13 +218,17 @@ def make_inputs(wl: Workload, heads=None) -> Dict[str, np.ndarray]:
     """
     B, S, Hh, D = wl.batch, wl.tokens, wl.heads, wl.head_dim
     hs = range(Hh) if heads is None else heads
-    out = {}
-    for name in ("q", "k", "v"):
-        arr = np.zeros((B, S, Hh, D), dtype=np.uint16)
-        for b in range(B):
-            for h in hs:
-                arr[b, :, h, :] = make_head(wl, name, b, h)
-        out[name] = arr
+    out = {name: np.zeros((B, S, Hh, D), dtype=np.uint16) for name in ("q", "k", "v")}
+
+    def fill(job):
+        name, b, h = job
+        out[name][b, :, h, :] = make_head(wl, name, b, h)
+
+    # Every head comes from its own stream, so the heads can be drawn in any
+    # order (and in parallel threads) with the same result.
+    jobs = [(name, b, h) for name in ("q", "k", "v") for b in range(B) for h in hs]
+    with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, os.cpu_count() or 1)) as ex:
+        list(ex.map(fill, jobs))
     return out
 
 
