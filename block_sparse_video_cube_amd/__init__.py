@@ -51,6 +51,7 @@ __all__ = [
     "sparse_attn_linear_fwd",
     "quant_fp8",
     "quant_fp8_workspace_bytes",
+    "quant_fp8_noalloc",
     "sparse_attn_fwd_fp8",
     "vsa_attention",
     "workspace_bytes",
@@ -346,13 +347,15 @@ def quant_fp8_workspace_bytes(g: VsaGeom) -> int:
 
 
 def quant_fp8(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, grid: Sequence[int], want_means: bool = False,
-              out=None, workspace: Optional[torch.Tensor] = None):
+              out=None, workspace: Optional[torch.Tensor] = None, noalloc: bool = False):
     """E4M3 codes of raster Q, K (per (b, h, cube)) and V (per (b, h, channel)).
 
     Returns (q8, qscale, k8, kscale, v8t, vscale, qmean, kmean): codes uint8
     [B, heads, Np, D] and [B, heads, Nc, D, 64], scales f32 [B, heads, Nc] and
     [B, heads, D], cube means f32 [B, heads, Nc, D] or None.  `out`: optional
     tuple of the same eight tensors to write into (means may be None).
+    noalloc: use vsa_quant_fp8_noalloc (the library's static scratch instead
+    of a workspace; with `out` given, nothing is allocated).
     """
     B, S, Hh, D = q.shape
     g = make_geom(B, Hh, D, grid)
@@ -379,6 +382,12 @@ def quant_fp8(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, grid: Sequence[
         if t is not None:
             _need(t, n, torch.float32, (B, Hh, d.n_cubes, D))
     lib = _lib.load()
+    if noalloc:
+        _lib.check("vsa_quant_fp8_noalloc", lib.vsa_quant_fp8_noalloc(
+            g, q.data_ptr(), k.data_ptr(), v.data_ptr(), q8.data_ptr(), qs.data_ptr(), k8.data_ptr(),
+            ks.data_ptr(), v8t.data_ptr(), vs.data_ptr(), qm.data_ptr() if qm is not None else None,
+            km.data_ptr() if km is not None else None, _stream()))
+        return q8, qs, k8, ks, v8t, vs, qm, km
     nbytes = lib.vsa_quant_fp8_workspace_bytes(g)
     if workspace is None:
         workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=dev)
@@ -388,6 +397,12 @@ def quant_fp8(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, grid: Sequence[
         km.data_ptr() if km is not None else None, workspace.data_ptr(),
         workspace.numel() * workspace.element_size(), _stream()))
     return q8, qs, k8, ks, v8t, vs, qm, km
+
+
+def quant_fp8_noalloc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, grid: Sequence[int],
+                      want_means: bool = False, out=None):
+    """quant_fp8 through vsa_quant_fp8_noalloc (no workspace; see include/vsa_cube.h)."""
+    return quant_fp8(q, k, v, grid, want_means=want_means, out=out, noalloc=True)
 
 
 def sparse_attn_fwd_fp8(q8: torch.Tensor, qscale: torch.Tensor, k8: torch.Tensor, kscale: torch.Tensor,

@@ -19,6 +19,8 @@ VSA_ERR_LAYOUT = 7
 VSA_ERR_SCALE = 8
 VSA_ERR_LAUNCH = 9
 VSA_ERR_WINDOW = 10
+VSA_ERR_SCRATCH = 11
+VSA_QUANT_SCRATCH_WORDS = 65536
 
 VSA_LAYOUT_TOKEN_MAJOR = 0
 VSA_LAYOUT_DIM_MAJOR = 1
@@ -56,6 +58,7 @@ ENTRY_POINTS = (
     "vsa_cube_permute_pool_compact",
     "vsa_sparse_attn_packed_workspace_bytes",
     "vsa_sparse_attn_fwd_packed",
+    "vsa_quant_fp8_noalloc",
 )
 
 
@@ -137,6 +140,7 @@ def load() -> ctypes.CDLL:
         "vsa_cube_permute_pool_compact": (i32, [G, P, P, P, P]),
         "vsa_sparse_attn_packed_workspace_bytes": (sz, [G, i32]),
         "vsa_sparse_attn_fwd_packed": (i32, [G, P, i32, P, P, P, i32, ctypes.c_float, P, P, P, sz, P]),
+        "vsa_quant_fp8_noalloc": (i32, [G, P, P, P, P, P, P, P, P, P, P, P, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)

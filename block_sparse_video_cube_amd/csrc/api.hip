@@ -59,6 +59,7 @@ const char* vsa_status_string(int32_t status) {
     case VSA_ERR_SCALE: return "softmax scale must be finite and positive";
     case VSA_ERR_LAUNCH: return "kernel launch failed";
     case VSA_ERR_WINDOW: return "sliding-tile window must be at least 1 cube on every axis";
+    case VSA_ERR_SCRATCH: return "problem larger than the library's static scratch (allocation-free entry point)";
     default: return "unknown status";
   }
 }
@@ -257,6 +258,26 @@ int32_t vsa_quant_fp8(const vsa_geom* g, const uint16_t* q, const uint16_t* k, c
   if (ws_bytes < vsa::quant_workspace_bytes(kg)) return VSA_ERR_WORKSPACE;
   return launch_status(vsa::launch_quant(kg, q, k, v, q8, qscale, k8, kscale, v8t, vscale, qmean, kmean, ws,
                                          static_cast<hipStream_t>(stream)));
+}
+
+int32_t vsa_quant_fp8_noalloc(const vsa_geom* g, const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                              uint8_t* q8, float* qscale, uint8_t* k8, float* kscale, uint8_t* v8t, float* vscale,
+                              float* qmean, float* kmean, void* stream) {
+  vsa_dims d;
+  vsa::KGeom kg;
+  int32_t st = prepare(g, &d, &kg);
+  if (st != VSA_OK) return st;
+  const void* ptrs[] = {q, k, v, q8, qscale, k8, kscale, v8t, vscale};
+  for (const void* p : ptrs)
+    if (!p) return VSA_ERR_NULL;
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return VSA_ERR_ALIGN;
+  if ((qmean && !aligned16(qmean)) || (kmean && !aligned16(kmean))) return VSA_ERR_ALIGN;
+  if ((int64_t)g->batch * g->heads * g->head_dim > VSA_QUANT_SCRATCH_WORDS) return VSA_ERR_SCRATCH;
+  uint32_t* ws = nullptr;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  if (vsa::quant_scratch(s, &ws) != hipSuccess) return VSA_ERR_LAUNCH;
+  return launch_status(vsa::launch_quant(kg, q, k, v, q8, qscale, k8, kscale, v8t, vscale, qmean, kmean, ws, s));
 }
 
 int32_t vsa_sparse_attn_fwd_fp8(const vsa_geom* g, const uint8_t* q8, const float* qscale, const uint8_t* k8,

@@ -168,6 +168,9 @@ size_t quant_workspace_bytes(const KGeom& g);
 hipError_t launch_quant(const KGeom& g, const uint16_t* q, const uint16_t* k, const uint16_t* v, uint8_t* q8,
                         float* qs, uint8_t* k8, float* ks, uint8_t* v8t, float* vs, float* qmean, float* kmean,
                         void* ws, hipStream_t s);
+// The device address of the quantizer's static scratch array (VSA_QUANT_SCRATCH_WORDS
+// words) on the device of stream s, looked up once per device.
+hipError_t quant_scratch(hipStream_t s, uint32_t** out);
 hipError_t launch_attn_fwd_fp8(const KGeom& g, const uint8_t* q8, const float* qs, const uint8_t* k8,
                                const float* ks, const uint8_t* v8t, const float* vs, const int32_t* idx, int topk,
                                float scale, bool raster_out, uint16_t* o, float* lse, hipStream_t s);

@@ -21,6 +21,8 @@
 //     atomic max on the fp32 bit patterns (non-negative floats order as
 //     unsigned integers);
 //   pass 2, one workgroup per (b, h, cube): V's codes, transposed per cube.
+#include <mutex>
+
 #include "common.h"
 
 namespace vsa {
@@ -258,6 +260,45 @@ void launch_quant_t(const KGeom& g, const uint16_t* q, const uint16_t* k, const 
 }
 
 }  // namespace
+
+// The allocation-free entry point keeps the head maxima of V in this static
+// array instead of a caller workspace: every device the library runs on holds
+// its own copy (until the process ends).  Host code reaches it only through
+// the address hipGetSymbolAddress returns for the device (quant_scratch);
+// the array's name is not a device address on the host.
+static __device__ __align__(256) uint32_t scratch[VSA_QUANT_SCRATCH_WORDS];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mu;
+uint32_t* scratch_ptr[kMaxDevices] = {};
+}  // namespace
+
+hipError_t quant_scratch(hipStream_t s, uint32_t** out) {
+  int dev = 0;
+  hipError_t e = s ? hipStreamGetDevice(s, &dev) : hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(scratch_mu);
+  if (!scratch_ptr[dev]) {
+    // Once per device, with that device current.
+    int cur = 0;
+    e = hipGetDevice(&cur);
+    if (e != hipSuccess) return e;
+    if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess) return e;
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (cur != dev) {
+      const hipError_t e2 = hipSetDevice(cur);
+      if (e == hipSuccess) e = e2;
+    }
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    scratch_ptr[dev] = static_cast<uint32_t*>(p);
+  }
+  *out = scratch_ptr[dev];
+  return hipSuccess;
+}
 
 size_t quant_workspace_bytes(const KGeom& g) {
   return ((size_t)g.B * g.H * g.D * sizeof(uint32_t) + 255) / 256 * 256;

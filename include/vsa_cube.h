@@ -62,7 +62,8 @@ typedef enum vsa_status {
   VSA_ERR_LAYOUT = 7,    /* unknown layout code                               */
   VSA_ERR_SCALE = 8,     /* softmax scale not finite and positive             */
   VSA_ERR_LAUNCH = 9,    /* a kernel launch failed (HIP error)                */
-  VSA_ERR_WINDOW = 10    /* a sliding-tile window below 1 cube on some axis   */
+  VSA_ERR_WINDOW = 10,   /* a sliding-tile window below 1 cube on some axis   */
+  VSA_ERR_SCRATCH = 11   /* problem larger than a static scratch array       */
 } vsa_status;
 
 /* Shape of one attention layer. */
@@ -300,6 +301,24 @@ size_t vsa_quant_fp8_workspace_bytes(const vsa_geom* g);
 int32_t vsa_quant_fp8(const vsa_geom* g, const uint16_t* q, const uint16_t* k, const uint16_t* v, uint8_t* q8,
                       float* qscale, uint8_t* k8, float* kscale, uint8_t* v8t, float* vscale, float* qmean,
                       float* kmean, void* ws, size_t ws_bytes, void* stream);
+/* vsa_quant_fp8 for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same launches and results, with the V head maxima kept in a static
+ * device array of the library instead of a caller workspace.  The array holds
+ * VSA_QUANT_SCRATCH_WORDS 32-bit words (256 KB) on every device the library
+ * runs on, until the process ends; its address is looked up once per device
+ * (on the first call there), and no call allocates or frees memory.  The
+ * launches clear the words they use (with a kernel, no memset).  Every call on
+ * one device shares that array and leaves its contents behind: calls that
+ * overlap on one device (several streams or threads) race, and the caller
+ * must order them.  The stream's device is used (the current device for the
+ * NULL stream).  Errors: as vsa_quant_fp8 (no ws arguments), and
+ * VSA_ERR_SCRATCH when B * heads * D > VSA_QUANT_SCRATCH_WORDS (nothing is
+ * launched); VSA_ERR_LAUNCH if the array's address cannot be obtained. */
+#define VSA_QUANT_SCRATCH_WORDS 65536
+int32_t vsa_quant_fp8_noalloc(const vsa_geom* g, const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                              uint8_t* q8, float* qscale, uint8_t* k8, float* kscale, uint8_t* v8t,
+                              float* vscale, float* qmean, float* kmean, void* stream);
 int32_t vsa_sparse_attn_fwd_fp8(const vsa_geom* g, const uint8_t* q8, const float* qscale,
                                 const uint8_t* k8, const float* kscale, const uint8_t* v8t,
                                 const float* vscale, const int32_t* idx, int32_t topk,

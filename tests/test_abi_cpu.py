@@ -42,7 +42,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 def test_abi_version_and_status_text(lib):
     assert lib.vsa_abi_version() == 2
-    for code in range(11):
+    for code in range(12):
         assert lib.vsa_status_string(code)
     assert lib.vsa_status_string(12345) == b"unknown status"
 
