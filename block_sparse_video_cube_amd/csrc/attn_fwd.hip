@@ -69,7 +69,8 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd(const uint16_t* __restri
                                                         const uint16_t* __restrict__ kc,
                                                         const uint16_t* __restrict__ vt,
                                                         const int32_t* __restrict__ idx,
-                                                        const int32_t* __restrict__ plan, int topk, float scale,
+                                                        const int32_t* __restrict__ plan,
+                                                        const int32_t* __restrict__ order, int topk, float scale,
                                                         float scale_log2, uint16_t* __restrict__ oc,
                                                         float* __restrict__ oc_f32, float* __restrict__ lse,
                                                         KGeom g, Placement pl) {
@@ -86,6 +87,9 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd(const uint16_t* __restri
   const int wq = w & 1, wk = w >> 1;  // wave-uniform
   const int hf = lane >> 5, n = lane & 31;
   const long long bh = (long long)b * g.H + h;
+  // PLAN: the query cubes of a head run in the order plan_order gives
+  // (most tiles first); each cube's result does not depend on that order.
+  if (PLAN) i = order[bh * g.nc + i];
   // K source: the head's cube-major rows, or (RASTER) its raster rows.
   const uint16_t* kbase = KRASTER ? kc + ((long long)b * g.S * g.H + h) * D : kc + bh * g.Np * D;
   const uint16_t* vbase = vt + bh * g.Np * D;
@@ -126,8 +130,7 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd(const uint16_t* __restri
   if (KRASTER) raster_lane_offsets<D>(g, w, lane, roff, rrow);
   // SLOTS: lane offsets of this wavefront's V slot (one contiguous block).
   uint32_t vso[NI];
-#pragma unroll
-  for (int e = 0; e < NI; ++e) vso[e] = (uint32_t)(e * 64 + lane) * 16u;
+  v_slot_offsets<D>(lane, vso);
   const uint32_t* voffs = SLOTS ? vso : toff.v;
   uint32_t kto[NI];
   // Buffer resource of this wavefront's K loads of tile m (offsets in kto).
@@ -380,13 +383,44 @@ __global__ void __launch_bounds__(256) block_plan(const int32_t* __restrict__ id
   }
 }
 
+// Launch order of the query cubes of each (b, h) for the packed fine stage:
+// by number of tiles, most first.  Workgroups that the hardware runs together
+// on an XCD (consecutive launch positions) then carry equal work, start and
+// finish together, and sweep their ascending key lists in step, so tiles that
+// several of them selected are fetched into the XCD's L2 once for all.
+// One workgroup per (b, h): a histogram of the tile counts in LDS, bins
+// ordered from the largest count, cubes placed with LDS atomics (the order
+// within a bin is arbitrary; it affects speed only).
+__global__ void __launch_bounds__(256) plan_order(const int32_t* __restrict__ plan, int topk,
+                                                  int32_t* __restrict__ order, int nc) {
+  extern __shared__ int bins[];  // topk + 1 counters, then the running offsets in place
+  const long long bh = blockIdx.x;
+  const long long stride = 4LL * (topk + 1);
+  const int32_t* rows = plan + bh * nc * stride;
+  for (int t = threadIdx.x; t <= topk; t += 256) bins[t] = 0;
+  __syncthreads();
+  for (int c = threadIdx.x; c < nc; c += 256) atomicAdd(&bins[rows[c * stride]], 1);
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int run = 0;  // bins from the largest tile count down: exclusive offsets
+    for (int t = topk; t >= 0; --t) {
+      const int cnt = bins[t];
+      bins[t] = run;
+      run += cnt;
+    }
+  }
+  __syncthreads();
+  for (int c = threadIdx.x; c < nc; c += 256) order[bh * nc + atomicAdd(&bins[rows[c * stride]], 1)] = c;
+}
+
 template <int D, bool PARTIAL, bool RASTER, bool KRASTER, bool SLOTS = false>
 void launch_fwd(const KGeom& g, const uint16_t* qc, const uint16_t* kc, const uint16_t* vt, const int32_t* idx,
-                const int32_t* plan, int topk, float scale, uint16_t* oc, float* oc_f32, float* lse, hipStream_t s) {
+                const int32_t* plan, const int32_t* order, int topk, float scale, uint16_t* oc, float* oc_f32,
+                float* lse, hipStream_t s) {
   const Placement pl = make_placement(g);
   const float scale_log2 = scale * 1.4426950408889634f;
   attn_fwd<D, PARTIAL, RASTER, KRASTER, SLOTS><<<dim3(grid_size(g)), dim3(kThreads), 0, s>>>(
-      qc, kc, vt, idx, plan, topk, scale, scale_log2, oc, oc_f32, lse, g, pl);
+      qc, kc, vt, idx, plan, order, topk, scale, scale_log2, oc, oc_f32, lse, g, pl);
 }
 
 template <bool RASTER, bool KRASTER>
@@ -394,11 +428,11 @@ hipError_t launch_fwd_any(const KGeom& g, const uint16_t* q, const uint16_t* k, 
                           const int32_t* idx, int topk, float scale, uint16_t* o, float* o_f32, float* lse,
                           hipStream_t s) {
   if (g.D == 64) {
-    if (g.partial) launch_fwd<64, true, RASTER, KRASTER>(g, q, k, vt, idx, nullptr, topk, scale, o, o_f32, lse, s);
-    else launch_fwd<64, false, RASTER, KRASTER>(g, q, k, vt, idx, nullptr, topk, scale, o, o_f32, lse, s);
+    if (g.partial) launch_fwd<64, true, RASTER, KRASTER>(g, q, k, vt, idx, nullptr, nullptr, topk, scale, o, o_f32, lse, s);
+    else launch_fwd<64, false, RASTER, KRASTER>(g, q, k, vt, idx, nullptr, nullptr, topk, scale, o, o_f32, lse, s);
   } else {
-    if (g.partial) launch_fwd<128, true, RASTER, KRASTER>(g, q, k, vt, idx, nullptr, topk, scale, o, o_f32, lse, s);
-    else launch_fwd<128, false, RASTER, KRASTER>(g, q, k, vt, idx, nullptr, topk, scale, o, o_f32, lse, s);
+    if (g.partial) launch_fwd<128, true, RASTER, KRASTER>(g, q, k, vt, idx, nullptr, nullptr, topk, scale, o, o_f32, lse, s);
+    else launch_fwd<128, false, RASTER, KRASTER>(g, q, k, vt, idx, nullptr, nullptr, topk, scale, o, o_f32, lse, s);
   }
   return hipGetLastError();
 }
@@ -418,21 +452,26 @@ hipError_t launch_attn_fwd_raster(const KGeom& g, const uint16_t* q, const uint1
   return launch_fwd_any<true, false>(g, q, k, vt, idx, topk, scale, o, nullptr, lse, s);
 }
 
+// Packed workspace: the plan (16 bytes per tile and a 16-byte header per
+// row), then the launch order (one int32 per query cube).
 size_t attn_packed_workspace_bytes(const KGeom& g, int topk) {
   if (!g.partial) return 0;
-  return (size_t)g.B * g.H * g.nc * 16u * ((size_t)topk + 1);
+  const size_t rows = (size_t)g.B * g.H * g.nc;
+  return rows * 16u * ((size_t)topk + 1) + (rows * 4u + 255) / 256 * 256;
 }
 
 hipError_t launch_attn_fwd_packed(const KGeom& g, const uint16_t* q, bool raster, const uint16_t* kc,
                                   const uint16_t* vs, const int32_t* idx, int topk, float scale, uint16_t* o,
                                   float* lse, void* ws, hipStream_t s) {
   int32_t* plan = static_cast<int32_t*>(ws);
+  const long long nrows = (long long)g.B * g.H * g.nc;
+  int32_t* order = plan + nrows * 4LL * (topk + 1);
   if (g.partial) {
-    const long long nrows = (long long)g.B * g.H * g.nc;
     block_plan<<<dim3((unsigned)((nrows + 3) / 4)), dim3(256), 0, s>>>(idx, topk, plan, g, nrows);
+    plan_order<<<dim3((unsigned)(g.B * g.H)), dim3(256), (topk + 1) * sizeof(int), s>>>(plan, topk, order, g.nc);
   }
 #define VSA_PACKED(DD, PP, RR) \
-  launch_fwd<DD, PP, RR, false, true>(g, q, kc, vs, idx, plan, topk, scale, o, nullptr, lse, s)
+  launch_fwd<DD, PP, RR, false, true>(g, q, kc, vs, idx, plan, order, topk, scale, o, nullptr, lse, s)
   if (g.D == 64) {
     if (g.partial) { if (raster) VSA_PACKED(64, true, true); else VSA_PACKED(64, true, false); }
     else { if (raster) VSA_PACKED(64, false, true); else VSA_PACKED(64, false, false); }

@@ -270,17 +270,37 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t v_slot_rsrc(const uint16_t* vh
   return make_rsrc(vhead + off, slot_count(code) ? (unsigned)(16 * D * 2) : 0u);
 }
 
+// In LDS a V slot is D channel rows of two 16-byte halves (keys 0..7 and
+// 8..15); the halves of rows with bit 3 set trade places, so the 16 lanes of
+// one pass of a 16-byte read (16 consecutive rows, one half) cover all banks.
+__device__ __forceinline__ int v_slot_half(int row, int h) { return h ^ ((row >> 3) & 1); }
+
+// Lane offsets of this wavefront's V slot load: lane L of instruction e fills
+// 16-byte position p = 64 e + L of the slot (row p / 2, half p % 2 after the
+// swap), from the same row and logical half of the slot in HBM.
+template <int D>
+__device__ __forceinline__ void v_slot_offsets(int lane, uint32_t* off) {
+#pragma unroll
+  for (int e = 0; e < D / 32; ++e) {
+    const int p = 64 * e + lane, row = p >> 1;
+    off[e] = (uint32_t)(2 * row + v_slot_half(row, p & 1)) * 16u;
+  }
+}
+
 // V^T fragments from a slot-layout V tile in LDS: the same operands as
 // read_v (chunk 4 wk + 2 kk + hf of channel row 32 dt + n is keys 8 hf ..
-// 8 hf + 7 of slot 2 wk + kk); a wavefront reads 1 KB contiguous.
+// 8 hf + 7 of slot 2 wk + kk).
 template <int D>
 __device__ __forceinline__ void read_v_slots(const uint16_t* vlds, int wk, int hf, int n,
                                              bf16x8 (&va)[D / 32][2]) {
 #pragma unroll
-  for (int dt = 0; dt < D / 32; ++dt)
+  for (int dt = 0; dt < D / 32; ++dt) {
+    const int row = 32 * dt + n;
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk)
-      va[dt][kk] = *reinterpret_cast<const bf16x8*>(vlds + (2 * wk + kk) * (D * 16) + (32 * dt + n) * 16 + 8 * hf);
+      va[dt][kk] = *reinterpret_cast<const bf16x8*>(vlds + (2 * wk + kk) * (D * 16) + row * 16 +
+                                                    8 * v_slot_half(row, hf));
+  }
 }
 
 // Keys of a packed tile past their slot's count take no weight.  In the S^T

@@ -291,9 +291,11 @@ def test_packed_entry_point_validation(lib):
     R, T = _lib.VSA_LAYOUT_RASTER, _lib.VSA_LAYOUT_TOKEN_MAJOR
     full = geom(grid=(8, 8, 8))
     part = geom(grid=(5, 6, 7))
-    # Workspace: the packing plan, 16 bytes per tile slot row; none for full grids.
+    # Workspace: the packing plan (16 bytes per tile and per row header), then
+    # the launch order (an int32 per query cube, rounded up to 256 bytes);
+    # none for full grids.
     assert lib.vsa_sparse_attn_packed_workspace_bytes(full, 2) == 0
-    assert lib.vsa_sparse_attn_packed_workspace_bytes(part, 3) == 1 * 2 * 8 * 16 * 4
+    assert lib.vsa_sparse_attn_packed_workspace_bytes(part, 3) == 1 * 2 * 8 * 16 * 4 + 256
     assert lib.vsa_sparse_attn_packed_workspace_bytes(part, 0) == 0
     assert lib.vsa_sparse_attn_packed_workspace_bytes(part, 9) == 0
     ws = lib.vsa_sparse_attn_packed_workspace_bytes(part, 3)

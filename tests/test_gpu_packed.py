@@ -9,7 +9,8 @@
 - The raster and cube-major forms are bit-identical (output and lse); on a
   grid without padding the packed stage is bit-identical to the unpacked one.
 - The packing plan in the workspace holds every selected cube's valid keys
-  exactly once.
+  exactly once, and the launch order of each head is a permutation of its
+  query cubes with the most tiles first.
 """
 
 import numpy as np
@@ -142,7 +143,15 @@ def test_packing_plan_covers_every_selected_key_once():
     kc = vsa.cube_permute(to_dev(inp["k"]), grid, layout="compact")
     vs = vsa.cube_permute(to_dev(inp["v"]), grid, layout="slots")
     vsa.sparse_attn_fwd_packed(run_q, kc, vs, idx_d, grid, workspace=ws)
-    plan = ws.view(torch.int32).cpu().numpy().reshape(1, wl.heads, wl.n_cubes, topk + 1, 4)
+    words = ws.view(torch.int32).cpu().numpy()
+    nplan = wl.heads * wl.n_cubes * (topk + 1) * 4
+    plan = words[:nplan].reshape(1, wl.heads, wl.n_cubes, topk + 1, 4)
+    # The launch order: per head a permutation of the query cubes, most tiles first.
+    order = words[nplan:nplan + wl.heads * wl.n_cubes].reshape(wl.heads, wl.n_cubes)
+    for h in range(wl.heads):
+        assert sorted(order[h].tolist()) == list(range(wl.n_cubes))
+        nt = plan[0, h, order[h], 0, 0]
+        assert np.all(np.diff(nt) <= 0)
     counts = oracle.valid_rows(grid).reshape(-1, 64).sum(axis=1)
     for h in range(wl.heads):
         for i in range(wl.n_cubes):
