@@ -72,14 +72,19 @@ int32_t vsa_geom_dims(const vsa_geom* g, vsa_dims* out) {
   if (g->head_dim != 64 && g->head_dim != 128) return VSA_ERR_HEAD_DIM;
   vsa_dims d;
   memset(&d, 0, sizeof(d));
-  d.pad_t = (int32_t)(((int64_t)g->grid_t + 3) / 4 * 4);
-  d.pad_h = (int32_t)(((int64_t)g->grid_h + 3) / 4 * 4);
-  d.pad_w = (int32_t)(((int64_t)g->grid_w + 3) / 4 * 4);
-  d.cubes_t = d.pad_t / 4;
-  d.cubes_h = d.pad_h / 4;
-  d.cubes_w = d.pad_w / 4;
-  const int64_t nc = (int64_t)d.cubes_t * d.cubes_h * d.cubes_w;
-  if (nc > (int64_t)1 << 24) return VSA_ERR_GEOMETRY;
+  // Cubes per axis in 64-bit, and their product checked factor by factor
+  // (every factor is at least 1), so nothing overflows or narrows before the
+  // n_cubes <= 2^24 limit holds.
+  const int64_t lim = (int64_t)1 << 24;
+  const int64_t ct = ((int64_t)g->grid_t + 3) / 4, ch = ((int64_t)g->grid_h + 3) / 4, cw = ((int64_t)g->grid_w + 3) / 4;
+  if (ct > lim || ch > lim || cw > lim || ct * ch > lim || ct * ch * cw > lim) return VSA_ERR_GEOMETRY;
+  const int64_t nc = ct * ch * cw;
+  d.cubes_t = (int32_t)ct;
+  d.cubes_h = (int32_t)ch;
+  d.cubes_w = (int32_t)cw;
+  d.pad_t = 4 * d.cubes_t;
+  d.pad_h = 4 * d.cubes_h;
+  d.pad_w = 4 * d.cubes_w;
   d.n_cubes = (int32_t)nc;
   d.tokens = (int64_t)g->grid_t * g->grid_h * g->grid_w;
   d.rows = 64 * nc;
@@ -384,6 +389,11 @@ int32_t vsa_sparse_attn_linear_fwd(const vsa_geom* g, const uint16_t* qc, const 
       (lse && !aligned16(lse)))
     return VSA_ERR_ALIGN;
   if (topk < 1 || topk > d.n_cubes) return VSA_ERR_TOPK;
+  // The fused pass subtracts the selected blocks from the total on the
+  // softmax branch's tiles; with more than half the cubes selected (and some
+  // left) that difference loses precision, and vsa_linear_branch sums the
+  // unselected cubes directly instead.
+  if (2 * (int64_t)topk > d.n_cubes && topk < d.n_cubes) return VSA_ERR_TOPK;
   if (!(softmax_scale > 0.f) || !isfinite(softmax_scale)) return VSA_ERR_SCALE;
   if (ws_bytes < vsa::linear_workspace_bytes(k)) return VSA_ERR_WORKSPACE;
   return launch_status(vsa::launch_attn_lin_fwd(k, qc, kc, vt, idx, topk, softmax_scale, ws, oc, lse,

@@ -575,7 +575,7 @@ struct BwdWs {
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 inline BwdWs carve(const KGeom& g, int topk, void* ws) {
-  char* p = static_cast<char*>(ws);
+  uintptr_t p = reinterpret_cast<uintptr_t>(ws);
   const size_t bh = (size_t)g.B * g.H;
   BwdWs w;
   w.delta = reinterpret_cast<float*>(p);

@@ -150,6 +150,15 @@ struct LinState {
   int group_size, group_count;
 };
 LinState lin_state_parts(const KGeom& g, void* ws);
+// Direct mode of the linear branch (more than half the cubes selected): the
+// complement lists in the workspace ([B, H, Nc, len] int32, ascending), built
+// by the forward's selected-block pass (launch_linear, launch_lin_bwd_rows).
+struct LinDirect {
+  int on;
+  const int32_t* comp;
+  int len;  // Nc - topk
+};
+LinDirect lin_direct(const KGeom& g, int topk, void* ws);
 hipError_t launch_block_lists_t(const KGeom& g, const int32_t* idx, int topk, int32_t* cnt, int32_t* off,
                                 int32_t* list, hipStream_t s);
 size_t linear_bwd_workspace_bytes(const KGeom& g, int topk);

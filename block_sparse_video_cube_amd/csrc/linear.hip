@@ -56,7 +56,19 @@ struct LinWs {
   uint16_t* st_hi;  // [B, H, D(e), D(d)] bf16
   uint16_t* st_lo;  // [B, H, D(e), D(d)] bf16
   float* z_tot;     // [B, H, D]
+  int32_t* comp;    // [B, H, Nc, comp_cap(g)]: unselected cubes per row (direct mode)
 };
+
+// Direct mode.  O_lin sums over the unselected cubes U.  The default form is
+// the total minus the selected blocks, which costs k blocks per query cube;
+// when more than half the cubes are selected, U is smaller than the list and
+// the difference of two nearly equal sums would magnify the bf16 rounding of
+// the selected products by about k / (Nc - k), so the branch sums U directly
+// from a complement list instead (Nc - k < k blocks, no cancellation).  The
+// lists hold at most Nc / 2 entries; grids above VSA_MAX_CUBES cubes keep the
+// total-minus-selected form.
+__host__ __device__ inline int comp_cap(const KGeom& g) { return g.nc <= VSA_MAX_CUBES ? g.nc / 2 : 0; }
+inline bool use_direct(const KGeom& g, int topk) { return 2 * topk > g.nc && topk < g.nc && comp_cap(g) > 0; }
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
@@ -64,8 +76,10 @@ LinWs carve(const KGeom& g, void* ws, size_t* total) {
   const size_t bh = (size_t)g.B * g.H;
   const size_t G = lin_groups(g).count;
   const size_t D = g.D;
+  // Addresses as integers: the sizing call passes no workspace (ws = NULL),
+  // and pointer arithmetic on a null pointer is undefined.
   size_t off = 0;
-  char* base = static_cast<char*>(ws);
+  const uintptr_t base = reinterpret_cast<uintptr_t>(ws);
   LinWs w;
   w.fk = reinterpret_cast<uint16_t*>(base + off);
   off += align256(bh * g.Np * D * 2);
@@ -79,6 +93,8 @@ LinWs carve(const KGeom& g, void* ws, size_t* total) {
   off += align256(bh * D * D * 2);
   w.z_tot = reinterpret_cast<float*>(base + off);
   off += align256(bh * D * 4);
+  w.comp = reinterpret_cast<int32_t*>(base + off);
+  off += align256(bh * g.nc * (size_t)comp_cap(g) * 4);
   if (total) *total = off;
   return w;
 }
@@ -213,6 +229,43 @@ __global__ void __launch_bounds__(256) lin_reduce(LinWs ws, KGeom g) {
   }
 }
 
+// The unselected cubes of every list row, ascending (direct mode), in rows of
+// cap = Nc - topk entries: one wavefront per row marks the selected cubes in
+// an LDS bitmask, then compacts the unmarked ones with ballots.  Rows hold
+// distinct entries, so there are exactly cap of them; extra ones (duplicate
+// entries) are dropped rather than written past the row.
+__global__ void __launch_bounds__(256) lin_complement(const int32_t* __restrict__ idx, int topk,
+                                                      int32_t* __restrict__ comp, int nc, int cap,
+                                                      long long nrows) {
+  __shared__ uint32_t bits[4][VSA_MAX_CUBES / 32];
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const long long row = (long long)blockIdx.x * 4 + wv;
+  const int nw = (nc + 31) / 32;
+  for (int t = lane; t < nw; t += 64) bits[wv][t] = 0u;
+  __builtin_amdgcn_wave_barrier();
+  if (row < nrows) {
+    const int32_t* irow = idx + row * topk;
+    for (int m = lane; m < topk; m += 64) {
+      const int j = irow[m];
+      if (j >= 0 && j < nc) atomicOr(&bits[wv][j >> 5], 1u << (j & 31));
+    }
+  }
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  if (row >= nrows) return;
+  int32_t* out = comp + row * cap;
+  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  int cnt = 0;
+  for (int base = 0; base < nc; base += 64) {
+    const int j = base + lane;
+    const bool un = j < nc && !((bits[wv][j >> 5] >> (j & 31)) & 1u);
+    const uint64_t mk = __ballot(un);
+    const int pos = cnt + __popcll(mk & below);
+    if (un && pos < cap) out[pos] = j;
+    cnt += __popcll(mk);
+  }
+}
+
 // Three phi(K) and two V^T tile buffers (80 KB at D = 128).
 template <int D>
 struct LinSmem {
@@ -232,13 +285,16 @@ struct LinSmem {
 // BWD: instead of the combine, the per-row inputs of the linear branch's
 // backward: w = dO / den (bf16), c = (dO . O_lin) / den (fp32) and phi(Q)
 // (bf16), zero on padded query rows and when no cube is left unselected.
+//
+// direct: the list is the row's complement list (ws.comp) and the branch
+// sums it (c and the denominator start at 0, weights not negated).
 template <int D, bool BWD>
 __global__ void __launch_bounds__(kThreads, 2) lin_apply(const uint16_t* __restrict__ qc,
                                                          const uint16_t* __restrict__ vt,
                                                          const int32_t* __restrict__ idx, int topk,
                                                          const float* __restrict__ o_sparse,
                                                          uint16_t* __restrict__ oc, LinWs ws, KGeom g,
-                                                         Placement pl, LinBwdRows br) {
+                                                         Placement pl, LinBwdRows br, int direct) {
   constexpr int DC = D / 16, DT = D / 32;
   __shared__ __attribute__((aligned(16))) LinSmem<D> sm;
   int i, h, b;
@@ -251,7 +307,9 @@ __global__ void __launch_bounds__(kThreads, 2) lin_apply(const uint16_t* __restr
   const int q = 32 * wq + n;
   const long long row = bh * g.Np + 64LL * i + q;
   const bool empty_u = topk >= g.nc;  // every cube selected: O_lin = 0
-  const int32_t* irow = idx + (bh * g.nc + i) * topk;
+  // The list the loop streams: the selected cubes, or (direct) the unselected ones.
+  topk = direct ? g.nc - topk : topk;
+  const int32_t* irow = (direct ? ws.comp : idx) + (bh * g.nc + i) * topk;
   const uint16_t* fkb = ws.fk + bh * g.Np * D;
   const uint16_t* vb = vt + bh * g.Np * D;
   const TileOffsets<D> toff(w, lane);
@@ -280,7 +338,7 @@ __global__ void __launch_bounds__(kThreads, 2) lin_apply(const uint16_t* __restr
         fq[dc][2 * e2] = __builtin_bit_cast(__bf16, p0);
         fq[dc][2 * e2 + 1] = __builtin_bit_cast(__bf16, p1);
         const int d = 16 * dc + 8 * hf + 2 * e2;
-        den_part += bf16_to_f32(p0) * zt[d] + bf16_to_f32(p1) * zt[d + 1];
+        if (!direct) den_part += bf16_to_f32(p0) * zt[d] + bf16_to_f32(p1) * zt[d + 1];
       }
       __builtin_amdgcn_sched_barrier(0);  // one chunk of loads at a time (register budget)
     }
@@ -290,11 +348,12 @@ __global__ void __launch_bounds__(kThreads, 2) lin_apply(const uint16_t* __restr
   // half), computed while the first tiles arrive; the loop below subtracts
   // the selected part by feeding the products exactly negated weights.
   f32x16 c[DT];
-  {
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) c[dt] = f32x16{};
+  if (!direct) {
     const uint16_t* st = (wk == 0 ? ws.st_hi : ws.st_lo) + bh * D * D;
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
-      c[dt] = f32x16{};
       const int e = 32 * dt + n;
 #pragma unroll
       for (int dc = 0; dc < DC; ++dc) {
@@ -303,6 +362,9 @@ __global__ void __launch_bounds__(kThreads, 2) lin_apply(const uint16_t* __restr
       }
     }
   }
+  // Selected blocks are subtracted (weights negated, exact in bf16); in
+  // direct mode the unselected blocks are added.
+  const uint32_t wsign = direct ? 0u : 0x80008000u;
 
   // Selected part, block by block.
   float dcorr = 0.f;
@@ -334,7 +396,7 @@ __global__ void __launch_bounds__(kThreads, 2) lin_apply(const uint16_t* __restr
         for (int r = 0; r < 8; ++r) {
           const bf16x2 pk = __builtin_convertvector((f32x2){sa[2 * r], sa[2 * r + 1]}, bf16x2);
           dcorr = __builtin_amdgcn_fdot2_f32_bf16(pk, ones, dcorr, false);
-          pw[r] = __builtin_bit_cast(uint32_t, pk) ^ 0x80008000u;  // -P' (exact in bf16)
+          pw[r] = __builtin_bit_cast(uint32_t, pk) ^ wsign;  // -P' (exact in bf16), or +P' (direct)
         }
         bf16x8 pb[2];
         pb[0] = __builtin_bit_cast(bf16x8, make_uint4(pw[0], pw[1], pw[2], pw[3]));
@@ -363,7 +425,7 @@ __global__ void __launch_bounds__(kThreads, 2) lin_apply(const uint16_t* __restr
   }
   __syncthreads();
   if (wk == 1) return;
-  const float den = (den_part + __shfl_xor(den_part, 32)) - (dcorr + xd[lane]);
+  const float den = direct ? dcorr + xd[lane] : (den_part + __shfl_xor(den_part, 32)) - (dcorr + xd[lane]);
   const float inv = empty_u ? 0.f : 1.f / den;
   if (BWD) {
     int ct, cy, cx;
@@ -421,6 +483,15 @@ __global__ void __launch_bounds__(kThreads, 2) lin_apply(const uint16_t* __restr
     }
 }
 
+// Direct mode (see comp_cap): the complement lists, and the mode flag.
+int launch_complement(const KGeom& g, const int32_t* idx, int topk, const LinWs& w, hipStream_t s) {
+  if (!use_direct(g, topk)) return 0;
+  const long long nrows = (long long)g.B * g.H * g.nc;
+  lin_complement<<<dim3((unsigned)((nrows + 3) / 4)), dim3(256), 0, s>>>(idx, topk, w.comp, g.nc, g.nc - topk,
+                                                                         nrows);
+  return 1;
+}
+
 }  // namespace
 
 size_t linear_workspace_bytes(const KGeom& g) {
@@ -455,24 +526,26 @@ hipError_t launch_linear(const KGeom& g, const uint16_t* qc, const uint16_t* kc,
   if (e != hipSuccess) return e;
   const LinWs w = carve(g, ws, nullptr);
   const LinBwdRows none{};
+  const int direct = launch_complement(g, idx, topk, w, s);
   if (g.D == 64)
     hipLaunchKernelGGL((lin_apply<64, false>), dim3(grid_size(g)), dim3(kThreads), 0, s, qc, vt, idx, topk,
-                       o_sparse, oc, w, g, make_placement(g), none);
+                       o_sparse, oc, w, g, make_placement(g), none, direct);
   else
     hipLaunchKernelGGL((lin_apply<128, false>), dim3(grid_size(g)), dim3(kThreads), 0, s, qc, vt, idx, topk,
-                       o_sparse, oc, w, g, make_placement(g), none);
+                       o_sparse, oc, w, g, make_placement(g), none, direct);
   return hipGetLastError();
 }
 
 hipError_t launch_lin_bwd_rows(const KGeom& g, const uint16_t* qc, const uint16_t* vt, const int32_t* idx, int topk,
                                const LinBwdRows& br, void* ws, hipStream_t s) {
   const LinWs w = carve(g, ws, nullptr);
+  const int direct = launch_complement(g, idx, topk, w, s);
   if (g.D == 64)
     hipLaunchKernelGGL((lin_apply<64, true>), dim3(grid_size(g)), dim3(kThreads), 0, s, qc, vt, idx, topk, nullptr,
-                       nullptr, w, g, make_placement(g), br);
+                       nullptr, w, g, make_placement(g), br, direct);
   else
     hipLaunchKernelGGL((lin_apply<128, true>), dim3(grid_size(g)), dim3(kThreads), 0, s, qc, vt, idx, topk,
-                       nullptr, nullptr, w, g, make_placement(g), br);
+                       nullptr, nullptr, w, g, make_placement(g), br, direct);
   return hipGetLastError();
 }
 
@@ -480,6 +553,12 @@ LinState lin_state_parts(const KGeom& g, void* ws) {
   const LinWs w = carve(g, ws, nullptr);
   const LinGroups lg = lin_groups(g);
   return LinState{w.fk, w.s_part, w.z_part, w.z_tot, lg.size, lg.count};
+}
+
+LinDirect lin_direct(const KGeom& g, int topk, void* ws) {
+  const LinWs w = carve(g, ws, nullptr);
+  const bool d = use_direct(g, topk);
+  return LinDirect{d ? 1 : 0, d ? w.comp : nullptr, d ? g.nc - topk : 0};
 }
 
 }  // namespace vsa

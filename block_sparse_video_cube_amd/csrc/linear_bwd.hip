@@ -60,9 +60,10 @@ inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 LinBwdWs carve_bwd(const KGeom& g, int topk, void* ws, size_t* total) {
   const size_t bh = (size_t)g.B * g.H, D = g.D, Np = g.Np, nc = g.nc;
   size_t off = align256(linear_workspace_bytes(g));
-  char* base = static_cast<char*>(ws);
+  // Addresses as integers: the sizing call passes no workspace (ws = NULL).
+  const uintptr_t base = reinterpret_cast<uintptr_t>(ws);
   auto take = [&](size_t bytes) {
-    char* p = base + off;
+    const uintptr_t p = base + off;
     off += align256(bytes);
     return p;
   };
@@ -247,7 +248,7 @@ __global__ void __launch_bounds__(kThreads, 2) lin_bwd_dq(const uint16_t* __rest
                                                           const uint16_t* __restrict__ fk,
                                                           const float* __restrict__ z_tot, LinBwdWs t,
                                                           const uint16_t* dq_add, uint16_t* dq, KGeom g,
-                                                          Placement pl) {
+                                                          Placement pl, int direct) {
   constexpr int DC = D / 16, DT = D / 32;
   __shared__ __attribute__((aligned(16))) uint16_t v0[64 * D];
   __shared__ __attribute__((aligned(16))) uint16_t v1[64 * D];
@@ -263,6 +264,7 @@ __global__ void __launch_bounds__(kThreads, 2) lin_bwd_dq(const uint16_t* __rest
   const long long bh = (long long)b * g.H + h;
   const int q = 32 * wq + n;
   const long long row = bh * g.Np + 64LL * i + q;
+  // idx: the selected cubes, or (direct) the rows of unselected ones, topk long.
   const int32_t* irow = idx + (bh * g.nc + i) * topk;
   const long long hbase = bh * g.Np * D;
   const TileOffsets<D> toff(w, lane);
@@ -282,13 +284,15 @@ __global__ void __launch_bounds__(kThreads, 2) lin_bwd_dq(const uint16_t* __rest
   bf16x8 wfr[DC];
 #pragma unroll
   for (int dc = 0; dc < DC; ++dc) wfr[dc] = *reinterpret_cast<const bf16x8*>(t.w + row * D + 16 * dc + 8 * hf);
-  // Total part: this key half's share of S_tot w (rows d, columns q).
+  // Total part: this key half's share of S_tot w (rows d, columns q); none
+  // in direct mode, where the blocks of U are added instead.
   f32x16 acc[DT];
-  {
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) acc[dt] = f32x16{};
+  if (!direct) {
     const uint16_t* sd = (wk == 0 ? t.sd_hi : t.sd_lo) + bh * D * D;
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
-      acc[dt] = f32x16{};
       const int d = 32 * dt + n;
 #pragma unroll
       for (int dc = 0; dc < DC; ++dc) {
@@ -298,6 +302,7 @@ __global__ void __launch_bounds__(kThreads, 2) lin_bwd_dq(const uint16_t* __rest
     }
   }
   const int prow = pi_row(n);
+  const uint32_t xsign = direct ? 0u : 0x80008000u;
   for (int jb = 0; jb < topk; jb += 2) {
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
@@ -319,7 +324,7 @@ __global__ void __launch_bounds__(kThreads, 2) lin_bwd_dq(const uint16_t* __rest
 #pragma unroll
         for (int r = 0; r < 8; ++r) {
           const bf16x2 pk = __builtin_convertvector((f32x2){x[2 * r], x[2 * r + 1]}, bf16x2);
-          xw[r] = __builtin_bit_cast(uint32_t, pk) ^ 0x80008000u;  // -X (exact in bf16)
+          xw[r] = __builtin_bit_cast(uint32_t, pk) ^ xsign;  // -X (exact in bf16), or +X (direct)
         }
         const bf16x8 xb[2] = {__builtin_bit_cast(bf16x8, make_uint4(xw[0], xw[1], xw[2], xw[3])),
                               __builtin_bit_cast(bf16x8, make_uint4(xw[4], xw[5], xw[6], xw[7]))};
@@ -375,7 +380,8 @@ __global__ void __launch_bounds__(kThreads, 2) lin_bwd_dq(const uint16_t* __rest
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         const int r = 4 * gq + u;
-        const float dphi = (acc[dt][r] + x[(dt * 16 + r) * 64 + lane]) - cq * (zt[d + u] - zs[d + u]);
+        const float zu = direct ? zs[d + u] : zt[d + u] - zs[d + u];  // z over U
+        const float dphi = (acc[dt][r] + x[(dt * 16 + r) * 64 + lane]) - cq * zu;
         o[u] = valid ? dphi * phi_grad(xq[u]) + ad[u] : 0.f;
       }
       *reinterpret_cast<uint2*>(out + d) = make_uint2(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]));
@@ -397,7 +403,7 @@ __global__ void __launch_bounds__(kThreads, 2) lin_bwd_dkv(const uint16_t* __res
                                                            const uint16_t* __restrict__ vc,
                                                            const uint16_t* __restrict__ fk, LinBwdWs t, int topk,
                                                            const uint16_t* add, uint16_t* out, KGeom g,
-                                                           Placement pl) {
+                                                           Placement pl, int direct) {
   constexpr int DC = D / 16, DT = D / 32;
   __shared__ __attribute__((aligned(16))) uint16_t w0[64 * D];
   __shared__ __attribute__((aligned(16))) uint16_t w1[64 * D];
@@ -433,11 +439,12 @@ __global__ void __launch_bounds__(kThreads, 2) lin_bwd_dkv(const uint16_t* __res
     for (int dc = 0; dc < DC; ++dc) kb[dc] = *reinterpret_cast<const bf16x8*>(src + 16 * dc + 8 * hf);
   }
   f32x16 acc[DT];
-  {
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) acc[dt] = f32x16{};
+  if (!direct) {
     const uint16_t* mm = (DV ? (wq == 0 ? t.me_hi : t.me_lo) : (wq == 0 ? t.md_hi : t.md_lo)) + bh * D * D;
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
-      acc[dt] = f32x16{};
       const int rr = 32 * dt + n;
 #pragma unroll
       for (int dc = 0; dc < DC; ++dc) {
@@ -454,6 +461,9 @@ __global__ void __launch_bounds__(kThreads, 2) lin_bwd_dkv(const uint16_t* __res
     }
   }
   const int prow = pi_row(n);
+  // Selected query cubes are subtracted from the totals; in direct mode the
+  // query cubes that left this key cube unselected are added (sign flipped).
+  const uint32_t ysign = direct ? 0x80008000u : 0u;
   // Register r of the 32 x 32 product holds query 32 wq + 16 (r/8) + 8 hf + r%8.
   const int q0 = 32 * wq + 8 * hf;
   for (int mb = 0; mb < cnt; mb += 2) {
@@ -481,13 +491,13 @@ __global__ void __launch_bounds__(kThreads, 2) lin_bwd_dkv(const uint16_t* __res
           for (int r = 0; r < 8; ++r) {
             const int r0 = 2 * r, r1 = 2 * r + 1;
             const f32x2 d2 = {c4[r0 / 4][r0 % 4] - y[r0], c4[r1 / 4][r1 % 4] - y[r1]};
-            yw[r] = __builtin_bit_cast(uint32_t, __builtin_convertvector(d2, bf16x2));
+            yw[r] = __builtin_bit_cast(uint32_t, __builtin_convertvector(d2, bf16x2)) ^ ysign;
           }
         } else {
 #pragma unroll
           for (int r = 0; r < 8; ++r) {
             const bf16x2 pk = __builtin_convertvector((f32x2){y[2 * r], y[2 * r + 1]}, bf16x2);
-            yw[r] = __builtin_bit_cast(uint32_t, pk) ^ 0x80008000u;  // -A (exact in bf16)
+            yw[r] = __builtin_bit_cast(uint32_t, pk) ^ 0x80008000u ^ ysign;  // -A (exact in bf16), or +A
           }
         }
         const bf16x8 yb[2] = {__builtin_bit_cast(bf16x8, make_uint4(yw[0], yw[1], yw[2], yw[3])),
@@ -566,20 +576,28 @@ hipError_t launch_t(const KGeom& g, const uint16_t* qc, const uint16_t* kc, cons
   // w, c, phi(Q) per row.
   e = launch_lin_bwd_rows(g, qc, vt, idx, topk, LinBwdRows{doc, t.w, t.c, t.fq}, ws, s);
   if (e != hipSuccess) return e;
-  // M and m (the S partials are consumed: their buffer takes M's partials).
-  hipLaunchKernelGGL(lin_bwd_state<D>, dim3(ls.group_count, g.H, g.B), dim3(256), 0, s, t.fq, t.w, t.c, ls.s_part,
-                     ls.z_part, g, ls.group_size, ls.group_count);
-  hipLaunchKernelGGL(state_reduce<D>, dim3(D * D / 256, bh), dim3(256), 0, s, ls.s_part, ls.z_part, ls.group_count,
-                     t.md_hi, t.md_lo, t.me_hi, t.me_lo, t.m_tot);
-  e = launch_block_lists_t(g, idx, topk, t.cnt, t.off, t.list, s);
+  // Direct mode (more than half the cubes selected): the sums run over the
+  // unselected cubes (the complement lists the rows pass just built) and
+  // over the query cubes that left each key cube unselected, from zero.
+  const LinDirect dm = lin_direct(g, topk, ws);
+  const int32_t* lists = dm.on ? dm.comp : idx;
+  const int len = dm.on ? dm.len : topk;
+  if (!dm.on) {
+    // M and m (the S partials are consumed: their buffer takes M's partials).
+    hipLaunchKernelGGL(lin_bwd_state<D>, dim3(ls.group_count, g.H, g.B), dim3(256), 0, s, t.fq, t.w, t.c,
+                       ls.s_part, ls.z_part, g, ls.group_size, ls.group_count);
+    hipLaunchKernelGGL(state_reduce<D>, dim3(D * D / 256, bh), dim3(256), 0, s, ls.s_part, ls.z_part,
+                       ls.group_count, t.md_hi, t.md_lo, t.me_hi, t.me_lo, t.m_tot);
+  }
+  e = launch_block_lists_t(g, lists, len, t.cnt, t.off, t.list, s);
   if (e != hipSuccess) return e;
   const Placement pl = make_placement(g);
-  hipLaunchKernelGGL(lin_bwd_dq<D>, dim3(grid_size(g)), dim3(kThreads), 0, s, qc, vc, idx, topk, ls.fk, ls.z_tot, t,
-                     add[0], dq, g, pl);
-  hipLaunchKernelGGL((lin_bwd_dkv<D, false>), dim3(grid_size(g)), dim3(kThreads), 0, s, kc, vc, ls.fk, t, topk,
-                     add[1], dk, g, pl);
-  hipLaunchKernelGGL((lin_bwd_dkv<D, true>), dim3(grid_size(g)), dim3(kThreads), 0, s, kc, vc, ls.fk, t, topk,
-                     add[2], dv, g, pl);
+  hipLaunchKernelGGL(lin_bwd_dq<D>, dim3(grid_size(g)), dim3(kThreads), 0, s, qc, vc, lists, len, ls.fk, ls.z_tot, t,
+                     add[0], dq, g, pl, dm.on);
+  hipLaunchKernelGGL((lin_bwd_dkv<D, false>), dim3(grid_size(g)), dim3(kThreads), 0, s, kc, vc, ls.fk, t, len,
+                     add[1], dk, g, pl, dm.on);
+  hipLaunchKernelGGL((lin_bwd_dkv<D, true>), dim3(grid_size(g)), dim3(kThreads), 0, s, kc, vc, ls.fk, t, len,
+                     add[2], dv, g, pl, dm.on);
   return hipGetLastError();
 }
 

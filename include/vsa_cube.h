@@ -359,7 +359,12 @@ int32_t vsa_sparse_attn_bwd(const vsa_geom* g, const uint16_t* qc, const uint16_
  * qc, kc: TOKEN_MAJOR bf16; vt: DIM_MAJOR bf16; idx as for the fine stage
  * (entries distinct); o_sparse: fp32 [B, heads, Np, D] (the oc_f32 output of
  * vsa_sparse_attn_fwd); oc: output bf16 TOKEN_MAJOR.  o_sparse and oc may not
- * overlap.  ws: at least vsa_linear_workspace_bytes(g) bytes. */
+ * overlap.  ws: at least vsa_linear_workspace_bytes(g) bytes.
+ * The sum over U is taken as the total minus the selected blocks while
+ * topk <= n_cubes / 2, and directly over U (a complement list built in ws)
+ * when more cubes are selected, so that the difference of two nearly equal
+ * sums never magnifies the rounding (n_cubes <= VSA_MAX_CUBES; larger grids
+ * keep the first form). */
 int32_t vsa_linear_branch(const vsa_geom* g, const uint16_t* qc, const uint16_t* kc,
                           const uint16_t* vt, const int32_t* idx, int32_t topk,
                           const float* o_sparse, uint16_t* oc, void* ws,
@@ -377,7 +382,9 @@ int32_t vsa_linear_branch(const vsa_geom* g, const uint16_t* qc, const uint16_t*
  * (overwritten: phi(K), the total state).  Three launches on `stream`.
  * The fp32 sums are those of the two-call chain, in the same order; outputs
  * can differ from it in the last bf16 bits where multiply-add contraction in
- * the final combine differs. */
+ * the final combine differs.  The linear part is the total minus the selected
+ * blocks, so topk must be at most n_cubes / 2 or equal to n_cubes (else
+ * VSA_ERR_TOPK; vsa_linear_branch covers the rest). */
 int32_t vsa_sparse_attn_linear_fwd(const vsa_geom* g, const uint16_t* qc, const uint16_t* kc,
                                    const uint16_t* vt, const int32_t* idx, int32_t topk,
                                    float softmax_scale, uint16_t* oc, float* lse, void* ws,

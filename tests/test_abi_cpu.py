@@ -245,6 +245,7 @@ def test_fused_linear_entry_point_validation(lib):
     assert f(g, P, P, P, P, 2, 0.125, P, ODD, P, ws, None) == _lib.VSA_ERR_ALIGN
     assert f(g, P, P, P, P, 0, 0.125, P, None, P, ws, None) == _lib.VSA_ERR_TOPK
     assert f(g, P, P, P, P, 9, 0.125, P, None, P, ws, None) == _lib.VSA_ERR_TOPK
+    assert f(g, P, P, P, P, 5, 0.125, P, None, P, ws, None) == _lib.VSA_ERR_TOPK  # more than half, not all
     assert f(g, P, P, P, P, 2, float("nan"), P, None, P, ws, None) == _lib.VSA_ERR_SCALE
     assert f(g, P, P, P, P, 2, 0.125, P, None, P, ws - 1, None) == _lib.VSA_ERR_WORKSPACE
     assert f(geom(D=32), P, P, P, P, 2, 0.125, P, None, P, ws, None) == _lib.VSA_ERR_HEAD_DIM
@@ -317,3 +318,15 @@ def test_packed_entry_point_validation(lib):
     assert lib.vsa_cube_permute(part, P, P, 5, None) == _lib.VSA_ERR_LAYOUT
     assert lib.vsa_cube_permute_pool_compact(part, P, None, P, None) == _lib.VSA_ERR_NULL
     assert lib.vsa_cube_permute_pool_compact(part, P, P, ODD, None) == _lib.VSA_ERR_ALIGN
+
+
+def test_geom_dims_reject_axes_that_overflow(lib):
+    # Axes near INT32_MAX: the cube counts are checked before any narrowing
+    # or product can overflow.
+    from block_sparse_video_cube_amd import _lib
+
+    d = _lib.VsaDims()
+    for grid in [(2**31 - 1, 2**31 - 1, 1), (2**31 - 1, 1, 1), (1, 2**26 + 1, 1), (2**13, 2**13, 2**13)]:
+        assert lib.vsa_geom_dims(geom(grid=grid), ctypes.byref(d)) == _lib.VSA_ERR_GEOMETRY, grid
+    assert lib.vsa_geom_dims(geom(B=1, H=1, grid=(2**26, 1, 1)), ctypes.byref(d)) == 0
+    assert d.n_cubes == 2**24 and d.pad_t == 2**26

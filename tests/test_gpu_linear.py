@@ -64,6 +64,37 @@ CASES = [
 ]
 
 
+# More than half the cubes selected: the branch sums the unselected cubes
+# directly (the total minus the selected part would magnify rounding).
+DIRECT_CASES = [
+    {"grid": (1, 9, 11), "topk": 8, "heads": 4, "head_dim": 64},   # one unselected cube of 16 or fewer keys
+    {"grid": (5, 6, 7), "topk": 6, "heads": 2},
+    {"grid": (16, 12, 16), "topk": 40, "heads": 2, "batch": 2},
+    {"grid": (16, 12, 16), "topk": 47, "heads": 1, "head_dim": 64},
+]
+
+
+@pytest.mark.parametrize("over", DIRECT_CASES)
+def test_hybrid_direct_sum_matches_oracle(over):
+    import block_sparse_video_cube_amd as vsa
+
+    wl = workloads.workload("hybrid").with_(**over)
+    inp = workloads.make_inputs(wl)
+    valid = oracle.valid_rows(wl.grid)
+    qc_o, kc_o, vc_o = (oracle.cube_permute(inp[n], wl.grid) for n in ("q", "k", "v"))
+    idx = oracle.select_topk(qc_o, kc_o, valid, wl.topk)
+    ref = oracle.sparse_attention(qc_o, kc_o, vc_o, valid, idx, wl.softmax_scale)[0]
+    ref = ref + oracle.linear_branch(qc_o, kc_o, vc_o, valid, idx)
+    qc, kc = vsa.cube_permute(to_dev(inp["q"]), wl.grid), vsa.cube_permute(to_dev(inp["k"]), wl.grid)
+    vt = vsa.cube_permute(to_dev(inp["v"]), wl.grid, layout="dim")
+    idx_d = torch.from_numpy(idx).to("cuda:0")
+    _, of, _ = vsa.sparse_attn_fwd(qc, kc, vt, idx_d, wl.grid, wl.softmax_scale, want_f32=True)
+    got = bf16_f64(vsa.linear_branch(qc, kc, vt, idx_d, of, wl.grid))
+    assert_close(got[:, :, valid], ref[:, :, valid], f"hybrid direct {over}")
+    with pytest.raises(vsa.VsaError):  # the fused pass takes at most half the cubes
+        vsa.sparse_attn_linear_fwd(qc, kc, vt, idx_d, wl.grid, wl.softmax_scale)
+
+
 @pytest.mark.parametrize("over", CASES)
 def test_hybrid_matches_oracle(over):
     wl = workloads.workload("hybrid").with_(**over)

@@ -57,6 +57,11 @@ CASES = [
     {"grid": (5, 6, 7), "topk": 3, "heads": 2, "head_dim": 64},
     {"grid": (16, 12, 16), "topk": 1, "heads": 1},          # 48 cubes, 47 unselected
     {"grid": (16, 12, 16), "topk": 10, "heads": 2, "batch": 2},
+    # More than half the cubes selected: direct sums over the unselected cubes
+    # (and, for dK and dV, over the query cubes that left a key cube out).
+    {"grid": (1, 9, 11), "topk": 8, "heads": 2, "head_dim": 64},   # one unselected cube per row
+    {"grid": (5, 6, 7), "topk": 6, "heads": 2},
+    {"grid": (16, 12, 16), "topk": 40, "heads": 1, "batch": 2},
 ]
 
 
