@@ -10,6 +10,7 @@ ordinary float code).
 from __future__ import annotations
 
 import concurrent.futures
+import ctypes
 import os
 import shutil
 import subprocess
@@ -65,6 +66,12 @@ def build(verbose: bool = False, jobs: int = 8) -> str:
     if rc != 0:
         print(out, file=sys.stderr)
         raise RuntimeError("hipcc link failed")
+    # The library must load: an unresolved symbol (for example a kernel whose
+    # host stub was not emitted) would otherwise only show at first use.
+    try:
+        ctypes.CDLL(tmp)
+    except OSError as e:
+        raise RuntimeError(f"the linked library does not load: {e}") from e
     shutil.move(tmp, OUT)
     return OUT
 
