@@ -149,6 +149,13 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd(const uint16_t* __restri
     else return make_rsrc(vbase + 64LL * blk(m) * D, 64 * D * 2);
   };
   const int vl_off = SLOTS ? w * 16 * D : w * NI * 8 * 64;
+  {
+    // V(-1) = 0.  Written before any tile load is in flight: the compiler
+    // orders LDS stores after every outstanding direct-to-LDS load.
+    uint4* z = reinterpret_cast<uint4*>(sm.v[1]);
+#pragma unroll
+    for (int e = tid; e < D * 64 * 2 / 16; e += kThreads) z[e] = make_uint4(0, 0, 0, 0);
+  }
   issue_k_tile<D>(k_rsrc(0), sm.k[0], w, kto);
   // Query row q of cube i: its raster token (RASTER) and whether it is real.
   bool qvalid = true;
@@ -169,11 +176,6 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd(const uint16_t* __restri
   }
   issue_k_tile<D>(k_rsrc(1), sm.k[1], w, kto);
   issue_k_tile<D>(k_rsrc(2), sm.k[2], w, kto);
-  {
-    uint4* z = reinterpret_cast<uint4*>(sm.v[1]);
-#pragma unroll
-    for (int e = tid; e < D * 64 * 2 / 16; e += kThreads) z[e] = make_uint4(0, 0, 0, 0);
-  }
   f32x16 o[DT];
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) o[dt] = f32x16{};

@@ -286,15 +286,18 @@ struct LinSmem {
 // backward: w = dO / den (bf16), c = (dO . O_lin) / den (fp32) and phi(Q)
 // (bf16), zero on padded query rows and when no cube is left unselected.
 //
-// direct: the list is the row's complement list (ws.comp) and the branch
-// sums it (c and the denominator start at 0, weights not negated).
+// direct: the list is the row's complement list (the workspace's comp) and
+// the branch sums it (c and the denominator start at 0, weights not
+// negated).  list holds len entries per row either way; empty_u: every cube
+// is selected (O_lin = 0).  The read-only inputs come as separate restrict
+// arguments so that the per-step list entries are scalar loads: a vector
+// load there would have to wait for every tile load in flight.
 template <int D, bool BWD>
-__global__ void __launch_bounds__(kThreads, 2) lin_apply(const uint16_t* __restrict__ qc,
-                                                         const uint16_t* __restrict__ vt,
-                                                         const int32_t* __restrict__ idx, int topk,
-                                                         const float* __restrict__ o_sparse,
-                                                         uint16_t* __restrict__ oc, LinWs ws, KGeom g,
-                                                         Placement pl, LinBwdRows br, int direct) {
+__global__ void __launch_bounds__(kThreads, 2) lin_apply(
+    const uint16_t* __restrict__ qc, const uint16_t* __restrict__ vt, const int32_t* __restrict__ list, int len,
+    int empty_u, int direct, const uint16_t* __restrict__ fk, const float* __restrict__ z_tot,
+    const uint16_t* __restrict__ st_hi, const uint16_t* __restrict__ st_lo, const float* __restrict__ o_sparse,
+    uint16_t* __restrict__ oc, KGeom g, Placement pl, LinBwdRows br) {
   constexpr int DC = D / 16, DT = D / 32;
   __shared__ __attribute__((aligned(16))) LinSmem<D> sm;
   int i, h, b;
@@ -306,11 +309,8 @@ __global__ void __launch_bounds__(kThreads, 2) lin_apply(const uint16_t* __restr
   const long long bh = (long long)b * g.H + h;
   const int q = 32 * wq + n;
   const long long row = bh * g.Np + 64LL * i + q;
-  const bool empty_u = topk >= g.nc;  // every cube selected: O_lin = 0
-  // The list the loop streams: the selected cubes, or (direct) the unselected ones.
-  topk = direct ? g.nc - topk : topk;
-  const int32_t* irow = (direct ? ws.comp : idx) + (bh * g.nc + i) * topk;
-  const uint16_t* fkb = ws.fk + bh * g.Np * D;
+  const int32_t* irow = list + (bh * g.nc + i) * len;
+  const uint16_t* fkb = fk + bh * g.Np * D;
   const uint16_t* vb = vt + bh * g.Np * D;
   const TileOffsets<D> toff(w, lane);
   // phiK(0), V(0) and phiK(1); past the end of the list (or with no
@@ -318,31 +318,44 @@ __global__ void __launch_bounds__(kThreads, 2) lin_apply(const uint16_t* __restr
   constexpr unsigned kTile = 64 * D * 2;
   issue_k_tile<D>(make_rsrc(fkb + 64LL * irow[0] * D, empty_u ? 0 : kTile), sm.f[0], w, toff.k);
   issue_v_tile<D>(make_rsrc(vb + 64LL * irow[0] * D, empty_u ? 0 : kTile), sm.v[0], w, toff.v);
-  issue_k_tile<D>(make_rsrc(fkb + 64LL * irow[topk > 1 ? 1 : 0] * D, (empty_u || topk < 2) ? 0 : kTile), sm.f[1], w,
+  issue_k_tile<D>(make_rsrc(fkb + 64LL * irow[len > 1 ? 1 : 0] * D, (empty_u || len < 2) ? 0 : kTile), sm.f[1], w,
                   toff.k);
 
-  // phi(Q) fragments (bf16) and this lane's part of phi(Q) . z_tot.
+  // phi(Q) fragments (bf16) and this lane's part of phi(Q) . z_tot: the Q
+  // row and the z_tot entries are all loaded first, then used.
   bf16x8 fq[DC];
   float den_part = 0.f;
   {
     const uint16_t* qrow = qc + row * D;
-    const float* zt = ws.z_tot + bh * D;
+    const float* zt = z_tot + bh * D + 8 * hf;
+    uint4 raw[DC];
+    float4 zv[DC][2];
 #pragma unroll
     for (int dc = 0; dc < DC; ++dc) {
-      const uint4 raw = *reinterpret_cast<const uint4*>(qrow + 16 * dc + 8 * hf);
-      const uint32_t wv[4] = {raw.x, raw.y, raw.z, raw.w};
+      raw[dc] = *reinterpret_cast<const uint4*>(qrow + 16 * dc + 8 * hf);
+      zv[dc][0] = *reinterpret_cast<const float4*>(zt + 16 * dc);
+      zv[dc][1] = *reinterpret_cast<const float4*>(zt + 16 * dc + 4);
+    }
+#pragma unroll
+    for (int dc = 0; dc < DC; ++dc) {
+      const uint32_t wv[4] = {raw[dc].x, raw[dc].y, raw[dc].z, raw[dc].w};
+      const float zz[8] = {zv[dc][0].x, zv[dc][0].y, zv[dc][0].z, zv[dc][0].w,
+                           zv[dc][1].x, zv[dc][1].y, zv[dc][1].z, zv[dc][1].w};
 #pragma unroll
       for (int e2 = 0; e2 < 4; ++e2) {
         const uint16_t p0 = f32_to_bf16(phi(__uint_as_float(wv[e2] << 16)));
         const uint16_t p1 = f32_to_bf16(phi(__uint_as_float(wv[e2] & 0xFFFF0000u)));
         fq[dc][2 * e2] = __builtin_bit_cast(__bf16, p0);
         fq[dc][2 * e2 + 1] = __builtin_bit_cast(__bf16, p1);
-        const int d = 16 * dc + 8 * hf + 2 * e2;
-        if (!direct) den_part += bf16_to_f32(p0) * zt[d] + bf16_to_f32(p1) * zt[d + 1];
+        den_part += bf16_to_f32(p0) * zz[2 * e2] + bf16_to_f32(p1) * zz[2 * e2 + 1];
       }
-      __builtin_amdgcn_sched_barrier(0);  // one chunk of loads at a time (register budget)
     }
+    if (direct) den_part = 0.f;  // the direct sum starts from zero
+    // Used only after the loop; without this the compiler sinks the sum
+    // there and keeps the z_tot values live across the loop.
+    asm volatile("" ::"v"(den_part));
   }
+  __builtin_amdgcn_sched_barrier(0);  // the S_tot loads below come after (register budget)
 
   // c starts as this key half's share of phi(Q) S_tot (the hi or the lo
   // half), computed while the first tiles arrive; the loop below subtracts
@@ -351,16 +364,7 @@ __global__ void __launch_bounds__(kThreads, 2) lin_apply(const uint16_t* __restr
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) c[dt] = f32x16{};
   if (!direct) {
-    const uint16_t* st = (wk == 0 ? ws.st_hi : ws.st_lo) + bh * D * D;
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
-      const int e = 32 * dt + n;
-#pragma unroll
-      for (int dc = 0; dc < DC; ++dc) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(st + e * D + 16 * dc + 8 * hf);
-        c[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, fq[dc], c[dt], 0, 0, 0);
-      }
-    }
+    mat_rows_mfma<D>((wk == 0 ? st_hi : st_lo) + bh * D * D, n, hf, fq, c);
   }
   // Selected blocks are subtracted (weights negated, exact in bf16); in
   // direct mode the unselected blocks are added.
@@ -372,17 +376,17 @@ __global__ void __launch_bounds__(kThreads, 2) lin_apply(const uint16_t* __restr
   const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
   // phiK runs two blocks ahead (three buffers), V one (two buffers); steps
   // come in groups of six so that every buffer index is compile-time.
-  for (int jb = 0; jb < (empty_u ? 0 : topk); jb += 6) {
+  for (int jb = 0; jb < (empty_u ? 0 : len); jb += 6) {
 #pragma unroll
     for (int u = 0; u < 6; ++u) {
       const int nb = jb + u;
-      if (nb < topk) {
+      if (nb < len) {
         // Outstanding, oldest first: phiK(nb), V(nb), phiK(nb+1).
         wait_vmcnt<TileOffsets<D>::NI>();
         pipeline_barrier();
-        issue_v_tile<D>(make_rsrc(vb + 64LL * irow[nb + 1 < topk ? nb + 1 : nb] * D, nb + 1 < topk ? kTile : 0),
+        issue_v_tile<D>(make_rsrc(vb + 64LL * irow[nb + 1 < len ? nb + 1 : nb] * D, nb + 1 < len ? kTile : 0),
                         sm.v[(u + 1) % 2], w, toff.v);
-        issue_k_tile<D>(make_rsrc(fkb + 64LL * irow[nb + 2 < topk ? nb + 2 : nb] * D, nb + 2 < topk ? kTile : 0),
+        issue_k_tile<D>(make_rsrc(fkb + 64LL * irow[nb + 2 < len ? nb + 2 : nb] * D, nb + 2 < len ? kTile : 0),
                         sm.f[(u + 2) % 3], w, toff.k);
         bf16x8 ka[DC];
         bf16x8 va[DT][2];
@@ -434,12 +438,17 @@ __global__ void __launch_bounds__(kThreads, 2) lin_apply(const uint16_t* __restr
     const uint16_t* dsrc = br.doc + row * D;
     uint16_t* wdst = br.w + row * D;
     float cp = 0.f;
+    uint2 dall[DT][4];  // the dO row, all loaded before use
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int gq = 0; gq < 4; ++gq) dall[dt][gq] = *reinterpret_cast<const uint2*>(dsrc + 32 * dt + 8 * gq + 4 * hf);
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
       for (int gq = 0; gq < 4; ++gq) {
         const int e = 32 * dt + 8 * gq + 4 * hf;
-        const uint2 draw = *reinterpret_cast<const uint2*>(dsrc + e);
+        const uint2 draw = dall[dt][gq];
         const float dov[4] = {__uint_as_float(draw.x << 16), __uint_as_float(draw.x & 0xFFFF0000u),
                               __uint_as_float(draw.y << 16), __uint_as_float(draw.y & 0xFFFF0000u)};
         // c is taken from the same bf16-rounded w that the backward's
@@ -492,6 +501,18 @@ int launch_complement(const KGeom& g, const int32_t* idx, int topk, const LinWs&
   return 1;
 }
 
+// lin_apply over the selected lists, or (direct) over the complement lists.
+template <int D, bool BWD>
+void launch_apply(const KGeom& g, const uint16_t* qc, const uint16_t* vt, const int32_t* idx, int topk,
+                  const float* o_sparse, uint16_t* oc, const LinWs& w, const LinBwdRows& br, int direct,
+                  hipStream_t s) {
+  const int32_t* list = direct ? w.comp : idx;
+  const int len = direct ? g.nc - topk : topk;
+  const int empty_u = topk >= g.nc ? 1 : 0;
+  hipLaunchKernelGGL((lin_apply<D, BWD>), dim3(grid_size(g)), dim3(kThreads), 0, s, qc, vt, list, len, empty_u,
+                     direct, w.fk, w.z_tot, w.st_hi, w.st_lo, o_sparse, oc, g, make_placement(g), br);
+}
+
 }  // namespace
 
 size_t linear_workspace_bytes(const KGeom& g) {
@@ -525,14 +546,9 @@ hipError_t launch_linear(const KGeom& g, const uint16_t* qc, const uint16_t* kc,
   hipError_t e = launch_lin_prep(g, kc, vt, ws, s);
   if (e != hipSuccess) return e;
   const LinWs w = carve(g, ws, nullptr);
-  const LinBwdRows none{};
   const int direct = launch_complement(g, idx, topk, w, s);
-  if (g.D == 64)
-    hipLaunchKernelGGL((lin_apply<64, false>), dim3(grid_size(g)), dim3(kThreads), 0, s, qc, vt, idx, topk,
-                       o_sparse, oc, w, g, make_placement(g), none, direct);
-  else
-    hipLaunchKernelGGL((lin_apply<128, false>), dim3(grid_size(g)), dim3(kThreads), 0, s, qc, vt, idx, topk,
-                       o_sparse, oc, w, g, make_placement(g), none, direct);
+  if (g.D == 64) launch_apply<64, false>(g, qc, vt, idx, topk, o_sparse, oc, w, LinBwdRows{}, direct, s);
+  else launch_apply<128, false>(g, qc, vt, idx, topk, o_sparse, oc, w, LinBwdRows{}, direct, s);
   return hipGetLastError();
 }
 
@@ -540,12 +556,8 @@ hipError_t launch_lin_bwd_rows(const KGeom& g, const uint16_t* qc, const uint16_
                                const LinBwdRows& br, void* ws, hipStream_t s) {
   const LinWs w = carve(g, ws, nullptr);
   const int direct = launch_complement(g, idx, topk, w, s);
-  if (g.D == 64)
-    hipLaunchKernelGGL((lin_apply<64, true>), dim3(grid_size(g)), dim3(kThreads), 0, s, qc, vt, idx, topk, nullptr,
-                       nullptr, w, g, make_placement(g), br, direct);
-  else
-    hipLaunchKernelGGL((lin_apply<128, true>), dim3(grid_size(g)), dim3(kThreads), 0, s, qc, vt, idx, topk,
-                       nullptr, nullptr, w, g, make_placement(g), br, direct);
+  if (g.D == 64) launch_apply<64, true>(g, qc, vt, idx, topk, nullptr, nullptr, w, br, direct, s);
+  else launch_apply<128, true>(g, qc, vt, idx, topk, nullptr, nullptr, w, br, direct, s);
   return hipGetLastError();
 }
 

@@ -276,11 +276,6 @@ __global__ void __launch_bounds__(kThreads, 2) lin_bwd_dq(const uint16_t* __rest
     issue_k_tile<D>(make_rsrc(fk + o, kTile), fs, w, ttoff.k);
   };
   issue(0, v0, f0);
-  if (tid < D) {  // z over the selected cubes
-    float s = 0.f;
-    for (int jb = 0; jb < topk; ++jb) s += t.zc[(bh * g.nc + irow[jb]) * D + tid];
-    zs[tid] = s;
-  }
   bf16x8 wfr[DC];
 #pragma unroll
   for (int dc = 0; dc < DC; ++dc) wfr[dc] = *reinterpret_cast<const bf16x8*>(t.w + row * D + 16 * dc + 8 * hf);
@@ -289,18 +284,7 @@ __global__ void __launch_bounds__(kThreads, 2) lin_bwd_dq(const uint16_t* __rest
   f32x16 acc[DT];
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) acc[dt] = f32x16{};
-  if (!direct) {
-    const uint16_t* sd = (wk == 0 ? t.sd_hi : t.sd_lo) + bh * D * D;
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
-      const int d = 32 * dt + n;
-#pragma unroll
-      for (int dc = 0; dc < DC; ++dc) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(sd + d * D + 16 * dc + 8 * hf);
-        acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, wfr[dc], acc[dt], 0, 0, 0);
-      }
-    }
-  }
+  if (!direct) mat_rows_mfma<D>((wk == 0 ? t.sd_hi : t.sd_lo) + bh * D * D, n, hf, wfr, acc);
   const int prow = pi_row(n);
   const uint32_t xsign = direct ? 0u : 0x80008000u;
   for (int jb = 0; jb < topk; jb += 2) {
@@ -349,6 +333,22 @@ __global__ void __launch_bounds__(kThreads, 2) lin_bwd_dq(const uint16_t* __rest
 #pragma unroll
       for (int r = 0; r < 16; ++r) x[(dt * 16 + r) * 64 + lane] = acc[dt][r];
   }
+  if (tid < D) {
+    // z over the listed cubes, summed in list order; eight loads in flight
+    // at a time (no tile load is left to wait for).
+    const float* zc = t.zc + bh * g.nc * D + tid;
+    float zsum = 0.f;
+    int jb = 0;
+    for (; jb + 8 <= topk; jb += 8) {
+      float zv[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) zv[e] = zc[(long long)irow[jb + e] * D];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) zsum += zv[e];
+    }
+    for (; jb < topk; ++jb) zsum += zc[(long long)irow[jb] * D];
+    zs[tid] = zsum;
+  }
   __syncthreads();
   if (wk == 1) return;
   int ct, cy, cx;
@@ -361,26 +361,35 @@ __global__ void __launch_bounds__(kThreads, 2) lin_bwd_dq(const uint16_t* __rest
   // addend elements before it writes the same elements.
   const uint16_t* arow = dq_add ? dq_add + row * D : nullptr;
   uint16_t* out = dq + row * D;
+  // Every input of the rows first (one round trip), then the arithmetic.
+  uint2 qall[DT][4], aall[DT][4];
+  float4 zall[DT][4];
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
     for (int gq = 0; gq < 4; ++gq) {
       const int d = 32 * dt + 8 * gq + 4 * hf;
-      const uint2 qraw = *reinterpret_cast<const uint2*>(qrow + d);
+      qall[dt][gq] = *reinterpret_cast<const uint2*>(qrow + d);
+      aall[dt][gq] = arow ? *reinterpret_cast<const uint2*>(arow + d) : make_uint2(0u, 0u);
+      zall[dt][gq] = *reinterpret_cast<const float4*>(zt + d);
+    }
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+    for (int gq = 0; gq < 4; ++gq) {
+      const int d = 32 * dt + 8 * gq + 4 * hf;
+      const uint2 qraw = qall[dt][gq];
       const float xq[4] = {__uint_as_float(qraw.x << 16), __uint_as_float(qraw.x & 0xFFFF0000u),
                            __uint_as_float(qraw.y << 16), __uint_as_float(qraw.y & 0xFFFF0000u)};
-      float o[4], ad[4] = {0.f, 0.f, 0.f, 0.f};
-      if (arow) {
-        const uint2 araw = *reinterpret_cast<const uint2*>(arow + d);
-        ad[0] = __uint_as_float(araw.x << 16);
-        ad[1] = __uint_as_float(araw.x & 0xFFFF0000u);
-        ad[2] = __uint_as_float(araw.y << 16);
-        ad[3] = __uint_as_float(araw.y & 0xFFFF0000u);
-      }
+      const uint2 araw = aall[dt][gq];
+      const float ad[4] = {__uint_as_float(araw.x << 16), __uint_as_float(araw.x & 0xFFFF0000u),
+                           __uint_as_float(araw.y << 16), __uint_as_float(araw.y & 0xFFFF0000u)};
+      const float ztv[4] = {zall[dt][gq].x, zall[dt][gq].y, zall[dt][gq].z, zall[dt][gq].w};
+      float o[4];
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         const int r = 4 * gq + u;
-        const float zu = direct ? zs[d + u] : zt[d + u] - zs[d + u];  // z over U
+        const float zu = direct ? zs[d + u] : ztv[u] - zs[d + u];  // z over U
         const float dphi = (acc[dt][r] + x[(dt * 16 + r) * 64 + lane]) - cq * zu;
         o[u] = valid ? dphi * phi_grad(xq[u]) + ad[u] : 0.f;
       }
@@ -402,6 +411,9 @@ template <int D, bool DV>
 __global__ void __launch_bounds__(kThreads, 2) lin_bwd_dkv(const uint16_t* __restrict__ kc,
                                                            const uint16_t* __restrict__ vc,
                                                            const uint16_t* __restrict__ fk, LinBwdWs t, int topk,
+                                                           const int32_t* __restrict__ tcnt,
+                                                           const int32_t* __restrict__ toffs,
+                                                           const int32_t* __restrict__ tlist,
                                                            const uint16_t* add, uint16_t* out, KGeom g,
                                                            Placement pl, int direct) {
   constexpr int DC = D / 16, DT = D / 32;
@@ -421,8 +433,10 @@ __global__ void __launch_bounds__(kThreads, 2) lin_bwd_dkv(const uint16_t* __res
   const long long hbase = bh * g.Np * D, rbase = bh * g.Np;
   const long long krow = rbase + 64LL * j + key;
   const TileOffsets<D, true> toff(w, lane);
-  const int cnt = t.cnt[bh * g.nc + j];
-  const int32_t* list = t.list + bh * (long long)g.nc * topk + t.off[bh * g.nc + j];
+  // The transposed lists (t.cnt, t.off, t.list) come as restrict arguments,
+  // so that their entries are scalar loads.
+  const int cnt = tcnt[bh * g.nc + j];
+  const int32_t* list = tlist + bh * (long long)g.nc * topk + toffs[bh * g.nc + j];
   constexpr unsigned kTile = 64 * D * 2;
   auto issue = [&](int m, uint16_t* ws_, uint16_t* ps_, float* cs_) {
     const int i = list[m];
@@ -443,21 +457,23 @@ __global__ void __launch_bounds__(kThreads, 2) lin_bwd_dkv(const uint16_t* __res
   for (int dt = 0; dt < DT; ++dt) acc[dt] = f32x16{};
   if (!direct) {
     const uint16_t* mm = (DV ? (wq == 0 ? t.me_hi : t.me_lo) : (wq == 0 ? t.md_hi : t.md_lo)) + bh * D * D;
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
-      const int rr = 32 * dt + n;
-#pragma unroll
-      for (int dc = 0; dc < DC; ++dc) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(mm + rr * D + 16 * dc + 8 * hf);
-        acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, kb[dc], acc[dt], 0, 0, 0);
-      }
-    }
+    mat_rows_mfma<D>(mm, n, hf, kb, acc);
     if (!DV && wq == 0) {
-      const float* mt = t.m_tot + bh * D;
+      const float* mt = t.m_tot + bh * D + 4 * hf;
+      float4 m4[DT][4];  // all loaded first
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) acc[dt][r] -= mt[32 * dt + 8 * (r >> 2) + 4 * hf + (r & 3)];
+        for (int r4 = 0; r4 < 4; ++r4) m4[dt][r4] = *reinterpret_cast<const float4*>(mt + 32 * dt + 8 * r4);
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+          acc[dt][4 * r4] -= m4[dt][r4].x;
+          acc[dt][4 * r4 + 1] -= m4[dt][r4].y;
+          acc[dt][4 * r4 + 2] -= m4[dt][r4].z;
+          acc[dt][4 * r4 + 3] -= m4[dt][r4].w;
+        }
     }
   }
   const int prow = pi_row(n);
@@ -533,22 +549,28 @@ __global__ void __launch_bounds__(kThreads, 2) lin_bwd_dkv(const uint16_t* __res
   // addend elements before it writes the same elements.
   const uint16_t* arow = add ? add + krow * D : nullptr;
   uint16_t* orow = out + krow * D;
+  // Every input of the rows first (one round trip), then the arithmetic.
+  uint2 kall[DT][4], aall[DT][4];
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
     for (int gq = 0; gq < 4; ++gq) {
       const int d = 32 * dt + 8 * gq + 4 * hf;
-      float o[4], ad[4] = {0.f, 0.f, 0.f, 0.f};
-      const uint2 kraw = *reinterpret_cast<const uint2*>(krw + d);
+      kall[dt][gq] = DV ? make_uint2(0u, 0u) : *reinterpret_cast<const uint2*>(krw + d);
+      aall[dt][gq] = arow ? *reinterpret_cast<const uint2*>(arow + d) : make_uint2(0u, 0u);
+    }
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+    for (int gq = 0; gq < 4; ++gq) {
+      const int d = 32 * dt + 8 * gq + 4 * hf;
+      float o[4];
+      const uint2 kraw = kall[dt][gq];
       const float xk[4] = {__uint_as_float(kraw.x << 16), __uint_as_float(kraw.x & 0xFFFF0000u),
                            __uint_as_float(kraw.y << 16), __uint_as_float(kraw.y & 0xFFFF0000u)};
-      if (arow) {
-        const uint2 araw = *reinterpret_cast<const uint2*>(arow + d);
-        ad[0] = __uint_as_float(araw.x << 16);
-        ad[1] = __uint_as_float(araw.x & 0xFFFF0000u);
-        ad[2] = __uint_as_float(araw.y << 16);
-        ad[3] = __uint_as_float(araw.y & 0xFFFF0000u);
-      }
+      const uint2 araw = aall[dt][gq];
+      const float ad[4] = {__uint_as_float(araw.x << 16), __uint_as_float(araw.x & 0xFFFF0000u),
+                           __uint_as_float(araw.y << 16), __uint_as_float(araw.y & 0xFFFF0000u)};
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         const int r = 4 * gq + u;
@@ -595,9 +617,9 @@ hipError_t launch_t(const KGeom& g, const uint16_t* qc, const uint16_t* kc, cons
   hipLaunchKernelGGL(lin_bwd_dq<D>, dim3(grid_size(g)), dim3(kThreads), 0, s, qc, vc, lists, len, ls.fk, ls.z_tot, t,
                      add[0], dq, g, pl, dm.on);
   hipLaunchKernelGGL((lin_bwd_dkv<D, false>), dim3(grid_size(g)), dim3(kThreads), 0, s, kc, vc, ls.fk, t, len,
-                     add[1], dk, g, pl, dm.on);
+                     t.cnt, t.off, t.list, add[1], dk, g, pl, dm.on);
   hipLaunchKernelGGL((lin_bwd_dkv<D, true>), dim3(grid_size(g)), dim3(kThreads), 0, s, kc, vc, ls.fk, t, len,
-                     add[2], dv, g, pl, dm.on);
+                     t.cnt, t.off, t.list, add[2], dv, g, pl, dm.on);
   return hipGetLastError();
 }
 

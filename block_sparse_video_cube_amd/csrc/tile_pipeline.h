@@ -137,6 +137,34 @@ __device__ __forceinline__ void issue_v_tile(__amdgpu_buffer_rsrc_t vr, uint16_t
     __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (lds_ptr_t)(vlds + (w * NI + e) * 8 * 64), 16, off[e], 0, 0, 0);
 }
 
+// acc[dt] += (rows 32 dt .. +31 of a row-major D x D bf16 matrix M) . B,
+// on the matrix cores: lane (hf, n) reads row 32 dt + n, elements
+// 16 dc + 8 hf .. +7 as A operands; b holds the B fragments.  Row block
+// dt + 1 is loaded while block dt is multiplied, so the 16 KB per wavefront
+// arrive in two round trips instead of one per load.
+template <int D>
+__device__ __forceinline__ void mat_rows_mfma(const uint16_t* m, int n, int hf, const bf16x8 (&b)[D / 16],
+                                              f32x16 (&acc)[D / 32]) {
+  constexpr int DC = D / 16, DT = D / 32;
+  const uint16_t* src = m + n * D + 8 * hf;
+  bf16x8 a[2][DC];
+#pragma unroll
+  for (int dc = 0; dc < DC; ++dc) a[0][dc] = *reinterpret_cast<const bf16x8*>(src + 16 * dc);
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) {
+    if (dt + 1 < DT) {
+#pragma unroll
+      for (int dc = 0; dc < DC; ++dc)
+        a[(dt + 1) & 1][dc] = *reinterpret_cast<const bf16x8*>(src + 32 * (dt + 1) * D + 16 * dc);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int dc = 0; dc < DC; ++dc)
+      acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[dt & 1][dc], b[dc], acc[dt], 0, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
 // Gathering a token-major tile straight from raster-order rows
 // ([B, S, heads, D]: consecutive tokens of one head are heads * D elements
 // apart).  Local token l of a cube sits (lt * Hg + ly) * W + lx tokens after
