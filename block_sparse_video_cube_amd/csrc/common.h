@@ -89,6 +89,14 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 // Feature map of the linear branch: phi(x) = elu(x) + 1 (alpha = 1).
 __device__ __forceinline__ float phi_elu1(float x) { return x > 0.f ? x + 1.f : __expf(x); }
 
+// phi of the two bf16 values packed in w (low half first), rounded to bf16
+// by one v_cvt_pk_bf16_f32 (round to nearest even, as f32_to_bf16 for the
+// finite values here).
+__device__ __forceinline__ uint32_t phi2_bf16(uint32_t w) {
+  const f32x2 x = {phi_elu1(__uint_as_float(w << 16)), phi_elu1(__uint_as_float(w & 0xFFFF0000u))};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(x, bf16x2));
+}
+
 }  // namespace vsa
 
 // Host launchers (each returns hipSuccess or the launch error).
@@ -166,7 +174,9 @@ hipError_t launch_linear_bwd(const KGeom& g, const uint16_t* qc, const uint16_t*
                              const uint16_t* vt, const int32_t* idx, int topk, const uint16_t* doc,
                              const uint16_t* dq_add, const uint16_t* dk_add, const uint16_t* dv_add, uint16_t* dq,
                              uint16_t* dk, uint16_t* dv, void* ws, hipStream_t s);
-hipError_t launch_lin_prep(const KGeom& g, const uint16_t* kc, const uint16_t* vt, void* ws, hipStream_t s);
+// write_fk = false: the totals only (S_tot, z_tot), no phi(K) rows.
+hipError_t launch_lin_prep(const KGeom& g, const uint16_t* kc, const uint16_t* vt, void* ws, hipStream_t s,
+                           bool write_fk = true);
 hipError_t launch_attn_lin_fwd(const KGeom& g, const uint16_t* qc, const uint16_t* kc, const uint16_t* vt,
                                const int32_t* idx, int topk, float scale, void* ws, uint16_t* oc, float* lse,
                                hipStream_t s);

@@ -47,8 +47,6 @@ __host__ __device__ inline LinGroups lin_groups(const KGeom& g) {
   return LinGroups{size, (g.nc + size - 1) / size};
 }
 
-__device__ __forceinline__ float phi(float x) { return phi_elu1(x); }
-
 struct LinWs {
   uint16_t* fk;     // [B, H, Np, D] bf16 phi(K), token-major
   float* s_part;    // [B, H, G, D, D]
@@ -106,7 +104,8 @@ LinWs carve(const KGeom& g, void* ws, size_t* total) {
 // its share of the next cube's K and V^T rows while the current cube's
 // products run, and one barrier per cube orders the slots.  Wavefront w owns
 // state rows d = 32 mt .. +31 and NT column tiles.
-template <int D>
+// WRITE_FK: also write phi(K) to the workspace (the fused pass makes its own).
+template <int D, bool WRITE_FK>
 __global__ void __launch_bounds__(256, 2) lin_state(const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vt,
                                                     LinWs ws, KGeom g) {
   constexpr int CH = D / 8;              // 16-byte chunks per row
@@ -154,14 +153,13 @@ __global__ void __launch_bounds__(256, 2) lin_state(const uint16_t* __restrict__
       uint32_t outw[4];
 #pragma unroll
       for (int e2 = 0; e2 < 4; ++e2) {
-        const float x0 = __uint_as_float(wv[e2] << 16), x1 = __uint_as_float(wv[e2] & 0xFFFF0000u);
-        const uint16_t p0 = valid ? f32_to_bf16(phi(x0)) : 0, p1 = valid ? f32_to_bf16(phi(x1)) : 0;
-        zacc[2 * e2] += bf16_to_f32(p0);
-        zacc[2 * e2 + 1] += bf16_to_f32(p1);
-        outw[e2] = (uint32_t)p0 | ((uint32_t)p1 << 16);
+        const uint32_t pp = valid ? phi2_bf16(wv[e2]) : 0u;
+        zacc[2 * e2] += __uint_as_float(pp << 16);
+        zacc[2 * e2 + 1] += __uint_as_float(pp & 0xFFFF0000u);
+        outw[e2] = pp;
       }
       const uint4 o = make_uint4(outw[0], outw[1], outw[2], outw[3]);
-      fdst[f] = o;
+      if (WRITE_FK) fdst[f] = o;
       *reinterpret_cast<uint4*>(&fks[slot][row * D + ((ch ^ kt_swz<D>(row)) << 3)]) = o;
       // V^T row e = f / 8 (64 tokens, 8 chunks of 8).
       const int vrow = f >> 3, vch = f & 7;
@@ -343,8 +341,8 @@ __global__ void __launch_bounds__(kThreads, 2) lin_apply(
                            zv[dc][1].x, zv[dc][1].y, zv[dc][1].z, zv[dc][1].w};
 #pragma unroll
       for (int e2 = 0; e2 < 4; ++e2) {
-        const uint16_t p0 = f32_to_bf16(phi(__uint_as_float(wv[e2] << 16)));
-        const uint16_t p1 = f32_to_bf16(phi(__uint_as_float(wv[e2] & 0xFFFF0000u)));
+        const uint32_t pp = phi2_bf16(wv[e2]);
+        const uint16_t p0 = (uint16_t)pp, p1 = (uint16_t)(pp >> 16);
         fq[dc][2 * e2] = __builtin_bit_cast(__bf16, p0);
         fq[dc][2 * e2 + 1] = __builtin_bit_cast(__bf16, p1);
         den_part += bf16_to_f32(p0) * zz[2 * e2] + bf16_to_f32(p1) * zz[2 * e2 + 1];
@@ -526,15 +524,19 @@ LinTensors lin_tensors(const KGeom& g, void* ws) {
   return LinTensors{w.fk, w.st_hi, w.st_lo, w.z_tot};
 }
 
-hipError_t launch_lin_prep(const KGeom& g, const uint16_t* kc, const uint16_t* vt, void* ws, hipStream_t s) {
+hipError_t launch_lin_prep(const KGeom& g, const uint16_t* kc, const uint16_t* vt, void* ws, hipStream_t s,
+                           bool write_fk) {
   const LinWs w = carve(g, ws, nullptr);
   const int G = lin_groups(g).count;
   const unsigned bh = (unsigned)(g.B * g.H);
+  const dim3 grid(G, g.H, g.B);
   if (g.D == 64) {
-    hipLaunchKernelGGL(lin_state<64>, dim3(G, g.H, g.B), dim3(256), 0, s, kc, vt, w, g);
+    if (write_fk) hipLaunchKernelGGL((lin_state<64, true>), grid, dim3(256), 0, s, kc, vt, w, g);
+    else hipLaunchKernelGGL((lin_state<64, false>), grid, dim3(256), 0, s, kc, vt, w, g);
     hipLaunchKernelGGL(lin_reduce<64>, dim3(64 * 64 / 256, bh), dim3(256), 0, s, w, g);
   } else {
-    hipLaunchKernelGGL(lin_state<128>, dim3(G, g.H, g.B), dim3(256), 0, s, kc, vt, w, g);
+    if (write_fk) hipLaunchKernelGGL((lin_state<128, true>), grid, dim3(256), 0, s, kc, vt, w, g);
+    else hipLaunchKernelGGL((lin_state<128, false>), grid, dim3(256), 0, s, kc, vt, w, g);
     hipLaunchKernelGGL(lin_reduce<128>, dim3(128 * 128 / 256, bh), dim3(256), 0, s, w, g);
   }
   return hipGetLastError();
