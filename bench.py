@@ -255,21 +255,26 @@ def time_backward(vsa, wl, q, k, v, o, qc, kc, vt, idx, args, dev):
     flops = 2.5 * wl.fine_flops
     lin = None
     if wl.linear:
-        # The linear branch's own gradients (recomputing its forward state).
+        # The linear branch's own gradients, from the forward's saved O_lin and 1/den
+        # (as the autograd node runs it), and recomputing them.
         vc, doc = layouts()
+        _, of, _ = vsa.sparse_attn_fwd(qc, kc, vt, idx, wl.grid, wl.softmax_scale, want_f32=True)
+        _, saved = vsa.linear_branch(qc, kc, vt, idx, of, wl.grid, save=True)
         wsl = torch.empty(max(16, vsa._lib.load().vsa_linear_bwd_workspace_bytes(
             vsa.make_geom(B, H, D, wl.grid), wl.topk)), dtype=torch.uint8, device=dev)
-        for _ in range(max(1, args.warmup)):
-            vsa.linear_branch_bwd(qc, kc, vc, vt, idx, doc, wl.grid, workspace=wsl)
-        torch.cuda.synchronize()
-        l0, l1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        l0.record()
-        for _ in range(args.steps):
-            lo = vsa.linear_branch_bwd(qc, kc, vc, vt, idx, doc, wl.grid, workspace=wsl)
-        l1.record()
-        torch.cuda.synchronize()
-        lin = {"ms": round(l0.elapsed_time(l1) / args.steps, 4),
-               "finite": all(bool(torch.isfinite(x.float()).all()) for x in lo)}
+        lin = {}
+        for key, sv in (("ms", saved), ("ms_recomputing", None)):
+            for _ in range(max(1, args.warmup)):
+                vsa.linear_branch_bwd(qc, kc, vc, vt, idx, doc, wl.grid, workspace=wsl, saved=sv)
+            torch.cuda.synchronize()
+            l0, l1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            l0.record()
+            for _ in range(args.steps):
+                lo = vsa.linear_branch_bwd(qc, kc, vc, vt, idx, doc, wl.grid, workspace=wsl, saved=sv)
+            l1.record()
+            torch.cuda.synchronize()
+            lin[key] = round(l0.elapsed_time(l1) / args.steps, 4)
+            lin["finite"] = lin.get("finite", True) and all(bool(torch.isfinite(x.float()).all()) for x in lo)
     return {
         "ms_per_layer": round(ms, 4),
         "stage_ms": {"layouts": round(lay, 4), "bwd_kernels": round(kern, 4), "unpermute": round(unp, 4)},

@@ -470,8 +470,12 @@ def sparse_attn_bwd(qc: torch.Tensor, kc: torch.Tensor, vc: torch.Tensor, oc: to
 
 def linear_branch(qc: torch.Tensor, kc: torch.Tensor, vt: torch.Tensor, idx: torch.Tensor,
                   o_sparse: torch.Tensor, grid: Sequence[int], out: Optional[torch.Tensor] = None,
-                  workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """bf16(o_sparse + O_lin), token-major."""
+                  workspace: Optional[torch.Tensor] = None, save: bool = False):
+    """bf16(o_sparse + O_lin), token-major.
+
+    save: also return (o_lin fp32 [B, heads, Np, D], inv_den fp32 [B, heads, Np]) for
+    linear_branch_bwd(saved=...): (out, (o_lin, inv_den)).
+    """
     B, Hh, Np, D = qc.shape
     g = make_geom(B, Hh, D, grid)
     d = geom_dims(g)
@@ -487,20 +491,27 @@ def linear_branch(qc: torch.Tensor, kc: torch.Tensor, vt: torch.Tensor, idx: tor
     nbytes = workspace_bytes(g, linear=True)
     if workspace is None:
         workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=qc.device)
+    o_lin = inv_den = None
+    if save:
+        o_lin = torch.empty((B, Hh, d.rows, D), dtype=torch.float32, device=qc.device)
+        inv_den = torch.empty((B, Hh, d.rows), dtype=torch.float32, device=qc.device)
     _lib.check("vsa_linear_branch", _lib.load().vsa_linear_branch(
         g, qc.data_ptr(), kc.data_ptr(), vt.data_ptr(), idx.data_ptr(), int(topk), o_sparse.data_ptr(),
-        out.data_ptr(), workspace.data_ptr(), workspace.numel() * workspace.element_size(), _stream()))
-    return out
+        out.data_ptr(), o_lin.data_ptr() if save else None, inv_den.data_ptr() if save else None,
+        workspace.data_ptr(), workspace.numel() * workspace.element_size(), _stream()))
+    return (out, (o_lin, inv_den)) if save else out
 
 
 def linear_branch_bwd(qc: torch.Tensor, kc: torch.Tensor, vc: torch.Tensor, vt: torch.Tensor, idx: torch.Tensor,
                       doc: torch.Tensor, grid: Sequence[int], workspace: Optional[torch.Tensor] = None,
-                      add: Optional[Tuple[torch.Tensor, torch.Tensor, torch.Tensor]] = None, out=None):
+                      add: Optional[Tuple[torch.Tensor, torch.Tensor, torch.Tensor]] = None, out=None,
+                      saved: Optional[Tuple[torch.Tensor, torch.Tensor]] = None):
     """Gradients of the linear branch.  Returns (dq, dk, dv), bf16 [B, heads, Np, D] token-major.
 
     qc, kc, vc, doc: Q, K, V and dO token-major; vt: V DIM_MAJOR; idx: the block lists.
     add: optional (dq, dk, dv) added before the one bf16 rounding (the fine stage's, for the
     hybrid layer); out: optional output tensors (may be the addends themselves).
+    saved: optional (o_lin, inv_den) from linear_branch(save=True) on the same inputs.
     """
     B, Hh, Np, D = qc.shape
     g = make_geom(B, Hh, D, grid)
@@ -521,9 +532,14 @@ def linear_branch_bwd(qc: torch.Tensor, kc: torch.Tensor, vc: torch.Tensor, vt: 
     for t, name in ((dq, "dq"), (dk, "dk"), (dv, "dv")):
         _need(t, name, torch.bfloat16, (B, Hh, d.rows, D))
     adds = [t.data_ptr() for t in add] if add is not None else [None, None, None]
+    sv = [None, None]
+    if saved is not None:
+        _need(saved[0], "o_lin", torch.float32, (B, Hh, d.rows, D))
+        _need(saved[1], "inv_den", torch.float32, (B, Hh, d.rows))
+        sv = [saved[0].data_ptr(), saved[1].data_ptr()]
     _lib.check("vsa_linear_branch_bwd", lib.vsa_linear_branch_bwd(
         g, qc.data_ptr(), kc.data_ptr(), vc.data_ptr(), vt.data_ptr(), idx.data_ptr(), topk, doc.data_ptr(),
-        *adds, dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), workspace.data_ptr(),
+        *sv, *adds, dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), workspace.data_ptr(),
         workspace.numel() * workspace.element_size(), _stream()))
     return dq, dk, dv
 
@@ -583,26 +599,28 @@ class _VsaAttention(torch.autograd.Function):
         vt = cube_permute(v, grid, layout="dim")
         if idx is None:
             idx = select_topk_pooled(qbar, kbar, grid, topk)
+        o_lin = inv_den = None
         if linear:
             oc_s, of, lse = sparse_attn_fwd(qc, kc, vt, idx, grid, scale, want_f32=True, want_lse=True)
-            oc = linear_branch(qc, kc, vt, idx, of, grid)
+            oc, (o_lin, inv_den) = linear_branch(qc, kc, vt, idx, of, grid, save=True)
         else:
             oc_s, _, lse = sparse_attn_fwd(qc, kc, vt, idx, grid, scale, want_lse=True)
             oc = oc_s
-        ctx.save_for_backward(qc, kc, vt, v, oc_s, lse, idx)
+        ctx.save_for_backward(qc, kc, vt, v, oc_s, lse, idx, o_lin, inv_den)
         ctx.grid, ctx.scale, ctx.linear = tuple(grid), scale, linear
         ctx.mark_non_differentiable(idx)
         return cube_unpermute(oc, grid), idx
 
     @staticmethod
     def backward(ctx, do, _unused):
-        qc, kc, vt, v, oc_s, lse, idx = ctx.saved_tensors
+        qc, kc, vt, v, oc_s, lse, idx, o_lin, inv_den = ctx.saved_tensors
         grid = ctx.grid
         doc = cube_permute(do.contiguous(), grid)
         vc = cube_permute(v, grid)
         dq, dk, dv = sparse_attn_bwd(qc, kc, vc, oc_s, doc, lse, idx, grid, ctx.scale)
         if ctx.linear:
-            dq, dk, dv = linear_branch_bwd(qc, kc, vc, vt, idx, doc, grid, add=(dq, dk, dv), out=(dq, dk, dv))
+            dq, dk, dv = linear_branch_bwd(qc, kc, vc, vt, idx, doc, grid, add=(dq, dk, dv), out=(dq, dk, dv),
+                                           saved=(o_lin, inv_den))
         return (cube_unpermute(dq, grid), cube_unpermute(dk, grid), cube_unpermute(dv, grid),
                 None, None, None, None, None)
 

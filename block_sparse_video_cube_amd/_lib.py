@@ -123,7 +123,7 @@ def load() -> ctypes.CDLL:
         "vsa_cube_unpermute": (i32, [G, P, P, P]),
         "vsa_select_topk": (i32, [G, P, P, i32, P, P, sz, P]),
         "vsa_sparse_attn_fwd": (i32, [G, P, P, P, P, i32, ctypes.c_float, P, P, P, P]),
-        "vsa_linear_branch": (i32, [G, P, P, P, P, i32, P, P, P, sz, P]),
+        "vsa_linear_branch": (i32, [G, P, P, P, P, i32, P, P, P, P, P, sz, P]),
         "vsa_sta_topk": (i32, [G, i32, i32, i32]),
         "vsa_sta_index": (i32, [G, i32, i32, i32, P, P]),
         "vsa_cube_pool": (i32, [G, P, P, P]),
@@ -136,7 +136,7 @@ def load() -> ctypes.CDLL:
         "vsa_sparse_attn_bwd": (i32, [G, P, P, P, P, P, P, P, i32, ctypes.c_float, P, P, P, P, sz, P]),
         "vsa_mfma_probe": (i32, [i32, i32, P, P, P]),
         "vsa_linear_bwd_workspace_bytes": (sz, [G, i32]),
-        "vsa_linear_branch_bwd": (i32, [G, P, P, P, P, P, i32, P, P, P, P, P, P, P, P, sz, P]),
+        "vsa_linear_branch_bwd": (i32, [G, P, P, P, P, P, i32, P, P, P, P, P, P, P, P, P, P, sz, P]),
         "vsa_cube_permute_pool_compact": (i32, [G, P, P, P, P]),
         "vsa_sparse_attn_packed_workspace_bytes": (sz, [G, i32]),
         "vsa_sparse_attn_fwd_packed": (i32, [G, P, i32, P, P, P, i32, ctypes.c_float, P, P, P, sz, P]),

@@ -124,9 +124,11 @@ size_t attn_packed_workspace_bytes(const KGeom& g, int topk);
 hipError_t launch_attn_fwd_packed(const KGeom& g, const uint16_t* q, bool raster, const uint16_t* kc,
                                   const uint16_t* vs, const int32_t* idx, int topk, float scale, uint16_t* o,
                                   float* lse, void* ws, hipStream_t s);
+// o_lin, inv_den: optional (both or neither) fp32 copies of O_lin [B, H, Np, D]
+// and of 1/den [B, H, Np] for the backward.
 hipError_t launch_linear(const KGeom& g, const uint16_t* qc, const uint16_t* kc, const uint16_t* vt,
-                         const int32_t* idx, int topk, const float* o_sparse, uint16_t* oc, void* ws,
-                         hipStream_t s);
+                         const int32_t* idx, int topk, const float* o_sparse, uint16_t* oc, float* o_lin,
+                         float* inv_den, void* ws, hipStream_t s);
 size_t linear_workspace_bytes(const KGeom& g);
 // The parts of the linear workspace the selected-block correction reads:
 // phi(K) token-major bf16 [B, H, Np, D], S_tot^T as bf16 hi + lo [B, H, D, D],
@@ -146,8 +148,11 @@ struct LinBwdRows {
   float* c;             // (dO . O_lin) / den, fp32 [B, H, Np]
   uint16_t* fq;         // phi(Q), bf16
 };
+// With the forward's saved O_lin and 1/den (both non-null) the rows come from
+// them (lin_rows); otherwise the selected-block pass recomputes them.
 hipError_t launch_lin_bwd_rows(const KGeom& g, const uint16_t* qc, const uint16_t* vt, const int32_t* idx, int topk,
-                               const LinBwdRows& br, void* ws, hipStream_t s);
+                               const float* o_lin, const float* inv_den, const LinBwdRows& br, void* ws,
+                               hipStream_t s);
 // The parts of the linear workspace the backward reuses: phi(K), the group
 // partials of the state (reused for the backward's own state), z_tot.
 struct LinState {
@@ -172,8 +177,9 @@ hipError_t launch_block_lists_t(const KGeom& g, const int32_t* idx, int topk, in
 size_t linear_bwd_workspace_bytes(const KGeom& g, int topk);
 hipError_t launch_linear_bwd(const KGeom& g, const uint16_t* qc, const uint16_t* kc, const uint16_t* vc,
                              const uint16_t* vt, const int32_t* idx, int topk, const uint16_t* doc,
-                             const uint16_t* dq_add, const uint16_t* dk_add, const uint16_t* dv_add, uint16_t* dq,
-                             uint16_t* dk, uint16_t* dv, void* ws, hipStream_t s);
+                             const float* o_lin, const float* inv_den, const uint16_t* dq_add,
+                             const uint16_t* dk_add, const uint16_t* dv_add, uint16_t* dq, uint16_t* dk, uint16_t* dv,
+                             void* ws, hipStream_t s);
 // write_fk = false: the totals only (S_tot, z_tot), no phi(K) rows.
 hipError_t launch_lin_prep(const KGeom& g, const uint16_t* kc, const uint16_t* vt, void* ws, hipStream_t s,
                            bool write_fk = true);

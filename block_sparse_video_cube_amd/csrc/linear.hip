@@ -295,7 +295,8 @@ __global__ void __launch_bounds__(kThreads, 2) lin_apply(
     const uint16_t* __restrict__ qc, const uint16_t* __restrict__ vt, const int32_t* __restrict__ list, int len,
     int empty_u, int direct, const uint16_t* __restrict__ fk, const float* __restrict__ z_tot,
     const uint16_t* __restrict__ st_hi, const uint16_t* __restrict__ st_lo, const float* __restrict__ o_sparse,
-    uint16_t* __restrict__ oc, KGeom g, Placement pl, LinBwdRows br) {
+    uint16_t* __restrict__ oc, float* __restrict__ o_lin_out, float* __restrict__ inv_out, KGeom g, Placement pl,
+    LinBwdRows br) {
   constexpr int DC = D / 16, DT = D / 32;
   __shared__ __attribute__((aligned(16))) LinSmem<D> sm;
   int i, h, b;
@@ -435,7 +436,10 @@ __global__ void __launch_bounds__(kThreads, 2) lin_apply(
     const float inv_b = local_valid(g, ct, cy, cx, q) ? inv : 0.f;
     const uint16_t* dsrc = br.doc + row * D;
     uint16_t* wdst = br.w + row * D;
-    float cp = 0.f;
+    // c = w . O_lin summed per 8-element chunk m = 4 dt + gq (this lane's
+    // four, then the partner half's four), then over the chunks by a
+    // balanced tree: the order lin_rows uses, so both give the same bits.
+    float cm[DT * 4];
     uint2 dall[DT][4];  // the dO row, all loaded before use
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt)
@@ -456,16 +460,23 @@ __global__ void __launch_bounds__(kThreads, 2) lin_apply(
                                        pack_bf16x2(dov[2] * inv_b, dov[3] * inv_b));
         const float wr[4] = {__uint_as_float(wbits.x << 16), __uint_as_float(wbits.x & 0xFFFF0000u),
                              __uint_as_float(wbits.y << 16), __uint_as_float(wbits.y & 0xFFFF0000u)};
+        float part = 0.f;
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
           const int r = 4 * gq + u;
           const float olin = (c[dt][r] + xo[(dt * 16 + r) * 64 + lane]) * inv;
-          cp = fmaf(wr[u], olin, cp);
+          part = fmaf(wr[u], olin, part);
         }
+        cm[4 * dt + gq] = part;
         *reinterpret_cast<uint2*>(wdst + e) = wbits;
       }
-    cp += __shfl_xor(cp, 32);
-    if (hf == 0) br.c[row] = cp;
+#pragma unroll
+    for (int m = 0; m < DT * 4; ++m) cm[m] += __shfl_xor(cm[m], 32);
+#pragma unroll
+    for (int st = 1; st < DT * 4; st *= 2)
+#pragma unroll
+      for (int m = 0; m < DT * 4; m += 2 * st) cm[m] = cm[m] + cm[m + st];
+    if (hf == 0) br.c[row] = cm[0];
 #pragma unroll
     for (int dc = 0; dc < DC; ++dc)
       *reinterpret_cast<bf16x8*>(br.fq + row * D + 16 * dc + 8 * hf) = inv_b != 0.f ? fq[dc] : bf16x8{};
@@ -487,7 +498,58 @@ __global__ void __launch_bounds__(kThreads, 2) lin_apply(
       }
       *reinterpret_cast<uint2*>(odst + e) =
           make_uint2(pack_bf16x2(os.x + v[0], os.y + v[1]), pack_bf16x2(os.z + v[2], os.w + v[3]));
+      if (o_lin_out) *reinterpret_cast<float4*>(o_lin_out + row * D + e) = make_float4(v[0], v[1], v[2], v[3]);
     }
+  if (inv_out && hf == 0) inv_out[row] = inv;
+}
+
+// The per-row inputs of the backward (the BWD outputs of lin_apply) from the
+// forward's saved O_lin and 1/den instead of a second pass over the tiles.
+// D / 8 consecutive lanes per row, lane m holding elements 8 m .. 8 m + 7
+// (contiguous rows per wavefront).  w = bf16(dO / den) and phi(Q) (bf16) are
+// elementwise; c = w . O_lin is summed per chunk (elements 8m .. 8m+3, then
+// 8m+4 .. 8m+7, each a fused multiply-add chain, the two added) and over the
+// chunks by a balanced tree of lane exchanges: lin_apply's order, so the two
+// paths agree bit for bit.  All zero on padded query rows and where U is
+// empty.
+template <int D>
+__global__ void __launch_bounds__(256) lin_rows(const uint16_t* __restrict__ qc, const float* __restrict__ o_lin,
+                                                const float* __restrict__ inv_den, LinBwdRows br, KGeom g,
+                                                long long nrows) {
+  constexpr int LPR = D / 8;  // lanes per row
+  const long long t = (long long)blockIdx.x * 256 + threadIdx.x;
+  const long long row = t / LPR;
+  const int m = (int)(t % LPR);
+  if (row >= nrows) return;  // whole rows leave together (256 is a multiple of LPR)
+  const int q = (int)(row % 64);
+  const int i = (int)((row % g.Np) / 64);
+  int ct, cy, cx;
+  cube_coords(g, i, ct, cy, cx);
+  const float inv_b = local_valid(g, ct, cy, cx, q) ? inv_den[row] : 0.f;
+  const long long e = row * D + 8 * m;
+  const uint4 draw = *reinterpret_cast<const uint4*>(br.doc + e);
+  const float4 o0 = *reinterpret_cast<const float4*>(o_lin + e);
+  const float4 o1 = *reinterpret_cast<const float4*>(o_lin + e + 4);
+  const uint4 qraw = *reinterpret_cast<const uint4*>(qc + e);
+  const uint32_t dw[4] = {draw.x, draw.y, draw.z, draw.w};
+  uint32_t wb[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k)
+    wb[k] = pack_bf16x2(__uint_as_float(dw[k] << 16) * inv_b, __uint_as_float(dw[k] & 0xFFFF0000u) * inv_b);
+  const float ol[8] = {o0.x, o0.y, o0.z, o0.w, o1.x, o1.y, o1.z, o1.w};
+  float p[2] = {0.f, 0.f};
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    p[k >> 1] = fmaf(__uint_as_float(wb[k] << 16), ol[2 * k], p[k >> 1]);
+    p[k >> 1] = fmaf(__uint_as_float(wb[k] & 0xFFFF0000u), ol[2 * k + 1], p[k >> 1]);
+  }
+  float cm = p[0] + p[1];
+#pragma unroll
+  for (int st = 1; st < LPR; st *= 2) cm += __shfl_xor(cm, st);
+  if (m == 0) br.c[row] = cm;
+  *reinterpret_cast<uint4*>(br.w + e) = make_uint4(wb[0], wb[1], wb[2], wb[3]);
+  const uint4 f = make_uint4(phi2_bf16(qraw.x), phi2_bf16(qraw.y), phi2_bf16(qraw.z), phi2_bf16(qraw.w));
+  *reinterpret_cast<uint4*>(br.fq + e) = inv_b != 0.f ? f : make_uint4(0, 0, 0, 0);
 }
 
 // Direct mode (see comp_cap): the complement lists, and the mode flag.
@@ -502,13 +564,14 @@ int launch_complement(const KGeom& g, const int32_t* idx, int topk, const LinWs&
 // lin_apply over the selected lists, or (direct) over the complement lists.
 template <int D, bool BWD>
 void launch_apply(const KGeom& g, const uint16_t* qc, const uint16_t* vt, const int32_t* idx, int topk,
-                  const float* o_sparse, uint16_t* oc, const LinWs& w, const LinBwdRows& br, int direct,
-                  hipStream_t s) {
+                  const float* o_sparse, uint16_t* oc, float* o_lin, float* inv_den, const LinWs& w,
+                  const LinBwdRows& br, int direct, hipStream_t s) {
   const int32_t* list = direct ? w.comp : idx;
   const int len = direct ? g.nc - topk : topk;
   const int empty_u = topk >= g.nc ? 1 : 0;
   hipLaunchKernelGGL((lin_apply<D, BWD>), dim3(grid_size(g)), dim3(kThreads), 0, s, qc, vt, list, len, empty_u,
-                     direct, w.fk, w.z_tot, w.st_hi, w.st_lo, o_sparse, oc, g, make_placement(g), br);
+                     direct, w.fk, w.z_tot, w.st_hi, w.st_lo, o_sparse, oc, o_lin, inv_den, g, make_placement(g),
+                     br);
 }
 
 }  // namespace
@@ -543,23 +606,34 @@ hipError_t launch_lin_prep(const KGeom& g, const uint16_t* kc, const uint16_t* v
 }
 
 hipError_t launch_linear(const KGeom& g, const uint16_t* qc, const uint16_t* kc, const uint16_t* vt,
-                         const int32_t* idx, int topk, const float* o_sparse, uint16_t* oc, void* ws,
-                         hipStream_t s) {
+                         const int32_t* idx, int topk, const float* o_sparse, uint16_t* oc, float* o_lin,
+                         float* inv_den, void* ws, hipStream_t s) {
   hipError_t e = launch_lin_prep(g, kc, vt, ws, s);
   if (e != hipSuccess) return e;
   const LinWs w = carve(g, ws, nullptr);
   const int direct = launch_complement(g, idx, topk, w, s);
-  if (g.D == 64) launch_apply<64, false>(g, qc, vt, idx, topk, o_sparse, oc, w, LinBwdRows{}, direct, s);
-  else launch_apply<128, false>(g, qc, vt, idx, topk, o_sparse, oc, w, LinBwdRows{}, direct, s);
+  if (g.D == 64)
+    launch_apply<64, false>(g, qc, vt, idx, topk, o_sparse, oc, o_lin, inv_den, w, LinBwdRows{}, direct, s);
+  else launch_apply<128, false>(g, qc, vt, idx, topk, o_sparse, oc, o_lin, inv_den, w, LinBwdRows{}, direct, s);
   return hipGetLastError();
 }
 
 hipError_t launch_lin_bwd_rows(const KGeom& g, const uint16_t* qc, const uint16_t* vt, const int32_t* idx, int topk,
-                               const LinBwdRows& br, void* ws, hipStream_t s) {
+                               const float* o_lin, const float* inv_den, const LinBwdRows& br, void* ws,
+                               hipStream_t s) {
   const LinWs w = carve(g, ws, nullptr);
+  // The complement lists are needed by the backward's kernels either way.
   const int direct = launch_complement(g, idx, topk, w, s);
-  if (g.D == 64) launch_apply<64, true>(g, qc, vt, idx, topk, nullptr, nullptr, w, br, direct, s);
-  else launch_apply<128, true>(g, qc, vt, idx, topk, nullptr, nullptr, w, br, direct, s);
+  if (o_lin && inv_den) {
+    const long long nrows = (long long)g.B * g.H * g.Np;
+    const unsigned blocks = (unsigned)((nrows * (g.D / 8) + 255) / 256);
+    if (g.D == 64) hipLaunchKernelGGL(lin_rows<64>, dim3(blocks), dim3(256), 0, s, qc, o_lin, inv_den, br, g, nrows);
+    else hipLaunchKernelGGL(lin_rows<128>, dim3(blocks), dim3(256), 0, s, qc, o_lin, inv_den, br, g, nrows);
+  } else if (g.D == 64) {
+    launch_apply<64, true>(g, qc, vt, idx, topk, nullptr, nullptr, nullptr, nullptr, w, br, direct, s);
+  } else {
+    launch_apply<128, true>(g, qc, vt, idx, topk, nullptr, nullptr, nullptr, nullptr, w, br, direct, s);
+  }
   return hipGetLastError();
 }
 

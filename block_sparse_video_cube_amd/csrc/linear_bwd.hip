@@ -583,8 +583,8 @@ __global__ void __launch_bounds__(kThreads, 2) lin_bwd_dkv(const uint16_t* __res
 
 template <int D>
 hipError_t launch_t(const KGeom& g, const uint16_t* qc, const uint16_t* kc, const uint16_t* vc, const uint16_t* vt,
-                    const int32_t* idx, int topk, const uint16_t* doc, const uint16_t* const* add, uint16_t* dq,
-                    uint16_t* dk, uint16_t* dv, void* ws, hipStream_t s) {
+                    const int32_t* idx, int topk, const uint16_t* doc, const float* o_lin, const float* inv_den,
+                    const uint16_t* const* add, uint16_t* dq, uint16_t* dk, uint16_t* dv, void* ws, hipStream_t s) {
   hipError_t e = launch_lin_prep(g, kc, vt, ws, s);  // phi(K), S_tot (e-major), z_tot; S partials kept
   if (e != hipSuccess) return e;
   const LinState ls = lin_state_parts(g, ws);
@@ -595,8 +595,8 @@ hipError_t launch_t(const KGeom& g, const uint16_t* qc, const uint16_t* kc, cons
   hipLaunchKernelGGL(state_reduce<D>, dim3(D * D / 256, bh), dim3(256), 0, s, ls.s_part, ls.z_part, ls.group_count,
                      t.sd_hi, t.sd_lo, nullptr, nullptr, nullptr);
   hipLaunchKernelGGL(lin_cube_z<D>, dim3((unsigned)((ncubes + 3) / 4)), dim3(256), 0, s, ls.fk, t.zc, ncubes);
-  // w, c, phi(Q) per row.
-  e = launch_lin_bwd_rows(g, qc, vt, idx, topk, LinBwdRows{doc, t.w, t.c, t.fq}, ws, s);
+  // w, c, phi(Q) per row: from the forward's saved O_lin and 1/den, or recomputed.
+  e = launch_lin_bwd_rows(g, qc, vt, idx, topk, o_lin, inv_den, LinBwdRows{doc, t.w, t.c, t.fq}, ws, s);
   if (e != hipSuccess) return e;
   // Direct mode (more than half the cubes selected): the sums run over the
   // unselected cubes (the complement lists the rows pass just built) and
@@ -633,11 +633,12 @@ size_t linear_bwd_workspace_bytes(const KGeom& g, int topk) {
 
 hipError_t launch_linear_bwd(const KGeom& g, const uint16_t* qc, const uint16_t* kc, const uint16_t* vc,
                              const uint16_t* vt, const int32_t* idx, int topk, const uint16_t* doc,
-                             const uint16_t* dq_add, const uint16_t* dk_add, const uint16_t* dv_add, uint16_t* dq,
-                             uint16_t* dk, uint16_t* dv, void* ws, hipStream_t s) {
+                             const float* o_lin, const float* inv_den, const uint16_t* dq_add,
+                             const uint16_t* dk_add, const uint16_t* dv_add, uint16_t* dq, uint16_t* dk, uint16_t* dv,
+                             void* ws, hipStream_t s) {
   const uint16_t* const add[3] = {dq_add, dk_add, dv_add};
-  if (g.D == 64) return launch_t<64>(g, qc, kc, vc, vt, idx, topk, doc, add, dq, dk, dv, ws, s);
-  return launch_t<128>(g, qc, kc, vc, vt, idx, topk, doc, add, dq, dk, dv, ws, s);
+  if (g.D == 64) return launch_t<64>(g, qc, kc, vc, vt, idx, topk, doc, o_lin, inv_den, add, dq, dk, dv, ws, s);
+  return launch_t<128>(g, qc, kc, vc, vt, idx, topk, doc, o_lin, inv_den, add, dq, dk, dv, ws, s);
 }
 
 }  // namespace vsa

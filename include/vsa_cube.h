@@ -49,7 +49,7 @@
 extern "C" {
 #endif
 
-#define VSA_ABI_VERSION 2
+#define VSA_ABI_VERSION 3
 
 typedef enum vsa_status {
   VSA_OK = 0,
@@ -359,7 +359,11 @@ int32_t vsa_sparse_attn_bwd(const vsa_geom* g, const uint16_t* qc, const uint16_
  * qc, kc: TOKEN_MAJOR bf16; vt: DIM_MAJOR bf16; idx as for the fine stage
  * (entries distinct); o_sparse: fp32 [B, heads, Np, D] (the oc_f32 output of
  * vsa_sparse_attn_fwd); oc: output bf16 TOKEN_MAJOR.  o_sparse and oc may not
- * overlap.  ws: at least vsa_linear_workspace_bytes(g) bytes.
+ * overlap.  o_lin, inv_den: optional outputs, both or neither (else
+ * VSA_ERR_NULL): O_lin before the combine, fp32 [B, heads, Np, D], and 1/den
+ * per query row, fp32 [B, heads, Np] (0 where U is empty), for
+ * vsa_linear_branch_bwd to use instead of recomputing the branch.
+ * ws: at least vsa_linear_workspace_bytes(g) bytes.
  * The sum over U is taken as the total minus the selected blocks while
  * topk <= n_cubes / 2, and directly over U (a complement list built in ws)
  * when more cubes are selected, so that the difference of two nearly equal
@@ -367,8 +371,8 @@ int32_t vsa_sparse_attn_bwd(const vsa_geom* g, const uint16_t* qc, const uint16_
  * keep the first form). */
 int32_t vsa_linear_branch(const vsa_geom* g, const uint16_t* qc, const uint16_t* kc,
                           const uint16_t* vt, const int32_t* idx, int32_t topk,
-                          const float* o_sparse, uint16_t* oc, void* ws,
-                          size_t ws_bytes, void* stream);
+                          const float* o_sparse, uint16_t* oc, float* o_lin, float* inv_den,
+                          void* ws, size_t ws_bytes, void* stream);
 
 /* Fine stage and linear branch in one pass:
  * oc = bf16(O_sparse + O_lin), the result of vsa_sparse_attn_fwd followed by
@@ -403,7 +407,11 @@ int32_t vsa_sparse_attn_linear_fwd(const vsa_geom* g, const uint16_t* qc, const 
  * phi'(x) = 1 for x > 0, e^x otherwise.  No gradient when every cube is
  * selected (O_lin is then the constant 0).
  * Inputs: qc, kc, vc, doc TOKEN_MAJOR bf16 (doc: dO, padded rows zero); vt
- * DIM_MAJOR bf16 (V); idx, topk as for vsa_linear_branch.  Outputs: dq, dk,
+ * DIM_MAJOR bf16 (V); idx, topk as for vsa_linear_branch.  o_lin, inv_den:
+ * optional, both or neither: the o_lin and inv_den outputs of the forward
+ * vsa_linear_branch on the same inputs; w and c then come from them in one
+ * pass over the rows instead of a second pass over the selected blocks, with
+ * bit-identical results.  Outputs: dq, dk,
  * dv bf16 TOKEN_MAJOR, padded rows zero.  dq_add, dk_add, dv_add: optional
  * (NULL or bf16 TOKEN_MAJOR) gradients to add before the one bf16 rounding,
  * e.g. those of the fine stage for the hybrid layer; an output may alias its
@@ -413,7 +421,8 @@ int32_t vsa_sparse_attn_linear_fwd(const vsa_geom* g, const uint16_t* qc, const 
 size_t vsa_linear_bwd_workspace_bytes(const vsa_geom* g, int32_t topk);
 int32_t vsa_linear_branch_bwd(const vsa_geom* g, const uint16_t* qc, const uint16_t* kc,
                               const uint16_t* vc, const uint16_t* vt, const int32_t* idx,
-                              int32_t topk, const uint16_t* doc, const uint16_t* dq_add,
+                              int32_t topk, const uint16_t* doc, const float* o_lin,
+                              const float* inv_den, const uint16_t* dq_add,
                               const uint16_t* dk_add, const uint16_t* dv_add, uint16_t* dq,
                               uint16_t* dk, uint16_t* dv, void* ws, size_t ws_bytes, void* stream);
 

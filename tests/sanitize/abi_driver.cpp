@@ -119,7 +119,8 @@ int main() {
          VSA_ERR_WORKSPACE);
   EXPECT(vsa_sparse_attn_fwd_packed(&g, p16, 4, p16, p16, pi, 2, 0.1f, w16, NULL, P, 1 << 20, NULL), VSA_ERR_LAYOUT);
   const size_t lws = vsa_linear_workspace_bytes(&g);
-  EXPECT(vsa_linear_branch(&g, p16, p16, p16, pi, 2, pf, w16, P, lws - 1, NULL), VSA_ERR_WORKSPACE);
+  EXPECT(vsa_linear_branch(&g, p16, p16, p16, pi, 2, pf, w16, NULL, NULL, P, lws - 1, NULL), VSA_ERR_WORKSPACE);
+  EXPECT(vsa_linear_branch(&g, p16, p16, p16, pi, 2, pf, w16, wf, NULL, P, lws, NULL), VSA_ERR_NULL);
   EXPECT(vsa_sparse_attn_linear_fwd(&g, p16, p16, p16, pi, 0, 0.1f, w16, NULL, P, lws, NULL), VSA_ERR_TOPK);
   const size_t bws = vsa_attn_bwd_workspace_bytes(&g, 2);
   EXPECT(vsa_sparse_attn_bwd(&g, p16, p16, p16, p16, p16, pf, pi, 2, 0.1f, w16, w16, w16, P, bws - 1, NULL),
@@ -127,9 +128,12 @@ int main() {
   EXPECT(vsa_sparse_attn_bwd(&g, p16, p16, p16, p16, NULL, pf, pi, 2, 0.1f, w16, w16, w16, P, bws, NULL),
          VSA_ERR_NULL);
   const size_t lbws = vsa_linear_bwd_workspace_bytes(&g, 2);
-  EXPECT(vsa_linear_branch_bwd(&g, p16, p16, p16, p16, pi, 2, p16, (const uint16_t*)Q, NULL, NULL, w16, w16, w16, P,
-                               lbws, NULL),
+  EXPECT(vsa_linear_branch_bwd(&g, p16, p16, p16, p16, pi, 2, p16, NULL, NULL, (const uint16_t*)Q, NULL, NULL, w16,
+                               w16, w16, P, lbws, NULL),
          VSA_ERR_ALIGN);
+  EXPECT(vsa_linear_branch_bwd(&g, p16, p16, p16, p16, pi, 2, p16, pf, NULL, NULL, NULL, NULL, w16, w16, w16, P, lbws,
+                               NULL),
+         VSA_ERR_NULL);
   const size_t qws = vsa_quant_fp8_workspace_bytes(&g);
   EXPECT(vsa_quant_fp8(&g, p16, p16, p16, w8, wf, w8, wf, w8, wf, NULL, NULL, P, qws - 1, NULL), VSA_ERR_WORKSPACE);
   EXPECT(vsa_quant_fp8_noalloc(&wide, p16, p16, p16, w8, wf, w8, wf, w8, wf, NULL, NULL, NULL), VSA_ERR_SCRATCH);

@@ -41,7 +41,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_abi_version_and_status_text(lib):
-    assert lib.vsa_abi_version() == 2
+    assert lib.vsa_abi_version() == 3
     for code in range(12):
         assert lib.vsa_status_string(code)
     assert lib.vsa_status_string(12345) == b"unknown status"
@@ -121,9 +121,13 @@ def test_entry_points_reject_bad_arguments_before_launch(lib):
     assert lib.vsa_sparse_attn_fwd(g, P, P, P, P, 2, 0.125, P, ODD, None, None) == _lib.VSA_ERR_ALIGN
     # Linear branch.
     lws = lib.vsa_linear_workspace_bytes(g)
-    assert lib.vsa_linear_branch(g, P, P, P, P, 2, None, P, P, lws, None) == _lib.VSA_ERR_NULL
-    assert lib.vsa_linear_branch(g, P, P, P, P, 2, P, P, P, lws - 1, None) == _lib.VSA_ERR_WORKSPACE
-    assert lib.vsa_linear_branch(g, P, P, P, P, 99, P, P, P, lws, None) == _lib.VSA_ERR_TOPK
+    assert lib.vsa_linear_branch(g, P, P, P, P, 2, None, P, None, None, P, lws, None) == _lib.VSA_ERR_NULL
+    assert lib.vsa_linear_branch(g, P, P, P, P, 2, P, P, None, None, P, lws - 1, None) == _lib.VSA_ERR_WORKSPACE
+    assert lib.vsa_linear_branch(g, P, P, P, P, 99, P, P, None, None, P, lws, None) == _lib.VSA_ERR_TOPK
+    # The saved O_lin and 1/den come as a pair, 16-byte aligned.
+    assert lib.vsa_linear_branch(g, P, P, P, P, 2, P, P, P, None, P, lws, None) == _lib.VSA_ERR_NULL
+    assert lib.vsa_linear_branch(g, P, P, P, P, 2, P, P, None, P, P, lws, None) == _lib.VSA_ERR_NULL
+    assert lib.vsa_linear_branch(g, P, P, P, P, 2, P, P, ODD, P, P, lws, None) == _lib.VSA_ERR_ALIGN
 
 
 def test_fused_entry_points_reject_bad_arguments(lib):
@@ -273,16 +277,22 @@ def test_linear_backward_entry_point_validation(lib):
     assert lib.vsa_linear_bwd_workspace_bytes(g, 0) == 0
     assert lib.vsa_linear_bwd_workspace_bytes(g, 9) == 0
     ins = [P] * 5  # qc kc vc vt idx
+    saved = [None] * 2  # o_lin, inv_den
     adds = [None] * 3
     outs = [P] * 3
-    assert lib.vsa_linear_branch_bwd(g, *ins, 2, None, *adds, *outs, P, ws, None) == _lib.VSA_ERR_NULL
-    assert lib.vsa_linear_branch_bwd(g, *ins, 2, P, *adds, P, P, None, P, ws, None) == _lib.VSA_ERR_NULL
-    assert lib.vsa_linear_branch_bwd(g, ODD, *ins[1:], 2, P, *adds, *outs, P, ws, None) == _lib.VSA_ERR_ALIGN
-    assert lib.vsa_linear_branch_bwd(g, *ins, 2, P, ODD, None, None, *outs, P, ws, None) == _lib.VSA_ERR_ALIGN
-    assert lib.vsa_linear_branch_bwd(g, *ins, 0, P, *adds, *outs, P, ws, None) == _lib.VSA_ERR_TOPK
-    assert lib.vsa_linear_branch_bwd(g, *ins, 9, P, *adds, *outs, P, ws, None) == _lib.VSA_ERR_TOPK
-    assert lib.vsa_linear_branch_bwd(g, *ins, 2, P, *adds, *outs, P, ws - 1, None) == _lib.VSA_ERR_WORKSPACE
-    assert lib.vsa_linear_branch_bwd(geom(D=48), *ins, 2, P, *adds, *outs, P, ws, None) == _lib.VSA_ERR_HEAD_DIM
+    assert lib.vsa_linear_branch_bwd(g, *ins, 2, None, *saved, *adds, *outs, P, ws, None) == _lib.VSA_ERR_NULL
+    assert lib.vsa_linear_branch_bwd(g, *ins, 2, P, *saved, *adds, P, P, None, P, ws, None) == _lib.VSA_ERR_NULL
+    assert lib.vsa_linear_branch_bwd(g, ODD, *ins[1:], 2, P, *saved, *adds, *outs, P, ws, None) == _lib.VSA_ERR_ALIGN
+    assert lib.vsa_linear_branch_bwd(g, *ins, 2, P, *saved, ODD, None, None, *outs, P, ws, None) == _lib.VSA_ERR_ALIGN
+    assert lib.vsa_linear_branch_bwd(g, *ins, 0, P, *saved, *adds, *outs, P, ws, None) == _lib.VSA_ERR_TOPK
+    assert lib.vsa_linear_branch_bwd(g, *ins, 9, P, *saved, *adds, *outs, P, ws, None) == _lib.VSA_ERR_TOPK
+    assert lib.vsa_linear_branch_bwd(g, *ins, 2, P, *saved, *adds, *outs, P, ws - 1, None) == _lib.VSA_ERR_WORKSPACE
+    assert lib.vsa_linear_branch_bwd(geom(D=48), *ins, 2, P, *saved, *adds, *outs, P, ws, None) == \
+        _lib.VSA_ERR_HEAD_DIM
+    # The saved forward values: a pair, 16-byte aligned.
+    assert lib.vsa_linear_branch_bwd(g, *ins, 2, P, P, None, *adds, *outs, P, ws, None) == _lib.VSA_ERR_NULL
+    assert lib.vsa_linear_branch_bwd(g, *ins, 2, P, None, P, *adds, *outs, P, ws, None) == _lib.VSA_ERR_NULL
+    assert lib.vsa_linear_branch_bwd(g, *ins, 2, P, P, ODD, *adds, *outs, P, ws, None) == _lib.VSA_ERR_ALIGN
 
 
 def test_packed_entry_point_validation(lib):

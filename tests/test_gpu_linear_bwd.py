@@ -1,6 +1,9 @@
 """GPU parity of the linear branch's backward (vsa_linear_branch_bwd) against
 the fp64 oracle (O11, pinned by torch autograd, finite differences and closed
-forms), on the oracle's block lists.
+forms), on the oracle's block lists.  Every case also runs the backward from
+the forward's saved O_lin and 1/den (vsa_linear_branch with its o_lin and
+inv_den outputs), which must give the recomputing pass's gradients bit for
+bit.
 
 Tolerance, against each gradient's own scale: max|d| <= 2^-6 max|ref| and
 mean|d| <= 2^-7 mean|ref|.  Along each path the kernels round to bf16 (2^-9
@@ -44,7 +47,13 @@ def run(wl, seed, idx=None, heads=None):
     vt = vsa.cube_permute(v, wl.grid, layout="dim")
     idx_d = torch.from_numpy(np.ascontiguousarray(idx, dtype=np.int32)).to("cuda:0")
     got = vsa.linear_branch_bwd(qc, kc, vc, vt, idx_d, doc, wl.grid)
+    # The same gradients from the forward's saved O_lin and 1/den.
+    _, of, _ = vsa.sparse_attn_fwd(qc, kc, vt, idx_d, wl.grid, wl.softmax_scale, want_f32=True)
+    _, saved = vsa.linear_branch(qc, kc, vt, idx_d, of, wl.grid, save=True)
+    got_saved = vsa.linear_branch_bwd(qc, kc, vc, vt, idx_d, doc, wl.grid, saved=saved)
     torch.cuda.synchronize()
+    for name, a, b in zip(("dq", "dk", "dv"), got, got_saved):
+        assert torch.equal(a, b), f"{name}: saved-forward path differs from the recomputing one"
     print(f"[linear bwd {wl.grid} D={wl.head_dim} k={wl.topk}] oracle", flush=True)
     ref = oracle.linear_branch_bwd(qc_o, kc_o, vc_o, valid, idx, doc_o, heads=heads)
     return [bf16_f64(x) for x in got], ref, valid
