@@ -8,7 +8,10 @@ vsa.layer_forward, the benchmark's chain.  Checked per example:
     (near-tie band 1e-5 relative);
   - the raster output equals the oracle's (fine stage, plus the linear
     branch) for the lists the GPU chose, within 2e-2 max-abs / 2e-3
-    mean-abs.
+    mean-abs;
+  - with the linear branch and k <= Nc / 2 or k = Nc, the single fused pass
+    (vsa_sparse_attn_linear_fwd) chooses the same lists and meets the same
+    bound.
 Examples are derandomized (the same cases every run), bounded in number, and
 the run stops at the first failure (no shrinking on the GPU).
 """
@@ -59,6 +62,12 @@ def check_layer(grid, D, topk, batch, heads, linear, seed):
         ref = ref + oracle.linear_branch(qc, kc, vc, valid, idx)
     ref_tok = oracle.cube_unpermute(np.nan_to_num(ref), grid)
     assert_close(bf16_f64(o), ref_tok, f"layer {grid} D={D} k={topk} B={batch} heads={heads} linear={linear}")
+    if linear and (2 * topk <= wl.n_cubes or topk == wl.n_cubes):
+        o_f, idx_f = vsa.layer_forward(to_dev(inp["q"]), to_dev(inp["k"]), to_dev(inp["v"]), grid, topk,
+                                       wl.softmax_scale, linear=True, fused_linear=True)
+        torch.cuda.synchronize()
+        assert np.array_equal(idx_f.cpu().numpy(), idx)
+        assert_close(bf16_f64(o_f), ref_tok, f"fused layer {grid} D={D} k={topk} B={batch} heads={heads}")
 
 
 @settings(max_examples=40, deadline=None, derandomize=True, database=None,
