@@ -327,9 +327,11 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd(const uint16_t* __restri
 // its valid keys first).  Cubes of three or four slots get a tile each (in
 // list order), then cubes of two slots go two to a tile, then cubes of one
 // slot four to a tile (each class in list order; the last tile of a class may
-// have empty slots).  Row layout (int32): word 0 the number of tiles, words
-// 1..3 unused, then four slot codes per tile (tile_pipeline.h).  Positions
-// come from ballot prefix counts: no atomics, the plan is deterministic.
+// have empty slots).  Row layout (int32): word 0 the number of tiles, word 1
+// the mean index of the cubes that have a tile of their own (0 if none; a
+// launch-order key), words 2..3 unused, then four slot codes per tile
+// (tile_pipeline.h).  Positions come from ballot prefix counts: no atomics,
+// the plan is deterministic.
 __global__ void __launch_bounds__(256) block_plan(const int32_t* __restrict__ idx, int topk,
                                                   int32_t* __restrict__ plan, KGeom g, long long nrows) {
   const int lane = threadIdx.x & 63;
@@ -354,6 +356,7 @@ __global__ void __launch_bounds__(256) block_plan(const int32_t* __restrict__ id
   const int t2 = (n2 + 1) >> 1, t1 = (n1 + 3) >> 2;
   const int base2 = nb, base1 = nb + t2;
   int cb = 0, c2 = 0, c1 = 0;
+  unsigned own = 0;  // sum of the indices of the cubes with a tile of their own
   for (int base = 0; base < topk; base += 64) {
     const int m = base + lane;
     const int j = m < topk ? irow[m] : 0;
@@ -365,6 +368,7 @@ __global__ void __launch_bounds__(256) block_plan(const int32_t* __restrict__ id
       return cnt ? (j << 8) | (sc << 5) | cnt : 0;
     };
     if (sl >= 3) {
+      own += j;
       const int t = cb + __popcll(mb & below);
       *reinterpret_cast<int4*>(prow + 4 * (t + 1)) = make_int4(code(0), code(1), code(2), code(3));
     } else if (sl == 2) {
@@ -378,8 +382,11 @@ __global__ void __launch_bounds__(256) block_plan(const int32_t* __restrict__ id
     c2 += __popcll(m2);
     c1 += __popcll(m1);
   }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) own += __shfl_xor(own, o);
   if (lane == 0) {
     prow[0] = nb + t2 + t1;
+    prow[1] = nb ? (int)(own / (unsigned)nb) : 0;
     if (n2 & 1) *reinterpret_cast<int2*>(prow + 4 * (base2 + t2) + 2) = make_int2(0, 0);
     for (int r = n1; r < 4 * t1; ++r) prow[4 * (base1 + (r >> 2) + 1) + (r & 3)] = 0;
   }
@@ -390,11 +397,67 @@ __global__ void __launch_bounds__(256) block_plan(const int32_t* __restrict__ id
 // on an XCD (consecutive launch positions) then carry equal work, start and
 // finish together, and sweep their ascending key lists in step, so tiles that
 // several of them selected are fetched into the XCD's L2 once for all.
-// One workgroup per (b, h): a histogram of the tile counts in LDS, bins
-// ordered from the largest count, cubes placed with LDS atomics (the order
-// within a bin is arbitrary; it affects speed only).
-__global__ void __launch_bounds__(256) plan_order(const int32_t* __restrict__ plan, int topk,
-                                                  int32_t* __restrict__ order, int nc) {
+// Within equal tile counts, by the mean index of the cubes with a tile of
+// their own (plan word 1), ascending and descending in turn from one tile
+// count to the next, then by query cube: workgroups that run together then
+// also sweep the key index range in phase, across the change of tile count
+// too.  One workgroup per (b, h): the occupied tile counts in LDS, then a
+// bitonic sort of (count, mean, cube) keys in LDS.  A query cube's result
+// does not depend on the order.
+constexpr int kOrderSortMax = 4096;  // query cubes per head sorted in LDS (32 KB of keys)
+
+__global__ void __launch_bounds__(1024) plan_order(const int32_t* __restrict__ plan, int topk,
+                                                   int32_t* __restrict__ order, int nc, int npow2) {
+  extern __shared__ unsigned long long keys[];  // npow2 keys, then topk + 1 ints
+  int* turn = reinterpret_cast<int*>(keys + npow2);
+  const long long bh = blockIdx.x;
+  const long long stride = 4LL * (topk + 1);
+  const int32_t* rows = plan + bh * nc * stride;
+  for (int t = threadIdx.x; t <= topk; t += 1024) turn[t] = 0;
+  __syncthreads();
+  for (int c = threadIdx.x; c < nc; c += 1024) atomicOr(&turn[rows[c * stride]], 1);
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int run = 0;  // occupied tile counts from the largest down: 1 on every second one
+    for (int t = topk; t >= 0; --t) {
+      const int occupied = turn[t];
+      turn[t] = run & 1;
+      run += occupied;
+    }
+  }
+  __syncthreads();
+  for (int c = threadIdx.x; c < npow2; c += 1024) {
+    unsigned long long key = ~0ull;  // padding sorts last
+    if (c < nc) {
+      const int2 hdr = *reinterpret_cast<const int2*>(rows + c * stride);
+      const unsigned mean = turn[hdr.x] ? (unsigned)(kOrderSortMax - 1 - hdr.y) : (unsigned)hdr.y;
+      key = ((unsigned long long)(topk - hdr.x) << 26) | ((unsigned long long)mean << 13) | (unsigned)c;
+    }
+    keys[c] = key;
+  }
+  __syncthreads();
+  for (int k = 2; k <= npow2; k <<= 1)
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      for (int t = threadIdx.x; t < npow2; t += 1024) {
+        const int p = t ^ j;
+        if (p > t) {
+          const unsigned long long a = keys[t], b = keys[p];
+          if ((a > b) == ((t & k) == 0)) {
+            keys[t] = b;
+            keys[p] = a;
+          }
+        }
+      }
+      __syncthreads();
+    }
+  for (int c = threadIdx.x; c < nc; c += 1024) order[bh * nc + c] = (int)(keys[c] & 0x1FFF);
+}
+
+// The same order by tile count only, for heads of more than kOrderSortMax
+// query cubes: a histogram of the tile counts in LDS, bins from the largest
+// count, cubes placed with LDS atomics (the order within a bin is arbitrary).
+__global__ void __launch_bounds__(256) plan_order_count(const int32_t* __restrict__ plan, int topk,
+                                                        int32_t* __restrict__ order, int nc) {
   extern __shared__ int bins[];  // topk + 1 counters, then the running offsets in place
   const long long bh = blockIdx.x;
   const long long stride = 4LL * (topk + 1);
@@ -470,7 +533,15 @@ hipError_t launch_attn_fwd_packed(const KGeom& g, const uint16_t* q, bool raster
   int32_t* order = plan + nrows * 4LL * (topk + 1);
   if (g.partial) {
     block_plan<<<dim3((unsigned)((nrows + 3) / 4)), dim3(256), 0, s>>>(idx, topk, plan, g, nrows);
-    plan_order<<<dim3((unsigned)(g.B * g.H)), dim3(256), (topk + 1) * sizeof(int), s>>>(plan, topk, order, g.nc);
+    if (g.nc <= kOrderSortMax) {
+      int npow2 = 1;
+      while (npow2 < g.nc) npow2 <<= 1;
+      const size_t lds = npow2 * sizeof(unsigned long long) + (topk + 1) * sizeof(int);
+      plan_order<<<dim3((unsigned)(g.B * g.H)), dim3(1024), lds, s>>>(plan, topk, order, g.nc, npow2);
+    } else {
+      plan_order_count<<<dim3((unsigned)(g.B * g.H)), dim3(256), (topk + 1) * sizeof(int), s>>>(plan, topk, order,
+                                                                                               g.nc);
+    }
   }
 #define VSA_PACKED(DD, PP, RR) \
   launch_fwd<DD, PP, RR, false, true>(g, q, kc, vs, idx, plan, order, topk, scale, o, nullptr, lse, s)

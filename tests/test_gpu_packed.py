@@ -9,8 +9,12 @@
 - The raster and cube-major forms are bit-identical (output and lse); on a
   grid without padding the packed stage is bit-identical to the unpacked one.
 - The packing plan in the workspace holds every selected cube's valid keys
-  exactly once, and the launch order of each head is a permutation of its
-  query cubes with the most tiles first.
+  exactly once, and the launch order of each head sorts its query cubes by
+  tile count (most first), then by the mean index of the cubes with a tile of
+  their own (ascending and descending in turn over the occupied tile counts),
+  then by cube; past 4096 query cubes per head (tile count only) it is a
+  permutation with the most tiles first, and the stage still matches the
+  oracle.
 """
 
 import numpy as np
@@ -146,17 +150,15 @@ def test_packing_plan_covers_every_selected_key_once():
     words = ws.view(torch.int32).cpu().numpy()
     nplan = wl.heads * wl.n_cubes * (topk + 1) * 4
     plan = words[:nplan].reshape(1, wl.heads, wl.n_cubes, topk + 1, 4)
-    # The launch order: per head a permutation of the query cubes, most tiles first.
     order = words[nplan:nplan + wl.heads * wl.n_cubes].reshape(wl.heads, wl.n_cubes)
-    for h in range(wl.heads):
-        assert sorted(order[h].tolist()) == list(range(wl.n_cubes))
-        nt = plan[0, h, order[h], 0, 0]
-        assert np.all(np.diff(nt) <= 0)
     counts = oracle.valid_rows(grid).reshape(-1, 64).sum(axis=1)
     for h in range(wl.heads):
         for i in range(wl.n_cubes):
             row = plan[0, h, i]
             ntiles = int(row[0, 0])
+            # Word 1: the mean index of the list's cubes with three or four slots.
+            own = [int(j) for j in idx[0, h, i] if counts[j] > 32]
+            assert row[0, 1] == (sum(own) // len(own) if own else 0), (h, i)
             slots = [int(c) for c in row[1:1 + ntiles].reshape(-1) if c != 0]
             got = sorted((c >> 8, (c >> 5) & 3, c & 31) for c in slots)
             want = sorted((int(j), sc, min(16, int(counts[j]) - 16 * sc))
@@ -165,3 +167,42 @@ def test_packing_plan_covers_every_selected_key_once():
             slots_of = [(int(counts[j]) + 15) // 16 for j in idx[0, h, i]]
             nb = sum(s >= 3 for s in slots_of)
             assert ntiles == nb + (sum(s == 2 for s in slots_of) + 1) // 2 + (sum(s == 1 for s in slots_of) + 3) // 4
+        # The launch order: tile count (most first), then word 1 ascending on
+        # the largest occupied count, descending on the next, and so on, then cube.
+        nt = plan[0, h, :, 0, 0].astype(int)
+        turn = {t: r % 2 for r, t in enumerate(sorted(set(nt.tolist()), reverse=True))}
+        key = [(-nt[i], -plan[0, h, i, 0, 1] if turn[nt[i]] else plan[0, h, i, 0, 1], i) for i in range(wl.n_cubes)]
+        assert order[h].tolist() == sorted(range(wl.n_cubes), key=lambda i: key[i]), h
+
+
+def test_packed_stage_past_the_sorted_order_limit():
+    """9537 query cubes per head: the launch order falls back to tile counts only."""
+    import block_sparse_video_cube_amd as vsa
+
+    grid, D, topk = (130, 66, 66), 64, 3
+    wl, inp = inputs(grid, D, heads=1, seed=7)
+    assert wl.n_cubes == 9537
+    idx = random_lists(wl, topk, np.random.default_rng(8))
+    idx_d = torch.from_numpy(idx).to("cuda:0")
+    g = vsa.make_geom(1, 1, D, grid)
+    ws = torch.zeros(vsa.packed_workspace_bytes(g, topk), dtype=torch.uint8, device="cuda:0")
+    kc = vsa.cube_permute(to_dev(inp["k"]), grid, layout="compact")
+    vs = vsa.cube_permute(to_dev(inp["v"]), grid, layout="slots")
+    print("[packed, 9537 cubes] fine stage", flush=True)
+    qc_d = vsa.cube_permute(to_dev(inp["q"]), grid)
+    oc, _ = vsa.sparse_attn_fwd_packed(qc_d, kc, vs, idx_d, grid, wl.softmax_scale, workspace=ws, raster=False)
+    words = ws.view(torch.int32).cpu().numpy()
+    nplan = wl.n_cubes * (topk + 1) * 4
+    plan = words[:nplan].reshape(wl.n_cubes, topk + 1, 4)
+    order = words[nplan:nplan + wl.n_cubes]
+    assert sorted(order.tolist()) == list(range(wl.n_cubes))
+    assert np.all(np.diff(plan[order, 0, 0]) <= 0)
+    cubes = [0, 1, 16, 288, 4000, 9520, 9536]
+    valid = oracle.valid_rows(grid)
+    qc, kc_o, vc = (oracle.cube_permute(inp[n], grid) for n in ("q", "k", "v"))
+    ref, _ = oracle.sparse_attention(qc, kc_o, vc, valid, idx, wl.softmax_scale, cubes=[(0, 0, i) for i in cubes])
+    rows = np.zeros(wl.rows, dtype=bool)
+    for i in cubes:
+        rows[64 * i:64 * i + 64] = True
+    rows &= valid
+    assert_close(bf16_f64(oc)[:, :, rows], ref[:, :, rows], "packed stage, 9537 cubes")
