@@ -675,6 +675,9 @@ class LayerBuffers:
         self.of = torch.empty((B, H, d.rows, D), dtype=torch.float32, device=dev) if linear else None
         self.ws_lin = (torch.empty(max(16, workspace_bytes(g, linear=True)), dtype=torch.uint8, device=dev)
                        if linear else None)
+        # Second stream (default priority) for the V permute, which depends on
+        # nothing the coarse stage makes and runs beside it.
+        self.side = torch.cuda.Stream(device=dev)
 
 
 def layer_stages(linear: bool = False, fused_linear: bool = False):
@@ -706,6 +709,13 @@ def layer_forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, grid: Seque
     K, runs the fine stage and the linear branch (two calls, or one fused pass
     with fused_linear) and unpermutes.  mark(i), if given, is called before
     stage 0 and after each stage i - 1 (layer_stages names them).
+
+    Streams: the V permute runs on a second stream (bufs.side) after the Q and
+    K pooling, beside the coarse stage (selection: matrix cores and lane
+    arithmetic; the permute: memory traffic); the caller's stream waits for it
+    before the fine stage, so the layer is ordered on the caller's stream as a
+    whole.  The stage marks are taken on the caller's stream (the select stage
+    ends once the permute has too).
     """
     B, S, H, D = q.shape
     if scale is None:
@@ -731,16 +741,22 @@ def layer_forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, grid: Seque
             cube_permute_pool(k, grid, out=b.kc, mean_out=b.kbar, compact=packed)
     elif not k_raster:
         cube_permute(k, grid, layout="compact" if packed else "token", out=b.kc)
-    if packed and not linear:
-        cube_permute(v, grid, layout="slots", out=b.vs)
-    else:
-        cube_permute(v, grid, layout="dim", out=b.vt)
+    main = torch.cuda.current_stream(q.device)
+    # The side stream starts once the pooling is queued (and so after the
+    # previous layer's reads of the V buffer on the caller's stream).
+    b.side.wait_stream(main)
+    with torch.cuda.stream(b.side):
+        if packed and not linear:
+            cube_permute(v, grid, layout="slots", out=b.vs)
+        else:
+            cube_permute(v, grid, layout="dim", out=b.vt)
     mark(1)
     if window is not None:
         # The sliding-tile list is static; it is rebuilt every layer all the same.
         sta_index(grid, window, B, H, head_dim=D, out=b.idx)
     else:
         select_topk_pooled(b.qbar, b.kbar, grid, topk, out=b.idx, workspace=b.ws_sel)
+    main.wait_stream(b.side)
     mark(2)
     if not linear:
         if packed:
