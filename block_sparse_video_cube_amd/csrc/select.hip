@@ -12,9 +12,10 @@
 //   block_score 32x32 tiles of the fp32 score matrix per (b, h) on the
 //               fp32 matrix cores;
 //   topk_rows   one wavefront per score row: exact k-th largest key by a
-//               32-step bitwise search over order-preserving uint32 keys,
-//               then an index-ordered compaction with ballots (no atomics,
-//               deterministic).
+//               bitwise search over order-preserving uint32 keys (upper 16
+//               bits over all keys, lower 16 over the keys of the threshold's
+//               bucket), then an index-ordered compaction with ballots (no
+//               atomics, deterministic).
 #include "common.h"
 
 namespace vsa {
@@ -86,11 +87,19 @@ __global__ void __launch_bounds__(256) cube_mean(const uint16_t* __restrict__ xc
 // fp32).  One wavefront per 32 x 32 output tile.  The contraction order over
 // d is permuted identically for both operands so that each lane reads four
 // consecutive floats: MFMA u of group t takes d = 8t + 4 h + u on lane half h.
+// Placement: the tiles of all heads, head by head and row by row, are cut
+// into 8 contiguous ranges, one per XCD (workgroup w runs on XCD w mod 8), so
+// each XCD works through whole heads in turn and their means stay in its L2.
 template <int D>
 __global__ void __launch_bounds__(64) block_score(const float* __restrict__ qbar, const float* __restrict__ kbar,
-                                                  float* __restrict__ scores, int nc) {
-  const long long bh = blockIdx.z;
-  const int i0 = blockIdx.y * 32, j0 = blockIdx.x * 32;
+                                                  float* __restrict__ scores, int nc, int tiles, long long per_xcd,
+                                                  long long units) {
+  const long long u = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
+  if (u >= units) return;
+  const int per_head = tiles * tiles;
+  const long long bh = u / per_head;
+  const int t = (int)(u - bh * per_head);
+  const int i0 = (t / tiles) * 32, j0 = (t % tiles) * 32;
   const int lane = threadIdx.x, h = lane >> 5, m = lane & 31;
   const float* qrow = qbar + (bh * nc + min(i0 + m, nc - 1)) * D;
   const float* krow = kbar + (bh * nc + min(j0 + m, nc - 1)) * D;
@@ -133,13 +142,23 @@ __device__ __forceinline__ uint32_t order_key(float f) {
 
 __device__ __forceinline__ int ballot_count(bool p) { return __popcll(__ballot(p)); }
 
-// One wavefront per score row; MAXV keys per lane (nc <= 64 * MAXV).
+// One wavefront per score row; MAXV keys per lane (nc <= 64 * MAXV).  The
+// k-th largest key is found bit by bit from the top: the largest threshold t
+// with count(key >= t) >= k.  The upper 16 bits are searched over all keys.
+// The k-th key then lies in the bucket of keys that share those 16 bits; the
+// keys above the bucket number fewer than k.  When the bucket holds at most
+// 64 keys (the usual case: about k / 2^16 of the row's spread), they are
+// compacted to one per lane through LDS and the lower 16 bits are searched
+// over them alone (one ballot per step instead of MAXV); otherwise (many equal
+// or nearly equal scores) over all keys as before.  Either way the threshold
+// is the same exact k-th largest key.
 template <int MAXV>
 __global__ void __launch_bounds__(256) topk_rows(const float* __restrict__ scores, int32_t* __restrict__ idx,
                                                  long long nrows, int nc, int k) {
-  const int lane = threadIdx.x & 63;
-  const long long row = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (row >= nrows) return;  // whole wavefront leaves together
+  __shared__ uint32_t bucket[4][64];  // per wavefront
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const long long row = (long long)blockIdx.x * 4 + wv;
+  if (row >= nrows) return;  // whole wavefront leaves together (no workgroup barrier below)
   const float* sr = scores + row * nc;
   uint32_t key[MAXV];
 #pragma unroll
@@ -147,28 +166,62 @@ __global__ void __launch_bounds__(256) topk_rows(const float* __restrict__ score
     const int j = v * 64 + lane;
     key[v] = (j < nc) ? order_key(sr[j]) : 0u;
   }
-  // Largest threshold t with count(key >= t) >= k: the k-th largest key.
+  const auto in = [&](int v) { return v * 64 + lane < nc; };
   uint32_t thr = 0;
-  for (int bit = 31; bit >= 0; --bit) {
+  for (int bit = 31; bit >= 16; --bit) {
     const uint32_t cand = thr | (1u << bit);
     int cnt = 0;
 #pragma unroll
-    for (int v = 0; v < MAXV; ++v) cnt += ballot_count(v * 64 + lane < nc && key[v] >= cand);
+    for (int v = 0; v < MAXV; ++v) cnt += ballot_count(in(v) && key[v] >= cand);
     if (cnt >= k) thr = cand;
   }
-  int gt = 0;
-#pragma unroll
-  for (int v = 0; v < MAXV; ++v) gt += ballot_count(v * 64 + lane < nc && key[v] > thr);
-  const int need_eq = k - gt;  // >= 1
+  const uint32_t hi = thr >> 16;
   const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  int above = 0, nb = 0;
+#pragma unroll
+  for (int v = 0; v < MAXV; ++v) {
+    above += ballot_count(in(v) && (key[v] >> 16) > hi);
+    const bool inb = in(v) && (key[v] >> 16) == hi;
+    const uint64_t m = __ballot(inb);
+    const int pos = nb + __popcll(m & lt_mask);
+    if (inb && pos < 64) bucket[wv][pos] = key[v];
+    nb += __popcll(m);
+  }
+  int gt;
+  if (nb <= 64) {
+    // The wavefront's own LDS writes above, read back by other lanes: LDS
+    // operations of one wavefront complete in order; the fences keep the
+    // compiler from moving the reads above the writes.
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    const bool has = lane < nb;
+    const uint32_t c = has ? bucket[wv][lane] : 0u;
+    for (int bit = 15; bit >= 0; --bit) {
+      const uint32_t cand = thr | (1u << bit);
+      if (above + ballot_count(has && c >= cand) >= k) thr = cand;
+    }
+    gt = above + ballot_count(has && c > thr);
+  } else {
+    for (int bit = 15; bit >= 0; --bit) {
+      const uint32_t cand = thr | (1u << bit);
+      int cnt = 0;
+#pragma unroll
+      for (int v = 0; v < MAXV; ++v) cnt += ballot_count(in(v) && key[v] >= cand);
+      if (cnt >= k) thr = cand;
+    }
+    gt = 0;
+#pragma unroll
+    for (int v = 0; v < MAXV; ++v) gt += ballot_count(in(v) && key[v] > thr);
+  }
+  const int need_eq = k - gt;  // >= 1
   int base = 0, eq_seen = 0;
   int32_t* out = idx + row * k;
 #pragma unroll
   for (int v = 0; v < MAXV; ++v) {
     const int j = v * 64 + lane;
-    const bool in = j < nc;
-    const bool is_gt = in && key[v] > thr;
-    const bool is_eq = in && key[v] == thr;
+    const bool is_gt = in(v) && key[v] > thr;
+    const bool is_eq = in(v) && key[v] == thr;
     const uint64_t eqm = __ballot(is_eq);
     const int eq_rank = eq_seen + __popcll(eqm & lt_mask);
     const bool sel = is_gt || (is_eq && eq_rank < need_eq);
@@ -223,15 +276,17 @@ hipError_t launch_select_pooled(const KGeom& g, const float* qbar, const float* 
                                 float* scores, hipStream_t s) {
   const size_t bh = (size_t)g.B * g.H;
   const int tiles = (g.nc + 31) / 32;
+  const long long units = (long long)bh * tiles * tiles, per_xcd = (units + 7) / 8;
+  const dim3 grid((unsigned)(8 * per_xcd));
   if (g.D == 64)
-    hipLaunchKernelGGL(block_score<64>, dim3(tiles, tiles, (unsigned)bh), dim3(64), 0, s, qbar, kbar, scores, g.nc);
+    hipLaunchKernelGGL(block_score<64>, grid, dim3(64), 0, s, qbar, kbar, scores, g.nc, tiles, per_xcd, units);
   else
-    hipLaunchKernelGGL(block_score<128>, dim3(tiles, tiles, (unsigned)bh), dim3(64), 0, s, qbar, kbar, scores, g.nc);
+    hipLaunchKernelGGL(block_score<128>, grid, dim3(64), 0, s, qbar, kbar, scores, g.nc, tiles, per_xcd, units);
   const long long nrows = (long long)bh * g.nc;
   const int per_lane = (g.nc + 63) / 64;
   // Every keys-per-lane count up to 8 has its own instantiation, larger ones
-  // come in steps of a quarter to a half (the 32-step search costs one ballot
-  // per key slot).
+  // come in steps of a quarter to a half (each step of the search over all
+  // keys costs one ballot per key slot).
   if (per_lane <= 1)
     launch_topk<1>(scores, idx, nrows, g.nc, topk, s);
   else if (per_lane <= 2)
