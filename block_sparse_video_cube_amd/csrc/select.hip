@@ -84,50 +84,67 @@ __global__ void __launch_bounds__(256) cube_mean(const uint16_t* __restrict__ xc
 
 // scores[bh, i, j] = sum_d qbar[bh, i, d] * kbar[bh, j, d] in fp32 on the
 // matrix cores (v_mfma_f32_32x32x2_f32: fp32 products are exact, sums are
-// fp32).  One wavefront per 32 x 32 output tile.  The contraction order over
-// d is permuted identically for both operands so that each lane reads four
-// consecutive floats: MFMA u of group t takes d = 8t + 4 h + u on lane half h.
+// fp32).  One wavefront per 32 x 64 output tile: two 32 x 32 accumulators
+// share the Q operand, and their products alternate, so neither waits for
+// its own previous product.  The contraction order over d is permuted
+// identically for both operands so that each lane reads four consecutive
+// floats: MFMA u of group t takes d = 8t + 4 h + u on lane half h (every
+// output element sums its products in the same order as with one
+// accumulator).  Operands are loaded a half of D at a time.
 // Placement: the tiles of all heads, head by head and row by row, are cut
 // into 8 contiguous ranges, one per XCD (workgroup w runs on XCD w mod 8), so
 // each XCD works through whole heads in turn and their means stay in its L2.
 template <int D>
 __global__ void __launch_bounds__(64) block_score(const float* __restrict__ qbar, const float* __restrict__ kbar,
-                                                  float* __restrict__ scores, int nc, int tiles, long long per_xcd,
-                                                  long long units) {
+                                                  float* __restrict__ scores, int nc, int ti, int tj,
+                                                  long long per_xcd, long long units) {
   const long long u = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
   if (u >= units) return;
-  const int per_head = tiles * tiles;
+  const int per_head = ti * tj;
   const long long bh = u / per_head;
   const int t = (int)(u - bh * per_head);
-  const int i0 = (t / tiles) * 32, j0 = (t % tiles) * 32;
+  const int i0 = (t / tj) * 32, j0 = (t % tj) * 64;
   const int lane = threadIdx.x, h = lane >> 5, m = lane & 31;
   const float* qrow = qbar + (bh * nc + min(i0 + m, nc - 1)) * D;
-  const float* krow = kbar + (bh * nc + min(j0 + m, nc - 1)) * D;
-  const bool qin = i0 + m < nc, kin = j0 + m < nc;
-  f32x16 acc = f32x16{};
-  // All operand loads are issued before the first product (fully unrolled).
-  float4 av[D / 8], bv[D / 8];
+  const float* krow0 = kbar + (bh * nc + min(j0 + m, nc - 1)) * D;
+  const float* krow1 = kbar + (bh * nc + min(j0 + 32 + m, nc - 1)) * D;
+  const bool qin = i0 + m < nc, kin0 = j0 + m < nc, kin1 = j0 + 32 + m < nc;
+  f32x16 acc0 = f32x16{}, acc1 = f32x16{};
+  constexpr int TH = D / 16;  // groups of 8 d per half
 #pragma unroll
-  for (int t = 0; t < D / 8; ++t) {
-    av[t] = *reinterpret_cast<const float4*>(qrow + 8 * t + 4 * h);
-    bv[t] = *reinterpret_cast<const float4*>(krow + 8 * t + 4 * h);
+  for (int half = 0; half < 2; ++half) {
+    float4 av[TH], bv0[TH], bv1[TH];
+#pragma unroll
+    for (int tt = 0; tt < TH; ++tt) {
+      const int d = 8 * (half * TH + tt) + 4 * h;
+      av[tt] = *reinterpret_cast<const float4*>(qrow + d);
+      bv0[tt] = *reinterpret_cast<const float4*>(krow0 + d);
+      bv1[tt] = *reinterpret_cast<const float4*>(krow1 + d);
+    }
+#pragma unroll
+    for (int tt = 0; tt < TH; ++tt) {
+      const float4 z = make_float4(0.f, 0.f, 0.f, 0.f);
+      const float4 a = qin ? av[tt] : z;
+      const float4 b0 = kin0 ? bv0[tt] : z;
+      const float4 b1 = kin1 ? bv1[tt] : z;
+      acc0 = __builtin_amdgcn_mfma_f32_32x32x2f32(a.x, b0.x, acc0, 0, 0, 0);
+      acc1 = __builtin_amdgcn_mfma_f32_32x32x2f32(a.x, b1.x, acc1, 0, 0, 0);
+      acc0 = __builtin_amdgcn_mfma_f32_32x32x2f32(a.y, b0.y, acc0, 0, 0, 0);
+      acc1 = __builtin_amdgcn_mfma_f32_32x32x2f32(a.y, b1.y, acc1, 0, 0, 0);
+      acc0 = __builtin_amdgcn_mfma_f32_32x32x2f32(a.z, b0.z, acc0, 0, 0, 0);
+      acc1 = __builtin_amdgcn_mfma_f32_32x32x2f32(a.z, b1.z, acc1, 0, 0, 0);
+      acc0 = __builtin_amdgcn_mfma_f32_32x32x2f32(a.w, b0.w, acc0, 0, 0, 0);
+      acc1 = __builtin_amdgcn_mfma_f32_32x32x2f32(a.w, b1.w, acc1, 0, 0, 0);
+    }
   }
+  // acc0[r] / acc1[r]: row i0 + 8 (r/4) + 4 h + r%4, column j0 + m / j0 + 32 + m.
 #pragma unroll
-  for (int t = 0; t < D / 8; ++t) {
-    const float4 a = qin ? av[t] : make_float4(0.f, 0.f, 0.f, 0.f);
-    const float4 b = kin ? bv[t] : make_float4(0.f, 0.f, 0.f, 0.f);
-    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a.x, b.x, acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a.y, b.y, acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a.z, b.z, acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a.w, b.w, acc, 0, 0, 0);
-  }
-  // acc[r]: row i0 + 8 (r/4) + 4 h + r%4, column j0 + m.
-  const int j = j0 + m;
-  if (j < nc) {
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int i = i0 + 8 * (r >> 2) + 4 * h + (r & 3);
-      if (i < nc) scores[(bh * nc + i) * nc + j] = acc[r];
+  for (int r = 0; r < 16; ++r) {
+    const int i = i0 + 8 * (r >> 2) + 4 * h + (r & 3);
+    if (i < nc) {
+      float* srow = scores + (bh * nc + i) * nc;
+      if (kin0) srow[j0 + m] = acc0[r];
+      if (kin1) srow[j0 + 32 + m] = acc1[r];
     }
   }
 }
@@ -275,13 +292,13 @@ size_t select_pooled_workspace_bytes(const KGeom& g) {
 hipError_t launch_select_pooled(const KGeom& g, const float* qbar, const float* kbar, int topk, int32_t* idx,
                                 float* scores, hipStream_t s) {
   const size_t bh = (size_t)g.B * g.H;
-  const int tiles = (g.nc + 31) / 32;
-  const long long units = (long long)bh * tiles * tiles, per_xcd = (units + 7) / 8;
+  const int ti = (g.nc + 31) / 32, tj = (g.nc + 63) / 64;
+  const long long units = (long long)bh * ti * tj, per_xcd = (units + 7) / 8;
   const dim3 grid((unsigned)(8 * per_xcd));
   if (g.D == 64)
-    hipLaunchKernelGGL(block_score<64>, grid, dim3(64), 0, s, qbar, kbar, scores, g.nc, tiles, per_xcd, units);
+    hipLaunchKernelGGL(block_score<64>, grid, dim3(64), 0, s, qbar, kbar, scores, g.nc, ti, tj, per_xcd, units);
   else
-    hipLaunchKernelGGL(block_score<128>, grid, dim3(64), 0, s, qbar, kbar, scores, g.nc, tiles, per_xcd, units);
+    hipLaunchKernelGGL(block_score<128>, grid, dim3(64), 0, s, qbar, kbar, scores, g.nc, ti, tj, per_xcd, units);
   const long long nrows = (long long)bh * g.nc;
   const int per_lane = (g.nc + 63) / 64;
   // Every keys-per-lane count up to 8 has its own instantiation, larger ones
