@@ -52,6 +52,9 @@ def parse():
     ap.add_argument("--unpacked", action="store_true",
                     help="the unpacked fine stage (one 64-key tile per selected cube, K token-major, V "
                          "cube-transposed) instead of the packed one (cubes with few valid keys share tiles)")
+    ap.add_argument("--one-stream", action="store_true",
+                    help="every launch on one stream (the V permute otherwise runs on a second stream beside the "
+                         "coarse stage); for per-kernel traces whose durations no other kernel shares")
     ap.add_argument("--backward", action="store_true",
                     help="also time the backward of the fine stage (dQ, dK, dV) after the forward steps; "
                          "reported under 'backward', not in 'value'")
@@ -372,7 +375,7 @@ def main():
                           fused_linear=args.fused_linear, k_raster=args.k_raster,
                           window=wl.window if wl.pattern == "sta" else None, bufs=bufs, out=o,
                           mark=(lambda i: ev[i].record()) if ev is not None else None,
-                          packed=not args.unpacked)
+                          packed=not args.unpacked, overlap=not args.one_stream)
 
     for _ in range(args.warmup):
         step()
@@ -446,6 +449,7 @@ def main():
                                                          "; packed tiles: compact k, slot-layout v"))),
             **({"precision": "fp8 e4m3: Q, K per cube, V per channel; P e4m3"} if args.fp8 else {}),
             **({"window_cubes": list(wl.window)} if wl.window else {}),
+            "streams": 1 if (args.one_stream or args.fp8) else 2,
             "computed_blocks": wl.blocks, "fine_flops": flops,
         },
         "ms_per_layer": round(ms_step, 4),

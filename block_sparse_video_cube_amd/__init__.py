@@ -693,7 +693,7 @@ def layer_forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, grid: Seque
                   scale: Optional[float] = None, linear: bool = False, fused_linear: bool = False,
                   k_raster: bool = False, window: Optional[Sequence[int]] = None,
                   bufs: Optional[LayerBuffers] = None, out: Optional[torch.Tensor] = None, mark=None,
-                  packed: bool = True):
+                  packed: bool = True, overlap: bool = True):
     """One forward attention layer on raster q, k, v [B, S, heads, D] bf16:
     returns (o [B, S, heads, D] bf16, idx).
 
@@ -715,7 +715,8 @@ def layer_forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, grid: Seque
     arithmetic; the permute: memory traffic); the caller's stream waits for it
     before the fine stage, so the layer is ordered on the caller's stream as a
     whole.  The stage marks are taken on the caller's stream (the select stage
-    ends once the permute has too).
+    ends once the permute has too).  overlap=False keeps every launch on the
+    caller's stream (for per-kernel timings that no other kernel shares).
     """
     B, S, H, D = q.shape
     if scale is None:
@@ -742,10 +743,11 @@ def layer_forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, grid: Seque
     elif not k_raster:
         cube_permute(k, grid, layout="compact" if packed else "token", out=b.kc)
     main = torch.cuda.current_stream(q.device)
+    side = b.side if overlap else main
     # The side stream starts once the pooling is queued (and so after the
     # previous layer's reads of the V buffer on the caller's stream).
-    b.side.wait_stream(main)
-    with torch.cuda.stream(b.side):
+    side.wait_stream(main)
+    with torch.cuda.stream(side):
         if packed and not linear:
             cube_permute(v, grid, layout="slots", out=b.vs)
         else:
@@ -756,7 +758,7 @@ def layer_forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, grid: Seque
         sta_index(grid, window, B, H, head_dim=D, out=b.idx)
     else:
         select_topk_pooled(b.qbar, b.kbar, grid, topk, out=b.idx, workspace=b.ws_sel)
-    main.wait_stream(b.side)
+    main.wait_stream(side)
     mark(2)
     if not linear:
         if packed:
