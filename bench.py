@@ -186,6 +186,32 @@ def mfma_probe(vsa, torch, blocks=2048, iters=2000):
             "shader_clock_ghz": round(ghz, 3), "ms": round(ms, 4)}
 
 
+def hbm_probe(vsa, torch, nbytes=1 << 30, reps=10):
+    """Rates of plain HBM streams (vsa_hbm_probe: copy, read, write over 1 GiB):
+    a measured denominator beside the published 8 TB/s for the memory-bound
+    steps (the permutes and pooling)."""
+    a = torch.ones(nbytes, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    out = {}
+    for kind, moved in (("copy", 2), ("read", 1), ("write", 1)):
+        def f():
+            vsa.hbm_probe(kind, a if kind != "write" else None, b if kind != "read" else None)
+        f()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            f()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        out[f"{kind}_tbps"] = round(moved * nbytes / (ms * 1e-3) / 1e12, 3)
+    del a, b
+    return {"kernel": "hbm_stream (vsa_hbm_probe): 16384 x 256 threads, four 16-byte words per thread per round, "
+                      "nontemporal stores", "bytes": nbytes, **out,
+            "frac_of_published": {k[:-5]: round(v / (PEAK_HBM_GBS / 1e3), 4) for k, v in out.items()}}
+
+
 def valid_fine_flops(wl, idx, torch):
     """Flops of the computed blocks over valid query and key tokens only
     (4 D n_valid(i) n_valid(j) per block), from the block lists."""
@@ -412,6 +438,7 @@ def main():
     step_ms = [evs[s][0].elapsed_time(evs[s][len(stages)]) for s in range(args.steps)]
     vflops = valid_fine_flops(wl, idx, torch)
     probe = mfma_probe(vsa, torch)
+    hbm = hbm_probe(vsa, torch)
     # Algorithmic bytes of one fine-stage launch: Q, K, V read once, O written
     # once (bf16; fp8 codes are one byte, plus their scales).
     alg_bytes = 4 * B * H * d.rows * D * 2
@@ -475,6 +502,7 @@ def main():
             "fine_stage_tflops": round(vflops / (fine_ms * 1e-3) / 1e12, 2),
         },
         "mfma_probe": probe,
+        "hbm_probe": hbm,
         "wall_s_timed": round(wall, 3),
         "device": torch.cuda.get_device_name(0),
     }

@@ -56,6 +56,7 @@ __all__ = [
     "vsa_attention",
     "workspace_bytes",
     "mfma_probe",
+    "hbm_probe",
     "linear_branch_bwd",
     "LayerBuffers",
     "layer_stages",
@@ -557,6 +558,22 @@ def mfma_probe(blocks: int, iters: int, device: str = "cuda:0"):
     _lib.check("vsa_mfma_probe", _lib.load().vsa_mfma_probe(int(blocks), int(iters), sink.data_ptr(),
                                                              clk.data_ptr(), _stream()))
     return sink, clk
+
+
+def hbm_probe(kind: str, src: Optional[torch.Tensor], dst: Optional[torch.Tensor]) -> None:
+    """Launch one HBM stream (vsa_hbm_probe) on the current stream: kind
+    "copy" (src -> dst, equal byte sizes), "read" (src) or "write" (dst)."""
+    code = {"copy": 0, "read": 1, "write": 2}[kind]
+    t = src if src is not None else dst
+    nbytes = t.numel() * t.element_size()
+    for x in (src, dst):
+        if x is not None and (not x.is_cuda or not x.is_contiguous()):
+            raise ValueError("hbm_probe: buffers must be contiguous GPU tensors")
+    if kind == "copy" and dst.numel() * dst.element_size() != nbytes:
+        raise ValueError("hbm_probe: copy buffers differ in size")
+    _lib.check("vsa_hbm_probe", _lib.load().vsa_hbm_probe(code, src.data_ptr() if src is not None else None,
+                                                           dst.data_ptr() if dst is not None else None, nbytes,
+                                                           _stream()))
 
 
 def sparse_attn_linear_fwd(qc: torch.Tensor, kc: torch.Tensor, vt: torch.Tensor, idx: torch.Tensor,

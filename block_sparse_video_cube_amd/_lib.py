@@ -53,6 +53,7 @@ ENTRY_POINTS = (
     "vsa_sparse_attn_fwd_fp8",
     "vsa_sparse_attn_linear_fwd",
     "vsa_mfma_probe",
+    "vsa_hbm_probe",
     "vsa_linear_bwd_workspace_bytes",
     "vsa_linear_branch_bwd",
     "vsa_cube_permute_pool_compact",
@@ -135,6 +136,7 @@ def load() -> ctypes.CDLL:
         "vsa_sparse_attn_linear_fwd": (i32, [G, P, P, P, P, i32, ctypes.c_float, P, P, P, sz, P]),
         "vsa_sparse_attn_bwd": (i32, [G, P, P, P, P, P, P, P, i32, ctypes.c_float, P, P, P, P, sz, P]),
         "vsa_mfma_probe": (i32, [i32, i32, P, P, P]),
+        "vsa_hbm_probe": (i32, [i32, P, P, sz, P]),
         "vsa_linear_bwd_workspace_bytes": (sz, [G, i32]),
         "vsa_linear_branch_bwd": (i32, [G, P, P, P, P, P, i32, P, P, P, P, P, P, P, P, P, P, sz, P]),
         "vsa_cube_permute_pool_compact": (i32, [G, P, P, P, P]),

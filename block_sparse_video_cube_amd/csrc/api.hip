@@ -432,6 +432,14 @@ int32_t vsa_linear_branch_bwd(const vsa_geom* g, const uint16_t* qc, const uint1
                                               dv_add, dq, dk, dv, ws, static_cast<hipStream_t>(stream)));
 }
 
+int32_t vsa_hbm_probe(int32_t kind, const void* src, void* dst, size_t bytes, void* stream) {
+  if (kind < 0 || kind > 2) return VSA_ERR_LAYOUT;
+  if ((kind != 2 && !src) || (kind != 1 && !dst)) return VSA_ERR_NULL;
+  if (!aligned16(src) || !aligned16(dst)) return VSA_ERR_ALIGN;
+  if (bytes < 16 || bytes % 16 != 0 || bytes > ((size_t)1 << 40)) return VSA_ERR_GEOMETRY;
+  return launch_status(vsa::launch_hbm_probe(kind, src, dst, (long long)(bytes / 16), static_cast<hipStream_t>(stream)));
+}
+
 int32_t vsa_mfma_probe(int32_t blocks, int32_t iters, float* sink, uint64_t* clk, void* stream) {
   if (!sink || !clk) return VSA_ERR_NULL;
   if (!aligned16(sink) || !aligned16(clk)) return VSA_ERR_ALIGN;

@@ -189,6 +189,7 @@ hipError_t launch_attn_lin_fwd(const KGeom& g, const uint16_t* qc, const uint16_
 hipError_t launch_sta_index(const KGeom& g, int wt, int wh, int ww, int32_t* idx, hipStream_t s);
 size_t attn_bwd_workspace_bytes(const KGeom& g, int topk);
 hipError_t launch_mfma_probe(int blocks, int iters, float* sink, unsigned long long* clk, hipStream_t s);
+hipError_t launch_hbm_probe(int kind, const void* src, void* dst, long long words, hipStream_t s);
 size_t quant_workspace_bytes(const KGeom& g);
 hipError_t launch_quant(const KGeom& g, const uint16_t* q, const uint16_t* k, const uint16_t* v, uint8_t* q8,
                         float* qs, uint8_t* k8, float* ks, uint8_t* v8t, float* vs, float* qmean, float* kmean,

@@ -438,6 +438,18 @@ int32_t vsa_linear_branch_bwd(const vsa_geom* g, const uint16_t* qc, const uint1
  * blocks > 2^20), VSA_ERR_LAUNCH. */
 int32_t vsa_mfma_probe(int32_t blocks, int32_t iters, float* sink, uint64_t* clk, void* stream);
 
+/* HBM stream probe (measurement support, not part of the attention path): the
+ * rates plain streams reach on this device, a measured denominator beside the
+ * published 8 TB/s for the memory-bound steps.  kind 0: copy bytes from src to
+ * dst; 1: read src (dst, if not NULL, may receive one 16-byte checksum word);
+ * 2: write dst (src unused, may be NULL).  Stores are nontemporal.  One launch
+ * of 16384 workgroups of 256 threads on `stream`, four 16-byte words per
+ * thread per round.  src, dst: device memory the caller owns, 16-byte
+ * aligned; bytes: a multiple of 16, at least 16, at most 2^40.
+ * Errors: VSA_ERR_LAYOUT (kind), VSA_ERR_NULL, VSA_ERR_ALIGN, VSA_ERR_GEOMETRY
+ * (bytes), VSA_ERR_LAUNCH. */
+int32_t vsa_hbm_probe(int32_t kind, const void* src, void* dst, size_t bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -142,6 +142,10 @@ int main() {
   EXPECT(vsa_mfma_probe(0, 1, wf, (uint64_t*)P, NULL), VSA_ERR_GEOMETRY);
   EXPECT(vsa_mfma_probe(1, INT32_MIN, wf, (uint64_t*)P, NULL), VSA_ERR_GEOMETRY);
   EXPECT(vsa_mfma_probe(INT32_MAX, 1, wf, (uint64_t*)P, NULL), VSA_ERR_GEOMETRY);
+  EXPECT(vsa_hbm_probe(7, P, P, 1024, NULL), VSA_ERR_LAYOUT);
+  EXPECT(vsa_hbm_probe(0, NULL, P, 1024, NULL), VSA_ERR_NULL);
+  EXPECT(vsa_hbm_probe(1, P, NULL, (size_t)-16, NULL), VSA_ERR_GEOMETRY);
+  EXPECT(vsa_hbm_probe(2, NULL, P, 24, NULL), VSA_ERR_GEOMETRY);
 
   printf("abi_driver: %d failures\n", failures);
   return failures ? 1 : 0;

@@ -267,6 +267,22 @@ def test_mfma_probe_validation(lib):
     assert lib.vsa_mfma_probe((1 << 20) + 1, 10, P, P, None) == _lib.VSA_ERR_GEOMETRY
 
 
+def test_hbm_probe_validation(lib):
+    from block_sparse_video_cube_amd import _lib
+
+    P = FAKE
+    assert lib.vsa_hbm_probe(3, P, P, 1024, None) == _lib.VSA_ERR_LAYOUT
+    assert lib.vsa_hbm_probe(-1, P, P, 1024, None) == _lib.VSA_ERR_LAYOUT
+    assert lib.vsa_hbm_probe(0, None, P, 1024, None) == _lib.VSA_ERR_NULL
+    assert lib.vsa_hbm_probe(0, P, None, 1024, None) == _lib.VSA_ERR_NULL
+    assert lib.vsa_hbm_probe(1, None, None, 1024, None) == _lib.VSA_ERR_NULL
+    assert lib.vsa_hbm_probe(2, None, None, 1024, None) == _lib.VSA_ERR_NULL
+    assert lib.vsa_hbm_probe(0, ODD, P, 1024, None) == _lib.VSA_ERR_ALIGN
+    assert lib.vsa_hbm_probe(0, P, P, 1000, None) == _lib.VSA_ERR_GEOMETRY
+    assert lib.vsa_hbm_probe(2, None, P, 0, None) == _lib.VSA_ERR_GEOMETRY
+    assert lib.vsa_hbm_probe(1, P, None, (1 << 40) + 16, None) == _lib.VSA_ERR_GEOMETRY
+
+
 def test_linear_backward_entry_point_validation(lib):
     from block_sparse_video_cube_amd import _lib
 
