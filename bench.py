@@ -356,8 +356,10 @@ def main():
     # writes the output in raster order, Q is only pooled, K is pooled and
     # permuted in one pass (contiguous 16 KB tiles stream faster than tiles
     # gathered from 64 raster rows; --k-raster gathers them instead), V is
-    # permuted into the cube-transposed layout.  The linear branch works on
-    # cube-major rows, so the hybrid layer keeps the permute / unpermute pair.
+    # permuted into the cube-transposed layout.  The hybrid layer permutes K
+    # (the linear branch's state reads cube-major keys); its two calls read
+    # raster Q and write the raster output (the fused pass keeps the
+    # permute / unpermute pair).
     stages = vsa.layer_stages(wl.linear, args.fused_linear)
     if args.fp8:
         if wl.linear:

@@ -267,10 +267,14 @@ def sparse_attn_fwd(qc: torch.Tensor, kc: torch.Tensor, vt: torch.Tensor, idx: t
 
 def sparse_attn_fwd_raster(q: torch.Tensor, k: torch.Tensor, vt: torch.Tensor, idx: torch.Tensor,
                            grid: Sequence[int], scale: Optional[float] = None, want_lse: bool = False,
-                           out: Optional[torch.Tensor] = None):
+                           out: Optional[torch.Tensor] = None, out_f32: Optional[torch.Tensor] = None,
+                           bf16_out: bool = True):
     """Fine stage on raster-order q and output: returns (o [B, S, heads, D] bf16, lse or None).
 
     k: raster [B, S, heads, D] (tiles gathered in the kernel) or cube-major [B, heads, Np, D].
+    out_f32: optional fp32 output in cube-major rows [B, heads, Np, D] (the
+    linear branch's o_sparse); bf16_out=False skips the bf16 output (o is
+    then None; out_f32 required).
     """
     B, S, Hh, D = q.shape
     g = make_geom(B, Hh, D, grid)
@@ -287,13 +291,21 @@ def sparse_attn_fwd_raster(q: torch.Tensor, k: torch.Tensor, vt: torch.Tensor, i
     _need(idx, "idx", torch.int32, (B, Hh, d.n_cubes, topk))
     if scale is None:
         scale = 1.0 / math.sqrt(D)
-    if out is None:
-        out = torch.empty_like(q)
-    _need(out, "o", torch.bfloat16, (B, d.tokens, Hh, D))
+    if bf16_out:
+        if out is None:
+            out = torch.empty_like(q)
+        _need(out, "o", torch.bfloat16, (B, d.tokens, Hh, D))
+    else:
+        if out_f32 is None:
+            raise ValueError("sparse_attn_fwd_raster: bf16_out=False needs out_f32")
+        out = None
+    if out_f32 is not None:
+        _need(out_f32, "o_f32", torch.float32, (B, Hh, d.rows, D))
     lse = torch.empty((B, Hh, d.rows), dtype=torch.float32, device=q.device) if want_lse else None
     _lib.check("vsa_sparse_attn_fwd_raster", _lib.load().vsa_sparse_attn_fwd_raster(
         g, q.data_ptr(), k.data_ptr(), k_layout, vt.data_ptr(), idx.data_ptr(), topk, float(scale),
-        out.data_ptr(), lse.data_ptr() if lse is not None else None, _stream()))
+        out.data_ptr() if out is not None else None, out_f32.data_ptr() if out_f32 is not None else None,
+        lse.data_ptr() if lse is not None else None, _stream()))
     return out, lse
 
 
@@ -471,24 +483,27 @@ def sparse_attn_bwd(qc: torch.Tensor, kc: torch.Tensor, vc: torch.Tensor, oc: to
 
 def linear_branch(qc: torch.Tensor, kc: torch.Tensor, vt: torch.Tensor, idx: torch.Tensor,
                   o_sparse: torch.Tensor, grid: Sequence[int], out: Optional[torch.Tensor] = None,
-                  workspace: Optional[torch.Tensor] = None, save: bool = False):
+                  workspace: Optional[torch.Tensor] = None, save: bool = False, raster: bool = False):
     """bf16(o_sparse + O_lin), token-major.
 
     save: also return (o_lin fp32 [B, heads, Np, D], inv_den fp32 [B, heads, Np]) for
     linear_branch_bwd(saved=...): (out, (o_lin, inv_den)).
+    raster: qc is the raster queries [B, S, heads, D] and the output is raster
+    [B, S, heads, D] (kc, vt, o_sparse and the saved values stay cube-major).
     """
-    B, Hh, Np, D = qc.shape
+    B, Hh, D = kc.shape[0], kc.shape[1], kc.shape[3]
     g = make_geom(B, Hh, D, grid)
     d = geom_dims(g)
     topk = idx.shape[-1]
-    _need(qc, "qc", torch.bfloat16, (B, Hh, d.rows, D))
+    qo_shape = (B, d.tokens, Hh, D) if raster else (B, Hh, d.rows, D)
+    _need(qc, "q" if raster else "qc", torch.bfloat16, qo_shape)
     _need(kc, "kc", torch.bfloat16, (B, Hh, d.rows, D))
     _need(vt, "vt", torch.bfloat16, (B, Hh, d.n_cubes, D, 64))
     _need(idx, "idx", torch.int32, (B, Hh, d.n_cubes, topk))
     _need(o_sparse, "o_sparse", torch.float32, (B, Hh, d.rows, D))
     if out is None:
-        out = torch.empty((B, Hh, d.rows, D), dtype=torch.bfloat16, device=qc.device)
-    _need(out, "oc", torch.bfloat16, (B, Hh, d.rows, D))
+        out = torch.empty(qo_shape, dtype=torch.bfloat16, device=qc.device)
+    _need(out, "o" if raster else "oc", torch.bfloat16, qo_shape)
     nbytes = workspace_bytes(g, linear=True)
     if workspace is None:
         workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=qc.device)
@@ -497,7 +512,8 @@ def linear_branch(qc: torch.Tensor, kc: torch.Tensor, vt: torch.Tensor, idx: tor
         o_lin = torch.empty((B, Hh, d.rows, D), dtype=torch.float32, device=qc.device)
         inv_den = torch.empty((B, Hh, d.rows), dtype=torch.float32, device=qc.device)
     _lib.check("vsa_linear_branch", _lib.load().vsa_linear_branch(
-        g, qc.data_ptr(), kc.data_ptr(), vt.data_ptr(), idx.data_ptr(), int(topk), o_sparse.data_ptr(),
+        g, qc.data_ptr(), _lib.VSA_LAYOUT_RASTER if raster else _lib.VSA_LAYOUT_TOKEN_MAJOR, kc.data_ptr(),
+        vt.data_ptr(), idx.data_ptr(), int(topk), o_sparse.data_ptr(),
         out.data_ptr(), o_lin.data_ptr() if save else None, inv_den.data_ptr() if save else None,
         workspace.data_ptr(), workspace.numel() * workspace.element_size(), _stream()))
     return (out, (o_lin, inv_den)) if save else out
@@ -702,7 +718,7 @@ def layer_stages(linear: bool = False, fused_linear: bool = False):
     called once before the first and once after each)."""
     if linear:
         return (["permute", "select", "fine+linear", "unpermute"] if fused_linear else
-                ["permute", "select", "fine", "linear", "unpermute"])
+                ["pool", "select", "fine", "linear"])
     return ["pool", "select", "fine"]
 
 
@@ -722,9 +738,10 @@ def layer_forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, grid: Seque
     token-major (or, with k_raster, only pooled and its tiles gathered by the
     fine stage), V cube-transposed and the unpacked stage.  window: a sliding-tile window
     (cubes per axis) whose static block lists replace the coarse stage.  The
-    linear branch works on cube-major rows, so the hybrid layer permutes Q and
-    K, runs the fine stage and the linear branch (two calls, or one fused pass
-    with fused_linear) and unpermutes.  mark(i), if given, is called before
+    hybrid layer (linear branch) permutes K into cube-major rows (the branch's
+    state reads them).  With two calls, the fine stage and the linear branch
+    both read raster Q and the branch writes the raster output, so Q is only
+    pooled; the fused pass (fused_linear) permutes Q too and unpermutes.  mark(i), if given, is called before
     stage 0 and after each stage i - 1 (layer_stages names them).
 
     Streams: the V permute runs on a second stream (bufs.side) after the Q and
@@ -749,7 +766,12 @@ def layer_forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, grid: Seque
     # stage is the unpacked one with another V layout (and slightly slower).
     packed = packed and not k_raster and any(int(x) % 4 for x in grid)
     if linear:
-        cube_permute_pool(q, grid, out=b.qc, mean_out=b.qbar)
+        # Two calls: both read raster Q and the linear branch writes the raster
+        # output, so Q is only pooled.  The fused pass works on cube-major Q.
+        if fused_linear:
+            cube_permute_pool(q, grid, out=b.qc, mean_out=b.qbar)
+        else:
+            cube_pool(q, grid, mean_out=b.qbar)
         cube_permute_pool(k, grid, out=b.kc, mean_out=b.kbar)
     elif window is None:
         cube_pool(q, grid, mean_out=b.qbar)
@@ -790,10 +812,8 @@ def layer_forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, grid: Seque
         cube_unpermute(b.oc2, grid, out=out)
         mark(4)
         return out, b.idx
-    sparse_attn_fwd(b.qc, b.kc, b.vt, b.idx, grid, scale, out=b.oc, out_f32=b.of)
+    sparse_attn_fwd_raster(q, b.kc, b.vt, b.idx, grid, scale, out_f32=b.of, bf16_out=False)
     mark(3)
-    linear_branch(b.qc, b.kc, b.vt, b.idx, b.of, grid, out=b.oc2, workspace=b.ws_lin)
+    linear_branch(q, b.kc, b.vt, b.idx, b.of, grid, out=out, workspace=b.ws_lin, raster=True)
     mark(4)
-    cube_unpermute(b.oc2, grid, out=out)
-    mark(5)
     return out, b.idx

@@ -124,11 +124,11 @@ def load() -> ctypes.CDLL:
         "vsa_cube_unpermute": (i32, [G, P, P, P]),
         "vsa_select_topk": (i32, [G, P, P, i32, P, P, sz, P]),
         "vsa_sparse_attn_fwd": (i32, [G, P, P, P, P, i32, ctypes.c_float, P, P, P, P]),
-        "vsa_linear_branch": (i32, [G, P, P, P, P, i32, P, P, P, P, P, sz, P]),
+        "vsa_linear_branch": (i32, [G, P, i32, P, P, P, i32, P, P, P, P, P, sz, P]),
         "vsa_sta_topk": (i32, [G, i32, i32, i32]),
         "vsa_sta_index": (i32, [G, i32, i32, i32, P, P]),
         "vsa_cube_pool": (i32, [G, P, P, P]),
-        "vsa_sparse_attn_fwd_raster": (i32, [G, P, P, i32, P, P, i32, ctypes.c_float, P, P, P]),
+        "vsa_sparse_attn_fwd_raster": (i32, [G, P, P, i32, P, P, i32, ctypes.c_float, P, P, P, P]),
         "vsa_attn_bwd_workspace_bytes": (sz, [G, i32]),
         "vsa_quant_fp8_workspace_bytes": (sz, [G]),
         "vsa_quant_fp8": (i32, [G, P, P, P, P, P, P, P, P, P, P, P, P, sz, P]),

@@ -333,21 +333,21 @@ int32_t vsa_select_topk(const vsa_geom* g, const uint16_t* qc, const uint16_t* k
 
 int32_t vsa_sparse_attn_fwd_raster(const vsa_geom* g, const uint16_t* q, const uint16_t* kk, int32_t k_layout,
                                    const uint16_t* vt, const int32_t* idx, int32_t topk, float softmax_scale,
-                                   uint16_t* o, float* lse, void* stream) {
+                                   uint16_t* o, float* o_f32, float* lse, void* stream) {
   vsa_dims d;
   vsa::KGeom k;
   int32_t st = prepare(g, &d, &k);
   if (st != VSA_OK) return st;
-  if (!q || !kk || !vt || !idx || !o) return VSA_ERR_NULL;
+  if (!q || !kk || !vt || !idx || (!o && !o_f32)) return VSA_ERR_NULL;
   if (!aligned16(q) || !aligned16(kk) || !aligned16(vt) || !aligned16(idx) || !aligned16(o) ||
-      (lse && !aligned16(lse)))
+      !aligned16(o_f32) || (lse && !aligned16(lse)))
     return VSA_ERR_ALIGN;
   if (k_layout != VSA_LAYOUT_TOKEN_MAJOR && k_layout != VSA_LAYOUT_RASTER) return VSA_ERR_LAYOUT;
   if (d.tokens * (int64_t)g->heads * g->head_dim * 2 >= ((int64_t)1 << 31)) return VSA_ERR_GEOMETRY;
   if (topk < 1 || topk > d.n_cubes) return VSA_ERR_TOPK;
   if (!(softmax_scale > 0.f) || !isfinite(softmax_scale)) return VSA_ERR_SCALE;
   return launch_status(vsa::launch_attn_fwd_raster(k, q, kk, k_layout == VSA_LAYOUT_RASTER, vt, idx, topk,
-                                                   softmax_scale, o, lse, static_cast<hipStream_t>(stream)));
+                                                   softmax_scale, o, o_f32, lse, static_cast<hipStream_t>(stream)));
 }
 
 int32_t vsa_cube_pool(const vsa_geom* g, const uint16_t* x, float* mean, void* stream) {
@@ -448,9 +448,9 @@ int32_t vsa_mfma_probe(int32_t blocks, int32_t iters, float* sink, uint64_t* clk
                                               static_cast<hipStream_t>(stream)));
 }
 
-int32_t vsa_linear_branch(const vsa_geom* g, const uint16_t* qc, const uint16_t* kc, const uint16_t* vt,
-                          const int32_t* idx, int32_t topk, const float* o_sparse, uint16_t* oc, float* o_lin,
-                          float* inv_den, void* ws, size_t ws_bytes, void* stream) {
+int32_t vsa_linear_branch(const vsa_geom* g, const uint16_t* qc, int32_t qo_layout, const uint16_t* kc,
+                          const uint16_t* vt, const int32_t* idx, int32_t topk, const float* o_sparse, uint16_t* oc,
+                          float* o_lin, float* inv_den, void* ws, size_t ws_bytes, void* stream) {
   vsa_dims d;
   vsa::KGeom k;
   int32_t st = prepare(g, &d, &k);
@@ -462,9 +462,10 @@ int32_t vsa_linear_branch(const vsa_geom* g, const uint16_t* qc, const uint16_t*
     return VSA_ERR_ALIGN;
   if ((o_lin && !aligned16(o_lin)) || (inv_den && !aligned16(inv_den))) return VSA_ERR_ALIGN;
   if (topk < 1 || topk > d.n_cubes) return VSA_ERR_TOPK;
+  if (qo_layout != VSA_LAYOUT_TOKEN_MAJOR && qo_layout != VSA_LAYOUT_RASTER) return VSA_ERR_LAYOUT;
   if (ws_bytes < vsa::linear_workspace_bytes(k)) return VSA_ERR_WORKSPACE;
-  return launch_status(vsa::launch_linear(k, qc, kc, vt, idx, topk, o_sparse, oc, o_lin, inv_den, ws,
-                                          static_cast<hipStream_t>(stream)));
+  return launch_status(vsa::launch_linear(k, qc, kc, vt, idx, topk, o_sparse, oc, o_lin, inv_den,
+                                          qo_layout == VSA_LAYOUT_RASTER, ws, static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

@@ -316,8 +316,8 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd(const uint16_t* __restri
         const int r = 4 * gq + e;
         v[e] = o[dt][r] * c0 + xo[(dt * 16 + r) * 64 + lane] * c1;
       }
-      if (qvalid) *reinterpret_cast<uint2*>(orow + d) = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
-      if (!RASTER && oc_f32) *reinterpret_cast<float4*>(oc_f32 + row * D + d) = make_float4(v[0], v[1], v[2], v[3]);
+      if (qvalid && oc) *reinterpret_cast<uint2*>(orow + d) = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+      if (oc_f32) *reinterpret_cast<float4*>(oc_f32 + row * D + d) = make_float4(v[0], v[1], v[2], v[3]);
     }
   if (lse && hf == 0) lse[row] = m * scale + logf(l_tot);
 }
@@ -512,9 +512,9 @@ hipError_t launch_attn_fwd(const KGeom& g, const uint16_t* qc, const uint16_t* k
 
 hipError_t launch_attn_fwd_raster(const KGeom& g, const uint16_t* q, const uint16_t* k, bool k_raster,
                                   const uint16_t* vt, const int32_t* idx, int topk, float scale, uint16_t* o,
-                                  float* lse, hipStream_t s) {
-  if (k_raster) return launch_fwd_any<true, true>(g, q, k, vt, idx, topk, scale, o, nullptr, lse, s);
-  return launch_fwd_any<true, false>(g, q, k, vt, idx, topk, scale, o, nullptr, lse, s);
+                                  float* o_f32, float* lse, hipStream_t s) {
+  if (k_raster) return launch_fwd_any<true, true>(g, q, k, vt, idx, topk, scale, o, o_f32, lse, s);
+  return launch_fwd_any<true, false>(g, q, k, vt, idx, topk, scale, o, o_f32, lse, s);
 }
 
 // Packed workspace: the plan (16 bytes per tile and a 16-byte header per

@@ -114,9 +114,11 @@ size_t select_pooled_workspace_bytes(const KGeom& g);
 hipError_t launch_attn_fwd(const KGeom& g, const uint16_t* qc, const uint16_t* kc, const uint16_t* vt,
                            const int32_t* idx, int topk, float scale, uint16_t* oc, float* oc_f32, float* lse,
                            hipStream_t s);
+// o: raster bf16 output (may be null when o_f32 is given); o_f32: optional
+// fp32 output in cube-major rows.
 hipError_t launch_attn_fwd_raster(const KGeom& g, const uint16_t* q, const uint16_t* k, bool k_raster,
                                   const uint16_t* vt, const int32_t* idx, int topk, float scale, uint16_t* o,
-                                  float* lse, hipStream_t s);
+                                  float* o_f32, float* lse, hipStream_t s);
 // Packed fine stage: K in compact cube-major rows, V in the slot layout;
 // q/o raster (raster = true) or cube-major.  ws: the packing plan of a grid
 // with partial cubes (attn_packed_workspace_bytes; 0 for full grids).
@@ -126,9 +128,12 @@ hipError_t launch_attn_fwd_packed(const KGeom& g, const uint16_t* q, bool raster
                                   float* lse, void* ws, hipStream_t s);
 // o_lin, inv_den: optional (both or neither) fp32 copies of O_lin [B, H, Np, D]
 // and of 1/den [B, H, Np] for the backward.
+// raster: q and the output oc are raster [B, S, H, D] (padded query rows not
+// written) instead of cube-major rows; o_sparse, o_lin and inv_den stay
+// cube-major.
 hipError_t launch_linear(const KGeom& g, const uint16_t* qc, const uint16_t* kc, const uint16_t* vt,
                          const int32_t* idx, int topk, const float* o_sparse, uint16_t* oc, float* o_lin,
-                         float* inv_den, void* ws, hipStream_t s);
+                         float* inv_den, bool raster, void* ws, hipStream_t s);
 size_t linear_workspace_bytes(const KGeom& g);
 // The parts of the linear workspace the selected-block correction reads:
 // phi(K) token-major bf16 [B, H, Np, D], S_tot^T as bf16 hi + lo [B, H, D, D],

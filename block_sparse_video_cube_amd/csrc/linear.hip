@@ -296,7 +296,7 @@ __global__ void __launch_bounds__(kThreads, 2) lin_apply(
     int empty_u, int direct, const uint16_t* __restrict__ fk, const float* __restrict__ z_tot,
     const uint16_t* __restrict__ st_hi, const uint16_t* __restrict__ st_lo, const float* __restrict__ o_sparse,
     uint16_t* __restrict__ oc, float* __restrict__ o_lin_out, float* __restrict__ inv_out, KGeom g, Placement pl,
-    LinBwdRows br) {
+    LinBwdRows br, int raster) {
   constexpr int DC = D / 16, DT = D / 32;
   __shared__ __attribute__((aligned(16))) LinSmem<D> sm;
   int i, h, b;
@@ -308,6 +308,17 @@ __global__ void __launch_bounds__(kThreads, 2) lin_apply(
   const long long bh = (long long)b * g.H + h;
   const int q = 32 * wq + n;
   const long long row = bh * g.Np + 64LL * i + q;
+  // Element offset of query row q in qc and oc: cube-major, or (raster, the
+  // forward only) its raster token, where padded query rows have none.
+  long long qoff = row * D;
+  bool qvalid = true;
+  if (!BWD && raster) {
+    int ct, cy, cx;
+    cube_coords(g, i, ct, cy, cx);
+    const int t = 4 * ct + (q >> 4), y = 4 * cy + ((q >> 2) & 3), x = 4 * cx + (q & 3);
+    qvalid = t < g.T && y < g.Hg && x < g.W;
+    qoff = qvalid ? (((long long)b * g.S + ((long long)t * g.Hg + y) * g.W + x) * g.H + h) * D : 0;
+  }
   const int32_t* irow = list + (bh * g.nc + i) * len;
   const uint16_t* fkb = fk + bh * g.Np * D;
   const uint16_t* vb = vt + bh * g.Np * D;
@@ -325,13 +336,14 @@ __global__ void __launch_bounds__(kThreads, 2) lin_apply(
   bf16x8 fq[DC];
   float den_part = 0.f;
   {
-    const uint16_t* qrow = qc + row * D;
+    const uint16_t* qrow = qc + qoff;
     const float* zt = z_tot + bh * D + 8 * hf;
     uint4 raw[DC];
     float4 zv[DC][2];
 #pragma unroll
     for (int dc = 0; dc < DC; ++dc) {
-      raw[dc] = *reinterpret_cast<const uint4*>(qrow + 16 * dc + 8 * hf);
+      // (A padded query row reads as zero, as its cube-major row holds.)
+      raw[dc] = qvalid ? *reinterpret_cast<const uint4*>(qrow + 16 * dc + 8 * hf) : make_uint4(0, 0, 0, 0);
       zv[dc][0] = *reinterpret_cast<const float4*>(zt + 16 * dc);
       zv[dc][1] = *reinterpret_cast<const float4*>(zt + 16 * dc + 4);
     }
@@ -483,7 +495,7 @@ __global__ void __launch_bounds__(kThreads, 2) lin_apply(
     return;
   }
   const float* osrc = o_sparse + row * D;
-  uint16_t* odst = oc + row * D;
+  uint16_t* odst = oc + qoff;
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
@@ -496,8 +508,9 @@ __global__ void __launch_bounds__(kThreads, 2) lin_apply(
         const int r = 4 * gq + u;
         v[u] = (c[dt][r] + xo[(dt * 16 + r) * 64 + lane]) * inv;
       }
-      *reinterpret_cast<uint2*>(odst + e) =
-          make_uint2(pack_bf16x2(os.x + v[0], os.y + v[1]), pack_bf16x2(os.z + v[2], os.w + v[3]));
+      if (qvalid)
+        *reinterpret_cast<uint2*>(odst + e) =
+            make_uint2(pack_bf16x2(os.x + v[0], os.y + v[1]), pack_bf16x2(os.z + v[2], os.w + v[3]));
       if (o_lin_out) *reinterpret_cast<float4*>(o_lin_out + row * D + e) = make_float4(v[0], v[1], v[2], v[3]);
     }
   if (inv_out && hf == 0) inv_out[row] = inv;
@@ -565,13 +578,13 @@ int launch_complement(const KGeom& g, const int32_t* idx, int topk, const LinWs&
 template <int D, bool BWD>
 void launch_apply(const KGeom& g, const uint16_t* qc, const uint16_t* vt, const int32_t* idx, int topk,
                   const float* o_sparse, uint16_t* oc, float* o_lin, float* inv_den, const LinWs& w,
-                  const LinBwdRows& br, int direct, hipStream_t s) {
+                  const LinBwdRows& br, int direct, bool raster, hipStream_t s) {
   const int32_t* list = direct ? w.comp : idx;
   const int len = direct ? g.nc - topk : topk;
   const int empty_u = topk >= g.nc ? 1 : 0;
   hipLaunchKernelGGL((lin_apply<D, BWD>), dim3(grid_size(g)), dim3(kThreads), 0, s, qc, vt, list, len, empty_u,
                      direct, w.fk, w.z_tot, w.st_hi, w.st_lo, o_sparse, oc, o_lin, inv_den, g, make_placement(g),
-                     br);
+                     br, raster ? 1 : 0);
 }
 
 }  // namespace
@@ -607,14 +620,17 @@ hipError_t launch_lin_prep(const KGeom& g, const uint16_t* kc, const uint16_t* v
 
 hipError_t launch_linear(const KGeom& g, const uint16_t* qc, const uint16_t* kc, const uint16_t* vt,
                          const int32_t* idx, int topk, const float* o_sparse, uint16_t* oc, float* o_lin,
-                         float* inv_den, void* ws, hipStream_t s) {
+                         float* inv_den, bool raster, void* ws, hipStream_t s) {
   hipError_t e = launch_lin_prep(g, kc, vt, ws, s);
   if (e != hipSuccess) return e;
   const LinWs w = carve(g, ws, nullptr);
   const int direct = launch_complement(g, idx, topk, w, s);
   if (g.D == 64)
-    launch_apply<64, false>(g, qc, vt, idx, topk, o_sparse, oc, o_lin, inv_den, w, LinBwdRows{}, direct, s);
-  else launch_apply<128, false>(g, qc, vt, idx, topk, o_sparse, oc, o_lin, inv_den, w, LinBwdRows{}, direct, s);
+    launch_apply<64, false>(g, qc, vt, idx, topk, o_sparse, oc, o_lin, inv_den, w, LinBwdRows{}, direct, raster,
+                            s);
+  else
+    launch_apply<128, false>(g, qc, vt, idx, topk, o_sparse, oc, o_lin, inv_den, w, LinBwdRows{}, direct, raster,
+                             s);
   return hipGetLastError();
 }
 
@@ -630,9 +646,9 @@ hipError_t launch_lin_bwd_rows(const KGeom& g, const uint16_t* qc, const uint16_
     if (g.D == 64) hipLaunchKernelGGL(lin_rows<64>, dim3(blocks), dim3(256), 0, s, qc, o_lin, inv_den, br, g, nrows);
     else hipLaunchKernelGGL(lin_rows<128>, dim3(blocks), dim3(256), 0, s, qc, o_lin, inv_den, br, g, nrows);
   } else if (g.D == 64) {
-    launch_apply<64, true>(g, qc, vt, idx, topk, nullptr, nullptr, nullptr, nullptr, w, br, direct, s);
+    launch_apply<64, true>(g, qc, vt, idx, topk, nullptr, nullptr, nullptr, nullptr, w, br, direct, false, s);
   } else {
-    launch_apply<128, true>(g, qc, vt, idx, topk, nullptr, nullptr, nullptr, nullptr, w, br, direct, s);
+    launch_apply<128, true>(g, qc, vt, idx, topk, nullptr, nullptr, nullptr, nullptr, w, br, direct, false, s);
   }
   return hipGetLastError();
 }

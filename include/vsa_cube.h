@@ -49,7 +49,7 @@
 extern "C" {
 #endif
 
-#define VSA_ABI_VERSION 3
+#define VSA_ABI_VERSION 4
 
 typedef enum vsa_status {
   VSA_OK = 0,
@@ -195,12 +195,15 @@ int32_t vsa_select_topk_pooled(const vsa_geom* g, const float* qbar, const float
  * or VSA_LAYOUT_RASTER, k = raster tokens whose 64-row tiles the kernel
  * gathers itself (no permute of K either).  vt stays DIM_MAJOR.  Results are
  * bit-identical to vsa_sparse_attn_fwd followed by vsa_cube_unpermute.
+ * o_f32: optional fp32 output in cube-major rows [B, heads, Np, D], as the
+ * oc_f32 of vsa_sparse_attn_fwd (the o_sparse input of vsa_linear_branch); o
+ * may be NULL when o_f32 is given (at least one of them, else VSA_ERR_NULL).
  * lse: optional fp32 [B, heads, Np] in cube-major row order, as there.
  * Limit: S * heads * D * 2 < 2^31 bytes (32-bit buffer offsets). */
 int32_t vsa_sparse_attn_fwd_raster(const vsa_geom* g, const uint16_t* q, const uint16_t* k,
                                    int32_t k_layout, const uint16_t* vt, const int32_t* idx,
-                                   int32_t topk, float softmax_scale, uint16_t* o, float* lse,
-                                   void* stream);
+                                   int32_t topk, float softmax_scale, uint16_t* o, float* o_f32,
+                                   float* lse, void* stream);
 
 /* Sliding-tile pattern (STA; FastVideo attention-backend article, item
  * "SLIDING_TILE_ATTN" and the figure comparing NATTEN, Tiled NATTEN and STA):
@@ -358,8 +361,13 @@ int32_t vsa_sparse_attn_bwd(const vsa_geom* g, const uint16_t* qc, const uint16_
  * valid keys of the cubes NOT in idx[b, h, i, :] (0 when none are left).
  * qc, kc: TOKEN_MAJOR bf16; vt: DIM_MAJOR bf16; idx as for the fine stage
  * (entries distinct); o_sparse: fp32 [B, heads, Np, D] (the oc_f32 output of
- * vsa_sparse_attn_fwd); oc: output bf16 TOKEN_MAJOR.  o_sparse and oc may not
- * overlap.  o_lin, inv_den: optional outputs, both or neither (else
+ * vsa_sparse_attn_fwd); oc: output bf16 TOKEN_MAJOR.  qo_layout:
+ * VSA_LAYOUT_TOKEN_MAJOR as described, or VSA_LAYOUT_RASTER: qc is then the
+ * raster query tokens [B, S, heads, D] and oc the raster output
+ * [B, S, heads, D] (every token written; the values are bit-identical to the
+ * TOKEN_MAJOR call followed by vsa_cube_unpermute), while kc, vt, o_sparse
+ * and the optional outputs stay cube-major; other codes give VSA_ERR_LAYOUT.
+ * o_sparse and oc may not overlap.  o_lin, inv_den: optional outputs, both or neither (else
  * VSA_ERR_NULL): O_lin before the combine, fp32 [B, heads, Np, D], and 1/den
  * per query row, fp32 [B, heads, Np] (0 where U is empty), for
  * vsa_linear_branch_bwd to use instead of recomputing the branch.
@@ -369,8 +377,8 @@ int32_t vsa_sparse_attn_bwd(const vsa_geom* g, const uint16_t* qc, const uint16_
  * when more cubes are selected, so that the difference of two nearly equal
  * sums never magnifies the rounding (n_cubes <= VSA_MAX_CUBES; larger grids
  * keep the first form). */
-int32_t vsa_linear_branch(const vsa_geom* g, const uint16_t* qc, const uint16_t* kc,
-                          const uint16_t* vt, const int32_t* idx, int32_t topk,
+int32_t vsa_linear_branch(const vsa_geom* g, const uint16_t* qc, int32_t qo_layout,
+                          const uint16_t* kc, const uint16_t* vt, const int32_t* idx, int32_t topk,
                           const float* o_sparse, uint16_t* oc, float* o_lin, float* inv_den,
                           void* ws, size_t ws_bytes, void* stream);
 

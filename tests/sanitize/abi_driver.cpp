@@ -112,15 +112,17 @@ int main() {
   EXPECT(vsa_sparse_attn_fwd(&g, p16, p16, p16, pi, 2, -1e-30f, w16, NULL, NULL, NULL), VSA_ERR_SCALE);
   EXPECT(vsa_sparse_attn_fwd(&g, p16, p16, p16, pi, INT32_MAX, 0.1f, w16, NULL, NULL, NULL), VSA_ERR_TOPK);
   EXPECT(vsa_sparse_attn_fwd(&g, p16, p16, p16, pi, 2, 0.1f, w16, (float*)Q, NULL, NULL), VSA_ERR_ALIGN);
-  EXPECT(vsa_sparse_attn_fwd_raster(&g, p16, p16, 1, p16, pi, 2, 0.1f, w16, NULL, NULL), VSA_ERR_LAYOUT);
+  EXPECT(vsa_sparse_attn_fwd_raster(&g, p16, p16, 1, p16, pi, 2, 0.1f, w16, NULL, NULL, NULL), VSA_ERR_LAYOUT);
+  EXPECT(vsa_sparse_attn_fwd_raster(&g, p16, p16, 0, p16, pi, 2, 0.1f, NULL, NULL, NULL, NULL), VSA_ERR_NULL);
   EXPECT(vsa_sparse_attn_fwd_packed(&g, p16, VSA_LAYOUT_RASTER, p16, p16, pi, 2, 0.1f, w16, NULL, NULL, 0, NULL),
          VSA_ERR_NULL);
   EXPECT(vsa_sparse_attn_fwd_packed(&g, p16, VSA_LAYOUT_RASTER, p16, p16, pi, 2, 0.1f, w16, NULL, P, 16, NULL),
          VSA_ERR_WORKSPACE);
   EXPECT(vsa_sparse_attn_fwd_packed(&g, p16, 4, p16, p16, pi, 2, 0.1f, w16, NULL, P, 1 << 20, NULL), VSA_ERR_LAYOUT);
   const size_t lws = vsa_linear_workspace_bytes(&g);
-  EXPECT(vsa_linear_branch(&g, p16, p16, p16, pi, 2, pf, w16, NULL, NULL, P, lws - 1, NULL), VSA_ERR_WORKSPACE);
-  EXPECT(vsa_linear_branch(&g, p16, p16, p16, pi, 2, pf, w16, wf, NULL, P, lws, NULL), VSA_ERR_NULL);
+  EXPECT(vsa_linear_branch(&g, p16, 0, p16, p16, pi, 2, pf, w16, NULL, NULL, P, lws - 1, NULL), VSA_ERR_WORKSPACE);
+  EXPECT(vsa_linear_branch(&g, p16, 3, p16, p16, pi, 2, pf, w16, NULL, NULL, P, lws, NULL), VSA_ERR_LAYOUT);
+  EXPECT(vsa_linear_branch(&g, p16, 0, p16, p16, pi, 2, pf, w16, wf, NULL, P, lws, NULL), VSA_ERR_NULL);
   EXPECT(vsa_sparse_attn_linear_fwd(&g, p16, p16, p16, pi, 0, 0.1f, w16, NULL, P, lws, NULL), VSA_ERR_TOPK);
   const size_t bws = vsa_attn_bwd_workspace_bytes(&g, 2);
   EXPECT(vsa_sparse_attn_bwd(&g, p16, p16, p16, p16, p16, pf, pi, 2, 0.1f, w16, w16, w16, P, bws - 1, NULL),

@@ -41,7 +41,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_abi_version_and_status_text(lib):
-    assert lib.vsa_abi_version() == 3
+    assert lib.vsa_abi_version() == 4
     for code in range(12):
         assert lib.vsa_status_string(code)
     assert lib.vsa_status_string(12345) == b"unknown status"
@@ -121,13 +121,16 @@ def test_entry_points_reject_bad_arguments_before_launch(lib):
     assert lib.vsa_sparse_attn_fwd(g, P, P, P, P, 2, 0.125, P, ODD, None, None) == _lib.VSA_ERR_ALIGN
     # Linear branch.
     lws = lib.vsa_linear_workspace_bytes(g)
-    assert lib.vsa_linear_branch(g, P, P, P, P, 2, None, P, None, None, P, lws, None) == _lib.VSA_ERR_NULL
-    assert lib.vsa_linear_branch(g, P, P, P, P, 2, P, P, None, None, P, lws - 1, None) == _lib.VSA_ERR_WORKSPACE
-    assert lib.vsa_linear_branch(g, P, P, P, P, 99, P, P, None, None, P, lws, None) == _lib.VSA_ERR_TOPK
+    assert lib.vsa_linear_branch(g, P, 0, P, P, P, 2, None, P, None, None, P, lws, None) == _lib.VSA_ERR_NULL
+    assert lib.vsa_linear_branch(g, P, 0, P, P, P, 2, P, P, None, None, P, lws - 1, None) == _lib.VSA_ERR_WORKSPACE
+    assert lib.vsa_linear_branch(g, P, 0, P, P, P, 99, P, P, None, None, P, lws, None) == _lib.VSA_ERR_TOPK
     # The saved O_lin and 1/den come as a pair, 16-byte aligned.
-    assert lib.vsa_linear_branch(g, P, P, P, P, 2, P, P, P, None, P, lws, None) == _lib.VSA_ERR_NULL
-    assert lib.vsa_linear_branch(g, P, P, P, P, 2, P, P, None, P, P, lws, None) == _lib.VSA_ERR_NULL
-    assert lib.vsa_linear_branch(g, P, P, P, P, 2, P, P, ODD, P, P, lws, None) == _lib.VSA_ERR_ALIGN
+    assert lib.vsa_linear_branch(g, P, 0, P, P, P, 2, P, P, P, None, P, lws, None) == _lib.VSA_ERR_NULL
+    assert lib.vsa_linear_branch(g, P, 0, P, P, P, 2, P, P, None, P, P, lws, None) == _lib.VSA_ERR_NULL
+    assert lib.vsa_linear_branch(g, P, 0, P, P, P, 2, P, P, ODD, P, P, lws, None) == _lib.VSA_ERR_ALIGN
+    # Q / output layout: token-major or raster only.
+    assert lib.vsa_linear_branch(g, P, 1, P, P, P, 2, P, P, None, None, P, lws, None) == _lib.VSA_ERR_LAYOUT
+    assert lib.vsa_linear_branch(g, P, 7, P, P, P, 2, P, P, None, None, P, lws, None) == _lib.VSA_ERR_LAYOUT
 
 
 def test_fused_entry_points_reject_bad_arguments(lib):
@@ -197,14 +200,15 @@ def test_raster_entry_point_validation(lib):
     assert lib.vsa_cube_pool(g, ODD, P, None) == _lib.VSA_ERR_ALIGN
     assert lib.vsa_cube_pool(geom(D=16), P, P, None) == _lib.VSA_ERR_HEAD_DIM
     R = _lib.VSA_LAYOUT_RASTER
-    assert lib.vsa_sparse_attn_fwd_raster(g, P, P, R, P, P, 2, 0.125, None, None, None) == _lib.VSA_ERR_NULL
-    assert lib.vsa_sparse_attn_fwd_raster(g, P, ODD, R, P, P, 2, 0.125, P, None, None) == _lib.VSA_ERR_ALIGN
-    assert lib.vsa_sparse_attn_fwd_raster(g, P, P, 1, P, P, 2, 0.125, P, None, None) == _lib.VSA_ERR_LAYOUT
-    assert lib.vsa_sparse_attn_fwd_raster(g, P, P, R, P, P, 0, 0.125, P, None, None) == _lib.VSA_ERR_TOPK
-    assert lib.vsa_sparse_attn_fwd_raster(g, P, P, 0, P, P, 2, 0.0, P, None, None) == _lib.VSA_ERR_SCALE
+    assert lib.vsa_sparse_attn_fwd_raster(g, P, P, R, P, P, 2, 0.125, None, None, None, None) == _lib.VSA_ERR_NULL
+    assert lib.vsa_sparse_attn_fwd_raster(g, P, P, R, P, P, 2, 0.125, None, ODD, None, None) == _lib.VSA_ERR_ALIGN
+    assert lib.vsa_sparse_attn_fwd_raster(g, P, ODD, R, P, P, 2, 0.125, P, None, None, None) == _lib.VSA_ERR_ALIGN
+    assert lib.vsa_sparse_attn_fwd_raster(g, P, P, 1, P, P, 2, 0.125, P, None, None, None) == _lib.VSA_ERR_LAYOUT
+    assert lib.vsa_sparse_attn_fwd_raster(g, P, P, R, P, P, 0, 0.125, P, None, None, None) == _lib.VSA_ERR_TOPK
+    assert lib.vsa_sparse_attn_fwd_raster(g, P, P, 0, P, P, 2, 0.0, P, None, None, None) == _lib.VSA_ERR_SCALE
     # 32-bit buffer offsets: S * heads * D * 2 must stay below 2^31
     huge = geom(B=1, H=512, D=128, grid=(64, 64, 64))
-    assert lib.vsa_sparse_attn_fwd_raster(huge, P, P, R, P, P, 2, 0.125, P, None, None) == _lib.VSA_ERR_GEOMETRY
+    assert lib.vsa_sparse_attn_fwd_raster(huge, P, P, R, P, P, 2, 0.125, P, None, None, None) == _lib.VSA_ERR_GEOMETRY
 
 
 def test_fp8_entry_point_validation(lib):

@@ -1,6 +1,10 @@
 """GPU parity: linear branch and combine (bf16(O_sparse + O_lin)) against the oracle,
 both as two calls (vsa_sparse_attn_fwd with its fp32 output, then
 vsa_linear_branch) and as the single fused pass (vsa_sparse_attn_linear_fwd).
+The two-call chain is also run on raster Q with a raster output
+(vsa_sparse_attn_fwd_raster with its fp32 cube-major output only, then
+vsa_linear_branch with the RASTER layout): bit-identical to the cube-major
+calls followed by the unpermute, in direct mode too.
 The two run the same fp32 sums in the same order; where the compiler fuses
 a multiply and an add in one kernel's combine but not in the other's, the
 fp32 results differ in the last bits, and a few outputs land on the other
@@ -20,6 +24,19 @@ from tests.gpu_util import assert_close, bf16_f64, to_dev
 pytestmark = pytest.mark.gpu
 
 
+def check_raster_chain(vsa, wl, inp, kc, vt, idx_d, of, out):
+    """The layer's two-call chain on raster Q and output equals the cube-major calls bit for bit."""
+    q = to_dev(inp["q"])
+    of_r = torch.full_like(of, float("nan"))
+    o_none, _ = vsa.sparse_attn_fwd_raster(q, kc, vt, idx_d, wl.grid, wl.softmax_scale, out_f32=of_r,
+                                           bf16_out=False)
+    assert o_none is None
+    out_r = vsa.linear_branch(q, kc, vt, idx_d, of_r, wl.grid, raster=True)
+    torch.cuda.synchronize()
+    assert torch.equal(of_r, of), "raster fine stage: fp32 output differs"
+    assert torch.equal(out_r, vsa.cube_unpermute(out, wl.grid)), "raster linear branch differs"
+
+
 def run(wl, inp, idx=None):
     import block_sparse_video_cube_amd as vsa
 
@@ -35,6 +52,7 @@ def run(wl, inp, idx=None):
     _, of, lse = vsa.sparse_attn_fwd(qc, kc, vt, idx_d, wl.grid, scale, want_f32=True, want_lse=True)
     out = vsa.linear_branch(qc, kc, vt, idx_d, of, wl.grid)
     fused, lse_f = vsa.sparse_attn_linear_fwd(qc, kc, vt, idx_d, wl.grid, scale, want_lse=True)
+    check_raster_chain(vsa, wl, inp, kc, vt, idx_d, of, out)
     torch.cuda.synchronize()
     ref_s, _ = oracle.sparse_attention(qc_o, kc_o, vc_o, valid, idx, scale)
     ref_l = oracle.linear_branch(qc_o, kc_o, vc_o, valid, idx)
@@ -89,7 +107,9 @@ def test_hybrid_direct_sum_matches_oracle(over):
     vt = vsa.cube_permute(to_dev(inp["v"]), wl.grid, layout="dim")
     idx_d = torch.from_numpy(idx).to("cuda:0")
     _, of, _ = vsa.sparse_attn_fwd(qc, kc, vt, idx_d, wl.grid, wl.softmax_scale, want_f32=True)
-    got = bf16_f64(vsa.linear_branch(qc, kc, vt, idx_d, of, wl.grid))
+    out = vsa.linear_branch(qc, kc, vt, idx_d, of, wl.grid)
+    check_raster_chain(vsa, wl, inp, kc, vt, idx_d, of, out)
+    got = bf16_f64(out)
     assert_close(got[:, :, valid], ref[:, :, valid], f"hybrid direct {over}")
     with pytest.raises(vsa.VsaError):  # the fused pass takes at most half the cubes
         vsa.sparse_attn_linear_fwd(qc, kc, vt, idx_d, wl.grid, wl.softmax_scale)
