@@ -44,6 +44,8 @@ __all__ = [
     "sta_index",
     "sparse_attn_fwd",
     "linear_branch",
+    "linear_state",
+    "linear_apply",
     "sparse_attn_fwd_raster",
     "sparse_attn_fwd_packed",
     "packed_workspace_bytes",
@@ -519,6 +521,43 @@ def linear_branch(qc: torch.Tensor, kc: torch.Tensor, vt: torch.Tensor, idx: tor
     return (out, (o_lin, inv_den)) if save else out
 
 
+def linear_state(kc: torch.Tensor, vt: torch.Tensor, grid: Sequence[int], workspace: torch.Tensor) -> None:
+    """The linear branch's state pass (vsa_linear_state): phi(K), S_tot and z_tot into `workspace`."""
+    B, Hh, _, D = kc.shape
+    g = make_geom(B, Hh, D, grid)
+    d = geom_dims(g)
+    _need(kc, "kc", torch.bfloat16, (B, Hh, d.rows, D))
+    _need(vt, "vt", torch.bfloat16, (B, Hh, d.n_cubes, D, 64))
+    _lib.check("vsa_linear_state", _lib.load().vsa_linear_state(
+        g, kc.data_ptr(), vt.data_ptr(), workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+        _stream()))
+
+
+def linear_apply(q: torch.Tensor, vt: torch.Tensor, idx: torch.Tensor, o_sparse: torch.Tensor,
+                 grid: Sequence[int], workspace: torch.Tensor, out: Optional[torch.Tensor] = None,
+                 raster: bool = False):
+    """The rest of linear_branch (vsa_linear_apply) on a workspace that
+    linear_state filled for the same keys and values: bf16(o_sparse + O_lin),
+    raster (q and output [B, S, heads, D]) or token-major."""
+    B, Hh, D = vt.shape[0], vt.shape[1], vt.shape[3]
+    g = make_geom(B, Hh, D, grid)
+    d = geom_dims(g)
+    topk = idx.shape[-1]
+    qo_shape = (B, d.tokens, Hh, D) if raster else (B, Hh, d.rows, D)
+    _need(q, "q" if raster else "qc", torch.bfloat16, qo_shape)
+    _need(vt, "vt", torch.bfloat16, (B, Hh, d.n_cubes, D, 64))
+    _need(idx, "idx", torch.int32, (B, Hh, d.n_cubes, topk))
+    _need(o_sparse, "o_sparse", torch.float32, (B, Hh, d.rows, D))
+    if out is None:
+        out = torch.empty(qo_shape, dtype=torch.bfloat16, device=q.device)
+    _need(out, "o" if raster else "oc", torch.bfloat16, qo_shape)
+    _lib.check("vsa_linear_apply", _lib.load().vsa_linear_apply(
+        g, q.data_ptr(), _lib.VSA_LAYOUT_RASTER if raster else _lib.VSA_LAYOUT_TOKEN_MAJOR, vt.data_ptr(),
+        idx.data_ptr(), int(topk), o_sparse.data_ptr(), out.data_ptr(), None, None, workspace.data_ptr(),
+        workspace.numel() * workspace.element_size(), _stream()))
+    return out
+
+
 def linear_branch_bwd(qc: torch.Tensor, kc: torch.Tensor, vc: torch.Tensor, vt: torch.Tensor, idx: torch.Tensor,
                       doc: torch.Tensor, grid: Sequence[int], workspace: Optional[torch.Tensor] = None,
                       add: Optional[Tuple[torch.Tensor, torch.Tensor, torch.Tensor]] = None, out=None,
@@ -711,6 +750,10 @@ class LayerBuffers:
         # Second stream (default priority) for the V permute, which depends on
         # nothing the coarse stage makes and runs beside it.
         self.side = torch.cuda.Stream(device=dev)
+        # Recorded on the side stream after the V permute and after the
+        # linear state pass; the caller's stream waits for each where needed.
+        self.ev_v = torch.cuda.Event()
+        self.ev_state = torch.cuda.Event()
 
 
 def layer_stages(linear: bool = False, fused_linear: bool = False):
@@ -747,8 +790,10 @@ def layer_forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, grid: Seque
     Streams: the V permute runs on a second stream (bufs.side) after the Q and
     K pooling, beside the coarse stage (selection: matrix cores and lane
     arithmetic; the permute: memory traffic); the caller's stream waits for it
-    before the fine stage, so the layer is ordered on the caller's stream as a
-    whole.  The stage marks are taken on the caller's stream (the select stage
+    before the fine stage.  In the hybrid two-call layer the linear branch's
+    state pass follows it there, beside the coarse and fine stages, and the
+    caller's stream waits for it before the rest of the branch.  The layer is
+    thus ordered on the caller's stream as a whole.  The stage marks are taken on the caller's stream (the select stage
     ends once the permute has too).  overlap=False keeps every launch on the
     caller's stream (for per-kernel timings that no other kernel shares).
     """
@@ -791,13 +836,19 @@ def layer_forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, grid: Seque
             cube_permute(v, grid, layout="slots", out=b.vs)
         else:
             cube_permute(v, grid, layout="dim", out=b.vt)
+        b.ev_v.record(side)
+        if linear and not fused_linear:
+            # The linear branch's state (phi(K), S_tot, z_tot) needs only K and
+            # V: it runs here too, beside the coarse and fine stages.
+            linear_state(b.kc, b.vt, grid, b.ws_lin)
+            b.ev_state.record(side)
     mark(1)
     if window is not None:
         # The sliding-tile list is static; it is rebuilt every layer all the same.
         sta_index(grid, window, B, H, head_dim=D, out=b.idx)
     else:
         select_topk_pooled(b.qbar, b.kbar, grid, topk, out=b.idx, workspace=b.ws_sel)
-    main.wait_stream(side)
+    main.wait_event(b.ev_v)
     mark(2)
     if not linear:
         if packed:
@@ -814,6 +865,7 @@ def layer_forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, grid: Seque
         return out, b.idx
     sparse_attn_fwd_raster(q, b.kc, b.vt, b.idx, grid, scale, out_f32=b.of, bf16_out=False)
     mark(3)
-    linear_branch(q, b.kc, b.vt, b.idx, b.of, grid, out=out, workspace=b.ws_lin, raster=True)
+    main.wait_event(b.ev_state)
+    linear_apply(q, b.vt, b.idx, b.of, grid, b.ws_lin, out=out, raster=True)
     mark(4)
     return out, b.idx

@@ -42,6 +42,8 @@ ENTRY_POINTS = (
     "vsa_select_topk_pooled",
     "vsa_sparse_attn_fwd",
     "vsa_linear_branch",
+    "vsa_linear_state",
+    "vsa_linear_apply",
     "vsa_sta_topk",
     "vsa_sta_index",
     "vsa_cube_pool",
@@ -125,6 +127,8 @@ def load() -> ctypes.CDLL:
         "vsa_select_topk": (i32, [G, P, P, i32, P, P, sz, P]),
         "vsa_sparse_attn_fwd": (i32, [G, P, P, P, P, i32, ctypes.c_float, P, P, P, P]),
         "vsa_linear_branch": (i32, [G, P, i32, P, P, P, i32, P, P, P, P, P, sz, P]),
+        "vsa_linear_state": (i32, [G, P, P, P, sz, P]),
+        "vsa_linear_apply": (i32, [G, P, i32, P, P, i32, P, P, P, P, P, sz, P]),
         "vsa_sta_topk": (i32, [G, i32, i32, i32]),
         "vsa_sta_index": (i32, [G, i32, i32, i32, P, P]),
         "vsa_cube_pool": (i32, [G, P, P, P]),

@@ -448,6 +448,37 @@ int32_t vsa_mfma_probe(int32_t blocks, int32_t iters, float* sink, uint64_t* clk
                                               static_cast<hipStream_t>(stream)));
 }
 
+int32_t vsa_linear_state(const vsa_geom* g, const uint16_t* kc, const uint16_t* vt, void* ws, size_t ws_bytes,
+                         void* stream) {
+  vsa_dims d;
+  vsa::KGeom k;
+  int32_t st = prepare(g, &d, &k);
+  if (st != VSA_OK) return st;
+  if (!kc || !vt || !ws) return VSA_ERR_NULL;
+  if (!aligned16(kc) || !aligned16(vt) || !aligned16(ws)) return VSA_ERR_ALIGN;
+  if (ws_bytes < vsa::linear_workspace_bytes(k)) return VSA_ERR_WORKSPACE;
+  return launch_status(vsa::launch_lin_prep(k, kc, vt, ws, static_cast<hipStream_t>(stream)));
+}
+
+int32_t vsa_linear_apply(const vsa_geom* g, const uint16_t* qc, int32_t qo_layout, const uint16_t* vt,
+                         const int32_t* idx, int32_t topk, const float* o_sparse, uint16_t* oc, float* o_lin,
+                         float* inv_den, void* ws, size_t ws_bytes, void* stream) {
+  vsa_dims d;
+  vsa::KGeom k;
+  int32_t st = prepare(g, &d, &k);
+  if (st != VSA_OK) return st;
+  if (!qc || !vt || !idx || !o_sparse || !oc || !ws) return VSA_ERR_NULL;
+  if (!o_lin != !inv_den) return VSA_ERR_NULL;
+  if (!aligned16(qc) || !aligned16(vt) || !aligned16(idx) || !aligned16(o_sparse) || !aligned16(oc) ||
+      !aligned16(ws) || (o_lin && !aligned16(o_lin)) || (inv_den && !aligned16(inv_den)))
+    return VSA_ERR_ALIGN;
+  if (topk < 1 || topk > d.n_cubes) return VSA_ERR_TOPK;
+  if (qo_layout != VSA_LAYOUT_TOKEN_MAJOR && qo_layout != VSA_LAYOUT_RASTER) return VSA_ERR_LAYOUT;
+  if (ws_bytes < vsa::linear_workspace_bytes(k)) return VSA_ERR_WORKSPACE;
+  return launch_status(vsa::launch_linear_apply(k, qc, vt, idx, topk, o_sparse, oc, o_lin, inv_den,
+                                                qo_layout == VSA_LAYOUT_RASTER, ws, static_cast<hipStream_t>(stream)));
+}
+
 int32_t vsa_linear_branch(const vsa_geom* g, const uint16_t* qc, int32_t qo_layout, const uint16_t* kc,
                           const uint16_t* vt, const int32_t* idx, int32_t topk, const float* o_sparse, uint16_t* oc,
                           float* o_lin, float* inv_den, void* ws, size_t ws_bytes, void* stream) {

@@ -134,6 +134,11 @@ hipError_t launch_attn_fwd_packed(const KGeom& g, const uint16_t* q, bool raster
 hipError_t launch_linear(const KGeom& g, const uint16_t* qc, const uint16_t* kc, const uint16_t* vt,
                          const int32_t* idx, int topk, const float* o_sparse, uint16_t* oc, float* o_lin,
                          float* inv_den, bool raster, void* ws, hipStream_t s);
+// launch_linear without the state pass: ws must hold phi(K), S_tot and z_tot
+// from launch_lin_prep (write_fk) for the same keys and values.
+hipError_t launch_linear_apply(const KGeom& g, const uint16_t* qc, const uint16_t* vt, const int32_t* idx, int topk,
+                               const float* o_sparse, uint16_t* oc, float* o_lin, float* inv_den, bool raster,
+                               void* ws, hipStream_t s);
 size_t linear_workspace_bytes(const KGeom& g);
 // The parts of the linear workspace the selected-block correction reads:
 // phi(K) token-major bf16 [B, H, Np, D], S_tot^T as bf16 hi + lo [B, H, D, D],

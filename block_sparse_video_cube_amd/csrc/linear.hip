@@ -623,6 +623,12 @@ hipError_t launch_linear(const KGeom& g, const uint16_t* qc, const uint16_t* kc,
                          float* inv_den, bool raster, void* ws, hipStream_t s) {
   hipError_t e = launch_lin_prep(g, kc, vt, ws, s);
   if (e != hipSuccess) return e;
+  return launch_linear_apply(g, qc, vt, idx, topk, o_sparse, oc, o_lin, inv_den, raster, ws, s);
+}
+
+hipError_t launch_linear_apply(const KGeom& g, const uint16_t* qc, const uint16_t* vt, const int32_t* idx, int topk,
+                               const float* o_sparse, uint16_t* oc, float* o_lin, float* inv_den, bool raster,
+                               void* ws, hipStream_t s) {
   const LinWs w = carve(g, ws, nullptr);
   const int direct = launch_complement(g, idx, topk, w, s);
   if (g.D == 64)

@@ -382,6 +382,24 @@ int32_t vsa_linear_branch(const vsa_geom* g, const uint16_t* qc, int32_t qo_layo
                           const float* o_sparse, uint16_t* oc, float* o_lin, float* inv_den,
                           void* ws, size_t ws_bytes, void* stream);
 
+/* The linear branch in two parts, so that the state pass (which reads only
+ * K and V) can run on another stream beside the coarse and fine stages:
+ * vsa_linear_state computes phi(K), S_tot and z_tot of every (b, h) into ws
+ * (kc TOKEN_MAJOR, vt DIM_MAJOR, as for vsa_linear_branch); ws keeps them
+ * until it is overwritten.  vsa_linear_apply then runs the rest of
+ * vsa_linear_branch (same arguments, without kc) on a ws that
+ * vsa_linear_state filled for the same kc and vt; the pair gives results
+ * bit-identical to vsa_linear_branch.  ws: at least
+ * vsa_linear_workspace_bytes(g) bytes for both.  The caller orders the two
+ * (vsa_linear_apply must run after vsa_linear_state completes on ws).
+ * Errors as vsa_linear_branch. */
+int32_t vsa_linear_state(const vsa_geom* g, const uint16_t* kc, const uint16_t* vt, void* ws,
+                         size_t ws_bytes, void* stream);
+int32_t vsa_linear_apply(const vsa_geom* g, const uint16_t* qc, int32_t qo_layout,
+                         const uint16_t* vt, const int32_t* idx, int32_t topk,
+                         const float* o_sparse, uint16_t* oc, float* o_lin, float* inv_den,
+                         void* ws, size_t ws_bytes, void* stream);
+
 /* Fine stage and linear branch in one pass:
  * oc = bf16(O_sparse + O_lin), the result of vsa_sparse_attn_fwd followed by
  * vsa_linear_branch, without the fp32 O_sparse round trip and without reading

@@ -122,6 +122,9 @@ int main() {
   const size_t lws = vsa_linear_workspace_bytes(&g);
   EXPECT(vsa_linear_branch(&g, p16, 0, p16, p16, pi, 2, pf, w16, NULL, NULL, P, lws - 1, NULL), VSA_ERR_WORKSPACE);
   EXPECT(vsa_linear_branch(&g, p16, 3, p16, p16, pi, 2, pf, w16, NULL, NULL, P, lws, NULL), VSA_ERR_LAYOUT);
+  EXPECT(vsa_linear_state(&g, p16, p16, P, lws - 1, NULL), VSA_ERR_WORKSPACE);
+  EXPECT(vsa_linear_apply(&g, p16, 5, p16, pi, 2, pf, w16, NULL, NULL, P, lws, NULL), VSA_ERR_LAYOUT);
+  EXPECT(vsa_linear_apply(&g, p16, 0, p16, pi, 2, pf, w16, wf, NULL, P, lws, NULL), VSA_ERR_NULL);
   EXPECT(vsa_linear_branch(&g, p16, 0, p16, p16, pi, 2, pf, w16, wf, NULL, P, lws, NULL), VSA_ERR_NULL);
   EXPECT(vsa_sparse_attn_linear_fwd(&g, p16, p16, p16, pi, 0, 0.1f, w16, NULL, P, lws, NULL), VSA_ERR_TOPK);
   const size_t bws = vsa_attn_bwd_workspace_bytes(&g, 2);

@@ -128,6 +128,17 @@ def test_entry_points_reject_bad_arguments_before_launch(lib):
     assert lib.vsa_linear_branch(g, P, 0, P, P, P, 2, P, P, P, None, P, lws, None) == _lib.VSA_ERR_NULL
     assert lib.vsa_linear_branch(g, P, 0, P, P, P, 2, P, P, None, P, P, lws, None) == _lib.VSA_ERR_NULL
     assert lib.vsa_linear_branch(g, P, 0, P, P, P, 2, P, P, ODD, P, P, lws, None) == _lib.VSA_ERR_ALIGN
+    # The branch in two parts.
+    assert lib.vsa_linear_state(g, None, P, P, lws, None) == _lib.VSA_ERR_NULL
+    assert lib.vsa_linear_state(g, P, ODD, P, lws, None) == _lib.VSA_ERR_ALIGN
+    assert lib.vsa_linear_state(g, P, P, P, lws - 1, None) == _lib.VSA_ERR_WORKSPACE
+    assert lib.vsa_linear_state(geom(D=32), P, P, P, lws, None) == _lib.VSA_ERR_HEAD_DIM
+    assert lib.vsa_linear_apply(g, P, 0, P, P, 2, None, P, None, None, P, lws, None) == _lib.VSA_ERR_NULL
+    assert lib.vsa_linear_apply(g, P, 0, P, P, 2, P, P, P, None, P, lws, None) == _lib.VSA_ERR_NULL
+    assert lib.vsa_linear_apply(g, P, 0, P, P, 2, P, ODD, None, None, P, lws, None) == _lib.VSA_ERR_ALIGN
+    assert lib.vsa_linear_apply(g, P, 0, P, P, 0, P, P, None, None, P, lws, None) == _lib.VSA_ERR_TOPK
+    assert lib.vsa_linear_apply(g, P, 1, P, P, 2, P, P, None, None, P, lws, None) == _lib.VSA_ERR_LAYOUT
+    assert lib.vsa_linear_apply(g, P, 2, P, P, 2, P, P, None, None, P, lws - 1, None) == _lib.VSA_ERR_WORKSPACE
     # Q / output layout: token-major or raster only.
     assert lib.vsa_linear_branch(g, P, 1, P, P, P, 2, P, P, None, None, P, lws, None) == _lib.VSA_ERR_LAYOUT
     assert lib.vsa_linear_branch(g, P, 7, P, P, P, 2, P, P, None, None, P, lws, None) == _lib.VSA_ERR_LAYOUT

@@ -4,7 +4,8 @@ vsa_linear_branch) and as the single fused pass (vsa_sparse_attn_linear_fwd).
 The two-call chain is also run on raster Q with a raster output
 (vsa_sparse_attn_fwd_raster with its fp32 cube-major output only, then
 vsa_linear_branch with the RASTER layout): bit-identical to the cube-major
-calls followed by the unpermute, in direct mode too.
+calls followed by the unpermute, in direct mode too; and the branch split
+into vsa_linear_state and vsa_linear_apply is bit-identical to the one call.
 The two run the same fp32 sums in the same order; where the compiler fuses
 a multiply and an add in one kernel's combine but not in the other's, the
 fp32 results differ in the last bits, and a few outputs land on the other
@@ -35,6 +36,16 @@ def check_raster_chain(vsa, wl, inp, kc, vt, idx_d, of, out):
     torch.cuda.synchronize()
     assert torch.equal(of_r, of), "raster fine stage: fp32 output differs"
     assert torch.equal(out_r, vsa.cube_unpermute(out, wl.grid)), "raster linear branch differs"
+    # The branch in two parts (state pass, then the rest) on a fresh workspace.
+    g = vsa.make_geom(wl.batch, wl.heads, wl.head_dim, wl.grid)
+    ws = torch.full((vsa.workspace_bytes(g, linear=True),), 0xA5, dtype=torch.uint8, device="cuda:0")
+    vsa.linear_state(kc, vt, wl.grid, ws)
+    out_a = vsa.linear_apply(q, vt, idx_d, of, wl.grid, ws, raster=True)
+    qc = vsa.cube_permute(q, wl.grid)
+    out_c = vsa.linear_apply(qc, vt, idx_d, of, wl.grid, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(out_a, out_r), "state + apply (raster) differs from the one call"
+    assert torch.equal(out_c, out), "state + apply (token-major) differs from the one call"
 
 
 def run(wl, inp, idx=None):
