@@ -382,8 +382,11 @@ int32_t vsa_linear_branch(const vsa_geom* g, const uint16_t* qc, int32_t qo_layo
                           const float* o_sparse, uint16_t* oc, float* o_lin, float* inv_den,
                           void* ws, size_t ws_bytes, void* stream);
 
-/* The linear branch in two parts, so that the state pass (which reads only
- * K and V) can run on another stream beside the coarse and fine stages:
+/* The linear branch (the linear-attention branch beside the sparse one:
+ * SparkDiffusion article, paragraph 3, RoLA; TurboDiffusion article, section
+ * "稀疏、蒸馏与全链路量化", SLA) in two parts, so that the state pass (which
+ * reads only K and V) can run on another stream beside the coarse and fine
+ * stages:
  * vsa_linear_state computes phi(K), S_tot and z_tot of every (b, h) into ws
  * (kc TOKEN_MAJOR, vt DIM_MAJOR, as for vsa_linear_branch); ws keeps them
  * until it is overwritten.  vsa_linear_apply then runs the rest of
