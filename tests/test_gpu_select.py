@@ -3,6 +3,10 @@
 Bit-exact on integer-valued inputs (all fp32 sums exact on both sides, exact
 ties resolved to the lower cube index); on float inputs every GPU row must be
 a valid top-k of the oracle's fp64 scores up to a relative 1e-5 near-tie band.
+Crafted score rows (exactly representable) put 1 to 90 keys in the 16-bit
+bucket of the k-th largest score, with and without ties, so that both paths
+of the top-k search (bucket compacted to one key per lane, or searched over
+all keys) are checked against the oracle bit for bit.
 """
 
 import numpy as np
@@ -180,3 +184,38 @@ def test_cube_means_identical_across_entry_points(grid, D):
     assert torch.equal(means[:n].view_as(qbar), qbar)
     assert torch.equal(means[n:].view_as(kbar), kbar)
     assert torch.equal(vsa.select_topk_pooled(qbar, kbar, wl.grid, wl.topk), idx)
+
+
+# Crafted scores through vsa_select_topk_pooled: with qbar = e0 every score
+# row is kbar[:, 0] exactly (fp32 products by 1).  A cluster of keys shares
+# the upper 16 bits of the k-th largest score (values 1 + 8 j ulp apart), the
+# rest lie far below or above it.  The search compacts that bucket when it
+# holds at most 64 keys and searches all keys otherwise; both must give the
+# oracle's rows, ties to the lower index included.
+@pytest.mark.parametrize("bucket,above,ties", [(63, 10, False), (64, 10, False), (65, 10, False), (90, 30, False),
+                                               (64, 0, True), (70, 5, True), (1, 40, False)])
+def test_topk_bucket_sizes_around_64(bucket, above, ties):
+    import torch
+
+    import block_sparse_video_cube_amd as vsa
+
+    grid, D, nc = (16, 32, 32), 64, 256
+    assert oracle.n_cubes(grid) == nc
+    rng = np.random.default_rng(bucket * 7 + above)
+    perm = rng.permutation(nc)
+    s = np.full(nc, 0.5, dtype=np.float32)
+    s[perm[:above]] = 2.0 + np.arange(above, dtype=np.float32)            # clearly above the bucket
+    cluster = perm[above:above + bucket]
+    if ties:
+        s[cluster] = np.float32(1.0) + np.float32(2.0 ** -20) * (np.arange(bucket) // 4).astype(np.float32)
+    else:
+        s[cluster] = np.float32(1.0) + np.float32(2.0 ** -20) * np.arange(bucket, dtype=np.float32)
+    kbar = np.zeros((1, 1, nc, D), dtype=np.float32)
+    kbar[0, 0, :, 0] = s
+    qbar = np.zeros((1, 1, nc, D), dtype=np.float32)
+    qbar[0, 0, :, 0] = 1.0
+    for topk in sorted({above + 1, above + bucket // 2, above + bucket, min(nc, above + bucket + 3)}):
+        got = vsa.select_topk_pooled(torch.from_numpy(qbar).to("cuda:0"), torch.from_numpy(kbar).to("cuda:0"),
+                                     grid, topk).cpu().numpy()
+        want = oracle.topk_row(s.astype(np.float64), topk)
+        assert np.all(got[0, 0] == want[None, :]), (bucket, above, ties, topk)
