@@ -304,7 +304,8 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd(const uint16_t* __restri
   const float inv = 1.f / l_tot;
   const float c0 = a0 * inv, c1 = a1 * inv;
   const long long row = bh * g.Np + 64LL * i + q;
-  uint16_t* orow = RASTER ? oc + qtok : oc + row * D;
+  // oc may be null (RASTER with only the fp32 output wanted): no pointer is formed from it then.
+  uint16_t* orow = oc ? (RASTER ? oc + qtok : oc + row * D) : nullptr;
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
@@ -316,7 +317,7 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd(const uint16_t* __restri
         const int r = 4 * gq + e;
         v[e] = o[dt][r] * c0 + xo[(dt * 16 + r) * 64 + lane] * c1;
       }
-      if (qvalid && oc) *reinterpret_cast<uint2*>(orow + d) = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+      if (qvalid && orow) *reinterpret_cast<uint2*>(orow + d) = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
       if (oc_f32) *reinterpret_cast<float4*>(oc_f32 + row * D + d) = make_float4(v[0], v[1], v[2], v[3]);
     }
   if (lse && hf == 0) lse[row] = m * scale + logf(l_tot);
