@@ -51,7 +51,8 @@ def parse():
                     help="let the fine stage gather K tiles from raster rows too (no K permute)")
     ap.add_argument("--unpacked", action="store_true",
                     help="the unpacked fine stage (one 64-key tile per selected cube, K token-major, V "
-                         "cube-transposed) instead of the packed one (cubes with few valid keys share tiles)")
+                         "cube-transposed) instead of the packed one (cubes with few valid keys share tiles); "
+                         "with --fp8 the unpacked fp8 stage")
     ap.add_argument("--one-stream", action="store_true",
                     help="every launch on one stream (the V permute otherwise runs on a second stream beside the "
                          "coarse stage); for per-kernel traces whose durations no other kernel shares")
@@ -368,14 +369,21 @@ def main():
         # Q, K quantized per cube and V per channel in the step; the fp8 fine
         # stage writes the raster-order output itself.
         stages = ["quant", "select", "fine"]
+        # On grids with partial cubes the packed fp8 stage (edge cubes share
+        # tiles; K codes in compact rows, V codes in 16-key slots), as the bf16
+        # layer does; full grids keep the unpacked one.
+        fp8_packed = any(int(x) % 4 for x in wl.grid) and not args.unpacked
         fp8_bufs = (torch.empty((B, H, d.rows, D), dtype=torch.uint8, device=dev),
                     torch.empty((B, H, d.n_cubes), dtype=torch.float32, device=dev),
                     torch.empty((B, H, d.rows, D), dtype=torch.uint8, device=dev),
                     torch.empty((B, H, d.n_cubes), dtype=torch.float32, device=dev),
-                    torch.empty((B, H, d.n_cubes, D, 64), dtype=torch.uint8, device=dev),
+                    torch.empty((B, H, d.n_cubes, 4, D, 16) if fp8_packed else (B, H, d.n_cubes, D, 64),
+                                dtype=torch.uint8, device=dev),
                     torch.empty((B, H, D), dtype=torch.float32, device=dev),
                     qbar if wl.pattern != "sta" else None, kbar if wl.pattern != "sta" else None)
         ws_q = torch.empty(vsa.quant_fp8_workspace_bytes(g), dtype=torch.uint8, device=dev)
+        nplan = vsa.packed_workspace_bytes(g, wl.topk) if fp8_packed else 0
+        ws_plan8 = torch.empty(nplan, dtype=torch.uint8, device=dev) if nplan else None
 
     def step_fp8(ev=None):
         def mark(i):
@@ -385,14 +393,19 @@ def main():
         mark(0)
         # One pass over Q, K, V: codes, scales, the cube means of Q and K for the
         # coarse stage, V's channel maxima; a second pass for V's codes.
-        q8, qs, k8, ks, v8t, vs, _, _ = vsa.quant_fp8(q, k, v, wl.grid, out=fp8_bufs, workspace=ws_q)
+        q8, qs, k8, ks, v8t, vs, _, _ = vsa.quant_fp8(q, k, v, wl.grid, out=fp8_bufs, workspace=ws_q,
+                                                      packed=fp8_packed)
         mark(1)
         if wl.pattern == "sta":
             vsa.sta_index(wl.grid, wl.window, B, H, head_dim=D, out=idx)
         else:
             vsa.select_topk_pooled(qbar, kbar, wl.grid, wl.topk, out=idx, workspace=ws_sel)
         mark(2)
-        vsa.sparse_attn_fwd_fp8(q8, qs, k8, ks, v8t, vs, idx, wl.grid, wl.softmax_scale, out=o, raster=True)
+        if fp8_packed:
+            vsa.sparse_attn_fwd_fp8_packed(q8, qs, k8, ks, v8t, vs, idx, wl.grid, wl.softmax_scale, out=o,
+                                           raster=True, workspace=ws_plan8)
+        else:
+            vsa.sparse_attn_fwd_fp8(q8, qs, k8, ks, v8t, vs, idx, wl.grid, wl.softmax_scale, out=o, raster=True)
         mark(3)
 
     def step(ev=None):
@@ -472,7 +485,9 @@ def main():
             "latent_grid": list(wl.grid), "padded_grid": list(wl.padded_grid),
             "tokens": wl.tokens, "n_cubes": wl.n_cubes, "topk": wl.topk,
             "sparsity": wl.sparsity, "linear_branch": wl.linear, "pattern": wl.pattern,
-            "layout": ("cube-major" if wl.linear else "raster q, k, v in; fp8 cube-major codes; raster o"
+            "layout": ("cube-major" if wl.linear else ("raster q, k, v in; fp8 cube-major codes" +
+                                                     ("; packed tiles: compact k, slot-layout v" if args.fp8 and
+                                                      fp8_packed else "") + "; raster o")
                        if args.fp8 else ("raster q/k/o" if args.k_raster else
                                          "raster q/o" + ("" if args.unpacked else
                                                          "; packed tiles: compact k, slot-layout v"))),

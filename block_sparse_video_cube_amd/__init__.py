@@ -55,6 +55,7 @@ __all__ = [
     "quant_fp8_workspace_bytes",
     "quant_fp8_noalloc",
     "sparse_attn_fwd_fp8",
+    "sparse_attn_fwd_fp8_packed",
     "vsa_attention",
     "workspace_bytes",
     "mfma_probe",
@@ -362,7 +363,7 @@ def quant_fp8_workspace_bytes(g: VsaGeom) -> int:
 
 
 def quant_fp8(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, grid: Sequence[int], want_means: bool = False,
-              out=None, workspace: Optional[torch.Tensor] = None, noalloc: bool = False):
+              out=None, workspace: Optional[torch.Tensor] = None, noalloc: bool = False, packed: bool = False):
     """E4M3 codes of raster Q, K (per (b, h, cube)) and V (per (b, h, channel)).
 
     Returns (q8, qscale, k8, kscale, v8t, vscale, qmean, kmean): codes uint8
@@ -371,6 +372,8 @@ def quant_fp8(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, grid: Sequence[
     tuple of the same eight tensors to write into (means may be None).
     noalloc: use vsa_quant_fp8_noalloc (the library's static scratch instead
     of a workspace; with `out` given, nothing is allocated).
+    packed: vsa_quant_fp8_packed, the layouts of the packed fp8 stage: K codes
+    in compact cube-major rows, V codes [B, heads, Nc, 4, D, 16] (slots).
     """
     B, S, Hh, D = q.shape
     g = make_geom(B, Hh, D, grid)
@@ -383,13 +386,15 @@ def quant_fp8(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, grid: Sequence[
         f32 = dict(dtype=torch.float32, device=dev)
         out = (torch.empty((B, Hh, d.rows, D), **u8), torch.empty((B, Hh, d.n_cubes), **f32),
                torch.empty((B, Hh, d.rows, D), **u8), torch.empty((B, Hh, d.n_cubes), **f32),
-               torch.empty((B, Hh, d.n_cubes, D, 64), **u8), torch.empty((B, Hh, D), **f32),
+               torch.empty((B, Hh, d.n_cubes, 4, D, 16) if packed else (B, Hh, d.n_cubes, D, 64), **u8),
+               torch.empty((B, Hh, D), **f32),
                torch.empty((B, Hh, d.n_cubes, D), **f32) if want_means else None,
                torch.empty((B, Hh, d.n_cubes, D), **f32) if want_means else None)
     q8, qs, k8, ks, v8t, vs, qm, km = out
     _need(q8, "q8", torch.uint8, (B, Hh, d.rows, D))
     _need(k8, "k8", torch.uint8, (B, Hh, d.rows, D))
-    _need(v8t, "v8t", torch.uint8, (B, Hh, d.n_cubes, D, 64))
+    _need(v8t, "v8s" if packed else "v8t", torch.uint8,
+          (B, Hh, d.n_cubes, 4, D, 16) if packed else (B, Hh, d.n_cubes, D, 64))
     _need(qs, "qscale", torch.float32, (B, Hh, d.n_cubes))
     _need(ks, "kscale", torch.float32, (B, Hh, d.n_cubes))
     _need(vs, "vscale", torch.float32, (B, Hh, D))
@@ -397,6 +402,8 @@ def quant_fp8(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, grid: Sequence[
         if t is not None:
             _need(t, n, torch.float32, (B, Hh, d.n_cubes, D))
     lib = _lib.load()
+    if noalloc and packed:
+        raise ValueError("quant_fp8: the allocation-free entry point writes the unpacked layouts only")
     if noalloc:
         _lib.check("vsa_quant_fp8_noalloc", lib.vsa_quant_fp8_noalloc(
             g, q.data_ptr(), k.data_ptr(), v.data_ptr(), q8.data_ptr(), qs.data_ptr(), k8.data_ptr(),
@@ -406,7 +413,8 @@ def quant_fp8(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, grid: Sequence[
     nbytes = lib.vsa_quant_fp8_workspace_bytes(g)
     if workspace is None:
         workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=dev)
-    _lib.check("vsa_quant_fp8", lib.vsa_quant_fp8(
+    fn = "vsa_quant_fp8_packed" if packed else "vsa_quant_fp8"
+    _lib.check(fn, getattr(lib, fn)(
         g, q.data_ptr(), k.data_ptr(), v.data_ptr(), q8.data_ptr(), qs.data_ptr(), k8.data_ptr(), ks.data_ptr(),
         v8t.data_ptr(), vs.data_ptr(), qm.data_ptr() if qm is not None else None,
         km.data_ptr() if km is not None else None, workspace.data_ptr(),
@@ -449,6 +457,44 @@ def sparse_attn_fwd_fp8(q8: torch.Tensor, qscale: torch.Tensor, k8: torch.Tensor
         g, q8.data_ptr(), qscale.data_ptr(), k8.data_ptr(), kscale.data_ptr(), v8t.data_ptr(), vscale.data_ptr(),
         idx.data_ptr(), topk, float(scale), layout, out.data_ptr(), lse.data_ptr() if lse is not None else None,
         _stream()))
+    return out, lse
+
+
+def sparse_attn_fwd_fp8_packed(q8: torch.Tensor, qscale: torch.Tensor, k8c: torch.Tensor, kscale: torch.Tensor,
+                               v8s: torch.Tensor, vscale: torch.Tensor, idx: torch.Tensor, grid: Sequence[int],
+                               scale: Optional[float] = None, want_lse: bool = False,
+                               out: Optional[torch.Tensor] = None, raster: bool = False,
+                               workspace: Optional[torch.Tensor] = None):
+    """fp8 fine stage on packed tiles (vsa_sparse_attn_fwd_fp8_packed), on the
+    layouts of quant_fp8(packed=True).  Returns (o bf16, lse or None) as
+    sparse_attn_fwd_fp8.  workspace: the packing plan (packed_workspace_bytes)."""
+    B, Hh, Np, D = q8.shape
+    g = make_geom(B, Hh, D, grid)
+    d = geom_dims(g)
+    topk = int(idx.shape[-1])
+    _need(q8, "q8", torch.uint8, (B, Hh, d.rows, D))
+    _need(k8c, "k8c", torch.uint8, (B, Hh, d.rows, D))
+    _need(v8s, "v8s", torch.uint8, (B, Hh, d.n_cubes, 4, D, 16))
+    _need(qscale, "qscale", torch.float32, (B, Hh, d.n_cubes))
+    _need(kscale, "kscale", torch.float32, (B, Hh, d.n_cubes))
+    _need(vscale, "vscale", torch.float32, (B, Hh, D))
+    _need(idx, "idx", torch.int32, (B, Hh, d.n_cubes, topk))
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    oshape = (B, d.tokens, Hh, D) if raster else (B, Hh, d.rows, D)
+    if out is None:
+        out = torch.empty(oshape, dtype=torch.bfloat16, device=q8.device)
+    _need(out, "o", torch.bfloat16, oshape)
+    lse = torch.empty((B, Hh, d.rows), dtype=torch.float32, device=q8.device) if want_lse else None
+    nbytes = packed_workspace_bytes(g, topk)
+    if workspace is None and nbytes:
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=q8.device)
+    layout = _lib.VSA_LAYOUT_RASTER if raster else _lib.VSA_LAYOUT_TOKEN_MAJOR
+    _lib.check("vsa_sparse_attn_fwd_fp8_packed", _lib.load().vsa_sparse_attn_fwd_fp8_packed(
+        g, q8.data_ptr(), qscale.data_ptr(), k8c.data_ptr(), kscale.data_ptr(), v8s.data_ptr(), vscale.data_ptr(),
+        idx.data_ptr(), topk, float(scale), layout, out.data_ptr(), lse.data_ptr() if lse is not None else None,
+        workspace.data_ptr() if workspace is not None else None,
+        workspace.numel() * workspace.element_size() if workspace is not None else 0, _stream()))
     return out, lse
 
 

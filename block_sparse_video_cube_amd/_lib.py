@@ -52,7 +52,9 @@ ENTRY_POINTS = (
     "vsa_sparse_attn_bwd",
     "vsa_quant_fp8_workspace_bytes",
     "vsa_quant_fp8",
+    "vsa_quant_fp8_packed",
     "vsa_sparse_attn_fwd_fp8",
+    "vsa_sparse_attn_fwd_fp8_packed",
     "vsa_sparse_attn_linear_fwd",
     "vsa_mfma_probe",
     "vsa_hbm_probe",
@@ -137,6 +139,8 @@ def load() -> ctypes.CDLL:
         "vsa_quant_fp8_workspace_bytes": (sz, [G]),
         "vsa_quant_fp8": (i32, [G, P, P, P, P, P, P, P, P, P, P, P, P, sz, P]),
         "vsa_sparse_attn_fwd_fp8": (i32, [G, P, P, P, P, P, P, P, i32, ctypes.c_float, i32, P, P, P]),
+        "vsa_quant_fp8_packed": (i32, [G, P, P, P, P, P, P, P, P, P, P, P, P, sz, P]),
+        "vsa_sparse_attn_fwd_fp8_packed": (i32, [G, P, P, P, P, P, P, P, i32, ctypes.c_float, i32, P, P, P, sz, P]),
         "vsa_sparse_attn_linear_fwd": (i32, [G, P, P, P, P, i32, ctypes.c_float, P, P, P, sz, P]),
         "vsa_sparse_attn_bwd": (i32, [G, P, P, P, P, P, P, P, i32, ctypes.c_float, P, P, P, P, sz, P]),
         "vsa_mfma_probe": (i32, [i32, i32, P, P, P]),

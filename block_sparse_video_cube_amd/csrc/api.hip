@@ -265,6 +265,24 @@ int32_t vsa_quant_fp8(const vsa_geom* g, const uint16_t* q, const uint16_t* k, c
                                          static_cast<hipStream_t>(stream)));
 }
 
+int32_t vsa_quant_fp8_packed(const vsa_geom* g, const uint16_t* q, const uint16_t* k, const uint16_t* v, uint8_t* q8,
+                             float* qscale, uint8_t* k8c, float* kscale, uint8_t* v8s, float* vscale, float* qmean,
+                             float* kmean, void* ws, size_t ws_bytes, void* stream) {
+  vsa_dims d;
+  vsa::KGeom kg;
+  int32_t st = prepare(g, &d, &kg);
+  if (st != VSA_OK) return st;
+  const void* ptrs[] = {q, k, v, q8, qscale, k8c, kscale, v8s, vscale, ws};
+  for (const void* p : ptrs)
+    if (!p) return VSA_ERR_NULL;
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return VSA_ERR_ALIGN;
+  if ((qmean && !aligned16(qmean)) || (kmean && !aligned16(kmean))) return VSA_ERR_ALIGN;
+  if (ws_bytes < vsa::quant_workspace_bytes(kg)) return VSA_ERR_WORKSPACE;
+  return launch_status(vsa::launch_quant(kg, q, k, v, q8, qscale, k8c, kscale, v8s, vscale, qmean, kmean, ws,
+                                         static_cast<hipStream_t>(stream), true));
+}
+
 int32_t vsa_quant_fp8_noalloc(const vsa_geom* g, const uint16_t* q, const uint16_t* k, const uint16_t* v,
                               uint8_t* q8, float* qscale, uint8_t* k8, float* kscale, uint8_t* v8t, float* vscale,
                               float* qmean, float* kmean, void* stream) {
@@ -305,6 +323,35 @@ int32_t vsa_sparse_attn_fwd_fp8(const vsa_geom* g, const uint8_t* q8, const floa
   return launch_status(vsa::launch_attn_fwd_fp8(k, q8, qscale, k8, kscale, v8t, vscale, idx, topk, softmax_scale,
                                                 o_layout == VSA_LAYOUT_RASTER, o, lse,
                                                 static_cast<hipStream_t>(stream)));
+}
+
+int32_t vsa_sparse_attn_fwd_fp8_packed(const vsa_geom* g, const uint8_t* q8, const float* qscale, const uint8_t* k8c,
+                                       const float* kscale, const uint8_t* v8s, const float* vscale,
+                                       const int32_t* idx, int32_t topk, float softmax_scale, int32_t o_layout,
+                                       uint16_t* o, float* lse, void* ws, size_t ws_bytes, void* stream) {
+  vsa_dims d;
+  vsa::KGeom k;
+  int32_t st = prepare(g, &d, &k);
+  if (st != VSA_OK) return st;
+  if (d.n_cubes >= (1 << 23)) return VSA_ERR_GEOMETRY;  // slot codes hold the cube index in 23 bits
+  const void* ptrs[] = {q8, qscale, k8c, kscale, v8s, vscale, idx, o};
+  for (const void* p : ptrs)
+    if (!p) return VSA_ERR_NULL;
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return VSA_ERR_ALIGN;
+  if (lse && !aligned16(lse)) return VSA_ERR_ALIGN;
+  if (topk < 1 || topk > d.n_cubes) return VSA_ERR_TOPK;
+  if (!(softmax_scale > 0.f) || !isfinite(softmax_scale)) return VSA_ERR_SCALE;
+  if (o_layout != VSA_LAYOUT_TOKEN_MAJOR && o_layout != VSA_LAYOUT_RASTER) return VSA_ERR_LAYOUT;
+  const size_t need = vsa::attn_packed_workspace_bytes(k, topk);
+  if (need) {
+    if (!ws) return VSA_ERR_NULL;
+    if (!aligned16(ws)) return VSA_ERR_ALIGN;
+    if (ws_bytes < need) return VSA_ERR_WORKSPACE;
+  }
+  return launch_status(vsa::launch_attn_fwd_fp8_packed(k, q8, qscale, k8c, kscale, v8s, vscale, idx, topk,
+                                                       softmax_scale, o_layout == VSA_LAYOUT_RASTER, o, lse, ws,
+                                                       static_cast<hipStream_t>(stream)));
 }
 
 int32_t vsa_cube_unpermute(const vsa_geom* g, const uint16_t* xc, uint16_t* x, void* stream) {

@@ -81,12 +81,18 @@ struct Offsets8 {
   }
 };
 
+// This wavefront's share of a K or V^T tile load: D / 32 instructions of
+// 1 KB; instruction e covers 1024 / D rows of the tile (K) and uses r[64 e / D]
+// (two resources: the two slots of the wavefront's K rows with packed tiles,
+// else the same one twice).
 template <int D>
-__device__ __forceinline__ void issue8(__amdgpu_buffer_rsrc_t r, uint8_t* lds, int w, const uint32_t* off) {
+__device__ __forceinline__ void issue8s(const __amdgpu_buffer_rsrc_t (&r)[2], uint8_t* lds, int w,
+                                        const uint32_t* off) {
   constexpr int NI = D / 32;
 #pragma unroll
   for (int e = 0; e < NI; ++e)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)(lds + (w * NI + e) * 1024), 16, off[e], 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r[(64 * e) / D], (lds_ptr_t)(lds + (w * NI + e) * 1024), 16, off[e], 0,
+                                             0, 0);
 }
 
 // A operand of S^T: 32 K rows of tile t (rows 32 t + pi(m)), 32 bytes of
@@ -124,6 +130,22 @@ __device__ __forceinline__ float max32(const f32x16& a, const f32x16& b) {
   return fmaxf(fmaxf(x, y), fmaxf(m[6], m[7]));
 }
 
+// Largest of 16 values.
+__device__ __forceinline__ float max16_8(const f32x16& a) {
+  float m[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) m[r] = fmaxf(fmaxf(a[4 * r], a[4 * r + 1]), fmaxf(a[4 * r + 2], a[4 * r + 3]));
+  return fmaxf(fmaxf(m[0], m[1]), fmaxf(m[2], m[3]));
+}
+
+// Packed tiles: S^T row m of a 32-key tile reads K row pi_slot8(m), so that
+// lane half h holds in its registers r = 0..15 the keys 16 h + r of the tile:
+// slot 2 t + h of tile t, key r of the slot.  P^T then packs into the B
+// operand with lane half h's 32 bytes = slot h (tile 0) then slot 2 + h
+// (tile 1), and a V^T row of the tile holds the slots' 16-byte chunks in the
+// order 0, 2, 1, 3 (chunk c: slot 2 (c & 1) + (c >> 1)).
+__device__ __forceinline__ int pi_slot8(int m) { return 16 * ((m >> 2) & 1) + 4 * (m >> 3) + (m & 3); }
+
 // Four fp32 P values -> four E4M3 codes (P <= 2^8 < 448 needs no clamp).
 __device__ __forceinline__ int pack_p(float a, float b, float c, float d) {
   int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
@@ -132,13 +154,18 @@ __device__ __forceinline__ int pack_p(float a, float b, float c, float d) {
 
 // One pipelined step n (as the bf16 stage): S^T(n+1) on the matrix cores
 // with the softmax of block n and P(n-1) V(n-1); tile loads of V(n), K(n+3).
-template <int D, bool PARTIAL>
+// c_cur / c_next: the logit multipliers of S^T tiles 0 and 1 of blocks n and
+// n+1 for this lane (one per block, or per slot with packed tiles); the
+// running max of block n+1 comes out scaled by them.  kr[h]: the K resource
+// of the tile rows this wavefront's load instruction e covers, h = 64 e / D.
+template <int D, bool PARTIAL, bool SLOTS, typename MaskF>
 __device__ __forceinline__ void step8(const i32x8 (&ka)[2][D / 64], const uint8_t* v_lds, int n, const i32x8& ones,
                                       const i32x8 (&qf)[D / 64], const f32x16 (&s_cur)[2], f32x16 (&s_next)[2],
                                       float& mx_next, const i32x8& p_prev, i32x8& p_cur, f32x16 (&o)[D / 32 + 1],
-                                      float c_cur, float mc, const KGeom& g, int j_next, int hf,
-                                      __amdgpu_buffer_rsrc_t vr, uint8_t* vl, const uint32_t* voff,
-                                      __amdgpu_buffer_rsrc_t kr, uint8_t* kl, const uint32_t* koff) {
+                                      const float (&c_cur)[SLOTS ? 2 : 1], const float (&c_next)[SLOTS ? 2 : 1],
+                                      float mc, MaskF mask_next,
+                                      int hf, __amdgpu_buffer_rsrc_t vr, uint8_t* vl, const uint32_t* voff,
+                                      const __amdgpu_buffer_rsrc_t (&kr)[2], uint8_t* kl, const uint32_t* koff) {
   constexpr int DC = D / 64, DT = D / 32, NI = D / 32;
 #pragma unroll
   for (int t = 0; t < 2; ++t) {
@@ -151,7 +178,7 @@ __device__ __forceinline__ void step8(const i32x8 (&ka)[2][D / 64], const uint8_
       if (t == 0)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (lds_ptr_t)(vl + e * 1024), 16, voff[e], 0, 0, 0);
       else
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, (lds_ptr_t)(kl + e * 1024), 16, koff[e], 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(kr[(64 * e) / D], (lds_ptr_t)(kl + e * 1024), 16, koff[e], 0, 0, 0);
     }
   }
   // V^T(n-1) operands only now, in the registers the K operands held.
@@ -164,18 +191,18 @@ __device__ __forceinline__ void step8(const i32x8 (&ka)[2][D / 64], const uint8_
     for (int r4 = 0; r4 < 4; ++r4) {
       float p[4];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) p[e] = __builtin_amdgcn_exp2f(fmaf(s_cur[t][4 * r4 + e], c_cur, -mc));
+      for (int e = 0; e < 4; ++e) p[e] = __builtin_amdgcn_exp2f(fmaf(s_cur[t][4 * r4 + e], c_cur[SLOTS ? t : 0], -mc));
       pw[4 * t + r4] = pack_p(p[0], p[1], p[2], p[3]);
     }
   p_cur = i32x8{pw[0], pw[1], pw[2], pw[3], pw[4], pw[5], pw[6], pw[7]};
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) o[dt] = mfma8(va[dt], p_prev, o[dt]);
   o[DT] = mfma8(ones, p_prev, o[DT]);
-  if (PARTIAL) {
-    mask_keys(s_next[0], g, j_next, 0, hf);
-    mask_keys(s_next[1], g, j_next, 1, hf);
-  }
-  mx_next = max32(s_next[0], s_next[1]);
+  if (PARTIAL) mask_next(s_next);
+  // (A multiplier is positive and rounding is monotone: the scaled maximum of
+  // each tile is the maximum of its scaled values.)
+  if constexpr (SLOTS) mx_next = fmaxf(max16_8(s_next[0]) * c_next[0], max16_8(s_next[1]) * c_next[1]);
+  else mx_next = max32(s_next[0], s_next[1]) * c_next[0];
   asm volatile("" ::"v"(pw[0]), "v"(pw[1]), "v"(pw[2]), "v"(pw[3]), "v"(pw[4]), "v"(pw[5]), "v"(pw[6]),
                "v"(pw[7]));
   // The first 32 vector instructions (the softmax of block n, which needs
@@ -194,16 +221,26 @@ __device__ __forceinline__ void step8(const i32x8 (&ka)[2][D / 64], const uint8_
 
 // RASTER: the output is written in raster order [B, S, heads, D] (padded
 // query rows skipped) instead of cube-major rows.
-template <int D, bool PARTIAL, bool RASTER>
+// SLOTS: packed tiles, as in the bf16 packed stage: K codes in compact
+// cube-major rows (k8 is then k8c), V codes in the slot layout
+// [B, H, Nc, 4, D, 16] (v8 is v8s: each 16-key slot transposed), every tile
+// four slot codes (cube, sub-slot, count).  With PARTIAL the tiles and the
+// launch order come from the packing plan (plan, order); without it every
+// tile is one whole cube of the list.  The logit multiplier and the key mask
+// go per slot: lane half h holds slot 2 t + h of S^T tile t (pi_slot8).
+template <int D, bool PARTIAL, bool RASTER, bool SLOTS>
 __global__ void __launch_bounds__(kThreads8, 2) attn_fwd_fp8(const uint8_t* __restrict__ q8,
                                                               const float* __restrict__ qscale,
                                                               const uint8_t* __restrict__ k8,
                                                               const float* __restrict__ kscale,
                                                               const uint8_t* __restrict__ v8t,
                                                               const float* __restrict__ vscale,
-                                                              const int32_t* __restrict__ idx, int topk,
+                                                              const int32_t* __restrict__ idx,
+                                                              const int32_t* __restrict__ plan,
+                                                              const int32_t* __restrict__ order, int topk,
                                                               float scale_log2, uint16_t* __restrict__ oc,
                                                               float* __restrict__ lse, KGeom g, Placement pl) {
+  constexpr bool PLAN = SLOTS && PARTIAL;
   constexpr int DC = D / 64, DT = D / 32, NI8 = D / 32;
   __shared__ __attribute__((aligned(16))) Smem8<D> sm;
   int i, h, b;
@@ -212,19 +249,102 @@ __global__ void __launch_bounds__(kThreads8, 2) attn_fwd_fp8(const uint8_t* __re
   const int wq = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int hf = lane >> 5, n = lane & 31;
   const long long bh = (long long)b * g.H + h;
+  // PLAN: the query cubes of a head run in the order plan_order gives.
+  if (PLAN) i = order[bh * g.nc + i];
   const uint8_t* kbase = k8 + bh * g.Np * D;
   const uint8_t* vbase = v8t + bh * g.Np * D;
   const float* ks = kscale + bh * g.nc;
   const int32_t* irow = idx + (bh * g.nc + i) * topk;
+  const int32_t* prow_plan = PLAN ? plan + (bh * g.nc + i) * 4LL * (topk + 1) : nullptr;
+  const int ntiles = PLAN ? prow_plan[0] : topk;
   const int q = 32 * wq + n;
-  const auto blk = [&](int m) { return irow[m < topk ? m : topk - 1]; };
+  const auto blk = [&](int m) { return irow[m < ntiles ? m : ntiles - 1]; };
+  // SLOTS: the code of slot s of tile m (tiles past the end: the last one).
+  const auto slot = [&](int m, int sl) {
+    const int mm = m < ntiles ? m : ntiles - 1;
+    return PLAN ? prow_plan[4 * (mm + 1) + sl] : ((irow[mm] << 8) | (sl << 5) | 16);
+  };
   // Per-block logit multiplier scale * log2(e) * sq_i * sk_j, kept above 0 so
   // that masked (-inf) logits stay -inf when a cube is all zero (scale 0).
   const float c_q = scale_log2 * qscale[bh * g.nc + i];
   const auto cblk = [&](int j) { return fmaxf(c_q * ks[j], 1e-30f); };
+  // This lane's multipliers of S^T tiles 0 and 1 of tile m, and (SLOTS) its
+  // slots' valid key counts.
+  constexpr int NCT = SLOTS ? 2 : 1;  // multipliers (and slot counts) per lane and tile
+  const auto tile_c = [&](int m, float (&c)[NCT], int (&cnt)[NCT]) {
+    if constexpr (SLOTS) {
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const int c0 = slot(m, 2 * t), c1 = slot(m, 2 * t + 1);
+        const int code = hf ? c1 : c0;
+        c[t] = cblk(slot_cube(code));
+        cnt[t] = slot_count(code);
+      }
+    } else {
+      c[0] = cblk(blk(m));
+      cnt[0] = 64;
+    }
+  };
+  const auto mask_of = [&](int m, const int (&cnt)[NCT]) {
+    const int j = blk(m);
+    return [=, &g](f32x16 (&sv)[2]) {
+      if constexpr (SLOTS) {
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) sv[t][r] = r < cnt[t] ? sv[t][r] : -INFINITY;
+      } else {
+        mask_keys(sv[0], g, j, 0, hf);
+        mask_keys(sv[1], g, j, 1, hf);
+      }
+    };
+  };
   const Offsets8<D> off(wq, lane);
+  // SLOTS: K tile rows of load instruction e lie in slot 2 wq + 64 e / D; the
+  // resource of slot s is based so that the unchanged lane offsets of its
+  // rows land on the slot's compact rows, with only its `count` rows in range.
+  const auto k_rsrc = [&](int m, __amdgpu_buffer_rsrc_t (&r)[2]) {
+    if constexpr (SLOTS) {
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int sg = 2 * wq + u, code = slot(m, sg), cnt = slot_count(code);
+        const long long row0 = 64LL * slot_cube(code) + 16 * slot_sub(code) - 16 * sg;
+        r[u] = make_rsrc(kbase + row0 * D, (m < ntiles && cnt) ? (unsigned)((16 * sg + cnt) * D) : 0u);
+      }
+    } else {
+      r[0] = r[1] = make_rsrc(kbase + 64LL * blk(m) * D, m < ntiles ? 64 * D : 0u);
+    }
+  };
+  // SLOTS: V^T tile instruction e of this lane fills row vr of the tile,
+  // chunk v8_chunk(vr, lane % 4), which holds slot 2 (c & 1) + (c >> 1) of
+  // chunk c; every lane reads its 16 bytes of that slot from the head's slot
+  // layout.
+  uint32_t vso[NI8];
+  const __amdgpu_buffer_rsrc_t vhead = make_rsrc(vbase, (unsigned)(g.Np * D));
+  const auto v_load = [&](int m) {
+    if constexpr (SLOTS) {
+      int sv[4];
+#pragma unroll
+      for (int sl = 0; sl < 4; ++sl) {
+        const int code = slot(m, sl);
+        sv[sl] = 4 * slot_cube(code) + slot_sub(code);
+      }
+#pragma unroll
+      for (int e = 0; e < NI8; ++e) {
+        const int vr = (wq * NI8 + e) * 16 + lane / 4, c = v8_chunk(vr, lane % 4);
+        const int sx = (c & 1) ? ((c >> 1) ? sv[3] : sv[2]) : ((c >> 1) ? sv[1] : sv[0]);
+        vso[e] = (uint32_t)((sx * D + vr) * 16);
+      }
+      return vhead;
+    } else {
+      return make_rsrc(vbase + 64LL * blk(m) * D, 64 * D);
+    }
+  };
+  const uint32_t* voffs = SLOTS ? vso : off.v;
+  __amdgpu_buffer_rsrc_t kr[2];
 
-  issue8<D>(make_rsrc(kbase + 64LL * blk(0) * D, 64 * D), sm.k[0], wq, off.k);
+  k_rsrc(0, kr);
+  issue8s<D>(kr, sm.k[0], wq, off.k);
   i32x8 qf[DC];
   {
     const uint8_t* qrow = q8 + (bh * g.Np + 64LL * i + q) * D;
@@ -235,8 +355,10 @@ __global__ void __launch_bounds__(kThreads8, 2) attn_fwd_fp8(const uint8_t* __re
       qf[c] = i32x8{(int)a.x, (int)a.y, (int)a.z, (int)a.w, (int)bb.x, (int)bb.y, (int)bb.z, (int)bb.w};
     }
   }
-  issue8<D>(make_rsrc(kbase + 64LL * blk(1) * D, 64 * D), sm.k[1], wq, off.k);
-  issue8<D>(make_rsrc(kbase + 64LL * blk(2) * D, 64 * D), sm.k[2], wq, off.k);
+  k_rsrc(1, kr);
+  issue8s<D>(kr, sm.k[1], wq, off.k);
+  k_rsrc(2, kr);
+  issue8s<D>(kr, sm.k[2], wq, off.k);
   {
     uint4* z = reinterpret_cast<uint4*>(sm.v[1]);  // V(-1) = 0
     for (int e = tid; e < D * 64 / 16; e += kThreads8) z[e] = make_uint4(0, 0, 0, 0);
@@ -248,11 +370,11 @@ __global__ void __launch_bounds__(kThreads8, 2) attn_fwd_fp8(const uint8_t* __re
 #pragma unroll
   for (int dt = 0; dt <= DT; ++dt) o[dt] = f32x16{};
   float m_run = -INFINITY;  // running max, log2 units of the scaled logits
-  const int prow = pi_row(n);
+  const int prow = SLOTS ? pi_slot8(n) : pi_row(n);
   i32x8 p_prev = {};
 
   f32x16 s_cur[2];
-  float c_cur;
+  float c_cur[NCT];
   float mx_cur;
   {
     wait_vmcnt<2 * NI8>();  // K(0) and Q in; K(1), K(2) may stay in flight
@@ -266,12 +388,11 @@ __global__ void __launch_bounds__(kThreads8, 2) attn_fwd_fp8(const uint8_t* __re
 #pragma unroll
       for (int c = 0; c < DC; ++c) s_cur[t] = mfma8(ka[t][c], qf[c], s_cur[t]);
     }
-    if (PARTIAL) {
-      mask_keys(s_cur[0], g, blk(0), 0, hf);
-      mask_keys(s_cur[1], g, blk(0), 1, hf);
-    }
-    c_cur = cblk(blk(0));
-    mx_cur = max32(s_cur[0], s_cur[1]) * c_cur;
+    int cnt[NCT];
+    tile_c(0, c_cur, cnt);
+    if (PARTIAL) mask_of(0, cnt)(s_cur);
+    if constexpr (SLOTS) mx_cur = fmaxf(max16_8(s_cur[0]) * c_cur[0], max16_8(s_cur[1]) * c_cur[1]);
+    else mx_cur = max32(s_cur[0], s_cur[1]) * c_cur[0];
   }
   bool move = __builtin_amdgcn_ballot_w64(mx_cur > m_run + kLazy8) != 0;
 
@@ -295,17 +416,18 @@ __global__ void __launch_bounds__(kThreads8, 2) attn_fwd_fp8(const uint8_t* __re
       m_run = grow ? row_max : m_run;
     }
     const float mc = (m_run == -INFINITY) ? 0.f : m_run - kShift8;
-    const int j_next = blk(nb + 1);
-    const float c_next = cblk(j_next);
+    float c_next[NCT];
+    int cnt_next[NCT];
+    tile_c(nb + 1, c_next, cnt_next);
     f32x16 s_next[2];
     float mx_next;
     i32x8 p_cur;
+    const __amdgpu_buffer_rsrc_t vr = v_load(nb);
     // Past the last block the padding loads of K target a zero-size range: no memory traffic.
-    step8<D, PARTIAL>(ka, sm.v[(u + 1) % 2], n, ones, qf, s_cur, s_next, mx_next, p_prev, p_cur, o, c_cur, mc, g, j_next, hf,
-                      make_rsrc(vbase + 64LL * blk(nb) * D, 64 * D), sm.v[u % 2] + wq * NI8 * 1024, off.v,
-                      (nb + 3 < topk ? make_rsrc(kbase + 64LL * blk(nb + 3) * D, 64 * D) : make_rsrc(kbase, 0)), sm.k[u % 3] + wq * NI8 * 1024,
-                      off.k);
-    mx_next *= c_next;
+    k_rsrc(nb + 3, kr);
+    step8<D, PARTIAL, SLOTS>(ka, sm.v[(u + 1) % 2], n, ones, qf, s_cur, s_next, mx_next, p_prev, p_cur, o, c_cur, c_next,
+                      mc, mask_of(nb + 1, cnt_next), hf, vr, sm.v[u % 2] + wq * NI8 * 1024, voffs, kr,
+                      sm.k[u % 3] + wq * NI8 * 1024, off.k);
     move = __builtin_amdgcn_ballot_w64(mx_next > m_run + kLazy8) != 0;
     if (resc) {
 #pragma unroll
@@ -313,12 +435,13 @@ __global__ void __launch_bounds__(kThreads8, 2) attn_fwd_fp8(const uint8_t* __re
     }
     s_cur[0] = s_next[0];
     s_cur[1] = s_next[1];
-    c_cur = c_next;
+#pragma unroll
+    for (int t = 0; t < NCT; ++t) c_cur[t] = c_next[t];
     mx_cur = mx_next;
     p_prev = p_cur;
   };
   int jb = 0;
-  for (; jb + 6 <= topk; jb += 6) {
+  for (; jb + 6 <= ntiles; jb += 6) {
     run_step(jb, StepC<0>{});
     run_step(jb + 1, StepC<1>{});
     run_step(jb + 2, StepC<2>{});
@@ -326,16 +449,16 @@ __global__ void __launch_bounds__(kThreads8, 2) attn_fwd_fp8(const uint8_t* __re
     run_step(jb + 4, StepC<4>{});
     run_step(jb + 5, StepC<5>{});
   }
-  if (jb < topk) run_step(jb, StepC<0>{});
-  if (jb + 1 < topk) run_step(jb + 1, StepC<1>{});
-  if (jb + 2 < topk) run_step(jb + 2, StepC<2>{});
-  if (jb + 3 < topk) run_step(jb + 3, StepC<3>{});
-  if (jb + 4 < topk) run_step(jb + 4, StepC<4>{});
+  if (jb < ntiles) run_step(jb, StepC<0>{});
+  if (jb + 1 < ntiles) run_step(jb + 1, StepC<1>{});
+  if (jb + 2 < ntiles) run_step(jb + 2, StepC<2>{});
+  if (jb + 3 < ntiles) run_step(jb + 3, StepC<3>{});
+  if (jb + 4 < ntiles) run_step(jb + 4, StepC<4>{});
   {
     wait_vmcnt<NI8>();
     pipeline_barrier();
     i32x8 va[DT];
-    read_v8<D>(sm.v[(topk - 1) & 1], hf, n, va);
+    read_v8<D>(sm.v[(ntiles - 1) & 1], hf, n, va);
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) o[dt] = mfma8(va[dt], p_prev, o[dt]);
     o[DT] = mfma8(ones, p_prev, o[DT]);
@@ -375,33 +498,53 @@ __global__ void __launch_bounds__(kThreads8, 2) attn_fwd_fp8(const uint8_t* __re
 
 }  // namespace
 
-template <int D, bool PARTIAL, bool RASTER>
+template <int D, bool PARTIAL, bool RASTER, bool SLOTS>
 static void launch_fp8_t(const KGeom& g, const uint8_t* q8, const float* qs, const uint8_t* k8, const float* ks,
-                         const uint8_t* v8t, const float* vs, const int32_t* idx, int topk, float scale,
-                         uint16_t* oc, float* lse, hipStream_t s) {
+                         const uint8_t* v8, const float* vs, const int32_t* idx, const int32_t* plan,
+                         const int32_t* order, int topk, float scale, uint16_t* oc, float* lse, hipStream_t s) {
   const Placement pl = make_placement(g);
-  attn_fwd_fp8<D, PARTIAL, RASTER><<<dim3(grid_size(g)), dim3(kThreads8), 0, s>>>(
-      q8, qs, k8, ks, v8t, vs, idx, topk, scale * 1.4426950408889634f, oc, lse, g, pl);
+  attn_fwd_fp8<D, PARTIAL, RASTER, SLOTS><<<dim3(grid_size(g)), dim3(kThreads8), 0, s>>>(
+      q8, qs, k8, ks, v8, vs, idx, plan, order, topk, scale * 1.4426950408889634f, oc, lse, g, pl);
 }
 
-template <bool RASTER>
+template <bool RASTER, bool SLOTS>
 static void launch_fp8_any(const KGeom& g, const uint8_t* q8, const float* qs, const uint8_t* k8, const float* ks,
-                           const uint8_t* v8t, const float* vs, const int32_t* idx, int topk, float scale,
-                           uint16_t* oc, float* lse, hipStream_t s) {
+                           const uint8_t* v8, const float* vs, const int32_t* idx, const int32_t* plan,
+                           const int32_t* order, int topk, float scale, uint16_t* oc, float* lse, hipStream_t s) {
+#define VSA_FP8(DD, PP) \
+  launch_fp8_t<DD, PP, RASTER, SLOTS>(g, q8, qs, k8, ks, v8, vs, idx, plan, order, topk, scale, oc, lse, s)
   if (g.D == 64) {
-    if (g.partial) launch_fp8_t<64, true, RASTER>(g, q8, qs, k8, ks, v8t, vs, idx, topk, scale, oc, lse, s);
-    else launch_fp8_t<64, false, RASTER>(g, q8, qs, k8, ks, v8t, vs, idx, topk, scale, oc, lse, s);
+    if (g.partial) VSA_FP8(64, true);
+    else VSA_FP8(64, false);
   } else {
-    if (g.partial) launch_fp8_t<128, true, RASTER>(g, q8, qs, k8, ks, v8t, vs, idx, topk, scale, oc, lse, s);
-    else launch_fp8_t<128, false, RASTER>(g, q8, qs, k8, ks, v8t, vs, idx, topk, scale, oc, lse, s);
+    if (g.partial) VSA_FP8(128, true);
+    else VSA_FP8(128, false);
   }
+#undef VSA_FP8
 }
 
 hipError_t launch_attn_fwd_fp8(const KGeom& g, const uint8_t* q8, const float* qs, const uint8_t* k8,
                                const float* ks, const uint8_t* v8t, const float* vs, const int32_t* idx, int topk,
                                float scale, bool raster_out, uint16_t* o, float* lse, hipStream_t s) {
-  if (raster_out) launch_fp8_any<true>(g, q8, qs, k8, ks, v8t, vs, idx, topk, scale, o, lse, s);
-  else launch_fp8_any<false>(g, q8, qs, k8, ks, v8t, vs, idx, topk, scale, o, lse, s);
+  if (raster_out) launch_fp8_any<true, false>(g, q8, qs, k8, ks, v8t, vs, idx, nullptr, nullptr, topk, scale, o, lse, s);
+  else launch_fp8_any<false, false>(g, q8, qs, k8, ks, v8t, vs, idx, nullptr, nullptr, topk, scale, o, lse, s);
+  return hipGetLastError();
+}
+
+hipError_t launch_attn_fwd_fp8_packed(const KGeom& g, const uint8_t* q8, const float* qs, const uint8_t* k8c,
+                                      const float* ks, const uint8_t* v8s, const float* vs, const int32_t* idx,
+                                      int topk, float scale, bool raster_out, uint16_t* o, float* lse, void* ws,
+                                      hipStream_t s) {
+  const int32_t* plan = nullptr;
+  const int32_t* order = nullptr;
+  if (g.partial) {
+    const hipError_t e = launch_packed_plan(g, idx, topk, ws, s);
+    if (e != hipSuccess) return e;
+    plan = static_cast<const int32_t*>(ws);
+    order = plan + (long long)g.B * g.H * g.nc * 4LL * (topk + 1);
+  }
+  if (raster_out) launch_fp8_any<true, true>(g, q8, qs, k8c, ks, v8s, vs, idx, plan, order, topk, scale, o, lse, s);
+  else launch_fp8_any<false, true>(g, q8, qs, k8c, ks, v8s, vs, idx, plan, order, topk, scale, o, lse, s);
   return hipGetLastError();
 }
 

@@ -526,9 +526,7 @@ size_t attn_packed_workspace_bytes(const KGeom& g, int topk) {
   return rows * 16u * ((size_t)topk + 1) + (rows * 4u + 255) / 256 * 256;
 }
 
-hipError_t launch_attn_fwd_packed(const KGeom& g, const uint16_t* q, bool raster, const uint16_t* kc,
-                                  const uint16_t* vs, const int32_t* idx, int topk, float scale, uint16_t* o,
-                                  float* lse, void* ws, hipStream_t s) {
+hipError_t launch_packed_plan(const KGeom& g, const int32_t* idx, int topk, void* ws, hipStream_t s) {
   int32_t* plan = static_cast<int32_t*>(ws);
   const long long nrows = (long long)g.B * g.H * g.nc;
   int32_t* order = plan + nrows * 4LL * (topk + 1);
@@ -544,6 +542,17 @@ hipError_t launch_attn_fwd_packed(const KGeom& g, const uint16_t* q, bool raster
                                                                                                g.nc);
     }
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_attn_fwd_packed(const KGeom& g, const uint16_t* q, bool raster, const uint16_t* kc,
+                                  const uint16_t* vs, const int32_t* idx, int topk, float scale, uint16_t* o,
+                                  float* lse, void* ws, hipStream_t s) {
+  int32_t* plan = static_cast<int32_t*>(ws);
+  const long long nrows = (long long)g.B * g.H * g.nc;
+  int32_t* order = plan + nrows * 4LL * (topk + 1);
+  const hipError_t e = launch_packed_plan(g, idx, topk, ws, s);
+  if (e != hipSuccess) return e;
 #define VSA_PACKED(DD, PP, RR) \
   launch_fwd<DD, PP, RR, false, true>(g, q, kc, vs, idx, plan, order, topk, scale, o, nullptr, lse, s)
   if (g.D == 64) {

@@ -126,6 +126,9 @@ size_t attn_packed_workspace_bytes(const KGeom& g, int topk);
 hipError_t launch_attn_fwd_packed(const KGeom& g, const uint16_t* q, bool raster, const uint16_t* kc,
                                   const uint16_t* vs, const int32_t* idx, int topk, float scale, uint16_t* o,
                                   float* lse, void* ws, hipStream_t s);
+// The packing plan and launch order of a grid with partial cubes into ws (the
+// packed stages' workspace; nothing for a full grid).
+hipError_t launch_packed_plan(const KGeom& g, const int32_t* idx, int topk, void* ws, hipStream_t s);
 // o_lin, inv_den: optional (both or neither) fp32 copies of O_lin [B, H, Np, D]
 // and of 1/den [B, H, Np] for the backward.
 // raster: q and the output oc are raster [B, S, H, D] (padded query rows not
@@ -203,13 +206,19 @@ hipError_t launch_hbm_probe(int kind, const void* src, void* dst, long long word
 size_t quant_workspace_bytes(const KGeom& g);
 hipError_t launch_quant(const KGeom& g, const uint16_t* q, const uint16_t* k, const uint16_t* v, uint8_t* q8,
                         float* qs, uint8_t* k8, float* ks, uint8_t* v8t, float* vs, float* qmean, float* kmean,
-                        void* ws, hipStream_t s);
+                        void* ws, hipStream_t s, bool packed = false);
 // The device address of the quantizer's static scratch array (VSA_QUANT_SCRATCH_WORDS
 // words) on the device of stream s, looked up once per device.
 hipError_t quant_scratch(hipStream_t s, uint32_t** out);
 hipError_t launch_attn_fwd_fp8(const KGeom& g, const uint8_t* q8, const float* qs, const uint8_t* k8,
                                const float* ks, const uint8_t* v8t, const float* vs, const int32_t* idx, int topk,
                                float scale, bool raster_out, uint16_t* o, float* lse, hipStream_t s);
+// The fp8 stage on packed tiles: K codes in compact rows (k8c), V codes in the
+// slot layout (v8s); ws as launch_attn_fwd_packed's.
+hipError_t launch_attn_fwd_fp8_packed(const KGeom& g, const uint8_t* q8, const float* qs, const uint8_t* k8c,
+                                      const float* ks, const uint8_t* v8s, const float* vs, const int32_t* idx,
+                                      int topk, float scale, bool raster_out, uint16_t* o, float* lse, void* ws,
+                                      hipStream_t s);
 hipError_t launch_attn_bwd(const KGeom& g, const uint16_t* qc, const uint16_t* kc, const uint16_t* vc,
                            const uint16_t* oc, const uint16_t* doc, const float* lse, const int32_t* idx, int topk,
                            float scale, uint16_t* dq, uint16_t* dk, uint16_t* dv, void* ws, hipStream_t s);

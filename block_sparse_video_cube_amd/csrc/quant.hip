@@ -86,10 +86,11 @@ __device__ __forceinline__ float block_max(float m, float* red) {
 // the threads of a chunk by exchanges at lane distances D/8 .. 32, then the
 // four wavefronts in order, divided by the count of valid tokens.  (Padded
 // rows hold zeros here; adding +0 to the fp32 sums changes no bit.)
-template <int D>
+template <int D, bool COMPACT>
 __device__ __forceinline__ void quant_block(const CubeRows<D>& r, uint8_t* __restrict__ x8,
                                             float* __restrict__ scale, float* __restrict__ mean, const KGeom& g,
-                                            long long bh, int c, int count, float* red, float (*part)[D]) {
+                                            long long bh, int c, int ct, int cy, int cx, int count, float* red,
+                                            float (*part)[D]) {
   constexpr int CH = D / 8, PER = CubeRows<D>::PER;
   float m = 0.f;
   float acc[8] = {};
@@ -113,7 +114,8 @@ __device__ __forceinline__ void quant_block(const CubeRows<D>& r, uint8_t* __res
     const uint32_t w4[4] = {r.x[k].x, r.x[k].y, r.x[k].z, r.x[k].w};
     const uint32_t lo = to_e4m3x4(bf_lo(w4[0]) * inv, bf_hi(w4[0]) * inv, bf_lo(w4[1]) * inv, bf_hi(w4[1]) * inv);
     const uint32_t hi = to_e4m3x4(bf_lo(w4[2]) * inv, bf_hi(w4[2]) * inv, bf_lo(w4[3]) * inv, bf_hi(w4[3]) * inv);
-    *reinterpret_cast<uint2*>(x8 + (row0 + l) * D + 8 * ch) = make_uint2(lo, hi);
+    const int rr = COMPACT ? compact_row(g, ct, cy, cx, l) : l;
+    *reinterpret_cast<uint2*>(x8 + (row0 + rr) * D + 8 * ch) = make_uint2(lo, hi);
   }
   if (threadIdx.x == 0) scale[bh * g.nc + c] = __fdiv_rn(m, kE4M3Max);
   if (mean == nullptr) return;
@@ -135,8 +137,9 @@ __device__ __forceinline__ void quant_block(const CubeRows<D>& r, uint8_t* __res
   }
 }
 
-// Pass 1.  vmax: [B, H, D] fp32 bit patterns, zero on entry.
-template <int D>
+// Pass 1.  vmax: [B, H, D] fp32 bit patterns, zero on entry.  KCOMPACT: the
+// K codes go to compact cube-major rows (the packed fp8 stage's layout).
+template <int D, bool KCOMPACT>
 __global__ void __launch_bounds__(kQThreads) quant_pass1(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                                                           const uint16_t* __restrict__ v, uint8_t* __restrict__ q8,
                                                           float* __restrict__ qscale, float* __restrict__ qmean,
@@ -155,8 +158,8 @@ __global__ void __launch_bounds__(kQThreads) quant_pass1(const uint16_t* __restr
   rk.load(k, g, b, h, ct, cy, cx);
   rv.load(v, g, b, h, ct, cy, cx);
   const int count = cube_count(g, ct, cy, cx);
-  quant_block<D>(rq, q8, qscale, qmean, g, bh, c, count, red[0], part[0]);
-  quant_block<D>(rk, k8, kscale, kmean, g, bh, c, count, red[1], part[1]);
+  quant_block<D, false>(rq, q8, qscale, qmean, g, bh, c, ct, cy, cx, count, red[0], part[0]);
+  quant_block<D, KCOMPACT>(rk, k8, kscale, kmean, g, bh, c, ct, cy, cx, count, red[1], part[1]);
   // V: largest |v| of every channel over the cube's rows.
   float cm[8] = {};
 #pragma unroll
@@ -196,9 +199,11 @@ __device__ __forceinline__ int vkey_pos(int k) {
 }
 
 // Pass 2: codes of v * (448 / vmax[channel]) stored as the cube transposed,
-// [B, H, Nc, D, 64] bytes with keys in vkey_pos order; cube 0's workgroup
-// also writes the scales [B, H, D].
-template <int D>
+// [B, H, Nc, D, 64] bytes with keys in vkey_pos order, or (SLOTS, the packed
+// fp8 stage's layout) [B, H, Nc, 4, D, 16]: the cube's keys in compact order
+// cut into four 16-key slots, each transposed; cube 0's workgroup also writes
+// the scales [B, H, D].
+template <int D, bool SLOTS>
 __global__ void __launch_bounds__(kQThreads) quant_pass2(const uint16_t* __restrict__ v,
                                                           const uint32_t* __restrict__ vmax,
                                                           uint8_t* __restrict__ v8t, float* __restrict__ vscale,
@@ -223,7 +228,7 @@ __global__ void __launch_bounds__(kQThreads) quant_pass2(const uint16_t* __restr
 #pragma unroll
   for (int k = 0; k < PER; ++k) {
     const int f = threadIdx.x + kQThreads * k, l = f / CH;
-    const int pos = vkey_pos(l);
+    const int pos = SLOTS ? compact_row(g, ct, cy, cx, l) : vkey_pos(l);
     const uint32_t w4[4] = {rv.x[k].x, rv.x[k].y, rv.x[k].z, rv.x[k].w};
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
@@ -237,7 +242,9 @@ __global__ void __launch_bounds__(kQThreads) quant_pass2(const uint16_t* __restr
   for (int f = threadIdx.x; f < D * 4; f += kQThreads) {
     const int d = f >> 2, qq = f & 3;
     const uint32_t* src = reinterpret_cast<const uint32_t*>(tile + d * LD + 16 * qq);
-    *reinterpret_cast<uint4*>(out + d * 64 + 16 * qq) = make_uint4(src[0], src[1], src[2], src[3]);
+    // SLOTS: bytes 16 qq .. +15 of row d are keys 0..15 of slot qq.
+    *reinterpret_cast<uint4*>(out + (SLOTS ? (qq * D + d) * 16 : d * 64 + 16 * qq)) =
+        make_uint4(src[0], src[1], src[2], src[3]);
   }
   if (c == 0 && threadIdx.x < D)
     vscale[bh * D + threadIdx.x] = __fdiv_rn(__uint_as_float(vmax[bh * D + threadIdx.x]), kE4M3Max);
@@ -251,12 +258,17 @@ __global__ void __launch_bounds__(kQThreads) zero_words(uint32_t* __restrict__ p
 template <int D>
 void launch_quant_t(const KGeom& g, const uint16_t* q, const uint16_t* k, const uint16_t* v, uint8_t* q8, float* qs,
                     uint8_t* k8, float* ks, uint8_t* v8t, float* vs, float* qmean, float* kmean, uint32_t* vmax,
-                    hipStream_t s) {
+                    bool packed, hipStream_t s) {
   const long long nmax = (long long)g.B * g.H * D;
   zero_words<<<dim3((unsigned)((nmax + kQThreads - 1) / kQThreads)), dim3(kQThreads), 0, s>>>(vmax, nmax);
   const dim3 grid(g.nc, g.H, g.B);
-  quant_pass1<D><<<grid, dim3(kQThreads), 0, s>>>(q, k, v, q8, qs, qmean, k8, ks, kmean, vmax, g);
-  quant_pass2<D><<<grid, dim3(kQThreads), 0, s>>>(v, vmax, v8t, vs, g);
+  if (packed) {
+    quant_pass1<D, true><<<grid, dim3(kQThreads), 0, s>>>(q, k, v, q8, qs, qmean, k8, ks, kmean, vmax, g);
+    quant_pass2<D, true><<<grid, dim3(kQThreads), 0, s>>>(v, vmax, v8t, vs, g);
+  } else {
+    quant_pass1<D, false><<<grid, dim3(kQThreads), 0, s>>>(q, k, v, q8, qs, qmean, k8, ks, kmean, vmax, g);
+    quant_pass2<D, false><<<grid, dim3(kQThreads), 0, s>>>(v, vmax, v8t, vs, g);
+  }
 }
 
 }  // namespace
@@ -306,10 +318,10 @@ size_t quant_workspace_bytes(const KGeom& g) {
 
 hipError_t launch_quant(const KGeom& g, const uint16_t* q, const uint16_t* k, const uint16_t* v, uint8_t* q8,
                         float* qs, uint8_t* k8, float* ks, uint8_t* v8t, float* vs, float* qmean, float* kmean,
-                        void* ws, hipStream_t s) {
+                        void* ws, hipStream_t s, bool packed) {
   uint32_t* vmax = static_cast<uint32_t*>(ws);
-  if (g.D == 64) launch_quant_t<64>(g, q, k, v, q8, qs, k8, ks, v8t, vs, qmean, kmean, vmax, s);
-  else launch_quant_t<128>(g, q, k, v, q8, qs, k8, ks, v8t, vs, qmean, kmean, vmax, s);
+  if (g.D == 64) launch_quant_t<64>(g, q, k, v, q8, qs, k8, ks, v8t, vs, qmean, kmean, vmax, packed, s);
+  else launch_quant_t<128>(g, q, k, v, q8, qs, k8, ks, v8t, vs, qmean, kmean, vmax, packed, s);
   return hipGetLastError();
 }
 

@@ -328,6 +328,37 @@ int32_t vsa_sparse_attn_fwd_fp8(const vsa_geom* g, const uint8_t* q8, const floa
                                 float softmax_scale, int32_t o_layout, uint16_t* o, float* lse,
                                 void* stream);
 
+/* The low-precision fine stage on packed tiles (the same method and passage
+ * as vsa_sparse_attn_fwd_fp8; tiles packed as for vsa_sparse_attn_fwd_packed:
+ * a selected cube with n valid keys fills ceil(n / 16) slots of 16 keys, and
+ * cubes of one or two slots share tiles; the query cubes of each head run in
+ * order of their tile count).
+ *
+ * vsa_quant_fp8_packed: vsa_quant_fp8 with the packed stage's layouts: the
+ *   same codes and scales, but k8c holds K's codes in compact cube-major rows
+ *   [B, heads, Np, D] (a cube's valid tokens first, as TOKEN_COMPACT; the
+ *   other rows zero) and v8s V's codes as [B, heads, Nc, 4, D, 16]: element
+ *   (b, h, c, s, d, e) = the code of channel d of compact key 16 s + e of cube
+ *   c (zero past its valid keys).  Arguments, workspace and errors otherwise
+ *   as vsa_quant_fp8.
+ * vsa_sparse_attn_fwd_fp8_packed: the fine stage of vsa_sparse_attn_fwd_fp8
+ *   on those layouts (q8, scales and outputs as there).  ws: at least
+ *   vsa_sparse_attn_packed_workspace_bytes(g, topk) bytes (the packing plan
+ *   and the launch order; 0 and ws may be NULL for a grid without padded
+ *   cubes).  Results agree with vsa_sparse_attn_fwd_fp8 within the rounding
+ *   of the weights to E4M3 and the fp32 summation order (blocks are visited in
+ *   tile order).  Limit: n_cubes < 2^23.  Errors as vsa_sparse_attn_fwd_fp8,
+ *   and VSA_ERR_WORKSPACE. */
+int32_t vsa_quant_fp8_packed(const vsa_geom* g, const uint16_t* q, const uint16_t* k,
+                             const uint16_t* v, uint8_t* q8, float* qscale, uint8_t* k8c,
+                             float* kscale, uint8_t* v8s, float* vscale, float* qmean,
+                             float* kmean, void* ws, size_t ws_bytes, void* stream);
+int32_t vsa_sparse_attn_fwd_fp8_packed(const vsa_geom* g, const uint8_t* q8, const float* qscale,
+                                       const uint8_t* k8c, const float* kscale, const uint8_t* v8s,
+                                       const float* vscale, const int32_t* idx, int32_t topk,
+                                       float softmax_scale, int32_t o_layout, uint16_t* o,
+                                       float* lse, void* ws, size_t ws_bytes, void* stream);
+
 /* Backward of the fine stage (the gradient of vsa_sparse_attn_fwd with respect
  * to Q, K and V; VSA and SLA are trained, FastVideo sparse-distillation
  * article section "2. 视频稀疏注意力VSA", TurboDiffusion article section

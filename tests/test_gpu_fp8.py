@@ -1,6 +1,10 @@
 """GPU parity of the low-precision fine stage (fp8 E4M3 codes, fp8 matrix
 products) against the fp64 oracle.
 
+The packed stage (vsa_quant_fp8_packed, vsa_sparse_attn_fwd_fp8_packed) is
+held to the same checks: its layouts bit-exact (K codes in compact rows, V
+codes in 16-key slots), and its outputs within the bounds of items 2 and 3.
+
 1. The quantizers are bit-exact against the oracle's (O10): codes and scales
    of Q and K per (b, h, cube), of V per (b, h, channel); V's codes in the
    documented tile order (each cube transposed, key k = 32 t + 16 g + 8 h + e
@@ -78,17 +82,18 @@ def dequant(codes, scale, per_cube: bool):
     return x * scale.astype(np.float64)[:, :, None, :]
 
 
-def gpu_fp8(inp, grid, idx_np, scale, q_zero=False):
+def gpu_fp8(inp, grid, idx_np, scale, q_zero=False, packed=False):
     import block_sparse_video_cube_amd as vsa
 
     q, k, v = (to_dev(inp[n]) for n in ("q", "k", "v"))
     if q_zero:
         q = torch.zeros_like(q)
-    q8, qs, k8, ks, v8t, vs, qm, km = vsa.quant_fp8(q, k, v, grid, want_means=True)
+    q8, qs, k8, ks, v8t, vs, qm, km = vsa.quant_fp8(q, k, v, grid, want_means=True, packed=packed)
     idx = torch.from_numpy(np.ascontiguousarray(idx_np, dtype=np.int32)).to("cuda:0")
-    oc, lse = vsa.sparse_attn_fwd_fp8(q8, qs, k8, ks, v8t, vs, idx, grid, scale, want_lse=True)
+    stage = vsa.sparse_attn_fwd_fp8_packed if packed else vsa.sparse_attn_fwd_fp8
+    oc, lse = stage(q8, qs, k8, ks, v8t, vs, idx, grid, scale, want_lse=True)
     # The raster-order output is the same values at raster positions.
-    o_r, lse_r = vsa.sparse_attn_fwd_fp8(q8, qs, k8, ks, v8t, vs, idx, grid, scale, want_lse=True, raster=True)
+    o_r, lse_r = stage(q8, qs, k8, ks, v8t, vs, idx, grid, scale, want_lse=True, raster=True)
     assert torch.equal(o_r, vsa.cube_unpermute(oc, grid)) and torch.equal(lse_r, lse)
     # The means for the coarse stage come out of the same pass, bit-identical to the pooling kernel's.
     assert torch.equal(qm, vsa.cube_pool(q, grid)) and torch.equal(km, vsa.cube_pool(k, grid))
@@ -172,9 +177,9 @@ def test_uniform_weights_give_mean_of_selected_values(B, H, D, grid, k):
     assert np.allclose(lse[:, :, valid], ref_lse[:, :, valid], rtol=0, atol=1e-5)
 
 
-def check_vs_dequantized(inp, grid, idx, scale, cubes=None, what=""):
+def check_vs_dequantized(inp, grid, idx, scale, cubes=None, what="", packed=False):
     valid = oracle.valid_rows(grid)
-    got, lse, _ = gpu_fp8(inp, grid, idx, scale)
+    got, lse, _ = gpu_fp8(inp, grid, idx, scale, packed=packed)
     (q8, qs), (k8, ks), (v8, vs) = oracle_codes(inp, grid)
     qd, kd, vd = dequant(q8, qs, True), dequant(k8, ks, True), dequant(v8, vs, False)
     ref, ref_lse = oracle.sparse_attention(qd, kd, vd, valid, idx, scale, cubes)
@@ -216,9 +221,10 @@ def test_fp8_matches_exact_oracle_loosely(B, H, D, grid, k):
     assert_close_rel(got[:, :, valid], ref[:, :, valid], "fp8 vs exact", MAX_REL_EXACT, MEAN_REL_EXACT)
 
 
-@pytest.mark.parametrize("name,head", [("wan1.3b", 0), ("720p", 5), ("wan14b", 3)])
-def test_fp8_full_size_sampled(name, head):
-    """One head at the full token grid and top-k; sampled query cubes."""
+@pytest.mark.parametrize("name,head,packed", [("wan1.3b", 0, False), ("720p", 5, False), ("wan14b", 3, False),
+                                              ("720p", 9, True), ("wan1.3b", 2, True)])
+def test_fp8_full_size_sampled(name, head, packed):
+    """One head at the full token grid and top-k; sampled query cubes (packed: the packed stage)."""
     wl = workloads.workload(name)
     full = workloads.make_inputs(wl, heads=[head])
     inp = {n: np.ascontiguousarray(full[n][:, :, [head], :]) for n in ("q", "k", "v")}
@@ -227,8 +233,54 @@ def test_fp8_full_size_sampled(name, head):
     nc = oracle.n_cubes(wl.grid)
     cubes = [(0, 0, i) for i in np.linspace(0, nc - 1, 12).astype(int)]
     print(f"[{name}] head {head}: GPU fp8 stage and oracle on {len(cubes)} cubes", flush=True)
-    got, rows = check_vs_dequantized(inp, wl.grid, idx, wl.softmax_scale, cubes, what=name)
+    got, rows = check_vs_dequantized(inp, wl.grid, idx, wl.softmax_scale, cubes, what=name, packed=packed)
     valid = oracle.valid_rows(wl.grid)
     qc, kc, vc = (oracle.cube_permute(inp[n], wl.grid) for n in ("q", "k", "v"))
     ref, _ = oracle.sparse_attention(qc, kc, vc, valid, idx, wl.softmax_scale, cubes)
     assert_close_rel(got[rows], ref[rows], f"{name} fp8 vs exact", MAX_REL_EXACT, MEAN_REL_EXACT)
+
+
+# ------------------------------------------------------------------ packed --
+# The packed stage's layouts (vsa_quant_fp8_packed) and the stage on them
+# (vsa_sparse_attn_fwd_fp8_packed): tiles of 16-key slots, edge cubes sharing
+# tiles (grids with partial cubes) or one cube per tile (full grids).
+
+def compact_rows(x: np.ndarray, grid) -> np.ndarray:
+    """[B, H, Np, D] cube-major rows -> the same rows in compact order per cube."""
+    order = oracle.compact_order(grid)
+    rows = (64 * np.arange(order.shape[0])[:, None] + order).reshape(-1)
+    return x[:, :, rows, :]
+
+
+@pytest.mark.parametrize("B,H,D,grid,k", CASES[:4])
+def test_packed_quantizers_bit_exact(B, H, D, grid, k):
+    wl, inp = make_case(B, H, D, grid, k, 4500 + D + k)
+    idx = select(inp, grid, k)
+    _, _, got = gpu_fp8(inp, grid, idx, wl.softmax_scale, packed=True)
+    (q8, qs), (k8, ks), (v8, vs) = oracle_codes(inp, grid)
+    valid = oracle.valid_rows(grid)
+    assert np.array_equal(got[0][:, :, valid], q8[:, :, valid]) and np.array_equal(got[1], qs)
+    assert np.array_equal(got[2], compact_rows(k8, grid)) and np.array_equal(got[3], ks)
+    assert np.array_equal(got[4], oracle.cube_slots(compact_rows(v8, grid))) and np.array_equal(got[5], vs)
+
+
+@pytest.mark.parametrize("B,H,D,grid,k", CASES + [(1, 2, 128, (21, 45, 20), 30), (2, 1, 64, (6, 9, 13), 20)])
+def test_packed_fp8_matches_oracle_on_dequantized_inputs(B, H, D, grid, k):
+    wl, inp = make_case(B, H, D, grid, k, 4600 + 7 * k + D)
+    check_vs_dequantized(inp, grid, select(inp, grid, k), wl.softmax_scale, packed=True,
+                         what=f"packed {B}x{H}x{D} {grid} k={k}")
+
+
+@pytest.mark.parametrize("B,H,D,grid,k", CASES[1:4])
+def test_packed_uniform_weights_give_mean_of_selected_values(B, H, D, grid, k):
+    wl, inp = make_case(B, H, D, grid, k, 4700 + k)
+    idx = select(inp, grid, k)
+    got, lse, _ = gpu_fp8(inp, grid, idx, wl.softmax_scale, q_zero=True, packed=True)
+    valid = oracle.valid_rows(grid)
+    _, _, (v8, vs) = oracle_codes(inp, grid)
+    vd = dequant(v8, vs, per_cube=False)
+    ref, ref_lse = oracle.sparse_attention(np.zeros_like(vd), np.zeros_like(vd), vd, valid, idx, wl.softmax_scale)
+    err = np.abs(got - ref)[:, :, valid]
+    tol = 2.0 ** -8 * np.abs(ref[:, :, valid]) + 2.0 ** -16 * np.abs(vd).max()
+    assert np.all(err <= tol)
+    assert np.allclose(lse[:, :, valid], ref_lse[:, :, valid], rtol=0, atol=1e-5)
