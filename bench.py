@@ -83,8 +83,8 @@ def copy_calibration(nbytes: int) -> None:
 
 
 KERNEL_SOURCES = {
-    "attn_fwd": ("attn_fwd.hip", "attn_core.h", "tile_pipeline.h", "common.h"),
-    "attn_fwd_fp8": ("attn_fp8.hip", "tile_pipeline.h", "common.h"),
+    "attn_fwd": ("attn_fwd.hip", "attn_core.h", "tile_pipeline.h", "device.h"),
+    "attn_fwd_fp8": ("attn_fp8.hip", "tile_pipeline.h", "device.h"),
 }
 
 
