@@ -98,7 +98,7 @@ __device__ __forceinline__ void issue8s(const __amdgpu_buffer_rsrc_t (&r)[2], ui
 // A operand of S^T: 32 K rows of tile t (rows 32 t + pi(m)), 32 bytes of
 // channels 64 c + 32 hf .. + 31 for each of the D / 64 products.
 template <int D>
-__device__ __forceinline__ void read_k8(const uint8_t* lds, int t, int hf, int prow, i32x8 (&ka)[D / 64]) {
+__device__ __forceinline__ void read_k8(const uint8_t* __restrict__ lds, int t, int hf, int prow, i32x8 (&ka)[D / 64]) {
   const int row = 32 * t + prow;
 #pragma unroll
   for (int c = 0; c < D / 64; ++c) {
@@ -111,7 +111,7 @@ __device__ __forceinline__ void read_k8(const uint8_t* lds, int t, int hf, int p
 
 // A operand of O^T: channel rows 32 dt + n, the 32 key bytes of lane half hf.
 template <int D>
-__device__ __forceinline__ void read_v8(const uint8_t* lds, int hf, int n, i32x8 (&va)[D / 32]) {
+__device__ __forceinline__ void read_v8(const uint8_t* __restrict__ lds, int hf, int n, i32x8 (&va)[D / 32]) {
 #pragma unroll
   for (int dt = 0; dt < D / 32; ++dt) {
     const int row = 32 * dt + n;
@@ -159,31 +159,33 @@ __device__ __forceinline__ int pack_p(float a, float b, float c, float d) {
 // running max of block n+1 comes out scaled by them.  kr[h]: the K resource
 // of the tile rows this wavefront's load instruction e covers, h = 64 e / D.
 template <int D, bool PARTIAL, bool SLOTS, typename MaskF>
-__device__ __forceinline__ void step8(const i32x8 (&ka)[2][D / 64], const uint8_t* v_lds, int n, const i32x8& ones,
+__device__ __forceinline__ void step8(const i32x8 (&ka)[2][D / 64], const uint8_t* __restrict__ v_lds, int n, const i32x8& ones,
                                       const i32x8 (&qf)[D / 64], const f32x16 (&s_cur)[2], f32x16 (&s_next)[2],
                                       float& mx_next, const i32x8& p_prev, i32x8& p_cur, f32x16 (&o)[D / 32 + 1],
                                       const float (&c_cur)[SLOTS ? 2 : 1], const float (&c_next)[SLOTS ? 2 : 1],
                                       float mc, MaskF mask_next,
-                                      int hf, __amdgpu_buffer_rsrc_t vr, uint8_t* vl, const uint32_t* voff,
-                                      const __amdgpu_buffer_rsrc_t (&kr)[2], uint8_t* kl, const uint32_t* koff) {
+                                      int hf, __amdgpu_buffer_rsrc_t vr, uint8_t* __restrict__ vl, const uint32_t* voff,
+                                      const __amdgpu_buffer_rsrc_t (&kr)[2], uint8_t* __restrict__ kl, const uint32_t* koff) {
   constexpr int DC = D / 64, DT = D / 32, NI = D / 32;
+  s_next[0] = f32x16{};
 #pragma unroll
-  for (int t = 0; t < 2; ++t) {
-    s_next[t] = f32x16{};
-#pragma unroll
-    for (int c = 0; c < DC; ++c) s_next[t] = mfma8(ka[t][c], qf[c], s_next[t]);
-    // The V tile's loads after the first key tile's products, the K tile's after the second.
-#pragma unroll
-    for (int e = 0; e < NI; ++e) {
-      if (t == 0)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (lds_ptr_t)(vl + e * 1024), 16, voff[e], 0, 0, 0);
-      else
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(kr[(64 * e) / D], (lds_ptr_t)(kl + e * 1024), 16, koff[e], 0, 0, 0);
-    }
-  }
-  // V^T(n-1) operands only now, in the registers the K operands held.
+  for (int c = 0; c < DC; ++c) s_next[0] = mfma8(ka[0][c], qf[c], s_next[0]);
+  // V^T(n-1) operands after the first key tile's products (in the registers
+  // its K operands held), and before this step's tile loads: the compiler
+  // cannot tell the buffers of a direct-to-LDS load apart, so an LDS read
+  // placed after one waits until it has landed.
   i32x8 va[DT];
   read_v8<D>(v_lds, hf, n, va);
+  // Then the V tile's loads, the second key tile's products and the K tile's loads.
+#pragma unroll
+  for (int e = 0; e < NI; ++e)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (lds_ptr_t)(vl + e * 1024), 16, voff[e], 0, 0, 0);
+  s_next[1] = f32x16{};
+#pragma unroll
+  for (int c = 0; c < DC; ++c) s_next[1] = mfma8(ka[1][c], qf[c], s_next[1]);
+#pragma unroll
+  for (int e = 0; e < NI; ++e)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(kr[(64 * e) / D], (lds_ptr_t)(kl + e * 1024), 16, koff[e], 0, 0, 0);
   int pw[8];
 #pragma unroll
   for (int t = 0; t < 2; ++t)
@@ -272,13 +274,22 @@ __global__ void __launch_bounds__(kThreads8, 2) attn_fwd_fp8(const uint8_t* __re
   // slots' valid key counts.
   constexpr int NCT = SLOTS ? 2 : 1;  // multipliers (and slot counts) per lane and tile
   const auto tile_c = [&](int m, float (&c)[NCT], int (&cnt)[NCT]) {
-    if constexpr (SLOTS) {
+    if constexpr (SLOTS && !PLAN) {
+      // Every tile is one whole cube: four full slots of the same cube.
+      c[0] = c[1] = cblk(blk(m));
+      cnt[0] = cnt[1] = 16;
+    } else if constexpr (SLOTS) {
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
         const int c0 = slot(m, 2 * t), c1 = slot(m, 2 * t + 1);
-        const int code = hf ? c1 : c0;
-        c[t] = cblk(slot_cube(code));
-        cnt[t] = slot_count(code);
+        // Both slots' key scales are loaded at their wave-uniform cubes and
+        // only then picked per lane half: a lane-dependent index would make
+        // the scale a vector load, and its wait would also cover every tile
+        // load in flight.  The empty asm keeps the two loads apart.
+        float s0 = ks[slot_cube(c0)], s1 = ks[slot_cube(c1)];
+        asm volatile("" : "+s"(s0), "+s"(s1));
+        c[t] = fmaxf(c_q * (hf ? s1 : s0), 1e-30f);
+        cnt[t] = slot_count(hf ? c1 : c0);
       }
     } else {
       c[0] = cblk(blk(m));
