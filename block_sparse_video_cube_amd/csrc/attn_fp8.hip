@@ -200,10 +200,15 @@ __device__ __forceinline__ void step8(const i32x8 (&ka)[2][D / 64], const uint8_
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) o[dt] = mfma8(va[dt], p_prev, o[dt]);
   o[DT] = mfma8(ones, p_prev, o[DT]);
-  if (PARTIAL) mask_next(s_next);
+  // Packed tiles with a plan (SLOTS and PARTIAL): the caller masks S^T(n+1)
+  // and takes its maximum after the step, and only masks tiles with a slot
+  // of fewer than 16 keys.
+  constexpr bool DEFER = SLOTS && PARTIAL;
+  if (PARTIAL && !DEFER) mask_next(s_next);
   // (A multiplier is positive and rounding is monotone: the scaled maximum of
   // each tile is the maximum of its scaled values.)
-  if constexpr (SLOTS) mx_next = fmaxf(max16_8(s_next[0]) * c_next[0], max16_8(s_next[1]) * c_next[1]);
+  if constexpr (DEFER) (void)c_next;
+  else if constexpr (SLOTS) mx_next = fmaxf(max16_8(s_next[0]) * c_next[0], max16_8(s_next[1]) * c_next[1]);
   else mx_next = max32(s_next[0], s_next[1]) * c_next[0];
   asm volatile("" ::"v"(pw[0]), "v"(pw[1]), "v"(pw[2]), "v"(pw[3]), "v"(pw[4]), "v"(pw[5]), "v"(pw[6]),
                "v"(pw[7]));
@@ -273,7 +278,9 @@ __global__ void __launch_bounds__(kThreads8, 2) attn_fwd_fp8(const uint8_t* __re
   // This lane's multipliers of S^T tiles 0 and 1 of tile m, and (SLOTS) its
   // slots' valid key counts.
   constexpr int NCT = SLOTS ? 2 : 1;  // multipliers (and slot counts) per lane and tile
-  const auto tile_c = [&](int m, float (&c)[NCT], int (&cnt)[NCT]) {
+  // full: every slot of the tile holds 16 valid keys (wave-uniform; PLAN only).
+  const auto tile_c = [&](int m, float (&c)[NCT], int (&cnt)[NCT], bool& full) {
+    full = true;
     if constexpr (SLOTS && !PLAN) {
       // Every tile is one whole cube: four full slots of the same cube.
       c[0] = c[1] = cblk(blk(m));
@@ -290,6 +297,7 @@ __global__ void __launch_bounds__(kThreads8, 2) attn_fwd_fp8(const uint8_t* __re
         asm volatile("" : "+s"(s0), "+s"(s1));
         c[t] = fmaxf(c_q * (hf ? s1 : s0), 1e-30f);
         cnt[t] = slot_count(hf ? c1 : c0);
+        full = full & (slot_count(c0) == 16) & (slot_count(c1) == 16);
       }
     } else {
       c[0] = cblk(blk(m));
@@ -354,6 +362,12 @@ __global__ void __launch_bounds__(kThreads8, 2) attn_fwd_fp8(const uint8_t* __re
   const uint32_t* voffs = SLOTS ? vso : off.v;
   __amdgpu_buffer_rsrc_t kr[2];
 
+  {
+    // V(-1) = 0, written before any tile load is in flight (an LDS store
+    // after a direct-to-LDS load would wait for it to land).
+    uint4* z = reinterpret_cast<uint4*>(sm.v[1]);
+    for (int e = tid; e < D * 64 / 16; e += kThreads8) z[e] = make_uint4(0, 0, 0, 0);
+  }
   k_rsrc(0, kr);
   issue8s<D>(kr, sm.k[0], wq, off.k);
   i32x8 qf[DC];
@@ -370,10 +384,6 @@ __global__ void __launch_bounds__(kThreads8, 2) attn_fwd_fp8(const uint8_t* __re
   issue8s<D>(kr, sm.k[1], wq, off.k);
   k_rsrc(2, kr);
   issue8s<D>(kr, sm.k[2], wq, off.k);
-  {
-    uint4* z = reinterpret_cast<uint4*>(sm.v[1]);  // V(-1) = 0
-    for (int e = tid; e < D * 64 / 16; e += kThreads8) z[e] = make_uint4(0, 0, 0, 0);
-  }
   // Ones row of the normaliser: row 0 of an extra 32-row A operand.
   const int one = (n == 0) ? 0x38383838 : 0;  // four E4M3 ones
   const i32x8 ones = {one, one, one, one, one, one, one, one};
@@ -400,7 +410,8 @@ __global__ void __launch_bounds__(kThreads8, 2) attn_fwd_fp8(const uint8_t* __re
       for (int c = 0; c < DC; ++c) s_cur[t] = mfma8(ka[t][c], qf[c], s_cur[t]);
     }
     int cnt[NCT];
-    tile_c(0, c_cur, cnt);
+    bool full0;
+    tile_c(0, c_cur, cnt, full0);
     if (PARTIAL) mask_of(0, cnt)(s_cur);
     if constexpr (SLOTS) mx_cur = fmaxf(max16_8(s_cur[0]) * c_cur[0], max16_8(s_cur[1]) * c_cur[1]);
     else mx_cur = max32(s_cur[0], s_cur[1]) * c_cur[0];
@@ -429,7 +440,8 @@ __global__ void __launch_bounds__(kThreads8, 2) attn_fwd_fp8(const uint8_t* __re
     const float mc = (m_run == -INFINITY) ? 0.f : m_run - kShift8;
     float c_next[NCT];
     int cnt_next[NCT];
-    tile_c(nb + 1, c_next, cnt_next);
+    bool full_next;
+    tile_c(nb + 1, c_next, cnt_next, full_next);
     f32x16 s_next[2];
     float mx_next;
     i32x8 p_cur;
@@ -439,6 +451,14 @@ __global__ void __launch_bounds__(kThreads8, 2) attn_fwd_fp8(const uint8_t* __re
     step8<D, PARTIAL, SLOTS>(ka, sm.v[(u + 1) % 2], n, ones, qf, s_cur, s_next, mx_next, p_prev, p_cur, o, c_cur, c_next,
                       mc, mask_of(nb + 1, cnt_next), hf, vr, sm.v[u % 2] + wq * NI8 * 1024, voffs, kr,
                       sm.k[u % 3] + wq * NI8 * 1024, off.k);
+    if constexpr (PLAN) {
+      // Most tiles hold four full slots (16 valid keys each) and need no
+      // mask; the test is on the tile's slot codes, so the branch is
+      // wave-uniform.  The masking is the step's largest piece of vector work
+      // after the exponentials.
+      if (!full_next) mask_of(nb + 1, cnt_next)(s_next);
+      mx_next = fmaxf(max16_8(s_next[0]) * c_next[0], max16_8(s_next[1]) * c_next[1]);
+    }
     move = __builtin_amdgcn_ballot_w64(mx_next > m_run + kLazy8) != 0;
     if (resc) {
 #pragma unroll
