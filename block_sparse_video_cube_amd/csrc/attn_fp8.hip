@@ -121,21 +121,24 @@ __device__ __forceinline__ void read_v8(const uint8_t* __restrict__ lds, int hf,
   }
 }
 
-// Largest of 32 values as a tree of three-input maxima (v_max3_f32).
+// Largest of 32 values as chains of three-input maxima (v_max3_f32).
 __device__ __forceinline__ float max32(const f32x16& a, const f32x16& b) {
-  float m[8];
-#pragma unroll
-  for (int r = 0; r < 8; ++r) m[r] = fmaxf(fmaxf(a[2 * r], a[2 * r + 1]), fmaxf(b[2 * r], b[2 * r + 1]));
-  const float x = fmaxf(fmaxf(m[0], m[1]), m[2]), y = fmaxf(fmaxf(m[3], m[4]), m[5]);
-  return fmaxf(fmaxf(x, y), fmaxf(m[6], m[7]));
+  const float x = fmaxf(fmaxf(a[0], a[1]), a[2]), y = fmaxf(fmaxf(a[3], a[4]), a[5]);
+  const float z = fmaxf(fmaxf(a[6], a[7]), a[8]), u = fmaxf(fmaxf(a[9], a[10]), a[11]);
+  const float v = fmaxf(fmaxf(a[12], a[13]), a[14]), w = fmaxf(fmaxf(a[15], b[0]), b[1]);
+  const float x2 = fmaxf(fmaxf(b[2], b[3]), b[4]), y2 = fmaxf(fmaxf(b[5], b[6]), b[7]);
+  const float z2 = fmaxf(fmaxf(b[8], b[9]), b[10]), u2 = fmaxf(fmaxf(b[11], b[12]), b[13]);
+  const float v2 = fmaxf(fmaxf(b[14], b[15]), x);
+  const float p = fmaxf(fmaxf(y, z), u), q = fmaxf(fmaxf(v, w), x2), r = fmaxf(fmaxf(y2, z2), u2);
+  return fmaxf(fmaxf(fmaxf(p, q), r), v2);
 }
 
-// Largest of 16 values.
+// Largest of 16 values (chains of three-input maxima).
 __device__ __forceinline__ float max16_8(const f32x16& a) {
-  float m[4];
-#pragma unroll
-  for (int r = 0; r < 4; ++r) m[r] = fmaxf(fmaxf(a[4 * r], a[4 * r + 1]), fmaxf(a[4 * r + 2], a[4 * r + 3]));
-  return fmaxf(fmaxf(m[0], m[1]), fmaxf(m[2], m[3]));
+  const float x = fmaxf(fmaxf(a[0], a[1]), a[2]), y = fmaxf(fmaxf(a[3], a[4]), a[5]);
+  const float z = fmaxf(fmaxf(a[6], a[7]), a[8]), u = fmaxf(fmaxf(a[9], a[10]), a[11]);
+  const float v = fmaxf(fmaxf(a[12], a[13]), a[14]);
+  return fmaxf(fmaxf(fmaxf(x, y), z), fmaxf(fmaxf(u, v), a[15]));
 }
 
 // Packed tiles: S^T row m of a 32-key tile reads K row pi_slot8(m), so that
