@@ -297,7 +297,7 @@ __global__ void __launch_bounds__(kThreads8, 2) attn_fwd_fp8(const uint8_t* __re
         // the scale a vector load, and its wait would also cover every tile
         // load in flight.  The empty asm keeps the two loads apart.
         float s0 = ks[slot_cube(c0)], s1 = ks[slot_cube(c1)];
-        asm volatile("" : "+s"(s0), "+s"(s1));
+        asm volatile("" : "+v"(s0), "+v"(s1));
         c[t] = fmaxf(c_q * (hf ? s1 : s0), 1e-30f);
         cnt[t] = slot_count(hf ? c1 : c0);
         full = full & (slot_count(c0) == 16) & (slot_count(c1) == 16);
