@@ -90,6 +90,11 @@ CASES = [
     {"grid": (5, 6, 7), "topk": 3, "heads": 2, "head_dim": 64},
     {"grid": (16, 12, 16), "topk": 1, "heads": 1},          # 48 cubes, 47 unselected
     {"grid": (16, 12, 16), "topk": 10, "heads": 2, "batch": 2},
+    # 728 query cubes, more than the fused pass's resident workgroups (one per
+    # compute unit): each takes several cubes in turn, with the next cube's
+    # first tiles loaded during the last steps of the one before; k = 11
+    # also gives each cube a padded step.
+    {"grid": (16, 28, 52), "topk": 11, "heads": 2, "batch": 1},
 ]
 
 
