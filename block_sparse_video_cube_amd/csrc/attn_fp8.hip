@@ -161,22 +161,27 @@ __device__ __forceinline__ int pack_p(float a, float b, float c, float d) {
 // n+1 for this lane (one per block, or per slot with packed tiles); the
 // running max of block n+1 comes out scaled by them.  kr[h]: the K resource
 // of the tile rows this wavefront's load instruction e covers, h = 64 e / D.
+// The LDS pointers are restrict: a step reads other ring slots (v_lds) than
+// it loads into (vl, kl), and saying so lets the compiler leave the loads in
+// flight across the step's LDS reads.
 template <int D, bool PARTIAL, bool SLOTS, typename MaskF>
-__device__ __forceinline__ void step8(const i32x8 (&ka)[2][D / 64], const uint8_t* __restrict__ v_lds, int n, const i32x8& ones,
+__device__ __forceinline__ void step8(const i32x8 (&ka)[2][D / 64], const uint8_t* __restrict__ v_lds, int n,
+                                      const i32x8& ones,
                                       const i32x8 (&qf)[D / 64], const f32x16 (&s_cur)[2], f32x16 (&s_next)[2],
                                       float& mx_next, const i32x8& p_prev, i32x8& p_cur, f32x16 (&o)[D / 32 + 1],
                                       const float (&c_cur)[SLOTS ? 2 : 1], const float (&c_next)[SLOTS ? 2 : 1],
                                       float mc, MaskF mask_next,
-                                      int hf, __amdgpu_buffer_rsrc_t vr, uint8_t* __restrict__ vl, const uint32_t* voff,
-                                      const __amdgpu_buffer_rsrc_t (&kr)[2], uint8_t* __restrict__ kl, const uint32_t* koff) {
+                                      int hf, __amdgpu_buffer_rsrc_t vr, uint8_t* __restrict__ vl,
+                                      const uint32_t* voff, const __amdgpu_buffer_rsrc_t (&kr)[2],
+                                      uint8_t* __restrict__ kl, const uint32_t* koff) {
   constexpr int DC = D / 64, DT = D / 32, NI = D / 32;
   s_next[0] = f32x16{};
 #pragma unroll
   for (int c = 0; c < DC; ++c) s_next[0] = mfma8(ka[0][c], qf[c], s_next[0]);
   // V^T(n-1) operands after the first key tile's products (in the registers
-  // its K operands held), and before this step's tile loads: the compiler
-  // cannot tell the buffers of a direct-to-LDS load apart, so an LDS read
-  // placed after one waits until it has landed.
+  // its K operands held), and before this step's tile loads, so that no LDS
+  // read of the step follows a direct-to-LDS load in program order (a read
+  // the compiler cannot prove apart from one waits until it has landed).
   i32x8 va[DT];
   read_v8<D>(v_lds, hf, n, va);
   // Then the V tile's loads, the second key tile's products and the K tile's loads.
@@ -451,9 +456,9 @@ __global__ void __launch_bounds__(kThreads8, 2) attn_fwd_fp8(const uint8_t* __re
     const __amdgpu_buffer_rsrc_t vr = v_load(nb);
     // Past the last block the padding loads of K target a zero-size range: no memory traffic.
     k_rsrc(nb + 3, kr);
-    step8<D, PARTIAL, SLOTS>(ka, sm.v[(u + 1) % 2], n, ones, qf, s_cur, s_next, mx_next, p_prev, p_cur, o, c_cur, c_next,
-                      mc, mask_of(nb + 1, cnt_next), hf, vr, sm.v[u % 2] + wq * NI8 * 1024, voffs, kr,
-                      sm.k[u % 3] + wq * NI8 * 1024, off.k);
+    step8<D, PARTIAL, SLOTS>(ka, sm.v[(u + 1) % 2], n, ones, qf, s_cur, s_next, mx_next, p_prev, p_cur, o, c_cur,
+                             c_next, mc, mask_of(nb + 1, cnt_next), hf, vr, sm.v[u % 2] + wq * NI8 * 1024, voffs,
+                             kr, sm.k[u % 3] + wq * NI8 * 1024, off.k);
     if constexpr (PLAN) {
       // Most tiles hold four full slots (16 valid keys each) and need no
       // mask; the test is on the tile's slot codes, so the branch is
@@ -560,7 +565,8 @@ static void launch_fp8_any(const KGeom& g, const uint8_t* q8, const float* qs, c
 hipError_t launch_attn_fwd_fp8(const KGeom& g, const uint8_t* q8, const float* qs, const uint8_t* k8,
                                const float* ks, const uint8_t* v8t, const float* vs, const int32_t* idx, int topk,
                                float scale, bool raster_out, uint16_t* o, float* lse, hipStream_t s) {
-  if (raster_out) launch_fp8_any<true, false>(g, q8, qs, k8, ks, v8t, vs, idx, nullptr, nullptr, topk, scale, o, lse, s);
+  if (raster_out)
+    launch_fp8_any<true, false>(g, q8, qs, k8, ks, v8t, vs, idx, nullptr, nullptr, topk, scale, o, lse, s);
   else launch_fp8_any<false, false>(g, q8, qs, k8, ks, v8t, vs, idx, nullptr, nullptr, topk, scale, o, lse, s);
   return hipGetLastError();
 }
