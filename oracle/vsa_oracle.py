@@ -106,6 +106,8 @@ __all__ = [
     "phi",
     "linear_cube",
     "linear_branch",
+    "linear_cube_states",
+    "unselected_sums",
     "forward",
     "sta_window",
     "sta_index",
@@ -401,6 +403,38 @@ def linear_branch(qc, kc, vc, valid, idx, cubes: Optional[Sequence[Tuple[int, in
         out[b, h, 64 * i:64 * i + 64] = linear_cube(qc[b, h, 64 * i:64 * i + 64],
                                                     states[(b, h)], idx[b, h, i])
     return out
+
+
+def linear_cube_states(kc: np.ndarray, vc: np.ndarray, valid: np.ndarray):
+    """O6's per-key-cube states of every (b, h): S [B, H, Nc, D, D] with
+    S[.., j, d, e] = sum over the valid tokens r of cube j of phi(k_r)[d] v_r[e],
+    and z [B, H, Nc, D], the sums of phi(k_r) over the same tokens."""
+    B, Hh, Np, D = kc.shape
+    nc = Np // 64
+    S = np.zeros((B, Hh, nc, D, vc.shape[3]))
+    z = np.zeros((B, Hh, nc, D))
+    for b in range(B):
+        for h in range(Hh):
+            S[b, h], z[b, h] = _cube_states(kc[b, h], vc[b, h], valid)
+    return S, z
+
+
+def unselected_sums(S: np.ndarray, z: np.ndarray, idx: np.ndarray):
+    """O6's state sums over the key cubes each query cube did not select:
+    S_U [B, H, Nc, D, D] and z_U [B, H, Nc, D] (zero where every cube is
+    selected).  O_lin of query row q is phi(q) S_U / (phi(q) . z_U)."""
+    B, Hh, nc = S.shape[:3]
+    S_u = np.zeros_like(S)
+    z_u = np.zeros_like(z)
+    for b in range(B):
+        for h in range(Hh):
+            for i in range(nc):
+                sel = set(int(j) for j in idx[b, h, i])
+                for j in range(nc):
+                    if j not in sel:
+                        S_u[b, h, i] += S[b, h, j]
+                        z_u[b, h, i] += z[b, h, j]
+    return S_u, z_u
 
 
 # --------------------------------------------------------------------------

@@ -111,3 +111,56 @@ def test_hybrid_forward_is_sum_of_branches():
     qc, kc, vc = (oracle.cube_permute(inp[n], grid) for n in ("q", "k", "v"))
     lin = oracle.cube_unpermute(oracle.linear_branch(qc, kc, vc, valid, idx), grid)
     assert np.abs(o_hyb - (o_sparse + lin)).max() < 1e-14
+
+
+@pytest.mark.parametrize("grid,topk", [((4, 4, 8), 1), ((5, 6, 7), 2), ((9, 5, 6), 4)])
+def test_state_sums_give_the_linear_branch(grid, topk):
+    """phi(Q) S_U / (phi(Q) . z_U) from the exported per-cube states and their
+    unselected sums equals linear_branch, which the per-query loops above pin."""
+    D = 8
+    rng = np.random.default_rng(5)
+    S = grid[0] * grid[1] * grid[2]
+    inp = {n: workloads.round_to_bf16_bits(rng.standard_normal((2, S, 2, D)).astype(np.float32))
+           for n in ("q", "k", "v")}
+    valid = oracle.valid_rows(grid)
+    qc, kc, vc = (oracle.cube_permute(inp[n], grid) for n in ("q", "k", "v"))
+    idx = oracle.select_topk(qc, kc, valid, topk)
+    st, z = oracle.linear_cube_states(kc, vc, valid)
+    su, zu = oracle.unselected_sums(st, z, idx)
+    nc = oracle.n_cubes(grid)
+    fq = oracle.phi(oracle.bf16_to_f64(qc)).reshape(2, 2, nc, 64, D)
+    num = np.einsum("bhird,bhide->bhire", fq, su)
+    den = np.einsum("bhird,bhid->bhir", fq, zu)
+    got = (num / den[..., None]).reshape(2, 2, nc * 64, D)
+    ref = oracle.linear_branch(qc, kc, vc, valid, idx)
+    assert np.abs(got - ref).max() < 1e-12
+
+
+def test_cube_states_sum_to_the_whole_grid():
+    """Summed over all cubes, the states are phi(K)^T V and the column sums of
+    phi(K) over every raster token of the grid (padding contributes nothing)."""
+    grid, D = (5, 7, 6), 8
+    rng = np.random.default_rng(9)
+    S = grid[0] * grid[1] * grid[2]
+    k = workloads.round_to_bf16_bits(rng.standard_normal((1, S, 1, D)).astype(np.float32))
+    v = workloads.round_to_bf16_bits(rng.standard_normal((1, S, 1, D)).astype(np.float32))
+    valid = oracle.valid_rows(grid)
+    st, z = oracle.linear_cube_states(oracle.cube_permute(k, grid), oracle.cube_permute(v, grid), valid)
+    kf = oracle.phi(oracle.bf16_to_f64(k[0, :, 0]))
+    vf = oracle.bf16_to_f64(v[0, :, 0])
+    assert np.abs(st[0, 0].sum(axis=0) - kf.T @ vf).max() < 1e-10
+    assert np.abs(z[0, 0].sum(axis=0) - kf.sum(axis=0)).max() < 1e-10
+
+
+def test_unselected_sums_of_a_full_selection_are_zero():
+    grid, D = (4, 8, 8), 4
+    rng = np.random.default_rng(2)
+    S = grid[0] * grid[1] * grid[2]
+    kc, vc = (oracle.cube_permute(workloads.round_to_bf16_bits(
+        rng.standard_normal((1, S, 1, D)).astype(np.float32)), grid) for _ in range(2))
+    valid = oracle.valid_rows(grid)
+    st, z = oracle.linear_cube_states(kc, vc, valid)
+    nc = oracle.n_cubes(grid)
+    idx = np.tile(np.arange(nc, dtype=np.int32), (1, 1, nc, 1))
+    su, zu = oracle.unselected_sums(st, z, idx)
+    assert not su.any() and not zu.any()
