@@ -62,6 +62,10 @@ def parse():
     ap.add_argument("--fused-linear", action="store_true",
                     help="hybrid layer: the fine stage and the linear branch in one fused pass "
                          "(vsa_sparse_attn_linear_fwd) instead of two calls with fp32 O_sparse in between")
+    ap.add_argument("--linear-tiles", action="store_true",
+                    help="hybrid layer: the linear branch as total minus selected blocks on K/V tiles "
+                         "(vsa_linear_state + vsa_linear_apply after the fine stage's fp32 output) instead of "
+                         "summed per-cube states applied in the fine stage's epilogue")
     ap.add_argument("--fp8", action="store_true",
                     help="low-precision layer: Q, K, V quantized to fp8 E4M3 in the step, fine stage on the "
                          "fp8 matrix cores (roofline against the fp8 peak)")
@@ -361,7 +365,8 @@ def main():
     # (the linear branch's state reads cube-major keys); its two calls read
     # raster Q and write the raster output (the fused pass keeps the
     # permute / unpermute pair).
-    stages = vsa.layer_stages(wl.linear, args.fused_linear)
+    linear_mode = "tiles" if args.linear_tiles else "states"
+    stages = vsa.layer_stages(wl.linear, args.fused_linear, linear_mode)
     if args.fp8:
         if wl.linear:
             print("--fp8 covers the fine stage without the linear branch", file=sys.stderr)
@@ -416,7 +421,7 @@ def main():
                           fused_linear=args.fused_linear, k_raster=args.k_raster,
                           window=wl.window if wl.pattern == "sta" else None, bufs=bufs, out=o,
                           mark=(lambda i: ev[i].record()) if ev is not None else None,
-                          packed=not args.unpacked, overlap=not args.one_stream)
+                          packed=not args.unpacked, overlap=not args.one_stream, linear_mode=linear_mode)
 
     for _ in range(args.warmup):
         step()
@@ -462,6 +467,9 @@ def main():
     if wl.linear and args.fused_linear:
         kname = "attn_lin_fwd (stage includes lin_state, lin_reduce)"
         traffic = None
+    elif wl.linear and linear_mode == "states":
+        kname = "attn_fwd with the linear branch's epilogue"
+        traffic = None
     if args.fp8:
         alg_bytes = B * H * d.rows * D * (1 + 1 + 1 + 2) + 4 * B * H * (2 * d.n_cubes + D)
         peak, kname = PEAK_FP8_TFLOPS, "attn_fwd_fp8"
@@ -485,7 +493,11 @@ def main():
             "latent_grid": list(wl.grid), "padded_grid": list(wl.padded_grid),
             "tokens": wl.tokens, "n_cubes": wl.n_cubes, "topk": wl.topk,
             "sparsity": wl.sparsity, "linear_branch": wl.linear, "pattern": wl.pattern,
-            "layout": ("cube-major" if wl.linear else ("raster q, k, v in; fp8 cube-major codes" +
+            **({"linear_branch_form": ("fused pass" if args.fused_linear else
+                                       ("tiles: total minus selected blocks" if linear_mode == "tiles" else
+                                        "summed per-cube states, applied in the fine stage's epilogue"))}
+               if wl.linear else {}),
+            "layout": ("raster q/o; cube-major k, cube-transposed v" if wl.linear else ("raster q, k, v in; fp8 cube-major codes" +
                                                      ("; packed tiles: compact k, slot-layout v" if args.fp8 and
                                                       fp8_packed else "") + "; raster o")
                        if args.fp8 else ("raster q/k/o" if args.k_raster else

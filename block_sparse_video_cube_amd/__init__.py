@@ -46,6 +46,10 @@ __all__ = [
     "linear_branch",
     "linear_state",
     "linear_apply",
+    "linear_cube_states",
+    "linear_unselected",
+    "linear_unselected_workspace_bytes",
+    "sparse_attn_fwd_linear",
     "sparse_attn_fwd_raster",
     "sparse_attn_fwd_packed",
     "packed_workspace_bytes",
@@ -604,6 +608,83 @@ def linear_apply(q: torch.Tensor, vt: torch.Tensor, idx: torch.Tensor, o_sparse:
     return out
 
 
+def linear_cube_states(kc: torch.Tensor, vt: torch.Tensor, grid: Sequence[int],
+                       out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Per-cube states of the linear branch (vsa_linear_cube_states): bf16
+    [B, heads, D + 1, Nc, D], [.., e, j, d] = (phi(K_j)^T V_j)[d, e] for e < D
+    and the column sums of phi(K_j) at e = D."""
+    B, Hh, _, D = kc.shape
+    g = make_geom(B, Hh, D, grid)
+    d = geom_dims(g)
+    _need(kc, "kc", torch.bfloat16, (B, Hh, d.rows, D))
+    _need(vt, "vt", torch.bfloat16, (B, Hh, d.n_cubes, D, 64))
+    shape = (B, Hh, D + 1, d.n_cubes, D)
+    if out is None:
+        out = torch.empty(shape, dtype=torch.bfloat16, device=kc.device)
+    _need(out, "states", torch.bfloat16, shape)
+    _lib.check("vsa_linear_cube_states", _lib.load().vsa_linear_cube_states(
+        g, kc.data_ptr(), vt.data_ptr(), out.data_ptr(), _stream()))
+    return out
+
+
+def linear_unselected_workspace_bytes(g: VsaGeom) -> int:
+    return int(_lib.load().vsa_linear_unselected_workspace_bytes(g))
+
+
+def linear_unselected(states: torch.Tensor, idx: torch.Tensor, grid: Sequence[int],
+                      out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Summed states of every query cube's unselected key cubes
+    (vsa_linear_unselected): bf16 [B, heads, Nc, D * D + D], S_U^T rows then z_U."""
+    B, Hh, D = states.shape[0], states.shape[1], states.shape[4]
+    g = make_geom(B, Hh, D, grid)
+    d = geom_dims(g)
+    topk = idx.shape[-1]
+    _need(states, "states", torch.bfloat16, (B, Hh, D + 1, d.n_cubes, D))
+    _need(idx, "idx", torch.int32, (B, Hh, d.n_cubes, topk))
+    shape = (B, Hh, d.n_cubes, D * D + D)
+    if out is None:
+        out = torch.empty(shape, dtype=torch.bfloat16, device=states.device)
+    _need(out, "su", torch.bfloat16, shape)
+    if workspace is None:
+        workspace = torch.empty(max(16, linear_unselected_workspace_bytes(g)), dtype=torch.uint8,
+                                device=states.device)
+    _lib.check("vsa_linear_unselected", _lib.load().vsa_linear_unselected(
+        g, states.data_ptr(), idx.data_ptr(), int(topk), out.data_ptr(), workspace.data_ptr(),
+        workspace.numel() * workspace.element_size(), _stream()))
+    return out
+
+
+def sparse_attn_fwd_linear(q: torch.Tensor, kc: torch.Tensor, vt: torch.Tensor, idx: torch.Tensor,
+                           su: torch.Tensor, grid: Sequence[int], scale: Optional[float] = None,
+                           raster: bool = True, out: Optional[torch.Tensor] = None,
+                           lse: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Fine stage plus the linear branch from summed states
+    (vsa_sparse_attn_fwd_linear): bf16(O_sparse + phi(Q) S_U / (phi(Q) . z_U)),
+    q and the output raster [B, S, heads, D] (or cube-major rows)."""
+    B, Hh, _, D = kc.shape
+    g = make_geom(B, Hh, D, grid)
+    d = geom_dims(g)
+    topk = idx.shape[-1]
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    qo_shape = (B, d.tokens, Hh, D) if raster else (B, Hh, d.rows, D)
+    _need(q, "q" if raster else "qc", torch.bfloat16, qo_shape)
+    _need(kc, "kc", torch.bfloat16, (B, Hh, d.rows, D))
+    _need(vt, "vt", torch.bfloat16, (B, Hh, d.n_cubes, D, 64))
+    _need(idx, "idx", torch.int32, (B, Hh, d.n_cubes, topk))
+    _need(su, "su", torch.bfloat16, (B, Hh, d.n_cubes, D * D + D))
+    if out is None:
+        out = torch.empty(qo_shape, dtype=torch.bfloat16, device=q.device)
+    _need(out, "o", torch.bfloat16, qo_shape)
+    if lse is not None:
+        _need(lse, "lse", torch.float32, (B, Hh, d.rows))
+    _lib.check("vsa_sparse_attn_fwd_linear", _lib.load().vsa_sparse_attn_fwd_linear(
+        g, q.data_ptr(), _lib.VSA_LAYOUT_RASTER if raster else _lib.VSA_LAYOUT_TOKEN_MAJOR, kc.data_ptr(),
+        vt.data_ptr(), idx.data_ptr(), int(topk), float(scale), su.data_ptr(), out.data_ptr(),
+        lse.data_ptr() if lse is not None else None, _stream()))
+    return out
+
+
 def linear_branch_bwd(qc: torch.Tensor, kc: torch.Tensor, vc: torch.Tensor, vt: torch.Tensor, idx: torch.Tensor,
                       doc: torch.Tensor, grid: Sequence[int], workspace: Optional[torch.Tensor] = None,
                       add: Optional[Tuple[torch.Tensor, torch.Tensor, torch.Tensor]] = None, out=None,
@@ -793,6 +874,13 @@ class LayerBuffers:
         self.of = torch.empty((B, H, d.rows, D), dtype=torch.float32, device=dev) if linear else None
         self.ws_lin = (torch.empty(max(16, workspace_bytes(g, linear=True)), dtype=torch.uint8, device=dev)
                        if linear else None)
+        # Linear branch from summed states: per-cube states, summed states per
+        # query cube and the selection bits.
+        self.states = (torch.empty((B, H, D + 1, d.n_cubes, D), dtype=torch.bfloat16, device=dev)
+                       if linear else None)
+        self.su = torch.empty((B, H, d.n_cubes, D * D + D), dtype=torch.bfloat16, device=dev) if linear else None
+        self.ws_bits = (torch.empty(max(16, linear_unselected_workspace_bytes(g)), dtype=torch.uint8, device=dev)
+                        if linear else None)
         # Second stream (default priority) for the V permute, which depends on
         # nothing the coarse stage makes and runs beside it.
         self.side = torch.cuda.Stream(device=dev)
@@ -802,12 +890,15 @@ class LayerBuffers:
         self.ev_state = torch.cuda.Event()
 
 
-def layer_stages(linear: bool = False, fused_linear: bool = False):
+def layer_stages(linear: bool = False, fused_linear: bool = False, linear_mode: str = "states"):
     """Names of the stages layer_forward runs, in order (its `mark` hook is
     called once before the first and once after each)."""
     if linear:
-        return (["permute", "select", "fine+linear", "unpermute"] if fused_linear else
-                ["pool", "select", "fine", "linear"])
+        if fused_linear:
+            return ["permute", "select", "fine+linear", "unpermute"]
+        if linear_mode == "states":
+            return ["pool", "select", "unselected", "fine+linear"]
+        return ["pool", "select", "fine", "linear"]
     return ["pool", "select", "fine"]
 
 
@@ -815,7 +906,7 @@ def layer_forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, grid: Seque
                   scale: Optional[float] = None, linear: bool = False, fused_linear: bool = False,
                   k_raster: bool = False, window: Optional[Sequence[int]] = None,
                   bufs: Optional[LayerBuffers] = None, out: Optional[torch.Tensor] = None, mark=None,
-                  packed: bool = True, overlap: bool = True):
+                  packed: bool = True, overlap: bool = True, linear_mode: str = "states"):
     """One forward attention layer on raster q, k, v [B, S, heads, D] bf16:
     returns (o [B, S, heads, D] bf16, idx).
 
@@ -846,6 +937,9 @@ def layer_forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, grid: Seque
     B, S, H, D = q.shape
     if scale is None:
         scale = 1.0 / math.sqrt(D)
+    if linear_mode not in ("states", "tiles"):
+        raise ValueError(f"linear_mode must be 'states' or 'tiles', not {linear_mode!r}")
+    states_mode = linear and not fused_linear and linear_mode == "states"
     if bufs is None:
         bufs = LayerBuffers(B, H, D, grid, topk, linear=linear, device=q.device)
     if out is None:
@@ -883,7 +977,12 @@ def layer_forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, grid: Seque
         else:
             cube_permute(v, grid, layout="dim", out=b.vt)
         b.ev_v.record(side)
-        if linear and not fused_linear:
+        if states_mode:
+            # The per-cube states need only K and V: they run here too, beside
+            # the coarse stage.
+            linear_cube_states(b.kc, b.vt, grid, out=b.states)
+            b.ev_state.record(side)
+        elif linear and not fused_linear:
             # The linear branch's state (phi(K), S_tot, z_tot) needs only K and
             # V: it runs here too, beside the coarse and fine stages.
             linear_state(b.kc, b.vt, grid, b.ws_lin)
@@ -902,6 +1001,15 @@ def layer_forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, grid: Seque
         else:
             sparse_attn_fwd_raster(q, k if k_raster else b.kc, b.vt, b.idx, grid, scale, out=out)
         mark(3)
+        return out, b.idx
+    if states_mode:
+        # The summed states of every query cube's unselected cubes, then the
+        # fine stage, which adds the linear branch in its epilogue.
+        main.wait_event(b.ev_state)
+        linear_unselected(b.states, b.idx, grid, out=b.su, workspace=b.ws_bits)
+        mark(3)
+        sparse_attn_fwd_linear(q, b.kc, b.vt, b.idx, b.su, grid, scale, raster=True, out=out)
+        mark(4)
         return out, b.idx
     if fused_linear:
         sparse_attn_linear_fwd(b.qc, b.kc, b.vt, b.idx, grid, scale, out=b.oc2, workspace=b.ws_lin)

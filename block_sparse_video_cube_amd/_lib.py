@@ -44,6 +44,12 @@ ENTRY_POINTS = (
     "vsa_linear_branch",
     "vsa_linear_state",
     "vsa_linear_apply",
+    "vsa_linear_states_bytes",
+    "vsa_linear_unselected_bytes",
+    "vsa_linear_unselected_workspace_bytes",
+    "vsa_linear_cube_states",
+    "vsa_linear_unselected",
+    "vsa_sparse_attn_fwd_linear",
     "vsa_sta_topk",
     "vsa_sta_index",
     "vsa_cube_pool",
@@ -131,6 +137,12 @@ def load() -> ctypes.CDLL:
         "vsa_linear_branch": (i32, [G, P, i32, P, P, P, i32, P, P, P, P, P, sz, P]),
         "vsa_linear_state": (i32, [G, P, P, P, sz, P]),
         "vsa_linear_apply": (i32, [G, P, i32, P, P, i32, P, P, P, P, P, sz, P]),
+        "vsa_linear_states_bytes": (sz, [G]),
+        "vsa_linear_unselected_bytes": (sz, [G]),
+        "vsa_linear_unselected_workspace_bytes": (sz, [G]),
+        "vsa_linear_cube_states": (i32, [G, P, P, P, P]),
+        "vsa_linear_unselected": (i32, [G, P, P, i32, P, P, sz, P]),
+        "vsa_sparse_attn_fwd_linear": (i32, [G, P, i32, P, P, P, i32, ctypes.c_float, P, P, P, P]),
         "vsa_sta_topk": (i32, [G, i32, i32, i32]),
         "vsa_sta_index": (i32, [G, i32, i32, i32, P, P]),
         "vsa_cube_pool": (i32, [G, P, P, P]),

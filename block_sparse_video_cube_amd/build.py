@@ -23,7 +23,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 OUT = os.path.join(PKG, "libvsa_cube.so")
 
-SOURCES = ["api.hip", "permute.hip", "select.hip", "sta.hip", "attn_fwd.hip", "attn_lin.hip", "attn_bwd.hip", "quant.hip", "attn_fp8.hip", "linear.hip", "linear_bwd.hip", "probe.hip"]
+SOURCES = ["api.hip", "permute.hip", "select.hip", "sta.hip", "attn_fwd.hip", "attn_lin.hip", "attn_bwd.hip", "quant.hip", "attn_fp8.hip", "linear.hip", "linear_bwd.hip", "linear_states.hip", "probe.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

@@ -546,4 +546,67 @@ int32_t vsa_linear_branch(const vsa_geom* g, const uint16_t* qc, int32_t qo_layo
                                           qo_layout == VSA_LAYOUT_RASTER, ws, static_cast<hipStream_t>(stream)));
 }
 
+size_t vsa_linear_states_bytes(const vsa_geom* g) {
+  vsa_dims d;
+  vsa::KGeom k;
+  if (prepare(g, &d, &k) != VSA_OK) return 0;
+  return vsa::linear_states_bytes(k);
+}
+
+size_t vsa_linear_unselected_bytes(const vsa_geom* g) {
+  vsa_dims d;
+  vsa::KGeom k;
+  if (prepare(g, &d, &k) != VSA_OK) return 0;
+  return vsa::linear_unsel_bytes(k);
+}
+
+size_t vsa_linear_unselected_workspace_bytes(const vsa_geom* g) {
+  vsa_dims d;
+  vsa::KGeom k;
+  if (prepare(g, &d, &k) != VSA_OK) return 0;
+  return vsa::linear_unsel_workspace_bytes(k);
+}
+
+int32_t vsa_linear_cube_states(const vsa_geom* g, const uint16_t* kc, const uint16_t* vt, uint16_t* states,
+                               void* stream) {
+  vsa_dims d;
+  vsa::KGeom k;
+  int32_t st = prepare(g, &d, &k);
+  if (st != VSA_OK) return st;
+  if (!kc || !vt || !states) return VSA_ERR_NULL;
+  if (!aligned16(kc) || !aligned16(vt) || !aligned16(states)) return VSA_ERR_ALIGN;
+  return launch_status(vsa::launch_lin_cube_states(k, kc, vt, states, static_cast<hipStream_t>(stream)));
+}
+
+int32_t vsa_linear_unselected(const vsa_geom* g, const uint16_t* states, const int32_t* idx, int32_t topk,
+                              uint16_t* su, void* ws, size_t ws_bytes, void* stream) {
+  vsa_dims d;
+  vsa::KGeom k;
+  int32_t st = prepare(g, &d, &k);
+  if (st != VSA_OK) return st;
+  if (!states || !idx || !su || !ws) return VSA_ERR_NULL;
+  if (!aligned16(states) || !aligned16(idx) || !aligned16(su) || !aligned16(ws)) return VSA_ERR_ALIGN;
+  if (topk < 1 || topk > d.n_cubes) return VSA_ERR_TOPK;
+  if (ws_bytes < vsa::linear_unsel_workspace_bytes(k)) return VSA_ERR_WORKSPACE;
+  return launch_status(vsa::launch_lin_unselected(k, states, idx, topk, su, ws, static_cast<hipStream_t>(stream)));
+}
+
+int32_t vsa_sparse_attn_fwd_linear(const vsa_geom* g, const uint16_t* q, int32_t qo_layout, const uint16_t* kc,
+                                   const uint16_t* vt, const int32_t* idx, int32_t topk, float softmax_scale,
+                                   const uint16_t* su, uint16_t* o, float* lse, void* stream) {
+  vsa_dims d;
+  vsa::KGeom k;
+  int32_t st = prepare(g, &d, &k);
+  if (st != VSA_OK) return st;
+  if (!q || !kc || !vt || !idx || !su || !o) return VSA_ERR_NULL;
+  if (!aligned16(q) || !aligned16(kc) || !aligned16(vt) || !aligned16(idx) || !aligned16(su) || !aligned16(o) ||
+      (lse && !aligned16(lse)))
+    return VSA_ERR_ALIGN;
+  if (qo_layout != VSA_LAYOUT_TOKEN_MAJOR && qo_layout != VSA_LAYOUT_RASTER) return VSA_ERR_LAYOUT;
+  if (topk < 1 || topk > d.n_cubes) return VSA_ERR_TOPK;
+  if (!(softmax_scale > 0.f) || !isfinite(softmax_scale)) return VSA_ERR_SCALE;
+  return launch_status(vsa::launch_attn_fwd_linear(k, q, qo_layout == VSA_LAYOUT_RASTER, kc, vt, idx, topk,
+                                                   softmax_scale, su, o, lse, static_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

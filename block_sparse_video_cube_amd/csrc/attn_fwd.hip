@@ -64,7 +64,11 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t k_tile_rsrc(const uint16_t* kb
 // tile.  With PARTIAL the tiles come from a packing plan (block_plan: up to
 // four cubes with few valid keys share a tile) and keys are masked by slot
 // counts; without it every tile is one whole cube of the list.
-template <int D, bool PARTIAL, bool RASTER, bool KRASTER, bool SLOTS>
+// LIN (full tiles, cube-major K): the linear branch over the unselected cubes
+// is added in the epilogue from the query cube's summed states (su: S_U^T
+// rows, then z_U, as lin_unsel_sum writes them): O = O_sparse + phi(Q) S_U /
+// (phi(Q) . z_U), rounded to bf16 once.
+template <int D, bool PARTIAL, bool RASTER, bool KRASTER, bool SLOTS, bool LIN = false>
 __global__ void __launch_bounds__(kThreads, 2) attn_fwd(const uint16_t* __restrict__ qc,
                                                         const uint16_t* __restrict__ kc,
                                                         const uint16_t* __restrict__ vt,
@@ -73,8 +77,9 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd(const uint16_t* __restri
                                                         const int32_t* __restrict__ order, int topk, float scale,
                                                         float scale_log2, uint16_t* __restrict__ oc,
                                                         float* __restrict__ oc_f32, float* __restrict__ lse,
-                                                        KGeom g, Placement pl) {
+                                                        KGeom g, Placement pl, const uint16_t* __restrict__ su) {
   static_assert(!(SLOTS && KRASTER), "packed tiles read cube-major K");
+  static_assert(!(LIN && (SLOTS || KRASTER)), "the linear epilogue runs on full tiles of cube-major K");
   constexpr bool PLAN = SLOTS && PARTIAL;
   constexpr int DC = D / 16, DT = D / 32;
   constexpr int NI = TileOffsets<D>::NI, KRPI = TileOffsets<D>::KRPI;
@@ -280,6 +285,51 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd(const uint16_t* __restri
         o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[dt][kk], p_prev[kk], o[dt], 0, 0, 0);
   }
 
+  // Linear branch (LIN): lin^T[e][q] = sum_d S_U^T[e][d] phi(Q)[q][d] for this
+  // wavefront's half of the value dims e (tiles DT/2 wk ..), the A operands
+  // straight from the query cube's S_U^T rows (eight consecutive d per lane),
+  // the B operands phi(Q) from the Q fragments; the wk = 0 wavefronts also
+  // form den = phi(Q) . z_U (both lane halves).
+  constexpr int LT = LIN ? DT / 2 : 1;
+  f32x16 lin[LT];
+  float den = 0.f;
+  if constexpr (LIN) {
+    const uint16_t* sui = su + (bh * g.nc + i) * (long long)(D * D + D);
+    bf16x8 fq[DC];
+#pragma unroll
+    for (int dc = 0; dc < DC; ++dc) {
+      const uint4 raw = __builtin_bit_cast(uint4, qf[dc]);
+      fq[dc] = __builtin_bit_cast(
+          bf16x8, make_uint4(phi2_bf16(raw.x), phi2_bf16(raw.y), phi2_bf16(raw.z), phi2_bf16(raw.w)));
+    }
+#pragma unroll
+    for (int t = 0; t < LT; ++t) {
+      const int dt = wk * LT + t;
+      bf16x8 a[DC];
+#pragma unroll
+      for (int dc = 0; dc < DC; ++dc)
+        a[dc] = *reinterpret_cast<const bf16x8*>(sui + (32 * dt + n) * D + 16 * dc + 8 * hf);
+      lin[t] = f32x16{};
+#pragma unroll
+      for (int dc = 0; dc < DC; ++dc) lin[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[dc], fq[dc], lin[t], 0, 0, 0);
+    }
+    if (wk == 0) {
+      uint4 zr[DC];
+#pragma unroll
+      for (int dc = 0; dc < DC; ++dc) zr[dc] = *reinterpret_cast<const uint4*>(sui + D * D + 16 * dc + 8 * hf);
+#pragma unroll
+      for (int dc = 0; dc < DC; ++dc) {
+        const uint4 fw = __builtin_bit_cast(uint4, fq[dc]);
+        const uint32_t fa[4] = {fw.x, fw.y, fw.z, fw.w}, za[4] = {zr[dc].x, zr[dc].y, zr[dc].z, zr[dc].w};
+#pragma unroll
+        for (int e2 = 0; e2 < 4; ++e2)
+          den = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, fa[e2]), __builtin_bit_cast(bf16x2, za[e2]),
+                                                den, false);
+      }
+      den += __shfl_xor(den, 32);
+    }
+  }
+
   // Merge the two key halves: wavefronts with wk = 1 hand (m, l, O^T) over.
   l_run += __shfl_xor(l_run, 32);
   wait_vmcnt<0>();  // the padding loads past the end target the K buffers
@@ -293,9 +343,20 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd(const uint16_t* __restri
       for (int r = 0; r < 16; ++r) xo[(dt * 16 + r) * 64 + lane] = o[dt][r];
     xm[lane] = m_run;
     xm[64 + lane] = l_run;
+    if constexpr (LIN) {
+      // Its value-dim tiles of the linear branch, in the second V buffer.
+      float* xl = reinterpret_cast<float*>(&sm.v[1][0]) + wq * (LT * 16 * 64);
+#pragma unroll
+      for (int t = 0; t < LT; ++t)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) xl[(t * 16 + r) * 64 + lane] = lin[t][r];
+    }
   }
   __syncthreads();
   if (wk == 1) return;
+  // No unselected cube (den = 0): the linear branch is 0.
+  const float inv_den = (LIN && den > 0.f) ? 1.f / den : 0.f;
+  const float* xl = reinterpret_cast<const float*>(&sm.v[1][0]) + wq * (LT * 16 * 64);
   const float m1 = xm[lane], l1 = xm[64 + lane];
   const float m = fmaxf(m_run, m1);
   const float a0 = __builtin_amdgcn_exp2f((m_run - m) * scale_log2);
@@ -316,6 +377,10 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd(const uint16_t* __restri
       for (int e = 0; e < 4; ++e) {
         const int r = 4 * gq + e;
         v[e] = o[dt][r] * c0 + xo[(dt * 16 + r) * 64 + lane] * c1;
+        if constexpr (LIN) {
+          const float lv = (dt < LT) ? lin[dt < LT ? dt : 0][r] : xl[((dt - LT) * 16 + r) * 64 + lane];
+          v[e] += lv * inv_den;
+        }
       }
       if (qvalid && orow) *reinterpret_cast<uint2*>(orow + d) = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
       if (oc_f32) *reinterpret_cast<float4*>(oc_f32 + row * D + d) = make_float4(v[0], v[1], v[2], v[3]);
@@ -479,14 +544,14 @@ __global__ void __launch_bounds__(256) plan_order_count(const int32_t* __restric
   for (int c = threadIdx.x; c < nc; c += 256) order[bh * nc + atomicAdd(&bins[rows[c * stride]], 1)] = c;
 }
 
-template <int D, bool PARTIAL, bool RASTER, bool KRASTER, bool SLOTS = false>
+template <int D, bool PARTIAL, bool RASTER, bool KRASTER, bool SLOTS = false, bool LIN = false>
 void launch_fwd(const KGeom& g, const uint16_t* qc, const uint16_t* kc, const uint16_t* vt, const int32_t* idx,
                 const int32_t* plan, const int32_t* order, int topk, float scale, uint16_t* oc, float* oc_f32,
-                float* lse, hipStream_t s) {
+                float* lse, hipStream_t s, const uint16_t* su = nullptr) {
   const Placement pl = make_placement(g);
   const float scale_log2 = scale * 1.4426950408889634f;
-  attn_fwd<D, PARTIAL, RASTER, KRASTER, SLOTS><<<dim3(grid_size(g)), dim3(kThreads), 0, s>>>(
-      qc, kc, vt, idx, plan, order, topk, scale, scale_log2, oc, oc_f32, lse, g, pl);
+  attn_fwd<D, PARTIAL, RASTER, KRASTER, SLOTS, LIN><<<dim3(grid_size(g)), dim3(kThreads), 0, s>>>(
+      qc, kc, vt, idx, plan, order, topk, scale, scale_log2, oc, oc_f32, lse, g, pl, su);
 }
 
 template <bool RASTER, bool KRASTER>
@@ -516,6 +581,22 @@ hipError_t launch_attn_fwd_raster(const KGeom& g, const uint16_t* q, const uint1
                                   float* o_f32, float* lse, hipStream_t s) {
   if (k_raster) return launch_fwd_any<true, true>(g, q, k, vt, idx, topk, scale, o, o_f32, lse, s);
   return launch_fwd_any<true, false>(g, q, k, vt, idx, topk, scale, o, o_f32, lse, s);
+}
+
+hipError_t launch_attn_fwd_linear(const KGeom& g, const uint16_t* q, bool raster, const uint16_t* kc,
+                                  const uint16_t* vt, const int32_t* idx, int topk, float scale, const uint16_t* su,
+                                  uint16_t* o, float* lse, hipStream_t s) {
+#define VSA_LIN(DD, PP, RR) \
+  launch_fwd<DD, PP, RR, false, false, true>(g, q, kc, vt, idx, nullptr, nullptr, topk, scale, o, nullptr, lse, s, su)
+  if (g.D == 64) {
+    if (g.partial) { if (raster) VSA_LIN(64, true, true); else VSA_LIN(64, true, false); }
+    else { if (raster) VSA_LIN(64, false, true); else VSA_LIN(64, false, false); }
+  } else {
+    if (g.partial) { if (raster) VSA_LIN(128, true, true); else VSA_LIN(128, true, false); }
+    else { if (raster) VSA_LIN(128, false, true); else VSA_LIN(128, false, false); }
+  }
+#undef VSA_LIN
+  return hipGetLastError();
 }
 
 // Packed workspace: the plan (16 bytes per tile and a 16-byte header per

@@ -35,6 +35,22 @@ size_t attn_packed_workspace_bytes(const KGeom& g, int topk);
 hipError_t launch_attn_fwd_packed(const KGeom& g, const uint16_t* q, bool raster, const uint16_t* kc,
                                   const uint16_t* vs, const int32_t* idx, int topk, float scale, uint16_t* o,
                                   float* lse, void* ws, hipStream_t s);
+// Linear branch through per-cube states (linear_states.hip): the states
+// [B, H, D + 1, Nc, D] bf16 of every key cube, the summed states of the
+// unselected cubes [B, H, Nc, D * D + D] bf16 of every query cube (ws: the
+// selection bits, linear_unsel_workspace_bytes), and the fine stage that adds
+// phi(Q) S_U / (phi(Q) . z_U) in its epilogue (q and o raster or cube-major;
+// kc cube-major token rows, vt cube-transposed).
+size_t linear_states_bytes(const KGeom& g);
+size_t linear_unsel_bytes(const KGeom& g);
+size_t linear_unsel_workspace_bytes(const KGeom& g);
+hipError_t launch_lin_cube_states(const KGeom& g, const uint16_t* kc, const uint16_t* vt, uint16_t* st,
+                                  hipStream_t s);
+hipError_t launch_lin_unselected(const KGeom& g, const uint16_t* st, const int32_t* idx, int topk, uint16_t* su,
+                                 void* ws, hipStream_t s);
+hipError_t launch_attn_fwd_linear(const KGeom& g, const uint16_t* q, bool raster, const uint16_t* kc,
+                                  const uint16_t* vt, const int32_t* idx, int topk, float scale, const uint16_t* su,
+                                  uint16_t* o, float* lse, hipStream_t s);
 // The packing plan and launch order of a grid with partial cubes into ws (the
 // packed stages' workspace; nothing for a full grid).
 hipError_t launch_packed_plan(const KGeom& g, const int32_t* idx, int topk, void* ws, hipStream_t s);

@@ -434,6 +434,55 @@ int32_t vsa_linear_apply(const vsa_geom* g, const uint16_t* qc, int32_t qo_layou
                          const float* o_sparse, uint16_t* oc, float* o_lin, float* inv_den,
                          void* ws, size_t ws_bytes, void* stream);
 
+/* The linear branch through summed per-cube states (the linear-attention
+ * branch over the cubes the top-k left out: SparkDiffusion article, paragraph
+ * 3, RoLA; TurboDiffusion article, section "稀疏、蒸馏与全链路量化", SLA).
+ * For query cube i with unselected key cubes U(i):
+ *   O_lin = phi(Q_i) S_U / (phi(Q_i) . z_U),  S_U = sum_{j in U(i)} S_j,
+ *   S_j = phi(K_j)^T V_j over the valid keys of cube j, z_j their phi(K_j) sums.
+ * Three calls, each asynchronous on `stream`, ordered by the caller:
+ *
+ * vsa_linear_cube_states: states [B, heads, D + 1, Nc, D] bf16 from kc
+ * (TOKEN_MAJOR) and vt (DIM_MAJOR): states[b, h, e, j, d] = S_j[d, e] for
+ * e < D (d the phi feature, e the value dim) and states[b, h, D, j, d] =
+ * z_j[d]; fp32 sums of the bf16-rounded phi(K) and V, rounded to bf16 once.
+ * vsa_linear_states_bytes(g) gives its size.
+ *
+ * vsa_linear_unselected: su [B, heads, Nc, D * D + D] bf16, for query cube i
+ * su[.., i, e * D + d] = S_U[d, e] and su[.., i, D * D + d] = z_U[d]: the
+ * states of the cubes NOT in idx[b, h, i, :] summed in fp32 (one dense 0/1
+ * product per head on the matrix cores), rounded to bf16 once; all zero when
+ * every cube is selected.  idx as for the fine stage (entries in 0..Nc-1; an
+ * entry outside that range selects nothing).  ws: at least
+ * vsa_linear_unselected_workspace_bytes(g) bytes (the selection bits);
+ * vsa_linear_unselected_bytes(g) gives the size of su.
+ *
+ * vsa_sparse_attn_fwd_linear: the fine stage of vsa_sparse_attn_fwd with the
+ * linear branch added before its one rounding: o = bf16(O_sparse + O_lin),
+ * O_lin = 0 where z_U = 0.  qo_layout: VSA_LAYOUT_RASTER (q and o raster
+ * [B, S, heads, D], every token written) or VSA_LAYOUT_TOKEN_MAJOR (q and o
+ * cube-major rows); kc TOKEN_MAJOR, vt DIM_MAJOR, idx and softmax_scale as for
+ * vsa_sparse_attn_fwd; su from vsa_linear_unselected for the same kc, vt and
+ * idx; lse: optional, as for vsa_sparse_attn_fwd (the softmax branch's).
+ *
+ * All pointers are device memory owned by the caller (16-byte aligned); none
+ * of the outputs may overlap an input.  Errors (nothing launched):
+ * VSA_ERR_NULL, VSA_ERR_ALIGN, VSA_ERR_GEOMETRY / VSA_ERR_HEAD_DIM (bad g),
+ * VSA_ERR_TOPK (topk outside 1..Nc), VSA_ERR_WORKSPACE (ws too small),
+ * VSA_ERR_LAYOUT (qo_layout), VSA_ERR_SCALE (softmax_scale not finite and
+ * positive), VSA_ERR_LAUNCH.  The sizing calls return 0 for a bad g. */
+size_t vsa_linear_states_bytes(const vsa_geom* g);
+size_t vsa_linear_unselected_bytes(const vsa_geom* g);
+size_t vsa_linear_unselected_workspace_bytes(const vsa_geom* g);
+int32_t vsa_linear_cube_states(const vsa_geom* g, const uint16_t* kc, const uint16_t* vt,
+                               uint16_t* states, void* stream);
+int32_t vsa_linear_unselected(const vsa_geom* g, const uint16_t* states, const int32_t* idx,
+                              int32_t topk, uint16_t* su, void* ws, size_t ws_bytes, void* stream);
+int32_t vsa_sparse_attn_fwd_linear(const vsa_geom* g, const uint16_t* q, int32_t qo_layout,
+                                   const uint16_t* kc, const uint16_t* vt, const int32_t* idx,
+                                   int32_t topk, float softmax_scale, const uint16_t* su,
+                                   uint16_t* o, float* lse, void* stream);
+
 /* Fine stage and linear branch in one pass:
  * oc = bf16(O_sparse + O_lin), the result of vsa_sparse_attn_fwd followed by
  * vsa_linear_branch, without the fp32 O_sparse round trip and without reading
