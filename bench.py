@@ -497,7 +497,8 @@ def main():
                                        ("tiles: total minus selected blocks" if linear_mode == "tiles" else
                                         "summed per-cube states, applied in the fine stage's epilogue"))}
                if wl.linear else {}),
-            "layout": ("raster q/o; cube-major k, cube-transposed v" if wl.linear else ("raster q, k, v in; fp8 cube-major codes" +
+            "layout": (("cube-major q/k/o (permute, unpermute), cube-transposed v" if args.fused_linear else
+                        "raster q/o; cube-major k, cube-transposed v") if wl.linear else ("raster q, k, v in; fp8 cube-major codes" +
                                                      ("; packed tiles: compact k, slot-layout v" if args.fp8 and
                                                       fp8_packed else "") + "; raster o")
                        if args.fp8 else ("raster q/k/o" if args.k_raster else
